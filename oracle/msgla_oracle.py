@@ -1,0 +1,289 @@
+"""Plain fp64 CPU oracle of the MS-GLA token-mixing layer.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke entry point and the
+benchmark's CPU-baseline leg may import this module.  The GPU library never
+calls it and shares no code with it.
+
+Source: the reading notes "MS-GLA：多时间尺度门控线性注意力研读笔记"
+(cc.laoqi.cc, notes on arXiv:2609.35664 "MS-GLA: Multi-Scale Gated Linear
+Attention ..."), Sec. 2.1 (GLA recurrence), Sec. 3.1-3.4 and Eqs. (8)-(11),
+and its paragraph on streaming inference (the author's per-branch cache).
+
+Everything is float64, one token at a time, in the order the notes describe:
+pool (Eq. 8) -> per-branch projections and gate -> GLA recurrence
+S_t = Diag(alpha_t) S_{t-1} + k_t^T v_t, o_t = q_t S_t -> per-branch output
+projection -> causal hold (Sec. 3.3) -> softmax fusion over branches from the
+unpooled x_t (Eqs. 10-11).  Row-vector convention throughout: x @ W with W
+stored [in][out].
+
+Readings where the notes leave a step open (all listed in the design doc):
+  * the gate is log(alpha) = logsigmoid((xp @ W_g1) @ W_g2 + b_g) / gamma with
+    gamma = 16 and no activation between the two factors; it is computed from
+    the branch's pooled input;
+  * each branch has an output projection W_o [h*d_v, d], no bias; the
+    per-branch normalisation the notes name without a form is omitted
+    (identity), as is any output gate; q is not scaled (q_scale = 1);
+  * only complete pooling blocks enter the recurrence; a partial tail block is
+    never read by the hold and is kept in the streaming cache instead;
+  * positions before a branch's first complete block take zero from that
+    branch, and the fusion weights are not renormalised there.
+
+Parity: every function here is pinned by tests under tests/ against values
+the notes print (the s=4 hold table, the first pooled input), closed forms,
+textbook identities and brute-force products; see the test module docstrings.
+"""
+from __future__ import annotations
+
+import math
+from typing import Dict, List, Optional
+
+import numpy as np
+
+# --------------------------------------------------------------------------
+# Elementary maps
+# --------------------------------------------------------------------------
+
+
+def logsigmoid(z: np.ndarray) -> np.ndarray:
+    """log(1 / (1 + exp(-z))), evaluated without overflow in either tail.
+
+    Gate form of the notes, Sec. 2.1 ("a sigmoid-type map of a low-rank
+    projection", values of alpha in (0, 1)); the logsigmoid/16 form is the
+    one the layer configuration fixes.
+    """
+    z = np.asarray(z, dtype=np.float64)
+    return np.where(z >= 0, -np.log1p(np.exp(-np.abs(z))), z - np.log1p(np.exp(-np.abs(z))))
+
+
+def softmax_lastdim(z: np.ndarray) -> np.ndarray:
+    """Softmax over the last axis with max subtraction (Eq. (10))."""
+    z = np.asarray(z, dtype=np.float64)
+    e = np.exp(z - z.max(axis=-1, keepdims=True))
+    return e / e.sum(axis=-1, keepdims=True)
+
+
+# --------------------------------------------------------------------------
+# Sec. 3.1, Eq. (8): non-overlapping (masked) mean pooling
+# --------------------------------------------------------------------------
+
+
+def pool_eq8(X: np.ndarray, s: int, M: Optional[np.ndarray] = None) -> np.ndarray:
+    """Eq. (8) over all ceil(L/s) blocks, right-padding with zeros.
+
+    X: [B, L, d]; M: [B, L] validity mask (1 = token, 0 = padding), default
+    all ones on the real tokens.  Padded positions carry mask 0, so a partial
+    tail block averages its real tokens, and an all-padding block gives 0
+    (the max(1, .) floor of the denominator).
+    """
+    B, L, d = X.shape
+    if M is None:
+        M = np.ones((B, L))
+    n = -(-L // s)
+    out = np.zeros((B, n, d))
+    for b in range(B):
+        for i in range(n):
+            num = np.zeros(d)
+            den = 0.0
+            for j in range(s):
+                t = i * s + j
+                if t < L:
+                    num += X[b, t] * M[b, t]
+                    den += M[b, t]
+            out[b, i] = num / max(1.0, den)
+    return out
+
+
+def pool_complete_blocks(X: np.ndarray, s: int) -> np.ndarray:
+    """Unmasked Eq. (8) restricted to the floor(L/s) complete blocks: [B, n_s, d]."""
+    B, L, d = X.shape
+    n = L // s
+    out = np.zeros((B, n, d))
+    for j in range(s):
+        out += X[:, j: n * s: s, :] if n > 0 else 0.0
+    return out / s
+
+
+# --------------------------------------------------------------------------
+# Sec. 3.2: independent per-branch projections and forget gate
+# --------------------------------------------------------------------------
+
+
+def branch_projections(xp: np.ndarray, bw, cfg):
+    """q, k, v and log(alpha) of one branch from its pooled input.
+
+    xp: [..., d].  Returns q, k [..., h, d_k], v [..., h, d_v], log_alpha
+    [..., h, d_k].  Head j owns column slice j of every projection.
+    """
+    h = bw.W_q.shape[1] // cfg.d_k
+    lead = xp.shape[:-1]
+    q = cfg.q_scale * (xp @ bw.W_q)
+    k = xp @ bw.W_k
+    v = xp @ bw.W_v
+    g = (xp @ bw.W_g1) @ bw.W_g2 + bw.b_g
+    log_alpha = logsigmoid(g) / cfg.gate_normalizer
+    return (q.reshape(*lead, h, cfg.d_k), k.reshape(*lead, h, cfg.d_k),
+            v.reshape(*lead, h, cfg.d_v), log_alpha.reshape(*lead, h, cfg.d_k))
+
+
+# --------------------------------------------------------------------------
+# Sec. 2.1: the GLA recurrence, one token at a time
+# --------------------------------------------------------------------------
+
+
+def gla_recurrence(q, k, v, log_alpha, S0=None):
+    """S_t = Diag(alpha_t) S_{t-1} + k_t^T v_t ;  o_t = q_t S_t.
+
+    q, k, log_alpha: [B, n, h, d_k]; v: [B, n, h, d_v]; S0: [B, h, d_k, d_v]
+    or None (zeros).  alpha_t scales row c of the state by alpha_{t,c}.
+    Returns (o [B, n, h, d_v], S_n [B, h, d_k, d_v]).
+    """
+    B, n, h, dk = q.shape
+    dv = v.shape[-1]
+    S = np.zeros((B, h, dk, dv)) if S0 is None else np.array(S0, dtype=np.float64)
+    o = np.zeros((B, n, h, dv))
+    alpha = np.exp(log_alpha)
+    for t in range(n):
+        S = alpha[:, t, :, :, None] * S + k[:, t, :, :, None] * v[:, t, :, None, :]
+        o[:, t] = np.einsum("bhc,bhcv->bhv", q[:, t], S)
+    return o, S
+
+
+# --------------------------------------------------------------------------
+# Sec. 3.3: causal hold and fusion
+# --------------------------------------------------------------------------
+
+
+def hold_index(t: int, s: int) -> int:
+    """Coarse output visible at original position t, or -1 for none.
+
+    Block j covers positions js .. js+s-1, so it is complete (usable) from
+    position (j+1)s-1 on, until block j+1 completes: t -> floor((t+1)/s) - 1.
+    """
+    return (t + 1) // s - 1
+
+
+def causal_hold(Y: np.ndarray, s: int, L: int, held_before: Optional[np.ndarray] = None):
+    """[B, n_s, d] coarse outputs -> [B, L, d] per original position."""
+    B, n, d = Y.shape
+    out = np.zeros((B, L, d))
+    for t in range(L):
+        j = hold_index(t, s)
+        if j >= 0:
+            out[:, t] = Y[:, j]
+        elif held_before is not None:
+            out[:, t] = held_before
+    return out
+
+
+def fusion_weights(X: np.ndarray, W_f: np.ndarray, b_f: np.ndarray) -> np.ndarray:
+    """Eq. (10): w_t = softmax(x_t W_f + b_f) from the unpooled x_t: [B, L, m]."""
+    return softmax_lastdim(X @ W_f + b_f)
+
+
+# --------------------------------------------------------------------------
+# The whole layer
+# --------------------------------------------------------------------------
+
+
+def branch_forward(X: np.ndarray, bw, s: int, cfg):
+    """One branch: pool -> project -> recurrence -> output projection.
+
+    Returns (Y [B, n_s, d], final state S [B, h, d_k, d_v], n_s).
+    """
+    B, L, d = X.shape
+    xp = pool_complete_blocks(X, s)
+    n = xp.shape[1]
+    q, k, v, la = branch_projections(xp, bw, cfg)
+    o, S = gla_recurrence(q, k, v, la)
+    Y = o.reshape(B, n, o.shape[2] * o.shape[3]) @ bw.W_o
+    return Y, S, n
+
+
+def layer_forward(X: np.ndarray, W, cfg, return_state: bool = False):
+    """MS-GLA layer forward from a fresh state (Sec. 3, Eqs. (8)-(11)).
+
+    X: [B, L, d] float64 (the values the device sees, upcast).  Returns O
+    [B, L, d]; with ``return_state`` also the streaming cache after the call
+    (see ``decode_step``).
+    """
+    X = np.asarray(X, dtype=np.float64)
+    B, L, d = X.shape
+    m = len(cfg.scales)
+    w = np.ones((B, L, 1)) if m == 1 else fusion_weights(X, W.W_f, W.b_f)
+    O = np.zeros((B, L, d))
+    state = {"pos": L, "branches": []}
+    for i, (s, bw) in enumerate(zip(cfg.scales, W.branches)):
+        Y, S, n = branch_forward(X, bw, s, cfg)
+        O += w[:, :, i: i + 1] * causal_hold(Y, s, L)
+        if return_state:
+            tail = X[:, n * s: L, :]
+            state["branches"].append({
+                "S": S,
+                "psum": tail.sum(axis=1),
+                "count": L - n * s,
+                "held": Y[:, n - 1] if n > 0 else np.zeros((B, d)),
+            })
+    return (O, state) if return_state else O
+
+
+def init_state(cfg, batch: int) -> Dict:
+    """Empty streaming cache: zero state, empty pooling buffer, zero held output."""
+    brs = []
+    for h in cfg.heads:
+        brs.append({"S": np.zeros((batch, h, cfg.d_k, cfg.d_v)),
+                    "psum": np.zeros((batch, cfg.d_model)), "count": 0,
+                    "held": np.zeros((batch, cfg.d_model))})
+    return {"pos": 0, "branches": brs}
+
+
+def decode_step(state: Dict, x_t: np.ndarray, W, cfg):
+    """One streaming step (the notes' paragraph on token-by-token inference).
+
+    Each branch keeps its GLA state, the not-yet-complete block of hidden
+    states (here its running sum and count) and its latest output.  A new
+    token is accumulated; when s tokens have arrived they are pooled, the
+    branch takes one recurrence step, and the held output is replaced;
+    otherwise the held output is reused.  The branches are then fused with
+    weights from the unpooled x_t (Eqs. (10)-(11)).
+    x_t: [B, d].  Returns (o_t [B, d], new state); the input state is not
+    modified.
+    """
+    x_t = np.asarray(x_t, dtype=np.float64)
+    B, d = x_t.shape
+    m = len(cfg.scales)
+    new = {"pos": state["pos"] + 1, "branches": []}
+    w = np.ones((B, 1)) if m == 1 else softmax_lastdim(x_t @ W.W_f + W.b_f)
+    o = np.zeros((B, d))
+    for i, (s, bw) in enumerate(zip(cfg.scales, W.branches)):
+        st = state["branches"][i]
+        psum = st["psum"] + x_t
+        count = st["count"] + 1
+        S, held = st["S"], st["held"]
+        if count == s:
+            xp = psum / s
+            q, k, v, la = branch_projections(xp[:, None, :], bw, cfg)
+            y, S = gla_recurrence(q, k, v, la, S0=S)
+            held = y.reshape(B, -1) @ bw.W_o
+            psum = np.zeros((B, d))
+            count = 0
+        new["branches"].append({"S": S, "psum": psum, "count": count, "held": held})
+        o += w[:, i: i + 1] * held
+    return o, new
+
+
+def recurrence_updates(cfg, L: int) -> int:
+    """Number of per-head state updates one forward of length L performs."""
+    return sum(h * (L // s) for s, h in zip(cfg.scales, cfg.heads))
+
+
+def row_relative_error(O_dev: np.ndarray, O_ref: np.ndarray):
+    """max_t ||O_t - Ref_t||_inf / ||Ref_t||_inf over rows with Ref_t != 0,
+    and whether every all-zero reference row is exactly zero on the device."""
+    O_dev = np.asarray(O_dev, dtype=np.float64).reshape(-1, O_ref.shape[-1])
+    O_ref = np.asarray(O_ref, dtype=np.float64).reshape(-1, O_ref.shape[-1])
+    den = np.abs(O_ref).max(axis=1)
+    num = np.abs(O_dev - O_ref).max(axis=1)
+    nz = den > 0
+    err = float((num[nz] / den[nz]).max()) if nz.any() else 0.0
+    zero_rows_exact = bool(np.all(O_dev[~nz] == 0.0))
+    return err, zero_rows_exact

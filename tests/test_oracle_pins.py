@@ -1,0 +1,366 @@
+"""Pins of the fp64 oracle against things other than itself (CPU only).
+
+Each test checks one part of the oracle against a value the MS-GLA reading
+notes print, a closed form, a textbook identity, or a brute-force product
+written differently from the oracle's recurrence.  Together they are meant to
+catch a dropped term, a wrong sign or index, or a transposed operand anywhere
+in the oracle:
+
+  recurrence    brute-force unrolled products (no logs, no recurrence),
+                alpha = 1 -> ((Q K^T) o tril) V, constant-gate impulse closed form
+  gate          logsigmoid closed forms and tails, the /16 normaliser
+  pooling       the notes' first s=4 input, masked Eq. (8) corner cases,
+                reshape-mean, pool/project commutation
+  hold          the notes' s=4 table (golden), repeat-then-shift construction
+  fusion        simplex, uniform at W_f = 0, two-branch closed form
+  whole layer   a hand-derived scalar example, causality, decode == forward,
+                edge cases ({2,4} at t=0, L < s), state budget and update
+                ratio (golden), the half-life remark of Sec. 3.3
+"""
+import math
+
+import numpy as np
+import pytest
+
+from oracle import msgla_oracle as orc
+from scale_gla_layer_amd.config import MsglaConfig, F32, WORKLOADS
+from scale_gla_layer_amd.synth import BranchWeights, LayerWeights, make_inputs
+from tests.golden_io import read_fixture
+
+
+def _rand(rng, *shape):
+    return rng.normal(0.0, 1.0, shape)
+
+
+# --------------------------------------------------------------------------- recurrence
+
+
+@pytest.mark.parametrize("n", [1, 3, 5, 8, 13])
+def test_recurrence_matches_unrolled_products(n):
+    """o_t = sum_{i<=t} sum_c q_tc k_ic (prod_{r=i+1..t} alpha_rc) v_i, by explicit loops."""
+    rng = np.random.default_rng(100 + n)
+    B, h, dk, dv = 2, 2, 3, 2
+    q, k = _rand(rng, B, n, h, dk), _rand(rng, B, n, h, dk)
+    v = _rand(rng, B, n, h, dv)
+    la = -np.abs(_rand(rng, B, n, h, dk)) * 0.7
+    o, S = orc.gla_recurrence(q, k, v, la)
+    alpha = [[[[math.exp(la[b, t, j, c]) for c in range(dk)] for j in range(h)]
+              for t in range(n)] for b in range(B)]
+    for b in range(B):
+        for j in range(h):
+            for t in range(n):
+                ref = [0.0] * dv
+                for i in range(t + 1):
+                    for c in range(dk):
+                        p = 1.0
+                        for r in range(i + 1, t + 1):
+                            p *= alpha[b][r][j][c]
+                        coef = q[b, t, j, c] * k[b, i, j, c] * p
+                        for e in range(dv):
+                            ref[e] += coef * v[b, i, j, e]
+                assert np.allclose(o[b, t, j], ref, rtol=0, atol=1e-12)
+            # final state S_n[c, :] = sum_i prod_{r>i} alpha_rc k_ic v_i
+            for c in range(dk):
+                ref = [0.0] * dv
+                for i in range(n):
+                    p = 1.0
+                    for r in range(i + 1, n):
+                        p *= alpha[b][r][j][c]
+                    for e in range(dv):
+                        ref[e] += p * k[b, i, j, c] * v[b, i, j, e]
+                assert np.allclose(S[b, j, c], ref, rtol=0, atol=1e-12)
+
+
+def test_unit_gate_is_causal_linear_attention():
+    """alpha = 1: o = ((Q K^T) o tril) V, the un-normalised causal linear attention."""
+    rng = np.random.default_rng(7)
+    B, n, h, dk, dv = 2, 17, 3, 5, 4
+    q, k, v = _rand(rng, B, n, h, dk), _rand(rng, B, n, h, dk), _rand(rng, B, n, h, dv)
+    o, _ = orc.gla_recurrence(q, k, v, np.zeros((B, n, h, dk)))
+    for b in range(B):
+        for j in range(h):
+            A = np.tril(q[b, :, j] @ k[b, :, j].T)
+            assert np.allclose(o[b, :, j], A @ v[b, :, j], rtol=1e-12, atol=1e-12)
+
+
+def test_constant_gate_impulse_closed_form():
+    """Constant alpha = a on every channel, only k_0 non-zero: o_j = a^j (q_j . k_0) v_0."""
+    rng = np.random.default_rng(11)
+    B, n, h, dk, dv = 1, 12, 1, 4, 3
+    a = 0.83
+    q, v = _rand(rng, B, n, h, dk), _rand(rng, B, n, h, dv)
+    k = np.zeros((B, n, h, dk))
+    k[:, 0] = _rand(rng, B, h, dk)
+    o, _ = orc.gla_recurrence(q, k, v, np.full((B, n, h, dk), math.log(a)))
+    for t in range(n):
+        ref = a ** t * float(q[0, t, 0] @ k[0, 0, 0]) * v[0, 0, 0]
+        assert np.allclose(o[0, t, 0], ref, rtol=1e-12, atol=1e-14)
+
+
+# --------------------------------------------------------------------------- gate
+
+
+@pytest.mark.parametrize("z", [-30.0, -3.0, -0.5, 0.0, 0.25, 2.0, 9.0])
+def test_logsigmoid_closed_form(z):
+    ref = math.log(1.0 / (1.0 + math.exp(-z)))
+    assert abs(float(orc.logsigmoid(np.array(z))) - ref) <= 1e-14 * max(1.0, abs(ref))
+
+
+def test_logsigmoid_tails_and_zero():
+    assert float(orc.logsigmoid(np.array(0.0))) == pytest.approx(-math.log(2.0), abs=1e-16)
+    assert float(orc.logsigmoid(np.array(-800.0))) == pytest.approx(-800.0, rel=1e-15)
+    assert float(orc.logsigmoid(np.array(40.0))) == pytest.approx(-math.exp(-40.0), rel=1e-12)
+    assert np.all(orc.logsigmoid(np.linspace(-50, 50, 101)) < 0)
+
+
+def test_gate_normaliser_closed_form():
+    """W_g2 = 0 and b_g = z0: alpha = sigmoid(z0)^(1/16) for every position and channel."""
+    cfg = MsglaConfig((1,), (1,), 4, 2, 3, 2, 16, 16.0, 1.0, F32)
+    rng = np.random.default_rng(3)
+    for z0 in (-4.0, 0.0, 1.5):
+        bw = BranchWeights(_rand(rng, 4, 2), _rand(rng, 4, 2), _rand(rng, 4, 3), _rand(rng, 4, 2),
+                           np.zeros((2, 2)), np.full(2, z0), _rand(rng, 3, 4))
+        *_, la = orc.branch_projections(_rand(rng, 5, 4), bw, cfg)
+        ref = (1.0 / (1.0 + math.exp(-z0))) ** (1.0 / 16.0)
+        assert np.allclose(np.exp(la), ref, rtol=1e-14)
+
+
+# --------------------------------------------------------------------------- pooling
+
+
+def test_first_pooled_input_s4_matches_notes():
+    fx = read_fixture("first_pooled_s4.txt")
+    s, members, div = int(fx["s"][0]), [int(x) for x in fx["members"]], float(fx["divisor"][0])
+    rng = np.random.default_rng(5)
+    X = _rand(rng, 1, 13, 6)
+    xp = orc.pool_complete_blocks(X, s)
+    ref = sum(X[0, i] for i in members) / div
+    assert np.allclose(xp[0, 0], ref, rtol=0, atol=1e-15)
+    assert np.allclose(orc.pool_eq8(X, s)[0, 0], ref, rtol=0, atol=1e-15)
+
+
+def test_pool_reshape_mean_and_eq8_agree():
+    rng = np.random.default_rng(6)
+    for s in (1, 2, 3, 4, 8):
+        for L in (1, 3, 8, 13, 16):
+            X = _rand(rng, 2, L, 5)
+            n = L // s
+            ref = X[:, : n * s].reshape(2, n, s, 5).mean(axis=2)
+            assert np.allclose(orc.pool_complete_blocks(X, s), ref, atol=1e-14)
+            assert np.allclose(orc.pool_eq8(X, s)[:, :n], ref, atol=1e-14)
+
+
+def test_masked_pooling_eq8_corner_cases():
+    """Mask: average of the valid tokens only; an all-padding block gives 0."""
+    rng = np.random.default_rng(8)
+    X = _rand(rng, 1, 12, 3)
+    M = np.ones((1, 12))
+    M[0, 4:8] = 0.0          # block 1 of s=4 is all padding
+    M[0, 9] = 0.0            # block 2 keeps tokens 8, 10, 11
+    xp = orc.pool_eq8(X, 4, M)
+    assert np.array_equal(xp[0, 1], np.zeros(3))
+    assert np.allclose(xp[0, 2], (X[0, 8] + X[0, 10] + X[0, 11]) / 3.0, atol=1e-15)
+    # ragged tail (L = 10, s = 4): the padded tail block averages its 2 real tokens
+    xp2 = orc.pool_eq8(X[:, :10], 4)
+    assert xp2.shape[1] == 3
+    assert np.allclose(xp2[0, 2], (X[0, 8] + X[0, 9]) / 2.0, atol=1e-15)
+
+
+def test_pool_then_project_equals_project_then_average():
+    rng = np.random.default_rng(9)
+    X, W = _rand(rng, 2, 16, 6), _rand(rng, 6, 4)
+    for s in (2, 4):
+        a = orc.pool_complete_blocks(X, s) @ W
+        b = orc.pool_complete_blocks(X @ W, s)
+        assert np.allclose(a, b, atol=1e-13)
+
+
+# --------------------------------------------------------------------------- hold
+
+
+def test_hold_table_s4_matches_notes():
+    fx = read_fixture("hold_table_s4.txt")
+    s = int(fx["s"][0])
+    for t, j in zip(map(int, fx["t"]), map(int, fx["j"])):
+        assert orc.hold_index(t, s) == j
+
+
+def test_hold_equals_repeat_then_shift():
+    """Repeat each coarse output s times, shift right by s-1, zero-fill, truncate to L."""
+    rng = np.random.default_rng(10)
+    for s in range(1, 9):
+        for L in range(1, 64):
+            n = L // s
+            Y = _rand(rng, 1, n, 2)
+            rep = np.repeat(Y, s, axis=1)
+            shifted = np.concatenate([np.zeros((1, s - 1, 2)), rep], axis=1)
+            ref = np.zeros((1, L, 2))
+            m = min(L, shifted.shape[1])
+            ref[:, :m] = shifted[:, :m]
+            assert np.array_equal(orc.causal_hold(Y, s, L), ref), (s, L)
+
+
+# --------------------------------------------------------------------------- fusion
+
+
+def test_fusion_weights_simplex_and_uniform():
+    rng = np.random.default_rng(12)
+    X = _rand(rng, 2, 9, 7)
+    w = orc.fusion_weights(X, _rand(rng, 7, 3), _rand(rng, 3))
+    assert w.shape == (2, 9, 3)
+    assert np.all(w > 0) and np.allclose(w.sum(-1), 1.0, atol=1e-15)
+    assert np.allclose(orc.fusion_weights(X, np.zeros((7, 3)), np.zeros(3)), 1.0 / 3.0, atol=1e-16)
+    w2 = orc.fusion_weights(X, np.zeros((7, 2)), np.array([0.0, math.log(3.0)]))
+    assert np.allclose(w2, [0.25, 0.75], atol=1e-15)
+
+
+# --------------------------------------------------------------------------- whole layer
+
+
+def _scalar_example():
+    cfg = MsglaConfig((1, 2), (1, 1), 1, 1, 1, 1, 16, 16.0, 1.0, F32)
+    one = lambda v: np.array([[v]], dtype=np.float64)
+    b1 = BranchWeights(one(1), one(1), one(1), one(0), one(0), np.array([0.0]), one(1))
+    b2 = BranchWeights(one(2), one(1), one(3), one(1), one(1), np.array([0.5]), one(0.5))
+    W = LayerWeights([b1, b2], np.array([[0.0, 1.0]]), np.zeros(2))
+    X = np.array([1.0, 2.0, 3.0, 4.0]).reshape(1, 4, 1)
+    return cfg, W, X
+
+
+def test_hand_derived_scalar_layer():
+    """d = d_k = d_v = r = 1, scales {1, 2}; every quantity written out by hand.
+
+    Branch s=1: q = k = v = x, alpha = sigmoid(0)^(1/16) = 2^(-1/16),
+    y1_t = x_t * sum_{i<=t} a^(t-i) x_i^2.
+    Branch s=2: pooled xp = (1.5, 3.5); q = 2xp, k = xp, v = 3xp,
+    alpha_j = sigmoid(xp_j + 0.5)^(1/16); y_0 = q_0 k_0 v_0,
+    y_1 = q_1 (alpha_1 k_0 v_0 + k_1 v_1); Y = 0.5 y; held as (0, Y0, Y0, Y1).
+    Fusion from the unpooled token: w_t = (1, e^{x_t}) / (1 + e^{x_t}).
+    """
+    cfg, W, X = _scalar_example()
+    x = [1.0, 2.0, 3.0, 4.0]
+    a = 2.0 ** (-1.0 / 16.0)
+    y1 = [x[t] * sum(a ** (t - i) * x[i] ** 2 for i in range(t + 1)) for t in range(4)]
+    xp = [1.5, 3.5]
+    al = [(1.0 / (1.0 + math.exp(-(xp[j] + 0.5)))) ** (1.0 / 16.0) for j in range(2)]
+    Y0 = 0.5 * (2 * xp[0]) * xp[0] * (3 * xp[0])
+    Y1 = 0.5 * (2 * xp[1]) * (al[1] * xp[0] * 3 * xp[0] + xp[1] * 3 * xp[1])
+    held = [0.0, Y0, Y0, Y1]
+    ref = [(y1[t] + math.exp(x[t]) * held[t]) / (1.0 + math.exp(x[t])) for t in range(4)]
+    O = orc.layer_forward(X, W, cfg)
+    assert np.allclose(O[0, :, 0], ref, rtol=1e-13, atol=0)
+
+
+def _tiny():
+    wl = WORKLOADS["tiny_f32"]
+    return wl.cfg
+
+
+def test_causality_whole_layer():
+    cfg = _tiny()
+    X, W = make_inputs(cfg, 1, 48, seed=1)
+    O = orc.layer_forward(X, W, cfg)
+    for t0 in (0, 5, 22, 46):
+        X2 = X.copy()
+        X2[:, t0 + 1:] += np.random.default_rng(t0).normal(0, 3.0, X2[:, t0 + 1:].shape)
+        O2 = orc.layer_forward(X2, W, cfg)
+        assert np.array_equal(O[:, : t0 + 1], O2[:, : t0 + 1])
+        assert not np.allclose(O[:, t0 + 1:], O2[:, t0 + 1:])
+
+
+def test_single_scale_layer_is_plain_gla():
+    """S = {1}: weights are 1, the hold is the identity, O = GLA(X) W_o."""
+    cfg = MsglaConfig((1,), (2,), 8, 4, 6, 2, 16, 16.0, 1.0, F32)
+    X, W = make_inputs(cfg, 2, 11, seed=4)
+    q, k, v, la = orc.branch_projections(X, W.branches[0], cfg)
+    o, _ = orc.gla_recurrence(q, k, v, la)
+    ref = o.reshape(2, 11, -1) @ W.branches[0].W_o
+    assert np.allclose(orc.layer_forward(X, W, cfg), ref, rtol=1e-13, atol=1e-15)
+
+
+@pytest.mark.parametrize("L0", [0, 1, 37, 40])
+def test_decode_equals_forward(L0):
+    cfg = _tiny()
+    L = 52
+    X, W = make_inputs(cfg, 2, L, seed=2)
+    O = orc.layer_forward(X, W, cfg)
+    if L0 == 0:
+        st = orc.init_state(cfg, 2)
+    else:
+        O0, st = orc.layer_forward(X[:, :L0], W, cfg, return_state=True)
+        assert np.allclose(O0, O[:, :L0], rtol=1e-12, atol=1e-14)
+    for t in range(L0, L):
+        o, st = orc.decode_step(st, X[:, t], W, cfg)
+        assert np.allclose(o, O[:, t], rtol=1e-11, atol=1e-13), t
+    assert st["pos"] == L
+
+
+def test_no_fine_branch_first_position_is_zero():
+    cfg = MsglaConfig((2, 4), (1, 1), 16, 4, 4, 2, 16, 16.0, 1.0, F32)
+    X, W = make_inputs(cfg, 2, 16, seed=3)
+    O = orc.layer_forward(X, W, cfg)
+    assert np.array_equal(O[:, 0], np.zeros((2, 16)))
+    assert np.all(np.abs(O[:, 1]) > 0)
+
+
+def test_branch_longer_than_sequence_contributes_nothing():
+    cfg = MsglaConfig((1, 8), (1, 1), 8, 4, 4, 2, 16, 16.0, 1.0, F32)
+    X, W = make_inputs(cfg, 1, 7, seed=5)
+    O = orc.layer_forward(X, W, cfg)
+    W.branches[1] = BranchWeights(*(np.zeros_like(a) for a in (
+        W.branches[1].W_q, W.branches[1].W_k, W.branches[1].W_v, W.branches[1].W_g1,
+        W.branches[1].W_g2, W.branches[1].b_g, W.branches[1].W_o)))
+    assert np.array_equal(O, orc.layer_forward(X, W, cfg))
+
+
+def test_state_budget_matches_notes():
+    fx = read_fixture("state_budget.txt")
+    d, H, dk, dv = (int(fx[k][0]) for k in ("d_model", "heads", "d_k", "d_v"))
+    for name in ("gla_baseline", "main", "sweep_1248", "sweep_24"):
+        cfg = WORKLOADS[name].cfg
+        assert (cfg.d_model, cfg.total_heads, cfg.d_k, cfg.d_v) == (d, H, dk, dv)
+        st = orc.init_state(cfg, 1)
+        assert sum(b["S"].size for b in st["branches"]) == int(fx["elements"][0])
+
+
+def test_update_ratio_matches_notes(monkeypatch):
+    """Count the updates the oracle actually executes for {1,2,4}/[2,1,1] vs GLA."""
+    fx = read_fixture("update_ratio.txt")
+    counted = []
+    real = orc.gla_recurrence
+
+    def counting(q, k, v, la, S0=None):
+        counted.append(q.shape[1] * q.shape[2])
+        return real(q, k, v, la, S0)
+
+    monkeypatch.setattr(orc, "gla_recurrence", counting)
+    small = lambda sc, hd: MsglaConfig(sc, hd, 8, 2, 2, 2, 16, 16.0, 1.0, F32)
+    L = 32
+    ms, gla = small((1, 2, 4), (2, 1, 1)), small((1,), (4,))
+    for cfg in (ms, gla):
+        X, W = make_inputs(cfg, 1, L, seed=0)
+        counted.clear()
+        orc.layer_forward(X, W, cfg)
+        assert sum(counted) == orc.recurrence_updates(cfg, L)
+    ratio = orc.recurrence_updates(ms, L) / orc.recurrence_updates(gla, L)
+    assert ratio == int(fx["numerator"][0]) / int(fx["denominator"][0])
+    assert ratio * 100 == float(fx["percent"][0])
+
+
+def test_half_life_remark():
+    """Sec. 3.3: under a constant per-update factor a, branch s keeps a write for
+    about s*ln(1/2)/ln(a) original tokens.  Impulse through recurrence + hold."""
+    a = 0.9
+    for s in (1, 2, 4):
+        L = 400
+        n = L // s
+        q = np.ones((1, n, 1, 1))
+        k = np.zeros((1, n, 1, 1))
+        k[0, 0] = 1.0
+        v = np.ones((1, n, 1, 1))
+        o, _ = orc.gla_recurrence(q, k, v, np.full((1, n, 1, 1), math.log(a)))
+        r = orc.causal_hold(o.reshape(1, n, 1), s, L)[0, :, 0]
+        first = s - 1                                  # block 0 becomes visible here
+        half = next(t for t in range(first, L) if r[t] <= 0.5 * r[first])
+        predicted = s * math.log(0.5) / math.log(a)
+        assert abs((half - first) - predicted) <= s, (s, half, predicted)
