@@ -1,0 +1,205 @@
+/*
+ * msgla.h — C ABI of the MS-GLA token-mixing layer forward for AMD MI355X (gfx950).
+ *
+ * The layer (reading notes "MS-GLA：多时间尺度门控线性注意力研读笔记" on
+ * arXiv:2609.35664, "MS-GLA: Multi-Scale Gated Linear Attention ...", Sec. 3,
+ * Eqs. (8)-(11)): for every scale s of the branch set, average-pool the hidden
+ * states X [L x d] over non-overlapping blocks of s tokens (Sec. 3.1, Eq. (8)),
+ * project the pooled states to q, k, v and a low-rank forget gate with
+ * per-branch weights (Sec. 3.2, Eq. (9)), run gated linear attention
+ *     S_t = Diag(alpha_t) S_{t-1} + k_t^T v_t,   o_t = q_t S_t
+ * (Sec. 2.1), project back to d, causally hold each coarse output from
+ * position (j+1)s-1 until the next block completes (Sec. 3.3), and fuse the
+ * branches per position with softmax weights computed from the unpooled x_t
+ * (Sec. 3.3, Eqs. (10)-(11)).
+ *
+ * Conventions shared by every entry point:
+ *  - All tensor pointers are DEVICE pointers unless stated otherwise, row-major,
+ *    16-byte aligned.  The caller owns every buffer (inputs, outputs, packed
+ *    weights, workspace, state); the library allocates nothing, keeps no
+ *    global state and never synchronises: work is enqueued on `stream` (a
+ *    hipStream_t; NULL = the null stream) and completes asynchronously.
+ *    Calls with distinct workspaces may run concurrently.
+ *  - Errors in arguments are detected on the host before anything is enqueued
+ *    and are returned synchronously; a failed kernel launch returns
+ *    MSGLA_ERR_HIP.  NaN and Inf in the data are not checked; they propagate.
+ *  - Element type: `dtype` of the config.  MSGLA_BF16 stores x, weights and
+ *    outputs as bfloat16 and accumulates in fp32 (the recurrent state, the
+ *    cumulative log-decay and all accumulators are fp32); MSGLA_F32 stores and
+ *    computes everything in fp32.  Biases are always fp32.
+ */
+#ifndef MSGLA_H
+#define MSGLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MSGLA_OK = 0,
+  MSGLA_ERR_INVALID_ARG = 1,  /* bad config, NULL or misaligned pointer, bad size */
+  MSGLA_ERR_UNSUPPORTED = 2,  /* valid request this build does not implement      */
+  MSGLA_ERR_WORKSPACE = 3,    /* workspace / buffer smaller than the size query    */
+  MSGLA_ERR_HIP = 4           /* a HIP runtime call or kernel launch failed        */
+} msgla_status;
+
+typedef enum { MSGLA_F32 = 0, MSGLA_BF16 = 1 } msgla_dtype;
+
+#define MSGLA_MAX_BRANCHES 8
+
+/*
+ * Layer configuration.  Branch i pools over blocks of scale[i] tokens and owns
+ * heads[i] heads of key width d_k and value width d_v (Sec. 3.2: the total head
+ * count H = sum heads[i] is what a single-scale GLA layer would have).
+ * gate_rank r: rank of the forget-gate projection W_g1 [d x r] W_g2 [r x h d_k];
+ * log(alpha) = logsigmoid(xp W_g1 W_g2 + b_g) / gate_normalizer.
+ * chunk: length of the GPU chunk schedule (16, 32 or 64); the result does not
+ * depend on it beyond rounding (Sec. 3.4 separates it from the pooling block).
+ * q_scale multiplies q (1.0 reproduces the notes' recurrence).
+ * Requirements: 1 <= n_branches <= 8; scales positive and distinct; heads
+ * positive; d_model a positive multiple of 64; d_k and d_v positive multiples
+ * of 16 with d_k <= 256 and d_v <= 512; 1 <= gate_rank <= 64.
+ */
+typedef struct {
+  int32_t n_branches;
+  int32_t scale[MSGLA_MAX_BRANCHES];
+  int32_t heads[MSGLA_MAX_BRANCHES];
+  int32_t d_model;
+  int32_t d_k;
+  int32_t d_v;
+  int32_t gate_rank;
+  int32_t chunk;
+  float gate_normalizer;
+  float q_scale;
+  int32_t dtype; /* msgla_dtype */
+} msgla_config;
+
+/*
+ * Unpacked weights of one branch, in the notes' row-vector convention
+ * (y = x W, W stored [in][out] row-major), element type = config dtype
+ * except the fp32 bias.  Head j of the branch owns column slice j of W_q, W_k,
+ * W_v, W_g2, b_g and row slice j of W_o.
+ *   W_q, W_k [d][h d_k]   W_v [d][h d_v]   W_g1 [d][r]   W_g2 [r][h d_k]
+ *   b_g [h d_k] (fp32)    W_o [h d_v][d]   (per-branch output projection, no bias)
+ */
+typedef struct {
+  const void* W_q;
+  const void* W_k;
+  const void* W_v;
+  const void* W_g1;
+  const void* W_g2;
+  const float* b_g;
+  const void* W_o;
+} msgla_branch_weights;
+
+/* All weights.  W_f [d][m] (config dtype) and b_f [m] (fp32) give the fusion
+ * logits z_t = x_t W_f + b_f over the m = n_branches branches (Eq. (10)); both
+ * are ignored (and may be NULL) when m == 1. */
+typedef struct {
+  msgla_branch_weights br[MSGLA_MAX_BRANCHES];
+  const void* W_f;
+  const float* b_f;
+} msgla_weights;
+
+/* Human-readable name of a status code (static string). */
+const char* msgla_status_str(msgla_status s);
+
+/* Host-only check of a configuration against the requirements above. */
+msgla_status msgla_validate_config(const msgla_config* cfg);
+
+/*
+ * Packed weights: one device blob in the layout the kernels read (per branch
+ * the concatenated, transposed [q|k|v|g1|fusion] projection, the fp32 gate
+ * factor and bias, and the stacked transposed output projections).  Packing is
+ * done once per set of weights; `msgla_forward` and `msgla_decode_step` read
+ * only the packed blob.  Returns 0 for an invalid config.
+ */
+size_t msgla_packed_weights_bytes(const msgla_config* cfg);
+
+/* Packs `w` (device pointers, layout above) into `packed` (device,
+ * >= msgla_packed_weights_bytes bytes) on `stream`.  `w` is read during the
+ * call's execution on the stream; the struct itself is copied at call time. */
+msgla_status msgla_pack_weights(const msgla_config* cfg, const msgla_weights* w, void* packed,
+                                size_t packed_bytes, void* stream);
+
+/* Device workspace needed by msgla_forward for batch B and length L (bytes). */
+size_t msgla_workspace_bytes(const msgla_config* cfg, int64_t B, int64_t L);
+
+/*
+ * Streaming state ("cache" of the notes' paragraph on token-by-token
+ * inference): per branch the fp32 GLA state S [B][h][d_k][d_v], the fp32 sum
+ * of the not-yet-complete pooling block [B][d] and the fp32 held output
+ * (the branch's latest coarse output after W_o) [B][d], plus the number of
+ * tokens consumed so far.  Opaque, versioned blob; its recurrent part is
+ * sum_s h_s d_k d_v fp32 elements per sequence.
+ */
+size_t msgla_state_bytes(const msgla_config* cfg, int64_t B);
+
+/* Writes an empty state (position 0, zero state, empty blocks, zero held
+ * outputs) into `state` (device, >= msgla_state_bytes). */
+msgla_status msgla_state_init(const msgla_config* cfg, int64_t B, void* state, size_t state_bytes,
+                              void* stream);
+
+/*
+ * Layer forward over a batch of B sequences of L tokens from an empty state.
+ *   x [B][L][d] (dtype) -> out [B][L][d] (dtype).
+ *   mask: must be NULL (masked pooling, Eq. (8) with M, is not implemented:
+ *         MSGLA_ERR_UNSUPPORTED).
+ *   state_in: must be NULL (continuing from a previous state is not
+ *         implemented: MSGLA_ERR_UNSUPPORTED).
+ *   state_out: NULL, or a buffer of msgla_state_bytes(cfg, B) that receives
+ *         the streaming state after the L tokens (for msgla_decode_step).
+ *   workspace: >= msgla_workspace_bytes(cfg, B, L) bytes of device memory;
+ *         its contents on entry are irrelevant.
+ * L may be any value >= 1; branches with s > L contribute zero.
+ */
+msgla_status msgla_forward(const msgla_config* cfg, const void* packed, const void* x,
+                           const uint8_t* mask, int64_t B, int64_t L, void* out,
+                           const void* state_in, void* state_out, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+/*
+ * Optional per-stage timing: hipEvent_t handles recorded on `stream`
+ * immediately before (start[i]) and after (stop[i]) stage i of the forward:
+ * 0 = pooled projection GEMM, 1 = chunk-local gate/decay/intra-chunk kernel,
+ * 2 = chunk-state recurrence kernel, 3 = hold + fusion + output projection
+ * GEMM.  NULL entries are skipped.  Events are recorded, never waited on.
+ */
+#define MSGLA_N_STAGES 4
+typedef struct {
+  void* start[MSGLA_N_STAGES];
+  void* stop[MSGLA_N_STAGES];
+} msgla_stage_events;
+
+/* msgla_forward with optional stage events (NULL = none). */
+msgla_status msgla_forward_timed(const msgla_config* cfg, const void* packed, const void* x,
+                                 const uint8_t* mask, int64_t B, int64_t L, void* out,
+                                 const void* state_in, void* state_out, void* workspace,
+                                 size_t workspace_bytes, void* stream,
+                                 const msgla_stage_events* events);
+
+/* Device workspace needed by msgla_decode_step for batch B (bytes). */
+size_t msgla_decode_workspace_bytes(const msgla_config* cfg, int64_t B);
+
+/*
+ * One streaming step for B sequences (the notes' per-branch cache): every
+ * branch adds x_t to its pending block; a branch whose block completes (s
+ * tokens) pools it, takes one recurrence step and replaces its held output;
+ * the others keep theirs; the held outputs are fused with weights from the
+ * unpooled x_t.  The result equals msgla_forward's output at the same
+ * position (up to rounding).
+ *   x_t [B][d] (dtype) -> out_t [B][d] (dtype); state: in/out (device,
+ *   produced by msgla_state_init or msgla_forward's state_out with the same B).
+ */
+msgla_status msgla_decode_step(const msgla_config* cfg, const void* packed, const void* x_t,
+                               int64_t B, void* state, void* out_t, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MSGLA_H */

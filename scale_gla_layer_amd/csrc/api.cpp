@@ -1,0 +1,592 @@
+// Host side of the C ABI declared in include/msgla.h: validation, the packed /
+// workspace / state layouts, and the launch sequence of the forward and the
+// decode step.  No allocation, no synchronisation, no global state.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+#include <cstring>
+
+#include "../../include/msgla.h"
+#include "layout.hpp"
+
+namespace msgla {
+// launchers (one per kernel file)
+hipError_t launch_k1(const K1Params& P, bool bf16_path, hipStream_t stream);
+hipError_t launch_k2a(const K2Params& P, bool bf16_path, hipStream_t stream);
+hipError_t launch_k2b(const K2Params& P, bool bf16_path, hipStream_t stream);
+hipError_t launch_k3(const K3Params& P, bool bf16_path, hipStream_t stream);
+hipError_t launch_state_export(const StateParams& P, bool bf16_path, hipStream_t st);
+hipError_t launch_state_header(void* state, int B, int m, int64_t pos, hipStream_t st);
+hipError_t launch_decode(const DecParams& P, int Nmax, int hmax, bool bf16_path, hipStream_t st);
+hipError_t pack_transpose(bool bf16_path, const void* src, int R, int Cn, void* dst,
+                          size_t dst_ld, hipStream_t st);
+hipError_t pack_to_f32(bool src_bf16, const void* src, size_t n, float* dst, hipStream_t st);
+hipError_t fill_zero(void* p, size_t bytes, hipStream_t st);
+size_t k2a_lds_bytes(int C, int dk, bool bf16_path);
+size_t k2b_lds_bytes(int C, int dk, bool bf16_path);
+int k2b_dvt();
+}  // namespace msgla
+
+using namespace msgla;
+
+namespace {
+
+constexpr int GEMM_TILE = 128;
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+int cdiv(int a, int b) { return (a + b - 1) / b; }
+
+struct BranchGeom {
+  int s, h;
+  int col_k, col_v, col_g, col_z, N;  // projection columns
+  int ko, kp;                         // stacked W_o^T K range
+  size_t off_Wp, off_W2, off_bg;      // packed offsets
+};
+
+struct PackGeom {
+  bool bf16;
+  int es, m, d, dk, dv, r, rp, C, Ktot, carrier;
+  size_t off_Wz;  // 0 if none (fusion carried by a branch or m == 1)
+  bool has_Wz;
+  size_t off_bf, off_WoT, total;
+  BranchGeom br[MSGLA_MAX_BRANCHES];
+};
+
+msgla_status check_config(const msgla_config* c) {
+  if (!c) return MSGLA_ERR_INVALID_ARG;
+  if (c->n_branches < 1 || c->n_branches > MSGLA_MAX_BRANCHES) return MSGLA_ERR_INVALID_ARG;
+  if (c->dtype != MSGLA_F32 && c->dtype != MSGLA_BF16) return MSGLA_ERR_INVALID_ARG;
+  const bool bf = c->dtype == MSGLA_BF16;
+  for (int i = 0; i < c->n_branches; ++i) {
+    if (c->scale[i] < 1 || c->heads[i] < 1 || c->heads[i] > 64) return MSGLA_ERR_INVALID_ARG;
+    for (int j = 0; j < i; ++j)
+      if (c->scale[j] == c->scale[i]) return MSGLA_ERR_INVALID_ARG;
+  }
+  if (c->d_model < 64 || c->d_model % 64 != 0 || c->d_model > 65536) return MSGLA_ERR_INVALID_ARG;
+  if (c->d_k < 16 || c->d_k > 256 || c->d_k % (bf ? 32 : 16) != 0) return MSGLA_ERR_INVALID_ARG;
+  if (c->d_v < 32 || c->d_v > 512 || c->d_v % 32 != 0) return MSGLA_ERR_INVALID_ARG;
+  if (c->gate_rank < 1 || c->gate_rank > 64) return MSGLA_ERR_INVALID_ARG;
+  if (bf ? (c->chunk != 32 && c->chunk != 64)
+         : (c->chunk != 16 && c->chunk != 32 && c->chunk != 64))
+    return MSGLA_ERR_INVALID_ARG;
+  if (!(c->gate_normalizer > 0.f) || !(c->q_scale == c->q_scale)) return MSGLA_ERR_INVALID_ARG;
+  return MSGLA_OK;
+}
+
+PackGeom pack_geom(const msgla_config* c) {
+  PackGeom g{};
+  g.bf16 = c->dtype == MSGLA_BF16;
+  g.es = g.bf16 ? 2 : 4;
+  g.m = c->n_branches;
+  g.d = c->d_model;
+  g.dk = c->d_k;
+  g.dv = c->d_v;
+  g.r = c->gate_rank;
+  g.rp = c->gate_rank <= 16 ? 16 : 64;
+  g.C = c->chunk;
+  g.carrier = -1;
+  if (g.m > 1)
+    for (int i = 0; i < g.m; ++i)
+      if (c->scale[i] == 1) {
+        g.carrier = i;
+        break;
+      }
+  const int e128 = 128 / g.es;
+  size_t cur = 0;
+  int ko = 0;
+  for (int i = 0; i < g.m; ++i) {
+    BranchGeom& b = g.br[i];
+    b.s = c->scale[i];
+    b.h = c->heads[i];
+    b.col_k = b.h * g.dk;
+    b.col_v = 2 * b.h * g.dk;
+    b.col_g = b.col_v + b.h * g.dv;
+    b.col_z = (i == g.carrier) ? b.col_g + g.rp : -1;
+    b.N = b.col_g + g.rp + ((i == g.carrier) ? 16 : 0);
+    b.off_Wp = cur;
+    cur += align256((size_t)b.N * g.d * g.es);
+    b.off_W2 = cur;
+    cur += align256((size_t)g.rp * b.h * g.dk * 4);
+    b.off_bg = cur;
+    cur += align256((size_t)b.h * g.dk * 4);
+    b.ko = ko;
+    b.kp = cdiv(b.h * g.dv, e128) * e128;
+    ko += b.kp;
+  }
+  g.Ktot = ko;
+  g.has_Wz = g.m > 1 && g.carrier < 0;
+  g.off_Wz = cur;
+  if (g.has_Wz) cur += align256((size_t)16 * g.d * g.es);
+  g.off_bf = cur;
+  cur += 256;
+  g.off_WoT = cur;
+  cur += align256((size_t)g.d * g.Ktot * g.es);
+  g.total = cur;
+  return g;
+}
+
+// forward workspace
+struct WsBranch {
+  int n, nch, np;
+  size_t q, k, qt, kT, vT, g, A, lam, y;
+};
+struct WsGeom {
+  WsBranch br[MSGLA_MAX_BRANCHES];
+  size_t w, total;
+};
+
+WsGeom ws_geom(const PackGeom& g, int64_t B, int64_t L) {
+  WsGeom w{};
+  size_t cur = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = cur;
+    cur += align256(bytes);
+    return o;
+  };
+  for (int i = 0; i < g.m; ++i) {
+    const BranchGeom& bg = g.br[i];
+    WsBranch& b = w.br[i];
+    b.n = (int)(L / bg.s);
+    b.nch = cdiv(b.n, g.C);
+    b.np = b.nch * g.C;
+    const size_t rows = (size_t)B * bg.h * b.np;
+    b.q = take(rows * g.dk * 4);
+    b.k = take(rows * g.dk * 4);
+    b.qt = take(rows * g.dk * g.es);
+    b.kT = take(rows * g.dk * g.es);
+    b.vT = take(rows * g.dv * g.es);
+    b.g = take((size_t)B * b.np * g.rp * 4);
+    b.A = take(rows * g.C * g.es);
+    b.lam = take((size_t)B * bg.h * b.nch * g.dk * 4);
+    b.y = take(rows * g.dv * g.es);
+  }
+  w.w = take((size_t)B * L * FUSION_STRIDE * 4);
+  w.total = cur;
+  return w;
+}
+
+struct StGeom {
+  size_t S[MSGLA_MAX_BRANCHES], psum[MSGLA_MAX_BRANCHES], held[MSGLA_MAX_BRANCHES];
+  size_t total;
+};
+
+StGeom st_geom(const PackGeom& g, int64_t B) {
+  StGeom s{};
+  size_t cur = STATE_HEADER;
+  for (int i = 0; i < g.m; ++i) {
+    s.S[i] = cur;
+    cur += align256((size_t)B * g.br[i].h * g.dk * g.dv * 4);
+    s.psum[i] = cur;
+    cur += align256((size_t)B * g.d * 4);
+    s.held[i] = cur;
+    cur += align256((size_t)B * g.d * 4);
+  }
+  s.total = cur;
+  return s;
+}
+
+struct DecGeom {
+  size_t xp[MSGLA_MAX_BRANCHES], proj[MSGLA_MAX_BRANCHES], y[MSGLA_MAX_BRANCHES];
+  size_t w, pos, total;
+};
+
+DecGeom dec_geom(const PackGeom& g, int64_t B) {
+  DecGeom d{};
+  size_t cur = 0;
+  for (int i = 0; i < g.m; ++i) {
+    d.xp[i] = cur;
+    cur += align256((size_t)B * g.d * 4);
+    d.proj[i] = cur;
+    cur += align256((size_t)B * g.br[i].N * 4);
+    d.y[i] = cur;
+    cur += align256((size_t)B * g.br[i].h * g.dv * 4);
+  }
+  d.w = cur;
+  cur += align256((size_t)B * FUSION_STRIDE * 4);
+  d.pos = cur;
+  cur += 256;
+  d.total = cur;
+  return d;
+}
+
+template <typename P> P* at(void* base, size_t off) {
+  return reinterpret_cast<P*>(static_cast<char*>(base) + off);
+}
+template <typename P> const P* at(const void* base, size_t off) {
+  return reinterpret_cast<const P*>(static_cast<const char*>(base) + off);
+}
+
+#define HIP_TRY(expr)                               \
+  do {                                              \
+    if ((expr) != hipSuccess) return MSGLA_ERR_HIP; \
+  } while (0)
+
+bool batch_ok(int64_t B, int64_t L) {
+  return B >= 1 && L >= 1 && B <= (1 << 20) && L <= (1 << 24) && B * L <= ((int64_t)1 << 31) / 8;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* msgla_status_str(msgla_status s) {
+  switch (s) {
+    case MSGLA_OK: return "ok";
+    case MSGLA_ERR_INVALID_ARG: return "invalid argument";
+    case MSGLA_ERR_UNSUPPORTED: return "unsupported";
+    case MSGLA_ERR_WORKSPACE: return "workspace or buffer too small";
+    case MSGLA_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+msgla_status msgla_validate_config(const msgla_config* cfg) { return check_config(cfg); }
+
+size_t msgla_packed_weights_bytes(const msgla_config* cfg) {
+  if (check_config(cfg) != MSGLA_OK) return 0;
+  return pack_geom(cfg).total;
+}
+
+size_t msgla_workspace_bytes(const msgla_config* cfg, int64_t B, int64_t L) {
+  if (check_config(cfg) != MSGLA_OK || !batch_ok(B, L)) return 0;
+  return ws_geom(pack_geom(cfg), B, L).total;
+}
+
+size_t msgla_state_bytes(const msgla_config* cfg, int64_t B) {
+  if (check_config(cfg) != MSGLA_OK || !batch_ok(B, 1)) return 0;
+  return st_geom(pack_geom(cfg), B).total;
+}
+
+size_t msgla_decode_workspace_bytes(const msgla_config* cfg, int64_t B) {
+  if (check_config(cfg) != MSGLA_OK || !batch_ok(B, 1)) return 0;
+  return dec_geom(pack_geom(cfg), B).total;
+}
+
+msgla_status msgla_pack_weights(const msgla_config* cfg, const msgla_weights* w, void* packed,
+                                size_t packed_bytes, void* stream) {
+  if (msgla_status st = check_config(cfg); st != MSGLA_OK) return st;
+  if (!w || !packed || !aligned16(packed)) return MSGLA_ERR_INVALID_ARG;
+  const PackGeom g = pack_geom(cfg);
+  if (packed_bytes < g.total) return MSGLA_ERR_WORKSPACE;
+  for (int i = 0; i < g.m; ++i) {
+    const msgla_branch_weights& b = w->br[i];
+    if (!b.W_q || !b.W_k || !b.W_v || !b.W_g1 || !b.W_g2 || !b.b_g || !b.W_o)
+      return MSGLA_ERR_INVALID_ARG;
+  }
+  if (g.m > 1 && (!w->W_f || !w->b_f)) return MSGLA_ERR_INVALID_ARG;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  HIP_TRY(fill_zero(packed, g.total, st));
+  for (int i = 0; i < g.m; ++i) {
+    const BranchGeom& b = g.br[i];
+    const msgla_branch_weights& s = w->br[i];
+    void* Wp = at<char>(packed, b.off_Wp);
+    const size_t rowb = (size_t)g.d * g.es;
+    HIP_TRY(pack_transpose(g.bf16, s.W_q, g.d, b.h * g.dk, Wp, g.d, st));
+    HIP_TRY(pack_transpose(g.bf16, s.W_k, g.d, b.h * g.dk, at<char>(Wp, b.col_k * rowb), g.d, st));
+    HIP_TRY(pack_transpose(g.bf16, s.W_v, g.d, b.h * g.dv, at<char>(Wp, b.col_v * rowb), g.d, st));
+    HIP_TRY(pack_transpose(g.bf16, s.W_g1, g.d, g.r, at<char>(Wp, b.col_g * rowb), g.d, st));
+    if (b.col_z >= 0)
+      HIP_TRY(pack_transpose(g.bf16, w->W_f, g.d, g.m, at<char>(Wp, b.col_z * rowb), g.d, st));
+    HIP_TRY(pack_to_f32(g.bf16, s.W_g2, (size_t)g.r * b.h * g.dk, at<float>(packed, b.off_W2), st));
+    HIP_TRY(hipMemcpyAsync(at<char>(packed, b.off_bg), s.b_g, (size_t)b.h * g.dk * 4,
+                           hipMemcpyDeviceToDevice, st));
+    // W_o [h dv][d] -> WoT[n][ko + k]
+    HIP_TRY(pack_transpose(g.bf16, s.W_o, b.h * g.dv, g.d, at<char>(packed, g.off_WoT + (size_t)b.ko * g.es),
+                           g.Ktot, st));
+  }
+  if (g.has_Wz) HIP_TRY(pack_transpose(g.bf16, w->W_f, g.d, g.m, at<char>(packed, g.off_Wz), g.d, st));
+  if (g.m > 1)
+    HIP_TRY(hipMemcpyAsync(at<char>(packed, g.off_bf), w->b_f, (size_t)g.m * 4,
+                           hipMemcpyDeviceToDevice, st));
+  return MSGLA_OK;
+}
+
+msgla_status msgla_state_init(const msgla_config* cfg, int64_t B, void* state, size_t state_bytes,
+                              void* stream) {
+  if (msgla_status st = check_config(cfg); st != MSGLA_OK) return st;
+  if (!batch_ok(B, 1) || !state || !aligned16(state)) return MSGLA_ERR_INVALID_ARG;
+  const PackGeom g = pack_geom(cfg);
+  const StGeom s = st_geom(g, B);
+  if (state_bytes < s.total) return MSGLA_ERR_WORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  HIP_TRY(fill_zero(state, s.total, st));
+  HIP_TRY(launch_state_header(state, (int)B, g.m, 0, st));
+  return MSGLA_OK;
+}
+
+msgla_status msgla_forward_timed(const msgla_config* cfg, const void* packed, const void* x,
+                                 const uint8_t* mask, int64_t B, int64_t L, void* out,
+                                 const void* state_in, void* state_out, void* workspace,
+                                 size_t workspace_bytes, void* stream,
+                                 const msgla_stage_events* events) {
+  if (msgla_status st = check_config(cfg); st != MSGLA_OK) return st;
+  if (!batch_ok(B, L)) return MSGLA_ERR_INVALID_ARG;
+  if (!packed || !x || !out || !workspace) return MSGLA_ERR_INVALID_ARG;
+  if (!aligned16(packed) || !aligned16(x) || !aligned16(out) || !aligned16(workspace) ||
+      (state_out && !aligned16(state_out)))
+    return MSGLA_ERR_INVALID_ARG;
+  if (mask || state_in) return MSGLA_ERR_UNSUPPORTED;
+  const PackGeom g = pack_geom(cfg);
+  const WsGeom W = ws_geom(g, B, L);
+  if (workspace_bytes < W.total) return MSGLA_ERR_WORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const StGeom S = st_geom(g, B);
+
+  auto ev = [&](int stage, bool start) -> hipError_t {
+    if (!events) return hipSuccess;
+    void* e = start ? events->start[stage] : events->stop[stage];
+    return e ? hipEventRecord(static_cast<hipEvent_t>(e), st) : hipSuccess;
+  };
+
+  // ---------------- K1 ----------------
+  K1Params p1{};
+  p1.x = x;
+  p1.B = (int)B;
+  p1.L = (int)L;
+  p1.d = g.d;
+  p1.dk = g.dk;
+  p1.dv = g.dv;
+  p1.rp = g.rp;
+  p1.C = g.C;
+  p1.m = g.m;
+  p1.bf = at<float>(packed, g.off_bf);
+  p1.w = at<float>(workspace, W.w);
+  int tiles = 0, ng = 0;
+  for (int i = 0; i < g.m; ++i) {
+    const BranchGeom& b = g.br[i];
+    const WsBranch& wb = W.br[i];
+    if (wb.n == 0) continue;
+    K1Group& G = p1.g[ng++];
+    G.Wp = at<char>(packed, b.off_Wp);
+    G.s = b.s;
+    G.n = wb.n;
+    G.M = (int)B * wb.n;
+    G.N = b.N;
+    G.tiles_n = cdiv(b.N, GEMM_TILE);
+    G.tile_begin = tiles;
+    tiles += cdiv(G.M, GEMM_TILE) * G.tiles_n;
+    G.h = b.h;
+    G.col_k = b.col_k;
+    G.col_v = b.col_v;
+    G.col_g = b.col_g;
+    G.col_z = b.col_z;
+    G.col_end = b.N;
+    G.np = wb.np;
+    G.nch = wb.nch;
+    G.q = at<float>(workspace, wb.q);
+    G.k = at<float>(workspace, wb.k);
+    G.vT = at<char>(workspace, wb.vT);
+    G.g = at<float>(workspace, wb.g);
+  }
+  if (g.has_Wz) {
+    K1Group& G = p1.g[ng++];
+    G.Wp = at<char>(packed, g.off_Wz);
+    G.s = 1;
+    G.n = (int)L;
+    G.M = (int)(B * L);
+    G.N = 16;
+    G.tiles_n = 1;
+    G.tile_begin = tiles;
+    tiles += cdiv(G.M, GEMM_TILE);
+    G.h = 0;
+    G.col_k = G.col_v = G.col_g = 0;
+    G.col_z = 0;
+    G.col_end = 16;
+  }
+  p1.ngroups = ng;
+  p1.total_tiles = tiles;
+  p1.per_xcd = cdiv(tiles, N_XCD);
+
+  // ---------------- K2 ----------------
+  K2Params p2{};
+  p2.B = (int)B;
+  p2.dk = g.dk;
+  p2.dv = g.dv;
+  p2.r = g.r;
+  p2.rp = g.rp;
+  p2.C = g.C;
+  p2.inv_gamma = 1.0f / cfg->gate_normalizer;
+  p2.q_scale = cfg->q_scale;
+  p2.nbranch = g.m;
+  int units = 0;
+  for (int i = 0; i < g.m; ++i) {
+    const BranchGeom& b = g.br[i];
+    const WsBranch& wb = W.br[i];
+    K2Branch& k = p2.br[i];
+    k.h = b.h;
+    k.n = wb.n;
+    k.nch = wb.nch;
+    k.np = wb.np;
+    k.unit_begin = units;
+    units += (int)B * b.h * wb.nch;
+    k.q = at<float>(workspace, wb.q);
+    k.k = at<float>(workspace, wb.k);
+    k.g = at<float>(workspace, wb.g);
+    k.W2 = at<float>(packed, b.off_W2);
+    k.bg = at<float>(packed, b.off_bg);
+    k.qt = at<char>(workspace, wb.qt);
+    k.kT = at<char>(workspace, wb.kT);
+    k.vT = at<char>(workspace, wb.vT);
+    k.A = at<char>(workspace, wb.A);
+    k.lam = at<float>(workspace, wb.lam);
+    k.y = at<char>(workspace, wb.y);
+    k.S_out = state_out ? at<float>(state_out, S.S[i]) : nullptr;
+  }
+  p2.total_units = units;
+  // K2b: sequences ordered by decreasing chunk count (longest walks start first)
+  int order[MSGLA_MAX_BRANCHES];
+  for (int i = 0; i < g.m; ++i) order[i] = i;
+  std::stable_sort(order, order + g.m, [&](int a, int b) { return W.br[a].nch > W.br[b].nch; });
+  int seqs = 0;
+  for (int o = 0; o < g.m; ++o) {
+    p2.order[o] = order[o];
+    p2.br[order[o]].seq_begin = seqs;
+    seqs += (int)B * g.br[order[o]].h;
+  }
+  p2.total_seqs = seqs;
+  p2.n_dvt = g.dv / k2b_dvt();
+
+  // ---------------- K3 ----------------
+  K3Params p3{};
+  p3.B = (int)B;
+  p3.L = (int)L;
+  p3.d = g.d;
+  p3.dv = g.dv;
+  p3.m = g.m;
+  p3.Ktot = g.Ktot;
+  p3.tiles_n = cdiv(g.d, GEMM_TILE);
+  p3.total_tiles = cdiv((int)(B * L), GEMM_TILE) * p3.tiles_n;
+  p3.per_xcd = cdiv(p3.total_tiles, N_XCD);
+  p3.WoT = at<char>(packed, g.off_WoT);
+  p3.w = at<float>(workspace, W.w);
+  p3.out = out;
+  for (int i = 0; i < g.m; ++i) {
+    K3Branch& k = p3.br[i];
+    k.y = at<char>(workspace, W.br[i].y);
+    k.s = g.br[i].s;
+    k.h = g.br[i].h;
+    k.np = W.br[i].np;
+    k.n = W.br[i].n;
+    k.ko = g.br[i].ko;
+    k.kp = g.br[i].kp;
+  }
+
+  HIP_TRY(ev(0, true));
+  if (p1.total_tiles > 0) HIP_TRY(launch_k1(p1, g.bf16, st));
+  HIP_TRY(ev(0, false));
+  HIP_TRY(ev(1, true));
+  if (p2.total_units > 0) HIP_TRY(launch_k2a(p2, g.bf16, st));
+  HIP_TRY(ev(1, false));
+  HIP_TRY(ev(2, true));
+  if (p2.total_seqs > 0) HIP_TRY(launch_k2b(p2, g.bf16, st));
+  HIP_TRY(ev(2, false));
+  HIP_TRY(ev(3, true));
+  HIP_TRY(launch_k3(p3, g.bf16, st));
+  HIP_TRY(ev(3, false));
+
+  if (state_out) {
+    StateParams ps{};
+    ps.B = (int)B;
+    ps.L = (int)L;
+    ps.d = g.d;
+    ps.dk = g.dk;
+    ps.dv = g.dv;
+    ps.m = g.m;
+    ps.Ktot = g.Ktot;
+    ps.pos = L;
+    ps.x = x;
+    ps.WoT = p3.WoT;
+    ps.state = state_out;
+    for (int i = 0; i < g.m; ++i) {
+      StateBranch& b = ps.br[i];
+      b.s = g.br[i].s;
+      b.h = g.br[i].h;
+      b.n = W.br[i].n;
+      b.np = W.br[i].np;
+      b.ko = g.br[i].ko;
+      b.S = at<float>(state_out, S.S[i]);
+      b.psum = at<float>(state_out, S.psum[i]);
+      b.held = at<float>(state_out, S.held[i]);
+      b.y = at<char>(workspace, W.br[i].y);
+    }
+    HIP_TRY(launch_state_export(ps, g.bf16, st));
+  }
+  return MSGLA_OK;
+}
+
+msgla_status msgla_forward(const msgla_config* cfg, const void* packed, const void* x,
+                           const uint8_t* mask, int64_t B, int64_t L, void* out,
+                           const void* state_in, void* state_out, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  return msgla_forward_timed(cfg, packed, x, mask, B, L, out, state_in, state_out, workspace,
+                             workspace_bytes, stream, nullptr);
+}
+
+msgla_status msgla_decode_step(const msgla_config* cfg, const void* packed, const void* x_t,
+                               int64_t B, void* state, void* out_t, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  if (msgla_status st = check_config(cfg); st != MSGLA_OK) return st;
+  if (!batch_ok(B, 1) || !packed || !x_t || !state || !out_t || !workspace)
+    return MSGLA_ERR_INVALID_ARG;
+  if (!aligned16(packed) || !aligned16(x_t) || !aligned16(state) || !aligned16(out_t) ||
+      !aligned16(workspace))
+    return MSGLA_ERR_INVALID_ARG;
+  const PackGeom g = pack_geom(cfg);
+  const DecGeom D = dec_geom(g, B);
+  if (workspace_bytes < D.total) return MSGLA_ERR_WORKSPACE;
+  const StGeom S = st_geom(g, B);
+  DecParams p{};
+  p.B = (int)B;
+  p.d = g.d;
+  p.dk = g.dk;
+  p.dv = g.dv;
+  p.r = g.r;
+  p.m = g.m;
+  p.Ktot = g.Ktot;
+  p.inv_gamma = 1.0f / cfg->gate_normalizer;
+  p.q_scale = cfg->q_scale;
+  p.x = x_t;
+  p.out = out_t;
+  p.state = state;
+  p.pos_ws = at<int64_t>(workspace, D.pos);
+  p.w = at<float>(workspace, D.w);
+  p.bf = at<float>(packed, g.off_bf);
+  p.WoT = at<char>(packed, g.off_WoT);
+  if (g.has_Wz)
+    p.Wz = at<char>(packed, g.off_Wz);
+  else if (g.carrier >= 0)
+    p.Wz = at<char>(packed, g.br[g.carrier].off_Wp + (size_t)g.br[g.carrier].col_z * g.d * g.es);
+  else
+    p.Wz = nullptr;
+  p.nbranch = g.m;
+  int Nmax = 0, hmax = 0;
+  for (int i = 0; i < g.m; ++i) {
+    const BranchGeom& b = g.br[i];
+    DecBranch& k = p.br[i];
+    k.s = b.s;
+    k.h = b.h;
+    k.N = b.N;
+    k.col_k = b.col_k;
+    k.col_v = b.col_v;
+    k.col_g = b.col_g;
+    k.col_z = b.col_z;
+    k.ko = b.ko;
+    k.Wp = at<char>(packed, b.off_Wp);
+    k.W2 = at<float>(packed, b.off_W2);
+    k.bg = at<float>(packed, b.off_bg);
+    k.S = at<float>(state, S.S[i]);
+    k.psum = at<float>(state, S.psum[i]);
+    k.held = at<float>(state, S.held[i]);
+    k.xp = at<float>(workspace, D.xp[i]);
+    k.proj = at<float>(workspace, D.proj[i]);
+    k.y = at<float>(workspace, D.y[i]);
+    Nmax = std::max(Nmax, b.N);
+    hmax = std::max(hmax, b.h);
+  }
+  HIP_TRY(launch_decode(p, Nmax, hmax, g.bf16, static_cast<hipStream_t>(stream)));
+  return MSGLA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,74 @@
+// Streaming-state header and the end-of-forward export of the per-branch cache.
+//
+// MS-GLA notes, paragraph on token-by-token inference (the author's cache):
+// each branch keeps its GLA state, the not-yet-complete block of hidden
+// states and its most recent output.  After a forward over L tokens branch s
+// has consumed n = floor(L/s) blocks: its GLA state is written by the state
+// kernel directly; this kernel adds the sum of the L - n s pending tokens and
+// the held output Y_{n-1} = y_{n-1} W_o (zero when n = 0), and sets the token
+// count in the header.
+#include "device_common.hpp"
+#include "layout.hpp"
+
+namespace msgla {
+
+__global__ void k_state_header(void* state, int B, int m, int64_t pos) {
+  if (threadIdx.x == 0 && blockIdx.x == 0) {
+    StateHeader* h = reinterpret_cast<StateHeader*>(state);
+    h->magic = STATE_MAGIC;
+    h->version = STATE_VERSION;
+    h->B = B;
+    h->m = m;
+    h->pos = pos;
+  }
+}
+
+// grid: (ceil(d / 256), B, m)
+template <typename T>
+__global__ void k_state_export(const StateParams P) {
+  const int col = blockIdx.x * blockDim.x + threadIdx.x;
+  const int b = blockIdx.y, i = blockIdx.z;
+  const StateBranch& Br = P.br[i];
+  if (col < P.d) {
+    // pending tokens of the incomplete block
+    const T* x = reinterpret_cast<const T*>(P.x);
+    float s = 0.f;
+    for (int t = Br.n * Br.s; t < P.L; ++t) s += to_f32(x[((size_t)b * P.L + t) * P.d + col]);
+    Br.psum[(size_t)b * P.d + col] = s;
+    // held output of the last complete block
+    float acc = 0.f;
+    if (Br.n > 0) {
+      const T* y = reinterpret_cast<const T*>(Br.y);
+      const T* wo = reinterpret_cast<const T*>(P.WoT) + (size_t)col * P.Ktot + Br.ko;
+      for (int hh = 0; hh < Br.h; ++hh) {
+        const T* yr = y + (((size_t)b * Br.h + hh) * Br.np + (Br.n - 1)) * P.dv;
+        for (int v = 0; v < P.dv; ++v) acc = fmaf(to_f32(yr[v]), to_f32(wo[hh * P.dv + v]), acc);
+      }
+    }
+    Br.held[(size_t)b * P.d + col] = acc;
+  }
+  // a branch that saw no complete block keeps a zero GLA state
+  if (Br.n == 0) {
+    const size_t per_b = (size_t)Br.h * P.dk * P.dv;
+    for (size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x; e < per_b;
+         e += (size_t)gridDim.x * blockDim.x)
+      Br.S[(size_t)b * per_b + e] = 0.f;
+  }
+}
+
+hipError_t launch_state_header(void* state, int B, int m, int64_t pos, hipStream_t st) {
+  hipLaunchKernelGGL(k_state_header, dim3(1), dim3(64), 0, st, state, B, m, pos);
+  return hipGetLastError();
+}
+
+hipError_t launch_state_export(const StateParams& P, bool bf16_path, hipStream_t st) {
+  const dim3 grid((P.d + 255) / 256, P.B, P.m);
+  if (bf16_path)
+    hipLaunchKernelGGL(k_state_export<bf16>, grid, dim3(256), 0, st, P);
+  else
+    hipLaunchKernelGGL(k_state_export<float>, grid, dim3(256), 0, st, P);
+  if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+  return launch_state_header(P.state, P.B, P.m, P.pos, st);
+}
+
+}  // namespace msgla

@@ -1,0 +1,186 @@
+// Kernel parameter blocks and memory layouts shared by the host API and the
+// kernels.  Everything here is plain data passed to kernels by value.
+//
+// Memory layouts (T = storage type: bf16 or fp32; C = chunk length):
+//
+// Packed weights, per branch i (h heads, scale s):
+//   Wp_i  [Np_i][d]  T   rows = output columns of the pooled projection:
+//                        [ q: h d_k | k: h d_k | v: h d_v | g: rp | z: 16 if
+//                        this branch carries the fusion logits ]
+//                        (transposed so the GEMM reads both operands along d;
+//                        rp = 16 if r <= 16 else 64, unused rows are zero)
+//   W2_i  [rp][h d_k] fp32 (rows >= r zero),  bg_i [h d_k] fp32
+// then, if fusion logits need their own pass (m > 1 and no scale-1 branch),
+//   Wz [16][d] T (W_f^T, zero padded),
+// then bf [16] fp32 (fusion bias, zero padded) and
+//   WoT [d][Ktot] T   stacked W_o^T of all branches along K; branch i occupies
+//                     columns [ko_i, ko_i + kp_i), kp_i = h_i d_v rounded up to
+//                     a 128-byte multiple (zero padded).
+//
+// Forward workspace, per branch i (n = floor(L/s) pooled rows, nch = ceil(n/C),
+// np = nch C):
+//   q, k        [B][h][np][d_k]   fp32  projections (kept in fp32: the intra-chunk
+//                                       products q_t . k_i can cancel strongly)
+//   qt          [B][h][np][d_k]   T     q ⊙ exp(b) (chunk-local)
+//   kT          [B][h][nch][d_k][C] T   (k ⊙ exp(b_last - b))^T per chunk
+//   vT          [B][h][nch][d_v][C] T   v^T per chunk
+//   g           [B][np][rp]       fp32  first gate factor xp W_g1
+//   A           [B][h][nch][C][C] T     masked decayed q k^T per chunk
+//   lam         [B][h][nch][d_k]  fp32  exp(b_last) per chunk
+//   y           [B][h][np][d_v]   T     GLA outputs o_t
+// plus the fusion weights w [B L][8] fp32.  Rows >= n of a chunk are never
+// written by the projection and are masked by every reader.
+//
+// State (fp32 except the header): 256-byte header {magic, version, B, m, pos},
+// then per branch S [B][h][d_k][d_v], psum [B][d], held [B][d].
+#pragma once
+#include <stdint.h>
+#include <stddef.h>
+
+#ifndef MSGLA_MAX_BRANCHES
+#define MSGLA_MAX_BRANCHES 8
+#endif
+
+namespace msgla {
+
+constexpr uint32_t STATE_MAGIC = 0x4C47534Du;  // "MSGL"
+constexpr uint32_t STATE_VERSION = 1;
+constexpr size_t STATE_HEADER = 256;
+constexpr int FUSION_STRIDE = 8;  // floats per row of the fusion-weight buffer
+constexpr int N_XCD = 8;          // XCDs (separate L2 caches) of an MI355X
+
+struct StateHeader {
+  uint32_t magic;
+  uint32_t version;
+  int32_t B;
+  int32_t m;
+  int64_t pos;
+};
+
+// ---------------- K1: pooled projection GEMM (+ fusion logits) ----------------
+struct K1Group {
+  const void* Wp;   // [N][d]
+  int s;            // pooling factor (1 for the fusion-only group)
+  int n;            // pooled rows per sequence
+  int M;            // B * n
+  int N;            // GEMM columns (multiple of 16)
+  int tiles_n;      // ceil(N / BN)
+  int tile_begin;   // first flattened tile of this group
+  int h;            // heads (0 for the fusion-only group)
+  int col_k, col_v, col_g, col_z, col_end;  // column ranges; col_q = 0; col_z < 0: none
+  int np, nch;      // padded rows and chunks per (b, head)
+  float* q;         // outputs (see layout)
+  float* k;
+  void* vT;
+  float* g;
+};
+
+struct K1Params {
+  const void* x;    // [B][L][d]
+  int B, L, d, dk, dv, rp, C, m;
+  int ngroups, total_tiles, per_xcd;
+  const float* bf;  // fusion bias [16]
+  float* w;         // fusion weights [B L][8]
+  K1Group g[MSGLA_MAX_BRANCHES + 1];
+};
+
+// ---------------- K2a: chunk-local gate, decay and intra-chunk matrix ----------
+struct K2Branch {
+  int h, n, nch, np;
+  int unit_begin;   // first flattened (b, head, chunk) unit of this branch (K2a)
+  int seq_begin;    // first flattened (b, head) sequence of this branch (K2b)
+  const float* q;
+  const float* k;
+  const float* g;
+  const float* W2;  // [rp][h dk], rows >= r are zero
+  const float* bg;  // [h dk]
+  void* qt;
+  void* kT;
+  const void* vT;
+  void* A;
+  float* lam;
+  void* y;
+  float* S_out;     // state S of this branch [B][h][dk][dv] or null
+};
+
+struct K2Params {
+  int B, dk, dv, r, rp, C;
+  float inv_gamma;
+  float q_scale;
+  int nbranch;
+  int total_units;  // K2a grid
+  int total_seqs;   // K2b: number of (branch, b, head) sequences
+  int n_dvt;        // K2b: d_v tiles per sequence
+  int per_xcd;      // K2b block remap
+  int order[MSGLA_MAX_BRANCHES];  // K2b: branches by decreasing chunk count
+  K2Branch br[MSGLA_MAX_BRANCHES];
+};
+
+// ---------------- K3: hold + fusion + stacked output projection GEMM ----------
+struct K3Branch {
+  const void* y;    // [B][h][np][dv]
+  int s, h, np, n;
+  int ko, kp;       // K offset / padded K range in the stacked W_o^T
+};
+
+struct K3Params {
+  int B, L, d, dv, m, Ktot;
+  int total_tiles, tiles_n, per_xcd;
+  const void* WoT;  // [d][Ktot]
+  const float* w;   // fusion weights [B L][8]
+  void* out;        // [B][L][d]
+  K3Branch br[MSGLA_MAX_BRANCHES];
+};
+
+// ---------------- packing ------------------------------------------------------
+struct PackSrc {
+  const void* W_q; const void* W_k; const void* W_v; const void* W_g1; const void* W_g2;
+  const float* b_g; const void* W_o;
+};
+
+// ---------------- state export / init ------------------------------------------
+struct StateBranch {
+  int s, h, n, np, ko;
+  float* S; float* psum; float* held;
+  const void* y;    // forward workspace y (export only)
+};
+
+struct StateParams {
+  int B, L, d, dk, dv, m, Ktot;
+  int64_t pos;
+  const void* x;    // forward input (export only)
+  const void* WoT;
+  void* state;      // header
+  StateBranch br[MSGLA_MAX_BRANCHES];
+};
+
+// ---------------- decode ---------------------------------------------------------
+struct DecBranch {
+  int s, h, N, col_k, col_v, col_g, col_z, ko;
+  const void* Wp;   // [N][d]
+  const float* W2;
+  const float* bg;
+  float* S;         // state [B][h][dk][dv]
+  float* psum;      // [B][d]
+  float* held;      // [B][d]
+  float* xp;        // workspace [B][d]: pooled block of this step
+  float* proj;      // workspace [B][N]
+  float* y;         // workspace [B][h dv]
+};
+
+struct DecParams {
+  int B, d, dk, dv, r, m, Ktot;
+  float inv_gamma, q_scale;
+  const void* x;    // [B][d]
+  void* out;        // [B][d]
+  void* state;      // header (pos)
+  int64_t* pos_ws;  // workspace copy of pos for this step
+  float* w;         // fusion weights [B][8]
+  const void* Wz;   // fusion-logit weights W_f^T [m][d] (inside a branch's Wp or separate)
+  const float* bf;
+  const void* WoT;
+  int nbranch;
+  DecBranch br[MSGLA_MAX_BRANCHES];
+};
+
+}  // namespace msgla

@@ -1,0 +1,136 @@
+"""Device-memory plumbing around the C ABI: uploads synthetic inputs and
+weights with torch, packs the weights once, owns the workspace, and calls the
+binding.  No arithmetic of the layer happens here."""
+from __future__ import annotations
+
+from typing import Optional
+
+import numpy as np
+
+from . import binding
+from .config import BF16, MsglaConfig
+from .synth import LayerWeights, storage_array
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def to_device(a: np.ndarray, dtype: str, device="cuda"):
+    """Host float64 array (already rounded) -> device tensor in the storage type."""
+    torch = _torch()
+    host = storage_array(a, dtype)
+    if dtype == BF16:
+        t = torch.from_numpy(host.view(np.int16).copy()).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(host.copy())
+    return t.to(device)
+
+
+def to_device_f32(a: np.ndarray, device="cuda"):
+    torch = _torch()
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device)
+
+
+def from_device(t) -> np.ndarray:
+    torch = _torch()
+    return t.detach().to("cpu", torch.float32).numpy().astype(np.float64)
+
+
+def empty_bytes(n: int, device="cuda"):
+    torch = _torch()
+    return torch.empty(max(int(n), 16), dtype=torch.uint8, device=device)
+
+
+class DeviceLayer:
+    """Packed weights + workspace for one configuration on one device."""
+
+    def __init__(self, cfg: MsglaConfig, W: LayerWeights, device="cuda", stream=None):
+        torch = _torch()
+        self.cfg, self.device, self.stream = cfg, device, stream
+        dt = cfg.dtype
+        self._src = []
+        for bw in W.branches:
+            self._src.append({
+                "W_q": to_device(bw.W_q, dt, device), "W_k": to_device(bw.W_k, dt, device),
+                "W_v": to_device(bw.W_v, dt, device), "W_g1": to_device(bw.W_g1, dt, device),
+                "W_g2": to_device(bw.W_g2, dt, device), "b_g": to_device_f32(bw.b_g, device),
+                "W_o": to_device(bw.W_o, dt, device)})
+        m = len(cfg.scales)
+        self._W_f = to_device(W.W_f, dt, device) if m > 1 else None
+        self._b_f = to_device_f32(W.b_f, device) if m > 1 else None
+        nbytes = binding.msgla_packed_weights_bytes(cfg)
+        if nbytes == 0:
+            raise ValueError("invalid configuration for the library")
+        self.packed = empty_bytes(nbytes, device)
+        binding.msgla_pack_weights(cfg, self._src, self._W_f, self._b_f, self.packed, stream)
+        torch.cuda.synchronize()
+        self._src = None  # the packed blob is all the kernels read
+        self._W_f = self._b_f = None
+        self.workspace = None
+        self.dec_workspace = None
+
+    def ensure_workspace(self, B: int, L: int):
+        n = binding.msgla_workspace_bytes(self.cfg, B, L)
+        if n == 0:
+            raise ValueError(f"invalid batch/length B={B} L={L}")
+        if self.workspace is None or self.workspace.numel() < n:
+            self.workspace = empty_bytes(n, self.device)
+        return self.workspace
+
+    def new_output(self, B: int, L: int):
+        torch = _torch()
+        dt = torch.bfloat16 if self.cfg.dtype == BF16 else torch.float32
+        return torch.empty((B, L, self.cfg.d_model), dtype=dt, device=self.device)
+
+    def new_state(self, B: int):
+        return empty_bytes(binding.msgla_state_bytes(self.cfg, B), self.device)
+
+    def forward(self, x, out=None, state_out=None, events=None):
+        B, L, _ = x.shape
+        ws = self.ensure_workspace(B, L)
+        if out is None:
+            out = self.new_output(B, L)
+        binding.msgla_forward(self.cfg, self.packed, x, B, L, out, ws, state_out=state_out,
+                              stream=self.stream, events=events)
+        return out
+
+    def state_init(self, state, B: int):
+        binding.msgla_state_init(self.cfg, B, state, self.stream)
+
+    def decode_step(self, x_t, state, out_t=None):
+        torch = _torch()
+        B = x_t.shape[0]
+        n = binding.msgla_decode_workspace_bytes(self.cfg, B)
+        if self.dec_workspace is None or self.dec_workspace.numel() < n:
+            self.dec_workspace = empty_bytes(n, self.device)
+        if out_t is None:
+            dt = torch.bfloat16 if self.cfg.dtype == BF16 else torch.float32
+            out_t = torch.empty((B, self.cfg.d_model), dtype=dt, device=self.device)
+        binding.msgla_decode_step(self.cfg, self.packed, x_t, B, state, out_t, self.dec_workspace,
+                                  self.stream)
+        return out_t
+
+
+def read_state(cfg: MsglaConfig, state, B: int) -> dict:
+    """Decode a state blob (device tensor) into numpy arrays, mirroring the
+    layout documented in include/msgla.h (header + per-branch S, psum, held)."""
+    raw = state.detach().cpu().numpy()
+    hdr = raw[:24].view(np.int32)
+    pos = int(raw[16:24].view(np.int64)[0])
+    cur = 256
+    align = lambda x: (x + 255) & ~255
+    out = {"magic": int(hdr[0]) & 0xffffffff, "version": int(hdr[1]), "B": int(hdr[2]),
+           "m": int(hdr[3]), "pos": pos, "branches": []}
+    for h in cfg.heads:
+        nS = B * h * cfg.d_k * cfg.d_v
+        S = raw[cur: cur + 4 * nS].view(np.float32).reshape(B, h, cfg.d_k, cfg.d_v)
+        cur += align(4 * nS)
+        psum = raw[cur: cur + 4 * B * cfg.d_model].view(np.float32).reshape(B, cfg.d_model)
+        cur += align(4 * B * cfg.d_model)
+        held = raw[cur: cur + 4 * B * cfg.d_model].view(np.float32).reshape(B, cfg.d_model)
+        cur += align(4 * B * cfg.d_model)
+        out["branches"].append({"S": S.astype(np.float64), "psum": psum.astype(np.float64),
+                                "held": held.astype(np.float64)})
+    return out

@@ -1,0 +1,142 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every entry point include/msgla.h declares, and validates its arguments
+before enqueueing anything."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from scale_gla_layer_amd import binding
+from scale_gla_layer_amd.config import MsglaConfig, F32, BF16, WORKLOADS
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_symbols():
+    with open(os.path.join(ROOT, "include", "msgla.h"), encoding="utf-8") as f:
+        text = f.read()
+    return sorted(set(re.findall(r"\b(msgla_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = binding.load_library()
+    declared = _declared_symbols()
+    assert declared, "no declarations found"
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert set(declared) == set(binding.SYMBOLS)
+
+
+def test_status_strings():
+    lib = binding.load_library()
+    for code in range(5):
+        assert lib.msgla_status_str(code)
+    assert lib.msgla_status_str(99) == b"unknown status"
+
+
+@pytest.mark.parametrize("name", sorted(WORKLOADS))
+def test_workload_configs_are_valid(name):
+    wl = WORKLOADS[name]
+    assert binding.msgla_validate_config(wl.cfg) == 0
+    assert binding.msgla_packed_weights_bytes(wl.cfg) > 0
+    assert binding.msgla_workspace_bytes(wl.cfg, wl.batch, wl.seq_len) > 0
+
+
+def test_state_bytes_hold_the_recurrent_budget():
+    """Per sequence the blob holds sum_s h_s d_k d_v fp32 state elements (131,072 at d=1024, H=4)."""
+    cfg = WORKLOADS["main"].cfg
+    for B in (1, 3, 16):
+        n = binding.msgla_state_bytes(cfg, B)
+        assert n >= 4 * B * 131072
+        assert n - 4 * B * 131072 < 4 * B * 3 * 2 * cfg.d_model + 4096
+
+
+def _cfg(**kw):
+    base = dict(scales=(1, 2, 4), heads=(2, 1, 1), d_model=128, d_k=32, d_v=64, gate_rank=16,
+                chunk=64, gate_normalizer=16.0, q_scale=1.0, dtype=BF16)
+    base.update(kw)
+    return base
+
+
+def _raw_cfg(**kw):
+    c = _cfg(**kw)
+    cc = binding.CConfig()
+    cc.n_branches = len(c["scales"])
+    for i, (s, h) in enumerate(zip(c["scales"], c["heads"])):
+        cc.scale[i], cc.heads[i] = s, h
+    cc.d_model, cc.d_k, cc.d_v = c["d_model"], c["d_k"], c["d_v"]
+    cc.gate_rank, cc.chunk = c["gate_rank"], c["chunk"]
+    cc.gate_normalizer, cc.q_scale = c["gate_normalizer"], c["q_scale"]
+    cc.dtype = 1 if c["dtype"] == BF16 else 0
+    return cc
+
+
+@pytest.mark.parametrize("bad", [
+    dict(scales=(1, 1), heads=(1, 1)),            # duplicate scale
+    dict(scales=(0, 2), heads=(1, 1)),            # non-positive scale
+    dict(scales=(1, 2), heads=(1, 0)),            # non-positive heads
+    dict(d_model=96),                             # not a multiple of 64
+    dict(d_k=48),                                 # bf16 needs d_k % 32 == 0
+    dict(d_v=48),                                 # d_v % 32
+    dict(gate_rank=0),
+    dict(gate_rank=65),
+    dict(chunk=16),                               # bf16 chunk must be 32 or 64
+    dict(chunk=48, dtype=F32),
+    dict(gate_normalizer=0.0),
+])
+def test_invalid_configs_are_rejected(bad):
+    lib = binding.load_library()
+    cc = _raw_cfg(**bad)
+    assert lib.msgla_validate_config(ctypes.byref(cc)) == 1
+    assert lib.msgla_packed_weights_bytes(ctypes.byref(cc)) == 0
+    assert lib.msgla_workspace_bytes(ctypes.byref(cc), 1, 8) == 0
+
+
+def test_too_many_branches_rejected():
+    lib = binding.load_library()
+    cc = _raw_cfg()
+    cc.n_branches = 9
+    assert lib.msgla_validate_config(ctypes.byref(cc)) == 1
+    cc.n_branches = 0
+    assert lib.msgla_validate_config(ctypes.byref(cc)) == 1
+
+
+def test_forward_argument_errors_need_no_gpu():
+    """Argument errors are returned before any HIP call (fake aligned pointers)."""
+    lib = binding.load_library()
+    cc = _raw_cfg()
+    fake = 1 << 20
+    ws = lib.msgla_workspace_bytes(ctypes.byref(cc), 2, 64)
+    f = lib.msgla_forward
+    # NULL input
+    assert f(ctypes.byref(cc), fake, None, None, 2, 64, fake, None, None, fake, ws, None) == 1
+    # misaligned output
+    assert f(ctypes.byref(cc), fake, fake, None, 2, 64, fake + 2, None, None, fake, ws, None) == 1
+    # bad sizes
+    assert f(ctypes.byref(cc), fake, fake, None, 0, 64, fake, None, None, fake, ws, None) == 1
+    assert f(ctypes.byref(cc), fake, fake, None, 2, 0, fake, None, None, fake, ws, None) == 1
+    # mask / state_in are not implemented
+    assert f(ctypes.byref(cc), fake, fake, fake, 2, 64, fake, None, None, fake, ws, None) == 2
+    assert f(ctypes.byref(cc), fake, fake, None, 2, 64, fake, fake, None, fake, ws, None) == 2
+    # workspace too small
+    assert f(ctypes.byref(cc), fake, fake, None, 2, 64, fake, None, None, fake, ws - 1, None) == 3
+    # decode
+    dws = lib.msgla_decode_workspace_bytes(ctypes.byref(cc), 2)
+    d = lib.msgla_decode_step
+    assert d(ctypes.byref(cc), fake, None, 2, fake, fake, fake, dws, None) == 1
+    assert d(ctypes.byref(cc), fake, fake, 2, fake, fake, fake, dws - 1, None) == 3
+    # packing
+    w = binding.CWeights()
+    assert lib.msgla_pack_weights(ctypes.byref(cc), ctypes.byref(w), fake,
+                                  lib.msgla_packed_weights_bytes(ctypes.byref(cc)), None) == 1
+    st = lib.msgla_state_bytes(ctypes.byref(cc), 2)
+    assert lib.msgla_state_init(ctypes.byref(cc), 2, fake, st - 1, None) == 3
+
+
+def test_workspace_grows_with_batch_and_length():
+    cfg = WORKLOADS["main"].cfg
+    a = binding.msgla_workspace_bytes(cfg, 1, 2048)
+    b = binding.msgla_workspace_bytes(cfg, 2, 2048)
+    c = binding.msgla_workspace_bytes(cfg, 1, 4096)
+    assert 0 < a < b and a < c
