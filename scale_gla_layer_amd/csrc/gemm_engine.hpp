@@ -4,17 +4,20 @@
 // 256 threads = 4 wave64s in a 2 x 2 grid; each wave owns a 64 x 64 sub-tile
 // (4 x 4 MFMA tiles of 16 x 16).  K advances in 128-byte row segments
 // (64 bf16 or 32 fp32 values = two 64-byte k-slabs) staged through LDS with
-// double buffering: the next segment's global loads are issued before the
-// current segment's MFMAs, and one barrier per segment separates the LDS write
-// of one stage from the reads of the other.  LDS rows are padded to 144 bytes
-// so the 16-byte fragment reads of 8 consecutive lanes hit distinct banks.
+// double buffering.  Each iteration issues the global loads of the next
+// segment, runs the MFMAs of the current one, and only then combines the
+// loaded data (pooling sums, fusion scaling) and writes it to the other LDS
+// stage, so memory latency overlaps the MFMAs; one barrier per segment.
+// LDS rows are padded to 144 bytes so the 16-byte fragment reads of 8
+// consecutive lanes hit distinct banks.
 //
 // The operand loaders and the epilogue come from a problem class:
-//   void a_setup(int i, int row)   / u32x4 a_load(int i, int kt, int c16)
-//   void b_setup(int i, int row)   / u32x4 b_load(int i, int kt, int c16)
+//   void a_setup(int i, int row) / void a_fetch(int i, int kt, int c16) / u32x4 a_get(int i)
+//   void b_setup(int i, int row) / void b_fetch(int i, int kt, int c16) / u32x4 b_get(int i)
 //   void epilogue(const float* C, int ldc)   (C = the 128 x 128 fp32 tile in LDS)
-// Thread t loads the 16-byte pieces (row = t/8 + 32 i, c16 = t % 8), i < 4, of
-// both 128 x 128-byte operand tiles; loaders return zeros outside the problem.
+// a_fetch issues the loads of piece i (row = t/8 + 32 i, c16 = t % 8) of
+// segment kt into the problem's registers; a_get, called after the MFMAs,
+// returns the 16 bytes to stage.  Loaders return zeros outside the problem.
 #pragma once
 #include "device_common.hpp"
 
@@ -55,32 +58,31 @@ __device__ __forceinline__ void gemm_tile_128(Prob& prob, int nk, int n_valid, c
 #pragma unroll
   for (int b = 0; b < 4; ++b) nb_valid += (wc * 64 + 16 * b < n_valid) ? 1 : 0;
 
-  u32x4 ra[4], rb[4];
-  auto gload = [&](int kt) {
+  auto fetch = [&](int kt) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      ra[i] = prob.a_load(i, kt, c16);
-      rb[i] = prob.b_load(i, kt, c16);
+      prob.a_fetch(i, kt, c16);
+      prob.b_fetch(i, kt, c16);
     }
   };
-  auto lstore = [&](int stage) {
-    char* sa = lds + stage * GEMM_STAGE;
+  auto stage = [&](int st) {
+    char* sa = lds + st * GEMM_STAGE;
     char* sb = sa + GEMM_BM * GEMM_ROWB;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = (tid >> 3) + 32 * i;
-      st16(sa + row * GEMM_ROWB + c16 * 16, ra[i]);
-      st16(sb + row * GEMM_ROWB + c16 * 16, rb[i]);
+      st16(sa + row * GEMM_ROWB + c16 * 16, prob.a_get(i));
+      st16(sb + row * GEMM_ROWB + c16 * 16, prob.b_get(i));
     }
   };
 
-  gload(0);
-  lstore(0);
+  fetch(0);
+  stage(0);
   __syncthreads();
 
   for (int kt = 0; kt < nk; ++kt) {
     const bool more = kt + 1 < nk;
-    if (more) gload(kt + 1);
+    if (more) fetch(kt + 1);
     const char* sa = lds + (kt & 1) * GEMM_STAGE;
     const char* sb = sa + GEMM_BM * GEMM_ROWB;
 #pragma unroll
@@ -100,7 +102,7 @@ __device__ __forceinline__ void gemm_tile_128(Prob& prob, int nk, int n_valid, c
         }
       }
     }
-    if (more) lstore((kt + 1) & 1);
+    if (more) stage((kt + 1) & 1);
     __syncthreads();
   }
 

@@ -13,9 +13,14 @@
 // wave w keeps rows c of S with (c / 16) % 4 == w — and after each update it
 // is published to LDS in the storage type (transposed, [v][c]) as the
 // B-operand of the next chunk's qt S.  Wave w also produces output rows
-// 16w .. 16w+15 of each chunk.  V of the chunk is staged in LDS (positions
-// beyond the sequence end are zeroed there) and serves both products.
+// 16w .. 16w+15 of each chunk.  The walk is latency-bound unless the inputs
+// of later chunks are already in flight: A, qt, kT, the chunk's V slice and
+// lam are copied global -> LDS asynchronously (global_load_lds_dwordx4, no
+// VGPRs) into NST rotating stages, NST-1 chunks ahead of the compute, with
+// vmcnt waits and one barrier per chunk.  V positions beyond the sequence end
+// are zeroed in the fragments (the workspace there is never written).
 // After the last chunk the fp32 state is optionally written out.
+#include "async_copy.hpp"
 #include "device_common.hpp"
 #include "layout.hpp"
 
@@ -24,7 +29,26 @@ namespace msgla {
 constexpr int K2B_THREADS = 256;
 constexpr int K2B_DVT = 32;  // d_v columns per workgroup
 
-template <typename T, int SRT>
+struct K2bStage {  // byte offsets of one pipeline stage (each a multiple of 1 KB)
+  int A, Q, K, V, L, bytes;
+};
+
+__host__ __device__ inline int k2b_kb(int b) { return (b + 1023) & ~1023; }
+
+__host__ __device__ inline K2bStage k2b_stage(int C, int dk, int es) {
+  K2bStage g;
+  g.A = 0;
+  g.Q = g.A + k2b_kb(C * C * es);
+  g.K = g.Q + k2b_kb(C * dk * es);
+  g.V = g.K + k2b_kb(dk * C * es);
+  g.L = g.V + k2b_kb(K2B_DVT * C * es);
+  g.bytes = g.L + k2b_kb(dk * 4);
+  return g;
+}
+
+__device__ __forceinline__ int ilog2(int x) { return 31 - __builtin_clz(x); }
+
+template <typename T, int SRT, int NST>
 __global__ __launch_bounds__(K2B_THREADS) void k2b_gla_state(const K2Params P) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int g = blockIdx.x;
@@ -38,118 +62,155 @@ __global__ __launch_bounds__(K2B_THREADS) void k2b_gla_state(const K2Params P) {
   const K2Branch& Bb = P.br[bi];
   const int bh = qseq - Bb.seq_begin;  // b * h + head
 
+  constexpr int es = sizeof(T);
+  constexpr int PER = per16<T>();
   const int C = P.C, dk = P.dk, dv = P.dv;
   const int v0 = tile * K2B_DVT;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lr = lane & 15, lg = lane >> 4;
-  const int nrt = dk / 16;  // state row tiles
+  const int lr = lane & 15, lgp = lane >> 4;
+  const int nrt = dk / 16;                  // state row tiles
+  const int lgC = ilog2(C * es);            // log2 bytes of an A / kT / V row
+  const int lgQ = ilog2(dk * es);           // log2 bytes of a qt row
+  const int lgL = ilog2(dk * 4);            // lam is one row of dk floats
+  const int nslab_c = C * es / 64;          // 64-byte k-slabs over positions
+  const int nslab_k = dk * es / 64;         // 64-byte k-slabs over key channels
 
-  // LDS: ST[2][DVT][dk + pad] (T) | VT[2][DVT][C + pad] (T)
-  const int lds_s = dk + 16 / (int)sizeof(T);
-  const int lds_v = C + 16 / (int)sizeof(T);
-  T* ST = reinterpret_cast<T*>(smem);
-  T* VS = ST + 2 * K2B_DVT * lds_s;
+  // LDS: NST stages | ST[2][DVT][dk + pad] (published state) | per-wave y staging
+  const K2bStage sg = k2b_stage(C, dk, es);
+  const int lds_s = dk + 16 / es;
+  T* ST = reinterpret_cast<T*>(smem + (size_t)NST * sg.bytes);
+  const int ldy = K2B_DVT + 16 / es;
+  T* ys = ST + 2 * K2B_DVT * lds_s + wave * 16 * ldy;
 
   const size_t chunk0 = (size_t)bh * Bb.nch;
-  const T* Ag = reinterpret_cast<const T*>(Bb.A);
-  const T* qtg = reinterpret_cast<const T*>(Bb.qt) + (size_t)bh * Bb.np * dk;
-  const T* kTg = reinterpret_cast<const T*>(Bb.kT);
-  const T* vTg = reinterpret_cast<const T*>(Bb.vT);
-  T* yg = reinterpret_cast<T*>(Bb.y) + (size_t)bh * Bb.np * dv;
+  const char* Ag = reinterpret_cast<const char*>(Bb.A) + chunk0 * C * C * es;
+  const char* Qg = reinterpret_cast<const char*>(Bb.qt) + (size_t)bh * Bb.np * dk * es;
+  const char* Kg = reinterpret_cast<const char*>(Bb.kT) + chunk0 * dk * C * es;
+  const char* Vg = reinterpret_cast<const char*>(Bb.vT) + (chunk0 * dv + v0) * C * es;
+  const char* Lg = reinterpret_cast<const char*>(Bb.lam + chunk0 * dk);
+  T* yg = reinterpret_cast<T*>(Bb.y) + (size_t)bh * Bb.np * dv + v0;
+  const int bA = C * C * es, bQ = C * dk * es, bV = K2B_DVT * C * es, bL = dk * 4;
 
-  // state accumulators: [SRT row tiles][2 col tiles]
+  // asynchronous copies of chunk c into stage c % NST (all contiguous blocks)
+  auto issue = [&](int c) -> int {
+    char* st = smem + (size_t)(c % NST) * sg.bytes;
+    int n = dma_block(Ag + (size_t)c * bA, bA, lgC, st + sg.A, wave, 4, lane);
+    n += dma_block(Qg + (size_t)c * bQ, bQ, lgQ, st + sg.Q, wave, 4, lane);
+    n += dma_block(Kg + (size_t)c * bQ, bQ, lgC, st + sg.K, wave, 4, lane);
+    n += dma_block(Vg + (size_t)c * dv * C * es, bV, lgC, st + sg.V, wave, 4, lane);
+    n += dma_block(Lg + (size_t)c * bL, bL, lgL, st + sg.L, wave, 4, lane);
+    return n;
+  };
+
   f32x4 S[SRT][2];
 #pragma unroll
   for (int a = 0; a < SRT; ++a) S[a][0] = S[a][1] = zero4();
 
-  // S_0 = 0 published to LDS buffer 0
+  int K = 0;  // copy instructions per chunk issued by this wave
+  for (int c = 0; c < NST - 1 && c < Bb.nch; ++c) K = issue(c);
   for (int i = tid; i < K2B_DVT * lds_s; i += K2B_THREADS) ST[i] = from_f32<T>(0.f);
 
-  // stage V of chunk c (positions >= valid zeroed) into buffer c & 1
-  auto stage_v = [&](int c) {
-    const int valid = min(C, Bb.n - c * C);
-    const T* src = vTg + ((chunk0 + c) * dv + v0) * C;
-    T* dst = VS + (c & 1) * K2B_DVT * lds_v;
-    const int per_row = C / per16<T>();
-    for (int p = tid; p < K2B_DVT * per_row; p += K2B_THREADS) {
-      const int vr = p / per_row, tp = (p - vr * per_row) * per16<T>();
-      u32x4 x = ld16(src + (size_t)vr * C + tp);
-      if (tp + per16<T>() > valid) {
-        float f[per16<T>()];
-        unpack16<T>(x, f);
-#pragma unroll
-        for (int e = 0; e < per16<T>(); ++e)
-          if (tp + e >= valid) f[e] = 0.f;
-        x = pack16<T>(f);
-      }
-      st16(dst + vr * lds_v + tp, x);
-    }
-  };
-  if (Bb.nch > 0) stage_v(0);
-  __syncthreads();
-
   for (int c = 0; c < Bb.nch; ++c) {
+    // stage c must have landed: with one later stage in flight at most K
+    // more copies may be outstanding (stores issued since only add to that)
+    if (NST > 2 && c + 1 < Bb.nch && K >= 8)
+      wait_vmcnt<8>();
+    else
+      wait_vmcnt<0>();
+    lds_barrier();
+    if (c + NST - 1 < Bb.nch) issue(c + NST - 1);
+
+    const char* st = smem + (size_t)(c % NST) * sg.bytes;
     const T* Sb = ST + (c & 1) * K2B_DVT * lds_s;
-    const T* Vb = VS + (c & 1) * K2B_DVT * lds_v;
-    // ---- y rows of this wave: y = A V + qt S ----
+    T* Sn = ST + ((c + 1) & 1) * K2B_DVT * lds_s;
+    const int valid = min(C, Bb.n - c * C);
+
+    // V fragments (B-operand of both products); positions >= valid zeroed
+    u32x4 vf[4][2];
+#pragma unroll
+    for (int sl = 0; sl < 4; ++sl)
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct)
+        if (sl < nslab_c) vf[sl][ct] = ld16(st + sg.V + tile_off(16 * ct + lr, sl * 4 + lgp, lgC));
+    if (valid < C) {
+#pragma unroll
+      for (int sl = 0; sl < 4; ++sl)
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+          if (sl < nslab_c) {
+            const int tau0 = (sl * 4 + lgp) * PER;
+            float u[PER];
+            unpack16<T>(vf[sl][ct], u);
+#pragma unroll
+            for (int e = 0; e < PER; ++e)
+              if (tau0 + e >= valid) u[e] = 0.f;
+            vf[sl][ct] = pack16<T>(u);
+          }
+        }
+    }
+
+    // ---- y rows 16w .. 16w+15: y = A V + qt S, staged for 16-byte stores ----
     if (wave < C / 16) {
       const int rt = wave;
       f32x4 y[2] = {zero4(), zero4()};
-      const T* Arow = Ag + ((chunk0 + c) * C + 16 * rt + lr) * C;
-      for (int i0 = 0; i0 < C; i0 += slab_elems<T>()) {
-        const u32x4 a = ld16(Arow + i0 + lg * per16<T>());
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct) {
-          const u32x4 bv = ld16(Vb + (16 * ct + lr) * lds_v + i0 + lg * per16<T>());
-          y[ct] = mma_slab<T>(a, bv, y[ct]);
+      for (int sl = 0; sl < 4; ++sl) {
+        if (sl < nslab_c) {
+          const u32x4 a = ld16(st + sg.A + tile_off(16 * rt + lr, sl * 4 + lgp, lgC));
+          y[0] = mma_slab<T>(a, vf[sl][0], y[0]);
+          y[1] = mma_slab<T>(a, vf[sl][1], y[1]);
         }
       }
-      const T* qrow = qtg + ((size_t)c * C + 16 * rt + lr) * dk;
-      for (int c0 = 0; c0 < dk; c0 += slab_elems<T>()) {
-        const u32x4 a = ld16(qrow + c0 + lg * per16<T>());
+      for (int sl = 0; sl < nslab_k; ++sl) {
+        const u32x4 a = ld16(st + sg.Q + tile_off(16 * rt + lr, sl * 4 + lgp, lgQ));
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct) {
-          const u32x4 bs = ld16(Sb + (16 * ct + lr) * lds_s + c0 + lg * per16<T>());
+          const u32x4 bs = ld16(Sb + (16 * ct + lr) * lds_s + sl * slab_elems<T>() + lgp * PER);
           y[ct] = mma_slab<T>(a, bs, y[ct]);
         }
       }
-      const int valid = min(C, Bb.n - c * C);
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int tau = 16 * rt + 4 * lg + e;
-          if (tau < valid) yg[((size_t)c * C + tau) * dv + v0 + 16 * ct + lr] = from_f32<T>(y[ct][e]);
-        }
+        for (int e = 0; e < 4; ++e) ys[(4 * lgp + e) * ldy + 16 * ct + lr] = from_f32<T>(y[ct][e]);
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (0 << 8));  // own LDS writes done
+      asm volatile("" ::: "memory");
+      // 16 rows x DVT values of this wave -> 16-byte global stores
+      constexpr int PR = K2B_DVT / PER;  // pieces per row
+      for (int p = lane; p < 16 * PR; p += 64) {
+        const int row = p / PR, pc = p - row * PR;
+        const int tau = 16 * rt + row;
+        if (tau < valid)
+          st16(yg + ((size_t)c * C + tau) * dv + pc * PER, ld16(ys + row * ldy + pc * PER));
+      }
     }
-    // ---- state update: S = Diag(lam) S + kT V, rows owned by this wave ----
-    const float* lam = Bb.lam + (chunk0 + c) * dk;
-    T* Sn = ST + ((c + 1) & 1) * K2B_DVT * lds_s;
+    // ---- state update: S = Diag(lam) S + kT V for the rows this wave owns ----
 #pragma unroll
     for (int a = 0; a < SRT; ++a) {
       const int rt = wave + 4 * a;
       if (rt < nrt) {
+        const int c4 = 16 * rt + 4 * lgp;  // first of this lane's 4 state rows
+        const f32x4 l4 = __builtin_bit_cast(f32x4, ld16(st + sg.L + tile_off(0, c4 >> 2, lgL)));
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float l = lam[16 * rt + 4 * lg + e];
-          S[a][0][e] *= l;
-          S[a][1][e] *= l;
+          S[a][0][e] *= l4[e];
+          S[a][1][e] *= l4[e];
         }
-        const T* krow = kTg + ((chunk0 + c) * dk + 16 * rt + lr) * C;
-        for (int t0 = 0; t0 < C; t0 += slab_elems<T>()) {
-          const u32x4 ak = ld16(krow + t0 + lg * per16<T>());
 #pragma unroll
-          for (int ct = 0; ct < 2; ++ct) {
-            const u32x4 bv = ld16(Vb + (16 * ct + lr) * lds_v + t0 + lg * per16<T>());
-            S[a][ct] = mma_slab<T>(ak, bv, S[a][ct]);
+        for (int sl = 0; sl < 4; ++sl) {
+          if (sl < nslab_c) {
+            const u32x4 ak = ld16(st + sg.K + tile_off(16 * rt + lr, sl * 4 + lgp, lgC));
+            S[a][0] = mma_slab<T>(ak, vf[sl][0], S[a][0]);
+            S[a][1] = mma_slab<T>(ak, vf[sl][1], S[a][1]);
           }
         }
         // publish S_{c+1}: ST[v][c], 4 consecutive c per lane
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct) {
           float f[4] = {S[a][ct][0], S[a][ct][1], S[a][ct][2], S[a][ct][3]};
-          T* dst = Sn + (16 * ct + lr) * lds_s + 16 * rt + 4 * lg;
+          T* dst = Sn + (16 * ct + lr) * lds_s + c4;
           if constexpr (sizeof(T) == 2)
             st8(dst, pack8<T>(f));
           else
@@ -157,8 +218,6 @@ __global__ __launch_bounds__(K2B_THREADS) void k2b_gla_state(const K2Params P) {
         }
       }
     }
-    if (c + 1 < Bb.nch) stage_v(c + 1);
-    __syncthreads();
   }
 
   if (Bb.S_out) {
@@ -171,37 +230,57 @@ __global__ __launch_bounds__(K2B_THREADS) void k2b_gla_state(const K2Params P) {
         for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            So[(size_t)(16 * rt + 4 * lg + e) * dv + v0 + 16 * ct + lr] = S[a][ct][e];
+            So[(size_t)(16 * rt + 4 * lgp + e) * dv + v0 + 16 * ct + lr] = S[a][ct][e];
       }
     }
   }
 }
 
+static size_t k2b_lds(int C, int dk, int es, int nst) {
+  return (size_t)nst * k2b_stage(C, dk, es).bytes + (size_t)2 * K2B_DVT * (dk + 16 / es) * es +
+         (size_t)4 * 16 * (K2B_DVT + 16 / es) * es;
+}
+
 size_t k2b_lds_bytes(int C, int dk, bool bf16_path) {
   const int es = bf16_path ? 2 : 4;
-  return (size_t)2 * K2B_DVT * (dk + 16 / es) * es + (size_t)2 * K2B_DVT * (C + 16 / es) * es;
+  return k2b_lds(C, dk, es, k2b_lds(C, dk, es, 3) <= 160 * 1024 ? 3 : 2);
 }
 
 int k2b_dvt() { return K2B_DVT; }
 
+template <typename T, int SRT, int NST>
+static void launch_k2b_n(const K2Params& P, dim3 grid, size_t lds, hipStream_t stream) {
+  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k2b_gla_state<T, SRT, NST>),
+                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  hipLaunchKernelGGL((k2b_gla_state<T, SRT, NST>), grid, dim3(K2B_THREADS), lds, stream, P);
+}
+
+template <typename T, int SRT>
+static void launch_k2b_s(const K2Params& P, dim3 grid, hipStream_t stream) {
+  const int es = sizeof(T);
+  if (k2b_lds(P.C, P.dk, es, 3) <= 160 * 1024)
+    launch_k2b_n<T, SRT, 3>(P, grid, k2b_lds(P.C, P.dk, es, 3), stream);
+  else
+    launch_k2b_n<T, SRT, 2>(P, grid, k2b_lds(P.C, P.dk, es, 2), stream);
+}
+
 template <typename T>
-static void launch_k2b_t(const K2Params& P, dim3 grid, size_t lds, hipStream_t stream) {
+static void launch_k2b_t(const K2Params& P, dim3 grid, hipStream_t stream) {
   const int nrt = P.dk / 16;
   if (nrt <= 4)
-    hipLaunchKernelGGL((k2b_gla_state<T, 1>), grid, dim3(K2B_THREADS), lds, stream, P);
+    launch_k2b_s<T, 1>(P, grid, stream);
   else if (nrt <= 8)
-    hipLaunchKernelGGL((k2b_gla_state<T, 2>), grid, dim3(K2B_THREADS), lds, stream, P);
+    launch_k2b_s<T, 2>(P, grid, stream);
   else
-    hipLaunchKernelGGL((k2b_gla_state<T, 4>), grid, dim3(K2B_THREADS), lds, stream, P);
+    launch_k2b_s<T, 4>(P, grid, stream);
 }
 
 hipError_t launch_k2b(const K2Params& P, bool bf16_path, hipStream_t stream) {
-  const size_t lds = k2b_lds_bytes(P.C, P.dk, bf16_path);
   const dim3 grid(((P.total_seqs + N_XCD - 1) / N_XCD) * N_XCD * P.n_dvt);
   if (bf16_path)
-    launch_k2b_t<bf16>(P, grid, lds, stream);
+    launch_k2b_t<bf16>(P, grid, stream);
   else
-    launch_k2b_t<float>(P, grid, lds, stream);
+    launch_k2b_t<float>(P, grid, stream);
   return hipGetLastError();
 }
 

@@ -24,6 +24,8 @@ struct K3Prob {
   int m0, n0;
   int ab[4], at[4];  // sequence and position of each loaded A row (-1: none)
   const T* brow[4];
+  u32x4 ra[4], rb[4];
+  float wv[4];
 
   __device__ K3Prob(const K3Params& p, int m0_, int n0_) : P(p), m0(m0_), n0(n0_) {}
 
@@ -37,38 +39,39 @@ struct K3Prob {
       at[i] = 0;
     }
   }
-  __device__ u32x4 a_load(int i, int kt, int c16) {
-    if (ab[i] < 0) return zero16();
+  // gather the held coarse row (Sec. 3.3) and its fusion weight; scaled in a_get
+  __device__ void a_fetch(int i, int kt, int c16) {
+    ra[i] = zero16();
+    wv[i] = 0.f;
+    if (ab[i] < 0) return;
     constexpr int E128 = 128 / sizeof(T);
     const int k0 = kt * E128;
     int bi = 0;
     while (bi + 1 < MSGLA_MAX_BRANCHES && bi + 1 < P.m && k0 >= P.br[bi + 1].ko) ++bi;
     const K3Branch& Br = P.br[bi];
-    const int j = (at[i] + 1) / Br.s - 1;            // held coarse row (Sec. 3.3)
-    const int kk = k0 - Br.ko + c16 * per16<T>();    // element inside the branch range
-    if (j < 0 || kk >= Br.h * P.dv) return zero16();
+    const int j = (at[i] + 1) / Br.s - 1;
+    const int kk = k0 - Br.ko + c16 * per16<T>();
+    if (j < 0 || kk >= Br.h * P.dv) return;
     const int hh = kk / P.dv, v = kk - hh * P.dv;
-    const T* src = reinterpret_cast<const T*>(Br.y) +
-                   (((size_t)ab[i] * Br.h + hh) * Br.np + j) * P.dv + v;
-    u32x4 x = ld16(src);
-    if (P.m > 1) {
-      const float wgt = P.w[((size_t)ab[i] * P.L + at[i]) * FUSION_STRIDE + bi];
-      float f[per16<T>()];
-      unpack16<T>(x, f);
+    ra[i] = ld16(reinterpret_cast<const T*>(Br.y) + (((size_t)ab[i] * Br.h + hh) * Br.np + j) * P.dv + v);
+    wv[i] = (P.m > 1) ? P.w[((size_t)ab[i] * P.L + at[i]) * FUSION_STRIDE + bi] : 1.f;
+  }
+  __device__ u32x4 a_get(int i) {
+    if (P.m == 1) return ra[i];
+    float f[per16<T>()];
+    unpack16<T>(ra[i], f);
 #pragma unroll
-      for (int e = 0; e < per16<T>(); ++e) f[e] *= wgt;
-      x = pack16<T>(f);
-    }
-    return x;
+    for (int e = 0; e < per16<T>(); ++e) f[e] *= wv[i];
+    return pack16<T>(f);
   }
   __device__ void b_setup(int i, int row) {
     const int n = n0 + row;
     brow[i] = (n < P.d) ? reinterpret_cast<const T*>(P.WoT) + (size_t)n * P.Ktot : nullptr;
   }
-  __device__ u32x4 b_load(int i, int kt, int c16) {
-    if (!brow[i]) return zero16();
-    return ld16(brow[i] + kt * (128 / sizeof(T)) + c16 * per16<T>());
+  __device__ void b_fetch(int i, int kt, int c16) {
+    rb[i] = brow[i] ? ld16(brow[i] + kt * (128 / sizeof(T)) + c16 * per16<T>()) : zero16();
   }
+  __device__ u32x4 b_get(int i) { return rb[i]; }
   __device__ void epilogue(const float* C, int ldc) {
     const int tid = threadIdx.x;
     T* out = reinterpret_cast<T*>(P.out);

@@ -7,7 +7,8 @@
 // For branch i (scale s): C_i = P_s(X) * Wp_i^T, where row (b, j) of P_s(X) is
 // the mean of X rows b*L + j*s .. + s-1 (only complete blocks), computed in
 // fp32 inside the A-operand loader and rounded once to the storage type, so
-// the pooled sequence never touches HBM.  Wp_i stacks the transposed q, k, v,
+// the pooled sequence never touches HBM (the s raw loads are issued before the
+// MFMAs of the previous K segment and summed after them).  Wp_i stacks the transposed q, k, v,
 // first-gate-factor and (for the branch that carries them) fusion-logit
 // weights; the epilogue routes each column range to its consumer layout:
 // q, k head-major fp32 rows, v transposed per chunk, the gate factor in fp32, and
@@ -20,13 +21,16 @@
 
 namespace msgla {
 
-template <typename T>
+template <typename T, int SMAX>
 struct K1Prob {
   const K1Params& P;
   const K1Group& G;
   int m0, n0;
   const T* arow[4];
   const T* brow[4];
+  const T* apos[4];        // first raw row of the piece being fetched
+  u32x4 raw[4][SMAX];      // raw 16-byte pieces of the s rows of a pooled block
+  u32x4 rb[4];
   float inv_s;
 
   __device__ K1Prob(const K1Params& p, const K1Group& g, int m0_, int n0_)
@@ -41,14 +45,30 @@ struct K1Prob {
       arow[i] = nullptr;
     }
   }
-  __device__ u32x4 a_load(int i, int kt, int c16) {
-    if (!arow[i]) return zero16();
+  // issue the loads of the s raw rows (consumed after the MFMAs in a_get)
+  __device__ void a_fetch(int i, int kt, int c16) {
+    if (!arow[i]) return;
     const T* p = arow[i] + kt * (128 / sizeof(T)) + c16 * per16<T>();
-    if (G.s == 1) return ld16(p);
+    apos[i] = p;
+#pragma unroll
+    for (int u = 0; u < SMAX; ++u)
+      if (u < G.s) raw[i][u] = ld16(p + (size_t)u * P.d);
+  }
+  __device__ u32x4 a_get(int i) {
+    if (!arow[i]) return zero16();
+    if (SMAX == 1 || G.s == 1) return raw[i][0];
     float sum[per16<T>()], tmp[per16<T>()];
-    unpack16<T>(ld16(p), sum);
-    for (int u = 1; u < G.s; ++u) {
-      unpack16<T>(ld16(p + (size_t)u * P.d), tmp);
+    unpack16<T>(raw[i][0], sum);
+#pragma unroll
+    for (int u = 1; u < SMAX; ++u) {
+      if (u < G.s) {
+        unpack16<T>(raw[i][u], tmp);
+#pragma unroll
+        for (int e = 0; e < per16<T>(); ++e) sum[e] += tmp[e];
+      }
+    }
+    for (int u = SMAX; u < G.s; ++u) {  // blocks longer than SMAX: remaining rows now
+      unpack16<T>(ld16(apos[i] + (size_t)u * P.d), tmp);
 #pragma unroll
       for (int e = 0; e < per16<T>(); ++e) sum[e] += tmp[e];
     }
@@ -60,10 +80,10 @@ struct K1Prob {
     const int n = n0 + row;
     brow[i] = (n < G.N) ? reinterpret_cast<const T*>(G.Wp) + (size_t)n * P.d : nullptr;
   }
-  __device__ u32x4 b_load(int i, int kt, int c16) {
-    if (!brow[i]) return zero16();
-    return ld16(brow[i] + kt * (128 / sizeof(T)) + c16 * per16<T>());
+  __device__ void b_fetch(int i, int kt, int c16) {
+    rb[i] = brow[i] ? ld16(brow[i] + kt * (128 / sizeof(T)) + c16 * per16<T>()) : zero16();
   }
+  __device__ u32x4 b_get(int i) { return rb[i]; }
 
   __device__ void store8(T* dst, const float* v) {
     if constexpr (sizeof(T) == 2) {
@@ -151,7 +171,7 @@ struct K1Prob {
   }
 };
 
-template <typename T>
+template <typename T, int SMAX>
 __global__ __launch_bounds__(GEMM_THREADS) void k1_pool_proj(const K1Params P) {
   __shared__ __attribute__((aligned(16))) char lds[GEMM_LDS_BYTES];
   const int tile = remap_xcd(blockIdx.x, P.per_xcd);
@@ -161,16 +181,31 @@ __global__ __launch_bounds__(GEMM_THREADS) void k1_pool_proj(const K1Params P) {
   const K1Group& G = P.g[gi];
   const int local = tile - G.tile_begin;
   const int tm = local / G.tiles_n, tn = local - tm * G.tiles_n;
-  K1Prob<T> prob(P, G, tm * GEMM_BM, tn * GEMM_BN);
+  K1Prob<T, SMAX> prob(P, G, tm * GEMM_BM, tn * GEMM_BN);
   gemm_tile_128<T>(prob, P.d * (int)sizeof(T) / 128, G.N - tn * GEMM_BN, lds);
 }
 
-hipError_t launch_k1(const K1Params& P, bool bf16_path, hipStream_t stream) {
-  const dim3 grid(P.per_xcd * N_XCD), block(GEMM_THREADS);
-  if (bf16_path)
-    hipLaunchKernelGGL(k1_pool_proj<bf16>, grid, block, 0, stream, P);
+template <typename T>
+static void launch_k1_t(const K1Params& P, dim3 grid, hipStream_t stream) {
+  int smax = 1;
+  for (int g = 0; g < P.ngroups; ++g) smax = smax > P.g[g].s ? smax : P.g[g].s;
+  const dim3 block(GEMM_THREADS);
+  if (smax <= 1)
+    hipLaunchKernelGGL((k1_pool_proj<T, 1>), grid, block, 0, stream, P);
+  else if (smax <= 2)
+    hipLaunchKernelGGL((k1_pool_proj<T, 2>), grid, block, 0, stream, P);
+  else if (smax <= 4)
+    hipLaunchKernelGGL((k1_pool_proj<T, 4>), grid, block, 0, stream, P);
   else
-    hipLaunchKernelGGL(k1_pool_proj<float>, grid, block, 0, stream, P);
+    hipLaunchKernelGGL((k1_pool_proj<T, 8>), grid, block, 0, stream, P);
+}
+
+hipError_t launch_k1(const K1Params& P, bool bf16_path, hipStream_t stream) {
+  const dim3 grid(P.per_xcd * N_XCD);
+  if (bf16_path)
+    launch_k1_t<bf16>(P, grid, stream);
+  else
+    launch_k1_t<float>(P, grid, stream);
   return hipGetLastError();
 }
 
