@@ -22,6 +22,7 @@ ARCH = os.environ.get("MSGLA_OFFLOAD_ARCH", "gfx950")
 
 SOURCES = [
     "api.cpp",
+    "k_pool.hip",
     "k_pool_proj.hip",
     "k_gla_chunk.hip",
     "k_gla_state.hip",

@@ -12,6 +12,7 @@
 
 namespace msgla {
 // launchers (one per kernel file)
+hipError_t launch_pool(const PoolParams& P, bool bf16_path, hipStream_t st);
 hipError_t launch_k1(const K1Params& P, bool bf16_path, hipStream_t stream);
 hipError_t launch_k2a(const K2Params& P, bool bf16_path, hipStream_t stream);
 hipError_t launch_k2b(const K2Params& P, bool bf16_path, hipStream_t stream);
@@ -50,7 +51,7 @@ struct PackGeom {
   int es, m, d, dk, dv, r, rp, C, Ktot, carrier;
   size_t off_Wz;  // 0 if none (fusion carried by a branch or m == 1)
   bool has_Wz;
-  size_t off_bf, off_WoT, total;
+  size_t off_bf, off_zero, off_WoT, total;
   BranchGeom br[MSGLA_MAX_BRANCHES];
 };
 
@@ -66,7 +67,8 @@ msgla_status check_config(const msgla_config* c) {
   }
   if (c->d_model < 64 || c->d_model % 64 != 0 || c->d_model > 65536) return MSGLA_ERR_INVALID_ARG;
   if (c->d_k < 16 || c->d_k > 256 || c->d_k % (bf ? 32 : 16) != 0) return MSGLA_ERR_INVALID_ARG;
-  if (c->d_v < 32 || c->d_v > 512 || c->d_v % 32 != 0) return MSGLA_ERR_INVALID_ARG;
+  // a 128-byte K segment of the output projection must lie inside one head
+  if (c->d_v < 32 || c->d_v > 512 || c->d_v % (bf ? 64 : 32) != 0) return MSGLA_ERR_INVALID_ARG;
   if (c->gate_rank < 1 || c->gate_rank > 64) return MSGLA_ERR_INVALID_ARG;
   if (bf ? (c->chunk != 32 && c->chunk != 64)
          : (c->chunk != 16 && c->chunk != 32 && c->chunk != 64))
@@ -121,6 +123,8 @@ PackGeom pack_geom(const msgla_config* c) {
   if (g.has_Wz) cur += align256((size_t)16 * g.d * g.es);
   g.off_bf = cur;
   cur += 256;
+  g.off_zero = cur;  // 256 zero bytes (the whole blob is zero-filled before packing)
+  cur += 256;
   g.off_WoT = cur;
   cur += align256((size_t)g.d * g.Ktot * g.es);
   g.total = cur;
@@ -130,7 +134,7 @@ PackGeom pack_geom(const msgla_config* c) {
 // forward workspace
 struct WsBranch {
   int n, nch, np;
-  size_t q, k, qt, kT, vT, g, A, lam, y;
+  size_t xp, q, k, qt, kT, vT, g, A, lam, y;
 };
 struct WsGeom {
   WsBranch br[MSGLA_MAX_BRANCHES];
@@ -152,6 +156,7 @@ WsGeom ws_geom(const PackGeom& g, int64_t B, int64_t L) {
     b.nch = cdiv(b.n, g.C);
     b.np = b.nch * g.C;
     const size_t rows = (size_t)B * bg.h * b.np;
+    b.xp = bg.s > 1 ? take((size_t)B * b.n * g.d * g.es) : 0;  // block means
     b.q = take(rows * g.dk * 4);
     b.k = take(rows * g.dk * 4);
     b.qt = take(rows * g.dk * g.es);
@@ -360,6 +365,7 @@ msgla_status msgla_forward_timed(const msgla_config* cfg, const void* packed, co
     if (wb.n == 0) continue;
     K1Group& G = p1.g[ng++];
     G.Wp = at<char>(packed, b.off_Wp);
+    G.A = b.s == 1 ? x : static_cast<const void*>(at<char>(workspace, wb.xp));
     G.s = b.s;
     G.n = wb.n;
     G.M = (int)B * wb.n;
@@ -383,6 +389,7 @@ msgla_status msgla_forward_timed(const msgla_config* cfg, const void* packed, co
   if (g.has_Wz) {
     K1Group& G = p1.g[ng++];
     G.Wp = at<char>(packed, g.off_Wz);
+    G.A = x;
     G.s = 1;
     G.n = (int)L;
     G.M = (int)(B * L);
@@ -460,6 +467,7 @@ msgla_status msgla_forward_timed(const msgla_config* cfg, const void* packed, co
   p3.total_tiles = cdiv((int)(B * L), GEMM_TILE) * p3.tiles_n;
   p3.per_xcd = cdiv(p3.total_tiles, N_XCD);
   p3.WoT = at<char>(packed, g.off_WoT);
+  p3.zero = at<char>(packed, g.off_zero);
   p3.w = at<float>(workspace, W.w);
   p3.out = out;
   for (int i = 0; i < g.m; ++i) {
@@ -473,7 +481,39 @@ msgla_status msgla_forward_timed(const msgla_config* cfg, const void* packed, co
     k.kp = g.br[i].kp;
   }
 
+  // pooling prepass: one pass for the scales dividing the largest coarse scale,
+  // one more per remaining coarse scale
+  PoolParams pp[MSGLA_MAX_BRANCHES];
+  int npass = 0;
+  {
+    bool done[MSGLA_MAX_BRANCHES] = {};
+    for (;;) {
+      int smax = 0;
+      for (int i = 0; i < g.m; ++i)
+        if (!done[i] && g.br[i].s > 1 && W.br[i].n > 0) smax = std::max(smax, g.br[i].s);
+      if (smax == 0) break;
+      PoolParams& q = pp[npass++];
+      q = PoolParams{};
+      q.x = x;
+      q.B = (int)B;
+      q.L = (int)L;
+      q.d = g.d;
+      q.smax = smax;
+      for (int i = 0; i < g.m; ++i) {
+        const int s = g.br[i].s;
+        if (done[i] || s <= 1 || W.br[i].n == 0 || smax % s != 0) continue;
+        PoolOut& o = q.out[q.nout++];
+        o.xp = at<char>(workspace, W.br[i].xp);
+        o.s = s;
+        o.n = W.br[i].n;
+        o.inv_s = 1.0f / (float)s;
+        done[i] = true;
+      }
+    }
+  }
+
   HIP_TRY(ev(0, true));
+  for (int i = 0; i < npass; ++i) HIP_TRY(launch_pool(pp[i], g.bf16, st));
   if (p1.total_tiles > 0) HIP_TRY(launch_k1(p1, g.bf16, st));
   HIP_TRY(ev(0, false));
   HIP_TRY(ev(1, true));

@@ -46,7 +46,17 @@ __host__ __device__ inline K2bStage k2b_stage(int C, int dk, int es) {
   return g;
 }
 
-__device__ __forceinline__ int ilog2(int x) { return 31 - __builtin_clz(x); }
+// Per-lane source offset of copy instruction k for a contiguous block stored
+// as swizzled 128-byte virtual rows (async_copy.hpp): source = block + 1024 k
+// + off.  The swizzle key of instruction k is ((8 k + lane / 8) >> hs) & 7;
+// rows of up to 512 bytes (hs <= 2) make it depend on k mod 4 only and rows of
+// 1024 bytes (hs = 3) on k mod 8, so wave w (instructions k = w, w + 4, ...)
+// needs one offset for its even-numbered and one for its odd-numbered copies.
+__device__ __forceinline__ int k2b_lane_off(int lg, int k, int lane) {
+  const int hs = blk_hs(lg);
+  const int vrow = 8 * k + (lane >> 3);
+  return 128 * (lane >> 3) + 16 * ((lane & 7) ^ ((vrow >> hs) & 7));
+}
 
 template <typename T, int SRT, int NST>
 __global__ __launch_bounds__(K2B_THREADS) void k2b_gla_state(const K2Params P) {
@@ -70,9 +80,9 @@ __global__ __launch_bounds__(K2B_THREADS) void k2b_gla_state(const K2Params P) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 15, lgp = lane >> 4;
   const int nrt = dk / 16;                  // state row tiles
-  const int lgC = ilog2(C * es);            // log2 bytes of an A / kT / V row
-  const int lgQ = ilog2(dk * es);           // log2 bytes of a qt row
-  const int lgL = ilog2(dk * 4);            // lam is one row of dk floats
+  const int lgC = 31 - __builtin_clz(C * es);   // log2 bytes of an A / kT / V row
+  const int lgQ = 31 - __builtin_clz(dk * es);  // log2 bytes of a qt row
+  const int lgL = 31 - __builtin_clz(dk * 4);   // lam: one row of dk floats
   const int nslab_c = C * es / 64;          // 64-byte k-slabs over positions
   const int nslab_k = dk * es / 64;         // 64-byte k-slabs over key channels
 
@@ -84,36 +94,74 @@ __global__ __launch_bounds__(K2B_THREADS) void k2b_gla_state(const K2Params P) {
   T* ys = ST + 2 * K2B_DVT * lds_s + wave * 16 * ldy;
 
   const size_t chunk0 = (size_t)bh * Bb.nch;
-  const char* Ag = reinterpret_cast<const char*>(Bb.A) + chunk0 * C * C * es;
+  const int bA = C * C * es, bQ = C * dk * es, bV = K2B_DVT * C * es, bL = dk * 4;
+  const char* Ag = reinterpret_cast<const char*>(Bb.A) + chunk0 * bA;
   const char* Qg = reinterpret_cast<const char*>(Bb.qt) + (size_t)bh * Bb.np * dk * es;
-  const char* Kg = reinterpret_cast<const char*>(Bb.kT) + chunk0 * dk * C * es;
+  const char* Kg = reinterpret_cast<const char*>(Bb.kT) + chunk0 * bQ;
   const char* Vg = reinterpret_cast<const char*>(Bb.vT) + (chunk0 * dv + v0) * C * es;
   const char* Lg = reinterpret_cast<const char*>(Bb.lam + chunk0 * dk);
   T* yg = reinterpret_cast<T*>(Bb.y) + (size_t)bh * Bb.np * dv + v0;
-  const int bA = C * C * es, bQ = C * dk * es, bV = K2B_DVT * C * es, bL = dk * 4;
 
-  // asynchronous copies of chunk c into stage c % NST (all contiguous blocks)
-  auto issue = [&](int c) -> int {
+  // hoisted copy offsets (one per block) and copy counts (per wave)
+  // (A, kT and V rows hold C <= 64 elements, at most 256 bytes; qt rows up to 1 KB)
+  const int oA = k2b_lane_off(lgC, wave, lane);
+  const int oQ0 = k2b_lane_off(lgQ, wave, lane), oQ1 = k2b_lane_off(lgQ, wave + 4, lane);
+  const int oL = 16 * lane;  // lam: one partial instruction, unswizzled row (key 0)
+  const int nA = (bA / 1024 + 3 - wave) / 4, nQ = (bQ / 1024 + 3 - wave) / 4;
+  const int nV = (bV / 1024 + 3 - wave) / 4;
+  const int K = nA + 2 * nQ + nV + (wave == 0 ? 1 : 0);  // copies per chunk of this wave
+  auto issue = [&](int c) {
     char* st = smem + (size_t)(c % NST) * sg.bytes;
-    int n = dma_block(Ag + (size_t)c * bA, bA, lgC, st + sg.A, wave, 4, lane);
-    n += dma_block(Qg + (size_t)c * bQ, bQ, lgQ, st + sg.Q, wave, 4, lane);
-    n += dma_block(Kg + (size_t)c * bQ, bQ, lgC, st + sg.K, wave, 4, lane);
-    n += dma_block(Vg + (size_t)c * dv * C * es, bV, lgC, st + sg.V, wave, 4, lane);
-    n += dma_block(Lg + (size_t)c * bL, bL, lgL, st + sg.L, wave, 4, lane);
-    return n;
+    const char* a = Ag + (size_t)c * bA;
+    const char* q = Qg + (size_t)c * bQ;
+    const char* kk = Kg + (size_t)c * bQ;
+    const char* v = Vg + (size_t)c * dv * C * es;
+    for (int i = 0; i < nA; ++i) {
+      const int k = wave + 4 * i;
+      __builtin_amdgcn_global_load_lds(a + 1024 * k + oA, (lds_void_t*)(st + sg.A + 1024 * k), 16, 0, 0);
+    }
+    for (int i = 0; i < nQ; ++i) {
+      const int k = wave + 4 * i;
+      __builtin_amdgcn_global_load_lds(q + 1024 * k + ((i & 1) ? oQ1 : oQ0),
+                                       (lds_void_t*)(st + sg.Q + 1024 * k), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(kk + 1024 * k + oA, (lds_void_t*)(st + sg.K + 1024 * k), 16, 0, 0);
+    }
+    for (int i = 0; i < nV; ++i) {
+      const int k = wave + 4 * i;
+      __builtin_amdgcn_global_load_lds(v + 1024 * k + oA, (lds_void_t*)(st + sg.V + 1024 * k), 16, 0, 0);
+    }
+    if (wave == 0) {
+      if (oL < bL)
+        __builtin_amdgcn_global_load_lds(Lg + (size_t)c * bL + oL, (lds_void_t*)(st + sg.L), 16, 0, 0);
+    }
   };
+
+  // hoisted LDS fragment offsets (inside a stage)
+  int offV[4][2], offA[4], offK[SRT][4], offQ[16];
+#pragma unroll
+  for (int sl = 0; sl < 4; ++sl) {
+    offV[sl][0] = sg.V + tile_off(lr, sl * 4 + lgp, lgC);
+    offV[sl][1] = sg.V + tile_off(16 + lr, sl * 4 + lgp, lgC);
+    offA[sl] = sg.A + tile_off(16 * wave + lr, sl * 4 + lgp, lgC);
+#pragma unroll
+    for (int a = 0; a < SRT; ++a) offK[a][sl] = sg.K + tile_off(16 * (wave + 4 * a) + lr, sl * 4 + lgp, lgC);
+  }
+#pragma unroll
+  for (int sl = 0; sl < 16; ++sl) offQ[sl] = sg.Q + tile_off(16 * wave + lr, sl * 4 + lgp, lgQ);
+  int offL[SRT];
+#pragma unroll
+  for (int a = 0; a < SRT; ++a) offL[a] = sg.L + tile_off(0, (16 * (wave + 4 * a) + 4 * lgp) >> 2, lgL);
 
   f32x4 S[SRT][2];
 #pragma unroll
   for (int a = 0; a < SRT; ++a) S[a][0] = S[a][1] = zero4();
 
-  int K = 0;  // copy instructions per chunk issued by this wave
-  for (int c = 0; c < NST - 1 && c < Bb.nch; ++c) K = issue(c);
+  for (int c = 0; c < NST - 1 && c < Bb.nch; ++c) issue(c);
   for (int i = tid; i < K2B_DVT * lds_s; i += K2B_THREADS) ST[i] = from_f32<T>(0.f);
 
   for (int c = 0; c < Bb.nch; ++c) {
-    // stage c must have landed: with one later stage in flight at most K
-    // more copies may be outstanding (stores issued since only add to that)
+    // stage c must have landed: with one later stage in flight at most K more
+    // copies may be outstanding (stores issued since only add to that count)
     if (NST > 2 && c + 1 < Bb.nch && K >= 8)
       wait_vmcnt<8>();
     else
@@ -130,9 +178,10 @@ __global__ __launch_bounds__(K2B_THREADS) void k2b_gla_state(const K2Params P) {
     u32x4 vf[4][2];
 #pragma unroll
     for (int sl = 0; sl < 4; ++sl)
-#pragma unroll
-      for (int ct = 0; ct < 2; ++ct)
-        if (sl < nslab_c) vf[sl][ct] = ld16(st + sg.V + tile_off(16 * ct + lr, sl * 4 + lgp, lgC));
+      if (sl < nslab_c) {
+        vf[sl][0] = ld16(st + offV[sl][0]);
+        vf[sl][1] = ld16(st + offV[sl][1]);
+      }
     if (valid < C) {
 #pragma unroll
       for (int sl = 0; sl < 4; ++sl)
@@ -157,17 +206,18 @@ __global__ __launch_bounds__(K2B_THREADS) void k2b_gla_state(const K2Params P) {
 #pragma unroll
       for (int sl = 0; sl < 4; ++sl) {
         if (sl < nslab_c) {
-          const u32x4 a = ld16(st + sg.A + tile_off(16 * rt + lr, sl * 4 + lgp, lgC));
+          const u32x4 a = ld16(st + offA[sl]);
           y[0] = mma_slab<T>(a, vf[sl][0], y[0]);
           y[1] = mma_slab<T>(a, vf[sl][1], y[1]);
         }
       }
-      for (int sl = 0; sl < nslab_k; ++sl) {
-        const u32x4 a = ld16(st + sg.Q + tile_off(16 * rt + lr, sl * 4 + lgp, lgQ));
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct) {
-          const u32x4 bs = ld16(Sb + (16 * ct + lr) * lds_s + sl * slab_elems<T>() + lgp * PER);
-          y[ct] = mma_slab<T>(a, bs, y[ct]);
+      for (int sl = 0; sl < 16; ++sl) {
+        if (sl < nslab_k) {
+          const u32x4 a = ld16(st + offQ[sl]);
+          const T* srow = Sb + lr * lds_s + sl * slab_elems<T>() + lgp * PER;
+          y[0] = mma_slab<T>(a, ld16(srow), y[0]);
+          y[1] = mma_slab<T>(a, ld16(srow + 16 * lds_s), y[1]);
         }
       }
 #pragma unroll
@@ -179,11 +229,12 @@ __global__ __launch_bounds__(K2B_THREADS) void k2b_gla_state(const K2Params P) {
       asm volatile("" ::: "memory");
       // 16 rows x DVT values of this wave -> 16-byte global stores
       constexpr int PR = K2B_DVT / PER;  // pieces per row
-      for (int p = lane; p < 16 * PR; p += 64) {
+#pragma unroll
+      for (int p0 = 0; p0 < 16 * PR; p0 += 64) {
+        const int p = p0 + lane;
         const int row = p / PR, pc = p - row * PR;
-        const int tau = 16 * rt + row;
-        if (tau < valid)
-          st16(yg + ((size_t)c * C + tau) * dv + pc * PER, ld16(ys + row * ldy + pc * PER));
+        if (p < 16 * PR && 16 * rt + row < valid)
+          st16(yg + ((size_t)c * C + 16 * rt + row) * dv + pc * PER, ld16(ys + row * ldy + pc * PER));
       }
     }
     // ---- state update: S = Diag(lam) S + kT V for the rows this wave owns ----
@@ -191,8 +242,7 @@ __global__ __launch_bounds__(K2B_THREADS) void k2b_gla_state(const K2Params P) {
     for (int a = 0; a < SRT; ++a) {
       const int rt = wave + 4 * a;
       if (rt < nrt) {
-        const int c4 = 16 * rt + 4 * lgp;  // first of this lane's 4 state rows
-        const f32x4 l4 = __builtin_bit_cast(f32x4, ld16(st + sg.L + tile_off(0, c4 >> 2, lgL)));
+        const f32x4 l4 = __builtin_bit_cast(f32x4, ld16(st + offL[a]));
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           S[a][0][e] *= l4[e];
@@ -201,12 +251,13 @@ __global__ __launch_bounds__(K2B_THREADS) void k2b_gla_state(const K2Params P) {
 #pragma unroll
         for (int sl = 0; sl < 4; ++sl) {
           if (sl < nslab_c) {
-            const u32x4 ak = ld16(st + sg.K + tile_off(16 * rt + lr, sl * 4 + lgp, lgC));
+            const u32x4 ak = ld16(st + offK[a][sl]);
             S[a][0] = mma_slab<T>(ak, vf[sl][0], S[a][0]);
             S[a][1] = mma_slab<T>(ak, vf[sl][1], S[a][1]);
           }
         }
         // publish S_{c+1}: ST[v][c], 4 consecutive c per lane
+        const int c4 = 16 * rt + 4 * lgp;
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct) {
           float f[4] = {S[a][ct][0], S[a][ct][1], S[a][ct][2], S[a][ct][3]};

@@ -8,75 +8,128 @@
 // Because W_o^{(i)} is linear,
 //   O_t = sum_i w_{t,i} y^{(i)}_{j_i(t)} W_o^{(i)}
 //       = [w_{t,1} y^{(1)}_{j_1(t)} | ... | w_{t,m} y^{(m)}_{j_m(t)}] [W_o^{(1)}; ...; W_o^{(m)}],
-// with j_i(t) = floor((t+1)/s_i) - 1 (a zero row when negative).  The A-operand
-// loader gathers the held coarse rows and applies the fusion weight, B is the
-// stacked W_o^T, and the epilogue writes O row-major.  Each 128-byte K segment
-// lies inside one branch (branch K ranges are padded to 128 bytes).
+// with j_i(t) = floor((t+1)/s_i) - 1 (a zero row when negative).  The A rows are
+// gathered straight from the held coarse rows by the asynchronous copies of
+// gemm_dma.hpp (a per-row source address; zeros come from a zero block), B is
+// the stacked W_o^T.  Each 128-byte K segment lies inside one head of one
+// branch, so the fusion weight is applied once per branch instead of per
+// element: the accumulators of branch i are folded into the total as
+// total += w_{t,i} * acc at the branch's last K segment.  The epilogue writes O
+// row-major.
 #include "device_common.hpp"
-#include "gemm_engine.hpp"
+#include "gemm_dma.hpp"
 #include "layout.hpp"
 
 namespace msgla {
+
+constexpr int K3_WM = 4, K3_WN = 4, K3_NST = 2;
+constexpr int K3_BM = GemmShape<K3_WM, K3_WN>::BM, K3_BN = GemmShape<K3_WM, K3_WN>::BN;
 
 template <typename T>
 struct K3Prob {
   const K3Params& P;
   int m0, n0;
-  int ab[4], at[4];  // sequence and position of each loaded A row (-1: none)
-  const T* brow[4];
-  u32x4 ra[4], rb[4];
-  float wv[4];
+  int rb[4], rt[4];            // sequence / position of the lane's copy rows (-1: none)
+  const char* brow[4];
+  const char* arow[4];         // row base of the branch currently being copied
+  int ib_issue = -1;           // branch of the K segments being copied
+  int ib_fold = 0;             // branch of the K segments being multiplied
+  f32x4 total[K3_WM][K3_WN];
 
   __device__ K3Prob(const K3Params& p, int m0_, int n0_) : P(p), m0(m0_), n0(n0_) {}
 
-  __device__ void a_setup(int i, int row) {
-    const int m = m0 + row;
-    if (m < P.B * P.L) {
-      ab[i] = m / P.L;
-      at[i] = m - ab[i] * P.L;
-    } else {
-      ab[i] = -1;
-      at[i] = 0;
+  __device__ int nk() const { return P.Ktot * (int)sizeof(T) / 128; }
+  __device__ int seg_begin(int i) const { return P.br[i].ko * (int)sizeof(T) / 128; }
+  __device__ int branch_of(int kt) const {
+    int bi = 0;
+    while (bi + 1 < P.m && kt >= seg_begin(bi + 1)) ++bi;
+    return bi;
+  }
+  __device__ void setup(int wave, int lane) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = 32 * wave + 8 * j + (lane >> 3);
+      const int m = m0 + r, n = n0 + r;
+      rb[j] = (m < P.B * P.L) ? m / P.L : -1;
+      rt[j] = (m < P.B * P.L) ? m - rb[j] * P.L : 0;
+      brow[j] = reinterpret_cast<const char*>(P.WoT) +
+                (size_t)(n < P.d ? n : 0) * P.Ktot * sizeof(T);
+    }
+    if (P.m > 1) {
+#pragma unroll
+      for (int a = 0; a < K3_WM; ++a)
+#pragma unroll
+        for (int b = 0; b < K3_WN; ++b) total[a][b] = zero4();
     }
   }
-  // gather the held coarse row (Sec. 3.3) and its fusion weight; scaled in a_get
-  __device__ void a_fetch(int i, int kt, int c16) {
-    ra[i] = zero16();
-    wv[i] = 0.f;
-    if (ab[i] < 0) return;
-    constexpr int E128 = 128 / sizeof(T);
-    const int k0 = kt * E128;
-    int bi = 0;
-    while (bi + 1 < MSGLA_MAX_BRANCHES && bi + 1 < P.m && k0 >= P.br[bi + 1].ko) ++bi;
+  // held coarse row of each copy row for branch bi (zero block before the first block)
+  __device__ void enter_branch(int bi) {
     const K3Branch& Br = P.br[bi];
-    const int j = (at[i] + 1) / Br.s - 1;
-    const int kk = k0 - Br.ko + c16 * per16<T>();
-    if (j < 0 || kk >= Br.h * P.dv) return;
-    const int hh = kk / P.dv, v = kk - hh * P.dv;
-    ra[i] = ld16(reinterpret_cast<const T*>(Br.y) + (((size_t)ab[i] * Br.h + hh) * Br.np + j) * P.dv + v);
-    wv[i] = (P.m > 1) ? P.w[((size_t)ab[i] * P.L + at[i]) * FUSION_STRIDE + bi] : 1.f;
-  }
-  __device__ u32x4 a_get(int i) {
-    if (P.m == 1) return ra[i];
-    float f[per16<T>()];
-    unpack16<T>(ra[i], f);
 #pragma unroll
-    for (int e = 0; e < per16<T>(); ++e) f[e] *= wv[i];
-    return pack16<T>(f);
+    for (int j = 0; j < 4; ++j) {
+      const int jr = (rt[j] + 1) / Br.s - 1;
+      arow[j] = (rb[j] < 0 || jr < 0)
+                    ? nullptr
+                    : reinterpret_cast<const char*>(Br.y) +
+                          ((size_t)rb[j] * Br.h * Br.np + jr) * P.dv * sizeof(T);
+    }
+    ib_issue = bi;
   }
-  __device__ void b_setup(int i, int row) {
-    const int n = n0 + row;
-    brow[i] = (n < P.d) ? reinterpret_cast<const T*>(P.WoT) + (size_t)n * P.Ktot : nullptr;
+  // per copied segment: branch (switching the held rows when it changes) and the
+  // byte offset of the segment inside a held row of that branch
+  size_t seg_off = 0;
+  __device__ void prep(int kt) {
+    const int bi = branch_of(kt);
+    if (bi != ib_issue) enter_branch(bi);
+    const int head_bytes = P.dv * (int)sizeof(T);
+    const int kb = (kt - seg_begin(bi)) * 128;  // bytes into the branch's K range
+    const int hh = kb / head_bytes;             // head of this segment
+    seg_off = (size_t)hh * P.br[bi].np * head_bytes + (kb - hh * head_bytes);
   }
-  __device__ void b_fetch(int i, int kt, int c16) {
-    rb[i] = brow[i] ? ld16(brow[i] + kt * (128 / sizeof(T)) + c16 * per16<T>()) : zero16();
+  __device__ const char* a_row(int j, int) const {
+    return arow[j] ? arow[j] + seg_off : reinterpret_cast<const char*>(P.zero);
   }
-  __device__ u32x4 b_get(int i) { return rb[i]; }
+  __device__ const char* b_row(int j, int kt) const { return brow[j] + kt * 128; }
+  __device__ bool seg_end(int kt) const {
+    return P.m > 1 && (ib_fold + 1 >= P.m ? kt + 1 == nk() : kt + 1 == seg_begin(ib_fold + 1));
+  }
+  // total += w_{row, branch} * acc for the 16 rows this lane holds; acc = 0
+  __device__ void fold(f32x4 (&acc)[K3_WM][K3_WN], int wr, int wc, int lane) {
+    const int lgrp = lane >> 4;
+#pragma unroll
+    for (int a = 0; a < K3_WM; ++a)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int m = m0 + wr * 16 * K3_WM + 16 * a + 4 * lgrp + e;
+        const float w = (m < P.B * P.L) ? P.w[(size_t)m * FUSION_STRIDE + ib_fold] : 0.f;
+#pragma unroll
+        for (int b = 0; b < K3_WN; ++b) {
+          total[a][b][e] += w * acc[a][b][e];
+          acc[a][b][e] = 0.f;
+        }
+      }
+    ++ib_fold;
+    (void)wc;
+  }
+  __device__ void finish(f32x4 (&acc)[K3_WM][K3_WN], int, int, int) {
+    if (P.m > 1) {
+#pragma unroll
+      for (int a = 0; a < K3_WM; ++a)
+#pragma unroll
+        for (int b = 0; b < K3_WN; ++b) acc[a][b] = total[a][b];
+    }
+  }
+  __device__ void store(const f32x4 (&acc)[K3_WM][K3_WN], int wr, int wc, int lane, char* lds) {
+    float* C = reinterpret_cast<float*>(lds);
+    gd_stage_tile<K3_WM, K3_WN>(acc, wr, wc, lane, C);
+    lds_barrier();
+    epilogue(C, gd_ldc<K3_WM, K3_WN>());
+  }
   __device__ void epilogue(const float* C, int ldc) {
     const int tid = threadIdx.x;
     T* out = reinterpret_cast<T*>(P.out);
-    for (int it = tid; it < GEMM_BM * (GEMM_BN / 8); it += GEMM_THREADS) {
-      const int r = it >> 4, cg = it & 15;
+    for (int it = tid; it < K3_BM * (K3_BN / 8); it += GD_THREADS) {
+      const int r = it / (K3_BN / 8), cg = it % (K3_BN / 8);
       const int m = m0 + r, col = n0 + cg * 8;
       if (m >= P.B * P.L || col >= P.d) continue;
       float v[8];
@@ -94,17 +147,17 @@ struct K3Prob {
 };
 
 template <typename T>
-__global__ __launch_bounds__(GEMM_THREADS) void k3_hold_fuse(const K3Params P) {
-  __shared__ __attribute__((aligned(16))) char lds[GEMM_LDS_BYTES];
+__global__ __launch_bounds__(GD_THREADS) void k3_hold_fuse(const K3Params P) {
+  __shared__ __attribute__((aligned(16))) char lds[gd_lds_bytes_staged<K3_WM, K3_WN, K3_NST>()];
   const int tile = remap_xcd(blockIdx.x, P.per_xcd);
   if (tile >= P.total_tiles) return;
   const int tm = tile / P.tiles_n, tn = tile - tm * P.tiles_n;
-  K3Prob<T> prob(P, tm * GEMM_BM, tn * GEMM_BN);
-  gemm_tile_128<T>(prob, P.Ktot * (int)sizeof(T) / 128, P.d - tn * GEMM_BN, lds);
+  K3Prob<T> prob(P, tm * K3_BM, tn * K3_BN);
+  gemm_dma_tile<T, K3_WM, K3_WN, K3_NST>(prob, P.d - tn * K3_BN, lds);
 }
 
 hipError_t launch_k3(const K3Params& P, bool bf16_path, hipStream_t stream) {
-  const dim3 grid(P.per_xcd * N_XCD), block(GEMM_THREADS);
+  const dim3 grid(P.per_xcd * N_XCD), block(GD_THREADS);
   if (bf16_path)
     hipLaunchKernelGGL(k3_hold_fuse<bf16>, grid, block, 0, stream, P);
   else

@@ -5,10 +5,11 @@
 // fusion logits of Eq. (10) from the unpooled x_t.
 //
 // For branch i (scale s): C_i = P_s(X) * Wp_i^T, where row (b, j) of P_s(X) is
-// the mean of X rows b*L + j*s .. + s-1 (only complete blocks), computed in
-// fp32 inside the A-operand loader and rounded once to the storage type, so
-// the pooled sequence never touches HBM (the s raw loads are issued before the
-// MFMAs of the previous K segment and summed after them).  Wp_i stacks the transposed q, k, v,
+// the mean of X rows b*L + j*s .. + s-1 (only complete blocks): X itself for
+// s = 1, otherwise the block means written by the pooling prepass (summed in
+// fp32, rounded once).  Both operands stream global -> LDS asynchronously
+// (gemm_dma.hpp), so the K loop issues no address or conversion arithmetic.
+// Wp_i stacks the transposed q, k, v,
 // first-gate-factor and (for the branch that carries them) fusion-logit
 // weights; the epilogue routes each column range to its consumer layout:
 // q, k head-major fp32 rows, v transposed per chunk, the gate factor in fp32, and
@@ -16,74 +17,48 @@
 // The work list is every (group, m-tile, n-tile), n fastest, laid out so each
 // XCD walks a contiguous range (tiles that share an A tile share an L2).
 #include "device_common.hpp"
-#include "gemm_engine.hpp"
+#include "gemm_dma.hpp"
 #include "layout.hpp"
 
 namespace msgla {
 
-template <typename T, int SMAX>
+constexpr int K1_WM = 4, K1_WN = 4, K1_NST = 2;
+constexpr int K1_BM = GemmShape<K1_WM, K1_WN>::BM, K1_BN = GemmShape<K1_WM, K1_WN>::BN;
+
+template <typename T>
 struct K1Prob {
   const K1Params& P;
   const K1Group& G;
   int m0, n0;
-  const T* arow[4];
-  const T* brow[4];
-  const T* apos[4];        // first raw row of the piece being fetched
-  u32x4 raw[4][SMAX];      // raw 16-byte pieces of the s rows of a pooled block
-  u32x4 rb[4];
-  float inv_s;
+  const char* arow[4];
+  const char* brow[4];
 
   __device__ K1Prob(const K1Params& p, const K1Group& g, int m0_, int n0_)
-      : P(p), G(g), m0(m0_), n0(n0_), inv_s(1.0f / (float)g.s) {}
+      : P(p), G(g), m0(m0_), n0(n0_) {}
 
-  __device__ void a_setup(int i, int row) {
-    const int m = m0 + row;
-    if (m < G.M) {
-      const int b = m / G.n, j = m - b * G.n;
-      arow[i] = reinterpret_cast<const T*>(P.x) + ((size_t)b * P.L + (size_t)j * G.s) * P.d;
-    } else {
-      arow[i] = nullptr;
+  __device__ int nk() const { return P.d * (int)sizeof(T) / 128; }
+  __device__ void setup(int wave, int lane) {
+    const size_t row_bytes = (size_t)P.d * sizeof(T);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = 32 * wave + 8 * j + (lane >> 3);
+      const int m = m0 + r, n = n0 + r;
+      arow[j] = reinterpret_cast<const char*>(G.A) + (size_t)(m < G.M ? m : 0) * row_bytes;
+      brow[j] = reinterpret_cast<const char*>(G.Wp) + (size_t)(n < G.N ? n : 0) * row_bytes;
     }
   }
-  // issue the loads of the s raw rows (consumed after the MFMAs in a_get)
-  __device__ void a_fetch(int i, int kt, int c16) {
-    if (!arow[i]) return;
-    const T* p = arow[i] + kt * (128 / sizeof(T)) + c16 * per16<T>();
-    apos[i] = p;
-#pragma unroll
-    for (int u = 0; u < SMAX; ++u)
-      if (u < G.s) raw[i][u] = ld16(p + (size_t)u * P.d);
+  __device__ void prep(int) {}
+  __device__ const char* a_row(int j, int kt) const { return arow[j] + kt * 128; }
+  __device__ const char* b_row(int j, int kt) const { return brow[j] + kt * 128; }
+  __device__ bool seg_end(int) const { return false; }
+  __device__ void fold(f32x4 (&)[K1_WM][K1_WN], int, int, int) {}
+  __device__ void finish(f32x4 (&)[K1_WM][K1_WN], int, int, int) {}
+  __device__ void store(const f32x4 (&acc)[K1_WM][K1_WN], int wr, int wc, int lane, char* lds) {
+    float* C = reinterpret_cast<float*>(lds);
+    gd_stage_tile<K1_WM, K1_WN>(acc, wr, wc, lane, C);
+    lds_barrier();
+    epilogue(C, gd_ldc<K1_WM, K1_WN>());
   }
-  __device__ u32x4 a_get(int i) {
-    if (!arow[i]) return zero16();
-    if (SMAX == 1 || G.s == 1) return raw[i][0];
-    float sum[per16<T>()], tmp[per16<T>()];
-    unpack16<T>(raw[i][0], sum);
-#pragma unroll
-    for (int u = 1; u < SMAX; ++u) {
-      if (u < G.s) {
-        unpack16<T>(raw[i][u], tmp);
-#pragma unroll
-        for (int e = 0; e < per16<T>(); ++e) sum[e] += tmp[e];
-      }
-    }
-    for (int u = SMAX; u < G.s; ++u) {  // blocks longer than SMAX: remaining rows now
-      unpack16<T>(ld16(apos[i] + (size_t)u * P.d), tmp);
-#pragma unroll
-      for (int e = 0; e < per16<T>(); ++e) sum[e] += tmp[e];
-    }
-#pragma unroll
-    for (int e = 0; e < per16<T>(); ++e) sum[e] *= inv_s;
-    return pack16<T>(sum);
-  }
-  __device__ void b_setup(int i, int row) {
-    const int n = n0 + row;
-    brow[i] = (n < G.N) ? reinterpret_cast<const T*>(G.Wp) + (size_t)n * P.d : nullptr;
-  }
-  __device__ void b_fetch(int i, int kt, int c16) {
-    rb[i] = brow[i] ? ld16(brow[i] + kt * (128 / sizeof(T)) + c16 * per16<T>()) : zero16();
-  }
-  __device__ u32x4 b_get(int i) { return rb[i]; }
 
   __device__ void store8(T* dst, const float* v) {
     if constexpr (sizeof(T) == 2) {
@@ -97,8 +72,8 @@ struct K1Prob {
   __device__ void epilogue(const float* C, int ldc) {
     const int tid = threadIdx.x;
     // (1) row-major destinations: q, k, gate factor, fusion weights
-    for (int it = tid; it < GEMM_BM * (GEMM_BN / 8); it += GEMM_THREADS) {
-      const int r = it >> 4, cg = it & 15;
+    for (int it = tid; it < K1_BM * (K1_BN / 8); it += GD_THREADS) {
+      const int r = it / (K1_BN / 8), cg = it % (K1_BN / 8);
       const int m = m0 + r, col = n0 + cg * 8;
       if (m >= G.M || col >= G.N) continue;
       if (col >= G.col_v && col < G.col_g) continue;  // v: transposed pass below
@@ -139,9 +114,9 @@ struct K1Prob {
       }
     }
     // (2) v, written transposed per chunk: vT[b][hh][chunk][v][tau]
-    if (G.col_g > G.col_v && n0 < G.col_g && n0 + GEMM_BN > G.col_v) {
-      for (int it = tid; it < GEMM_BN * (GEMM_BM / 8); it += GEMM_THREADS) {
-        const int cl = it & (GEMM_BN - 1), rg = it >> 7;
+    if (G.col_g > G.col_v && n0 < G.col_g && n0 + K1_BN > G.col_v) {
+      for (int it = tid; it < K1_BN * (K1_BM / 8); it += GD_THREADS) {
+        const int cl = it % K1_BN, rg = it / K1_BN;
         const int col = n0 + cl;
         if (col < G.col_v || col >= G.col_g) continue;
         const int cv = col - G.col_v;
@@ -171,9 +146,9 @@ struct K1Prob {
   }
 };
 
-template <typename T, int SMAX>
-__global__ __launch_bounds__(GEMM_THREADS) void k1_pool_proj(const K1Params P) {
-  __shared__ __attribute__((aligned(16))) char lds[GEMM_LDS_BYTES];
+template <typename T>
+__global__ __launch_bounds__(GD_THREADS) void k1_pool_proj(const K1Params P) {
+  __shared__ __attribute__((aligned(16))) char lds[gd_lds_bytes_staged<K1_WM, K1_WN, K1_NST>()];
   const int tile = remap_xcd(blockIdx.x, P.per_xcd);
   if (tile >= P.total_tiles) return;
   int gi = 0;
@@ -181,31 +156,16 @@ __global__ __launch_bounds__(GEMM_THREADS) void k1_pool_proj(const K1Params P) {
   const K1Group& G = P.g[gi];
   const int local = tile - G.tile_begin;
   const int tm = local / G.tiles_n, tn = local - tm * G.tiles_n;
-  K1Prob<T, SMAX> prob(P, G, tm * GEMM_BM, tn * GEMM_BN);
-  gemm_tile_128<T>(prob, P.d * (int)sizeof(T) / 128, G.N - tn * GEMM_BN, lds);
-}
-
-template <typename T>
-static void launch_k1_t(const K1Params& P, dim3 grid, hipStream_t stream) {
-  int smax = 1;
-  for (int g = 0; g < P.ngroups; ++g) smax = smax > P.g[g].s ? smax : P.g[g].s;
-  const dim3 block(GEMM_THREADS);
-  if (smax <= 1)
-    hipLaunchKernelGGL((k1_pool_proj<T, 1>), grid, block, 0, stream, P);
-  else if (smax <= 2)
-    hipLaunchKernelGGL((k1_pool_proj<T, 2>), grid, block, 0, stream, P);
-  else if (smax <= 4)
-    hipLaunchKernelGGL((k1_pool_proj<T, 4>), grid, block, 0, stream, P);
-  else
-    hipLaunchKernelGGL((k1_pool_proj<T, 8>), grid, block, 0, stream, P);
+  K1Prob<T> prob(P, G, tm * K1_BM, tn * K1_BN);
+  gemm_dma_tile<T, K1_WM, K1_WN, K1_NST>(prob, G.N - tn * K1_BN, lds);
 }
 
 hipError_t launch_k1(const K1Params& P, bool bf16_path, hipStream_t stream) {
-  const dim3 grid(P.per_xcd * N_XCD);
+  const dim3 grid(P.per_xcd * N_XCD), block(GD_THREADS);
   if (bf16_path)
-    launch_k1_t<bf16>(P, grid, stream);
+    hipLaunchKernelGGL(k1_pool_proj<bf16>, grid, block, 0, stream, P);
   else
-    launch_k1_t<float>(P, grid, stream);
+    hipLaunchKernelGGL(k1_pool_proj<float>, grid, block, 0, stream, P);
   return hipGetLastError();
 }
 

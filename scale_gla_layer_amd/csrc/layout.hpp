@@ -57,9 +57,23 @@ struct StateHeader {
   int64_t pos;
 };
 
+// ---------------- pooling prepass ------------------------------------------------
+struct PoolOut {
+  void* xp;         // [B][n][d] block means of scale s
+  int s, n;
+  float inv_s;
+};
+
+struct PoolParams {
+  const void* x;    // [B][L][d]
+  int B, L, d, smax, nout;
+  PoolOut out[MSGLA_MAX_BRANCHES];
+};
+
 // ---------------- K1: pooled projection GEMM (+ fusion logits) ----------------
 struct K1Group {
   const void* Wp;   // [N][d]
+  const void* A;    // A rows: x (scale 1) or the pooled block means [M][d]
   int s;            // pooling factor (1 for the fusion-only group)
   int n;            // pooled rows per sequence
   int M;            // B * n
@@ -125,6 +139,7 @@ struct K3Branch {
 
 struct K3Params {
   int B, L, d, dv, m, Ktot;
+  const void* zero; // >= 128 zero bytes (rows before a branch's first block)
   int total_tiles, tiles_n, per_xcd;
   const void* WoT;  // [d][Ktot]
   const float* w;   // fusion weights [B L][8]

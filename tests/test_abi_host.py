@@ -78,7 +78,8 @@ def _raw_cfg(**kw):
     dict(scales=(1, 2), heads=(1, 0)),            # non-positive heads
     dict(d_model=96),                             # not a multiple of 64
     dict(d_k=48),                                 # bf16 needs d_k % 32 == 0
-    dict(d_v=48),                                 # d_v % 32
+    dict(d_v=96),                                 # bf16 needs d_v % 64 == 0
+    dict(d_v=48, dtype=F32, chunk=16),            # d_v % 32
     dict(gate_rank=0),
     dict(gate_rank=65),
     dict(chunk=16),                               # bf16 chunk must be 32 or 64
