@@ -25,7 +25,6 @@ hipError_t pack_transpose(bool bf16_path, const void* src, int R, int Cn, void* 
 hipError_t pack_to_f32(bool src_bf16, const void* src, size_t n, float* dst, hipStream_t st);
 hipError_t fill_zero(void* p, size_t bytes, hipStream_t st);
 size_t k2a_lds_bytes(int C, int dk, int rp, bool bf16_path);
-size_t k2b_lds_bytes(int C, int dk, bool bf16_path);
 int k2b_dvt();
 }  // namespace msgla
 
@@ -66,7 +65,8 @@ msgla_status check_config(const msgla_config* c) {
       if (c->scale[j] == c->scale[i]) return MSGLA_ERR_INVALID_ARG;
   }
   if (c->d_model < 64 || c->d_model % 64 != 0 || c->d_model > 65536) return MSGLA_ERR_INVALID_ARG;
-  if (c->d_k < 16 || c->d_k > 256 || c->d_k % (bf ? 32 : 16) != 0) return MSGLA_ERR_INVALID_ARG;
+  // d_k: a power of two, 32 .. 256 (bf16) or 16 .. 256 (fp32)
+  if (c->d_k < (bf ? 32 : 16) || c->d_k > 256 || (c->d_k & (c->d_k - 1)) != 0) return MSGLA_ERR_INVALID_ARG;
   // a 128-byte K segment of the output projection must lie inside one head
   if (c->d_v < 32 || c->d_v > 512 || c->d_v % (bf ? 64 : 32) != 0) return MSGLA_ERR_INVALID_ARG;
   if (c->gate_rank < 1 || c->gate_rank > 64) return MSGLA_ERR_INVALID_ARG;

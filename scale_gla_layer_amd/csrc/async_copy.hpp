@@ -13,6 +13,12 @@ namespace msgla {
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
+// One 16-byte-per-lane asynchronous copy global -> LDS (a __device__ wrapper:
+// kernels that name the builtin directly get no host-side launch stub).
+__device__ __forceinline__ void dma16(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void_t*)lds, 16, 0, 0);
+}
+
 __device__ __forceinline__ int swz(int r, int c, int W) { return c ^ (r & ((W < 8 ? W : 8) - 1)); }
 
 // byte offset of piece (r, c) in a swizzled tile of W pieces per row

@@ -15,6 +15,8 @@
 // Problem class interface (A slot j of a lane copies tile row
 // ra_j = (BM / 4) wave + 8 j + lane / 8, B slot j row rb_j likewise with BN):
 //   void setup(int wave, int lane)      precompute the lane's row sources
+//   void started(char* lds)             after the first segments are in flight
+//                                        (may fill LDS beyond the NST stages)
 //   void prep(int kt)                    once per copied segment, before a_row/b_row
 //   const char* a_row(int j, int kt)    byte address of slot j's row, K segment kt
 //   const char* b_row(int j, int kt)    (valid memory even for rows outside the
@@ -105,6 +107,7 @@ __device__ __forceinline__ void gemm_dma_tile(Prob& prob, int n_valid, char* lds
   for (int b = 0; b < WN; ++b) nb_valid += (wc * 16 * WN + 16 * b < n_valid) ? 1 : 0;
 
   for (int kt = 0; kt < NST - 1 && kt < nk; ++kt) issue(kt);
+  prob.started(lds);
 
   for (int kt = 0; kt < nk; ++kt) {
     // segment kt has landed once only the copies of later segments remain

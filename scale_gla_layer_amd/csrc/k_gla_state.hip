@@ -29,22 +29,34 @@ namespace msgla {
 constexpr int K2B_THREADS = 256;
 constexpr int K2B_DVT = 32;  // d_v columns per workgroup
 
-struct K2bStage {  // byte offsets of one pipeline stage (each a multiple of 1 KB)
-  int A, Q, K, V, L, bytes;
+constexpr int k2b_kb(int b) { return (b + 1023) & ~1023; }
+constexpr int k2b_ilog2(int x) { return x <= 1 ? 0 : 1 + k2b_ilog2(x / 2); }
+
+// Compile-time geometry for chunk length C and key width DK (powers of two).
+// A pipeline stage holds, 1 KB aligned: A [C][C], qt [C][DK], kT [DK][C],
+// the chunk's V slice [DVT][C] (storage type) and lam [DK] (fp32).
+template <typename T, int C, int DK>
+struct K2bGeom {
+  static constexpr int es = sizeof(T);
+  static constexpr int NSC = C * es / 64;   // 64-byte k-slabs over positions
+  static constexpr int NSK = DK * es / 64;  // 64-byte k-slabs over key channels
+  static constexpr int NRT = DK / 16;       // 16-row tiles of the state
+  static constexpr int SRT = (NRT + 3) / 4; // state row tiles per wave
+  static constexpr int bA = C * C * es, bQ = C * DK * es, bV = K2B_DVT * C * es, bL = DK * 4;
+  static constexpr int oA = 0, oQ = k2b_kb(bA), oK = oQ + k2b_kb(bQ), oV = oK + k2b_kb(bQ),
+                       oL = oV + k2b_kb(bV), STAGE = oL + k2b_kb(bL);
+  static constexpr int nA = bA / 1024, nQ = bQ / 1024, nV = bV / 1024;  // copy instructions
+  static constexpr int lgC = k2b_ilog2(C * es), lgQ = k2b_ilog2(DK * es), lgL = k2b_ilog2(DK * 4);
+  static constexpr int LDS_S = DK + 16 / es;       // published-state row stride (elements)
+  static constexpr int LDY = K2B_DVT + 16 / es;    // y staging row stride (elements)
+  static constexpr int EXTRA = 2 * K2B_DVT * LDS_S * es + 4 * 16 * LDY * es;
+  static constexpr int NST = 3 * STAGE + EXTRA <= 160 * 1024 ? 3 : 2;
+  static constexpr int LDS = NST * STAGE + EXTRA;
+  // copies every wave issues per chunk at least (the lam copy comes on top for wave 0)
+  static constexpr int KMIN = nA / 4 + 2 * (nQ / 4) + nV / 4;
+  static_assert(bA % 1024 == 0 && bQ % 1024 == 0 && bV % 1024 == 0 && bL <= 1024, "block sizes");
+  static_assert(NSC >= 1 && NSC <= 4 && NSK >= 1 && NSK <= 16, "slab counts");
 };
-
-__host__ __device__ inline int k2b_kb(int b) { return (b + 1023) & ~1023; }
-
-__host__ __device__ inline K2bStage k2b_stage(int C, int dk, int es) {
-  K2bStage g;
-  g.A = 0;
-  g.Q = g.A + k2b_kb(C * C * es);
-  g.K = g.Q + k2b_kb(C * dk * es);
-  g.V = g.K + k2b_kb(dk * C * es);
-  g.L = g.V + k2b_kb(K2B_DVT * C * es);
-  g.bytes = g.L + k2b_kb(dk * 4);
-  return g;
-}
 
 // Per-lane source offset of copy instruction k for a contiguous block stored
 // as swizzled 128-byte virtual rows (async_copy.hpp): source = block + 1024 k
@@ -58,8 +70,9 @@ __device__ __forceinline__ int k2b_lane_off(int lg, int k, int lane) {
   return 128 * (lane >> 3) + 16 * ((lane & 7) ^ ((vrow >> hs) & 7));
 }
 
-template <typename T, int SRT, int NST>
+template <typename T, int C, int DK>
 __global__ __launch_bounds__(K2B_THREADS) void k2b_gla_state(const K2Params P) {
+  using G = K2bGeom<T, C, DK>;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int g = blockIdx.x;
   const int slot = g / N_XCD, xcd = g % N_XCD;
@@ -72,158 +85,147 @@ __global__ __launch_bounds__(K2B_THREADS) void k2b_gla_state(const K2Params P) {
   const K2Branch& Bb = P.br[bi];
   const int bh = qseq - Bb.seq_begin;  // b * h + head
 
-  constexpr int es = sizeof(T);
+  constexpr int es = G::es;
   constexpr int PER = per16<T>();
-  const int C = P.C, dk = P.dk, dv = P.dv;
+  constexpr int NST = G::NST;
+  const int dv = P.dv;
   const int v0 = tile * K2B_DVT;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 15, lgp = lane >> 4;
-  const int nrt = dk / 16;                  // state row tiles
-  const int lgC = 31 - __builtin_clz(C * es);   // log2 bytes of an A / kT / V row
-  const int lgQ = 31 - __builtin_clz(dk * es);  // log2 bytes of a qt row
-  const int lgL = 31 - __builtin_clz(dk * 4);   // lam: one row of dk floats
-  const int nslab_c = C * es / 64;          // 64-byte k-slabs over positions
-  const int nslab_k = dk * es / 64;         // 64-byte k-slabs over key channels
 
-  // LDS: NST stages | ST[2][DVT][dk + pad] (published state) | per-wave y staging
-  const K2bStage sg = k2b_stage(C, dk, es);
-  const int lds_s = dk + 16 / es;
-  T* ST = reinterpret_cast<T*>(smem + (size_t)NST * sg.bytes);
-  const int ldy = K2B_DVT + 16 / es;
-  T* ys = ST + 2 * K2B_DVT * lds_s + wave * 16 * ldy;
+  // LDS: NST stages | ST[2][DVT][DK + pad] (published state) | per-wave y staging
+  T* ST = reinterpret_cast<T*>(smem + NST * G::STAGE);
+  T* ys = ST + 2 * K2B_DVT * G::LDS_S + wave * 16 * G::LDY;
 
   const size_t chunk0 = (size_t)bh * Bb.nch;
-  const int bA = C * C * es, bQ = C * dk * es, bV = K2B_DVT * C * es, bL = dk * 4;
-  const char* Ag = reinterpret_cast<const char*>(Bb.A) + chunk0 * bA;
-  const char* Qg = reinterpret_cast<const char*>(Bb.qt) + (size_t)bh * Bb.np * dk * es;
-  const char* Kg = reinterpret_cast<const char*>(Bb.kT) + chunk0 * bQ;
+  const char* Ag = reinterpret_cast<const char*>(Bb.A) + chunk0 * G::bA;
+  const char* Qg = reinterpret_cast<const char*>(Bb.qt) + (size_t)bh * Bb.np * DK * es;
+  const char* Kg = reinterpret_cast<const char*>(Bb.kT) + chunk0 * G::bQ;
   const char* Vg = reinterpret_cast<const char*>(Bb.vT) + (chunk0 * dv + v0) * C * es;
-  const char* Lg = reinterpret_cast<const char*>(Bb.lam + chunk0 * dk);
+  const char* Lg = reinterpret_cast<const char*>(Bb.lam + chunk0 * DK);
   T* yg = reinterpret_cast<T*>(Bb.y) + (size_t)bh * Bb.np * dv + v0;
 
-  // hoisted copy offsets (one per block) and copy counts (per wave)
-  // (A, kT and V rows hold C <= 64 elements, at most 256 bytes; qt rows up to 1 KB)
-  const int oA = k2b_lane_off(lgC, wave, lane);
-  const int oQ0 = k2b_lane_off(lgQ, wave, lane), oQ1 = k2b_lane_off(lgQ, wave + 4, lane);
-  const int oL = 16 * lane;  // lam: one partial instruction, unswizzled row (key 0)
-  const int nA = (bA / 1024 + 3 - wave) / 4, nQ = (bQ / 1024 + 3 - wave) / 4;
-  const int nV = (bV / 1024 + 3 - wave) / 4;
-  const int K = nA + 2 * nQ + nV + (wave == 0 ? 1 : 0);  // copies per chunk of this wave
+  // copy offsets: one per block (two for qt rows of 1 KB), see k2b_lane_off
+  const int oA = k2b_lane_off(G::lgC, wave, lane);
+  const int oQ0 = k2b_lane_off(G::lgQ, wave, lane), oQ1 = k2b_lane_off(G::lgQ, wave + 4, lane);
+  const int oL = 16 * lane;  // lam: one partial instruction of one virtual row (key 0)
   auto issue = [&](int c) {
-    char* st = smem + (size_t)(c % NST) * sg.bytes;
-    const char* a = Ag + (size_t)c * bA;
-    const char* q = Qg + (size_t)c * bQ;
-    const char* kk = Kg + (size_t)c * bQ;
+    char* st = smem + (c % NST) * G::STAGE;
+    const char* a = Ag + (size_t)c * G::bA;
+    const char* q = Qg + (size_t)c * G::bQ;
+    const char* kk = Kg + (size_t)c * G::bQ;
     const char* v = Vg + (size_t)c * dv * C * es;
-    for (int i = 0; i < nA; ++i) {
+#pragma unroll
+    for (int i = 0; i < (G::nA + 3) / 4; ++i) {
       const int k = wave + 4 * i;
-      __builtin_amdgcn_global_load_lds(a + 1024 * k + oA, (lds_void_t*)(st + sg.A + 1024 * k), 16, 0, 0);
+      if (k < G::nA)
+        dma16(a + 1024 * k + oA, st + G::oA + 1024 * k);
     }
-    for (int i = 0; i < nQ; ++i) {
+#pragma unroll
+    for (int i = 0; i < (G::nQ + 3) / 4; ++i) {
       const int k = wave + 4 * i;
-      __builtin_amdgcn_global_load_lds(q + 1024 * k + ((i & 1) ? oQ1 : oQ0),
-                                       (lds_void_t*)(st + sg.Q + 1024 * k), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(kk + 1024 * k + oA, (lds_void_t*)(st + sg.K + 1024 * k), 16, 0, 0);
+      if (k < G::nQ) {
+        dma16(q + 1024 * k + ((i & 1) ? oQ1 : oQ0), st + G::oQ + 1024 * k);
+        dma16(kk + 1024 * k + oA, st + G::oK + 1024 * k);
+      }
     }
-    for (int i = 0; i < nV; ++i) {
+#pragma unroll
+    for (int i = 0; i < (G::nV + 3) / 4; ++i) {
       const int k = wave + 4 * i;
-      __builtin_amdgcn_global_load_lds(v + 1024 * k + oA, (lds_void_t*)(st + sg.V + 1024 * k), 16, 0, 0);
+      if (k < G::nV)
+        dma16(v + 1024 * k + oA, st + G::oV + 1024 * k);
     }
-    if (wave == 0) {
-      if (oL < bL)
-        __builtin_amdgcn_global_load_lds(Lg + (size_t)c * bL + oL, (lds_void_t*)(st + sg.L), 16, 0, 0);
-    }
+    if (wave == 0 && oL < G::bL)
+      dma16(Lg + (size_t)c * G::bL + oL, st + G::oL);
   };
 
-  // hoisted LDS fragment offsets (inside a stage)
-  int offV[4][2], offA[4], offK[SRT][4], offQ[16];
+  // LDS fragment offsets inside a stage
+  int offV[G::NSC][2], offA[G::NSC], offK[G::SRT][G::NSC], offQ[G::NSK], offL[G::SRT];
 #pragma unroll
-  for (int sl = 0; sl < 4; ++sl) {
-    offV[sl][0] = sg.V + tile_off(lr, sl * 4 + lgp, lgC);
-    offV[sl][1] = sg.V + tile_off(16 + lr, sl * 4 + lgp, lgC);
-    offA[sl] = sg.A + tile_off(16 * wave + lr, sl * 4 + lgp, lgC);
+  for (int sl = 0; sl < G::NSC; ++sl) {
+    offV[sl][0] = G::oV + tile_off(lr, sl * 4 + lgp, G::lgC);
+    offV[sl][1] = G::oV + tile_off(16 + lr, sl * 4 + lgp, G::lgC);
+    offA[sl] = G::oA + tile_off(16 * wave + lr, sl * 4 + lgp, G::lgC);
 #pragma unroll
-    for (int a = 0; a < SRT; ++a) offK[a][sl] = sg.K + tile_off(16 * (wave + 4 * a) + lr, sl * 4 + lgp, lgC);
+    for (int a = 0; a < G::SRT; ++a) offK[a][sl] = G::oK + tile_off(16 * (wave + 4 * a) + lr, sl * 4 + lgp, G::lgC);
   }
 #pragma unroll
-  for (int sl = 0; sl < 16; ++sl) offQ[sl] = sg.Q + tile_off(16 * wave + lr, sl * 4 + lgp, lgQ);
-  int offL[SRT];
+  for (int sl = 0; sl < G::NSK; ++sl) offQ[sl] = G::oQ + tile_off(16 * wave + lr, sl * 4 + lgp, G::lgQ);
 #pragma unroll
-  for (int a = 0; a < SRT; ++a) offL[a] = sg.L + tile_off(0, (16 * (wave + 4 * a) + 4 * lgp) >> 2, lgL);
+  for (int a = 0; a < G::SRT; ++a) offL[a] = G::oL + tile_off(0, (16 * (wave + 4 * a) + 4 * lgp) >> 2, G::lgL);
 
-  f32x4 S[SRT][2];
+  f32x4 S[G::SRT][2];
 #pragma unroll
-  for (int a = 0; a < SRT; ++a) S[a][0] = S[a][1] = zero4();
+  for (int a = 0; a < G::SRT; ++a) S[a][0] = S[a][1] = zero4();
 
   for (int c = 0; c < NST - 1 && c < Bb.nch; ++c) issue(c);
-  for (int i = tid; i < K2B_DVT * lds_s; i += K2B_THREADS) ST[i] = from_f32<T>(0.f);
+  for (int i = tid; i < K2B_DVT * G::LDS_S; i += K2B_THREADS) ST[i] = from_f32<T>(0.f);
 
   for (int c = 0; c < Bb.nch; ++c) {
-    // stage c must have landed: with one later stage in flight at most K more
-    // copies may be outstanding (stores issued since only add to that count)
-    if (NST > 2 && c + 1 < Bb.nch && K >= 8)
-      wait_vmcnt<8>();
+    // stage c must have landed: every wave issued at least KMIN copies of the
+    // next stage after it (and any stores since only add to that count)
+    if (NST > 2 && G::KMIN > 0 && c + 1 < Bb.nch)
+      wait_vmcnt<(G::KMIN < 63 ? G::KMIN : 63)>();
     else
       wait_vmcnt<0>();
     lds_barrier();
     if (c + NST - 1 < Bb.nch) issue(c + NST - 1);
 
-    const char* st = smem + (size_t)(c % NST) * sg.bytes;
-    const T* Sb = ST + (c & 1) * K2B_DVT * lds_s;
-    T* Sn = ST + ((c + 1) & 1) * K2B_DVT * lds_s;
+    const char* st = smem + (c % NST) * G::STAGE;
+    const T* Sb = ST + (c & 1) * K2B_DVT * G::LDS_S;
+    T* Sn = ST + ((c + 1) & 1) * K2B_DVT * G::LDS_S;
     const int valid = min(C, Bb.n - c * C);
 
     // V fragments (B-operand of both products); positions >= valid zeroed
-    u32x4 vf[4][2];
+    u32x4 vf[G::NSC][2];
 #pragma unroll
-    for (int sl = 0; sl < 4; ++sl)
-      if (sl < nslab_c) {
-        vf[sl][0] = ld16(st + offV[sl][0]);
-        vf[sl][1] = ld16(st + offV[sl][1]);
-      }
+    for (int sl = 0; sl < G::NSC; ++sl) {
+      vf[sl][0] = ld16(st + offV[sl][0]);
+      vf[sl][1] = ld16(st + offV[sl][1]);
+    }
     if (valid < C) {
 #pragma unroll
-      for (int sl = 0; sl < 4; ++sl)
+      for (int sl = 0; sl < G::NSC; ++sl)
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct) {
-          if (sl < nslab_c) {
-            const int tau0 = (sl * 4 + lgp) * PER;
-            float u[PER];
-            unpack16<T>(vf[sl][ct], u);
+          const int tau0 = (sl * 4 + lgp) * PER;
+          float u[PER];
+          unpack16<T>(vf[sl][ct], u);
 #pragma unroll
-            for (int e = 0; e < PER; ++e)
-              if (tau0 + e >= valid) u[e] = 0.f;
-            vf[sl][ct] = pack16<T>(u);
-          }
+          for (int e = 0; e < PER; ++e)
+            if (tau0 + e >= valid) u[e] = 0.f;
+          vf[sl][ct] = pack16<T>(u);
         }
     }
 
     // ---- y rows 16w .. 16w+15: y = A V + qt S, staged for 16-byte stores ----
     if (wave < C / 16) {
-      const int rt = wave;
+      u32x4 af[G::NSC], qf[G::NSK], sf[G::NSK][2];
+#pragma unroll
+      for (int sl = 0; sl < G::NSC; ++sl) af[sl] = ld16(st + offA[sl]);
+#pragma unroll
+      for (int sl = 0; sl < G::NSK; ++sl) {
+        qf[sl] = ld16(st + offQ[sl]);
+        const T* srow = Sb + lr * G::LDS_S + sl * slab_elems<T>() + lgp * PER;
+        sf[sl][0] = ld16(srow);
+        sf[sl][1] = ld16(srow + 16 * G::LDS_S);
+      }
       f32x4 y[2] = {zero4(), zero4()};
 #pragma unroll
-      for (int sl = 0; sl < 4; ++sl) {
-        if (sl < nslab_c) {
-          const u32x4 a = ld16(st + offA[sl]);
-          y[0] = mma_slab<T>(a, vf[sl][0], y[0]);
-          y[1] = mma_slab<T>(a, vf[sl][1], y[1]);
-        }
+      for (int sl = 0; sl < G::NSC; ++sl) {
+        y[0] = mma_slab<T>(af[sl], vf[sl][0], y[0]);
+        y[1] = mma_slab<T>(af[sl], vf[sl][1], y[1]);
       }
 #pragma unroll
-      for (int sl = 0; sl < 16; ++sl) {
-        if (sl < nslab_k) {
-          const u32x4 a = ld16(st + offQ[sl]);
-          const T* srow = Sb + lr * lds_s + sl * slab_elems<T>() + lgp * PER;
-          y[0] = mma_slab<T>(a, ld16(srow), y[0]);
-          y[1] = mma_slab<T>(a, ld16(srow + 16 * lds_s), y[1]);
-        }
+      for (int sl = 0; sl < G::NSK; ++sl) {
+        y[0] = mma_slab<T>(qf[sl], sf[sl][0], y[0]);
+        y[1] = mma_slab<T>(qf[sl], sf[sl][1], y[1]);
       }
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) ys[(4 * lgp + e) * ldy + 16 * ct + lr] = from_f32<T>(y[ct][e]);
+        for (int e = 0; e < 4; ++e) ys[(4 * lgp + e) * G::LDY + 16 * ct + lr] = from_f32<T>(y[ct][e]);
       asm volatile("" ::: "memory");
       __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (0 << 8));  // own LDS writes done
       asm volatile("" ::: "memory");
@@ -233,15 +235,18 @@ __global__ __launch_bounds__(K2B_THREADS) void k2b_gla_state(const K2Params P) {
       for (int p0 = 0; p0 < 16 * PR; p0 += 64) {
         const int p = p0 + lane;
         const int row = p / PR, pc = p - row * PR;
-        if (p < 16 * PR && 16 * rt + row < valid)
-          st16(yg + ((size_t)c * C + 16 * rt + row) * dv + pc * PER, ld16(ys + row * ldy + pc * PER));
+        if (p < 16 * PR && 16 * wave + row < valid)
+          st16(yg + ((size_t)c * C + 16 * wave + row) * dv + pc * PER, ld16(ys + row * G::LDY + pc * PER));
       }
     }
     // ---- state update: S = Diag(lam) S + kT V for the rows this wave owns ----
 #pragma unroll
-    for (int a = 0; a < SRT; ++a) {
+    for (int a = 0; a < G::SRT; ++a) {
       const int rt = wave + 4 * a;
-      if (rt < nrt) {
+      if (rt < G::NRT) {
+        u32x4 kf[G::NSC];
+#pragma unroll
+        for (int sl = 0; sl < G::NSC; ++sl) kf[sl] = ld16(st + offK[a][sl]);
         const f32x4 l4 = __builtin_bit_cast(f32x4, ld16(st + offL[a]));
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -249,19 +254,16 @@ __global__ __launch_bounds__(K2B_THREADS) void k2b_gla_state(const K2Params P) {
           S[a][1][e] *= l4[e];
         }
 #pragma unroll
-        for (int sl = 0; sl < 4; ++sl) {
-          if (sl < nslab_c) {
-            const u32x4 ak = ld16(st + offK[a][sl]);
-            S[a][0] = mma_slab<T>(ak, vf[sl][0], S[a][0]);
-            S[a][1] = mma_slab<T>(ak, vf[sl][1], S[a][1]);
-          }
+        for (int sl = 0; sl < G::NSC; ++sl) {
+          S[a][0] = mma_slab<T>(kf[sl], vf[sl][0], S[a][0]);
+          S[a][1] = mma_slab<T>(kf[sl], vf[sl][1], S[a][1]);
         }
         // publish S_{c+1}: ST[v][c], 4 consecutive c per lane
         const int c4 = 16 * rt + 4 * lgp;
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct) {
           float f[4] = {S[a][ct][0], S[a][ct][1], S[a][ct][2], S[a][ct][3]};
-          T* dst = Sn + (16 * ct + lr) * lds_s + c4;
+          T* dst = Sn + (16 * ct + lr) * G::LDS_S + c4;
           if constexpr (sizeof(T) == 2)
             st8(dst, pack8<T>(f));
           else
@@ -272,11 +274,11 @@ __global__ __launch_bounds__(K2B_THREADS) void k2b_gla_state(const K2Params P) {
   }
 
   if (Bb.S_out) {
-    float* So = Bb.S_out + (size_t)bh * dk * dv;
+    float* So = Bb.S_out + (size_t)bh * DK * dv;
 #pragma unroll
-    for (int a = 0; a < SRT; ++a) {
+    for (int a = 0; a < G::SRT; ++a) {
       const int rt = wave + 4 * a;
-      if (rt < nrt) {
+      if (rt < G::NRT) {
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
@@ -287,51 +289,42 @@ __global__ __launch_bounds__(K2B_THREADS) void k2b_gla_state(const K2Params P) {
   }
 }
 
-static size_t k2b_lds(int C, int dk, int es, int nst) {
-  return (size_t)nst * k2b_stage(C, dk, es).bytes + (size_t)2 * K2B_DVT * (dk + 16 / es) * es +
-         (size_t)4 * 16 * (K2B_DVT + 16 / es) * es;
+template <typename T, int C, int DK>
+static void launch_k2b_cd(const K2Params& P, dim3 grid, hipStream_t stream) {
+  using G = K2bGeom<T, C, DK>;
+  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k2b_gla_state<T, C, DK>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, G::LDS);
+  hipLaunchKernelGGL((k2b_gla_state<T, C, DK>), grid, dim3(K2B_THREADS), G::LDS, stream, P);
 }
 
-size_t k2b_lds_bytes(int C, int dk, bool bf16_path) {
-  const int es = bf16_path ? 2 : 4;
-  return k2b_lds(C, dk, es, k2b_lds(C, dk, es, 3) <= 160 * 1024 ? 3 : 2);
+template <typename T, int C>
+static bool launch_k2b_c(const K2Params& P, dim3 grid, hipStream_t stream) {
+  switch (P.dk) {
+    case 16: if constexpr (sizeof(T) == 4) { launch_k2b_cd<T, C, 16>(P, grid, stream); return true; } return false;
+    case 32: launch_k2b_cd<T, C, 32>(P, grid, stream); return true;
+    case 64: launch_k2b_cd<T, C, 64>(P, grid, stream); return true;
+    case 128: launch_k2b_cd<T, C, 128>(P, grid, stream); return true;
+    case 256: launch_k2b_cd<T, C, 256>(P, grid, stream); return true;
+    default: return false;
+  }
+}
+
+template <typename T>
+static bool launch_k2b_t(const K2Params& P, dim3 grid, hipStream_t stream) {
+  switch (P.C) {
+    case 16: if constexpr (sizeof(T) == 4) return launch_k2b_c<T, 16>(P, grid, stream); return false;
+    case 32: return launch_k2b_c<T, 32>(P, grid, stream);
+    case 64: return launch_k2b_c<T, 64>(P, grid, stream);
+    default: return false;
+  }
 }
 
 int k2b_dvt() { return K2B_DVT; }
 
-template <typename T, int SRT, int NST>
-static void launch_k2b_n(const K2Params& P, dim3 grid, size_t lds, hipStream_t stream) {
-  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k2b_gla_state<T, SRT, NST>),
-                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  hipLaunchKernelGGL((k2b_gla_state<T, SRT, NST>), grid, dim3(K2B_THREADS), lds, stream, P);
-}
-
-template <typename T, int SRT>
-static void launch_k2b_s(const K2Params& P, dim3 grid, hipStream_t stream) {
-  const int es = sizeof(T);
-  if (k2b_lds(P.C, P.dk, es, 3) <= 160 * 1024)
-    launch_k2b_n<T, SRT, 3>(P, grid, k2b_lds(P.C, P.dk, es, 3), stream);
-  else
-    launch_k2b_n<T, SRT, 2>(P, grid, k2b_lds(P.C, P.dk, es, 2), stream);
-}
-
-template <typename T>
-static void launch_k2b_t(const K2Params& P, dim3 grid, hipStream_t stream) {
-  const int nrt = P.dk / 16;
-  if (nrt <= 4)
-    launch_k2b_s<T, 1>(P, grid, stream);
-  else if (nrt <= 8)
-    launch_k2b_s<T, 2>(P, grid, stream);
-  else
-    launch_k2b_s<T, 4>(P, grid, stream);
-}
-
 hipError_t launch_k2b(const K2Params& P, bool bf16_path, hipStream_t stream) {
   const dim3 grid(((P.total_seqs + N_XCD - 1) / N_XCD) * N_XCD * P.n_dvt);
-  if (bf16_path)
-    launch_k2b_t<bf16>(P, grid, stream);
-  else
-    launch_k2b_t<float>(P, grid, stream);
+  const bool ok = bf16_path ? launch_k2b_t<bf16>(P, grid, stream) : launch_k2b_t<float>(P, grid, stream);
+  if (!ok) return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

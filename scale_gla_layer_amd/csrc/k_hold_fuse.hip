@@ -24,6 +24,12 @@ namespace msgla {
 
 constexpr int K3_WM = 4, K3_WN = 4, K3_NST = 2;
 constexpr int K3_BM = GemmShape<K3_WM, K3_WN>::BM, K3_BN = GemmShape<K3_WM, K3_WN>::BN;
+// the tile's fusion weights [BM][FUSION_STRIDE] fp32 live in LDS after the stages
+constexpr int K3_W_OFF = gd_lds_bytes<K3_WM, K3_WN, K3_NST>();
+constexpr int K3_LDS = gd_lds_bytes_staged<K3_WM, K3_WN, K3_NST>() > K3_W_OFF + K3_BM * FUSION_STRIDE * 4
+                           ? gd_lds_bytes_staged<K3_WM, K3_WN, K3_NST>()
+                           : K3_W_OFF + K3_BM * FUSION_STRIDE * 4;
+static_assert(K3_BM * FUSION_STRIDE * 4 == GD_THREADS * 16, "one 16-byte piece per thread");
 
 template <typename T>
 struct K3Prob {
@@ -35,6 +41,7 @@ struct K3Prob {
   int ib_issue = -1;           // branch of the K segments being copied
   int ib_fold = 0;             // branch of the K segments being multiplied
   f32x4 total[K3_WM][K3_WN];
+  const float* wl = nullptr;   // LDS copy of the tile's fusion weights
 
   __device__ K3Prob(const K3Params& p, int m0_, int n0_) : P(p), m0(m0_), n0(n0_) {}
 
@@ -61,6 +68,19 @@ struct K3Prob {
 #pragma unroll
         for (int b = 0; b < K3_WN; ++b) total[a][b] = zero4();
     }
+  }
+  // stage the tile's fusion weights (consumed by fold, which runs after at
+  // least one LDS barrier of the K loop; the final staging of the output
+  // overwrites them only after the last fold)
+  __device__ void started(char* lds) {
+    float* w = reinterpret_cast<float*>(lds + K3_W_OFF);
+    if (P.m > 1) {
+      const int tid = threadIdx.x;
+      const int r = tid / (FUSION_STRIDE / 4), m = m0 + r;
+      st16(w + 4 * tid, m < P.B * P.L ? ld16(P.w + (size_t)m * FUSION_STRIDE + 4 * (tid % (FUSION_STRIDE / 4)))
+                                       : zero16());
+    }
+    wl = w;
   }
   // held coarse row of each copy row for branch bi (zero block before the first block)
   __device__ void enter_branch(int bi) {
@@ -100,8 +120,7 @@ struct K3Prob {
     for (int a = 0; a < K3_WM; ++a)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int m = m0 + wr * 16 * K3_WM + 16 * a + 4 * lgrp + e;
-        const float w = (m < P.B * P.L) ? P.w[(size_t)m * FUSION_STRIDE + ib_fold] : 0.f;
+        const float w = wl[(wr * 16 * K3_WM + 16 * a + 4 * lgrp + e) * FUSION_STRIDE + ib_fold];
 #pragma unroll
         for (int b = 0; b < K3_WN; ++b) {
           total[a][b][e] += w * acc[a][b][e];
@@ -147,8 +166,8 @@ struct K3Prob {
 };
 
 template <typename T>
-__global__ __launch_bounds__(GD_THREADS) void k3_hold_fuse(const K3Params P) {
-  __shared__ __attribute__((aligned(16))) char lds[gd_lds_bytes_staged<K3_WM, K3_WN, K3_NST>()];
+__global__ __launch_bounds__(GD_THREADS) __attribute__((amdgpu_waves_per_eu(2))) void k3_hold_fuse(const K3Params P) {
+  __shared__ __attribute__((aligned(16))) char lds[K3_LDS];
   const int tile = remap_xcd(blockIdx.x, P.per_xcd);
   if (tile >= P.total_tiles) return;
   const int tm = tile / P.tiles_n, tn = tile - tm * P.tiles_n;

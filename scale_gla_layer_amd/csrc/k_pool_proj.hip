@@ -47,6 +47,7 @@ struct K1Prob {
       brow[j] = reinterpret_cast<const char*>(G.Wp) + (size_t)(n < G.N ? n : 0) * row_bytes;
     }
   }
+  __device__ void started(char*) {}
   __device__ void prep(int) {}
   __device__ const char* a_row(int j, int kt) const { return arow[j] + kt * 128; }
   __device__ const char* b_row(int j, int kt) const { return brow[j] + kt * 128; }

@@ -77,7 +77,10 @@ def _raw_cfg(**kw):
     dict(scales=(0, 2), heads=(1, 1)),            # non-positive scale
     dict(scales=(1, 2), heads=(1, 0)),            # non-positive heads
     dict(d_model=96),                             # not a multiple of 64
-    dict(d_k=48),                                 # bf16 needs d_k % 32 == 0
+    dict(d_k=48),                                 # d_k must be a power of two
+    dict(d_k=96),
+    dict(d_k=16),                                 # bf16 needs d_k >= 32
+    dict(d_k=512),
     dict(d_v=96),                                 # bf16 needs d_v % 64 == 0
     dict(d_v=48, dtype=F32, chunk=16),            # d_v % 32
     dict(gate_rank=0),
