@@ -24,7 +24,6 @@ hipError_t pack_transpose(bool bf16_path, const void* src, int R, int Cn, void* 
                           size_t dst_ld, hipStream_t st);
 hipError_t pack_to_f32(bool src_bf16, const void* src, size_t n, float* dst, hipStream_t st);
 hipError_t fill_zero(void* p, size_t bytes, hipStream_t st);
-size_t k2a_lds_bytes(int C, int dk, int rp, bool bf16_path);
 int k2b_dvt();
 }  // namespace msgla
 

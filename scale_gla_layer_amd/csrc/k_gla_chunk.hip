@@ -15,31 +15,31 @@
 //   qt    = q ⊙ e^{b}          (inter-chunk query)
 //   kT    = (k ⊙ e^{b_last - b})^T             (state-update key, transposed)
 //   A     = [sum_c q_tc k_ic e^{b_tc - b_ic}]_{t >= i}   (zero above the diagonal)
+// b is kept in base-2 units (log2 alpha), so every decay factor is one exp2.
 // q and k arrive in fp32 (a single q_t . k_i can cancel strongly, and A scales
-// whole output rows), A is formed with a split-bf16 product (hi*hi + hi*lo +
-// lo*hi, ~16 mantissa bits) and rounded once to the storage type.
+// whole output rows); for bf16 storage A is formed with a split-bf16 product
+// (hi*hi + hi*lo + lo*hi, ~16 mantissa bits) and rounded once.
 // Every exponent used is <= 0 except one bounded by 15 positions of decay:
-// A is built from 16-row sub-blocks with the reference point at the first row
-// 16T of the query sub-block T:  q_t e^{b_t - b_16T} (<= 1), k_i e^{b_16J - b_i}
-// (growth over < 16 positions inside key sub-block J) and
-// D_TJ = e^{b_16T - b_16J} (<= 1) for J < T; on the diagonal D = 1 and the mask
-// selects t >= i.  Rows beyond the sequence end are treated as q = k = 0 and
-// log alpha = 0, which leaves the state untouched.
+// the 16 x 16 block A[T][J] (query tile T, key tile J <= T) is built as
+// (q_t e^{b_t - b_16J}) . (k_i e^{b_16J - b_i}); the query factor is <= 1 and
+// the key factor grows over less than 16 positions.  Rows beyond the sequence
+// end are treated as q = k = 0 and log alpha = 0, which leaves the state
+// untouched.
 //
-// Layout of the work: the gate pre-activation z^T = W_g2^T (xp W_g1)^T of the
-// chunk comes from fp32 MFMA, so lane l of a wave holds channels 4(l/16)+i of a
-// 16-channel tile for position 16 ct + l%16 of each 16-position tile ct.  The
-// cumulative sum over positions is then a DPP prefix scan inside each 16-lane
-// row plus a carry across the position tiles, all in registers; the decay
-// factors and the scaled q / k are formed in the same layout.  Wave J then
-// computes the 16 x 16 blocks A[T][J], T >= J, with MFMA as (k-side)(q-side)^T
-// so that each lane holds 4 consecutive keys of one query row.
+// Work layout: wave w owns the 16 positions 16w .. 16w+15 of the chunk and all
+// key channels.  Its gate pre-activations z^T = W_g2^T (xp W_g1)^T come from
+// fp32 MFMA, so lane l holds channels 16 rt + 4 (l/16) + i of position
+// 16 w + l % 16 for every channel tile rt.  The cumulative sum over positions
+// is a DPP prefix scan inside each 16-lane row; the waves then exchange their
+// totals (and first values) through LDS.  The key side of A goes to LDS, the
+// query side stays in registers, and wave w forms the blocks A[w][J], J <= w,
+// with MFMA as (key side)(query side)^T so that each lane holds 4 consecutive
+// keys of one query row.  All shapes are compile-time (chunk C, key width DK,
+// padded gate rank RP), so every loop unrolls.
 #include "device_common.hpp"
 #include "layout.hpp"
 
 namespace msgla {
-
-constexpr int K2A_THREADS = 256;
 
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float x) {
@@ -56,16 +56,43 @@ __device__ __forceinline__ float row_scan16(float x) {
   return x;
 }
 
-// value of lane (l & ~15) | src of the caller's 16-lane row
-__device__ __forceinline__ float row_bcast(float x, int lane, int src) {
-  return __shfl(x, (lane & ~15) | src, WAVE);
+constexpr float K2A_LOG2E = 1.4426950408889634f;
+
+// log2(sigmoid(z)) = min(z, 0) log2(e) - log2(1 + u), u = e^{-|z|} in (0, 1].
+// log2(1 + u) is taken as log2(v) with v = 1 + u rounded, plus the first-order
+// correction (u - (v - 1)) / (v ln 2) for that rounding, so small u keep
+// their relative accuracy.
+__device__ __forceinline__ float log2sigmoid(float z) {
+  const float u = __builtin_amdgcn_exp2f(-fabsf(z) * K2A_LOG2E);
+  const float v = 1.f + u;
+  const float corr = (u - (v - 1.f)) * __builtin_amdgcn_rcpf(v) * K2A_LOG2E;
+  return fminf(z, 0.f) * K2A_LOG2E - (__builtin_amdgcn_logf(v) + corr);
 }
 
-constexpr int K2A_SRT = 4;  // channel tiles per wave (d_k <= 256)
-constexpr int K2A_PT = 4;   // position tiles (C <= 64)
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
-template <typename T, int RP>
-__global__ __launch_bounds__(K2A_THREADS) void k2a_gla_chunk(const K2Params P) {
+template <typename T, int C, int DK>
+struct K2aGeom {
+  static constexpr int NW = C / 16;            // waves, one per 16-position tile
+  static constexpr int NT = DK / 16;           // 16-channel tiles
+  static constexpr int THREADS = 64 * NW;
+  static constexpr bool BF = sizeof(T) == 2;
+  // key-side rows in LDS (per plane: hi and lo for bf16, one fp32 plane otherwise),
+  // padded by 16 bytes against bank conflicts between rows
+  static constexpr int KROW = (BF ? DK * 2 : DK * 4) + 16;
+  static constexpr int XCH = 3 * NW * DK * 4;  // wave totals, first values, references
+  static constexpr int KS = (BF ? 2 : 1) * C * KROW;
+  static constexpr int LDT = C + 16 / (int)sizeof(T);  // kT staging row stride (elements)
+  static constexpr int KTS = DK * LDT * (int)sizeof(T);
+  static constexpr int LDS = XCH + KS + KTS;
+  static_assert(C == 16 || C == 32 || C == 64, "chunk");
+  static_assert(BF ? (DK >= 32 && DK % 32 == 0) : (DK >= 16 && DK % 16 == 0), "key width");
+};
+
+template <typename T, int C, int DK, int RP>
+__global__ __launch_bounds__(256) void k2a_gla_chunk(const K2Params P) {
+  using G = K2aGeom<T, C, DK>;
+  constexpr int NW = G::NW, NT = G::NT;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int unit = blockIdx.x;
   int bi = 0;
@@ -76,233 +103,228 @@ __global__ __launch_bounds__(K2A_THREADS) void k2a_gla_chunk(const K2Params P) {
   const int bh = local / Bb.nch;  // b * h + head
   const int b = bh / Bb.h, hh = bh - b * Bb.h;
 
-  const int C = P.C, dk = P.dk;
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 15, lg = lane >> 4;
-  const int row0 = chunk * C;                       // first pooled row of the chunk
-  const int valid = min(C, Bb.n - row0);            // real rows in this chunk
-  const int nsub = C / 16;                          // 16-position tiles
-  const int nrt = dk / 16;                          // 16-channel tiles
+  const int row0 = chunk * C;                  // first pooled row of the chunk
+  const int valid = min(C, Bb.n - row0);       // real rows in this chunk
+  const int p = 16 * w + lr;                   // this lane's position in the chunk
+  const bool live = p < valid;
 
-  // LDS: qs, ks fp32 [C][dk+4] | D fp32 [4][4][dk] | kTs T [dk][C+pad]
-  //      (phase 0 keeps the gate factor [C][RP] and W2 [RP][dk] where kTs goes)
-  const int ldq = dk + 4;
-  const int ldt = C + 16 / (int)sizeof(T);
-  float* qs = reinterpret_cast<float*>(smem);
-  float* ks = qs + (size_t)C * ldq;
-  float* Dm = ks + (size_t)C * ldq;
-  T* kTs = reinterpret_cast<T*>(Dm + 16 * dk);
-  float* gs = reinterpret_cast<float*>(kTs);
-  float* w2s = gs + C * RP;
+  float* tot = reinterpret_cast<float*>(smem);  // [NW][DK] wave totals of log2 alpha
+  float* first = tot + NW * DK;                 // [NW][DK] value at each wave's first row
+  float* brf = first + NW * DK;                 // [NW][DK] b at each wave's first row
+  char* ks = smem + G::XCH;                     // key side [C][KROW] (x2 planes for bf16)
+  T* kTs = reinterpret_cast<T*>(smem + G::XCH + G::KS);
 
   const size_t seq_row = (size_t)bh * Bb.np + row0;  // row index in [B][h][np]
-  const float* qg = Bb.q + seq_row * dk;
-  const float* kg = Bb.k + seq_row * dk;
-  T* qtg = reinterpret_cast<T*>(Bb.qt) + seq_row * dk;
-  T* kTg = reinterpret_cast<T*>(Bb.kT) + ((size_t)bh * Bb.nch + chunk) * dk * C;
-  float* lamg = Bb.lam + ((size_t)bh * Bb.nch + chunk) * dk;
-  const int hdk = Bb.h * dk;
 
-  // ---- phase 0: stage the gate factor rows and this head's W2 slice ----
+  // ---- operands of this lane's position: q, k (4 channels per tile), gate factor ----
+  float qv[NT][4], kv[NT][4], gb[RP / 4];
   {
-    const float* gsrc = Bb.g + ((size_t)b * Bb.np + row0) * RP;
-    for (int p = tid; p < C * RP / 4; p += K2A_THREADS) {
-      const int t = (p * 4) / RP;
-      st16(gs + p * 4, t < valid ? ld16(gsrc + p * 4) : zero16());
+    const float* qg = Bb.q + (seq_row + p) * DK + 4 * lg;
+    const float* kg = Bb.k + (seq_row + p) * DK + 4 * lg;
+    const float* gr = Bb.g + ((size_t)b * Bb.np + row0 + p) * RP + lg;
+#pragma unroll
+    for (int rt = 0; rt < NT; ++rt) {
+      unpack16<float>(live ? ld16(qg + 16 * rt) : zero16(), qv[rt]);
+      unpack16<float>(live ? ld16(kg + 16 * rt) : zero16(), kv[rt]);
     }
-    for (int p = tid; p < RP * dk / 4; p += K2A_THREADS) {
-      const int r = (p * 4) / dk, c = p * 4 - r * dk;
-      st16(w2s + p * 4, ld16(Bb.W2 + (size_t)r * hdk + hh * dk + c));
-    }
+#pragma unroll
+    for (int k4 = 0; k4 < RP / 4; ++k4) gb[k4] = live ? gr[4 * k4] : 0.f;
   }
-  __syncthreads();
 
-  // ---- phase 1a: z^T[c][t] = sum_r W2[r][c] g[t][r] (fp32 MFMA), then log alpha ----
-  // register z[a][ct][i]: channel c = 16 (wave + 4a) + 4 lg + i, position t = 16 ct + lr
-  float x[K2A_SRT][K2A_PT][4];
+  // ---- z^T[c][t] = sum_r W2[r][c] g[t][r] (fp32 MFMA), then log2 alpha and its scan ----
+  float x[NT][4];
+  {
+    const int hdk = Bb.h * DK;
+    const float* w2 = Bb.W2 + hh * DK + lr;
+    const float scale = P.inv_gamma;
 #pragma unroll
-  for (int a = 0; a < K2A_SRT; ++a) {
-    const int rt = wave + 4 * a;
-#pragma unroll
-    for (int ct = 0; ct < K2A_PT; ++ct) {
+    for (int rt = 0; rt < NT; ++rt) {
       f32x4 acc = zero4();
-      if (rt < nrt && ct < nsub) {
 #pragma unroll
-        for (int k4 = 0; k4 < RP; k4 += 4) {
-          const float wa = w2s[(k4 + lg) * dk + 16 * rt + lr];
-          const float gb = gs[(16 * ct + lr) * RP + k4 + lg];
-          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(wa, gb, acc, 0, 0, 0);
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) x[a][ct][i] = acc[i];
-    }
-  }
-  __syncthreads();  // gs / w2s are overwritten by kTs below
-
-  float blast[K2A_SRT][4];
-#pragma unroll
-  for (int a = 0; a < K2A_SRT; ++a) {
-    const int rt = wave + 4 * a;
-    if (rt >= nrt) continue;
-    const int c0 = 16 * rt + 4 * lg;  // first of this lane's 4 channels
-    const f32x4 bgv = __builtin_bit_cast(f32x4, ld16(Bb.bg + hh * dk + c0));
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float carry = 0.f;
-#pragma unroll
-      for (int ct = 0; ct < K2A_PT; ++ct) {
-        if (ct < nsub) {
-          const int t = 16 * ct + lr;
-          const float la = (t < valid) ? logsigmoid_f(x[a][ct][i] + bgv[i]) * P.inv_gamma : 0.f;
-          const float v = row_scan16(la) + carry;  // b_t = sum_{u <= t} log alpha_u
-          carry = row_bcast(v, lane, 15);
-          x[a][ct][i] = v;
-        }
-      }
-      blast[a][i] = carry;  // b at the last position of the chunk
-    }
-
-    // ---- phase 1b: decay factors and scaled operands, same register layout ----
-    float bref[K2A_PT][4];
-#pragma unroll
-    for (int ct = 0; ct < K2A_PT; ++ct)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) bref[ct][i] = (ct < nsub) ? row_bcast(x[a][ct][i], lane, 0) : 0.f;
-    if (lr == 0) {
-      // D_TJ = exp(b_16T - b_16J), J < T;  lam = exp(b_last)
-#pragma unroll
-      for (int T_ = 1; T_ < K2A_PT; ++T_)
-#pragma unroll
-        for (int J = 0; J < T_; ++J)
-          if (T_ < nsub) {
-            float dv[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) dv[i] = __expf(bref[T_][i] - bref[J][i]);
-            st16(Dm + (T_ * 4 + J) * dk + c0, pack16<float>(dv));
-          }
-      float lv[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) lv[i] = __expf(blast[a][i]);
-      st16(lamg + c0, pack16<float>(lv));
-    }
-#pragma unroll
-    for (int ct = 0; ct < K2A_PT; ++ct) {
-      if (ct >= nsub) continue;
-      const int t = 16 * ct + lr;
-      float qv[4] = {0.f, 0.f, 0.f, 0.f}, kv[4] = {0.f, 0.f, 0.f, 0.f};
-      if (t < valid) {
-        unpack16<float>(ld16(qg + (size_t)t * dk + c0), qv);
-        unpack16<float>(ld16(kg + (size_t)t * dk + c0), kv);
-      }
-      float qsv[4], ksv[4], qo[4];
+      for (int k4 = 0; k4 < RP / 4; ++k4)
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(w2[(4 * k4 + lg) * hdk + 16 * rt], gb[k4], acc, 0, 0, 0);
+      const f32x4 bgv = __builtin_bit_cast(f32x4, ld16(Bb.bg + hh * DK + 16 * rt + 4 * lg));
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float bt = x[a][ct][i];
-        qv[i] *= P.q_scale;
-        qsv[i] = qv[i] * __expf(bt - bref[ct][i]);   // query side of A, <= |q|
-        ksv[i] = kv[i] * __expf(bref[ct][i] - bt);   // key side of A (growth < 16 steps)
-        qo[i] = qv[i] * __expf(bt);                  // inter-chunk query
-        kTs[(size_t)(c0 + i) * ldt + t] = from_f32<T>(kv[i] * __expf(blast[a][i] - bt));
+        const float la = live ? log2sigmoid(acc[i] + bgv[i]) * scale : 0.f;
+        x[rt][i] = row_scan16(la);  // inclusive scan over this wave's 16 positions
       }
-      st16(qs + (size_t)t * ldq + c0, pack16<float>(qsv));
-      st16(ks + (size_t)t * ldq + c0, pack16<float>(ksv));
-      if constexpr (sizeof(T) == 2)
-        st8(qtg + (size_t)t * dk + c0, pack8<T>(qo));
-      else
-        st16(qtg + (size_t)t * dk + c0, pack16<T>(qo));
+      if (lr == 15) st16(tot + w * DK + 16 * rt + 4 * lg, pack16<float>(x[rt]));
+      if (lr == 0) st16(first + w * DK + 16 * rt + 4 * lg, pack16<float>(x[rt]));
     }
   }
   __syncthreads();
-  // ---- phase 2: A = masked decayed q k^T from 16 x 16 sub-blocks (wave J) ----
-  const int J = wave;
-  if (J < nsub) {
-    const int lr = lane & 15, lg = lane >> 4;
-    T* Ag = reinterpret_cast<T*>(Bb.A) + ((size_t)bh * Bb.nch + chunk) * C * C;
-    for (int T_ = 0; T_ < nsub; ++T_) {
+
+  // ---- per channel tile: b_t = own scan + totals of the earlier waves; outputs
+  // qt (global), kT (staged in LDS), lam, the key side of A (LDS) and b at this
+  // wave's first position (LDS, the reference of the blocks A[.][w]) ----
+  {
+    T* qtg = reinterpret_cast<T*>(Bb.qt) + (seq_row + p) * DK + 4 * lg;
+    float* lamg = Bb.lam + ((size_t)bh * Bb.nch + chunk) * DK + 4 * lg;
+    char* krow = ks + p * G::KROW + 16 * lg;
+    constexpr int TPS = G::BF ? 2 : 1;  // channel tiles per 64-byte slab
+#pragma unroll
+    for (int s = 0; s < NT / TPS; ++s) {
+      float kside[TPS][4];
+#pragma unroll
+      for (int u = 0; u < TPS; ++u) {
+        const int rt = TPS * s + u;
+        float carry[4] = {0.f, 0.f, 0.f, 0.f}, blast[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int v = 0; v < NW; ++v) {
+          float t4[4];
+          unpack16<float>(ld16(tot + v * DK + 16 * rt + 4 * lg), t4);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            blast[i] += t4[i];
+            if (v < w) carry[i] += t4[i];
+          }
+        }
+        float f4[4], bref[4], qo[4];
+        unpack16<float>(ld16(first + w * DK + 16 * rt + 4 * lg), f4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float bt = x[rt][i] + carry[i];
+          x[rt][i] = bt;
+          bref[i] = carry[i] + f4[i];
+          qv[rt][i] *= P.q_scale;
+          qo[i] = qv[rt][i] * exp2_fast(bt);
+          kTs[(16 * rt + 4 * lg + i) * G::LDT + p] = from_f32<T>(kv[rt][i] * exp2_fast(blast[i] - bt));
+          kside[u][i] = kv[rt][i] * exp2_fast(bref[i] - bt);
+        }
+        if constexpr (G::BF)
+          st8(qtg + 16 * rt, pack8<T>(qo));
+        else
+          st16(qtg + 16 * rt, pack16<T>(qo));
+        if (lr == 0) {
+          st16(brf + w * DK + 16 * rt + 4 * lg, pack16<float>(bref));
+          if (w == 0) {
+            float lv[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) lv[i] = exp2_fast(blast[i]);
+            st16(lamg + 16 * rt, pack16<float>(lv));
+          }
+        }
+      }
+      // bf16 slab s (32 channels) holds tiles 2s and 2s+1; lane group lg owns
+      // k-slots 8 lg .. 8 lg + 7 = channels 4 lg + i of both tiles (the query
+      // side below uses the same slot order)
+      if constexpr (G::BF) {
+        const float v8[8] = {kside[0][0], kside[0][1], kside[0][2], kside[0][3],
+                             kside[1][0], kside[1][1], kside[1][2], kside[1][3]};
+        u32x4 hi, lo;
+        split_bf16(v8, hi, lo);
+        st16(krow + 64 * s, hi);
+        st16(krow + C * G::KROW + 64 * s, lo);
+      } else {
+        st16(krow + 64 * s, pack16<float>(kside[0]));
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- A[w][J] for J <= w (zero blocks above the diagonal) ----
+  {
+    T* Ag = reinterpret_cast<T*>(Bb.A) + (((size_t)bh * Bb.nch + chunk) * C + p) * C + 4 * lg;
+    constexpr int TPS = G::BF ? 2 : 1;
+#pragma unroll
+    for (int J = 0; J < NW; ++J) {
       float out[4] = {0.f, 0.f, 0.f, 0.f};
-      if (T_ >= J) {
+      if (J <= w) {
+        const char* krow = ks + (16 * J + lr) * G::KROW + 16 * lg;
         f32x4 acc = zero4();
-        const int i_row = 16 * J + lr;   // key row for the A-operand
-        const int t_row = 16 * T_ + lr;  // query row for the B-operand
-        for (int c0 = 0; c0 < dk; c0 += slab_elems<T>()) {
-          const int cc = c0 + lg * per16<T>();
-          float kf[per16<T>()], qf[per16<T>()];
 #pragma unroll
-          for (int e = 0; e < per16<T>(); e += 4) {
-            unpack16<float>(ld16(ks + (size_t)i_row * ldq + cc + e), kf + e);
-            unpack16<float>(ld16(qs + (size_t)t_row * ldq + cc + e), qf + e);
-          }
-          if (T_ > J) {
+        for (int s = 0; s < NT / TPS; ++s) {
+          // query side q_t e^{b_t - b_16J} for the slab's channels
+          float qs[4 * TPS];
 #pragma unroll
-            for (int e = 0; e < per16<T>(); ++e) qf[e] *= Dm[(T_ * 4 + J) * dk + cc + e];
+          for (int u = 0; u < TPS; ++u) {
+            const int rt = TPS * s + u;
+            float r4[4];
+            unpack16<float>(ld16(brf + J * DK + 16 * rt + 4 * lg), r4);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) qs[4 * u + i] = qv[rt][i] * exp2_fast(x[rt][i] - r4[i]);
           }
-          if constexpr (sizeof(T) == 2) {
-            // split-bf16 product (hi*hi + hi*lo + lo*hi): A is a scalar weight of
-            // whole output rows, so it is formed to ~16 mantissa bits.
-            u32x4 kh, kl, qh, ql;
-            split_bf16(kf, kh, kl);
-            split_bf16(qf, qh, ql);
+          if constexpr (G::BF) {
+            u32x4 qh, ql;
+            split_bf16(qs, qh, ql);
+            const u32x4 kh = ld16(krow + 64 * s), kl = ld16(krow + C * G::KROW + 64 * s);
             acc = mma_slab<bf16>(kh, qh, acc);
             acc = mma_slab<bf16>(kh, ql, acc);
             acc = mma_slab<bf16>(kl, qh, acc);
           } else {
-            acc = mma_slab<float>(pack16<float>(kf), pack16<float>(qf), acc);
+            acc = mma_slab<float>(ld16(krow + 64 * s), pack16<float>(qs), acc);
           }
         }
-        // acc[e] = A[16T + lr][16J + 4 lg + e]
+        // acc[e] = A[16 w + lr][16 J + 4 lg + e]; causal mask on the diagonal block
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const bool keep = (T_ > J) || (4 * lg + e <= lr);
-          out[e] = keep ? acc[e] : 0.f;
-        }
+        for (int e = 0; e < 4; ++e) out[e] = (J < w || 4 * lg + e <= lr) ? acc[e] : 0.f;
       }
-      T* dst = Ag + (size_t)(16 * T_ + lr) * C + 16 * J + 4 * lg;
-      if constexpr (sizeof(T) == 2) {
-        st8(dst, pack8<T>(out));
-      } else {
-        st16(dst, pack16<T>(out));
-      }
+      if constexpr (G::BF)
+        st8(Ag + 16 * J, pack8<T>(out));
+      else
+        st16(Ag + 16 * J, pack16<T>(out));
     }
   }
 
-  // ---- phase 3: the transposed state-update key, coalesced ----
+  // ---- the transposed state-update key, coalesced ----
   constexpr int PER = per16<T>();
-  for (int p = tid; p < dk * C / PER; p += K2A_THREADS) {
-    const int c = (p * PER) / C, t0 = p * PER - c * C;
-    st16(kTg + (size_t)c * C + t0, ld16(kTs + (size_t)c * ldt + t0));
+  T* kTg = reinterpret_cast<T*>(Bb.kT) + ((size_t)bh * Bb.nch + chunk) * DK * C;
+#pragma unroll
+  for (int i = 0; i < (DK * C / PER + G::THREADS - 1) / G::THREADS; ++i) {
+    const int pc = tid + i * G::THREADS;
+    if (pc < DK * C / PER) {
+      const int c = (pc * PER) / C, t0 = pc * PER - c * C;
+      st16(kTg + (size_t)c * C + t0, ld16(kTs + c * G::LDT + t0));
+    }
   }
 }
 
-size_t k2a_lds_bytes(int C, int dk, int rp, bool bf16_path) {
-  const int es = bf16_path ? 2 : 4;
-  const size_t kts = (size_t)dk * (C + 16 / es) * es;
-  const size_t gw = (size_t)(C * rp + rp * dk) * 4;
-  return (size_t)2 * C * (dk + 4) * 4 + (size_t)16 * dk * 4 + (kts > gw ? kts : gw);
+template <typename T, int C, int DK, int RP>
+static void launch_k2a_cdr(const K2Params& P, hipStream_t stream) {
+  using G = K2aGeom<T, C, DK>;
+  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k2a_gla_chunk<T, C, DK, RP>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, G::LDS);
+  hipLaunchKernelGGL((k2a_gla_chunk<T, C, DK, RP>), dim3(P.total_units), dim3(G::THREADS), G::LDS,
+                     stream, P);
 }
 
-template <typename T, int RP>
-static void launch_k2a_rp(const K2Params& P, size_t lds, hipStream_t stream) {
-  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k2a_gla_chunk<T, RP>),
-                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  hipLaunchKernelGGL((k2a_gla_chunk<T, RP>), dim3(P.total_units), dim3(K2A_THREADS), lds, stream, P);
+template <typename T, int C, int DK>
+static void launch_k2a_cd(const K2Params& P, hipStream_t stream) {
+  if (P.rp == 16)
+    launch_k2a_cdr<T, C, DK, 16>(P, stream);
+  else
+    launch_k2a_cdr<T, C, DK, 64>(P, stream);
+}
+
+template <typename T, int C>
+static bool launch_k2a_c(const K2Params& P, hipStream_t stream) {
+  switch (P.dk) {
+    case 16: if constexpr (sizeof(T) == 4) { launch_k2a_cd<T, C, 16>(P, stream); return true; } return false;
+    case 32: launch_k2a_cd<T, C, 32>(P, stream); return true;
+    case 64: launch_k2a_cd<T, C, 64>(P, stream); return true;
+    case 128: launch_k2a_cd<T, C, 128>(P, stream); return true;
+    case 256: launch_k2a_cd<T, C, 256>(P, stream); return true;
+    default: return false;
+  }
 }
 
 template <typename T>
-static void launch_k2a_t(const K2Params& P, size_t lds, hipStream_t stream) {
-  if (P.rp == 16)
-    launch_k2a_rp<T, 16>(P, lds, stream);
-  else
-    launch_k2a_rp<T, 64>(P, lds, stream);
+static bool launch_k2a_t(const K2Params& P, hipStream_t stream) {
+  switch (P.C) {
+    case 16: if constexpr (sizeof(T) == 4) return launch_k2a_c<T, 16>(P, stream); return false;
+    case 32: return launch_k2a_c<T, 32>(P, stream);
+    case 64: return launch_k2a_c<T, 64>(P, stream);
+    default: return false;
+  }
 }
 
 hipError_t launch_k2a(const K2Params& P, bool bf16_path, hipStream_t stream) {
-  const size_t lds = k2a_lds_bytes(P.C, P.dk, P.rp, bf16_path);
-  if (bf16_path)
-    launch_k2a_t<bf16>(P, lds, stream);
-  else
-    launch_k2a_t<float>(P, lds, stream);
+  const bool ok = bf16_path ? launch_k2a_t<bf16>(P, stream) : launch_k2a_t<float>(P, stream);
+  if (!ok) return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
