@@ -1,24 +1,27 @@
 // MFMA GEMM core for gfx950 with asynchronous operand copies:
 // C = A * B^T, both operands read along K ("NT"), fp32 accumulation.
 //
-// Four waves in a 2 x 2 grid; each wave owns a (16 WM) x (16 WN) sub-tile
-// (WM x WN v_mfma 16 x 16 tiles), so the workgroup tile is BM x BN with
-// BM = 32 WM, BN = 32 WN.  Every operand row is a 128-byte K segment of some
-// global row; the problem class supplies, per row, where it starts (which
-// makes gathers such as the causal hold free).  Each K segment of both
-// operands is copied global -> LDS with global_load_lds_dwordx4 (one
-// instruction = 8 rows x 128 bytes, without VGPRs) into one of NST rotating
-// stages, NST-1 segments ahead of the MFMAs; one LDS-only barrier per segment.
-// Inside a stage, 16-byte piece p of row r lives at r * 128 + ((p ^ (r & 7)) << 4),
-// so the fragment reads of 8 consecutive rows hit distinct banks.
+// A workgroup of WGM x WGN waves computes a BM x BN tile; each wave owns a
+// (16 WM) x (16 WN) sub-tile of v_mfma 16 x 16 tiles.  K advances in segments
+// of KSEG bytes (64 or 128) per operand row; the problem class supplies, per
+// row and segment, where that segment starts in memory (which makes gathers
+// such as the causal hold free).  Every segment of both operands is copied
+// global -> LDS with global_load_lds_dwordx4 (one instruction = 1 KB: 8 rows
+// of 128 bytes or 16 rows of 64 bytes, no VGPRs) into one of NST rotating
+// stages, NST-1 segments ahead of the MFMAs, with one LDS-only barrier per
+// segment.  The copies of later segments stay in flight while earlier ones are
+// multiplied: the vmcnt wait at segment kt allows exactly the copies of the
+// segments issued after it.  Inside a stage, 16-byte piece p of row r is
+// XOR-swizzled (KSEG 128: p ^ (r & 7); KSEG 64: p ^ ((r >> 2) & 3)) so that the
+// fragment reads of 16 consecutive rows spread over all banks.
 //
-// Problem class interface (A slot j of a lane copies tile row
-// ra_j = (BM / 4) wave + 8 j + lane / 8, B slot j row rb_j likewise with BN):
+// Problem class interface (Cfg::a_row / b_row give the tile row a lane's copy
+// slot j holds):
 //   void setup(int wave, int lane)      precompute the lane's row sources
 //   void started(char* lds)             after the first segments are in flight
-//                                        (may fill LDS beyond the NST stages)
+//                                        (may fill LDS beyond Cfg::LDS)
 //   void prep(int kt)                    once per copied segment, before a_row/b_row
-//   const char* a_row(int j, int kt)    byte address of slot j's row, K segment kt
+//   const char* a_row(int j, int kt)    byte address of segment kt of slot j's row
 //   const char* b_row(int j, int kt)    (valid memory even for rows outside the
 //                                        problem: their results are discarded)
 //   int  nk()                           number of K segments
@@ -33,67 +36,89 @@
 
 namespace msgla {
 
-constexpr int GD_THREADS = 256;
+template <int WM_, int WN_, int WGM_, int WGN_, int KSEG_, int NST_>
+struct GemmCfg {
+  static constexpr int WM = WM_, WN = WN_;      // 16 x 16 tiles per wave
+  static constexpr int WGM = WGM_, WGN = WGN_;  // wave grid (row-major)
+  static constexpr int NW = WGM * WGN, THREADS = 64 * NW;
+  static constexpr int BM = 16 * WM * WGM, BN = 16 * WN * WGN;
+  static constexpr int KSEG = KSEG_, NSL = KSEG_ / 64, NST = NST_;
+  static constexpr int A_BYTES = BM * KSEG, B_BYTES = BN * KSEG, STAGE = A_BYTES + B_BYTES;
+  static constexpr int LDS = NST * STAGE;
+  static constexpr int RPI = 1024 / KSEG;       // rows per copy instruction
+  static constexpr int A_SLOTS = BM / (RPI * NW), B_SLOTS = BN / (RPI * NW);
+  static constexpr int COPIES = A_SLOTS + B_SLOTS;  // copy instructions per wave and segment
+  static constexpr int LDC = BN + 4;            // fp32 staging row stride of gd_stage_tile
+  static constexpr int LDS_STAGED = LDS > BM * LDC * 4 ? LDS : BM * LDC * 4;
+  static_assert(KSEG == 64 || KSEG == 128, "segment");
+  static_assert(NST >= 2 && NST <= 8, "stages");
+  static_assert(A_SLOTS >= 1 && B_SLOTS >= 1 && A_SLOTS * RPI * NW == BM && B_SLOTS * RPI * NW == BN,
+                "copy slots");
+  static_assert((NST - 2) * COPIES < 64, "vmcnt range");
 
-template <int WM, int WN>
-struct GemmShape {
-  static constexpr int BM = 32 * WM, BN = 32 * WN;
-  static constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128, STAGE = A_BYTES + B_BYTES;
-  static constexpr int A_SLOTS = BM / 32, B_SLOTS = BN / 32;  // copy instructions per wave
+  // tile row held by copy slot j of a lane
+  __device__ static int a_row(int j, int wave, int lane) { return RPI * (A_SLOTS * wave + j) + lane / (KSEG / 16); }
+  __device__ static int b_row(int j, int wave, int lane) { return RPI * (B_SLOTS * wave + j) + lane / (KSEG / 16); }
+  // LDS byte offset of 16-byte piece p of row r inside an operand block
+  __device__ static int off(int r, int p) {
+    if constexpr (KSEG == 128)
+      return r * 128 + ((p ^ (r & 7)) << 4);
+    else
+      return r * 64 + ((p ^ ((r >> 2) & 3)) << 4);
+  }
+  // byte offset inside the row segment of the piece a lane copies (its LDS
+  // slot is 16 * lane of the instruction; the swizzle is an involution)
+  __device__ static int cp_piece(int lane) {
+    if constexpr (KSEG == 128)
+      return ((lane & 7) ^ (lane >> 3)) << 4;
+    else
+      return ((lane & 3) ^ ((lane >> 4) & 3)) << 4;
+  }
 };
 
-template <int WM, int WN, int NST>
-constexpr int gd_lds_bytes() {
-  return NST * GemmShape<WM, WN>::STAGE;
+// s_waitcnt vmcnt(n * COPIES) for a wave-uniform n in [0, MAXN]
+template <int COPIES, int MAXN>
+__device__ __forceinline__ void wait_stages(int n) {
+  if constexpr (MAXN <= 0) {
+    wait_vmcnt<0>();
+  } else {
+    if (n >= MAXN)
+      wait_vmcnt<MAXN * COPIES>();
+    else
+      wait_stages<COPIES, MAXN - 1>(n);
+  }
 }
 
-template <typename T, int WM, int WN, int NST, class Prob>
+template <typename T, class Cfg, class Prob>
 __device__ __forceinline__ void gemm_dma_tile(Prob& prob, int n_valid, char* lds) {
-  static_assert(NST == 2 || NST == 3, "2 or 3 pipeline stages");
-  using S = GemmShape<WM, WN>;
-  constexpr int COPIES = S::A_SLOTS + S::B_SLOTS;  // copy instructions per wave per segment
+  constexpr int WM = Cfg::WM, WN = Cfg::WN, NST = Cfg::NST;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wr = wave >> 1, wc = wave & 1;
+  const int wr = wave / Cfg::WGN, wc = wave % Cfg::WGN;
   const int lrow = lane & 15, lgrp = lane >> 4;
   const int nk = prob.nk();
   prob.setup(wave, lane);
 
-  // this lane's copy slots: piece (lane & 7) ^ (lane >> 3) of rows 8 k + lane / 8
-  const int cp_piece = ((lane & 7) ^ (lane >> 3)) << 4;
+  const int cpp = Cfg::cp_piece(lane);
   auto issue = [&](int kt) {
-    char* st = lds + (kt % NST) * S::STAGE;
+    char* st = lds + (kt % NST) * Cfg::STAGE;
     prob.prep(kt);
 #pragma unroll
-    for (int j = 0; j < S::A_SLOTS; ++j) {
-      const int k = S::A_SLOTS * wave + j;
-      __builtin_amdgcn_global_load_lds(prob.a_row(j, kt) + cp_piece, (lds_void_t*)(st + 1024 * k),
-                                       16, 0, 0);
-    }
+    for (int j = 0; j < Cfg::A_SLOTS; ++j)
+      dma16(prob.a_row(j, kt) + cpp, st + 1024 * (Cfg::A_SLOTS * wave + j));
 #pragma unroll
-    for (int j = 0; j < S::B_SLOTS; ++j) {
-      const int k = S::B_SLOTS * wave + j;
-      __builtin_amdgcn_global_load_lds(prob.b_row(j, kt) + cp_piece,
-                                       (lds_void_t*)(st + S::A_BYTES + 1024 * k), 16, 0, 0);
-    }
+    for (int j = 0; j < Cfg::B_SLOTS; ++j)
+      dma16(prob.b_row(j, kt) + cpp, st + Cfg::A_BYTES + 1024 * (Cfg::B_SLOTS * wave + j));
   };
 
-  // fragment offsets inside a stage (the same for every segment)
-  int offA[WM][2], offB[WN][2];
+  // fragment offsets inside a stage (the same for every segment): rows of a
+  // 16-row tile differ by multiples of 16, which leave the swizzle key alone
+  int offA[Cfg::NSL], offB[Cfg::NSL];
 #pragma unroll
-  for (int sl = 0; sl < 2; ++sl) {
-    const int p = sl * 4 + lgrp;
-#pragma unroll
-    for (int a = 0; a < WM; ++a) {
-      const int r = wr * 16 * WM + 16 * a + lrow;
-      offA[a][sl] = r * 128 + ((p ^ (r & 7)) << 4);
-    }
-#pragma unroll
-    for (int b = 0; b < WN; ++b) {
-      const int r = wc * 16 * WN + 16 * b + lrow;
-      offB[b][sl] = S::A_BYTES + r * 128 + ((p ^ (r & 7)) << 4);
-    }
+  for (int sl = 0; sl < Cfg::NSL; ++sl) {
+    offA[sl] = Cfg::off(wr * 16 * WM + lrow, sl * 4 + lgrp);
+    offB[sl] = Cfg::A_BYTES + Cfg::off(wc * 16 * WN + lrow, sl * 4 + lgrp);
   }
 
   f32x4 acc[WM][WN];
@@ -111,20 +136,17 @@ __device__ __forceinline__ void gemm_dma_tile(Prob& prob, int n_valid, char* lds
 
   for (int kt = 0; kt < nk; ++kt) {
     // segment kt has landed once only the copies of later segments remain
-    if (NST == 3 && kt + 1 < nk)
-      wait_vmcnt<COPIES>();
-    else
-      wait_vmcnt<0>();
+    wait_stages<Cfg::COPIES, NST - 2>(min(NST - 2, nk - 1 - kt));
     lds_barrier();
     if (kt + NST - 1 < nk) issue(kt + NST - 1);
-    const char* st = lds + (kt % NST) * S::STAGE;
+    const char* st = lds + (kt % NST) * Cfg::STAGE;
 #pragma unroll
-    for (int sl = 0; sl < 2; ++sl) {
+    for (int sl = 0; sl < Cfg::NSL; ++sl) {
       u32x4 fa[WM], fb[WN];
 #pragma unroll
-      for (int a = 0; a < WM; ++a) fa[a] = ld16(st + offA[a][sl]);
+      for (int a = 0; a < WM; ++a) fa[a] = ld16(st + offA[sl] + a * 16 * Cfg::KSEG);
 #pragma unroll
-      for (int b = 0; b < WN; ++b) fb[b] = ld16(st + offB[b][sl]);
+      for (int b = 0; b < WN; ++b) fb[b] = ld16(st + offB[sl] + b * 16 * Cfg::KSEG);
 #pragma unroll
       for (int b = 0; b < WN; ++b) {
         if (b < nb_valid) {
@@ -141,56 +163,20 @@ __device__ __forceinline__ void gemm_dma_tile(Prob& prob, int n_valid, char* lds
 }
 
 // Whole-tile fp32 staging for epilogues that route values by row and column:
-// C[r][c] at C + r * (BN + 4) + c.  Call after gemm_dma_tile's final barrier
+// C[r][c] at C + r * Cfg::LDC + c.  Call after gemm_dma_tile's final barrier
 // (the stages are free), then lds_barrier() before reading other waves' values.
-template <int WM, int WN>
-constexpr int gd_ldc() {
-  return 32 * WN + 4;
-}
-template <int WM, int WN, int NST>
-constexpr int gd_lds_bytes_staged() {
-  return gd_lds_bytes<WM, WN, NST>() > 32 * WM * gd_ldc<WM, WN>() * 4
-             ? gd_lds_bytes<WM, WN, NST>()
-             : 32 * WM * gd_ldc<WM, WN>() * 4;
-}
-template <int WM, int WN>
-__device__ __forceinline__ void gd_stage_tile(const f32x4 (&acc)[WM][WN], int wr, int wc, int lane,
-                                              float* C) {
-  constexpr int LDC = gd_ldc<WM, WN>();
+template <class Cfg>
+__device__ __forceinline__ void gd_stage_tile(const f32x4 (&acc)[Cfg::WM][Cfg::WN], int wr, int wc,
+                                              int lane, float* C) {
   const int lrow = lane & 15, lgrp = lane >> 4;
 #pragma unroll
-  for (int a = 0; a < WM; ++a)
+  for (int a = 0; a < Cfg::WM; ++a)
 #pragma unroll
-    for (int b = 0; b < WN; ++b)
+    for (int b = 0; b < Cfg::WN; ++b)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        C[(wr * 16 * WM + 16 * a + 4 * lgrp + i) * LDC + wc * 16 * WN + 16 * b + lrow] = acc[a][b][i];
-}
-
-// Writes a wave's accumulators through a per-wave LDS staging area in row
-// blocks of 16 (one MFMA row tile across all its columns) and hands each
-// staged block to emit(row0, C, ldc), C = 16 x (16 WN) fp32 starting at row
-// row0 of the wave's sub-tile.  `stage` holds 4 * 16 * (16 WN + 4) floats.
-template <int WM, int WN, class Emit>
-__device__ __forceinline__ void stage_rows16(f32x4 (&acc)[WM][WN], int wave, int lane,
-                                             float* stage, Emit&& emit) {
-  constexpr int LDC = 16 * WN + 4;
-  float* C = stage + wave * 16 * LDC;
-  const int lrow = lane & 15, lgrp = lane >> 4;
-#pragma unroll
-  for (int a = 0; a < WM; ++a) {
-#pragma unroll
-    for (int b = 0; b < WN; ++b)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) C[(4 * lgrp + i) * LDC + 16 * b + lrow] = acc[a][b][i];
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (0 << 8));  // own LDS writes done
-    asm volatile("" ::: "memory");
-    emit(16 * a, C, LDC);
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (0 << 8));  // reads done before reuse
-    asm volatile("" ::: "memory");
-  }
+        C[(wr * 16 * Cfg::WM + 16 * a + 4 * lgrp + i) * Cfg::LDC + wc * 16 * Cfg::WN + 16 * b + lrow] =
+            acc[a][b][i];
 }
 
 }  // namespace msgla

@@ -22,22 +22,23 @@
 
 namespace msgla {
 
-constexpr int K3_WM = 4, K3_WN = 4, K3_NST = 2;
-constexpr int K3_BM = GemmShape<K3_WM, K3_WN>::BM, K3_BN = GemmShape<K3_WM, K3_WN>::BN;
+using K3Cfg = GemmCfg<4, 4, 2, 2, 128, 2>;  // 128 x 128 tiles, 4 waves, double-buffered 128-byte K segments
+constexpr int K3_WM = K3Cfg::WM, K3_WN = K3Cfg::WN;
+constexpr int K3_BM = K3Cfg::BM, K3_BN = K3Cfg::BN;
 // the tile's fusion weights [BM][FUSION_STRIDE] fp32 live in LDS after the stages
-constexpr int K3_W_OFF = gd_lds_bytes<K3_WM, K3_WN, K3_NST>();
-constexpr int K3_LDS = gd_lds_bytes_staged<K3_WM, K3_WN, K3_NST>() > K3_W_OFF + K3_BM * FUSION_STRIDE * 4
-                           ? gd_lds_bytes_staged<K3_WM, K3_WN, K3_NST>()
+constexpr int K3_W_OFF = K3Cfg::LDS;
+constexpr int K3_LDS = K3Cfg::LDS_STAGED > K3_W_OFF + K3_BM * FUSION_STRIDE * 4
+                           ? K3Cfg::LDS_STAGED
                            : K3_W_OFF + K3_BM * FUSION_STRIDE * 4;
-static_assert(K3_BM * FUSION_STRIDE * 4 == GD_THREADS * 16, "one 16-byte piece per thread");
+static_assert(K3_BM * FUSION_STRIDE * 4 == K3Cfg::THREADS * 16, "one 16-byte piece per thread");
 
 template <typename T>
 struct K3Prob {
   const K3Params& P;
   int m0, n0;
-  int rb[4], rt[4];            // sequence / position of the lane's copy rows (-1: none)
-  const char* brow[4];
-  const char* arow[4];         // row base of the branch currently being copied
+  int rb[K3Cfg::A_SLOTS], rt[K3Cfg::A_SLOTS];  // sequence / position of the lane's copy rows (-1: none)
+  const char* brow[K3Cfg::B_SLOTS];
+  const char* arow[K3Cfg::A_SLOTS];            // row base of the branch currently being copied
   int ib_issue = -1;           // branch of the K segments being copied
   int ib_fold = 0;             // branch of the K segments being multiplied
   f32x4 total[K3_WM][K3_WN];
@@ -45,8 +46,8 @@ struct K3Prob {
 
   __device__ K3Prob(const K3Params& p, int m0_, int n0_) : P(p), m0(m0_), n0(n0_) {}
 
-  __device__ int nk() const { return P.Ktot * (int)sizeof(T) / 128; }
-  __device__ int seg_begin(int i) const { return P.br[i].ko * (int)sizeof(T) / 128; }
+  __device__ int nk() const { return P.Ktot * (int)sizeof(T) / K3Cfg::KSEG; }
+  __device__ int seg_begin(int i) const { return P.br[i].ko * (int)sizeof(T) / K3Cfg::KSEG; }
   __device__ int branch_of(int kt) const {
     int bi = 0;
     while (bi + 1 < P.m && kt >= seg_begin(bi + 1)) ++bi;
@@ -54,13 +55,15 @@ struct K3Prob {
   }
   __device__ void setup(int wave, int lane) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int r = 32 * wave + 8 * j + (lane >> 3);
-      const int m = m0 + r, n = n0 + r;
+    for (int j = 0; j < K3Cfg::A_SLOTS; ++j) {
+      const int m = m0 + K3Cfg::a_row(j, wave, lane);
       rb[j] = (m < P.B * P.L) ? m / P.L : -1;
       rt[j] = (m < P.B * P.L) ? m - rb[j] * P.L : 0;
-      brow[j] = reinterpret_cast<const char*>(P.WoT) +
-                (size_t)(n < P.d ? n : 0) * P.Ktot * sizeof(T);
+    }
+#pragma unroll
+    for (int j = 0; j < K3Cfg::B_SLOTS; ++j) {
+      const int n = n0 + K3Cfg::b_row(j, wave, lane);
+      brow[j] = reinterpret_cast<const char*>(P.WoT) + (size_t)(n < P.d ? n : 0) * P.Ktot * sizeof(T);
     }
     if (P.m > 1) {
 #pragma unroll
@@ -86,7 +89,7 @@ struct K3Prob {
   __device__ void enter_branch(int bi) {
     const K3Branch& Br = P.br[bi];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < K3Cfg::A_SLOTS; ++j) {
       const int jr = (rt[j] + 1) / Br.s - 1;
       arow[j] = (rb[j] < 0 || jr < 0)
                     ? nullptr
@@ -102,14 +105,14 @@ struct K3Prob {
     const int bi = branch_of(kt);
     if (bi != ib_issue) enter_branch(bi);
     const int head_bytes = P.dv * (int)sizeof(T);
-    const int kb = (kt - seg_begin(bi)) * 128;  // bytes into the branch's K range
+    const int kb = (kt - seg_begin(bi)) * K3Cfg::KSEG;  // bytes into the branch's K range
     const int hh = kb / head_bytes;             // head of this segment
     seg_off = (size_t)hh * P.br[bi].np * head_bytes + (kb - hh * head_bytes);
   }
   __device__ const char* a_row(int j, int) const {
     return arow[j] ? arow[j] + seg_off : reinterpret_cast<const char*>(P.zero);
   }
-  __device__ const char* b_row(int j, int kt) const { return brow[j] + kt * 128; }
+  __device__ const char* b_row(int j, int kt) const { return brow[j] + kt * K3Cfg::KSEG; }
   __device__ bool seg_end(int kt) const {
     return P.m > 1 && (ib_fold + 1 >= P.m ? kt + 1 == nk() : kt + 1 == seg_begin(ib_fold + 1));
   }
@@ -140,14 +143,14 @@ struct K3Prob {
   }
   __device__ void store(const f32x4 (&acc)[K3_WM][K3_WN], int wr, int wc, int lane, char* lds) {
     float* C = reinterpret_cast<float*>(lds);
-    gd_stage_tile<K3_WM, K3_WN>(acc, wr, wc, lane, C);
+    gd_stage_tile<K3Cfg>(acc, wr, wc, lane, C);
     lds_barrier();
-    epilogue(C, gd_ldc<K3_WM, K3_WN>());
+    epilogue(C, K3Cfg::LDC);
   }
   __device__ void epilogue(const float* C, int ldc) {
     const int tid = threadIdx.x;
     T* out = reinterpret_cast<T*>(P.out);
-    for (int it = tid; it < K3_BM * (K3_BN / 8); it += GD_THREADS) {
+    for (int it = tid; it < K3_BM * (K3_BN / 8); it += K3Cfg::THREADS) {
       const int r = it / (K3_BN / 8), cg = it % (K3_BN / 8);
       const int m = m0 + r, col = n0 + cg * 8;
       if (m >= P.B * P.L || col >= P.d) continue;
@@ -166,17 +169,17 @@ struct K3Prob {
 };
 
 template <typename T>
-__global__ __launch_bounds__(GD_THREADS) __attribute__((amdgpu_waves_per_eu(2))) void k3_hold_fuse(const K3Params P) {
+__global__ __launch_bounds__(K3Cfg::THREADS) __attribute__((amdgpu_waves_per_eu(2))) void k3_hold_fuse(const K3Params P) {
   __shared__ __attribute__((aligned(16))) char lds[K3_LDS];
   const int tile = remap_xcd(blockIdx.x, P.per_xcd);
   if (tile >= P.total_tiles) return;
   const int tm = tile / P.tiles_n, tn = tile - tm * P.tiles_n;
   K3Prob<T> prob(P, tm * K3_BM, tn * K3_BN);
-  gemm_dma_tile<T, K3_WM, K3_WN, K3_NST>(prob, P.d - tn * K3_BN, lds);
+  gemm_dma_tile<T, K3Cfg>(prob, P.d - tn * K3_BN, lds);
 }
 
 hipError_t launch_k3(const K3Params& P, bool bf16_path, hipStream_t stream) {
-  const dim3 grid(P.per_xcd * N_XCD), block(GD_THREADS);
+  const dim3 grid(P.per_xcd * N_XCD), block(K3Cfg::THREADS);
   if (bf16_path)
     hipLaunchKernelGGL(k3_hold_fuse<bf16>, grid, block, 0, stream, P);
   else

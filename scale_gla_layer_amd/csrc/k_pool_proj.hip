@@ -22,43 +22,46 @@
 
 namespace msgla {
 
-constexpr int K1_WM = 4, K1_WN = 4, K1_NST = 2;
-constexpr int K1_BM = GemmShape<K1_WM, K1_WN>::BM, K1_BN = GemmShape<K1_WM, K1_WN>::BN;
+using K1Cfg = GemmCfg<4, 4, 2, 2, 128, 2>;  // 128 x 128 tiles, 4 waves, double-buffered 128-byte K segments
+constexpr int K1_BM = K1Cfg::BM, K1_BN = K1Cfg::BN;
 
 template <typename T>
 struct K1Prob {
   const K1Params& P;
   const K1Group& G;
   int m0, n0;
-  const char* arow[4];
-  const char* brow[4];
+  const char* arow[K1Cfg::A_SLOTS];
+  const char* brow[K1Cfg::B_SLOTS];
 
   __device__ K1Prob(const K1Params& p, const K1Group& g, int m0_, int n0_)
       : P(p), G(g), m0(m0_), n0(n0_) {}
 
-  __device__ int nk() const { return P.d * (int)sizeof(T) / 128; }
+  __device__ int nk() const { return P.d * (int)sizeof(T) / K1Cfg::KSEG; }
   __device__ void setup(int wave, int lane) {
     const size_t row_bytes = (size_t)P.d * sizeof(T);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int r = 32 * wave + 8 * j + (lane >> 3);
-      const int m = m0 + r, n = n0 + r;
+    for (int j = 0; j < K1Cfg::A_SLOTS; ++j) {
+      const int m = m0 + K1Cfg::a_row(j, wave, lane);
       arow[j] = reinterpret_cast<const char*>(G.A) + (size_t)(m < G.M ? m : 0) * row_bytes;
+    }
+#pragma unroll
+    for (int j = 0; j < K1Cfg::B_SLOTS; ++j) {
+      const int n = n0 + K1Cfg::b_row(j, wave, lane);
       brow[j] = reinterpret_cast<const char*>(G.Wp) + (size_t)(n < G.N ? n : 0) * row_bytes;
     }
   }
   __device__ void started(char*) {}
   __device__ void prep(int) {}
-  __device__ const char* a_row(int j, int kt) const { return arow[j] + kt * 128; }
-  __device__ const char* b_row(int j, int kt) const { return brow[j] + kt * 128; }
+  __device__ const char* a_row(int j, int kt) const { return arow[j] + kt * K1Cfg::KSEG; }
+  __device__ const char* b_row(int j, int kt) const { return brow[j] + kt * K1Cfg::KSEG; }
   __device__ bool seg_end(int) const { return false; }
-  __device__ void fold(f32x4 (&)[K1_WM][K1_WN], int, int, int) {}
-  __device__ void finish(f32x4 (&)[K1_WM][K1_WN], int, int, int) {}
-  __device__ void store(const f32x4 (&acc)[K1_WM][K1_WN], int wr, int wc, int lane, char* lds) {
+  __device__ void fold(f32x4 (&)[K1Cfg::WM][K1Cfg::WN], int, int, int) {}
+  __device__ void finish(f32x4 (&)[K1Cfg::WM][K1Cfg::WN], int, int, int) {}
+  __device__ void store(const f32x4 (&acc)[K1Cfg::WM][K1Cfg::WN], int wr, int wc, int lane, char* lds) {
     float* C = reinterpret_cast<float*>(lds);
-    gd_stage_tile<K1_WM, K1_WN>(acc, wr, wc, lane, C);
+    gd_stage_tile<K1Cfg>(acc, wr, wc, lane, C);
     lds_barrier();
-    epilogue(C, gd_ldc<K1_WM, K1_WN>());
+    epilogue(C, K1Cfg::LDC);
   }
 
   __device__ void store8(T* dst, const float* v) {
@@ -73,7 +76,7 @@ struct K1Prob {
   __device__ void epilogue(const float* C, int ldc) {
     const int tid = threadIdx.x;
     // (1) row-major destinations: q, k, gate factor, fusion weights
-    for (int it = tid; it < K1_BM * (K1_BN / 8); it += GD_THREADS) {
+    for (int it = tid; it < K1_BM * (K1_BN / 8); it += K1Cfg::THREADS) {
       const int r = it / (K1_BN / 8), cg = it % (K1_BN / 8);
       const int m = m0 + r, col = n0 + cg * 8;
       if (m >= G.M || col >= G.N) continue;
@@ -116,7 +119,7 @@ struct K1Prob {
     }
     // (2) v, written transposed per chunk: vT[b][hh][chunk][v][tau]
     if (G.col_g > G.col_v && n0 < G.col_g && n0 + K1_BN > G.col_v) {
-      for (int it = tid; it < K1_BN * (K1_BM / 8); it += GD_THREADS) {
+      for (int it = tid; it < K1_BN * (K1_BM / 8); it += K1Cfg::THREADS) {
         const int cl = it % K1_BN, rg = it / K1_BN;
         const int col = n0 + cl;
         if (col < G.col_v || col >= G.col_g) continue;
@@ -148,8 +151,8 @@ struct K1Prob {
 };
 
 template <typename T>
-__global__ __launch_bounds__(GD_THREADS) void k1_pool_proj(const K1Params P) {
-  __shared__ __attribute__((aligned(16))) char lds[gd_lds_bytes_staged<K1_WM, K1_WN, K1_NST>()];
+__global__ __launch_bounds__(K1Cfg::THREADS) void k1_pool_proj(const K1Params P) {
+  __shared__ __attribute__((aligned(16))) char lds[K1Cfg::LDS_STAGED];
   const int tile = remap_xcd(blockIdx.x, P.per_xcd);
   if (tile >= P.total_tiles) return;
   int gi = 0;
@@ -158,11 +161,11 @@ __global__ __launch_bounds__(GD_THREADS) void k1_pool_proj(const K1Params P) {
   const int local = tile - G.tile_begin;
   const int tm = local / G.tiles_n, tn = local - tm * G.tiles_n;
   K1Prob<T> prob(P, G, tm * K1_BM, tn * K1_BN);
-  gemm_dma_tile<T, K1_WM, K1_WN, K1_NST>(prob, G.N - tn * K1_BN, lds);
+  gemm_dma_tile<T, K1Cfg>(prob, G.N - tn * K1_BN, lds);
 }
 
 hipError_t launch_k1(const K1Params& P, bool bf16_path, hipStream_t stream) {
-  const dim3 grid(P.per_xcd * N_XCD), block(GD_THREADS);
+  const dim3 grid(P.per_xcd * N_XCD), block(K1Cfg::THREADS);
   if (bf16_path)
     hipLaunchKernelGGL(k1_pool_proj<bf16>, grid, block, 0, stream, P);
   else
