@@ -3,22 +3,29 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload main]
 
-One step = one msgla_forward (pool+projection GEMM, chunk-local GLA kernel,
-chunk-state GLA kernel, hold+fusion+output-projection GEMM) over the whole
-batch, inputs and packed weights already resident in HBM.  W untimed warm-up
-steps, then K timed steps bracketed by device synchronisation; per-stage
-durations come from HIP events the library records on the same stream inside
-the timed region.  The single-scale GLA layer (4 heads at scale 1, same
-shapes) is timed the same way for the ratio.  The fp64 CPU oracle is timed on
-the host on a bounded sample of the same workload.  Prints one JSON line.
+One step = one msgla_forward (pooling prepass, projection GEMM, chunk-local
+GLA kernel, chunk-state GLA kernel, hold+fusion+output-projection GEMM) over
+the whole batch, inputs and packed weights already resident in HBM.  W untimed
+warm-up steps, then K timed steps bracketed by device synchronisation;
+per-kernel durations come from HIP events the library records on its own
+stream inside the timed region.  The single-scale GLA layer (4 heads at scale
+1, same shapes) is timed the same way for the ratio.  The fp64 CPU oracle is
+timed on the host on a bounded sample of the same workload.  Prints one JSON
+line.
 
 Inputs are seeded synthetic Gaussians (see scale_gla_layer_amd/synth.py);
 the workloads of the MS-GLA notes were trained-model runs on FineWeb-Edu, and
 the layer's cost does not depend on data values.
+
+    python bench.py --copy-calibration
+
+runs only a plain 256 MiB device copy (the reference kernel for scaling the
+FETCH_SIZE / WRITE_SIZE counters to bytes) and prints nothing else.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -30,26 +37,53 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK = {"bf16_mfma_tflops": 2500.0, "fp32_mfma_tflops": 157.3, "hbm_gbs": 8000.0}
-STAGES = ("pool_proj", "gla_chunk", "gla_state", "hold_fuse")
+# stage i of msgla_forward_timed and the kernel it times
+STAGES = ("pool", "proj", "gla_chunk", "gla_state", "hold_fuse")
+KERNELS = {"pool": "k_pool", "proj": "k1_pool_proj", "gla_chunk": "k2a_gla_chunk",
+           "gla_state": "k2b_gla_state", "hold_fuse": "k3_hold_fuse"}
+# sources a kernel's code depends on (a committed counter summary is only used
+# while these are unchanged)
+KERNEL_SOURCES = {
+    "k1_pool_proj": ["k_pool_proj.hip", "gemm_dma.hpp", "async_copy.hpp", "device_common.hpp",
+                     "layout.hpp"],
+    "k3_hold_fuse": ["k_hold_fuse.hip", "gemm_dma.hpp", "async_copy.hpp", "device_common.hpp",
+                     "layout.hpp"],
+    "k2a_gla_chunk": ["k_gla_chunk.hip", "device_common.hpp", "layout.hpp"],
+    "k2b_gla_state": ["k_gla_state.hip", "async_copy.hpp", "device_common.hpp", "layout.hpp"],
+    "k_pool": ["k_pool.hip", "device_common.hpp", "layout.hpp"],
+}
+COPY_CAL_BYTES = 256 << 20
 
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+def kernel_source_hash(kernel: str) -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, "scale_gla_layer_amd", "csrc", name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
 def algorithmic(cfg, B, L):
-    """Algorithmic flops and bytes of the layer and of each stage.
+    """Algorithmic flops and bytes of the layer and of each kernel.
 
     Flops: projections 2 T d (h(2dk+dv)+r), gate 2 T r h dk, GLA core
     T h (4 dk dv + (C+1)(dk+dv)) per pooled token T, output projection at the
-    coarse length 2 T h dv d, fusion logits 2 B L d m.  Bytes: x, out and the
-    weights once (storage type), the GLA core's q/k/v/g in and y out."""
+    coarse length 2 T h dv d, fusion logits 2 B L d m.  Layer bytes: x, out
+    and the weights once (storage type).  Per kernel: the pooling prepass
+    reads x and writes the block means; the GLA core moves q, k, v, the gate
+    factor and y once (split as q, k, g into the chunk-local kernel and v, y
+    through the state kernel); the GEMMs are counted by their flops."""
     es = 2 if cfg.dtype == "bf16" else 4
     d, dk, dv, r, C = cfg.d_model, cfg.d_k, cfg.d_v, cfg.gate_rank, cfg.chunk
     m = len(cfg.scales)
     f_proj = f_gate = f_scan = f_out = 0.0
     w_bytes = 0.0
-    core_bytes = 0.0
+    chunk_bytes = state_bytes = 0.0
+    pool_bytes = 0.0
     for s, h in zip(cfg.scales, cfg.heads):
         T = B * (L // s)
         f_proj += 2.0 * T * d * (h * (2 * dk + dv) + r)
@@ -57,7 +91,12 @@ def algorithmic(cfg, B, L):
         f_scan += float(T) * h * (4 * dk * dv + (C + 1) * (dk + dv))
         f_out += 2.0 * T * h * dv * d
         w_bytes += es * (d * (h * (2 * dk + dv) + r) + r * h * dk + h * dv * d) + 4 * h * dk
-        core_bytes += T * (h * (2 * dk + 2 * dv) * es + r * 4)
+        chunk_bytes += T * (h * 2 * dk * es + r * 4)
+        state_bytes += T * h * 2 * dv * es
+        if s > 1:
+            pool_bytes += T * d * es
+    if pool_bytes:
+        pool_bytes += B * L * d * es
     f_fuse = 2.0 * B * L * d * m if m > 1 else 0.0
     w_bytes += es * d * m if m > 1 else 0
     io_bytes = 2.0 * B * L * d * es
@@ -65,9 +104,10 @@ def algorithmic(cfg, B, L):
         "flops": f_proj + f_gate + f_scan + f_out + f_fuse,
         "bytes": io_bytes + w_bytes,
         "stage": {
-            "pool_proj": ("mfma", f_proj + f_fuse),
-            "gla_chunk": ("hbm", core_bytes),
-            "gla_state": ("hbm", core_bytes),
+            "pool": ("hbm", pool_bytes),
+            "proj": ("mfma", f_proj + f_fuse),
+            "gla_chunk": ("hbm", chunk_bytes),
+            "gla_state": ("hbm", state_bytes),
             "hold_fuse": ("mfma", f_out),
         },
     }
@@ -100,6 +140,20 @@ def time_forward(layer, x, steps, warmup, events_per_step=True):
     return dt / steps * 1e3, stage_ms
 
 
+def traffic_from_profile(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` from the committed counter summary, or
+    None when there is none or the kernel's sources changed since."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path, encoding="utf-8") as f:
+        rec = json.load(f)
+    if rec.get("source_hash") != kernel_source_hash(kernel):
+        log(f"[bench] {path}: counters predate the current {kernel} sources; traffic = null")
+        return None
+    return rec.get("hbm_bytes_per_dispatch")
+
+
 def cpu_baseline(cfg, X, W, budget_s=12.0):
     from oracle import msgla_oracle as orc
     try:
@@ -119,6 +173,112 @@ def cpu_baseline(cfg, X, W, budget_s=12.0):
                       f"BLAS threads {threads}, the recurrence loop itself is single-threaded)"}
 
 
+PROFILE_COMMANDS = {
+    "ktrace": "rocprofv3 --kernel-trace --stats -f csv -d {d}/ktrace -o main -- "
+              "python3 bench.py --steps 20 --warmup 5 --no-cpu-baseline --no-gla",
+    "fetch": "rocprofv3 --pmc FETCH_SIZE -f csv -d {d}/pmc_fetch -o main -- "
+             "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-gla",
+    "write": "rocprofv3 --pmc WRITE_SIZE -f csv -d {d}/pmc_write -o main -- "
+             "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-gla",
+    "cal_fetch": "rocprofv3 --pmc FETCH_SIZE -f csv -d {d}/cal_fetch -o copy -- "
+                 "python3 bench.py --copy-calibration",
+    "cal_write": "rocprofv3 --pmc WRITE_SIZE -f csv -d {d}/cal_write -o copy -- "
+                 "python3 bench.py --copy-calibration",
+}
+
+
+def _short(name: str) -> str:
+    for k in KERNELS.values():
+        if k in name:
+            return k
+    return name[:48]
+
+
+def _counter_means(path: str) -> dict:
+    import csv
+    acc = {}
+    with open(path, newline="", encoding="utf-8") as f:
+        for r in csv.DictReader(f):
+            acc.setdefault(_short(r["Kernel_Name"]), []).append(float(r["Counter_Value"]))
+    return {k: (sum(v) / len(v), len(v)) for k, v in acc.items()}
+
+
+def summarize_profiles(d: str, workload: str = "main"):
+    """Writes profiles/kernels_<workload>.md (kernel trace) and, per kernel of
+    the forward, profiles/<kernel>_<workload>_traffic.json (FETCH_SIZE and
+    WRITE_SIZE per dispatch scaled by the plain-copy calibration) from the
+    rocprofv3 output directories under d (see PROFILE_COMMANDS)."""
+    import csv
+    from scale_gla_layer_amd.config import WORKLOADS
+    wl = WORKLOADS[workload]
+    alg = algorithmic(wl.cfg, wl.batch, wl.seq_len)["stage"]
+    out_dir = os.path.join(ROOT, "profiles")
+    os.makedirs(out_dir, exist_ok=True)
+    cmds = {k: v.format(d="<out>") for k, v in PROFILE_COMMANDS.items()}
+
+    with open(os.path.join(d, "ktrace", "main_kernel_stats.csv"), newline="", encoding="utf-8") as f:
+        stats = list(csv.DictReader(f))
+    lines = [f"# Kernel trace, workload {workload} ({wl.description})", "",
+             "Command (from the repository root, `<out>` any output directory):", "",
+             f"    {cmds['ktrace']}", "",
+             "25 forwards (5 warm-up + 20 timed) under the tracer.", "",
+             "| kernel | calls | avg us | min us | max us | share |", "|---|---|---|---|---|---|"]
+    for r in stats:
+        lines.append(f"| {_short(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                     f"{float(r['Percentage']):.1f}% |")
+    with open(os.path.join(out_dir, f"kernels_{workload}.md"), "w", encoding="utf-8") as f:
+        f.write("\n".join(lines) + "\n")
+
+    cal_f = _counter_means(os.path.join(d, "cal_fetch", "copy_counter_collection.csv"))
+    cal_w = _counter_means(os.path.join(d, "cal_write", "copy_counter_collection.csv"))
+    # the copy is the runtime's buffer-copy blit of COPY_CAL_BYTES (read once, written once)
+    ref_f = cal_f["__amd_rocclr_copyBuffer"][0] * 1024.0
+    ref_w = cal_w["__amd_rocclr_copyBuffer"][0] * 1024.0
+    f_fac, w_fac = COPY_CAL_BYTES / ref_f, COPY_CAL_BYTES / ref_w
+    fetch = _counter_means(os.path.join(d, "pmc_fetch", "main_counter_collection.csv"))
+    write = _counter_means(os.path.join(d, "pmc_write", "main_counter_collection.csv"))
+    rows = ["# HBM traffic per dispatch, workload " + workload, "",
+            "Commands (from the repository root):", ""] + [f"    {cmds[k]}" for k in
+                                                        ("fetch", "write", "cal_fetch", "cal_write")]
+    rows += ["", f"Calibration: a plain copy of {COPY_CAL_BYTES} bytes reads FETCH_SIZE "
+             f"{ref_f / 1024:.0f} KiB and WRITE_SIZE {ref_w / 1024:.0f} KiB, so bytes = "
+             f"FETCH_SIZE x 1024 x {f_fac:.3f} + WRITE_SIZE x 1024 x {w_fac:.3f}.", "",
+             "| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM MB | algorithmic | traffic / algorithmic |",
+             "|---|---|---|---|---|---|"]
+    for stage, kernel in KERNELS.items():
+        if kernel not in fetch or kernel not in write:
+            continue
+        fk, wk = fetch[kernel][0], write[kernel][0]
+        hbm = fk * 1024 * f_fac + wk * 1024 * w_fac
+        bound, amount = alg[stage]
+        alg_txt = f"{amount / 1e6:.1f} MB" if bound == "hbm" else f"{amount / 1e9:.1f} GFLOP"
+        ratio = f"{hbm / amount:.2f}" if bound == "hbm" and amount else "-"
+        rows.append(f"| {kernel} | {fk:.0f} | {wk:.0f} | {hbm / 1e6:.1f} | {alg_txt} | {ratio} |")
+        rec = {"kernel": kernel, "workload": workload, "source_hash": kernel_source_hash(kernel),
+               "fetch_kib_per_dispatch": fk, "write_kib_per_dispatch": wk,
+               "fetch_factor": f_fac, "write_factor": w_fac, "hbm_bytes_per_dispatch": round(hbm),
+               "dispatches": fetch[kernel][1], "commands": [cmds[k] for k in
+                                                            ("fetch", "write", "cal_fetch", "cal_write")]}
+        with open(os.path.join(out_dir, f"{kernel}_{workload}_traffic.json"), "w", encoding="utf-8") as f:
+            json.dump(rec, f, indent=1)
+            f.write("\n")
+    with open(os.path.join(out_dir, f"traffic_{workload}.md"), "w", encoding="utf-8") as f:
+        f.write("\n".join(rows) + "\n")
+    log(f"[bench] wrote profiles for {workload} from {d}")
+
+
+def copy_calibration():
+    """A plain device copy of COPY_CAL_BYTES (read once, written once), 5 times."""
+    import torch
+    src = torch.ones(COPY_CAL_BYTES // 2, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"[bench] copy calibration: 5 copies of {COPY_CAL_BYTES} bytes")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -127,13 +287,23 @@ def main():
     ap.add_argument("--workload", default="main")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-gla", action="store_true", help="skip the single-scale GLA comparison")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run the plain-copy reference kernel for counter scaling")
+    ap.add_argument("--summarize-profiles", metavar="DIR",
+                    help="write profiles/ summaries from rocprofv3 output under DIR (no GPU)")
     args = ap.parse_args()
+    if args.summarize_profiles:
+        summarize_profiles(args.summarize_profiles, args.workload)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (this layer's path is built and timed on a single "
               f"MI355X); --gpus {args.gpus} is not supported.", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
 
-    import torch
+    import torch  # noqa: F401
     from scale_gla_layer_amd.config import WORKLOADS
     from scale_gla_layer_amd.runner import DeviceLayer, to_device
     from scale_gla_layer_amd.synth import make_inputs
@@ -141,32 +311,36 @@ def main():
     wl = WORKLOADS[args.workload]
     cfg, B, L = wl.cfg, wl.batch, wl.seq_len
     log(f"[bench] workload {wl.name}: {wl.description}")
+    log("[bench] kernel source hashes: " + json.dumps({k: kernel_source_hash(k) for k in KERNEL_SOURCES}))
     X, W = make_inputs(cfg, B, L, seed=0, gate_bias=wl.gate_bias)
     layer = DeviceLayer(cfg, W)
     x = to_device(X, cfg.dtype)
     ms, stage_ms = time_forward(layer, x, args.steps, args.warmup)
     tok_s = B * L / (ms * 1e-3)
-    log(f"[bench] {ms * 1e3:.1f} us/step, {tok_s / 1e6:.1f} M tokens/s; stages (us): " +
+    log(f"[bench] {ms * 1e3:.1f} us/step, {tok_s / 1e6:.1f} M tokens/s; kernels (us): " +
         ", ".join(f"{k} {v * 1e3:.1f}" for k, v in stage_ms.items()))
 
     alg = algorithmic(cfg, B, L)
     peak_f = PEAK["bf16_mfma_tflops"] if cfg.dtype == "bf16" else PEAK["fp32_mfma_tflops"]
     layer_tflops = alg["flops"] / (ms * 1e-3) / 1e12
     t_roof = max(alg["flops"] / (peak_f * 1e12), alg["bytes"] / (PEAK["hbm_gbs"] * 1e9))
-    dom = max(stage_ms, key=stage_ms.get)
-    bound, amount = alg["stage"][dom]
-    dur = stage_ms[dom] * 1e-3
-    if bound == "mfma":
-        achieved, peak, unit = amount / dur / 1e12, peak_f, "TFLOP/s"
-    else:
-        achieved, peak, unit = amount / dur / 1e9, PEAK["hbm_gbs"], "GB/s"
     stages = {}
     for name, t in stage_ms.items():
         b, a = alg["stage"][name]
+        if a <= 0:
+            continue
         rate = a / (t * 1e-3) / (1e12 if b == "mfma" else 1e9)
-        stages[name] = {"us": round(t * 1e3, 2), "bound": b,
+        peak = peak_f if b == "mfma" else PEAK["hbm_gbs"]
+        stages[name] = {"kernel": KERNELS[name], "us": round(t * 1e3, 2), "bound": b,
                         "achieved": round(rate, 1), "unit": "TFLOP/s" if b == "mfma" else "GB/s",
-                        "frac": round(rate / (peak_f if b == "mfma" else PEAK["hbm_gbs"]), 4)}
+                        "peak": peak, "frac": round(rate / peak, 4),
+                        "algorithmic": a}
+    dom = max(stages, key=lambda k: stages[k]["us"])
+    d = stages[dom]
+    roofline = {"bound": d["bound"], "kernel": d["kernel"], "achieved": d["achieved"],
+                "peak": d["peak"], "unit": d["unit"], "frac": d["frac"],
+                "traffic": traffic_from_profile(d["kernel"], wl.name),
+                "algorithmic_per_launch": d["algorithmic"]}
 
     ratio_vs_gla = None
     gla = None
@@ -204,14 +378,13 @@ def main():
         "config": {"workload": wl.name, "batch": B, "seq_len": L, "d_model": cfg.d_model,
                    "scales": list(cfg.scales), "heads": list(cfg.heads), "d_k": cfg.d_k,
                    "d_v": cfg.d_v, "gate_rank": cfg.gate_rank, "chunk": cfg.chunk},
-        "roofline": {"bound": bound, "kernel": dom, "achieved": round(achieved, 1), "peak": peak,
-                     "unit": unit, "frac": round(achieved / peak, 4), "traffic": None},
+        "roofline": roofline,
         "layer_roofline": {"algorithmic_gflop": round(alg["flops"] / 1e9, 2),
                            "algorithmic_mb": round(alg["bytes"] / 1e6, 2),
                            "achieved_tflops": round(layer_tflops, 1),
                            "t_roof_us": round(t_roof * 1e6, 2),
                            "frac": round(t_roof / (ms * 1e-3), 4)},
-        "stages": stages,
+        "kernels": stages,
         "ratio_vs_gla": None if ratio_vs_gla is None else round(ratio_vs_gla, 4),
         "gla_tokens_per_s": None if gla is None else round(gla, 1),
         "cpu_baseline": cpu,

@@ -164,11 +164,13 @@ msgla_status msgla_forward(const msgla_config* cfg, const void* packed, const vo
 /*
  * Optional per-stage timing: hipEvent_t handles recorded on `stream`
  * immediately before (start[i]) and after (stop[i]) stage i of the forward:
- * 0 = pooled projection GEMM, 1 = chunk-local gate/decay/intra-chunk kernel,
- * 2 = chunk-state recurrence kernel, 3 = hold + fusion + output projection
- * GEMM.  NULL entries are skipped.  Events are recorded, never waited on.
+ * 0 = pooling prepass (block means of the coarse scales; empty when every
+ * branch has scale 1), 1 = projection GEMM, 2 = chunk-local
+ * gate/decay/intra-chunk kernel, 3 = chunk-state recurrence kernel,
+ * 4 = hold + fusion + output projection GEMM.  NULL entries are skipped.
+ * Events are recorded, never waited on.
  */
-#define MSGLA_N_STAGES 4
+#define MSGLA_N_STAGES 5
 typedef struct {
   void* start[MSGLA_N_STAGES];
   void* stop[MSGLA_N_STAGES];

@@ -15,7 +15,7 @@ from typing import Optional, Sequence
 from .config import BF16, F32, MsglaConfig
 
 MAX_BRANCHES = 8
-N_STAGES = 4
+N_STAGES = 5
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmsgla.so")
 
 STATUS = {0: "MSGLA_OK", 1: "MSGLA_ERR_INVALID_ARG", 2: "MSGLA_ERR_UNSUPPORTED",
@@ -172,7 +172,7 @@ def msgla_state_init(cfg: MsglaConfig, B: int, state, stream=None):
 
 def msgla_forward(cfg: MsglaConfig, packed, x, B: int, L: int, out, workspace,
                   state_out=None, mask=None, state_in=None, stream=None, events=None):
-    """events: optional (start[4], stop[4]) lists of torch.cuda.Event (or None entries)."""
+    """events: optional (start[N_STAGES], stop[N_STAGES]) lists of torch.cuda.Event (or None entries)."""
     lib = load_library()
     args = (ctypes.byref(c_config(cfg)), _ptr(packed), _ptr(x), _ptr(mask), B, L, _ptr(out),
             _ptr(state_in), _ptr(state_out), _ptr(workspace),

@@ -513,17 +513,19 @@ msgla_status msgla_forward_timed(const msgla_config* cfg, const void* packed, co
 
   HIP_TRY(ev(0, true));
   for (int i = 0; i < npass; ++i) HIP_TRY(launch_pool(pp[i], g.bf16, st));
-  if (p1.total_tiles > 0) HIP_TRY(launch_k1(p1, g.bf16, st));
   HIP_TRY(ev(0, false));
   HIP_TRY(ev(1, true));
-  if (p2.total_units > 0) HIP_TRY(launch_k2a(p2, g.bf16, st));
+  if (p1.total_tiles > 0) HIP_TRY(launch_k1(p1, g.bf16, st));
   HIP_TRY(ev(1, false));
   HIP_TRY(ev(2, true));
-  if (p2.total_seqs > 0) HIP_TRY(launch_k2b(p2, g.bf16, st));
+  if (p2.total_units > 0) HIP_TRY(launch_k2a(p2, g.bf16, st));
   HIP_TRY(ev(2, false));
   HIP_TRY(ev(3, true));
-  HIP_TRY(launch_k3(p3, g.bf16, st));
+  if (p2.total_seqs > 0) HIP_TRY(launch_k2b(p2, g.bf16, st));
   HIP_TRY(ev(3, false));
+  HIP_TRY(ev(4, true));
+  HIP_TRY(launch_k3(p3, g.bf16, st));
+  HIP_TRY(ev(4, false));
 
   if (state_out) {
     StateParams ps{};
