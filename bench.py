@@ -38,16 +38,18 @@ sys.path.insert(0, ROOT)
 
 PEAK = {"bf16_mfma_tflops": 2500.0, "fp32_mfma_tflops": 157.3, "hbm_gbs": 8000.0}
 # stage i of msgla_forward_timed and the kernel it times
-STAGES = ("pool", "proj", "gla_chunk", "gla_state", "hold_fuse")
+STAGES = ("pool", "proj", "gla_chunk", "gla_state", "out_coarse", "hold_fuse")
 KERNELS = {"pool": "k_pool", "proj": "k1_pool_proj", "gla_chunk": "k2a_gla_chunk",
-           "gla_state": "k2b_gla_state", "hold_fuse": "k3_hold_fuse"}
+           "gla_state": "k2b_gla_state", "out_coarse": "k3c_coarse", "hold_fuse": "k3f_fine_fuse"}
 # sources a kernel's code depends on (a committed counter summary is only used
 # while these are unchanged)
 KERNEL_SOURCES = {
     "k1_pool_proj": ["k_pool_proj.hip", "gemm_dma.hpp", "async_copy.hpp", "device_common.hpp",
                      "layout.hpp"],
-    "k3_hold_fuse": ["k_hold_fuse.hip", "gemm_dma.hpp", "async_copy.hpp", "device_common.hpp",
-                     "layout.hpp"],
+    "k3c_coarse": ["k_hold_fuse.hip", "gemm_dma.hpp", "async_copy.hpp", "device_common.hpp",
+                   "layout.hpp"],
+    "k3f_fine_fuse": ["k_hold_fuse.hip", "gemm_dma.hpp", "async_copy.hpp", "device_common.hpp",
+                      "layout.hpp"],
     "k2a_gla_chunk": ["k_gla_chunk.hip", "device_common.hpp", "layout.hpp"],
     "k2b_gla_state": ["k_gla_state.hip", "async_copy.hpp", "device_common.hpp", "layout.hpp"],
     "k_pool": ["k_pool.hip", "device_common.hpp", "layout.hpp"],
@@ -76,11 +78,14 @@ def algorithmic(cfg, B, L):
     and the weights once (storage type).  Per kernel: the pooling prepass
     reads x and writes the block means; the GLA core moves q, k, v, the gate
     factor and y once (split as q, k, g into the chunk-local kernel and v, y
-    through the state kernel); the GEMMs are counted by their flops."""
+    through the state kernel); the GEMMs are counted by their flops (the
+    output projections split into the coarse branches and the scale-1
+    branch, whose GEMM carries the hold and fusion)."""
     es = 2 if cfg.dtype == "bf16" else 4
     d, dk, dv, r, C = cfg.d_model, cfg.d_k, cfg.d_v, cfg.gate_rank, cfg.chunk
     m = len(cfg.scales)
-    f_proj = f_gate = f_scan = f_out = 0.0
+    f_proj = f_gate = f_scan = f_out = f_out_coarse = 0.0
+    fuse_bytes = 2.0 * B * L * d * es if len(cfg.scales) > 1 else 0.0
     w_bytes = 0.0
     chunk_bytes = state_bytes = 0.0
     pool_bytes = 0.0
@@ -90,6 +95,9 @@ def algorithmic(cfg, B, L):
         f_gate += 2.0 * T * r * h * dk
         f_scan += float(T) * h * (4 * dk * dv + (C + 1) * (dk + dv))
         f_out += 2.0 * T * h * dv * d
+        if s > 1:
+            f_out_coarse += 2.0 * T * h * dv * d
+            fuse_bytes += T * d * es
         w_bytes += es * (d * (h * (2 * dk + dv) + r) + r * h * dk + h * dv * d) + 4 * h * dk
         chunk_bytes += T * (h * 2 * dk * es + r * 4)
         state_bytes += T * h * 2 * dv * es
@@ -108,7 +116,10 @@ def algorithmic(cfg, B, L):
             "proj": ("mfma", f_proj + f_fuse),
             "gla_chunk": ("hbm", chunk_bytes),
             "gla_state": ("hbm", state_bytes),
-            "hold_fuse": ("mfma", f_out),
+            "out_coarse": ("mfma", f_out_coarse),
+            # the scale-1 projection if there is one, else the hold + fusion traffic
+            "hold_fuse": ("mfma", f_out - f_out_coarse) if f_out > f_out_coarse else
+                         ("hbm", fuse_bytes),
         },
     }
 

@@ -167,10 +167,11 @@ msgla_status msgla_forward(const msgla_config* cfg, const void* packed, const vo
  * 0 = pooling prepass (block means of the coarse scales; empty when every
  * branch has scale 1), 1 = projection GEMM, 2 = chunk-local
  * gate/decay/intra-chunk kernel, 3 = chunk-state recurrence kernel,
- * 4 = hold + fusion + output projection GEMM.  NULL entries are skipped.
- * Events are recorded, never waited on.
+ * 4 = output projections of the coarse branches (empty without one),
+ * 5 = scale-1 output projection + causal hold + fusion.  NULL entries are
+ * skipped.  Events are recorded, never waited on.
  */
-#define MSGLA_N_STAGES 5
+#define MSGLA_N_STAGES 6
 typedef struct {
   void* start[MSGLA_N_STAGES];
   void* stop[MSGLA_N_STAGES];

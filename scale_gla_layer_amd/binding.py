@@ -15,7 +15,7 @@ from typing import Optional, Sequence
 from .config import BF16, F32, MsglaConfig
 
 MAX_BRANCHES = 8
-N_STAGES = 5
+N_STAGES = 6
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmsgla.so")
 
 STATUS = {0: "MSGLA_OK", 1: "MSGLA_ERR_INVALID_ARG", 2: "MSGLA_ERR_UNSUPPORTED",

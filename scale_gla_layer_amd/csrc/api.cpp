@@ -16,7 +16,8 @@ hipError_t launch_pool(const PoolParams& P, bool bf16_path, hipStream_t st);
 hipError_t launch_k1(const K1Params& P, bool bf16_path, hipStream_t stream);
 hipError_t launch_k2a(const K2Params& P, bool bf16_path, hipStream_t stream);
 hipError_t launch_k2b(const K2Params& P, bool bf16_path, hipStream_t stream);
-hipError_t launch_k3(const K3Params& P, bool bf16_path, hipStream_t stream);
+hipError_t launch_k3c(const K3Params& P, bool bf16_path, hipStream_t stream);
+hipError_t launch_k3f(const K3Params& P, bool bf16_path, hipStream_t stream);
 hipError_t launch_state_export(const StateParams& P, bool bf16_path, hipStream_t st);
 hipError_t launch_state_header(void* state, int B, int m, int64_t pos, hipStream_t st);
 hipError_t launch_decode(const DecParams& P, int Nmax, int hmax, bool bf16_path, hipStream_t st);
@@ -455,6 +456,8 @@ msgla_status msgla_forward_timed(const msgla_config* cfg, const void* packed, co
   p2.n_dvt = g.dv / k2b_dvt();
 
   // ---------------- K3 ----------------
+  // coarse outputs Y = y W_o reuse the block-mean buffers of their branch
+  // (same [B][n][d] shape, dead once the projection GEMM has run)
   K3Params p3{};
   p3.B = (int)B;
   p3.L = (int)L;
@@ -462,13 +465,13 @@ msgla_status msgla_forward_timed(const msgla_config* cfg, const void* packed, co
   p3.dv = g.dv;
   p3.m = g.m;
   p3.Ktot = g.Ktot;
+  p3.fine = -1;
   p3.tiles_n = cdiv(g.d, GEMM_TILE);
-  p3.total_tiles = cdiv((int)(B * L), GEMM_TILE) * p3.tiles_n;
-  p3.per_xcd = cdiv(p3.total_tiles, N_XCD);
   p3.WoT = at<char>(packed, g.off_WoT);
   p3.zero = at<char>(packed, g.off_zero);
   p3.w = at<float>(workspace, W.w);
   p3.out = out;
+  int ctiles = 0;
   for (int i = 0; i < g.m; ++i) {
     K3Branch& k = p3.br[i];
     k.y = at<char>(workspace, W.br[i].y);
@@ -477,8 +480,19 @@ msgla_status msgla_forward_timed(const msgla_config* cfg, const void* packed, co
     k.np = W.br[i].np;
     k.n = W.br[i].n;
     k.ko = g.br[i].ko;
-    k.kp = g.br[i].kp;
+    if (k.s == 1) {
+      p3.fine = i;
+    } else if (k.n > 0) {
+      k.yc = at<char>(workspace, W.br[i].xp);
+      k.tile_begin = ctiles;
+      ctiles += cdiv((int)B * k.n, GEMM_TILE) * p3.tiles_n;
+      p3.coarse[p3.ncoarse++] = i;
+    }
   }
+  p3.c_total = ctiles;
+  p3.c_per_xcd = cdiv(ctiles, N_XCD);
+  p3.f_total = cdiv((int)(B * L), GEMM_TILE) * p3.tiles_n;
+  p3.f_per_xcd = cdiv(p3.f_total, N_XCD);
 
   // pooling prepass: one pass for the scales dividing the largest coarse scale,
   // one more per remaining coarse scale
@@ -524,8 +538,11 @@ msgla_status msgla_forward_timed(const msgla_config* cfg, const void* packed, co
   if (p2.total_seqs > 0) HIP_TRY(launch_k2b(p2, g.bf16, st));
   HIP_TRY(ev(3, false));
   HIP_TRY(ev(4, true));
-  HIP_TRY(launch_k3(p3, g.bf16, st));
+  HIP_TRY(launch_k3c(p3, g.bf16, st));
   HIP_TRY(ev(4, false));
+  HIP_TRY(ev(5, true));
+  HIP_TRY(launch_k3f(p3, g.bf16, st));
+  HIP_TRY(ev(5, false));
 
   if (state_out) {
     StateParams ps{};

@@ -1,21 +1,23 @@
-// K3 — causal hold, softmax fusion and the per-branch output projections as
-// one GEMM.
+// K3 — per-branch output projections, causal hold and softmax fusion.
 //
 // MS-GLA notes, Sec. 3.2 (each branch projects back to the common d space with
 // its own output projection) and Sec. 3.3 (causal upsampling: coarse output j
 // of branch s is usable from position (j+1)s-1 until block j+1 completes, zero
 // before the first block; Eqs. (10)-(11): O_t = sum_i w_{t,i} Yhat^{(i)}_t).
-// Because W_o^{(i)} is linear,
-//   O_t = sum_i w_{t,i} y^{(i)}_{j_i(t)} W_o^{(i)}
-//       = [w_{t,1} y^{(1)}_{j_1(t)} | ... | w_{t,m} y^{(m)}_{j_m(t)}] [W_o^{(1)}; ...; W_o^{(m)}],
-// with j_i(t) = floor((t+1)/s_i) - 1 (a zero row when negative).  The A rows are
-// gathered straight from the held coarse rows by the asynchronous copies of
-// gemm_dma.hpp (a per-row source address; zeros come from a zero block), B is
-// the stacked W_o^T.  Each 128-byte K segment lies inside one head of one
-// branch, so the fusion weight is applied once per branch instead of per
-// element: the accumulators of branch i are folded into the total as
-// total += w_{t,i} * acc at the branch's last K segment.  The epilogue writes O
-// row-major.
+//
+// Two launches:
+//  K3c  Y^{(i)} = y^{(i)} W_o^{(i)} at the coarse length for every branch with
+//       s > 1 (one grouped GEMM), written in the storage type.  Projecting
+//       before the hold costs 2 (BL/s) h d_v d flops instead of s times that.
+//  K3f  the scale-1 branch's projection y^{(1)} W_o^{(1)} (if there is one) as
+//       a GEMM whose epilogue forms
+//         O_t = w_{t,1} (y^{(1)} W_o^{(1)})_t + sum_{s_i > 1} w_{t,i} Y^{(i)}_{j_i(t)},
+//       j_i(t) = floor((t+1)/s_i) - 1 (the term is absent while negative), and
+//       writes O row-major.  Without a scale-1 branch the GEMM part is empty.
+// The A rows of both GEMMs are the per-head y rows of one coarse position,
+// gathered by the asynchronous copies of gemm_dma.hpp (each K segment of
+// 128 bytes lies inside one head); B is the branch's slice of the stacked
+// W_o^T.
 #include "device_common.hpp"
 #include "gemm_dma.hpp"
 #include "layout.hpp"
@@ -23,167 +25,245 @@
 namespace msgla {
 
 using K3Cfg = GemmCfg<4, 4, 2, 2, 128, 2>;  // 128 x 128 tiles, 4 waves, double-buffered 128-byte K segments
-constexpr int K3_WM = K3Cfg::WM, K3_WN = K3Cfg::WN;
 constexpr int K3_BM = K3Cfg::BM, K3_BN = K3Cfg::BN;
-// the tile's fusion weights [BM][FUSION_STRIDE] fp32 live in LDS after the stages
-constexpr int K3_W_OFF = K3Cfg::LDS;
-constexpr int K3_LDS = K3Cfg::LDS_STAGED > K3_W_OFF + K3_BM * FUSION_STRIDE * 4
-                           ? K3Cfg::LDS_STAGED
-                           : K3_W_OFF + K3_BM * FUSION_STRIDE * 4;
-static_assert(K3_BM * FUSION_STRIDE * 4 == K3Cfg::THREADS * 16, "one 16-byte piece per thread");
+using K3Acc = f32x4[K3Cfg::WM][K3Cfg::WN];
 
+// A operand: rows (b, j) of one branch's y, K = the branch's h d_v columns;
+// B operand: the branch's rows of W_o^T.
 template <typename T>
-struct K3Prob {
+struct K3Rows {
   const K3Params& P;
+  const K3Branch& Br;
   int m0, n0;
-  int rb[K3Cfg::A_SLOTS], rt[K3Cfg::A_SLOTS];  // sequence / position of the lane's copy rows (-1: none)
+  const char* arow[K3Cfg::A_SLOTS];  // head-0 segment of the lane's copy rows (nullptr: zero row)
   const char* brow[K3Cfg::B_SLOTS];
-  const char* arow[K3Cfg::A_SLOTS];            // row base of the branch currently being copied
-  int ib_issue = -1;           // branch of the K segments being copied
-  int ib_fold = 0;             // branch of the K segments being multiplied
-  f32x4 total[K3_WM][K3_WN];
-  const float* wl = nullptr;   // LDS copy of the tile's fusion weights
+  size_t seg_off = 0;
 
-  __device__ K3Prob(const K3Params& p, int m0_, int n0_) : P(p), m0(m0_), n0(n0_) {}
+  __device__ K3Rows(const K3Params& p, const K3Branch& br, int m0_, int n0_)
+      : P(p), Br(br), m0(m0_), n0(n0_) {}
 
-  __device__ int nk() const { return P.Ktot * (int)sizeof(T) / K3Cfg::KSEG; }
-  __device__ int seg_begin(int i) const { return P.br[i].ko * (int)sizeof(T) / K3Cfg::KSEG; }
-  __device__ int branch_of(int kt) const {
-    int bi = 0;
-    while (bi + 1 < P.m && kt >= seg_begin(bi + 1)) ++bi;
-    return bi;
-  }
-  __device__ void setup(int wave, int lane) {
+  __device__ int nk() const { return Br.h * P.dv * (int)sizeof(T) / K3Cfg::KSEG; }
+  // rows: (b, j) = (m / rows_per_seq, m % rows_per_seq), M = B * rows_per_seq
+  __device__ void setup_rows(int wave, int lane, int rows_per_seq) {
+    const int M = P.B * rows_per_seq;
 #pragma unroll
     for (int j = 0; j < K3Cfg::A_SLOTS; ++j) {
       const int m = m0 + K3Cfg::a_row(j, wave, lane);
-      rb[j] = (m < P.B * P.L) ? m / P.L : -1;
-      rt[j] = (m < P.B * P.L) ? m - rb[j] * P.L : 0;
+      const int b = m / rows_per_seq, r = m - b * rows_per_seq;
+      arow[j] = (m < M) ? reinterpret_cast<const char*>(Br.y) +
+                              ((size_t)b * Br.h * Br.np + r) * P.dv * sizeof(T)
+                        : nullptr;
     }
 #pragma unroll
     for (int j = 0; j < K3Cfg::B_SLOTS; ++j) {
       const int n = n0 + K3Cfg::b_row(j, wave, lane);
-      brow[j] = reinterpret_cast<const char*>(P.WoT) + (size_t)(n < P.d ? n : 0) * P.Ktot * sizeof(T);
-    }
-    if (P.m > 1) {
-#pragma unroll
-      for (int a = 0; a < K3_WM; ++a)
-#pragma unroll
-        for (int b = 0; b < K3_WN; ++b) total[a][b] = zero4();
+      brow[j] = reinterpret_cast<const char*>(P.WoT) +
+                ((size_t)(n < P.d ? n : 0) * P.Ktot + Br.ko) * sizeof(T);
     }
   }
-  // stage the tile's fusion weights (consumed by fold, which runs after at
-  // least one LDS barrier of the K loop; the final staging of the output
-  // overwrites them only after the last fold)
-  __device__ void started(char* lds) {
-    float* w = reinterpret_cast<float*>(lds + K3_W_OFF);
-    if (P.m > 1) {
-      const int tid = threadIdx.x;
-      const int r = tid / (FUSION_STRIDE / 4), m = m0 + r;
-      st16(w + 4 * tid, m < P.B * P.L ? ld16(P.w + (size_t)m * FUSION_STRIDE + 4 * (tid % (FUSION_STRIDE / 4)))
-                                       : zero16());
-    }
-    wl = w;
-  }
-  // held coarse row of each copy row for branch bi (zero block before the first block)
-  __device__ void enter_branch(int bi) {
-    const K3Branch& Br = P.br[bi];
-#pragma unroll
-    for (int j = 0; j < K3Cfg::A_SLOTS; ++j) {
-      const int jr = (rt[j] + 1) / Br.s - 1;
-      arow[j] = (rb[j] < 0 || jr < 0)
-                    ? nullptr
-                    : reinterpret_cast<const char*>(Br.y) +
-                          ((size_t)rb[j] * Br.h * Br.np + jr) * P.dv * sizeof(T);
-    }
-    ib_issue = bi;
-  }
-  // per copied segment: branch (switching the held rows when it changes) and the
-  // byte offset of the segment inside a held row of that branch
-  size_t seg_off = 0;
+  __device__ void started(char*) {}
+  // byte offset of K segment kt inside the branch's head-major y rows
   __device__ void prep(int kt) {
-    const int bi = branch_of(kt);
-    if (bi != ib_issue) enter_branch(bi);
     const int head_bytes = P.dv * (int)sizeof(T);
-    const int kb = (kt - seg_begin(bi)) * K3Cfg::KSEG;  // bytes into the branch's K range
-    const int hh = kb / head_bytes;             // head of this segment
-    seg_off = (size_t)hh * P.br[bi].np * head_bytes + (kb - hh * head_bytes);
+    const int kb = kt * K3Cfg::KSEG;
+    const int hh = kb / head_bytes;
+    seg_off = (size_t)hh * Br.np * head_bytes + (kb - hh * head_bytes);
   }
   __device__ const char* a_row(int j, int) const {
     return arow[j] ? arow[j] + seg_off : reinterpret_cast<const char*>(P.zero);
   }
   __device__ const char* b_row(int j, int kt) const { return brow[j] + kt * K3Cfg::KSEG; }
-  __device__ bool seg_end(int kt) const {
-    return P.m > 1 && (ib_fold + 1 >= P.m ? kt + 1 == nk() : kt + 1 == seg_begin(ib_fold + 1));
+  __device__ bool seg_end(int) const { return false; }
+  __device__ void fold(K3Acc&, int, int, int) {}
+  __device__ void finish(K3Acc&, int, int, int) {}
+};
+
+template <typename T>
+__device__ __forceinline__ void k3_store8(T* dst, const float* v) {
+  if constexpr (sizeof(T) == 2) {
+    st16(dst, pack16<T>(v));
+  } else {
+    st16(dst, pack16<T>(v));
+    st16(dst + 4, pack16<T>(v + 4));
   }
-  // total += w_{row, branch} * acc for the 16 rows this lane holds; acc = 0
-  __device__ void fold(f32x4 (&acc)[K3_WM][K3_WN], int wr, int wc, int lane) {
-    const int lgrp = lane >> 4;
-#pragma unroll
-    for (int a = 0; a < K3_WM; ++a)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float w = wl[(wr * 16 * K3_WM + 16 * a + 4 * lgrp + e) * FUSION_STRIDE + ib_fold];
-#pragma unroll
-        for (int b = 0; b < K3_WN; ++b) {
-          total[a][b][e] += w * acc[a][b][e];
-          acc[a][b][e] = 0.f;
-        }
-      }
-    ++ib_fold;
-    (void)wc;
+}
+
+template <typename T>
+__device__ __forceinline__ void k3_load8(const T* src, float* v) {
+  if constexpr (sizeof(T) == 2) {
+    unpack16<T>(ld16(src), v);
+  } else {
+    unpack16<T>(ld16(src), v);
+    unpack16<T>(ld16(src + 4), v + 4);
   }
-  __device__ void finish(f32x4 (&acc)[K3_WM][K3_WN], int, int, int) {
-    if (P.m > 1) {
-#pragma unroll
-      for (int a = 0; a < K3_WM; ++a)
-#pragma unroll
-        for (int b = 0; b < K3_WN; ++b) acc[a][b] = total[a][b];
-    }
-  }
-  __device__ void store(const f32x4 (&acc)[K3_WM][K3_WN], int wr, int wc, int lane, char* lds) {
+}
+
+// ---- K3c: coarse projections, Y^{(i)} [B][n_i][d] ----
+template <typename T>
+struct K3Coarse : K3Rows<T> {
+  using K3Rows<T>::K3Rows;
+  __device__ void setup(int wave, int lane) { this->setup_rows(wave, lane, this->Br.n); }
+  __device__ void store(const K3Acc& acc, int wr, int wc, int lane, char* lds) {
     float* C = reinterpret_cast<float*>(lds);
     gd_stage_tile<K3Cfg>(acc, wr, wc, lane, C);
     lds_barrier();
-    epilogue(C, K3Cfg::LDC);
-  }
-  __device__ void epilogue(const float* C, int ldc) {
-    const int tid = threadIdx.x;
-    T* out = reinterpret_cast<T*>(P.out);
-    for (int it = tid; it < K3_BM * (K3_BN / 8); it += K3Cfg::THREADS) {
+    const K3Params& P = this->P;
+    const int M = P.B * this->Br.n;
+    T* yc = reinterpret_cast<T*>(this->Br.yc);
+    for (int it = threadIdx.x; it < K3_BM * (K3_BN / 8); it += K3Cfg::THREADS) {
       const int r = it / (K3_BN / 8), cg = it % (K3_BN / 8);
-      const int m = m0 + r, col = n0 + cg * 8;
-      if (m >= P.B * P.L || col >= P.d) continue;
-      float v[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = C[r * ldc + cg * 8 + e];
-      T* dst = out + (size_t)m * P.d + col;
-      if constexpr (sizeof(T) == 2) {
-        st16(dst, pack16<T>(v));
-      } else {
-        st16(dst, pack16<T>(v));
-        st16(dst + 4, pack16<T>(v + 4));
-      }
+      const int m = this->m0 + r, col = this->n0 + cg * 8;
+      if (m >= M || col >= P.d) continue;
+      k3_store8(yc + (size_t)m * P.d + col, C + r * K3Cfg::LDC + cg * 8);
     }
   }
 };
 
 template <typename T>
-__global__ __launch_bounds__(K3Cfg::THREADS) __attribute__((amdgpu_waves_per_eu(2))) void k3_hold_fuse(const K3Params P) {
-  __shared__ __attribute__((aligned(16))) char lds[K3_LDS];
-  const int tile = remap_xcd(blockIdx.x, P.per_xcd);
-  if (tile >= P.total_tiles) return;
-  const int tm = tile / P.tiles_n, tn = tile - tm * P.tiles_n;
-  K3Prob<T> prob(P, tm * K3_BM, tn * K3_BN);
+__global__ __launch_bounds__(K3Cfg::THREADS) void k3c_coarse(const K3Params P) {
+  __shared__ __attribute__((aligned(16))) char lds[K3Cfg::LDS_STAGED];
+  const int tile = remap_xcd(blockIdx.x, P.c_per_xcd);
+  if (tile >= P.c_total) return;
+  int ci = 0;
+  while (ci + 1 < P.ncoarse && tile >= P.br[P.coarse[ci + 1]].tile_begin) ++ci;
+  const K3Branch& Br = P.br[P.coarse[ci]];
+  const int local = tile - Br.tile_begin;
+  const int tm = local / P.tiles_n, tn = local - tm * P.tiles_n;
+  K3Coarse<T> prob(P, Br, tm * K3_BM, tn * K3_BN);
   gemm_dma_tile<T, K3Cfg>(prob, P.d - tn * K3_BN, lds);
 }
 
-hipError_t launch_k3(const K3Params& P, bool bf16_path, hipStream_t stream) {
-  const dim3 grid(P.per_xcd * N_XCD), block(K3Cfg::THREADS);
+// ---- K3f: scale-1 projection + hold + fusion -> O [B][L][d] ----
+// The tile's fusion weights are staged in LDS behind the output staging area
+// when the GEMM starts; the epilogue walks the tile 4 row pieces at a time,
+// issuing all gathered loads of the NC coarse branches for those pieces
+// before using any of them.
+constexpr int K3F_W_OFF = K3Cfg::LDS_STAGED;
+constexpr int K3F_LDS = K3F_W_OFF + K3_BM * FUSION_STRIDE * 4;
+static_assert(K3_BM * FUSION_STRIDE * 4 == K3Cfg::THREADS * 16, "one 16-byte piece per thread");
+
+template <typename T, int NC>
+struct K3Fine : K3Rows<T> {
+  bool has_fine;
+  __device__ K3Fine(const K3Params& p, const K3Branch& br, bool fine, int m0_, int n0_)
+      : K3Rows<T>(p, br, m0_, n0_), has_fine(fine) {}
+  __device__ int nk() const { return has_fine ? K3Rows<T>::nk() : 0; }
+  __device__ void setup(int wave, int lane) {
+    if (has_fine) this->setup_rows(wave, lane, this->P.L);
+  }
+  __device__ void started(char* lds) {
+    const K3Params& P = this->P;
+    if (P.m > 1) {
+      const int tid = threadIdx.x;
+      const int m = this->m0 + tid / (FUSION_STRIDE / 4);
+      st16(lds + K3F_W_OFF + 16 * tid,
+           m < P.B * P.L ? ld16(P.w + (size_t)m * FUSION_STRIDE + 4 * (tid % (FUSION_STRIDE / 4)))
+                         : zero16());
+    }
+  }
+  __device__ void store(const K3Acc& acc, int wr, int wc, int lane, char* lds) {
+    float* C = reinterpret_cast<float*>(lds);
+    const float* wl = reinterpret_cast<const float*>(lds + K3F_W_OFF);
+    if (has_fine) gd_stage_tile<K3Cfg>(acc, wr, wc, lane, C);
+    lds_barrier();  // staged tile and fusion weights visible to all waves
+    const K3Params& P = this->P;
+    T* out = reinterpret_cast<T*>(P.out);
+    constexpr int PIECES = K3_BM * (K3_BN / 8), U = 4;
+    static_assert(PIECES % (U * K3Cfg::THREADS) == 0, "epilogue batches");
+#pragma unroll 1
+    for (int it0 = threadIdx.x; it0 < PIECES; it0 += U * K3Cfg::THREADS) {
+      int r[U], col[U], b[U], t[U];
+      bool ok[U];
+      float y[U][NC > 0 ? NC : 1][8];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int it = it0 + u * K3Cfg::THREADS;
+        r[u] = it / (K3_BN / 8);
+        col[u] = this->n0 + (it % (K3_BN / 8)) * 8;
+        const int m = this->m0 + r[u];
+        ok[u] = m < P.B * P.L && col[u] < P.d;
+        b[u] = m / P.L;
+        t[u] = m - b[u] * P.L;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          const K3Branch& Bi = P.br[P.coarse[c]];
+          const int j = (t[u] + 1) / Bi.s - 1;  // held coarse row (none before the first block)
+          if (ok[u] && j >= 0) {
+            k3_load8(reinterpret_cast<const T*>(Bi.yc) + ((size_t)b[u] * Bi.n + j) * P.d + col[u], y[u][c]);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) y[u][c][e] = 0.f;
+          }
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (!ok[u]) continue;
+        const float* wr_ = wl + r[u] * FUSION_STRIDE;
+        float v[8];
+        if (has_fine) {
+          const float wf = P.m > 1 ? wr_[P.fine] : 1.f;
+          const float* crow = C + r[u] * K3Cfg::LDC + (col[u] - this->n0);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = wf * crow[e];
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = 0.f;
+        }
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          const float wi = P.m > 1 ? wr_[P.coarse[c]] : 1.f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] += wi * y[u][c][e];
+        }
+        k3_store8(out + (size_t)(this->m0 + r[u]) * P.d + col[u], v);
+      }
+    }
+  }
+};
+
+template <typename T, int NC>
+__global__ __launch_bounds__(K3Cfg::THREADS) void k3f_fine_fuse(const K3Params P) {
+  __shared__ __attribute__((aligned(16))) char lds[K3F_LDS];
+  const int tile = remap_xcd(blockIdx.x, P.f_per_xcd);
+  if (tile >= P.f_total) return;
+  const int tm = tile / P.tiles_n, tn = tile - tm * P.tiles_n;
+  const bool fine = P.fine >= 0;
+  K3Fine<T, NC> prob(P, P.br[fine ? P.fine : 0], fine, tm * K3_BM, tn * K3_BN);
+  gemm_dma_tile<T, K3Cfg>(prob, P.d - tn * K3_BN, lds);
+}
+
+hipError_t launch_k3c(const K3Params& P, bool bf16_path, hipStream_t stream) {
+  if (P.c_total == 0) return hipSuccess;
+  const dim3 grid(P.c_per_xcd * N_XCD), block(K3Cfg::THREADS);
   if (bf16_path)
-    hipLaunchKernelGGL(k3_hold_fuse<bf16>, grid, block, 0, stream, P);
+    hipLaunchKernelGGL(k3c_coarse<bf16>, grid, block, 0, stream, P);
   else
-    hipLaunchKernelGGL(k3_hold_fuse<float>, grid, block, 0, stream, P);
+    hipLaunchKernelGGL(k3c_coarse<float>, grid, block, 0, stream, P);
+  return hipGetLastError();
+}
+
+template <typename T>
+static void launch_k3f_t(const K3Params& P, dim3 grid, dim3 block, hipStream_t stream) {
+  switch (P.ncoarse) {
+    case 0: hipLaunchKernelGGL((k3f_fine_fuse<T, 0>), grid, block, 0, stream, P); break;
+    case 1: hipLaunchKernelGGL((k3f_fine_fuse<T, 1>), grid, block, 0, stream, P); break;
+    case 2: hipLaunchKernelGGL((k3f_fine_fuse<T, 2>), grid, block, 0, stream, P); break;
+    case 3: hipLaunchKernelGGL((k3f_fine_fuse<T, 3>), grid, block, 0, stream, P); break;
+    case 4: hipLaunchKernelGGL((k3f_fine_fuse<T, 4>), grid, block, 0, stream, P); break;
+    case 5: hipLaunchKernelGGL((k3f_fine_fuse<T, 5>), grid, block, 0, stream, P); break;
+    case 6: hipLaunchKernelGGL((k3f_fine_fuse<T, 6>), grid, block, 0, stream, P); break;
+    case 7: hipLaunchKernelGGL((k3f_fine_fuse<T, 7>), grid, block, 0, stream, P); break;
+    default: hipLaunchKernelGGL((k3f_fine_fuse<T, 8>), grid, block, 0, stream, P); break;
+  }
+}
+
+hipError_t launch_k3f(const K3Params& P, bool bf16_path, hipStream_t stream) {
+  const dim3 grid(P.f_per_xcd * N_XCD), block(K3Cfg::THREADS);
+  if (bf16_path)
+    launch_k3f_t<bf16>(P, grid, block, stream);
+  else
+    launch_k3f_t<float>(P, grid, block, stream);
   return hipGetLastError();
 }
 

@@ -130,17 +130,24 @@ struct K2Params {
   K2Branch br[MSGLA_MAX_BRANCHES];
 };
 
-// ---------------- K3: hold + fusion + stacked output projection GEMM ----------
+// ---------------- K3: output projections, hold and fusion ---------------------
 struct K3Branch {
   const void* y;    // [B][h][np][dv]
+  void* yc;         // coarse outputs y W_o [B][n][d] (branches with s > 1)
   int s, h, np, n;
-  int ko, kp;       // K offset / padded K range in the stacked W_o^T
+  int ko;           // K offset of the branch in the stacked W_o^T
+  int tile_begin;   // first tile of the branch in the coarse work list
 };
 
 struct K3Params {
   int B, L, d, dv, m, Ktot;
-  const void* zero; // >= 128 zero bytes (rows before a branch's first block)
-  int total_tiles, tiles_n, per_xcd;
+  int fine;                           // branch with scale 1, or -1
+  int ncoarse;                        // branches with s > 1, in work-list order
+  int coarse[MSGLA_MAX_BRANCHES];
+  int tiles_n;                        // column tiles of d
+  int c_total, c_per_xcd;             // coarse GEMM work list (K3c)
+  int f_total, f_per_xcd;             // fine GEMM + fusion work list (K3f)
+  const void* zero; // >= 128 zero bytes (rows outside the problem)
   const void* WoT;  // [d][Ktot]
   const float* w;   // fusion weights [B L][8]
   void* out;        // [B][L][d]
