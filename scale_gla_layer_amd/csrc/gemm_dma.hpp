@@ -31,6 +31,8 @@
 //   void finish(acc, wr, wc, lane)      final accumulators into acc
 //   void store(acc, wr, wc, lane, lds)  write the tile out (LDS may be reused)
 #pragma once
+#include <type_traits>
+
 #include "async_copy.hpp"
 #include "device_common.hpp"
 
@@ -134,29 +136,37 @@ __device__ __forceinline__ void gemm_dma_tile(Prob& prob, int n_valid, char* lds
   for (int kt = 0; kt < NST - 1 && kt < nk; ++kt) issue(kt);
   prob.started(lds);
 
-  for (int kt = 0; kt < nk; ++kt) {
-    // segment kt has landed once only the copies of later segments remain
-    wait_stages<Cfg::COPIES, NST - 2>(min(NST - 2, nk - 1 - kt));
-    lds_barrier();
-    if (kt + NST - 1 < nk) issue(kt + NST - 1);
-    const char* st = lds + (kt % NST) * Cfg::STAGE;
+  // FULL: every 16-column tile of this wave is inside the problem, so the MFMA
+  // block has no branches and its LDS reads can be scheduled freely
+  auto kloop = [&](auto full) {
+    for (int kt = 0; kt < nk; ++kt) {
+      // segment kt has landed once only the copies of later segments remain
+      wait_stages<Cfg::COPIES, NST - 2>(min(NST - 2, nk - 1 - kt));
+      lds_barrier();
+      if (kt + NST - 1 < nk) issue(kt + NST - 1);
+      const char* st = lds + (kt % NST) * Cfg::STAGE;
 #pragma unroll
-    for (int sl = 0; sl < Cfg::NSL; ++sl) {
-      u32x4 fa[WM], fb[WN];
+      for (int sl = 0; sl < Cfg::NSL; ++sl) {
+        u32x4 fa[WM], fb[WN];
 #pragma unroll
-      for (int a = 0; a < WM; ++a) fa[a] = ld16(st + offA[sl] + a * 16 * Cfg::KSEG);
+        for (int a = 0; a < WM; ++a) fa[a] = ld16(st + offA[sl] + a * 16 * Cfg::KSEG);
 #pragma unroll
-      for (int b = 0; b < WN; ++b) fb[b] = ld16(st + offB[sl] + b * 16 * Cfg::KSEG);
+        for (int b = 0; b < WN; ++b) fb[b] = ld16(st + offB[sl] + b * 16 * Cfg::KSEG);
 #pragma unroll
-      for (int b = 0; b < WN; ++b) {
-        if (b < nb_valid) {
+        for (int b = 0; b < WN; ++b) {
+          if (decltype(full)::value || b < nb_valid) {
 #pragma unroll
-          for (int a = 0; a < WM; ++a) acc[a][b] = mma_slab<T>(fa[a], fb[b], acc[a][b]);
+            for (int a = 0; a < WM; ++a) acc[a][b] = mma_slab<T>(fa[a], fb[b], acc[a][b]);
+          }
         }
       }
+      if (prob.seg_end(kt)) prob.fold(acc, wr, wc, lane);
     }
-    if (prob.seg_end(kt)) prob.fold(acc, wr, wc, lane);
-  }
+  };
+  if (nb_valid == WN)
+    kloop(std::integral_constant<bool, true>());
+  else
+    kloop(std::integral_constant<bool, false>());
   prob.finish(acc, wr, wc, lane);
   lds_barrier();  // all waves are done with the stages
   prob.store(acc, wr, wc, lane, lds);
@@ -165,18 +175,22 @@ __device__ __forceinline__ void gemm_dma_tile(Prob& prob, int n_valid, char* lds
 // Whole-tile fp32 staging for epilogues that route values by row and column:
 // C[r][c] at C + r * Cfg::LDC + c.  Call after gemm_dma_tile's final barrier
 // (the stages are free), then lds_barrier() before reading other waves' values.
+// The stores are volatile so that they stay single ds_write_b32: the ROCm 7.2
+// compiler, pairing these stores into ds_write2_b32 around a re-based address
+// (offsets beyond the 8-bit dword range), has emitted a wrong offset for one of
+// the pair in this very pattern.
 template <class Cfg>
 __device__ __forceinline__ void gd_stage_tile(const f32x4 (&acc)[Cfg::WM][Cfg::WN], int wr, int wc,
                                               int lane, float* C) {
   const int lrow = lane & 15, lgrp = lane >> 4;
+  typedef __attribute__((address_space(3))) volatile float lds_vfloat;
+  lds_vfloat* base = (lds_vfloat*)(C + (wr * 16 * Cfg::WM + 4 * lgrp) * Cfg::LDC + wc * 16 * Cfg::WN + lrow);
 #pragma unroll
   for (int a = 0; a < Cfg::WM; ++a)
 #pragma unroll
     for (int b = 0; b < Cfg::WN; ++b)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        C[(wr * 16 * Cfg::WM + 16 * a + 4 * lgrp + i) * Cfg::LDC + wc * 16 * Cfg::WN + 16 * b + lrow] =
-            acc[a][b][i];
+      for (int i = 0; i < 4; ++i) base[(16 * a + i) * Cfg::LDC + 16 * b] = acc[a][b][i];
 }
 
 }  // namespace msgla
