@@ -24,7 +24,7 @@
 
 namespace msgla {
 
-using K3Cfg = GemmCfg<4, 4, 2, 2, 128, 2>;  // 128 x 128 tiles, 4 waves, double-buffered 128-byte K segments
+using K3Cfg = GemmCfg<2, 4, 4, 2, 128, 2>;  // 128 x 128 tiles, 8 waves (32 x 64 each), double-buffered 128-byte K segments
 constexpr int K3_BM = K3Cfg::BM, K3_BN = K3Cfg::BN;
 using K3Acc = f32x4[K3Cfg::WM][K3Cfg::WN];
 
@@ -135,12 +135,12 @@ __global__ __launch_bounds__(K3Cfg::THREADS) void k3c_coarse(const K3Params P) {
 
 // ---- K3f: scale-1 projection + hold + fusion -> O [B][L][d] ----
 // The tile's fusion weights are staged in LDS behind the output staging area
-// when the GEMM starts; the epilogue walks the tile 4 row pieces at a time,
-// issuing all gathered loads of the NC coarse branches for those pieces
+// when the GEMM starts; the epilogue walks the tile a few row pieces at a
+// time, issuing all gathered loads of the NC coarse branches for those pieces
 // before using any of them.
 constexpr int K3F_W_OFF = K3Cfg::LDS_STAGED;
 constexpr int K3F_LDS = K3F_W_OFF + K3_BM * FUSION_STRIDE * 4;
-static_assert(K3_BM * FUSION_STRIDE * 4 == K3Cfg::THREADS * 16, "one 16-byte piece per thread");
+static_assert(K3_BM * FUSION_STRIDE * 4 <= K3Cfg::THREADS * 16, "one 16-byte piece per thread");
 
 template <typename T, int NC>
 struct K3Fine : K3Rows<T> {
@@ -153,8 +153,8 @@ struct K3Fine : K3Rows<T> {
   }
   __device__ void started(char* lds) {
     const K3Params& P = this->P;
-    if (P.m > 1) {
-      const int tid = threadIdx.x;
+    const int tid = threadIdx.x;
+    if (P.m > 1 && tid < K3_BM * FUSION_STRIDE / 4) {
       const int m = this->m0 + tid / (FUSION_STRIDE / 4);
       st16(lds + K3F_W_OFF + 16 * tid,
            m < P.B * P.L ? ld16(P.w + (size_t)m * FUSION_STRIDE + 4 * (tid % (FUSION_STRIDE / 4)))
@@ -168,7 +168,8 @@ struct K3Fine : K3Rows<T> {
     lds_barrier();  // staged tile and fusion weights visible to all waves
     const K3Params& P = this->P;
     T* out = reinterpret_cast<T*>(P.out);
-    constexpr int PIECES = K3_BM * (K3_BN / 8), U = 4;
+    // pieces in flight per thread, fewer when many coarse rows are gathered per piece
+    constexpr int PIECES = K3_BM * (K3_BN / 8), U = NC <= 2 ? 4 : (NC <= 4 ? 2 : 1);
     static_assert(PIECES % (U * K3Cfg::THREADS) == 0, "epilogue batches");
 #pragma unroll 1
     for (int it0 = threadIdx.x; it0 < PIECES; it0 += U * K3Cfg::THREADS) {

@@ -22,7 +22,7 @@
 
 namespace msgla {
 
-using K1Cfg = GemmCfg<4, 4, 2, 2, 128, 2>;  // 128 x 128 tiles, 4 waves, double-buffered 128-byte K segments
+using K1Cfg = GemmCfg<2, 4, 4, 2, 128, 2>;  // 128 x 128 tiles, 8 waves (32 x 64 each), double-buffered 128-byte K segments
 constexpr int K1_BM = K1Cfg::BM, K1_BN = K1Cfg::BN;
 
 template <typename T>
