@@ -9,11 +9,13 @@
 // One workgroup owns one (branch, sequence, head) and a 32-wide slice of d_v
 // and walks its chunks in order; the slices of one sequence run on the same
 // XCD (they read the same A / qt / kT, which then stay in that XCD's L2).
-// The state slice lives in fp32 MFMA accumulators across the whole walk —
-// wave w keeps rows c of S with (c / 16) % 4 == w — and after each update it
-// is published to LDS in the storage type (transposed, [v][c]) as the
-// B-operand of the next chunk's qt S.  Wave w also produces output rows
-// 16w .. 16w+15 of each chunk.  The walk is latency-bound unless the inputs
+// The eight waves split the two products of a chunk: waves 0-3 ("output
+// waves") form y rows 16w .. 16w+15 from S_c, waves 4-7 ("state waves") keep
+// 16-row tiles of S in fp32 MFMA accumulators across the whole walk
+// (rows c with (c / 16) % 4 == w - 4), form S_{c+1} and publish it to LDS in
+// the storage type (transposed, [v][c], double-buffered by chunk parity) as
+// the B-operand of the next chunk's qt S.  On each SIMD one output and one
+// state wave run side by side.  The walk is latency-bound unless the inputs
 // of later chunks are already in flight: A, qt, kT, the chunk's V slice and
 // lam are copied global -> LDS asynchronously (global_load_lds_dwordx4, no
 // VGPRs) into NST rotating stages, NST-1 chunks ahead of the compute, with
@@ -26,7 +28,7 @@
 
 namespace msgla {
 
-constexpr int K2B_THREADS = 256;
+constexpr int K2B_THREADS = 512;  // 4 output waves + 4 state waves
 constexpr int K2B_DVT = 32;  // d_v columns per workgroup
 
 constexpr int k2b_kb(int b) { return (b + 1023) & ~1023; }
@@ -41,7 +43,7 @@ struct K2bGeom {
   static constexpr int NSC = C * es / 64;   // 64-byte k-slabs over positions
   static constexpr int NSK = DK * es / 64;  // 64-byte k-slabs over key channels
   static constexpr int NRT = DK / 16;       // 16-row tiles of the state
-  static constexpr int SRT = (NRT + 3) / 4; // state row tiles per wave
+  static constexpr int SRT = (NRT + 3) / 4; // state row tiles per state wave
   static constexpr int bA = C * C * es, bQ = C * DK * es, bV = K2B_DVT * C * es, bL = DK * 4;
   static constexpr int oA = 0, oQ = k2b_kb(bA), oK = oQ + k2b_kb(bQ), oV = oK + k2b_kb(bQ),
                        oL = oV + k2b_kb(bV), STAGE = oL + k2b_kb(bL);
@@ -52,18 +54,18 @@ struct K2bGeom {
   static constexpr int EXTRA = 2 * K2B_DVT * LDS_S * es + 4 * 16 * LDY * es;
   static constexpr int NST = 3 * STAGE + EXTRA <= 160 * 1024 ? 3 : 2;
   static constexpr int LDS = NST * STAGE + EXTRA;
-  // copies every wave issues per chunk at least (the lam copy comes on top for wave 0)
-  static constexpr int KMIN = nA / 4 + 2 * (nQ / 4) + nV / 4;
+  // copies every wave issues per chunk at least (copy k goes to wave k % 8;
+  // the lam copy comes on top for wave 0)
+  static constexpr int KMIN = nA / 8 + 2 * (nQ / 8) + nV / 8;
   static_assert(bA % 1024 == 0 && bQ % 1024 == 0 && bV % 1024 == 0 && bL <= 1024, "block sizes");
   static_assert(NSC >= 1 && NSC <= 4 && NSK >= 1 && NSK <= 16, "slab counts");
 };
 
 // Per-lane source offset of copy instruction k for a contiguous block stored
 // as swizzled 128-byte virtual rows (async_copy.hpp): source = block + 1024 k
-// + off.  The swizzle key of instruction k is ((8 k + lane / 8) >> hs) & 7;
-// rows of up to 512 bytes (hs <= 2) make it depend on k mod 4 only and rows of
-// 1024 bytes (hs = 3) on k mod 8, so wave w (instructions k = w, w + 4, ...)
-// needs one offset for its even-numbered and one for its odd-numbered copies.
+// + off.  The swizzle key of instruction k is ((8 k + lane / 8) >> hs) & 7,
+// which for rows of up to 1 KB (hs <= 3) depends on k mod 8 only, so wave w
+// (instructions k = w, w + 8, ...) needs one offset per block.
 __device__ __forceinline__ int k2b_lane_off(int lg, int k, int lane) {
   const int hs = blk_hs(lg);
   const int vrow = 8 * k + (lane >> 3);
@@ -92,11 +94,13 @@ __global__ __launch_bounds__(K2B_THREADS) void k2b_gla_state(const K2Params P) {
   const int v0 = tile * K2B_DVT;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool out_wave = wave < 4;
+  const int w4 = wave & 3;  // index among the output waves or among the state waves
   const int lr = lane & 15, lgp = lane >> 4;
 
-  // LDS: NST stages | ST[2][DVT][DK + pad] (published state) | per-wave y staging
+  // LDS: NST stages | ST[2][DVT][DK + pad] (published state) | per-output-wave y staging
   T* ST = reinterpret_cast<T*>(smem + NST * G::STAGE);
-  T* ys = ST + 2 * K2B_DVT * G::LDS_S + wave * 16 * G::LDY;
+  T* ys = ST + 2 * K2B_DVT * G::LDS_S + w4 * 16 * G::LDY;
 
   const size_t chunk0 = (size_t)bh * Bb.nch;
   const char* Ag = reinterpret_cast<const char*>(Bb.A) + chunk0 * G::bA;
@@ -106,9 +110,9 @@ __global__ __launch_bounds__(K2B_THREADS) void k2b_gla_state(const K2Params P) {
   const char* Lg = reinterpret_cast<const char*>(Bb.lam + chunk0 * DK);
   T* yg = reinterpret_cast<T*>(Bb.y) + (size_t)bh * Bb.np * dv + v0;
 
-  // copy offsets: one per block (two for qt rows of 1 KB), see k2b_lane_off
+  // copy offsets: one per block, see k2b_lane_off
   const int oA = k2b_lane_off(G::lgC, wave, lane);
-  const int oQ0 = k2b_lane_off(G::lgQ, wave, lane), oQ1 = k2b_lane_off(G::lgQ, wave + 4, lane);
+  const int oQ = k2b_lane_off(G::lgQ, wave, lane);
   const int oL = 16 * lane;  // lam: one partial instruction of one virtual row (key 0)
   auto issue = [&](int c) {
     char* st = smem + (c % NST) * G::STAGE;
@@ -117,27 +121,24 @@ __global__ __launch_bounds__(K2B_THREADS) void k2b_gla_state(const K2Params P) {
     const char* kk = Kg + (size_t)c * G::bQ;
     const char* v = Vg + (size_t)c * dv * C * es;
 #pragma unroll
-    for (int i = 0; i < (G::nA + 3) / 4; ++i) {
-      const int k = wave + 4 * i;
-      if (k < G::nA)
-        dma16(a + 1024 * k + oA, st + G::oA + 1024 * k);
+    for (int i = 0; i < (G::nA + 7) / 8; ++i) {
+      const int k = wave + 8 * i;
+      if (k < G::nA) dma16(a + 1024 * k + oA, st + G::oA + 1024 * k);
     }
 #pragma unroll
-    for (int i = 0; i < (G::nQ + 3) / 4; ++i) {
-      const int k = wave + 4 * i;
+    for (int i = 0; i < (G::nQ + 7) / 8; ++i) {
+      const int k = wave + 8 * i;
       if (k < G::nQ) {
-        dma16(q + 1024 * k + ((i & 1) ? oQ1 : oQ0), st + G::oQ + 1024 * k);
+        dma16(q + 1024 * k + oQ, st + G::oQ + 1024 * k);
         dma16(kk + 1024 * k + oA, st + G::oK + 1024 * k);
       }
     }
 #pragma unroll
-    for (int i = 0; i < (G::nV + 3) / 4; ++i) {
-      const int k = wave + 4 * i;
-      if (k < G::nV)
-        dma16(v + 1024 * k + oA, st + G::oV + 1024 * k);
+    for (int i = 0; i < (G::nV + 7) / 8; ++i) {
+      const int k = wave + 8 * i;
+      if (k < G::nV) dma16(v + 1024 * k + oA, st + G::oV + 1024 * k);
     }
-    if (wave == 0 && oL < G::bL)
-      dma16(Lg + (size_t)c * G::bL + oL, st + G::oL);
+    if (wave == 0 && oL < G::bL) dma16(Lg + (size_t)c * G::bL + oL, st + G::oL);
   };
 
   // LDS fragment offsets inside a stage
@@ -146,14 +147,14 @@ __global__ __launch_bounds__(K2B_THREADS) void k2b_gla_state(const K2Params P) {
   for (int sl = 0; sl < G::NSC; ++sl) {
     offV[sl][0] = G::oV + tile_off(lr, sl * 4 + lgp, G::lgC);
     offV[sl][1] = G::oV + tile_off(16 + lr, sl * 4 + lgp, G::lgC);
-    offA[sl] = G::oA + tile_off(16 * wave + lr, sl * 4 + lgp, G::lgC);
+    offA[sl] = G::oA + tile_off(16 * w4 + lr, sl * 4 + lgp, G::lgC);
 #pragma unroll
-    for (int a = 0; a < G::SRT; ++a) offK[a][sl] = G::oK + tile_off(16 * (wave + 4 * a) + lr, sl * 4 + lgp, G::lgC);
+    for (int a = 0; a < G::SRT; ++a) offK[a][sl] = G::oK + tile_off(16 * (w4 + 4 * a) + lr, sl * 4 + lgp, G::lgC);
   }
 #pragma unroll
-  for (int sl = 0; sl < G::NSK; ++sl) offQ[sl] = G::oQ + tile_off(16 * wave + lr, sl * 4 + lgp, G::lgQ);
+  for (int sl = 0; sl < G::NSK; ++sl) offQ[sl] = G::oQ + tile_off(16 * w4 + lr, sl * 4 + lgp, G::lgQ);
 #pragma unroll
-  for (int a = 0; a < G::SRT; ++a) offL[a] = G::oL + tile_off(0, (16 * (wave + 4 * a) + 4 * lgp) >> 2, G::lgL);
+  for (int a = 0; a < G::SRT; ++a) offL[a] = G::oL + tile_off(0, (16 * (w4 + 4 * a) + 4 * lgp) >> 2, G::lgL);
 
   f32x4 S[G::SRT][2];
 #pragma unroll
@@ -173,8 +174,6 @@ __global__ __launch_bounds__(K2B_THREADS) void k2b_gla_state(const K2Params P) {
     if (c + NST - 1 < Bb.nch) issue(c + NST - 1);
 
     const char* st = smem + (c % NST) * G::STAGE;
-    const T* Sb = ST + (c & 1) * K2B_DVT * G::LDS_S;
-    T* Sn = ST + ((c + 1) & 1) * K2B_DVT * G::LDS_S;
     const int valid = min(C, Bb.n - c * C);
 
     // V fragments (B-operand of both products); positions >= valid zeroed
@@ -199,85 +198,90 @@ __global__ __launch_bounds__(K2B_THREADS) void k2b_gla_state(const K2Params P) {
         }
     }
 
-    // ---- y rows 16w .. 16w+15: y = A V + qt S, staged for 16-byte stores ----
-    if (wave < C / 16) {
-      u32x4 af[G::NSC], qf[G::NSK], sf[G::NSK][2];
+    if (out_wave) {
+      // ---- y rows 16w .. 16w+15: y = A V + qt S_c, staged for 16-byte stores ----
+      if (w4 < C / 16) {
+        const T* Sb = ST + (c & 1) * K2B_DVT * G::LDS_S;
+        u32x4 af[G::NSC], qf[G::NSK], sf[G::NSK][2];
 #pragma unroll
-      for (int sl = 0; sl < G::NSC; ++sl) af[sl] = ld16(st + offA[sl]);
+        for (int sl = 0; sl < G::NSC; ++sl) af[sl] = ld16(st + offA[sl]);
 #pragma unroll
-      for (int sl = 0; sl < G::NSK; ++sl) {
-        qf[sl] = ld16(st + offQ[sl]);
-        const T* srow = Sb + lr * G::LDS_S + sl * slab_elems<T>() + lgp * PER;
-        sf[sl][0] = ld16(srow);
-        sf[sl][1] = ld16(srow + 16 * G::LDS_S);
-      }
-      f32x4 y[2] = {zero4(), zero4()};
-#pragma unroll
-      for (int sl = 0; sl < G::NSC; ++sl) {
-        y[0] = mma_slab<T>(af[sl], vf[sl][0], y[0]);
-        y[1] = mma_slab<T>(af[sl], vf[sl][1], y[1]);
-      }
-#pragma unroll
-      for (int sl = 0; sl < G::NSK; ++sl) {
-        y[0] = mma_slab<T>(qf[sl], sf[sl][0], y[0]);
-        y[1] = mma_slab<T>(qf[sl], sf[sl][1], y[1]);
-      }
-#pragma unroll
-      for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) ys[(4 * lgp + e) * G::LDY + 16 * ct + lr] = from_f32<T>(y[ct][e]);
-      asm volatile("" ::: "memory");
-      __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (0 << 8));  // own LDS writes done
-      asm volatile("" ::: "memory");
-      // 16 rows x DVT values of this wave -> 16-byte global stores
-      constexpr int PR = K2B_DVT / PER;  // pieces per row
-#pragma unroll
-      for (int p0 = 0; p0 < 16 * PR; p0 += 64) {
-        const int p = p0 + lane;
-        const int row = p / PR, pc = p - row * PR;
-        if (p < 16 * PR && 16 * wave + row < valid)
-          st16(yg + ((size_t)c * C + 16 * wave + row) * dv + pc * PER, ld16(ys + row * G::LDY + pc * PER));
-      }
-    }
-    // ---- state update: S = Diag(lam) S + kT V for the rows this wave owns ----
-#pragma unroll
-    for (int a = 0; a < G::SRT; ++a) {
-      const int rt = wave + 4 * a;
-      if (rt < G::NRT) {
-        u32x4 kf[G::NSC];
-#pragma unroll
-        for (int sl = 0; sl < G::NSC; ++sl) kf[sl] = ld16(st + offK[a][sl]);
-        const f32x4 l4 = __builtin_bit_cast(f32x4, ld16(st + offL[a]));
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          S[a][0][e] *= l4[e];
-          S[a][1][e] *= l4[e];
+        for (int sl = 0; sl < G::NSK; ++sl) {
+          qf[sl] = ld16(st + offQ[sl]);
+          const T* srow = Sb + lr * G::LDS_S + sl * slab_elems<T>() + lgp * PER;
+          sf[sl][0] = ld16(srow);
+          sf[sl][1] = ld16(srow + 16 * G::LDS_S);
         }
+        f32x4 y[2] = {zero4(), zero4()};
 #pragma unroll
         for (int sl = 0; sl < G::NSC; ++sl) {
-          S[a][0] = mma_slab<T>(kf[sl], vf[sl][0], S[a][0]);
-          S[a][1] = mma_slab<T>(kf[sl], vf[sl][1], S[a][1]);
+          y[0] = mma_slab<T>(af[sl], vf[sl][0], y[0]);
+          y[1] = mma_slab<T>(af[sl], vf[sl][1], y[1]);
         }
-        // publish S_{c+1}: ST[v][c], 4 consecutive c per lane
-        const int c4 = 16 * rt + 4 * lgp;
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct) {
-          float f[4] = {S[a][ct][0], S[a][ct][1], S[a][ct][2], S[a][ct][3]};
-          T* dst = Sn + (16 * ct + lr) * G::LDS_S + c4;
-          if constexpr (sizeof(T) == 2)
-            st8(dst, pack8<T>(f));
-          else
-            st16(dst, pack16<T>(f));
+        for (int sl = 0; sl < G::NSK; ++sl) {
+          y[0] = mma_slab<T>(qf[sl], sf[sl][0], y[0]);
+          y[1] = mma_slab<T>(qf[sl], sf[sl][1], y[1]);
+        }
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ys[(4 * lgp + e) * G::LDY + 16 * ct + lr] = from_f32<T>(y[ct][e]);
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (0 << 8));  // own LDS writes done
+        asm volatile("" ::: "memory");
+        // 16 rows x DVT values of this wave -> 16-byte global stores
+        constexpr int PR = K2B_DVT / PER;  // pieces per row
+#pragma unroll
+        for (int p0 = 0; p0 < 16 * PR; p0 += 64) {
+          const int p = p0 + lane;
+          const int row = p / PR, pc = p - row * PR;
+          if (p < 16 * PR && 16 * w4 + row < valid)
+            st16(yg + ((size_t)c * C + 16 * w4 + row) * dv + pc * PER, ld16(ys + row * G::LDY + pc * PER));
+        }
+      }
+    } else {
+      // ---- state rows: S_{c+1} = Diag(lam) S_c + kT V, published for chunk c+1 ----
+      T* Sn = ST + ((c + 1) & 1) * K2B_DVT * G::LDS_S;
+#pragma unroll
+      for (int a = 0; a < G::SRT; ++a) {
+        const int rt = w4 + 4 * a;
+        if (rt < G::NRT) {
+          u32x4 kf[G::NSC];
+#pragma unroll
+          for (int sl = 0; sl < G::NSC; ++sl) kf[sl] = ld16(st + offK[a][sl]);
+          const f32x4 l4 = __builtin_bit_cast(f32x4, ld16(st + offL[a]));
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            S[a][0][e] *= l4[e];
+            S[a][1][e] *= l4[e];
+          }
+#pragma unroll
+          for (int sl = 0; sl < G::NSC; ++sl) {
+            S[a][0] = mma_slab<T>(kf[sl], vf[sl][0], S[a][0]);
+            S[a][1] = mma_slab<T>(kf[sl], vf[sl][1], S[a][1]);
+          }
+          // publish S_{c+1}: ST[v][c], 4 consecutive c per lane
+          const int c4 = 16 * rt + 4 * lgp;
+#pragma unroll
+          for (int ct = 0; ct < 2; ++ct) {
+            float f[4] = {S[a][ct][0], S[a][ct][1], S[a][ct][2], S[a][ct][3]};
+            T* dst = Sn + (16 * ct + lr) * G::LDS_S + c4;
+            if constexpr (sizeof(T) == 2)
+              st8(dst, pack8<T>(f));
+            else
+              st16(dst, pack16<T>(f));
+          }
         }
       }
     }
   }
 
-  if (Bb.S_out) {
+  if (!out_wave && Bb.S_out) {
     float* So = Bb.S_out + (size_t)bh * DK * dv;
 #pragma unroll
     for (int a = 0; a < G::SRT; ++a) {
-      const int rt = wave + 4 * a;
+      const int rt = w4 + 4 * a;
       if (rt < G::NRT) {
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct)
