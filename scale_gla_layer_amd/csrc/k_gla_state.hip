@@ -50,8 +50,7 @@ struct K2bGeom {
   static constexpr int nA = bA / 1024, nQ = bQ / 1024, nV = bV / 1024;  // copy instructions
   static constexpr int lgC = k2b_ilog2(C * es), lgQ = k2b_ilog2(DK * es), lgL = k2b_ilog2(DK * 4);
   static constexpr int LDS_S = DK + 16 / es;       // published-state row stride (elements)
-  static constexpr int LDY = K2B_DVT + 16 / es;    // y staging row stride (elements)
-  static constexpr int EXTRA = 2 * K2B_DVT * LDS_S * es + 4 * 16 * LDY * es;
+  static constexpr int EXTRA = 2 * K2B_DVT * LDS_S * es;
   static constexpr int NST = 3 * STAGE + EXTRA <= 160 * 1024 ? 3 : 2;
   static constexpr int LDS = NST * STAGE + EXTRA;
   // copies every wave issues per chunk at least (copy k goes to wave k % 8;
@@ -98,9 +97,8 @@ __global__ __launch_bounds__(K2B_THREADS) void k2b_gla_state(const K2Params P) {
   const int w4 = wave & 3;  // index among the output waves or among the state waves
   const int lr = lane & 15, lgp = lane >> 4;
 
-  // LDS: NST stages | ST[2][DVT][DK + pad] (published state) | per-output-wave y staging
+  // LDS: NST stages | ST[2][DVT][DK + pad] (published state)
   T* ST = reinterpret_cast<T*>(smem + NST * G::STAGE);
-  T* ys = ST + 2 * K2B_DVT * G::LDS_S + w4 * 16 * G::LDY;
 
   const size_t chunk0 = (size_t)bh * Bb.nch;
   const char* Ag = reinterpret_cast<const char*>(Bb.A) + chunk0 * G::bA;
@@ -199,7 +197,9 @@ __global__ __launch_bounds__(K2B_THREADS) void k2b_gla_state(const K2Params P) {
     }
 
     if (out_wave) {
-      // ---- y rows 16w .. 16w+15: y = A V + qt S_c, staged for 16-byte stores ----
+      // ---- y rows 16w .. 16w+15 as y^T = V^T A^T + S_c^T qt^T: with V (and the
+      // published S^T) as the A-operand, lane l holds 4 consecutive v of
+      // position 16w + l % 16, which go straight to global memory ----
       if (w4 < C / 16) {
         const T* Sb = ST + (c & 1) * K2B_DVT * G::LDS_S;
         u32x4 af[G::NSC], qf[G::NSK], sf[G::NSK][2];
@@ -212,32 +212,32 @@ __global__ __launch_bounds__(K2B_THREADS) void k2b_gla_state(const K2Params P) {
           sf[sl][0] = ld16(srow);
           sf[sl][1] = ld16(srow + 16 * G::LDS_S);
         }
-        f32x4 y[2] = {zero4(), zero4()};
+        // two accumulators per column tile (intra-chunk, inter-chunk) keep the
+        // dependent MFMA chains short
+        f32x4 yi[2] = {zero4(), zero4()}, yo[2] = {zero4(), zero4()};
 #pragma unroll
         for (int sl = 0; sl < G::NSC; ++sl) {
-          y[0] = mma_slab<T>(af[sl], vf[sl][0], y[0]);
-          y[1] = mma_slab<T>(af[sl], vf[sl][1], y[1]);
+          yi[0] = mma_slab<T>(vf[sl][0], af[sl], yi[0]);
+          yi[1] = mma_slab<T>(vf[sl][1], af[sl], yi[1]);
         }
 #pragma unroll
         for (int sl = 0; sl < G::NSK; ++sl) {
-          y[0] = mma_slab<T>(qf[sl], sf[sl][0], y[0]);
-          y[1] = mma_slab<T>(qf[sl], sf[sl][1], y[1]);
+          yo[0] = mma_slab<T>(sf[sl][0], qf[sl], yo[0]);
+          yo[1] = mma_slab<T>(sf[sl][1], qf[sl], yo[1]);
         }
+        const int t = 16 * w4 + lr;
+        if (t < valid) {
+          T* dst = yg + ((size_t)c * C + t) * dv + 4 * lgp;
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct)
+          for (int ct = 0; ct < 2; ++ct) {
+            float f[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) ys[(4 * lgp + e) * G::LDY + 16 * ct + lr] = from_f32<T>(y[ct][e]);
-        asm volatile("" ::: "memory");
-        __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (0 << 8));  // own LDS writes done
-        asm volatile("" ::: "memory");
-        // 16 rows x DVT values of this wave -> 16-byte global stores
-        constexpr int PR = K2B_DVT / PER;  // pieces per row
-#pragma unroll
-        for (int p0 = 0; p0 < 16 * PR; p0 += 64) {
-          const int p = p0 + lane;
-          const int row = p / PR, pc = p - row * PR;
-          if (p < 16 * PR && 16 * w4 + row < valid)
-            st16(yg + ((size_t)c * C + 16 * w4 + row) * dv + pc * PER, ld16(ys + row * G::LDY + pc * PER));
+            for (int e = 0; e < 4; ++e) f[e] = yi[ct][e] + yo[ct][e];
+            if constexpr (sizeof(T) == 2)
+              st8(dst + 16 * ct, pack8<T>(f));
+            else
+              st16(dst + 16 * ct, pack16<T>(f));
+          }
         }
       }
     } else {
