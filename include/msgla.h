@@ -56,12 +56,16 @@ typedef enum { MSGLA_F32 = 0, MSGLA_BF16 = 1 } msgla_dtype;
  * count H = sum heads[i] is what a single-scale GLA layer would have).
  * gate_rank r: rank of the forget-gate projection W_g1 [d x r] W_g2 [r x h d_k];
  * log(alpha) = logsigmoid(xp W_g1 W_g2 + b_g) / gate_normalizer.
- * chunk: length of the GPU chunk schedule (16, 32 or 64); the result does not
- * depend on it beyond rounding (Sec. 3.4 separates it from the pooling block).
+ * chunk: length of the GPU chunk schedule; the result does not depend on it
+ * beyond rounding (Sec. 3.4 separates it from the pooling block).
  * q_scale multiplies q (1.0 reproduces the notes' recurrence).
- * Requirements: 1 <= n_branches <= 8; scales positive and distinct; heads
- * positive; d_model a positive multiple of 64; d_k and d_v positive multiples
- * of 16 with d_k <= 256 and d_v <= 512; 1 <= gate_rank <= 64.
+ * Requirements (MSGLA_ERR_INVALID_ARG otherwise): 1 <= n_branches <= 8; scales
+ * positive and distinct; 1 <= heads <= 64; d_model a multiple of 64 up to
+ * 65536; 1 <= gate_rank <= 64; gate_normalizer > 0; and, by storage type,
+ *   bf16: d_k in {32, 64, 128, 256}, d_v a multiple of 64 in [64, 512],
+ *         chunk 32 or 64;
+ *   fp32: d_k in {16, 32, 64, 128, 256}, d_v a multiple of 32 in [32, 512],
+ *         chunk 16, 32 or 64.
  */
 typedef struct {
   int32_t n_branches;
