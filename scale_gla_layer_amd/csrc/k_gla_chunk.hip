@@ -17,25 +17,28 @@
 //   A     = [sum_c q_tc k_ic e^{b_tc - b_ic}]_{t >= i}   (zero above the diagonal)
 // b is kept in base-2 units (log2 alpha), so every decay factor is one exp2.
 // q and k arrive in fp32 (a single q_t . k_i can cancel strongly, and A scales
-// whole output rows); for bf16 storage A is formed with a split-bf16 product
-// (hi*hi + hi*lo + lo*hi, ~16 mantissa bits) and rounded once.
+// whole output rows); A is formed with fp32 MFMA and rounded once to the
+// storage type.
 // Every exponent used is <= 0 except one bounded by 15 positions of decay:
 // the 16 x 16 block A[T][J] (query tile T, key tile J <= T) is built as
-// (q_t e^{b_t - b_16J}) . (k_i e^{b_16J - b_i}); the query factor is <= 1 and
-// the key factor grows over less than 16 positions.  Rows beyond the sequence
-// end are treated as q = k = 0 and log alpha = 0, which leaves the state
-// untouched.
+// (q_t e^{b_t - b_16T}) . (k_i e^{b_16J - b_i} D_TJ) with D_TJ = e^{b_16T - b_16J};
+// the query factor and D_TJ are <= 1 and the key factor grows over less than
+// 16 positions.  Rows beyond the sequence end are treated as q = k = 0 and
+// log alpha = 0, which leaves the state untouched.
 //
 // Work layout: wave w owns the 16 positions 16w .. 16w+15 of the chunk and all
 // key channels.  Its gate pre-activations z^T = W_g2^T (xp W_g1)^T come from
 // fp32 MFMA, so lane l holds channels 16 rt + 4 (l/16) + i of position
 // 16 w + l % 16 for every channel tile rt.  The cumulative sum over positions
 // is a DPP prefix scan inside each 16-lane row; the waves then exchange their
-// totals (and first values) through LDS.  The key side of A goes to LDS, the
-// query side stays in registers, and wave w forms the blocks A[w][J], J <= w,
-// with MFMA as (key side)(query side)^T so that each lane holds 4 consecutive
-// keys of one query row.  All shapes are compile-time (chunk C, key width DK,
-// padded gate rank RP), so every loop unrolls.
+// totals (and first values) through LDS.  The key side of A (fp32, referenced
+// at its own tile) goes to LDS; the query side stays in registers, referenced
+// at the wave's first position, so it is formed once; wave w scales the key
+// side of tile J by D_wJ (a per-channel table it fills in LDS) and forms the
+// blocks A[w][J], J <= w, with fp32 MFMA as (key side)(query side)^T so that
+// each lane holds 4 consecutive keys of one query row.  All shapes are
+// compile-time (chunk C, key width DK, padded gate rank RP), so every loop
+// unrolls.
 #include "device_common.hpp"
 #include "layout.hpp"
 
@@ -77,14 +80,14 @@ struct K2aGeom {
   static constexpr int NT = DK / 16;           // 16-channel tiles
   static constexpr int THREADS = 64 * NW;
   static constexpr bool BF = sizeof(T) == 2;
-  // key-side rows in LDS (per plane: hi and lo for bf16, one fp32 plane otherwise),
-  // padded by 16 bytes against bank conflicts between rows
-  static constexpr int KROW = (BF ? DK * 2 : DK * 4) + 16;
+  // key-side rows in LDS (fp32), padded by 16 bytes against bank conflicts between rows
+  static constexpr int KROW = DK * 4 + 16;
   static constexpr int XCH = 3 * NW * DK * 4;  // wave totals, first values, references
-  static constexpr int KS = (BF ? 2 : 1) * C * KROW;
+  static constexpr int KS = C * KROW;
   static constexpr int LDT = C + 16 / (int)sizeof(T);  // kT staging row stride (elements)
   static constexpr int KTS = DK * LDT * (int)sizeof(T);
-  static constexpr int LDS = XCH + KS + KTS;
+  static constexpr int DT = NW * (NW - 1) * DK * 4;  // per wave: D_wJ for J < w
+  static constexpr int LDS = XCH + KS + KTS + DT;
   static_assert(C == 16 || C == 32 || C == 64, "chunk");
   static_assert(BF ? (DK >= 32 && DK % 32 == 0) : (DK >= 16 && DK % 16 == 0), "key width");
 };
@@ -114,8 +117,9 @@ __global__ __launch_bounds__(256) void k2a_gla_chunk(const K2Params P) {
   float* tot = reinterpret_cast<float*>(smem);  // [NW][DK] wave totals of log2 alpha
   float* first = tot + NW * DK;                 // [NW][DK] value at each wave's first row
   float* brf = first + NW * DK;                 // [NW][DK] b at each wave's first row
-  char* ks = smem + G::XCH;                     // key side [C][KROW] (x2 planes for bf16)
+  char* ks = smem + G::XCH;                     // key side [C][KROW] fp32
   T* kTs = reinterpret_cast<T*>(smem + G::XCH + G::KS);
+  float* Dw = reinterpret_cast<float*>(smem + G::XCH + G::KS + G::KTS) + w * (NW - 1) * DK;  // [J][DK]
 
   const size_t seq_row = (size_t)bh * Bb.np + row0;  // row index in [B][h][np]
 
@@ -159,77 +163,76 @@ __global__ __launch_bounds__(256) void k2a_gla_chunk(const K2Params P) {
   __syncthreads();
 
   // ---- per channel tile: b_t = own scan + totals of the earlier waves; outputs
-  // qt (global), kT (staged in LDS), lam, the key side of A (LDS) and b at this
-  // wave's first position (LDS, the reference of the blocks A[.][w]) ----
+  // qt (global), kT (staged in LDS), lam, the key side of A (LDS), the query side
+  // of A (registers, in place of q) and b at this wave's first position (LDS) ----
   {
     T* qtg = reinterpret_cast<T*>(Bb.qt) + (seq_row + p) * DK + 4 * lg;
     float* lamg = Bb.lam + ((size_t)bh * Bb.nch + chunk) * DK + 4 * lg;
     char* krow = ks + p * G::KROW + 16 * lg;
-    constexpr int TPS = G::BF ? 2 : 1;  // channel tiles per 64-byte slab
 #pragma unroll
-    for (int s = 0; s < NT / TPS; ++s) {
-      float kside[TPS][4];
+    for (int rt = 0; rt < NT; ++rt) {
+      float carry[4] = {0.f, 0.f, 0.f, 0.f}, blast[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int u = 0; u < TPS; ++u) {
-        const int rt = TPS * s + u;
-        float carry[4] = {0.f, 0.f, 0.f, 0.f}, blast[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int v = 0; v < NW; ++v) {
-          float t4[4];
-          unpack16<float>(ld16(tot + v * DK + 16 * rt + 4 * lg), t4);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            blast[i] += t4[i];
-            if (v < w) carry[i] += t4[i];
-          }
-        }
-        float f4[4], bref[4], qo[4];
-        unpack16<float>(ld16(first + w * DK + 16 * rt + 4 * lg), f4);
+      for (int v = 0; v < NW; ++v) {
+        float t4[4];
+        unpack16<float>(ld16(tot + v * DK + 16 * rt + 4 * lg), t4);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float bt = x[rt][i] + carry[i];
-          x[rt][i] = bt;
-          bref[i] = carry[i] + f4[i];
-          qv[rt][i] *= P.q_scale;
-          qo[i] = qv[rt][i] * exp2_fast(bt);
-          kTs[(16 * rt + 4 * lg + i) * G::LDT + p] = from_f32<T>(kv[rt][i] * exp2_fast(blast[i] - bt));
-          kside[u][i] = kv[rt][i] * exp2_fast(bref[i] - bt);
-        }
-        if constexpr (G::BF)
-          st8(qtg + 16 * rt, pack8<T>(qo));
-        else
-          st16(qtg + 16 * rt, pack16<T>(qo));
-        if (lr == 0) {
-          st16(brf + w * DK + 16 * rt + 4 * lg, pack16<float>(bref));
-          if (w == 0) {
-            float lv[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) lv[i] = exp2_fast(blast[i]);
-            st16(lamg + 16 * rt, pack16<float>(lv));
-          }
+          blast[i] += t4[i];
+          if (v < w) carry[i] += t4[i];
         }
       }
-      // bf16 slab s (32 channels) holds tiles 2s and 2s+1; lane group lg owns
-      // k-slots 8 lg .. 8 lg + 7 = channels 4 lg + i of both tiles (the query
-      // side below uses the same slot order)
-      if constexpr (G::BF) {
-        const float v8[8] = {kside[0][0], kside[0][1], kside[0][2], kside[0][3],
-                             kside[1][0], kside[1][1], kside[1][2], kside[1][3]};
-        u32x4 hi, lo;
-        split_bf16(v8, hi, lo);
-        st16(krow + 64 * s, hi);
-        st16(krow + C * G::KROW + 64 * s, lo);
-      } else {
-        st16(krow + 64 * s, pack16<float>(kside[0]));
+      float f4[4], bref[4], qo[4], kside[4];
+      unpack16<float>(ld16(first + w * DK + 16 * rt + 4 * lg), f4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float bt = x[rt][i] + carry[i];
+        bref[i] = carry[i] + f4[i];
+        const float q = qv[rt][i] * P.q_scale;
+        qo[i] = q * exp2_fast(bt);
+        qv[rt][i] = q * exp2_fast(bt - bref[i]);  // query side of A, <= |q|
+        kTs[(16 * rt + 4 * lg + i) * G::LDT + p] = from_f32<T>(kv[rt][i] * exp2_fast(blast[i] - bt));
+        kside[i] = kv[rt][i] * exp2_fast(bref[i] - bt);  // key side, growth < 16 positions
+      }
+      if constexpr (G::BF)
+        st8(qtg + 16 * rt, pack8<T>(qo));
+      else
+        st16(qtg + 16 * rt, pack16<T>(qo));
+      st16(krow + 64 * rt, pack16<float>(kside));
+      if (lr == 0) {
+        st16(brf + w * DK + 16 * rt + 4 * lg, pack16<float>(bref));
+        if (w == 0) {
+          float lv[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) lv[i] = exp2_fast(blast[i]);
+          st16(lamg + 16 * rt, pack16<float>(lv));
+        }
       }
     }
   }
   __syncthreads();
 
-  // ---- A[w][J] for J <= w (zero blocks above the diagonal) ----
+  // ---- D_wJ = e^{b_16w - b_16J} per channel for J < w, into this wave's table ----
+  {
+    constexpr int PAIRS_PER_LANE = (DK + 63) / 64;
+#pragma unroll
+    for (int J = 0; J < NW - 1; ++J) {
+      if (J < w) {
+#pragma unroll
+        for (int u = 0; u < PAIRS_PER_LANE; ++u) {
+          const int ch = lane + 64 * u;
+          if (ch < DK) Dw[J * DK + ch] = exp2_fast(brf[w * DK + ch] - brf[J * DK + ch]);
+        }
+      }
+    }
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (0 << 8));  // own LDS writes done
+    asm volatile("" ::: "memory");
+  }
+
+  // ---- A[w][J] for J <= w (zero blocks above the diagonal), fp32 MFMA ----
   {
     T* Ag = reinterpret_cast<T*>(Bb.A) + (((size_t)bh * Bb.nch + chunk) * C + p) * C + 4 * lg;
-    constexpr int TPS = G::BF ? 2 : 1;
 #pragma unroll
     for (int J = 0; J < NW; ++J) {
       float out[4] = {0.f, 0.f, 0.f, 0.f};
@@ -237,27 +240,17 @@ __global__ __launch_bounds__(256) void k2a_gla_chunk(const K2Params P) {
         const char* krow = ks + (16 * J + lr) * G::KROW + 16 * lg;
         f32x4 acc = zero4();
 #pragma unroll
-        for (int s = 0; s < NT / TPS; ++s) {
-          // query side q_t e^{b_t - b_16J} for the slab's channels
-          float qs[4 * TPS];
+        for (int rt = 0; rt < NT; ++rt) {
+          u32x4 kf = ld16(krow + 64 * rt);
+          if (J < w) {  // key side re-referenced to this wave's first position
+            float k4[4], d4[4];
+            unpack16<float>(kf, k4);
+            unpack16<float>(ld16(Dw + J * DK + 16 * rt + 4 * lg), d4);
 #pragma unroll
-          for (int u = 0; u < TPS; ++u) {
-            const int rt = TPS * s + u;
-            float r4[4];
-            unpack16<float>(ld16(brf + J * DK + 16 * rt + 4 * lg), r4);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) qs[4 * u + i] = qv[rt][i] * exp2_fast(x[rt][i] - r4[i]);
+            for (int i = 0; i < 4; ++i) k4[i] *= d4[i];
+            kf = pack16<float>(k4);
           }
-          if constexpr (G::BF) {
-            u32x4 qh, ql;
-            split_bf16(qs, qh, ql);
-            const u32x4 kh = ld16(krow + 64 * s), kl = ld16(krow + C * G::KROW + 64 * s);
-            acc = mma_slab<bf16>(kh, qh, acc);
-            acc = mma_slab<bf16>(kh, ql, acc);
-            acc = mma_slab<bf16>(kl, qh, acc);
-          } else {
-            acc = mma_slab<float>(ld16(krow + 64 * s), pack16<float>(qs), acc);
-          }
+          acc = mma_slab<float>(kf, pack16<float>(qv[rt]), acc);
         }
         // acc[e] = A[16 w + lr][16 J + 4 lg + e]; causal mask on the diagonal block
 #pragma unroll
