@@ -39,6 +39,7 @@
 // each lane holds 4 consecutive keys of one query row.  All shapes are
 // compile-time (chunk C, key width DK, padded gate rank RP), so every loop
 // unrolls.
+#include "async_copy.hpp"
 #include "device_common.hpp"
 #include "layout.hpp"
 
@@ -63,13 +64,13 @@ constexpr float K2A_LOG2E = 1.4426950408889634f;
 
 // log2(sigmoid(z)) = min(z, 0) log2(e) - log2(1 + u), u = e^{-|z|} in (0, 1].
 // log2(1 + u) is taken as log2(v) with v = 1 + u rounded, plus the first-order
-// correction (u - (v - 1)) / (v ln 2) for that rounding, so small u keep
-// their relative accuracy.
+// correction (u - (v - 1)) log2(e) for that rounding (the exact factor 1 / v
+// differs from 1 by at most u, which leaves a relative error below 2^-23), so
+// small u keep their relative accuracy.
 __device__ __forceinline__ float log2sigmoid(float z) {
   const float u = __builtin_amdgcn_exp2f(-fabsf(z) * K2A_LOG2E);
   const float v = 1.f + u;
-  const float corr = (u - (v - 1.f)) * __builtin_amdgcn_rcpf(v) * K2A_LOG2E;
-  return fminf(z, 0.f) * K2A_LOG2E - (__builtin_amdgcn_logf(v) + corr);
+  return (fminf(z, 0.f) - (u - (v - 1.f))) * K2A_LOG2E - __builtin_amdgcn_logf(v);
 }
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -82,12 +83,10 @@ struct K2aGeom {
   static constexpr bool BF = sizeof(T) == 2;
   // key-side rows in LDS (fp32), padded by 16 bytes against bank conflicts between rows
   static constexpr int KROW = DK * 4 + 16;
-  static constexpr int XCH = 3 * NW * DK * 4;  // wave totals, first values, references
+  static constexpr int XCH = 4 * NW * DK * 4;  // wave totals, first values, two factor tables
   static constexpr int KS = C * KROW;
-  static constexpr int LDT = C + 16 / (int)sizeof(T);  // kT staging row stride (elements)
-  static constexpr int KTS = DK * LDT * (int)sizeof(T);
   static constexpr int DT = NW * (NW - 1) * DK * 4;  // per wave: D_wJ for J < w
-  static constexpr int LDS = XCH + KS + KTS + DT;
+  static constexpr int LDS = XCH + KS + DT;  // 47 KB at C 64, d_k 128: three workgroups per CU
   static_assert(C == 16 || C == 32 || C == 64, "chunk");
   static_assert(BF ? (DK >= 32 && DK % 32 == 0) : (DK >= 16 && DK % 16 == 0), "key width");
 };
@@ -116,14 +115,37 @@ __global__ __launch_bounds__(256) void k2a_gla_chunk(const K2Params P) {
 
   float* tot = reinterpret_cast<float*>(smem);  // [NW][DK] wave totals of log2 alpha
   float* first = tot + NW * DK;                 // [NW][DK] value at each wave's first row
-  float* brf = first + NW * DK;                 // [NW][DK] b at each wave's first row
+  float* Ew = first + NW * DK + w * 2 * DK;     // [NW][2][DK] e^{b_16w}, e^{b_last - b_16w}
   char* ks = smem + G::XCH;                     // key side [C][KROW] fp32
-  T* kTs = reinterpret_cast<T*>(smem + G::XCH + G::KS);
-  float* Dw = reinterpret_cast<float*>(smem + G::XCH + G::KS + G::KTS) + w * (NW - 1) * DK;  // [J][DK]
+  float* Dw = reinterpret_cast<float*>(smem + G::XCH + G::KS) + w * (NW - 1) * DK;  // [J][DK]
 
   const size_t seq_row = (size_t)bh * Bb.np + row0;  // row index in [B][h][np]
 
   // ---- operands of this lane's position: q, k (4 channels per tile), gate factor ----
+  // The head's W_g2 slice [RP][DK] and gate bias [DK] are copied global -> LDS
+  // (into the key-side area, which is written only after the gate is formed)
+  // while q and k load, so the gate MFMAs read them without a memory round
+  // trip each; configurations where they do not fit read them from global.
+  constexpr bool STAGE_W = RP * DK * 4 + 1024 <= G::KS;
+  const int hdk = Bb.h * DK;
+  float* w2s = reinterpret_cast<float*>(ks);  // [RP][DK]
+  float* bgs = w2s + RP * DK;                 // [DK] (+ padding to 1 KB)
+  if constexpr (STAGE_W) {
+    constexpr int NI = RP * DK / 256;  // 1 KB copy instructions for W_g2
+    const float* w2g = Bb.W2 + hh * DK;
+    for (int k = w; k <= NI; k += NW) {
+      const int q4 = 64 * k + lane;  // 16-byte piece
+      const float* src;
+      if (k < NI) {
+        const int r = q4 / (DK / 4), c4 = q4 - r * (DK / 4);
+        src = w2g + (size_t)r * hdk + 4 * c4;
+      } else {
+        src = Bb.bg + hh * DK + 4 * min(lane, DK / 4 - 1);
+      }
+      dma16(src, reinterpret_cast<char*>(w2s) + 1024 * k);
+    }
+  }
+
   float qv[NT][4], kv[NT][4], gb[RP / 4];
   {
     const float* qg = Bb.q + (seq_row + p) * DK + 4 * lg;
@@ -140,20 +162,24 @@ __global__ __launch_bounds__(256) void k2a_gla_chunk(const K2Params P) {
 
   // ---- z^T[c][t] = sum_r W2[r][c] g[t][r] (fp32 MFMA), then log2 alpha and its scan ----
   float x[NT][4];
+  if constexpr (STAGE_W) {
+    wait_vmcnt<0>();
+    __syncthreads();
+  }
   {
-    const int hdk = Bb.h * DK;
-    const float* w2 = Bb.W2 + hh * DK + lr;
+    const float* w2 = STAGE_W ? w2s + lr : Bb.W2 + hh * DK + lr;
+    const int w2stride = STAGE_W ? DK : hdk;
+    const float* bgp = STAGE_W ? bgs : Bb.bg + hh * DK;
     const float scale = P.inv_gamma;
 #pragma unroll
     for (int rt = 0; rt < NT; ++rt) {
-      f32x4 acc = zero4();
+      f32x4 acc = __builtin_bit_cast(f32x4, ld16(bgp + 16 * rt + 4 * lg));  // gate bias
 #pragma unroll
       for (int k4 = 0; k4 < RP / 4; ++k4)
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(w2[(4 * k4 + lg) * hdk + 16 * rt], gb[k4], acc, 0, 0, 0);
-      const f32x4 bgv = __builtin_bit_cast(f32x4, ld16(Bb.bg + hh * DK + 16 * rt + 4 * lg));
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(w2[(4 * k4 + lg) * w2stride + 16 * rt], gb[k4], acc, 0, 0, 0);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float la = live ? log2sigmoid(acc[i] + bgv[i]) * scale : 0.f;
+        const float la = live ? log2sigmoid(acc[i]) * scale : 0.f;
         x[rt][i] = row_scan16(la);  // inclusive scan over this wave's 16 positions
       }
       if (lr == 15) st16(tot + w * DK + 16 * rt + 4 * lg, pack16<float>(x[rt]));
@@ -162,66 +188,32 @@ __global__ __launch_bounds__(256) void k2a_gla_chunk(const K2Params P) {
   }
   __syncthreads();
 
-  // ---- per channel tile: b_t = own scan + totals of the earlier waves; outputs
-  // qt (global), kT (staged in LDS), lam, the key side of A (LDS), the query side
-  // of A (registers, in place of q) and b at this wave's first position (LDS) ----
+  // ---- per channel (lane owns channels lane, lane + 64, ...): b at this wave's
+  // first position b_16w = (totals of the earlier waves) + (first value), the
+  // factors e^{b_16w} and e^{b_last - b_16w} (LDS), D_wJ = e^{b_16w - b_16J}
+  // for J < w (LDS) and, from wave 0, lam = e^{b_last} (global) ----
   {
-    T* qtg = reinterpret_cast<T*>(Bb.qt) + (seq_row + p) * DK + 4 * lg;
-    float* lamg = Bb.lam + ((size_t)bh * Bb.nch + chunk) * DK + 4 * lg;
-    char* krow = ks + p * G::KROW + 16 * lg;
+    float* lamg = Bb.lam + ((size_t)bh * Bb.nch + chunk) * DK;
 #pragma unroll
-    for (int rt = 0; rt < NT; ++rt) {
-      float carry[4] = {0.f, 0.f, 0.f, 0.f}, blast[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int u = 0; u < (DK + 63) / 64; ++u) {
+      const int ch = lane + 64 * u;
+      if (ch < DK) {
+        float carry = 0.f, blast = 0.f;
 #pragma unroll
-      for (int v = 0; v < NW; ++v) {
-        float t4[4];
-        unpack16<float>(ld16(tot + v * DK + 16 * rt + 4 * lg), t4);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          blast[i] += t4[i];
-          if (v < w) carry[i] += t4[i];
+        for (int v = 0; v < NW; ++v) {
+          const float tv = tot[v * DK + ch];
+          blast += tv;
+          if (v < w) carry += tv;
         }
-      }
-      float f4[4], bref[4], qo[4], kside[4];
-      unpack16<float>(ld16(first + w * DK + 16 * rt + 4 * lg), f4);
+        const float bw = carry + first[w * DK + ch];
+        Ew[ch] = exp2_fast(bw);
+        Ew[DK + ch] = exp2_fast(blast - bw);
+        if (w == 0) lamg[ch] = exp2_fast(blast);
+        float cj = 0.f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float bt = x[rt][i] + carry[i];
-        bref[i] = carry[i] + f4[i];
-        const float q = qv[rt][i] * P.q_scale;
-        qo[i] = q * exp2_fast(bt);
-        qv[rt][i] = q * exp2_fast(bt - bref[i]);  // query side of A, <= |q|
-        kTs[(16 * rt + 4 * lg + i) * G::LDT + p] = from_f32<T>(kv[rt][i] * exp2_fast(blast[i] - bt));
-        kside[i] = kv[rt][i] * exp2_fast(bref[i] - bt);  // key side, growth < 16 positions
-      }
-      if constexpr (G::BF)
-        st8(qtg + 16 * rt, pack8<T>(qo));
-      else
-        st16(qtg + 16 * rt, pack16<T>(qo));
-      st16(krow + 64 * rt, pack16<float>(kside));
-      if (lr == 0) {
-        st16(brf + w * DK + 16 * rt + 4 * lg, pack16<float>(bref));
-        if (w == 0) {
-          float lv[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) lv[i] = exp2_fast(blast[i]);
-          st16(lamg + 16 * rt, pack16<float>(lv));
-        }
-      }
-    }
-  }
-  __syncthreads();
-
-  // ---- D_wJ = e^{b_16w - b_16J} per channel for J < w, into this wave's table ----
-  {
-    constexpr int PAIRS_PER_LANE = (DK + 63) / 64;
-#pragma unroll
-    for (int J = 0; J < NW - 1; ++J) {
-      if (J < w) {
-#pragma unroll
-        for (int u = 0; u < PAIRS_PER_LANE; ++u) {
-          const int ch = lane + 64 * u;
-          if (ch < DK) Dw[J * DK + ch] = exp2_fast(brf[w * DK + ch] - brf[J * DK + ch]);
+        for (int J = 0; J < NW - 1; ++J) {
+          if (J < w) Dw[J * DK + ch] = exp2_fast(bw - (cj + first[J * DK + ch]));
+          cj += tot[J * DK + ch];
         }
       }
     }
@@ -229,6 +221,52 @@ __global__ __launch_bounds__(256) void k2a_gla_chunk(const K2Params P) {
     __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (0 << 8));  // own LDS writes done
     asm volatile("" ::: "memory");
   }
+
+  // ---- per element, with d = b_t - b_16w (this lane's scan minus the wave's first
+  // value): query side of A q e^d (registers, in place of q), key side k e^{-d}
+  // (LDS), qt = q e^{b_t} = (q e^d) e^{b_16w} and kT = k e^{b_last - b_t} =
+  // (k e^{-d}) e^{b_last - b_16w} (global) ----
+  {
+    T* qtg = reinterpret_cast<T*>(Bb.qt) + (seq_row + p) * DK + 4 * lg;
+    T* kTg = reinterpret_cast<T*>(Bb.kT) + ((size_t)bh * Bb.nch + chunk) * DK * C;
+    const int odd = lr & 1;
+    char* krow = ks + p * G::KROW + 16 * lg;
+#pragma unroll
+    for (int rt = 0; rt < NT; ++rt) {
+      float f4[4], e1[4], e2[4], qo[4], kside[4], kt[4];
+      unpack16<float>(ld16(first + w * DK + 16 * rt + 4 * lg), f4);
+      unpack16<float>(ld16(Ew + 16 * rt + 4 * lg), e1);
+      unpack16<float>(ld16(Ew + DK + 16 * rt + 4 * lg), e2);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float d = x[rt][i] - f4[i];
+        const float qs = qv[rt][i] * P.q_scale * exp2_fast(d);  // <= |q|
+        qv[rt][i] = qs;
+        qo[i] = qs * e1[i];
+        kside[i] = kv[rt][i] * exp2_fast(-d);  // growth < 16 positions
+        kt[i] = kside[i] * e2[i];
+      }
+      if constexpr (G::BF)
+        st8(qtg + 16 * rt, pack8<T>(qo));
+      else
+        st16(qtg + 16 * rt, pack16<T>(qo));
+      st16(krow + 64 * rt, pack16<float>(kside));
+      // kT[c][t]: neighbouring lanes (positions p, p ^ 1) swap one value so that
+      // the even lane stores channel c at (p, p + 1) and the odd lane channel
+      // c + 1 at (p - 1, p), two consecutive elements per store
+#pragma unroll
+      for (int i = 0; i < 4; i += 2) {
+        const float recv = dpp_f<0xB1>(odd ? kt[i] : kt[i + 1]);  // quad_perm [1, 0, 3, 2]
+        const float pr[4] = {odd ? recv : kt[i], odd ? kt[i + 1] : recv, 0.f, 0.f};
+        T* dst = kTg + (size_t)(16 * rt + 4 * lg + i + odd) * C + (p - odd);
+        if constexpr (G::BF)
+          *reinterpret_cast<uint32_t*>(dst) = pack8<T>(pr)[0];
+        else
+          st8(dst, pack8<T>(pr));
+      }
+    }
+  }
+  __syncthreads();
 
   // ---- A[w][J] for J <= w (zero blocks above the diagonal), fp32 MFMA ----
   {
@@ -260,18 +298,6 @@ __global__ __launch_bounds__(256) void k2a_gla_chunk(const K2Params P) {
         st8(Ag + 16 * J, pack8<T>(out));
       else
         st16(Ag + 16 * J, pack16<T>(out));
-    }
-  }
-
-  // ---- the transposed state-update key, coalesced ----
-  constexpr int PER = per16<T>();
-  T* kTg = reinterpret_cast<T*>(Bb.kT) + ((size_t)bh * Bb.nch + chunk) * DK * C;
-#pragma unroll
-  for (int i = 0; i < (DK * C / PER + G::THREADS - 1) / G::THREADS; ++i) {
-    const int pc = tid + i * G::THREADS;
-    if (pc < DK * C / PER) {
-      const int c = (pc * PER) / C, t0 = pc * PER - c * C;
-      st16(kTg + (size_t)c * C + t0, ld16(kTs + c * G::LDT + t0));
     }
   }
 }
