@@ -162,7 +162,7 @@ WsGeom ws_geom(const PackGeom& g, int64_t B, int64_t L) {
     b.qt = take(rows * g.dk * g.es);
     b.kT = take(rows * g.dk * g.es);
     b.vT = take(rows * g.dv * g.es);
-    b.g = take((size_t)B * b.np * g.rp * 4);
+    b.g = take((size_t)B * L * g.rp * 4);  // x W_g1 at every unpooled position
     b.A = take(rows * g.C * g.es);
     b.lam = take((size_t)B * bg.h * b.nch * g.dk * 4);
     b.y = take(rows * g.dv * g.es);
@@ -347,17 +347,11 @@ msgla_status msgla_forward_timed(const msgla_config* cfg, const void* packed, co
 
   // ---------------- K1 ----------------
   K1Params p1{};
-  p1.x = x;
   p1.B = (int)B;
-  p1.L = (int)L;
   p1.d = g.d;
   p1.dk = g.dk;
   p1.dv = g.dv;
-  p1.rp = g.rp;
   p1.C = g.C;
-  p1.m = g.m;
-  p1.bf = at<float>(packed, g.off_bf);
-  p1.w = at<float>(workspace, W.w);
   int tiles = 0, ng = 0;
   for (int i = 0; i < g.m; ++i) {
     const BranchGeom& b = g.br[i];
@@ -369,38 +363,52 @@ msgla_status msgla_forward_timed(const msgla_config* cfg, const void* packed, co
     G.s = b.s;
     G.n = wb.n;
     G.M = (int)B * wb.n;
-    G.N = b.N;
-    G.tiles_n = cdiv(b.N, GEMM_TILE);
+    G.N = b.col_g;  // q, k and v columns
+    G.tiles_n = cdiv(G.N, GEMM_TILE);
     G.tile_begin = tiles;
     tiles += cdiv(G.M, GEMM_TILE) * G.tiles_n;
     G.h = b.h;
     G.col_k = b.col_k;
     G.col_v = b.col_v;
-    G.col_g = b.col_g;
-    G.col_z = b.col_z;
-    G.col_end = b.N;
     G.np = wb.np;
     G.nch = wb.nch;
     G.q = at<float>(workspace, wb.q);
     G.k = at<float>(workspace, wb.k);
     G.vT = at<char>(workspace, wb.vT);
-    G.g = at<float>(workspace, wb.g);
   }
-  if (g.has_Wz) {
+  {
+    // the small projection over the unpooled rows: gate first factors, fusion logits
+    K1Small& S = p1.sm;
+    S.m = g.m;
+    S.rp = g.rp;
+    int Ns = 0;
+    for (int i = 0; i < g.m; ++i) {
+      const BranchGeom& b = g.br[i];
+      S.seg[S.nseg++] = XSeg{at<char>(packed, b.off_Wp + (size_t)b.col_g * g.d * g.es), Ns, g.rp};
+      S.g[i] = at<float>(workspace, W.br[i].g);
+      Ns += g.rp;
+    }
+    S.zcol = -1;
+    if (g.m > 1) {
+      const size_t zoff = g.carrier >= 0
+                              ? g.br[g.carrier].off_Wp + (size_t)g.br[g.carrier].col_z * g.d * g.es
+                              : g.off_Wz;
+      S.seg[S.nseg++] = XSeg{at<char>(packed, zoff), Ns, 16};
+      S.zcol = Ns;
+      Ns += 16;
+    }
+    S.bf = at<float>(packed, g.off_bf);
+    S.w = at<float>(workspace, W.w);
+    S.group = ng;
     K1Group& G = p1.g[ng++];
-    G.Wp = at<char>(packed, g.off_Wz);
     G.A = x;
     G.s = 1;
     G.n = (int)L;
     G.M = (int)(B * L);
-    G.N = 16;
-    G.tiles_n = 1;
+    G.N = Ns;
+    G.tiles_n = cdiv(Ns, GEMM_TILE);
     G.tile_begin = tiles;
-    tiles += cdiv(G.M, GEMM_TILE);
-    G.h = 0;
-    G.col_k = G.col_v = G.col_g = 0;
-    G.col_z = 0;
-    G.col_end = 16;
+    tiles += cdiv(G.M, GEMM_TILE) * G.tiles_n;
   }
   p1.ngroups = ng;
   p1.total_tiles = tiles;
@@ -409,6 +417,7 @@ msgla_status msgla_forward_timed(const msgla_config* cfg, const void* packed, co
   // ---------------- K2 ----------------
   K2Params p2{};
   p2.B = (int)B;
+  p2.L = (int)L;
   p2.dk = g.dk;
   p2.dv = g.dv;
   p2.r = g.r;
@@ -423,6 +432,7 @@ msgla_status msgla_forward_timed(const msgla_config* cfg, const void* packed, co
     const WsBranch& wb = W.br[i];
     K2Branch& k = p2.br[i];
     k.h = b.h;
+    k.s = b.s;
     k.n = wb.n;
     k.nch = wb.nch;
     k.np = wb.np;

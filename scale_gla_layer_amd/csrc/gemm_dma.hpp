@@ -36,6 +36,12 @@
 #include "async_copy.hpp"
 #include "device_common.hpp"
 
+// Optional timing hook: a build may define MSGLA_TILE_MARK(stage) to record
+// when a tile starts (0), finishes its K loop (1) and finishes its store (2).
+#ifndef MSGLA_TILE_MARK
+#define MSGLA_TILE_MARK(stage) ((void)0)
+#endif
+
 namespace msgla {
 
 template <int WM_, int WN_, int WGM_, int WGN_, int KSEG_, int NST_>
@@ -100,6 +106,7 @@ __device__ __forceinline__ void gemm_dma_tile(Prob& prob, int n_valid, char* lds
   const int wr = wave / Cfg::WGN, wc = wave % Cfg::WGN;
   const int lrow = lane & 15, lgrp = lane >> 4;
   const int nk = prob.nk();
+  MSGLA_TILE_MARK(0);
   prob.setup(wave, lane);
 
   const int cpp = Cfg::cp_piece(lane);
@@ -167,9 +174,11 @@ __device__ __forceinline__ void gemm_dma_tile(Prob& prob, int n_valid, char* lds
     kloop(std::integral_constant<bool, true>());
   else
     kloop(std::integral_constant<bool, false>());
+  MSGLA_TILE_MARK(1);
   prob.finish(acc, wr, wc, lane);
   lds_barrier();  // all waves are done with the stages
   prob.store(acc, wr, wc, lane, lds);
+  MSGLA_TILE_MARK(2);
 }
 
 // Whole-tile fp32 staging for epilogues that route values by row and column:

@@ -150,7 +150,8 @@ __global__ __launch_bounds__(256) void k2a_gla_chunk(const K2Params P) {
   {
     const float* qg = Bb.q + (seq_row + p) * DK + 4 * lg;
     const float* kg = Bb.k + (seq_row + p) * DK + 4 * lg;
-    const float* gr = Bb.g + ((size_t)b * Bb.np + row0 + p) * RP + lg;
+    // x W_g1 is given per unpooled position: the block's mean is this row's value
+    const float* gr = Bb.g + ((size_t)b * P.L + (size_t)(row0 + p) * Bb.s) * RP + lg;
 #pragma unroll
     for (int rt = 0; rt < NT; ++rt) {
       unpack16<float>(live ? ld16(qg + 16 * rt) : zero16(), qv[rt]);
@@ -158,6 +159,14 @@ __global__ __launch_bounds__(256) void k2a_gla_chunk(const K2Params P) {
     }
 #pragma unroll
     for (int k4 = 0; k4 < RP / 4; ++k4) gb[k4] = live ? gr[4 * k4] : 0.f;
+    if (Bb.s > 1) {
+      for (int u = 1; u < Bb.s; ++u)
+#pragma unroll
+        for (int k4 = 0; k4 < RP / 4; ++k4) gb[k4] += live ? gr[(size_t)u * RP + 4 * k4] : 0.f;
+      const float inv_s = 1.0f / (float)Bb.s;
+#pragma unroll
+      for (int k4 = 0; k4 < RP / 4; ++k4) gb[k4] *= inv_s;
+    }
   }
 
   // ---- z^T[c][t] = sum_r W2[r][c] g[t][r] (fp32 MFMA), then log2 alpha and its scan ----

@@ -1,21 +1,24 @@
 // K1 — pooled projection GEMM over all branches in one launch.
 //
-// MS-GLA notes, Sec. 3.1 (Eq. (8), non-overlapping mean pooling) and Sec. 3.2
-// (independent q, k, v and low-rank gate projections per branch), plus the
-// fusion logits of Eq. (10) from the unpooled x_t.
+// MS-GLA notes, Sec. 3.1 (Eq. (8), non-overlapping mean pooling), Sec. 3.2
+// (independent q, k, v and low-rank gate projections per branch) and Sec. 3.3
+// (Eq. (10), fusion logits from the unpooled x_t).
 //
 // For branch i (scale s): C_i = P_s(X) * Wp_i^T, where row (b, j) of P_s(X) is
 // the mean of X rows b*L + j*s .. + s-1 (only complete blocks): X itself for
 // s = 1, otherwise the block means written by the pooling prepass (summed in
-// fp32, rounded once).  Both operands stream global -> LDS asynchronously
-// (gemm_dma.hpp), so the K loop issues no address or conversion arithmetic.
-// Wp_i stacks the transposed q, k, v,
-// first-gate-factor and (for the branch that carries them) fusion-logit
-// weights; the epilogue routes each column range to its consumer layout:
-// q, k head-major fp32 rows, v transposed per chunk, the gate factor in fp32, and
-// the fusion logits turned into softmax weights (Eq. (10)) with the bias.
-// The work list is every (group, m-tile, n-tile), n fastest, laid out so each
-// XCD walks a contiguous range (tiles that share an A tile share an L2).
+// fp32, rounded once).  Wp_i stacks the transposed q, k and v weights; the
+// epilogue writes q, k head-major fp32 rows and v transposed per chunk.
+// One more group, the small projection X [W_g1^(1) | ... | W_g1^(m) | W_f]
+// over the unpooled rows, gives every branch's gate first factor at every
+// position (by linearity mean(x) W_g1 = mean(x W_g1), so the recurrence
+// kernel averages it over each block) and the fusion weights: softmax of the
+// logits plus bias (Eq. (10)).  Keeping those few columns out of the branch
+// groups keeps every branch tile full width.
+// Both operands stream global -> LDS asynchronously (gemm_dma.hpp), so the K
+// loop issues no address or conversion arithmetic.  The work list is every
+// (group, m-tile, n-tile), n fastest, laid out so each XCD walks a contiguous
+// range (tiles that share an A tile share an L2).
 #include "device_common.hpp"
 #include "gemm_dma.hpp"
 #include "layout.hpp"
@@ -30,11 +33,12 @@ struct K1Prob {
   const K1Params& P;
   const K1Group& G;
   int m0, n0;
+  bool small;  // the small-projection group
   const char* arow[K1Cfg::A_SLOTS];
   const char* brow[K1Cfg::B_SLOTS];
 
-  __device__ K1Prob(const K1Params& p, const K1Group& g, int m0_, int n0_)
-      : P(p), G(g), m0(m0_), n0(n0_) {}
+  __device__ K1Prob(const K1Params& p, const K1Group& g, int m0_, int n0_, bool small_)
+      : P(p), G(g), m0(m0_), n0(n0_), small(small_) {}
 
   __device__ int nk() const { return P.d * (int)sizeof(T) / K1Cfg::KSEG; }
   __device__ void setup(int wave, int lane) {
@@ -47,7 +51,15 @@ struct K1Prob {
 #pragma unroll
     for (int j = 0; j < K1Cfg::B_SLOTS; ++j) {
       const int n = n0 + K1Cfg::b_row(j, wave, lane);
-      brow[j] = reinterpret_cast<const char*>(G.Wp) + (size_t)(n < G.N ? n : 0) * row_bytes;
+      if (!small) {
+        brow[j] = reinterpret_cast<const char*>(G.Wp) + (size_t)(n < G.N ? n : 0) * row_bytes;
+      } else {
+        const char* src = reinterpret_cast<const char*>(P.sm.seg[0].W);  // columns past Ns: any row
+        for (int q = 0; q < P.sm.nseg; ++q)
+          if (n >= P.sm.seg[q].col0 && n < P.sm.seg[q].col0 + P.sm.seg[q].cnt)
+            src = reinterpret_cast<const char*>(P.sm.seg[q].W) + (size_t)(n - P.sm.seg[q].col0) * row_bytes;
+        brow[j] = src;
+      }
     }
   }
   __device__ void started(char*) {}
@@ -61,7 +73,47 @@ struct K1Prob {
     float* C = reinterpret_cast<float*>(lds);
     gd_stage_tile<K1Cfg>(acc, wr, wc, lane, C);
     lds_barrier();
-    epilogue(C, K1Cfg::LDC);
+    if (small)
+      epilogue_small(C, K1Cfg::LDC);
+    else
+      epilogue(C, K1Cfg::LDC);
+  }
+
+  // gate first factors (fp32 rows of rp) and fusion weights, per unpooled position m
+  __device__ void epilogue_small(const float* C, int ldc) {
+    const K1Small& S = P.sm;
+    const int gcols = S.m * S.rp;
+    for (int it = threadIdx.x; it < K1_BM * (K1_BN / 8); it += K1Cfg::THREADS) {
+      const int r = it / (K1_BN / 8), cg = it % (K1_BN / 8);
+      const int m = m0 + r, col = n0 + cg * 8;
+      if (m >= G.M || col >= G.N) continue;
+      const float* src = C + r * ldc + cg * 8;
+      if (col < gcols) {
+        const int i = col / S.rp, c = col - i * S.rp;
+        float* dst = S.g[i] + (size_t)m * S.rp + c;
+        st16(dst, ld16(src));
+        st16(dst + 4, ld16(src + 4));
+      } else if (col == S.zcol) {
+        // softmax over the m fusion logits of this position (Eq. (10))
+        float z[8], mx = -INFINITY, sum = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          z[e] = (e < S.m) ? src[e] + S.bf[e] : -INFINITY;
+          mx = fmaxf(mx, z[e]);
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          z[e] = (e < S.m) ? __expf(z[e] - mx) : 0.f;
+          sum += z[e];
+        }
+        const float inv = 1.0f / sum;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) z[e] *= inv;
+        float* dst = S.w + (size_t)m * FUSION_STRIDE;
+        st16(dst, pack16<float>(z));
+        st16(dst + 4, pack16<float>(z + 4));
+      }
+    }
   }
 
   __device__ void store8(T* dst, const float* v) {
@@ -75,54 +127,28 @@ struct K1Prob {
 
   __device__ void epilogue(const float* C, int ldc) {
     const int tid = threadIdx.x;
-    // (1) row-major destinations: q, k, gate factor, fusion weights
+    // (1) row-major destinations: q, k
     for (int it = tid; it < K1_BM * (K1_BN / 8); it += K1Cfg::THREADS) {
       const int r = it / (K1_BN / 8), cg = it % (K1_BN / 8);
       const int m = m0 + r, col = n0 + cg * 8;
-      if (m >= G.M || col >= G.N) continue;
-      if (col >= G.col_v && col < G.col_g) continue;  // v: transposed pass below
+      if (m >= G.M || col >= G.col_v) continue;  // v: transposed pass below
       const int b = m / G.n, j = m - b * G.n;
       float v[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) v[e] = C[r * ldc + cg * 8 + e];
-      if (col < G.col_v) {
-        const bool isq = col < G.col_k;
-        const int c = isq ? col : col - G.col_k;
-        const int hh = c / P.dk, ch = c - hh * P.dk;
-        float* dst = (isq ? G.q : G.k) + (((size_t)b * G.h + hh) * G.np + j) * P.dk + ch;
-        st16(dst, pack16<float>(v));
-        st16(dst + 4, pack16<float>(v + 4));
-      } else if (col < (G.col_z >= 0 ? G.col_z : G.col_end)) {
-        float* dst = G.g + ((size_t)b * G.np + j) * P.rp + (col - G.col_g);
-        st16(dst, pack16<float>(v));
-        st16(dst + 4, pack16<float>(v + 4));
-      } else if (G.col_z >= 0 && col == G.col_z) {
-        // softmax over the m fusion logits of this (unpooled) position, Eq. (10)
-        float z[8], mx = -INFINITY, sum = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          z[e] = (e < P.m) ? v[e] + P.bf[e] : -INFINITY;
-          mx = fmaxf(mx, z[e]);
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          z[e] = (e < P.m) ? __expf(z[e] - mx) : 0.f;
-          sum += z[e];
-        }
-        const float inv = 1.0f / sum;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) z[e] *= inv;
-        float* dst = P.w + ((size_t)b * P.L + j) * FUSION_STRIDE;
-        st16(dst, pack16<float>(z));
-        st16(dst + 4, pack16<float>(z + 4));
-      }
+      const bool isq = col < G.col_k;
+      const int c = isq ? col : col - G.col_k;
+      const int hh = c / P.dk, ch = c - hh * P.dk;
+      float* dst = (isq ? G.q : G.k) + (((size_t)b * G.h + hh) * G.np + j) * P.dk + ch;
+      st16(dst, pack16<float>(v));
+      st16(dst + 4, pack16<float>(v + 4));
     }
     // (2) v, written transposed per chunk: vT[b][hh][chunk][v][tau]
-    if (G.col_g > G.col_v && n0 < G.col_g && n0 + K1_BN > G.col_v) {
+    if (n0 + K1_BN > G.col_v) {
       for (int it = tid; it < K1_BN * (K1_BM / 8); it += K1Cfg::THREADS) {
         const int cl = it % K1_BN, rg = it / K1_BN;
         const int col = n0 + cl;
-        if (col < G.col_v || col >= G.col_g) continue;
+        if (col < G.col_v || col >= G.N) continue;
         const int cv = col - G.col_v;
         const int hh = cv / P.dv, vch = cv - hh * P.dv;
         const int mA = m0 + rg * 8;
@@ -160,7 +186,7 @@ __global__ __launch_bounds__(K1Cfg::THREADS) void k1_pool_proj(const K1Params P)
   const K1Group& G = P.g[gi];
   const int local = tile - G.tile_begin;
   const int tm = local / G.tiles_n, tn = local - tm * G.tiles_n;
-  K1Prob<T> prob(P, G, tm * K1_BM, tn * K1_BN);
+  K1Prob<T> prob(P, G, tm * K1_BM, tn * K1_BN, gi == P.sm.group);
   gemm_dma_tile<T, K1Cfg>(prob, G.N - tn * K1_BN, lds);
 }
 

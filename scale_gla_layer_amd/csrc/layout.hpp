@@ -70,42 +70,60 @@ struct PoolParams {
   PoolOut out[MSGLA_MAX_BRANCHES];
 };
 
-// ---------------- K1: pooled projection GEMM (+ fusion logits) ----------------
+// ---------------- K1: pooled projection GEMM ----------------------------------
+// B-operand rows [col0, col0 + cnt) of the small projection start at W (row
+// stride d elements): each branch's gate first factor, then the fusion logits.
+struct XSeg {
+  const void* W;
+  int col0, cnt;
+};
+
 struct K1Group {
-  const void* Wp;   // [N][d]
-  const void* A;    // A rows: x (scale 1) or the pooled block means [M][d]
-  int s;            // pooling factor (1 for the fusion-only group)
+  const void* Wp;   // [N][d]: the transposed q, k and v projections (branch groups)
+  const void* A;    // A rows: x (scale 1 and the small group) or the block means [M][d]
+  int s;            // pooling factor
   int n;            // pooled rows per sequence
   int M;            // B * n
-  int N;            // GEMM columns (multiple of 16)
+  int N;            // GEMM columns: h (2 dk + dv), or Ns for the small group
   int tiles_n;      // ceil(N / BN)
   int tile_begin;   // first flattened tile of this group
-  int h;            // heads (0 for the fusion-only group)
-  int col_k, col_v, col_g, col_z, col_end;  // column ranges; col_q = 0; col_z < 0: none
+  int h;            // heads
+  int col_k, col_v; // column ranges: q [0, col_k), k [col_k, col_v), v [col_v, N)
   int np, nch;      // padded rows and chunks per (b, head)
   float* q;         // outputs (see layout)
   float* k;
   void* vT;
-  float* g;
+};
+
+// The small projection x [W_g1^(1) | ... | W_g1^(m) | W_f] over the unpooled
+// rows: each branch's gate first factor at every position and the fusion weights.
+struct K1Small {
+  int group;        // index of its group in K1Params::g, -1 if none
+  int m, rp;
+  int nseg;
+  XSeg seg[MSGLA_MAX_BRANCHES + 1];
+  float* g[MSGLA_MAX_BRANCHES];  // per branch [B L][rp] fp32
+  int zcol;         // first fusion-logit column, -1 if none
+  const float* bf;  // fusion bias [m]
+  float* w;         // fusion weights [B L][FUSION_STRIDE]
 };
 
 struct K1Params {
-  const void* x;    // [B][L][d]
-  int B, L, d, dk, dv, rp, C, m;
+  int B, d, dk, dv, C;
   int ngroups, total_tiles, per_xcd;
-  const float* bf;  // fusion bias [16]
-  float* w;         // fusion weights [B L][8]
   K1Group g[MSGLA_MAX_BRANCHES + 1];
+  K1Small sm;
 };
 
 // ---------------- K2a: chunk-local gate, decay and intra-chunk matrix ----------
 struct K2Branch {
   int h, n, nch, np;
+  int s;            // pooling factor
   int unit_begin;   // first flattened (b, head, chunk) unit of this branch (K2a)
   int seq_begin;    // first flattened (b, head) sequence of this branch (K2b)
   const float* q;
   const float* k;
-  const float* g;
+  const float* g;   // x W_g1 at every unpooled position [B L][rp] (averaged over each block here)
   const float* W2;  // [rp][h dk], rows >= r are zero
   const float* bg;  // [h dk]
   void* qt;
@@ -118,7 +136,7 @@ struct K2Branch {
 };
 
 struct K2Params {
-  int B, dk, dv, r, rp, C;
+  int B, L, dk, dv, r, rp, C;
   float inv_gamma;
   float q_scale;
   int nbranch;
