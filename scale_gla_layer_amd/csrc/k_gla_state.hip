@@ -18,8 +18,11 @@
 // state wave run side by side.  The walk is latency-bound unless the inputs
 // of later chunks are already in flight: A, qt, kT, the chunk's V slice and
 // lam are copied global -> LDS asynchronously (global_load_lds_dwordx4, no
-// VGPRs) into NST rotating stages, NST-1 chunks ahead of the compute, with
-// vmcnt waits and one barrier per chunk.  V positions beyond the sequence end
+// VGPRs) into NST rotating stages, NST-1 chunks ahead of the compute, by a
+// ninth wave that does nothing else (the copies of one chunk keep the CU's
+// vector-memory path busy for about as long as the chunk's products take, and
+// a compute wave that issued them would wait that long), with vmcnt waits on
+// the copy wave and one barrier per chunk.  V positions beyond the sequence end
 // are zeroed in the fragments (the workspace there is never written).
 // After the last chunk the fp32 state is optionally written out.
 #include "async_copy.hpp"
@@ -28,7 +31,7 @@
 
 namespace msgla {
 
-constexpr int K2B_THREADS = 512;  // 4 output waves + 4 state waves
+constexpr int K2B_THREADS = 576;  // 4 output waves + 4 state waves + 1 copy wave
 constexpr int K2B_DVT = 32;  // d_v columns per workgroup
 
 constexpr int k2b_kb(int b) { return (b + 1023) & ~1023; }
@@ -53,9 +56,8 @@ struct K2bGeom {
   static constexpr int EXTRA = 2 * K2B_DVT * LDS_S * es;
   static constexpr int NST = 3 * STAGE + EXTRA <= 160 * 1024 ? 3 : 2;
   static constexpr int LDS = NST * STAGE + EXTRA;
-  // copies every wave issues per chunk at least (copy k goes to wave k % 8;
-  // the lam copy comes on top for wave 0)
-  static constexpr int KMIN = nA / 8 + 2 * (nQ / 8) + nV / 8;
+  // copy instructions per chunk (all issued by the copy wave)
+  static constexpr int NCOPY = nA + 2 * nQ + nV + (bL <= 1024 ? 1 : 0);
   static_assert(bA % 1024 == 0 && bQ % 1024 == 0 && bV % 1024 == 0 && bL <= 1024, "block sizes");
   static_assert(NSC >= 1 && NSC <= 4 && NSK >= 1 && NSK <= 16, "slab counts");
 };
@@ -108,9 +110,10 @@ __global__ __launch_bounds__(K2B_THREADS) void k2b_gla_state(const K2Params P) {
   const char* Lg = reinterpret_cast<const char*>(Bb.lam + chunk0 * DK);
   T* yg = reinterpret_cast<T*>(Bb.y) + (size_t)bh * Bb.np * dv + v0;
 
-  // copy offsets: one per block, see k2b_lane_off
-  const int oA = k2b_lane_off(G::lgC, wave, lane);
-  const int oQ = k2b_lane_off(G::lgQ, wave, lane);
+  // Wave 8 issues every copy (a chunk's ~45 copy instructions occupy the CU's
+  // vector-memory path for about as long as the chunk's products take): the
+  // compute waves never queue behind copy instructions, and the copy wave's
+  // vmcnt holds nothing but copies, so its waits are exact.
   const int oL = 16 * lane;  // lam: one partial instruction of one virtual row (key 0)
   auto issue = [&](int c) {
     char* st = smem + (c % NST) * G::STAGE;
@@ -118,26 +121,31 @@ __global__ __launch_bounds__(K2B_THREADS) void k2b_gla_state(const K2Params P) {
     const char* q = Qg + (size_t)c * G::bQ;
     const char* kk = Kg + (size_t)c * G::bQ;
     const char* v = Vg + (size_t)c * dv * C * es;
+    // the V slice first: the one block that comes from HBM rather than L2
 #pragma unroll
-    for (int i = 0; i < (G::nA + 7) / 8; ++i) {
-      const int k = wave + 8 * i;
-      if (k < G::nA) dma16(a + 1024 * k + oA, st + G::oA + 1024 * k);
+    for (int k = 0; k < G::nV; ++k) dma16(v + 1024 * k + k2b_lane_off(G::lgC, k, lane), st + G::oV + 1024 * k);
+    if (oL < G::bL) dma16(Lg + (size_t)c * G::bL + oL, st + G::oL);
+#pragma unroll
+    for (int k = 0; k < G::nQ; ++k) {
+      dma16(kk + 1024 * k + k2b_lane_off(G::lgC, k, lane), st + G::oK + 1024 * k);
+      dma16(q + 1024 * k + k2b_lane_off(G::lgQ, k, lane), st + G::oQ + 1024 * k);
     }
 #pragma unroll
-    for (int i = 0; i < (G::nQ + 7) / 8; ++i) {
-      const int k = wave + 8 * i;
-      if (k < G::nQ) {
-        dma16(q + 1024 * k + oQ, st + G::oQ + 1024 * k);
-        dma16(kk + 1024 * k + oA, st + G::oK + 1024 * k);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < (G::nV + 7) / 8; ++i) {
-      const int k = wave + 8 * i;
-      if (k < G::nV) dma16(v + 1024 * k + oA, st + G::oV + 1024 * k);
-    }
-    if (wave == 0 && oL < G::bL) dma16(Lg + (size_t)c * G::bL + oL, st + G::oL);
+    for (int k = 0; k < G::nA; ++k) dma16(a + 1024 * k + k2b_lane_off(G::lgC, k, lane), st + G::oA + 1024 * k);
   };
+  if (wave == 8) {
+    for (int c = 0; c < NST - 1 && c < Bb.nch; ++c) issue(c);
+    for (int c = 0; c < Bb.nch; ++c) {
+      // stage c has landed once only the copies of later stages remain
+      if (NST > 2 && c + 1 < Bb.nch)
+        wait_vmcnt<(G::NCOPY < 63 ? G::NCOPY : 63)>();
+      else
+        wait_vmcnt<0>();
+      lds_barrier();
+      if (c + NST - 1 < Bb.nch) issue(c + NST - 1);
+    }
+    return;
+  }
 
   // LDS fragment offsets inside a stage
   int offV[G::NSC][2], offA[G::NSC], offK[G::SRT][G::NSC], offQ[G::NSK], offL[G::SRT];
@@ -158,18 +166,10 @@ __global__ __launch_bounds__(K2B_THREADS) void k2b_gla_state(const K2Params P) {
 #pragma unroll
   for (int a = 0; a < G::SRT; ++a) S[a][0] = S[a][1] = zero4();
 
-  for (int c = 0; c < NST - 1 && c < Bb.nch; ++c) issue(c);
-  for (int i = tid; i < K2B_DVT * G::LDS_S; i += K2B_THREADS) ST[i] = from_f32<T>(0.f);
+  for (int i = tid; i < K2B_DVT * G::LDS_S; i += 512) ST[i] = from_f32<T>(0.f);
 
   for (int c = 0; c < Bb.nch; ++c) {
-    // stage c must have landed: every wave issued at least KMIN copies of the
-    // next stage after it (and any stores since only add to that count)
-    if (NST > 2 && G::KMIN > 0 && c + 1 < Bb.nch)
-      wait_vmcnt<(G::KMIN < 63 ? G::KMIN : 63)>();
-    else
-      wait_vmcnt<0>();
-    lds_barrier();
-    if (c + NST - 1 < Bb.nch) issue(c + NST - 1);
+    lds_barrier();  // stage c has landed (the copy wave waited for it)
 
     const char* st = smem + (c % NST) * G::STAGE;
     const int valid = min(C, Bb.n - c * C);
