@@ -164,39 +164,44 @@ struct K3Fine : K3Rows<T> {
   __device__ void store(const K3Acc& acc, int wr, int wc, int lane, char* lds) {
     float* C = reinterpret_cast<float*>(lds);
     const float* wl = reinterpret_cast<const float*>(lds + K3F_W_OFF);
-    if (has_fine) gd_stage_tile<K3Cfg>(acc, wr, wc, lane, C);
-    lds_barrier();  // staged tile and fusion weights visible to all waves
     const K3Params& P = this->P;
     T* out = reinterpret_cast<T*>(P.out);
     // pieces in flight per thread, fewer when many coarse rows are gathered per piece
     constexpr int PIECES = K3_BM * (K3_BN / 8), U = NC <= 2 ? 4 : (NC <= 4 ? 2 : 1);
     static_assert(PIECES % (U * K3Cfg::THREADS) == 0, "epilogue batches");
-#pragma unroll 1
-    for (int it0 = threadIdx.x; it0 < PIECES; it0 += U * K3Cfg::THREADS) {
-      int r[U], col[U], b[U], t[U];
-      bool ok[U];
-      float y[U][NC > 0 ? NC : 1][8];
+    constexpr int PER = per16<T>();
+    constexpr int NP = 8 / PER;  // 16-byte pieces per 8 outputs
+    // the first batch's gathered coarse rows are requested before the tile is
+    // staged, so their latency overlaps the staging and its barrier
+    int it0 = threadIdx.x;
+    int r[U], col[U];
+    bool ok[U];
+    u32x4 raw[U][NC > 0 ? NC : 1][NP];
+    auto gather = [&](int it_first) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int it = it0 + u * K3Cfg::THREADS;
+        const int it = it_first + u * K3Cfg::THREADS;
         r[u] = it / (K3_BN / 8);
         col[u] = this->n0 + (it % (K3_BN / 8)) * 8;
         const int m = this->m0 + r[u];
         ok[u] = m < P.B * P.L && col[u] < P.d;
-        b[u] = m / P.L;
-        t[u] = m - b[u] * P.L;
+        const int b = ok[u] ? m / P.L : 0;
+        const int t = m - b * P.L;
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
           const K3Branch& Bi = P.br[P.coarse[c]];
-          const int j = (t[u] + 1) / Bi.s - 1;  // held coarse row (none before the first block)
-          if (ok[u] && j >= 0) {
-            k3_load8(reinterpret_cast<const T*>(Bi.yc) + ((size_t)b[u] * Bi.n + j) * P.d + col[u], y[u][c]);
-          } else {
+          const int j = (t + 1) / Bi.s - 1;  // held coarse row (none before the first block)
+          const T* src = reinterpret_cast<const T*>(Bi.yc) + ((size_t)b * Bi.n + j) * P.d + col[u];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) y[u][c][e] = 0.f;
-          }
+          for (int q = 0; q < NP; ++q) raw[u][c][q] = (ok[u] && j >= 0) ? ld16(src + q * PER) : zero16();
         }
       }
+    };
+    gather(it0);
+    if (has_fine) gd_stage_tile<K3Cfg>(acc, wr, wc, lane, C);
+    lds_barrier();  // staged tile and fusion weights visible to all waves
+#pragma unroll 1
+    for (;;) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         if (!ok[u]) continue;
@@ -214,11 +219,17 @@ struct K3Fine : K3Rows<T> {
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
           const float wi = P.m > 1 ? wr_[P.coarse[c]] : 1.f;
+          float y[8];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) v[e] += wi * y[u][c][e];
+          for (int q = 0; q < NP; ++q) unpack16<T>(raw[u][c][q], y + q * PER);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] += wi * y[e];
         }
         k3_store8(out + (size_t)(this->m0 + r[u]) * P.d + col[u], v);
       }
+      it0 += U * K3Cfg::THREADS;
+      if (it0 >= PIECES) break;
+      gather(it0);
     }
   }
 };
