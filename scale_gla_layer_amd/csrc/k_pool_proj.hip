@@ -70,6 +70,10 @@ struct K1Prob {
   __device__ void fold(f32x4 (&)[K1Cfg::WM][K1Cfg::WN], int, int, int) {}
   __device__ void finish(f32x4 (&)[K1Cfg::WM][K1Cfg::WN], int, int, int) {}
   __device__ void store(const f32x4 (&acc)[K1Cfg::WM][K1Cfg::WN], int wr, int wc, int lane, char* lds) {
+    if (!small && n0 + K1_BN <= G.col_v) {
+      store_qk(acc, wr, wc, lane);
+      return;
+    }
     float* C = reinterpret_cast<float*>(lds);
     gd_stage_tile<K1Cfg>(acc, wr, wc, lane, C);
     lds_barrier();
@@ -77,6 +81,32 @@ struct K1Prob {
       epilogue_small(C, K1Cfg::LDC);
     else
       epilogue(C, K1Cfg::LDC);
+  }
+
+  // q / k tiles go straight from the accumulators to their head-major fp32 rows:
+  // each store instruction writes 16 consecutive channels of 4 rows
+  __device__ void store_qk(const f32x4 (&acc)[K1Cfg::WM][K1Cfg::WN], int wr, int wc, int lane) {
+    const int lrow = lane & 15, lgrp = lane >> 4;
+    float* dstc[K1Cfg::WN];
+#pragma unroll
+    for (int bb = 0; bb < K1Cfg::WN; ++bb) {
+      const int col = n0 + wc * 16 * K1Cfg::WN + 16 * bb + lrow;
+      const bool isq = col < G.col_k;
+      const int c = isq ? col : col - G.col_k;
+      const int hh = c / P.dk, ch = c - hh * P.dk;
+      dstc[bb] = (isq ? G.q : G.k) + (size_t)hh * G.np * P.dk + ch;
+    }
+#pragma unroll
+    for (int a = 0; a < K1Cfg::WM; ++a)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = m0 + wr * 16 * K1Cfg::WM + 16 * a + 4 * lgrp + i;
+        if (m >= G.M) continue;
+        const int b = m / G.n, j = m - b * G.n;
+        const size_t roff = ((size_t)b * G.h * G.np + j) * P.dk;
+#pragma unroll
+        for (int bb = 0; bb < K1Cfg::WN; ++bb) dstc[bb][roff] = acc[a][bb][i];
+      }
   }
 
   // gate first factors (fp32 rows of rp) and fusion weights, per unpooled position m
