@@ -157,6 +157,31 @@ def time_forward(layer, x, steps, warmup, per_kernel=True):
     return dt / steps * 1e3, stage_ms
 
 
+def per_call_distribution(layer, x, calls=100, scrub=False):
+    """p10 / p50 / p90 of `calls` forwards, each bracketed by its own pair of
+    events.  scrub=True writes a 512 MiB buffer before every call, which evicts
+    the 256 MB MALL, so each forward starts with cold caches (its inputs and
+    weights come from HBM)."""
+    import torch
+    B, L, _ = x.shape
+    out = layer.new_output(B, L)
+    junk = torch.empty(512 << 20, dtype=torch.uint8, device=x.device) if scrub else None
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(calls)]
+    for _ in range(5):
+        layer.forward(x, out=out)
+    for a, b in ev:
+        if junk is not None:
+            junk.zero_()
+        a.record()
+        layer.forward(x, out=out)
+        b.record()
+    torch.cuda.synchronize()
+    t = np.array([a.elapsed_time(b) * 1e3 for a, b in ev])
+    return {"calls": calls, "p10": round(float(np.percentile(t, 10)), 2),
+            "p50": round(float(np.percentile(t, 50)), 2), "p90": round(float(np.percentile(t, 90)), 2)}
+
+
 def traffic_from_profile(kernel: str, workload: str):
     """HBM bytes per launch of `kernel` from the committed counter summary, or
     None when there is none or the kernel's sources changed since."""
@@ -197,11 +222,11 @@ def cpu_baseline(cfg, X, W, min_s=10.0, max_s=30.0):
 
 PROFILE_COMMANDS = {
     "ktrace": "rocprofv3 --kernel-trace --stats -f csv -d {d}/ktrace -o main -- "
-              "python3 bench.py --steps 20 --warmup 5 --no-cpu-baseline --no-gla",
+              "python3 bench.py --steps 20 --warmup 5 --no-cpu-baseline --no-gla --no-per-call",
     "fetch": "rocprofv3 --pmc FETCH_SIZE -f csv -d {d}/pmc_fetch -o main -- "
-             "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-gla",
+             "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-gla --no-per-call",
     "write": "rocprofv3 --pmc WRITE_SIZE -f csv -d {d}/pmc_write -o main -- "
-             "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-gla",
+             "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-gla --no-per-call",
     "cal_fetch": "rocprofv3 --pmc FETCH_SIZE -f csv -d {d}/cal_fetch -o copy -- "
                  "python3 bench.py --copy-calibration",
     "cal_write": "rocprofv3 --pmc WRITE_SIZE -f csv -d {d}/cal_write -o copy -- "
@@ -304,11 +329,13 @@ def copy_calibration():
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="main")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-gla", action="store_true", help="skip the single-scale GLA comparison")
+    ap.add_argument("--no-per-call", action="store_true",
+                    help="skip the per-call (warm and cold-MALL) distributions")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run the plain-copy reference kernel for counter scaling")
     ap.add_argument("--summarize-profiles", metavar="DIR",
@@ -341,6 +368,13 @@ def main():
     tok_s = B * L / (ms * 1e-3)
     log(f"[bench] {ms * 1e3:.1f} us/step, {tok_s / 1e6:.1f} M tokens/s; kernels (us, event pass): " +
         ", ".join(f"{k} {v * 1e3:.1f}" for k, v in stage_ms.items()))
+
+    warm = cold = None
+    if not args.no_per_call:
+        warm = per_call_distribution(layer, x)
+        cold = per_call_distribution(layer, x, scrub=True)
+        log(f"[bench] per call (us): warm p10/p50/p90 {warm['p10']}/{warm['p50']}/{warm['p90']}, "
+            f"cold MALL {cold['p10']}/{cold['p50']}/{cold['p90']}")
 
     alg = algorithmic(cfg, B, L)
     peak_f = PEAK["bf16_mfma_tflops"] if cfg.dtype == "bf16" else PEAK["fp32_mfma_tflops"]
@@ -407,6 +441,8 @@ def main():
                            "t_roof_us": round(t_roof * 1e6, 2),
                            "frac": round(t_roof / (ms * 1e-3), 4)},
         "kernels": stages,
+        "per_call_us": warm,
+        "per_call_cold_mall_us": cold,
         "ratio_vs_gla": None if ratio_vs_gla is None else round(ratio_vs_gla, 4),
         "gla_tokens_per_s": None if gla is None else round(gla, 1),
         "cpu_baseline": cpu,

@@ -100,7 +100,18 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     return lib
 
 
+_CFG_CACHE: dict = {}
+
+
 def c_config(cfg: MsglaConfig) -> CConfig:
+    """The C struct of a configuration (built once per distinct configuration)."""
+    c = _CFG_CACHE.get(cfg)
+    if c is None:
+        c = _CFG_CACHE[cfg] = _build_config(cfg)
+    return c
+
+
+def _build_config(cfg: MsglaConfig) -> CConfig:
     c = CConfig()
     c.n_branches = len(cfg.scales)
     for i, (s, h) in enumerate(zip(cfg.scales, cfg.heads)):
