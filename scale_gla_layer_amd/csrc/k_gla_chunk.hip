@@ -146,34 +146,58 @@ __global__ __launch_bounds__(256) void k2a_gla_chunk(const K2Params P) {
     }
   }
 
-  float qv[NT][4], kv[NT][4], gb[RP / 4];
+  // The gate factor loads first and q, k after it: the gate, its scan and the
+  // waves' exchange need only the gate factor, so they run while q and k are
+  // still in flight.  Every lane issues the same loads (dead positions load a
+  // valid row and discard it), so the copies and the gate factor have landed
+  // once only the 2 NT q / k loads remain.
+  const int pl = live ? p : 0;
+  float gb[RP / 4];
   {
-    const float* qg = Bb.q + (seq_row + p) * DK + 4 * lg;
-    const float* kg = Bb.k + (seq_row + p) * DK + 4 * lg;
     // x W_g1 is given per unpooled position: the block's mean is this row's value
-    const float* gr = Bb.g + ((size_t)b * P.L + (size_t)(row0 + p) * Bb.s) * RP + lg;
+    const float* gr = Bb.g + ((size_t)b * P.L + (size_t)(row0 + pl) * Bb.s) * RP + lg;
 #pragma unroll
-    for (int rt = 0; rt < NT; ++rt) {
-      unpack16<float>(live ? ld16(qg + 16 * rt) : zero16(), qv[rt]);
-      unpack16<float>(live ? ld16(kg + 16 * rt) : zero16(), kv[rt]);
-    }
-#pragma unroll
-    for (int k4 = 0; k4 < RP / 4; ++k4) gb[k4] = live ? gr[4 * k4] : 0.f;
+    for (int k4 = 0; k4 < RP / 4; ++k4) gb[k4] = gr[4 * k4];
     if (Bb.s > 1) {
-      for (int u = 1; u < Bb.s; ++u)
+      // three rows per round trip (dead slots reload the last row and are dropped)
+      for (int u0 = 1; u0 < Bb.s; u0 += 3) {
+        float t[3][RP / 4];
 #pragma unroll
-        for (int k4 = 0; k4 < RP / 4; ++k4) gb[k4] += live ? gr[(size_t)u * RP + 4 * k4] : 0.f;
+        for (int j = 0; j < 3; ++j) {
+          const int u = min(u0 + j, Bb.s - 1);
+#pragma unroll
+          for (int k4 = 0; k4 < RP / 4; ++k4) t[j][k4] = gr[(size_t)u * RP + 4 * k4];
+        }
+#pragma unroll
+        for (int j = 0; j < 3; ++j)
+#pragma unroll
+          for (int k4 = 0; k4 < RP / 4; ++k4) gb[k4] += u0 + j < Bb.s ? t[j][k4] : 0.f;
+      }
       const float inv_s = 1.0f / (float)Bb.s;
 #pragma unroll
       for (int k4 = 0; k4 < RP / 4; ++k4) gb[k4] *= inv_s;
     }
+#pragma unroll
+    for (int k4 = 0; k4 < RP / 4; ++k4) gb[k4] = live ? gb[k4] : 0.f;
   }
+  asm volatile("" ::: "memory");  // keep the q / k loads behind the copies and the gate factor
+  u32x4 qraw[NT], kraw[NT];
+  {
+    const float* qg = Bb.q + (seq_row + pl) * DK + 4 * lg;
+    const float* kg = Bb.k + (seq_row + pl) * DK + 4 * lg;
+#pragma unroll
+    for (int rt = 0; rt < NT; ++rt) {
+      qraw[rt] = ld16(qg + 16 * rt);
+      kraw[rt] = ld16(kg + 16 * rt);
+    }
+  }
+  asm volatile("" ::: "memory");
 
   // ---- z^T[c][t] = sum_r W2[r][c] g[t][r] (fp32 MFMA), then log2 alpha and its scan ----
   float x[NT][4];
   if constexpr (STAGE_W) {
-    wait_vmcnt<0>();
-    __syncthreads();
+    wait_vmcnt<2 * NT>();  // copies and gate factor landed; q, k may still be in flight
+    lds_barrier();         // (a full fence here would wait for q and k too)
   }
   {
     const float* w2 = STAGE_W ? w2s + lr : Bb.W2 + hh * DK + lr;
@@ -195,7 +219,7 @@ __global__ __launch_bounds__(256) void k2a_gla_chunk(const K2Params P) {
       if (lr == 0) st16(first + w * DK + 16 * rt + 4 * lg, pack16<float>(x[rt]));
     }
   }
-  __syncthreads();
+  lds_barrier();  // the exchange is through LDS only; q and k may still be loading
 
   // ---- per channel (lane owns channels lane, lane + 64, ...): b at this wave's
   // first position b_16w = (totals of the earlier waves) + (first value), the
@@ -235,6 +259,12 @@ __global__ __launch_bounds__(256) void k2a_gla_chunk(const K2Params P) {
   // value): query side of A q e^d (registers, in place of q), key side k e^{-d}
   // (LDS), qt = q e^{b_t} = (q e^d) e^{b_16w} and kT = k e^{b_last - b_t} =
   // (k e^{-d}) e^{b_last - b_16w} (global) ----
+  float qv[NT][4], kv[NT][4];
+#pragma unroll
+  for (int rt = 0; rt < NT; ++rt) {
+    unpack16<float>(live ? qraw[rt] : zero16(), qv[rt]);
+    unpack16<float>(live ? kraw[rt] : zero16(), kv[rt]);
+  }
   {
     T* qtg = reinterpret_cast<T*>(Bb.qt) + (seq_row + p) * DK + 4 * lg;
     T* kTg = reinterpret_cast<T*>(Bb.kT) + ((size_t)bh * Bb.nch + chunk) * DK * C;
@@ -275,7 +305,7 @@ __global__ __launch_bounds__(256) void k2a_gla_chunk(const K2Params P) {
       }
     }
   }
-  __syncthreads();
+  lds_barrier();  // key side in LDS; the qt, kT stores drain meanwhile
 
   // ---- A[w][J] for J <= w (zero blocks above the diagonal), fp32 MFMA ----
   {
