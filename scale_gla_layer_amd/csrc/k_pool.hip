@@ -71,14 +71,80 @@ __global__ __launch_bounds__(256) void k_pool(const PoolParams P) {
   }
 }
 
-hipError_t launch_pool(const PoolParams& P, bool bf16_path, hipStream_t st) {
-  const int per = bf16_path ? 8 : 4;
-  const long threads = (long)P.B * ((P.L + P.smax - 1) / P.smax) * (P.d / per);
-  const dim3 grid((unsigned)((threads + 255) / 256));
+// Power-of-two s_max (every pooled scale is then a power of two dividing it):
+// the thread loads all S = 2^LS rows of its block at once, then forms the block
+// sums level by level, pairs of the previous level, and emits the means of
+// each requested scale as its level completes.  The loads are unconditional (a
+// short tail block re-reads its last row; blocks it does not complete are not
+// emitted), so the S loads of a thread are in flight together.
+template <typename T, int LS>
+__global__ __launch_bounds__(256) void k_pool_pow2(const PoolParams P) {
+  constexpr int PER = per16<T>(), S = 1 << LS;
+  const int pieces = P.d / PER;
+  const int nblk = (P.L + S - 1) / S;
+  const int idx = blockIdx.x * 256 + threadIdx.x;  // the launcher keeps the count below 2^31
+  if (idx >= P.B * nblk * pieces) return;
+  const int grp = idx / pieces, piece = idx - grp * pieces;
+  const int b = grp / nblk, q = grp - b * nblk;
+  const T* x = reinterpret_cast<const T*>(P.x) + ((size_t)b * P.L + (size_t)q * S) * P.d + piece * PER;
+  const int last = min(S, P.L - q * S) - 1;
+  u32x4 raw[S];
+#pragma unroll
+  for (int u = 0; u < S; ++u) raw[u] = ld16(x + (size_t)min(u, last) * P.d);
+  // every load is issued before the first one is used (the scheduler would
+  // otherwise start unpacking between them and wait on the early ones)
+#pragma unroll
+  for (int u = 0; u < S; ++u) asm volatile("" : "+v"(raw[u])::"memory");
+  float v[S][PER];
+#pragma unroll
+  for (int u = 0; u < S; ++u) unpack16<T>(raw[u], v[u]);
+#pragma unroll
+  for (int l = 1; l <= LS; ++l) {
+#pragma unroll
+    for (int j = 0; j < (S >> l); ++j)
+#pragma unroll
+      for (int e = 0; e < PER; ++e) v[j][e] = v[2 * j][e] + v[2 * j + 1][e];
+    const int i = P.lvl[l];
+    if (i >= 0) {
+      const PoolOut& o = P.out[i];
+      T* dst = reinterpret_cast<T*>(o.xp) + piece * PER;
+#pragma unroll
+      for (int j = 0; j < (S >> l); ++j) {
+        const int jo = q * (S >> l) + j;
+        if (jo < o.n) {
+          float m[PER];
+#pragma unroll
+          for (int e = 0; e < PER; ++e) m[e] = v[j][e] * o.inv_s;
+          st16(dst + ((size_t)b * o.n + jo) * P.d, pack16<T>(m));
+        }
+      }
+    }
+  }
+}
+
+template <typename T>
+static void launch_pool_t(const PoolParams& P, hipStream_t st) {
+  const long threads = (long)P.B * ((P.L + P.smax - 1) / P.smax) * (P.d / per16<T>());
+  const dim3 grid((unsigned)((threads + 255) / 256)), block(256);
+  switch (threads + 255 < (1L << 31) ? P.smax : 0) {
+    case 2: hipLaunchKernelGGL((k_pool_pow2<T, 1>), grid, block, 0, st, P); return;
+    case 4: hipLaunchKernelGGL((k_pool_pow2<T, 2>), grid, block, 0, st, P); return;
+    case 8: hipLaunchKernelGGL((k_pool_pow2<T, 3>), grid, block, 0, st, P); return;
+    case 16: hipLaunchKernelGGL((k_pool_pow2<T, 4>), grid, block, 0, st, P); return;
+    default: hipLaunchKernelGGL(k_pool<T>, grid, block, 0, st, P); return;
+  }
+}
+
+hipError_t launch_pool(const PoolParams& P0, bool bf16_path, hipStream_t st) {
+  PoolParams P = P0;
+  for (int l = 0; l < 8; ++l) P.lvl[l] = -1;
+  for (int i = 0; i < P.nout; ++i)
+    for (int l = 1; l < 8; ++l)
+      if (P.out[i].s == (1 << l)) P.lvl[l] = i;
   if (bf16_path)
-    hipLaunchKernelGGL(k_pool<bf16>, grid, dim3(256), 0, st, P);
+    launch_pool_t<bf16>(P, st);
   else
-    hipLaunchKernelGGL(k_pool<float>, grid, dim3(256), 0, st, P);
+    launch_pool_t<float>(P, st);
   return hipGetLastError();
 }
 

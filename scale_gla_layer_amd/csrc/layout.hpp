@@ -68,6 +68,7 @@ struct PoolParams {
   const void* x;    // [B][L][d]
   int B, L, d, smax, nout;
   PoolOut out[MSGLA_MAX_BRANCHES];
+  int lvl[8];       // power-of-two smax: out index of scale 2^l, or -1 (set by the launcher)
 };
 
 // ---------------- K1: pooled projection GEMM ----------------------------------
