@@ -175,8 +175,10 @@ struct K3Fine : K3Rows<T> {
     // staged, so their latency overlaps the staging and its barrier
     int it0 = threadIdx.x;
     int r[U], col[U];
-    bool ok[U];
+    bool ok[U], held[U][NC > 0 ? NC : 1];
     u32x4 raw[U][NC > 0 ? NC : 1][NP];
+    // every lane issues all loads of a batch (pieces outside the problem and
+    // positions before a branch's first block read a valid row and drop it)
     auto gather = [&](int it_first) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
@@ -186,14 +188,16 @@ struct K3Fine : K3Rows<T> {
         const int m = this->m0 + r[u];
         ok[u] = m < P.B * P.L && col[u] < P.d;
         const int b = ok[u] ? m / P.L : 0;
-        const int t = m - b * P.L;
+        const int t = ok[u] ? m - b * P.L : 0;
+        const int cc = ok[u] ? col[u] : 0;
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
           const K3Branch& Bi = P.br[P.coarse[c]];
           const int j = (t + 1) / Bi.s - 1;  // held coarse row (none before the first block)
-          const T* src = reinterpret_cast<const T*>(Bi.yc) + ((size_t)b * Bi.n + j) * P.d + col[u];
+          held[u][c] = j >= 0;
+          const T* src = reinterpret_cast<const T*>(Bi.yc) + ((size_t)b * Bi.n + max(j, 0)) * P.d + cc;
 #pragma unroll
-          for (int q = 0; q < NP; ++q) raw[u][c][q] = (ok[u] && j >= 0) ? ld16(src + q * PER) : zero16();
+          for (int q = 0; q < NP; ++q) raw[u][c][q] = ld16(src + q * PER);
         }
       }
     };
@@ -202,6 +206,14 @@ struct K3Fine : K3Rows<T> {
     lds_barrier();  // staged tile and fusion weights visible to all waves
 #pragma unroll 1
     for (;;) {
+      // all gathered values are in registers before the first store, so the
+      // stores are not serialised behind waits for the loads
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+#pragma unroll
+          for (int q = 0; q < NP; ++q) asm volatile("" : "+v"(raw[u][c][q])::"memory");
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         if (!ok[u]) continue;
@@ -221,7 +233,7 @@ struct K3Fine : K3Rows<T> {
           const float wi = P.m > 1 ? wr_[P.coarse[c]] : 1.f;
           float y[8];
 #pragma unroll
-          for (int q = 0; q < NP; ++q) unpack16<T>(raw[u][c][q], y + q * PER);
+          for (int q = 0; q < NP; ++q) unpack16<T>(held[u][c] ? raw[u][c][q] : zero16(), y + q * PER);
 #pragma unroll
           for (int e = 0; e < 8; ++e) v[e] += wi * y[e];
         }
