@@ -74,6 +74,10 @@ struct K1Prob {
       store_qk(acc, wr, wc, lane);
       return;
     }
+    if (!small && n0 >= G.col_v && G.n % 4 == 0) {
+      store_v(acc, wr, wc, lane);
+      return;
+    }
     float* C = reinterpret_cast<float*>(lds);
     gd_stage_tile<K1Cfg>(acc, wr, wc, lane, C);
     lds_barrier();
@@ -107,6 +111,42 @@ struct K1Prob {
 #pragma unroll
         for (int bb = 0; bb < K1Cfg::WN; ++bb) dstc[bb][roff] = acc[a][bb][i];
       }
+  }
+
+  // v tiles go straight from the accumulators to vT[b][hh][chunk][v][tau]: a
+  // lane's 4 consecutive rows are 4 consecutive positions of one channel, in
+  // one chunk of one sequence (n and the chunk length are multiples of 4)
+  __device__ void store_v(const f32x4 (&acc)[K1Cfg::WM][K1Cfg::WN], int wr, int wc, int lane) {
+    const int lrow = lane & 15, lgrp = lane >> 4;
+    T* vT = reinterpret_cast<T*>(G.vT);
+    size_t cbase[K1Cfg::WN];
+    bool cok[K1Cfg::WN];
+#pragma unroll
+    for (int bb = 0; bb < K1Cfg::WN; ++bb) {
+      const int col = n0 + wc * 16 * K1Cfg::WN + 16 * bb + lrow;
+      cok[bb] = col < G.N;
+      const int cv = cok[bb] ? col - G.col_v : 0;
+      const int hh = cv / P.dv, vch = cv - hh * P.dv;
+      cbase[bb] = ((size_t)hh * G.nch * P.dv + vch) * P.C;
+    }
+#pragma unroll
+    for (int a = 0; a < K1Cfg::WM; ++a) {
+      const int m = m0 + wr * 16 * K1Cfg::WM + 16 * a + 4 * lgrp;
+      if (m >= G.M) continue;
+      const int b = m / G.n, j = m - b * G.n;
+      const int chunk = j / P.C, tau = j - chunk * P.C;
+      const size_t roff = (((size_t)b * G.h * G.nch + chunk) * P.dv) * P.C + tau;
+#pragma unroll
+      for (int bb = 0; bb < K1Cfg::WN; ++bb) {
+        if (!cok[bb]) continue;
+        const float f[4] = {acc[a][bb][0], acc[a][bb][1], acc[a][bb][2], acc[a][bb][3]};
+        T* dst = vT + roff + cbase[bb];
+        if constexpr (sizeof(T) == 2)
+          st8(dst, pack8<T>(f));
+        else
+          st16(dst, pack16<T>(f));
+      }
+    }
   }
 
   // gate first factors (fp32 rows of rp) and fusion weights, per unpooled position m
