@@ -152,6 +152,7 @@ __device__ __forceinline__ void gemm_dma_tile(Prob& prob, int n_valid, char* lds
       lds_barrier();
       if (kt + NST - 1 < nk) issue(kt + NST - 1);
       const char* st = lds + (kt % NST) * Cfg::STAGE;
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int sl = 0; sl < Cfg::NSL; ++sl) {
         u32x4 fa[WM], fb[WN];
@@ -167,6 +168,7 @@ __device__ __forceinline__ void gemm_dma_tile(Prob& prob, int n_valid, char* lds
           }
         }
       }
+      __builtin_amdgcn_s_setprio(0);
       if (prob.seg_end(kt)) prob.fold(acc, wr, wc, lane);
     }
   };
