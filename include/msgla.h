@@ -66,6 +66,9 @@ typedef enum { MSGLA_F32 = 0, MSGLA_BF16 = 1 } msgla_dtype;
  *         chunk 32 or 64;
  *   fp32: d_k in {16, 32, 64, 128, 256}, d_v a multiple of 32 in [32, 512],
  *         chunk 16, 32 or 64.
+ * Valid shapes whose chunk-state stages exceed a CU's 160 KB of LDS are not
+ * implemented (MSGLA_ERR_UNSUPPORTED): bf16 d_k 256 with chunk 64; fp32 d_k
+ * 256 with chunk 32 or 64; fp32 d_k 128 with chunk 64.
  */
 typedef struct {
   int32_t n_branches;

@@ -26,6 +26,7 @@ hipError_t pack_transpose(bool bf16_path, const void* src, int R, int Cn, void* 
 hipError_t pack_to_f32(bool src_bf16, const void* src, size_t n, float* dst, hipStream_t st);
 hipError_t fill_zero(void* p, size_t bytes, hipStream_t st);
 int k2b_dvt();
+int k2b_lds_bytes(bool bf16_path, int C, int dk);
 }  // namespace msgla
 
 using namespace msgla;
@@ -74,6 +75,10 @@ msgla_status check_config(const msgla_config* c) {
          : (c->chunk != 16 && c->chunk != 32 && c->chunk != 64))
     return MSGLA_ERR_INVALID_ARG;
   if (!(c->gate_normalizer > 0.f) || !(c->q_scale == c->q_scale)) return MSGLA_ERR_INVALID_ARG;
+  // the state kernel keeps three (or two) chunks of A, qt, kT and V in LDS:
+  // shapes whose stages do not fit the CU's 160 KB are not implemented
+  const int lds = k2b_lds_bytes(bf, c->chunk, c->d_k);
+  if (lds <= 0 || lds > 160 * 1024) return MSGLA_ERR_UNSUPPORTED;
   return MSGLA_OK;
 }
 

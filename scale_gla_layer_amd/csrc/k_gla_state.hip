@@ -325,6 +325,31 @@ static bool launch_k2b_t(const K2Params& P, dim3 grid, hipStream_t stream) {
 
 int k2b_dvt() { return K2B_DVT; }
 
+// LDS bytes one workgroup of the state kernel needs (0: shape not instantiated)
+template <typename T, int C>
+static int k2b_lds_c(int dk) {
+  switch (dk) {
+    case 16: if constexpr (sizeof(T) == 4) return K2bGeom<T, C, 16>::LDS; return 0;
+    case 32: return K2bGeom<T, C, 32>::LDS;
+    case 64: return K2bGeom<T, C, 64>::LDS;
+    case 128: return K2bGeom<T, C, 128>::LDS;
+    case 256: return K2bGeom<T, C, 256>::LDS;
+    default: return 0;
+  }
+}
+
+int k2b_lds_bytes(bool bf16_path, int C, int dk) {
+  if (bf16_path) {
+    if (C == 32) return k2b_lds_c<bf16, 32>(dk);
+    if (C == 64) return k2b_lds_c<bf16, 64>(dk);
+    return 0;
+  }
+  if (C == 16) return k2b_lds_c<float, 16>(dk);
+  if (C == 32) return k2b_lds_c<float, 32>(dk);
+  if (C == 64) return k2b_lds_c<float, 64>(dk);
+  return 0;
+}
+
 hipError_t launch_k2b(const K2Params& P, bool bf16_path, hipStream_t stream) {
   const dim3 grid(((P.total_seqs + N_XCD - 1) / N_XCD) * N_XCD * P.n_dvt);
   const bool ok = bf16_path ? launch_k2b_t<bf16>(P, grid, stream) : launch_k2b_t<float>(P, grid, stream);

@@ -97,6 +97,25 @@ def test_invalid_configs_are_rejected(bad):
     assert lib.msgla_workspace_bytes(ctypes.byref(cc), 1, 8) == 0
 
 
+@pytest.mark.parametrize("shape,status", [
+    (dict(d_k=256, chunk=64), 2),                    # state stages beyond 160 KB of LDS
+    (dict(d_k=256, chunk=32), 0),
+    (dict(d_k=128, chunk=64), 0),
+    (dict(d_k=128, chunk=64, dtype=F32, d_v=64), 2),
+    (dict(d_k=128, chunk=32, dtype=F32, d_v=64), 0),
+    (dict(d_k=256, chunk=32, dtype=F32, d_v=64), 2),
+    (dict(d_k=256, chunk=16, dtype=F32, d_v=64), 0),
+    (dict(d_k=64, chunk=64, dtype=F32, d_v=64), 0),
+])
+def test_state_kernel_lds_limit(shape, status):
+    """Shapes the state kernel cannot stage in one CU's LDS are reported as
+    unsupported by validation, not found out by a failed launch."""
+    lib = binding.load_library()
+    cc = _raw_cfg(**shape)
+    assert lib.msgla_validate_config(ctypes.byref(cc)) == status
+    assert (lib.msgla_packed_weights_bytes(ctypes.byref(cc)) == 0) == (status != 0)
+
+
 def test_too_many_branches_rejected():
     lib = binding.load_library()
     cc = _raw_cfg()

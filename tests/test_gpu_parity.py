@@ -52,6 +52,14 @@ def test_fp32_wider_heads_and_ranks():
     layer_case(cfg, 3, 150, seed=3)
 
 
+@pytest.mark.parametrize("dk,chunk", [(128, 32), (256, 16), (64, 64)])
+def test_fp32_key_width_at_the_lds_limit(dk, chunk):
+    """Widest key widths whose chunk-state stages still fit one CU's LDS
+    (d_k 128 at chunk 32 needs 156 KB; d_k 256 at chunk 16 drops to two stages)."""
+    cfg = MsglaConfig((1, 2), (1, 1), 128, dk, 64, 8, chunk, 16.0, 1.0, F32)
+    layer_case(cfg, 2, 100, seed=9)
+
+
 def test_fp32_strong_and_weak_gates():
     """Gate bias -8 (fast decay, 16-step sub-block growth exercised) and +8 (alpha ~ 1)."""
     for lo, hi in ((-8.0, -8.0), (8.0, 8.0), (-8.0, 8.0)):
@@ -73,6 +81,13 @@ def test_bf16_short_sequences(L):
 
 def test_bf16_chunk32():
     layer_case(_with(MAIN, chunk=32), 2, 200, seed=6)
+
+
+@pytest.mark.parametrize("dk,chunk", [(256, 32), (64, 64), (32, 32)])
+def test_bf16_key_widths(dk, chunk):
+    """Other key widths, including d_k 256 (chunk 32: 144 KB of state-kernel stages)."""
+    cfg = MsglaConfig((1, 2, 4), (1, 1, 1), 256, dk, 128, 16, chunk, 16.0, 1.0, BF16)
+    layer_case(cfg, 2, 200, seed=10)
 
 
 def test_bf16_no_fine_branch_first_row_zero():
