@@ -227,6 +227,9 @@ PROFILE_COMMANDS = {
              "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-gla --no-per-call",
     "write": "rocprofv3 --pmc WRITE_SIZE -f csv -d {d}/pmc_write -o main -- "
              "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-gla --no-per-call",
+    "util": "rocprofv3 --pmc MfmaUtil VALUBusy LdsUtil LDSBankConflict MfmaFlopsBF16 MfmaFlopsF32 "
+            "-f csv -d {d}/pmc_util -o main -- "
+            "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-gla --no-per-call",
     "cal_fetch": "rocprofv3 --pmc FETCH_SIZE -f csv -d {d}/cal_fetch -o copy -- "
                  "python3 bench.py --copy-calibration",
     "cal_write": "rocprofv3 --pmc WRITE_SIZE -f csv -d {d}/cal_write -o copy -- "
@@ -312,6 +315,46 @@ def summarize_profiles(d: str, workload: str = "main"):
             f.write("\n")
     with open(os.path.join(out_dir, f"traffic_{workload}.md"), "w", encoding="utf-8") as f:
         f.write("\n".join(rows) + "\n")
+
+    # utilisation counters (derived metrics of rocprofv3), next to the trace's
+    # average durations and the traffic above
+    util_csv = os.path.join(d, "pmc_util", "main_counter_collection.csv")
+    if os.path.exists(util_csv):
+        per = {}
+        with open(util_csv, newline="", encoding="utf-8") as f:
+            for r in csv.DictReader(f):
+                per.setdefault(_short(r["Kernel_Name"]), {}).setdefault(r["Counter_Name"], []).append(
+                    float(r["Counter_Value"]))
+        avg_us = {_short(r["Name"]): float(r["AverageNs"]) / 1e3 for r in stats}
+        urows = [f"# Utilisation counters per dispatch, workload {workload}", "",
+                 "Command (from the repository root):", "", f"    {cmds['util']}", "",
+                 "MfmaUtil: MFMA-busy cycles over (GPU-active cycles x SIMDs); VALUBusy: "
+                 "cycles with a VALU instruction (MFMA included) active per CU; LdsUtil: "
+                 "cycles the LDS is indexed per CU; LDSBankConflict: bank-conflict cycles per "
+                 "CU, all in percent of the kernel's active cycles. MFMA TFLOP/s and HBM GB/s "
+                 "divide the counted MFMA flops and the calibrated traffic "
+                 f"(traffic_{workload}.md) by the trace's average duration "
+                 f"(kernels_{workload}.md); peaks 2500 TFLOP/s (bf16 dense), 157.3 (fp32) and "
+                 "8000 GB/s.", "",
+                 "| kernel | avg us | MfmaUtil % | VALUBusy % | LdsUtil % | LDS conflict % | "
+                 "MFMA GFLOP | MFMA TFLOP/s | HBM MB | HBM GB/s |",
+                 "|---|---|---|---|---|---|---|---|---|---|"]
+        for stage, kernel in KERNELS.items():
+            if kernel not in per or kernel not in avg_us:
+                continue
+            m = {k: sum(v) / len(v) for k, v in per[kernel].items()}
+            us = avg_us[kernel]
+            fl = m.get("MfmaFlopsBF16", 0.0) + m.get("MfmaFlopsF32", 0.0)
+            hbm = None
+            if kernel in fetch and kernel in write:
+                hbm = fetch[kernel][0] * 1024 * f_fac + write[kernel][0] * 1024 * w_fac
+            urows.append(
+                f"| {kernel} | {us:.2f} | {m.get('MfmaUtil', 0):.1f} | {m.get('VALUBusy', 0):.1f} | "
+                f"{m.get('LdsUtil', 0):.1f} | {m.get('LDSBankConflict', 0):.2f} | {fl / 1e9:.2f} | "
+                f"{fl / (us * 1e-6) / 1e12:.0f} | "
+                + (f"{hbm / 1e6:.1f} | {hbm / (us * 1e-6) / 1e9:.0f} |" if hbm is not None else "- | - |"))
+        with open(os.path.join(out_dir, f"counters_{workload}.md"), "w", encoding="utf-8") as f:
+            f.write("\n".join(urows) + "\n")
     log(f"[bench] wrote profiles for {workload} from {d}")
 
 
