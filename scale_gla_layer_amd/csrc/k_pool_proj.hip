@@ -101,16 +101,23 @@ struct K1Prob {
       dstc[bb] = (isq ? G.q : G.k) + (size_t)hh * G.np * P.dk + ch;
     }
 #pragma unroll
-    for (int a = 0; a < K1Cfg::WM; ++a)
+    for (int a = 0; a < K1Cfg::WM; ++a) {
+      const int ma = m0 + wr * 16 * K1Cfg::WM + 16 * a;  // wave-uniform
+      const int ba = ma / G.n, ja = ma - ba * G.n;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int m = m0 + wr * 16 * K1Cfg::WM + 16 * a + 4 * lgrp + i;
-        if (m >= G.M) continue;
-        const int b = m / G.n, j = m - b * G.n;
+        const int r = 4 * lgrp + i;
+        if (ma + r >= G.M) continue;
+        int b = ba, j = ja + r;
+        while (j >= G.n) {
+          j -= G.n;
+          ++b;
+        }
         const size_t roff = ((size_t)b * G.h * G.np + j) * P.dk;
 #pragma unroll
         for (int bb = 0; bb < K1Cfg::WN; ++bb) dstc[bb][roff] = acc[a][bb][i];
       }
+    }
   }
 
   // v tiles go straight from the accumulators to vT[b][hh][chunk][v][tau]: a
