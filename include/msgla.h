@@ -155,8 +155,15 @@ msgla_status msgla_state_init(const msgla_config* cfg, int64_t B, void* state, s
  *   x [B][L][d] (dtype) -> out [B][L][d] (dtype).
  *   mask: must be NULL (masked pooling, Eq. (8) with M, is not implemented:
  *         MSGLA_ERR_UNSUPPORTED).
- *   state_in: must be NULL (continuing from a previous state is not
- *         implemented: MSGLA_ERR_UNSUPPORTED).
+ *   state_in: NULL (start from an empty state), or a state of the same
+ *         config and B (written by msgla_forward's state_out,
+ *         msgla_state_init or msgla_decode_step) to continue from: its GLA
+ *         states seed the recurrences and its held outputs fill the
+ *         positions before each coarse branch's first block of this call.
+ *         Its position must be a multiple of every scale (no block in
+ *         progress; MSGLA_ERR_UNSUPPORTED otherwise), and a header that does
+ *         not match the config or B gives MSGLA_ERR_INVALID_ARG.  Reading the
+ *         header synchronises `stream` once.  state_in may equal state_out.
  *   state_out: NULL, or a buffer of msgla_state_bytes(cfg, B) that receives
  *         the streaming state after the L tokens (for msgla_decode_step).
  *   workspace: >= msgla_workspace_bytes(cfg, B, L) bytes of device memory;

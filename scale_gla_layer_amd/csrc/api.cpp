@@ -335,14 +335,28 @@ msgla_status msgla_forward_timed(const msgla_config* cfg, const void* packed, co
   if (!batch_ok(B, L)) return MSGLA_ERR_INVALID_ARG;
   if (!packed || !x || !out || !workspace) return MSGLA_ERR_INVALID_ARG;
   if (!aligned16(packed) || !aligned16(x) || !aligned16(out) || !aligned16(workspace) ||
-      (state_out && !aligned16(state_out)))
+      (state_out && !aligned16(state_out)) || (state_in && !aligned16(state_in)))
     return MSGLA_ERR_INVALID_ARG;
-  if (mask || state_in) return MSGLA_ERR_UNSUPPORTED;
+  if (mask) return MSGLA_ERR_UNSUPPORTED;
   const PackGeom g = pack_geom(cfg);
   const WsGeom W = ws_geom(g, B, L);
   if (workspace_bytes < W.total) return MSGLA_ERR_WORKSPACE;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const StGeom S = st_geom(g, B);
+  // Continuing from a state: its header (read once, in stream order) must
+  // describe this batch and a position at a block boundary of every branch,
+  // so that the blocks of this call start at its first token.
+  int64_t pos_in = 0;
+  if (state_in) {
+    StateHeader h{};
+    HIP_TRY(hipMemcpyAsync(&h, state_in, sizeof h, hipMemcpyDeviceToHost, st));
+    HIP_TRY(hipStreamSynchronize(st));
+    if (h.magic != STATE_MAGIC || h.version != STATE_VERSION || h.B != B || h.m != g.m || h.pos < 0)
+      return MSGLA_ERR_INVALID_ARG;
+    for (int i = 0; i < g.m; ++i)
+      if (h.pos % g.br[i].s != 0) return MSGLA_ERR_UNSUPPORTED;
+    pos_in = h.pos;
+  }
 
   auto ev = [&](int stage, bool start) -> hipError_t {
     if (!events) return hipSuccess;
@@ -455,6 +469,7 @@ msgla_status msgla_forward_timed(const msgla_config* cfg, const void* packed, co
     k.lam = at<float>(workspace, wb.lam);
     k.y = at<char>(workspace, wb.y);
     k.S_out = state_out ? at<float>(state_out, S.S[i]) : nullptr;
+    k.S_in = state_in ? at<float>(state_in, S.S[i]) : nullptr;
   }
   p2.total_units = units;
   // K2b: sequences ordered by decreasing chunk count (longest walks start first)
@@ -495,6 +510,7 @@ msgla_status msgla_forward_timed(const msgla_config* cfg, const void* packed, co
     k.np = W.br[i].np;
     k.n = W.br[i].n;
     k.ko = g.br[i].ko;
+    k.held_in = state_in ? at<float>(state_in, S.held[i]) : nullptr;
     if (k.s == 1) {
       p3.fine = i;
     } else if (k.n > 0) {
@@ -504,6 +520,16 @@ msgla_status msgla_forward_timed(const msgla_config* cfg, const void* packed, co
       p3.coarse[p3.ncoarse++] = i;
     }
   }
+  // a coarse branch with no complete block in this call still contributes the
+  // output it held on entry: fused only (no K3c tiles), after the others
+  for (int i = 0; i < g.m; ++i) {
+    K3Branch& k = p3.br[i];
+    if (k.s > 1 && k.n == 0 && k.held_in) {
+      k.tile_begin = ctiles;
+      p3.coarse[p3.ncoarse++] = i;
+    }
+  }
+  p3.held_in = state_in != nullptr;
   p3.c_total = ctiles;
   p3.c_per_xcd = cdiv(ctiles, N_XCD);
   p3.f_total = cdiv((int)(B * L), GEMM_TILE) * p3.tiles_n;
@@ -568,7 +594,7 @@ msgla_status msgla_forward_timed(const msgla_config* cfg, const void* packed, co
     ps.dv = g.dv;
     ps.m = g.m;
     ps.Ktot = g.Ktot;
-    ps.pos = L;
+    ps.pos = pos_in + L;
     ps.x = x;
     ps.WoT = p3.WoT;
     ps.state = state_out;
@@ -583,6 +609,8 @@ msgla_status msgla_forward_timed(const msgla_config* cfg, const void* packed, co
       b.psum = at<float>(state_out, S.psum[i]);
       b.held = at<float>(state_out, S.held[i]);
       b.y = at<char>(workspace, W.br[i].y);
+      b.S_in = state_in ? at<float>(state_in, S.S[i]) : nullptr;
+      b.held_in = state_in ? at<float>(state_in, S.held[i]) : nullptr;
     }
     HIP_TRY(launch_state_export(ps, g.bf16, st));
   }

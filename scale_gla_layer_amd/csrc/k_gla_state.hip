@@ -166,7 +166,31 @@ __global__ __launch_bounds__(K2B_THREADS) void k2b_gla_state(const K2Params P) {
 #pragma unroll
   for (int a = 0; a < G::SRT; ++a) S[a][0] = S[a][1] = zero4();
 
-  for (int i = tid; i < K2B_DVT * G::LDS_S; i += 512) ST[i] = from_f32<T>(0.f);
+  if (!Bb.S_in) {
+    for (int i = tid; i < K2B_DVT * G::LDS_S; i += 512) ST[i] = from_f32<T>(0.f);
+  } else if (!out_wave) {
+    // continuing from a state: each state wave loads its rows of S and
+    // publishes them for chunk 0 as it would a carried state
+    const float* Si = Bb.S_in + (size_t)bh * DK * dv;
+#pragma unroll
+    for (int a = 0; a < G::SRT; ++a) {
+      const int rt = w4 + 4 * a;
+      if (rt < G::NRT) {
+        const int c4 = 16 * rt + 4 * lgp;
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) S[a][ct][e] = Si[(size_t)(c4 + e) * dv + v0 + 16 * ct + lr];
+          const float f[4] = {S[a][ct][0], S[a][ct][1], S[a][ct][2], S[a][ct][3]};
+          T* dst = ST + (16 * ct + lr) * G::LDS_S + c4;
+          if constexpr (sizeof(T) == 2)
+            st8(dst, pack8<T>(f));
+          else
+            st16(dst, pack16<T>(f));
+        }
+      }
+    }
+  }
 
   for (int c = 0; c < Bb.nch; ++c) {
     lds_barrier();  // stage c has landed (the copy wave waited for it)

@@ -142,7 +142,7 @@ constexpr int K3F_W_OFF = K3Cfg::LDS_STAGED;
 constexpr int K3F_LDS = K3F_W_OFF + K3_BM * FUSION_STRIDE * 4;
 static_assert(K3_BM * FUSION_STRIDE * 4 <= K3Cfg::THREADS * 16, "one 16-byte piece per thread");
 
-template <typename T, int NC>
+template <typename T, int NC, bool HELD>
 struct K3Fine : K3Rows<T> {
   bool has_fine;
   __device__ K3Fine(const K3Params& p, const K3Branch& br, bool fine, int m0_, int n0_)
@@ -195,7 +195,11 @@ struct K3Fine : K3Rows<T> {
           const K3Branch& Bi = P.br[P.coarse[c]];
           const int j = (t + 1) / Bi.s - 1;  // held coarse row (none before the first block)
           held[u][c] = j >= 0;
-          const T* src = reinterpret_cast<const T*>(Bi.yc) + ((size_t)b * Bi.n + max(j, 0)) * P.d + cc;
+          // a branch without a block in this call has no coarse rows: read a
+          // valid word of its entry output instead (dropped)
+          const T* src = !HELD || Bi.n > 0
+                             ? reinterpret_cast<const T*>(Bi.yc) + ((size_t)b * Bi.n + max(j, 0)) * P.d + cc
+                             : reinterpret_cast<const T*>(Bi.held_in) + cc;
 #pragma unroll
           for (int q = 0; q < NP; ++q) raw[u][c][q] = ld16(src + q * PER);
         }
@@ -230,10 +234,17 @@ struct K3Fine : K3Rows<T> {
         }
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
+          const K3Branch& Bi = P.br[P.coarse[c]];
           const float wi = P.m > 1 ? wr_[P.coarse[c]] : 1.f;
           float y[8];
 #pragma unroll
           for (int q = 0; q < NP; ++q) unpack16<T>(held[u][c] ? raw[u][c][q] : zero16(), y + q * PER);
+          if (HELD && !held[u][c]) {
+            // before this call's first block: the output held on entry (fp32)
+            const float* hp = Bi.held_in + (size_t)((this->m0 + r[u]) / P.L) * P.d + col[u];
+            unpack16<float>(ld16(hp), y);
+            unpack16<float>(ld16(hp + 4), y + 4);
+          }
 #pragma unroll
           for (int e = 0; e < 8; ++e) v[e] += wi * y[e];
         }
@@ -246,14 +257,16 @@ struct K3Fine : K3Rows<T> {
   }
 };
 
-template <typename T, int NC>
+// HELD: the call continues from a state, so positions before a coarse
+// branch's first block take the output that branch held on entry.
+template <typename T, int NC, bool HELD>
 __global__ __launch_bounds__(K3Cfg::THREADS) void k3f_fine_fuse(const K3Params P) {
   __shared__ __attribute__((aligned(16))) char lds[K3F_LDS];
   const int tile = remap_xcd(blockIdx.x, P.f_per_xcd);
   if (tile >= P.f_total) return;
   const int tm = tile / P.tiles_n, tn = tile - tm * P.tiles_n;
   const bool fine = P.fine >= 0;
-  K3Fine<T, NC> prob(P, P.br[fine ? P.fine : 0], fine, tm * K3_BM, tn * K3_BN);
+  K3Fine<T, NC, HELD> prob(P, P.br[fine ? P.fine : 0], fine, tm * K3_BM, tn * K3_BN);
   gemm_dma_tile<T, K3Cfg>(prob, P.d - tn * K3_BN, lds);
 }
 
@@ -267,19 +280,27 @@ hipError_t launch_k3c(const K3Params& P, bool bf16_path, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <typename T, bool HELD>
+static void launch_k3f_th(const K3Params& P, dim3 grid, dim3 block, hipStream_t stream) {
+  switch (P.ncoarse) {
+    case 0: hipLaunchKernelGGL((k3f_fine_fuse<T, 0, HELD>), grid, block, 0, stream, P); break;
+    case 1: hipLaunchKernelGGL((k3f_fine_fuse<T, 1, HELD>), grid, block, 0, stream, P); break;
+    case 2: hipLaunchKernelGGL((k3f_fine_fuse<T, 2, HELD>), grid, block, 0, stream, P); break;
+    case 3: hipLaunchKernelGGL((k3f_fine_fuse<T, 3, HELD>), grid, block, 0, stream, P); break;
+    case 4: hipLaunchKernelGGL((k3f_fine_fuse<T, 4, HELD>), grid, block, 0, stream, P); break;
+    case 5: hipLaunchKernelGGL((k3f_fine_fuse<T, 5, HELD>), grid, block, 0, stream, P); break;
+    case 6: hipLaunchKernelGGL((k3f_fine_fuse<T, 6, HELD>), grid, block, 0, stream, P); break;
+    case 7: hipLaunchKernelGGL((k3f_fine_fuse<T, 7, HELD>), grid, block, 0, stream, P); break;
+    default: hipLaunchKernelGGL((k3f_fine_fuse<T, 8, HELD>), grid, block, 0, stream, P); break;
+  }
+}
+
 template <typename T>
 static void launch_k3f_t(const K3Params& P, dim3 grid, dim3 block, hipStream_t stream) {
-  switch (P.ncoarse) {
-    case 0: hipLaunchKernelGGL((k3f_fine_fuse<T, 0>), grid, block, 0, stream, P); break;
-    case 1: hipLaunchKernelGGL((k3f_fine_fuse<T, 1>), grid, block, 0, stream, P); break;
-    case 2: hipLaunchKernelGGL((k3f_fine_fuse<T, 2>), grid, block, 0, stream, P); break;
-    case 3: hipLaunchKernelGGL((k3f_fine_fuse<T, 3>), grid, block, 0, stream, P); break;
-    case 4: hipLaunchKernelGGL((k3f_fine_fuse<T, 4>), grid, block, 0, stream, P); break;
-    case 5: hipLaunchKernelGGL((k3f_fine_fuse<T, 5>), grid, block, 0, stream, P); break;
-    case 6: hipLaunchKernelGGL((k3f_fine_fuse<T, 6>), grid, block, 0, stream, P); break;
-    case 7: hipLaunchKernelGGL((k3f_fine_fuse<T, 7>), grid, block, 0, stream, P); break;
-    default: hipLaunchKernelGGL((k3f_fine_fuse<T, 8>), grid, block, 0, stream, P); break;
-  }
+  if (P.held_in)
+    launch_k3f_th<T, true>(P, grid, block, stream);
+  else
+    launch_k3f_th<T, false>(P, grid, block, stream);
 }
 
 hipError_t launch_k3f(const K3Params& P, bool bf16_path, hipStream_t stream) {

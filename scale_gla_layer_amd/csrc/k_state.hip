@@ -35,9 +35,11 @@ __global__ void k_state_export(const StateParams P) {
     float s = 0.f;
     for (int t = Br.n * Br.s; t < P.L; ++t) s += to_f32(x[((size_t)b * P.L + t) * P.d + col]);
     Br.psum[(size_t)b * P.d + col] = s;
-    // held output of the last complete block
-    float acc = 0.f;
+    // held output of the last complete block (or, without one, the output
+    // held on entry)
+    float acc = Br.held_in ? Br.held_in[(size_t)b * P.d + col] : 0.f;
     if (Br.n > 0) {
+      acc = 0.f;
       const T* y = reinterpret_cast<const T*>(Br.y);
       const T* wo = reinterpret_cast<const T*>(P.WoT) + (size_t)col * P.Ktot + Br.ko;
       for (int hh = 0; hh < Br.h; ++hh) {
@@ -47,8 +49,9 @@ __global__ void k_state_export(const StateParams P) {
     }
     Br.held[(size_t)b * P.d + col] = acc;
   }
-  // a branch that saw no complete block keeps a zero GLA state
-  if (Br.n == 0) {
+  // a branch that saw no complete block keeps its GLA state: zero, or the
+  // entry state, which the state kernel has already copied to the output
+  if (Br.n == 0 && !Br.S_in) {
     const size_t per_b = (size_t)Br.h * P.dk * P.dv;
     for (size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x; e < per_b;
          e += (size_t)gridDim.x * blockDim.x)

@@ -134,6 +134,7 @@ struct K2Branch {
   float* lam;
   void* y;
   float* S_out;     // state S of this branch [B][h][dk][dv] or null
+  const float* S_in;  // state S the walk starts from [B][h][dk][dv], null: zero
 };
 
 struct K2Params {
@@ -156,6 +157,7 @@ struct K3Branch {
   int s, h, np, n;
   int ko;           // K offset of the branch in the stacked W_o^T
   int tile_begin;   // first tile of the branch in the coarse work list
+  const float* held_in;  // output held from before this call [B][d] fp32, null: zero
 };
 
 struct K3Params {
@@ -166,6 +168,7 @@ struct K3Params {
   int tiles_n;                        // column tiles of d
   int c_total, c_per_xcd;             // coarse GEMM work list (K3c)
   int f_total, f_per_xcd;             // fine GEMM + fusion work list (K3f)
+  int held_in;                        // the call continues from a state
   const void* zero; // >= 128 zero bytes (rows outside the problem)
   const void* WoT;  // [d][Ktot]
   const float* w;   // fusion weights [B L][8]
@@ -184,6 +187,8 @@ struct StateBranch {
   int s, h, n, np, ko;
   float* S; float* psum; float* held;
   const void* y;    // forward workspace y (export only)
+  const float* S_in;     // state the forward started from (kept when n == 0), or null
+  const float* held_in;
 };
 
 struct StateParams {
