@@ -25,9 +25,9 @@ TINY = WORKLOADS["tiny_f32"].cfg
 MAIN = WORKLOADS["main"].cfg
 
 
-def _split_run(cfg, B, L1, L2, seed, same_buffer):
+def _split_run(cfg, B, L1, L2, seed, same_buffer, gate_bias=None):
     import torch
-    X, W = make_inputs(cfg, B, L1 + L2, seed=seed)
+    X, W = make_inputs(cfg, B, L1 + L2, seed=seed, gate_bias=gate_bias)
     layer = DeviceLayer(cfg, W)
     s1 = layer.new_state(B)
     s2 = s1 if same_buffer else layer.new_state(B)
@@ -59,6 +59,16 @@ def test_continue_matches_one_pass(cfg_name, B, L1, L2, same):
                 a, b = bd[key], br[key]
                 scale = max(1e-30, np.abs(b).max())
                 assert np.abs(a - b).max() <= TOL["f32"] * scale + 1e-12, (i, key)
+
+
+def test_sequence_shards_at_long_context_gates():
+    """Two 2048-token shards of one sequence with the long workload's gates
+    (alpha near 1, so the carried state dominates the second shard)."""
+    wl = WORKLOADS["long"]
+    say("state_in shards B=1 2 x 2048, gate bias U(1,4)")
+    X, W, O, _ = _split_run(wl.cfg, 1, 2048, 2048, seed=14, same_buffer=True,
+                            gate_bias=wl.gate_bias)
+    check_against_oracle(wl.cfg, X, W, O)
 
 
 def test_position_inside_a_block_is_unsupported():
