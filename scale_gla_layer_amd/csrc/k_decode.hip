@@ -10,10 +10,11 @@
 // branch whose block is not complete skips its work:
 //   D0 pool:   psum += x_t; on completion xp = psum / s, psum = 0;
 //              plus the fusion weights of x_t (one block per sequence)
-//   D1 proj:   [q | k | v | g] = xp Wp^T for completing branches (one wave per column)
+//   D1 proj:   [q | k | v | g] = xp Wp^T for completing branches (MFMA, 16 sequences x
+//              16 columns per wave)
 //   D2 state:  gate, state update and o = q S per (branch, sequence, head, d_v tile)
-//   D3 out:    held = o W_o for completing branches, out = sum_i w_i held_i,
-//              header position + 1
+//   D3 out:    held = o W_o for completing branches (MFMA as D1), out = sum_i w_i
+//              held_i, header position + 1
 #include "device_common.hpp"
 #include "layout.hpp"
 
@@ -81,21 +82,47 @@ __global__ __launch_bounds__(DEC_THREADS) void k_dec_pool(const DecParams P) {
   }
 }
 
-// grid (ceil(Nmax / 4), m): each wave computes one projection column for all B
+// Batched row-times-matrix products of the step as MFMA tiles: the (up to)
+// 16 sequences of a batch tile are the 16 rows of the A operand, 16 weight
+// rows the B operand, K the model width (one 64-byte k-slab per MFMA), so one
+// wave forms 16 x 16 outputs and every weight is read once per batch tile.
+// A-operand rows come from fp32 vectors rounded to the storage type, as the
+// forward rounds its pooled rows and its y.
+template <typename T>
+__device__ __forceinline__ f32x4 dec_rows_times_cols(const float* xrow, bool xok, const T* wrow, int K) {
+  constexpr int PER = per16<T>(), SLAB = 4 * PER;
+  f32x4 acc = zero4();
+#pragma unroll 4
+  for (int k0 = 0; k0 < K; k0 += SLAB) {
+    const u32x4 wf = ld16(wrow + k0);
+    float xv[PER];
+#pragma unroll
+    for (int q = 0; q < PER; q += 4) unpack16<float>(xok ? ld16(xrow + k0 + q) : zero16(), xv + q);
+    acc = mma_slab<T>(pack16<T>(xv), wf, acc);
+  }
+  return acc;
+}
+
+// grid (ceil(Nmax / 64), m, ceil(B / 16)); wave w: projection columns
+// 64 x + 16 w .. + 15 for sequences 16 z .. 16 z + 15
 template <typename T>
 __global__ __launch_bounds__(DEC_THREADS) void k_dec_proj(const DecParams P) {
   const DecBranch& Br = P.br[blockIdx.y];
   if (!completes(dec_pos(P.state), Br.s)) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int n = blockIdx.x * 4 + wave;
-  if (n >= Br.N) return;
-  const T* w = reinterpret_cast<const T*>(Br.Wp) + (size_t)n * P.d;
-  for (int b = 0; b < P.B; ++b) {
-    const float* xp = Br.xp + (size_t)b * P.d;
-    float acc = 0.f;
-    for (int c = lane; c < P.d; c += WAVE) acc = fmaf(xp[c], to_f32(w[c]), acc);
-    acc = wave_sum(acc);
-    if (lane == 0) Br.proj[(size_t)b * Br.N + n] = acc;
+  const int lr = lane & 15, lg = lane >> 4;
+  const int n0 = blockIdx.x * 64 + wave * 16, b0 = blockIdx.z * 16;
+  if (n0 >= Br.N) return;
+  constexpr int PER = per16<T>();
+  const int n = min(n0 + lr, Br.N - 1), b = b0 + lr;  // B-operand row, A-operand row
+  const T* wrow = reinterpret_cast<const T*>(Br.Wp) + (size_t)n * P.d + PER * lg;
+  const float* xrow = Br.xp + (size_t)(b < P.B ? b : 0) * P.d + PER * lg;
+  const f32x4 acc = dec_rows_times_cols<T>(xrow, b < P.B, wrow, P.d);
+  // acc[e]: sequence b0 + 4 lg + e, column n0 + lr
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int bb = b0 + 4 * lg + e;
+    if (bb < P.B && n0 + lr < Br.N) Br.proj[(size_t)bb * Br.N + n0 + lr] = acc[e];
   }
 }
 
@@ -139,43 +166,63 @@ __global__ __launch_bounds__(DEC_THREADS) void k_dec_state(const DecParams P) {
     Br.y[(size_t)b * Br.h * P.dv + hh * P.dv + v] = part[lane] + part[64 + lane] + part[128 + lane] + part[192 + lane];
 }
 
-// grid (ceil(d / 4)); each wave produces one output column for all B
+// grid (d / 64, ceil(B / 16)); wave w: output columns 64 x + 16 w .. + 15 for
+// sequences 16 y .. 16 y + 15.  A completing branch replaces its held output
+// by y W_o (MFMA over K = h d_v), the others keep theirs; out = sum_i w_i held_i.
 template <typename T>
 __global__ __launch_bounds__(DEC_THREADS) void k_dec_out(const DecParams P) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int n = blockIdx.x * 4 + wave;
+  const int lr = lane & 15, lg = lane >> 4;
+  const int n0 = blockIdx.x * 64 + wave * 16, b0 = blockIdx.y * 16;
   const int64_t pos = *P.pos_ws;
-  if (blockIdx.x == 0 && threadIdx.x == 0) reinterpret_cast<StateHeader*>(P.state)->pos = pos + 1;
-  if (n >= P.d) return;
-  const T* wo = reinterpret_cast<const T*>(P.WoT) + (size_t)n * P.Ktot;
-  T* out = reinterpret_cast<T*>(P.out);
-  for (int b = 0; b < P.B; ++b) {
-    float o = 0.f;
-    for (int i = 0; i < P.nbranch; ++i) {
-      const DecBranch& Br = P.br[i];
-      float held;
-      if (completes(pos, Br.s)) {
-        const int K = Br.h * P.dv;
-        const float* y = Br.y + (size_t)b * K;
-        float acc = 0.f;
-        for (int k = lane; k < K; k += WAVE) acc = fmaf(y[k], to_f32(wo[Br.ko + k]), acc);
-        held = wave_sum(acc);
-        if (lane == 0) Br.held[(size_t)b * P.d + n] = held;
-      } else {
-        held = Br.held[(size_t)b * P.d + n];
+  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0)
+    reinterpret_cast<StateHeader*>(P.state)->pos = pos + 1;
+  if (n0 >= P.d) return;
+  constexpr int PER = per16<T>();
+  const int n = n0 + lr;  // d is a multiple of 64
+  float o[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < P.nbranch; ++i) {
+    const DecBranch& Br = P.br[i];
+    float held[4];
+    if (completes(pos, Br.s)) {
+      const int K = Br.h * P.dv, b = b0 + lr;
+      const T* wrow = reinterpret_cast<const T*>(P.WoT) + (size_t)n * P.Ktot + Br.ko + PER * lg;
+      const float* yrow = Br.y + (size_t)(b < P.B ? b : 0) * K + PER * lg;
+      const f32x4 acc = dec_rows_times_cols<T>(yrow, b < P.B, wrow, K);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        held[e] = acc[e];
+        const int bb = b0 + 4 * lg + e;
+        if (bb < P.B) Br.held[(size_t)bb * P.d + n] = held[e];
       }
-      o += (P.m > 1 ? P.w[(size_t)b * FUSION_STRIDE + i] : 1.f) * held;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int bb = b0 + 4 * lg + e;
+        held[e] = bb < P.B ? Br.held[(size_t)bb * P.d + n] : 0.f;
+      }
     }
-    if (lane == 0) out[(size_t)b * P.d + n] = from_f32<T>(o);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int bb = b0 + 4 * lg + e;
+      o[e] += (P.m > 1 && bb < P.B ? P.w[(size_t)bb * FUSION_STRIDE + i] : 1.f) * held[e];
+    }
+  }
+  T* out = reinterpret_cast<T*>(P.out);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int bb = b0 + 4 * lg + e;
+    if (bb < P.B) out[(size_t)bb * P.d + n] = from_f32<T>(o[e]);
   }
 }
 
 hipError_t launch_decode(const DecParams& P, int Nmax, int hmax, bool bf16_path, hipStream_t st) {
   const dim3 blk(DEC_THREADS);
   const dim3 g0((P.d + DEC_THREADS - 1) / DEC_THREADS, P.B, P.nbranch + 1);
-  const dim3 g1((Nmax + 3) / 4, P.nbranch);
+  const int btiles = (P.B + 15) / 16;
+  const dim3 g1((Nmax + 63) / 64, P.nbranch, btiles);
   const dim3 g2(P.B * hmax, (P.dv + 63) / 64, P.nbranch);
-  const dim3 g3((P.d + 3) / 4);
+  const dim3 g3(P.d / 64, btiles);
   const size_t lds2 = (size_t)(3 * P.dk + 4 * 64) * sizeof(float);
   if (bf16_path) {
     hipLaunchKernelGGL(k_dec_pool<bf16>, g0, blk, 0, st, P);
