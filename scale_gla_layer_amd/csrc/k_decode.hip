@@ -84,40 +84,74 @@ __global__ __launch_bounds__(DEC_THREADS) void k_dec_pool(const DecParams P) {
 
 // Batched row-times-matrix products of the step as MFMA tiles: the (up to)
 // 16 sequences of a batch tile are the 16 rows of the A operand, 16 weight
-// rows the B operand, K the model width (one 64-byte k-slab per MFMA), so one
+// rows the B operand, and K runs in 64-byte k-slabs (one MFMA each), so a
 // wave forms 16 x 16 outputs and every weight is read once per batch tile.
 // A-operand rows come from fp32 vectors rounded to the storage type, as the
-// forward rounds its pooled rows and its y.
+// forward rounds its pooled rows and its y.  The slabs of a wave's K range
+// are loaded NS at a time before any is used (a decode step is latency-bound).
 template <typename T>
-__device__ __forceinline__ f32x4 dec_rows_times_cols(const float* xrow, bool xok, const T* wrow, int K) {
-  constexpr int PER = per16<T>(), SLAB = 4 * PER;
-  f32x4 acc = zero4();
-#pragma unroll 4
-  for (int k0 = 0; k0 < K; k0 += SLAB) {
-    const u32x4 wf = ld16(wrow + k0);
-    float xv[PER];
+__device__ __forceinline__ f32x4 dec_rows_times_cols(const float* xrow, bool xok, const T* wrow, int K,
+                                                     f32x4 acc) {
+  constexpr int PER = per16<T>(), SLAB = 4 * PER, NS = 8;
+  for (int k0 = 0; k0 < K; k0 += NS * SLAB) {
+    u32x4 wf[NS], xf[NS * PER / 4];
 #pragma unroll
-    for (int q = 0; q < PER; q += 4) unpack16<float>(xok ? ld16(xrow + k0 + q) : zero16(), xv + q);
-    acc = mma_slab<T>(pack16<T>(xv), wf, acc);
+    for (int u = 0; u < NS; ++u) {
+      const bool in = k0 + u * SLAB < K;
+      wf[u] = in ? ld16(wrow + k0 + u * SLAB) : zero16();
+#pragma unroll
+      for (int q = 0; q < PER / 4; ++q)
+        xf[u * (PER / 4) + q] = in && xok ? ld16(xrow + k0 + u * SLAB + 4 * q) : zero16();
+    }
+#pragma unroll
+    for (int u = 0; u < NS; ++u) {
+      float xv[PER];
+#pragma unroll
+      for (int q = 0; q < PER / 4; ++q) unpack16<float>(xf[u * (PER / 4) + q], xv + 4 * q);
+      acc = mma_slab<T>(pack16<T>(xv), wf[u], acc);
+    }
   }
   return acc;
 }
 
-// grid (ceil(Nmax / 64), m, ceil(B / 16)); wave w: projection columns
-// 64 x + 16 w .. + 15 for sequences 16 z .. 16 z + 15
+// Sum of the four waves' 16 x 16 partial tiles through LDS; wave 0 returns it.
+__device__ __forceinline__ f32x4 dec_reduce4(f32x4 acc, float* red, int wave, int lane) {
+  if (wave > 0) {
+    const float t[4] = {acc[0], acc[1], acc[2], acc[3]};
+    st16(red + ((wave - 1) * 64 + lane) * 4, pack16<float>(t));
+  }
+  __syncthreads();
+  if (wave == 0)
+#pragma unroll
+    for (int w = 0; w < 3; ++w) {
+      float t[4];
+      unpack16<float>(ld16(red + (w * 64 + lane) * 4), t);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] += t[e];
+    }
+  return acc;
+}
+
+// grid (ceil(Nmax / 16), m, ceil(B / 16)): projection columns 16 x .. 16 x + 15
+// for sequences 16 z .. 16 z + 15; the four waves take a quarter of K each
 template <typename T>
 __global__ __launch_bounds__(DEC_THREADS) void k_dec_proj(const DecParams P) {
   const DecBranch& Br = P.br[blockIdx.y];
   if (!completes(dec_pos(P.state), Br.s)) return;
+  __shared__ __attribute__((aligned(16))) float red[3 * 64 * 4];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int lr = lane & 15, lg = lane >> 4;
-  const int n0 = blockIdx.x * 64 + wave * 16, b0 = blockIdx.z * 16;
+  const int n0 = blockIdx.x * 16, b0 = blockIdx.z * 16;
   if (n0 >= Br.N) return;
-  constexpr int PER = per16<T>();
+  constexpr int PER = per16<T>(), SLAB = 4 * PER;
   const int n = min(n0 + lr, Br.N - 1), b = b0 + lr;  // B-operand row, A-operand row
-  const T* wrow = reinterpret_cast<const T*>(Br.Wp) + (size_t)n * P.d + PER * lg;
-  const float* xrow = Br.xp + (size_t)(b < P.B ? b : 0) * P.d + PER * lg;
-  const f32x4 acc = dec_rows_times_cols<T>(xrow, b < P.B, wrow, P.d);
+  // wave w: k-slabs [w nsl / 4, (w + 1) nsl / 4) of the nsl = d / SLAB
+  const int nsl = P.d / SLAB, k_lo = wave * nsl / 4 * SLAB, k_hi = (wave + 1) * nsl / 4 * SLAB;
+  const T* wrow = reinterpret_cast<const T*>(Br.Wp) + (size_t)n * P.d + k_lo + PER * lg;
+  const float* xrow = Br.xp + (size_t)(b < P.B ? b : 0) * P.d + k_lo + PER * lg;
+  f32x4 acc = dec_rows_times_cols<T>(xrow, b < P.B, wrow, k_hi - k_lo, zero4());
+  acc = dec_reduce4(acc, red, wave, lane);
+  if (wave != 0) return;
   // acc[e]: sequence b0 + 4 lg + e, column n0 + lr
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
@@ -166,29 +200,30 @@ __global__ __launch_bounds__(DEC_THREADS) void k_dec_state(const DecParams P) {
     Br.y[(size_t)b * Br.h * P.dv + hh * P.dv + v] = part[lane] + part[64 + lane] + part[128 + lane] + part[192 + lane];
 }
 
-// grid (d / 64, ceil(B / 16)); wave w: output columns 64 x + 16 w .. + 15 for
-// sequences 16 y .. 16 y + 15.  A completing branch replaces its held output
-// by y W_o (MFMA over K = h d_v), the others keep theirs; out = sum_i w_i held_i.
+// grid (d / 16, ceil(B / 16)): output columns 16 x .. 16 x + 15 for sequences
+// 16 y .. 16 y + 15.  Wave w takes branches w, w + 4, ...: a completing branch
+// replaces its held output by y W_o (MFMA over K = h d_v), the others keep
+// theirs; the waves' weighted sums meet in LDS and out = sum_i w_i held_i.
 template <typename T>
 __global__ __launch_bounds__(DEC_THREADS) void k_dec_out(const DecParams P) {
+  __shared__ __attribute__((aligned(16))) float red[3 * 64 * 4];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int lr = lane & 15, lg = lane >> 4;
-  const int n0 = blockIdx.x * 64 + wave * 16, b0 = blockIdx.y * 16;
+  const int n0 = blockIdx.x * 16, b0 = blockIdx.y * 16;
   const int64_t pos = *P.pos_ws;
   if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0)
     reinterpret_cast<StateHeader*>(P.state)->pos = pos + 1;
-  if (n0 >= P.d) return;
   constexpr int PER = per16<T>();
   const int n = n0 + lr;  // d is a multiple of 64
-  float o[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int i = 0; i < P.nbranch; ++i) {
+  f32x4 o = zero4();
+  for (int i = wave; i < P.nbranch; i += 4) {
     const DecBranch& Br = P.br[i];
     float held[4];
     if (completes(pos, Br.s)) {
       const int K = Br.h * P.dv, b = b0 + lr;
       const T* wrow = reinterpret_cast<const T*>(P.WoT) + (size_t)n * P.Ktot + Br.ko + PER * lg;
       const float* yrow = Br.y + (size_t)(b < P.B ? b : 0) * K + PER * lg;
-      const f32x4 acc = dec_rows_times_cols<T>(yrow, b < P.B, wrow, K);
+      const f32x4 acc = dec_rows_times_cols<T>(yrow, b < P.B, wrow, K, zero4());
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         held[e] = acc[e];
@@ -208,6 +243,8 @@ __global__ __launch_bounds__(DEC_THREADS) void k_dec_out(const DecParams P) {
       o[e] += (P.m > 1 && bb < P.B ? P.w[(size_t)bb * FUSION_STRIDE + i] : 1.f) * held[e];
     }
   }
+  o = dec_reduce4(o, red, wave, lane);
+  if (wave != 0) return;
   T* out = reinterpret_cast<T*>(P.out);
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
@@ -220,9 +257,9 @@ hipError_t launch_decode(const DecParams& P, int Nmax, int hmax, bool bf16_path,
   const dim3 blk(DEC_THREADS);
   const dim3 g0((P.d + DEC_THREADS - 1) / DEC_THREADS, P.B, P.nbranch + 1);
   const int btiles = (P.B + 15) / 16;
-  const dim3 g1((Nmax + 63) / 64, P.nbranch, btiles);
+  const dim3 g1((Nmax + 15) / 16, P.nbranch, btiles);
   const dim3 g2(P.B * hmax, (P.dv + 63) / 64, P.nbranch);
-  const dim3 g3(P.d / 64, btiles);
+  const dim3 g3(P.d / 16, btiles);
   const size_t lds2 = (size_t)(3 * P.dk + 4 * 64) * sizeof(float);
   if (bf16_path) {
     hipLaunchKernelGGL(k_dec_pool<bf16>, g0, blk, 0, st, P);

@@ -46,6 +46,13 @@ def test_decode_tiny_fp32(L0):
     _decode_case(WORKLOADS["tiny_f32"].cfg, 2, L0, 20, seed=3)
 
 
+def test_decode_bf16_narrow_model():
+    """d = 64: the step's projection splits K into fewer slabs than waves."""
+    from scale_gla_layer_amd.config import BF16, MsglaConfig
+    cfg = MsglaConfig((1, 2), (1, 1), 64, 32, 64, 4, 32, 16.0, 1.0, BF16)
+    _decode_case(cfg, 3, 9, 12, seed=6)
+
+
 @pytest.mark.parametrize("name", ["main", "sweep_1248", "sweep_24"])
 def test_decode_bf16_small(name):
     _decode_case(WORKLOADS[name].cfg, 2, 45, 24, seed=4)
