@@ -198,7 +198,7 @@ StGeom st_geom(const PackGeom& g, int64_t B) {
 }
 
 struct DecGeom {
-  size_t xp[MSGLA_MAX_BRANCHES], proj[MSGLA_MAX_BRANCHES], y[MSGLA_MAX_BRANCHES];
+  size_t proj[MSGLA_MAX_BRANCHES], y[MSGLA_MAX_BRANCHES];
   size_t w, pos, total;
 };
 
@@ -206,8 +206,6 @@ DecGeom dec_geom(const PackGeom& g, int64_t B) {
   DecGeom d{};
   size_t cur = 0;
   for (int i = 0; i < g.m; ++i) {
-    d.xp[i] = cur;
-    cur += align256((size_t)B * g.d * 4);
     d.proj[i] = cur;
     cur += align256((size_t)B * g.br[i].N * 4);
     d.y[i] = cur;
@@ -680,7 +678,6 @@ msgla_status msgla_decode_step(const msgla_config* cfg, const void* packed, cons
     k.S = at<float>(state, S.S[i]);
     k.psum = at<float>(state, S.psum[i]);
     k.held = at<float>(state, S.held[i]);
-    k.xp = at<float>(workspace, D.xp[i]);
     k.proj = at<float>(workspace, D.proj[i]);
     k.y = at<float>(workspace, D.y[i]);
     Nmax = std::max(Nmax, b.N);

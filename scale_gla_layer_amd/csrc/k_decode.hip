@@ -5,16 +5,17 @@
 // o = q S, and the held output is replaced; the branches are fused with
 // softmax weights from the unpooled token, Eqs. (10)-(11)).
 //
-// Four launches per token, all enqueued without host synchronisation; each
+// Three launches per token, all enqueued without host synchronisation; each
 // kernel reads the token count from the state header on the device and a
 // branch whose block is not complete skips its work:
-//   D0 pool:   psum += x_t; on completion xp = psum / s, psum = 0;
-//              plus the fusion weights of x_t (one block per sequence)
-//   D1 proj:   [q | k | v | g] = xp Wp^T for completing branches (MFMA, 16 sequences x
-//              16 columns per wave)
+//   D1 proj:   [q | k | v | g] = xp Wp^T for completing branches, where the
+//              pooled row xp = (pending sum + x_t) / s is formed as the MFMA
+//              operand is loaded, plus the fusion logits x_t W_f
+//              (MFMA, 16 sequences x 16 columns per block)
 //   D2 state:  gate, state update and o = q S per (branch, sequence, head, d_v tile)
-//   D3 out:    held = o W_o for completing branches (MFMA as D1), out = sum_i w_i
-//              held_i, header position + 1
+//   D3 out:    held = o W_o for completing branches (MFMA as D1), the fusion
+//              softmax, out = sum_i w_i held_i, the pending sums (reset or
+//              accumulate x_t), header position + 1
 #include "device_common.hpp"
 #include "layout.hpp"
 
@@ -33,81 +34,48 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-// grid (ceil(d/256), B, m + 1): z == m computes the fusion weights of sequence y
-template <typename T>
-__global__ __launch_bounds__(DEC_THREADS) void k_dec_pool(const DecParams P) {
-  const int b = blockIdx.y, i = blockIdx.z;
-  const int64_t pos = dec_pos(P.state);
-  const T* x = reinterpret_cast<const T*>(P.x) + (size_t)b * P.d;
-  if (i < P.nbranch) {
-    const DecBranch& Br = P.br[i];
-    const int col = blockIdx.x * DEC_THREADS + threadIdx.x;
-    if (col < P.d) {
-      const float ps = Br.psum[(size_t)b * P.d + col] + to_f32(x[col]);
-      if (completes(pos, Br.s)) {
-        Br.xp[(size_t)b * P.d + col] = ps / (float)Br.s;
-        Br.psum[(size_t)b * P.d + col] = 0.f;
-      } else {
-        Br.psum[(size_t)b * P.d + col] = ps;
-      }
-    }
-    if (blockIdx.x == 0 && b == 0 && i == 0 && threadIdx.x == 0) *P.pos_ws = pos;
-    return;
-  }
-  if (blockIdx.x != 0) return;
-  // fusion weights of this token (Eq. (10)); m == 1 -> weight 1
-  __shared__ float red[DEC_THREADS / WAVE][FUSION_STRIDE];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const T* wz = reinterpret_cast<const T*>(P.Wz);
-  float z[FUSION_STRIDE];
-  for (int e = 0; e < P.m; ++e) {
-    float acc = 0.f;
-    if (P.m > 1)
-      for (int c = threadIdx.x; c < P.d; c += DEC_THREADS) acc += to_f32(x[c]) * to_f32(wz[(size_t)e * P.d + c]);
-    acc = wave_sum(acc);
-    if (lane == 0) red[wave][e] = acc;
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    float mx = -INFINITY, sum = 0.f;
-    for (int e = 0; e < P.m; ++e) {
-      z[e] = red[0][e] + red[1][e] + red[2][e] + red[3][e] + P.bf[e];
-      mx = fmaxf(mx, z[e]);
-    }
-    for (int e = 0; e < P.m; ++e) {
-      z[e] = __expf(z[e] - mx);
-      sum += z[e];
-    }
-    for (int e = 0; e < FUSION_STRIDE; ++e) P.w[(size_t)b * FUSION_STRIDE + e] = (e < P.m) ? z[e] / sum : 0.f;
-  }
-}
-
 // Batched row-times-matrix products of the step as MFMA tiles: the (up to)
 // 16 sequences of a batch tile are the 16 rows of the A operand, 16 weight
 // rows the B operand, and K runs in 64-byte k-slabs (one MFMA each), so a
 // wave forms 16 x 16 outputs and every weight is read once per batch tile.
-// A-operand rows come from fp32 vectors rounded to the storage type, as the
-// forward rounds its pooled rows and its y.  The slabs of a wave's K range
-// are loaded NS at a time before any is used (a decode step is latency-bound).
-template <typename T>
-__device__ __forceinline__ f32x4 dec_rows_times_cols(const float* xrow, bool xok, const T* wrow, int K,
-                                                     f32x4 acc) {
-  constexpr int PER = per16<T>(), SLAB = 4 * PER, NS = 8;
+// A-operand row k is (F ? frow[k] : 0) + (X ? trow[k] : 0), times `scale`, in
+// fp32, rounded to the storage type as the forward rounds its pooled rows and
+// its y.  The slabs of a wave's K range are loaded NS at a time before any is
+// used (a decode step is latency-bound).
+template <typename T, bool F, bool X>
+__device__ __forceinline__ f32x4 dec_rows_times_cols(const float* frow, const T* trow, float scale,
+                                                     bool rok, const T* wrow, int K, f32x4 acc) {
+  constexpr int PER = per16<T>(), SLAB = 4 * PER, NS = 8, NF = PER / 4;
   for (int k0 = 0; k0 < K; k0 += NS * SLAB) {
-    u32x4 wf[NS], xf[NS * PER / 4];
+    u32x4 wf[NS], ff[NS * NF], tf[NS];
 #pragma unroll
     for (int u = 0; u < NS; ++u) {
-      const bool in = k0 + u * SLAB < K;
-      wf[u] = in ? ld16(wrow + k0 + u * SLAB) : zero16();
+      const int k = k0 + u * SLAB;
+      const bool in = k < K;
+      wf[u] = in ? ld16(wrow + k) : zero16();
+      if constexpr (F) {
 #pragma unroll
-      for (int q = 0; q < PER / 4; ++q)
-        xf[u * (PER / 4) + q] = in && xok ? ld16(xrow + k0 + u * SLAB + 4 * q) : zero16();
+        for (int q = 0; q < NF; ++q) ff[u * NF + q] = in && rok ? ld16(frow + k + 4 * q) : zero16();
+      }
+      if constexpr (X) tf[u] = in && rok ? ld16(trow + k) : zero16();
     }
 #pragma unroll
     for (int u = 0; u < NS; ++u) {
       float xv[PER];
 #pragma unroll
-      for (int q = 0; q < PER / 4; ++q) unpack16<float>(xf[u * (PER / 4) + q], xv + 4 * q);
+      for (int e = 0; e < PER; ++e) xv[e] = 0.f;
+      if constexpr (F) {
+#pragma unroll
+        for (int q = 0; q < NF; ++q) unpack16<float>(ff[u * NF + q], xv + 4 * q);
+      }
+      if constexpr (X) {
+        float tv[PER];
+        unpack16<T>(tf[u], tv);
+#pragma unroll
+        for (int e = 0; e < PER; ++e) xv[e] += tv[e];
+      }
+#pragma unroll
+      for (int e = 0; e < PER; ++e) xv[e] *= scale;
       acc = mma_slab<T>(pack16<T>(xv), wf[u], acc);
     }
   }
@@ -132,31 +100,49 @@ __device__ __forceinline__ f32x4 dec_reduce4(f32x4 acc, float* red, int wave, in
   return acc;
 }
 
-// grid (ceil(Nmax / 16), m, ceil(B / 16)): projection columns 16 x .. 16 x + 15
-// for sequences 16 z .. 16 z + 15; the four waves take a quarter of K each
+// grid (ceil(Nmax / 16), m + 1, ceil(B / 16)): projection columns 16 x .. 16 x
+// + 15 of branch y (y == m: the fusion logits) for sequences 16 z .. 16 z + 15;
+// the four waves take a quarter of K each
 template <typename T>
 __global__ __launch_bounds__(DEC_THREADS) void k_dec_proj(const DecParams P) {
-  const DecBranch& Br = P.br[blockIdx.y];
-  if (!completes(dec_pos(P.state), Br.s)) return;
+  const int64_t pos = dec_pos(P.state);
+  if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x == 0)
+    *P.pos_ws = pos;  // this step's position, for the output kernel
+  const bool logits = blockIdx.y == P.nbranch;
+  if (logits && P.m == 1) return;
+  const DecBranch& Br = P.br[logits ? 0 : blockIdx.y];
+  if (!logits && !completes(pos, Br.s)) return;
+  const int N = logits ? P.m : Br.N;
   __shared__ __attribute__((aligned(16))) float red[3 * 64 * 4];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int lr = lane & 15, lg = lane >> 4;
   const int n0 = blockIdx.x * 16, b0 = blockIdx.z * 16;
-  if (n0 >= Br.N) return;
+  if (n0 >= N) return;
   constexpr int PER = per16<T>(), SLAB = 4 * PER;
-  const int n = min(n0 + lr, Br.N - 1), b = b0 + lr;  // B-operand row, A-operand row
+  const int n = min(n0 + lr, N - 1), b = b0 + lr;  // B-operand row, A-operand row
+  const int bc = b < P.B ? b : 0;
   // wave w: k-slabs [w nsl / 4, (w + 1) nsl / 4) of the nsl = d / SLAB
   const int nsl = P.d / SLAB, k_lo = wave * nsl / 4 * SLAB, k_hi = (wave + 1) * nsl / 4 * SLAB;
-  const T* wrow = reinterpret_cast<const T*>(Br.Wp) + (size_t)n * P.d + k_lo + PER * lg;
-  const float* xrow = Br.xp + (size_t)(b < P.B ? b : 0) * P.d + k_lo + PER * lg;
-  f32x4 acc = dec_rows_times_cols<T>(xrow, b < P.B, wrow, k_hi - k_lo, zero4());
+  const T* wrow = reinterpret_cast<const T*>(logits ? P.Wz : Br.Wp) + (size_t)n * P.d + k_lo + PER * lg;
+  const T* trow = reinterpret_cast<const T*>(P.x) + (size_t)bc * P.d + k_lo + PER * lg;
+  f32x4 acc;
+  if (logits) {
+    acc = dec_rows_times_cols<T, false, true>(nullptr, trow, 1.f, b < P.B, wrow, k_hi - k_lo, zero4());
+  } else {
+    // the completed block: (pending sum + x_t) / s
+    const float* frow = Br.psum + (size_t)bc * P.d + k_lo + PER * lg;
+    acc = dec_rows_times_cols<T, true, true>(frow, trow, 1.0f / (float)Br.s, b < P.B, wrow, k_hi - k_lo,
+                                             zero4());
+  }
   acc = dec_reduce4(acc, red, wave, lane);
   if (wave != 0) return;
   // acc[e]: sequence b0 + 4 lg + e, column n0 + lr
+  float* dst = logits ? P.w : Br.proj;
+  const int ld = logits ? FUSION_STRIDE : N;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int bb = b0 + 4 * lg + e;
-    if (bb < P.B && n0 + lr < Br.N) Br.proj[(size_t)bb * Br.N + n0 + lr] = acc[e];
+    if (bb < P.B && n0 + lr < N) dst[(size_t)bb * ld + n0 + lr] = acc[e];
   }
 }
 
@@ -186,12 +172,22 @@ __global__ __launch_bounds__(DEC_THREADS) void k_dec_state(const DecParams P) {
   float acc = 0.f;
   if (v < P.dv) {
     const float vv = pr[Br.col_v + hh * P.dv + v];
-    float* S = Br.S + (size_t)bh * P.dk * P.dv;
-    const int cq = (P.dk + 3) / 4;
-    for (int c = wave * cq; c < min(P.dk, (wave + 1) * cq); ++c) {
-      const float s = fmaf(alpha[c], S[(size_t)c * P.dv + v], kk[c] * vv);
-      S[(size_t)c * P.dv + v] = s;
-      acc = fmaf(qq[c], s, acc);
+    float* S = Br.S + (size_t)bh * P.dk * P.dv + v;
+    const int cq = (P.dk + 3) / 4, c1 = min(P.dk, (wave + 1) * cq);
+    // rows of S 16 at a time, all 16 loads in flight before the updates
+    for (int c0 = wave * cq; c0 < c1; c0 += 16) {
+      float sv[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) sv[u] = c0 + u < c1 ? S[(size_t)(c0 + u) * P.dv] : 0.f;
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const int c = c0 + u;
+        if (c < c1) {
+          const float sn = fmaf(alpha[c], sv[u], kk[c] * vv);
+          S[(size_t)c * P.dv] = sn;
+          acc = fmaf(qq[c], sn, acc);
+        }
+      }
     }
   }
   part[wave * 64 + lane] = acc;
@@ -203,7 +199,10 @@ __global__ __launch_bounds__(DEC_THREADS) void k_dec_state(const DecParams P) {
 // grid (d / 16, ceil(B / 16)): output columns 16 x .. 16 x + 15 for sequences
 // 16 y .. 16 y + 15.  Wave w takes branches w, w + 4, ...: a completing branch
 // replaces its held output by y W_o (MFMA over K = h d_v), the others keep
-// theirs; the waves' weighted sums meet in LDS and out = sum_i w_i held_i.
+// theirs; the waves' weighted sums meet in LDS and out = sum_i w_i held_i, with
+// w the softmax of the logits + b_f (Eq. (10)).  The block then moves its 16 x
+// 16 entries of every branch's pending sum on (reset after a completed block,
+// else + x_t), after the projection kernel has read them.
 template <typename T>
 __global__ __launch_bounds__(DEC_THREADS) void k_dec_out(const DecParams P) {
   __shared__ __attribute__((aligned(16))) float red[3 * 64 * 4];
@@ -215,6 +214,18 @@ __global__ __launch_bounds__(DEC_THREADS) void k_dec_out(const DecParams P) {
     reinterpret_cast<StateHeader*>(P.state)->pos = pos + 1;
   constexpr int PER = per16<T>();
   const int n = n0 + lr;  // d is a multiple of 64
+  // fusion weights of this lane's four sequences: the softmax's maximum and sum
+  float zmax[4], zsum[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int bb = min(b0 + 4 * lg + e, P.B - 1);
+    zmax[e] = -INFINITY;
+    zsum[e] = 0.f;
+    if (P.m > 1) {
+      for (int i = 0; i < P.m; ++i) zmax[e] = fmaxf(zmax[e], P.w[(size_t)bb * FUSION_STRIDE + i] + P.bf[i]);
+      for (int i = 0; i < P.m; ++i) zsum[e] += __expf(P.w[(size_t)bb * FUSION_STRIDE + i] + P.bf[i] - zmax[e]);
+    }
+  }
   f32x4 o = zero4();
   for (int i = wave; i < P.nbranch; i += 4) {
     const DecBranch& Br = P.br[i];
@@ -223,7 +234,7 @@ __global__ __launch_bounds__(DEC_THREADS) void k_dec_out(const DecParams P) {
       const int K = Br.h * P.dv, b = b0 + lr;
       const T* wrow = reinterpret_cast<const T*>(P.WoT) + (size_t)n * P.Ktot + Br.ko + PER * lg;
       const float* yrow = Br.y + (size_t)(b < P.B ? b : 0) * K + PER * lg;
-      const f32x4 acc = dec_rows_times_cols<T>(yrow, b < P.B, wrow, K, zero4());
+      const f32x4 acc = dec_rows_times_cols<T, true, false>(yrow, nullptr, 1.f, b < P.B, wrow, K, zero4());
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         held[e] = acc[e];
@@ -239,35 +250,46 @@ __global__ __launch_bounds__(DEC_THREADS) void k_dec_out(const DecParams P) {
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int bb = b0 + 4 * lg + e;
-      o[e] += (P.m > 1 && bb < P.B ? P.w[(size_t)bb * FUSION_STRIDE + i] : 1.f) * held[e];
+      const int bb = min(b0 + 4 * lg + e, P.B - 1);
+      const float wi = P.m > 1 ? __expf(P.w[(size_t)bb * FUSION_STRIDE + i] + P.bf[i] - zmax[e]) / zsum[e]
+                               : 1.f;
+      o[e] += wi * held[e];
     }
   }
   o = dec_reduce4(o, red, wave, lane);
-  if (wave != 0) return;
-  T* out = reinterpret_cast<T*>(P.out);
+  if (wave == 0) {
+    T* out = reinterpret_cast<T*>(P.out);
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int bb = b0 + 4 * lg + e;
-    if (bb < P.B) out[(size_t)bb * P.d + n] = from_f32<T>(o[e]);
+    for (int e = 0; e < 4; ++e) {
+      const int bb = b0 + 4 * lg + e;
+      if (bb < P.B) out[(size_t)bb * P.d + n] = from_f32<T>(o[e]);
+    }
+  }
+  // pending sums of this block's entries (the projection kernel has read them)
+  {
+    const int bb = b0 + (threadIdx.x >> 4), nn = n0 + (threadIdx.x & 15);
+    if (bb < P.B) {
+      const float xv = to_f32(reinterpret_cast<const T*>(P.x)[(size_t)bb * P.d + nn]);
+      for (int i = 0; i < P.nbranch; ++i) {
+        float* ps = P.br[i].psum + (size_t)bb * P.d + nn;
+        *ps = completes(pos, P.br[i].s) ? 0.f : *ps + xv;
+      }
+    }
   }
 }
 
 hipError_t launch_decode(const DecParams& P, int Nmax, int hmax, bool bf16_path, hipStream_t st) {
   const dim3 blk(DEC_THREADS);
-  const dim3 g0((P.d + DEC_THREADS - 1) / DEC_THREADS, P.B, P.nbranch + 1);
   const int btiles = (P.B + 15) / 16;
-  const dim3 g1((Nmax + 15) / 16, P.nbranch, btiles);
+  const int ncols = Nmax > P.m ? Nmax : P.m;
+  const dim3 g1((ncols + 15) / 16, P.nbranch + 1, btiles);
   const dim3 g2(P.B * hmax, (P.dv + 63) / 64, P.nbranch);
   const dim3 g3(P.d / 16, btiles);
   const size_t lds2 = (size_t)(3 * P.dk + 4 * 64) * sizeof(float);
-  if (bf16_path) {
-    hipLaunchKernelGGL(k_dec_pool<bf16>, g0, blk, 0, st, P);
+  if (bf16_path)
     hipLaunchKernelGGL(k_dec_proj<bf16>, g1, blk, 0, st, P);
-  } else {
-    hipLaunchKernelGGL(k_dec_pool<float>, g0, blk, 0, st, P);
+  else
     hipLaunchKernelGGL(k_dec_proj<float>, g1, blk, 0, st, P);
-  }
   hipLaunchKernelGGL(k_dec_state, g2, blk, lds2, st, P);
   if (bf16_path)
     hipLaunchKernelGGL(k_dec_out<bf16>, g3, blk, 0, st, P);

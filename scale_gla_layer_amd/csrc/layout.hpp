@@ -209,7 +209,6 @@ struct DecBranch {
   float* S;         // state [B][h][dk][dv]
   float* psum;      // [B][d]
   float* held;      // [B][d]
-  float* xp;        // workspace [B][d]: pooled block of this step
   float* proj;      // workspace [B][N]
   float* y;         // workspace [B][h dv]
 };
@@ -221,7 +220,7 @@ struct DecParams {
   void* out;        // [B][d]
   void* state;      // header (pos)
   int64_t* pos_ws;  // workspace copy of pos for this step
-  float* w;         // fusion weights [B][8]
+  float* w;         // fusion logits x_t W_f [B][8] of this step (projection kernel)
   const void* Wz;   // fusion-logit weights W_f^T [m][d] (inside a branch's Wp or separate)
   const float* bf;
   const void* WoT;
