@@ -124,6 +124,61 @@ def algorithmic(cfg, B, L):
     }
 
 
+def decode_algorithmic_bytes(cfg, B):
+    """Average HBM bytes of one decode step: a branch of scale s completes a
+    block on one step in s, and then reads its projection weights (q, k, v
+    and the gate's first factor), the gate's second factor, W_o, and reads and
+    writes its fp32 state; every step every branch reads and writes its fp32
+    pending sum and reads or writes its fp32 held output; x_t, out_t and the
+    fusion weights are read or written once."""
+    es = 2 if cfg.dtype == "bf16" else 4
+    d, dk, dv, r = cfg.d_model, cfg.d_k, cfg.d_v, cfg.gate_rank
+    m = len(cfg.scales)
+    total = 2.0 * B * d * es + (d * m * es if m > 1 else 0)
+    for s, h in zip(cfg.scales, cfg.heads):
+        block = (es * d * (h * (2 * dk + dv) + r) + 4 * (r * h * dk + h * dk) + es * h * dv * d
+                 + 2.0 * 4 * B * h * dk * dv)
+        total += block / s + 3.0 * 4 * B * d
+    return total
+
+
+def measure_decode(workload="sweep_1248", steps=256, warmup=32):
+    """Streaming decode: prefill the workload's sequences, then time `steps`
+    back-to-back msgla_decode_step calls (HIP events around the loop)."""
+    import time
+    import torch
+    from scale_gla_layer_amd.config import WORKLOADS
+    from scale_gla_layer_amd.runner import DeviceLayer, to_device
+    from scale_gla_layer_amd.synth import make_inputs
+    wl = WORKLOADS[workload]
+    B, L0 = wl.batch, wl.seq_len
+    X, W = make_inputs(wl.cfg, B, L0 + warmup + steps, seed=0)
+    layer = DeviceLayer(wl.cfg, W)
+    st = layer.new_state(B)
+    layer.forward(to_device(X[:, :L0], wl.cfg.dtype), state_out=st)
+    xs = [to_device(np.ascontiguousarray(X[:, t]), wl.cfg.dtype) for t in range(L0, L0 + warmup + steps)]
+    out = layer.decode_step(xs[0], st)
+    for t in range(1, warmup):
+        layer.decode_step(xs[t], st, out_t=out)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    h0 = time.perf_counter()
+    for t in range(warmup, warmup + steps):
+        layer.decode_step(xs[t], st, out_t=out)
+    h1 = time.perf_counter()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / steps
+    alg = decode_algorithmic_bytes(wl.cfg, B)
+    return {"workload": workload, "batch": B, "prefill": L0, "steps": steps,
+            "us_per_step": round(us, 2), "tokens_per_s": round(B / (us * 1e-6), 1),
+            "host_us_per_call": round((h1 - h0) * 1e6 / steps, 2),
+            "algorithmic_mb_per_step": round(alg / 1e6, 2),
+            "achieved_gb_s": round(alg / (us * 1e-6) / 1e9, 1),
+            "peak_gb_s": 8000.0, "frac": round(alg / (us * 1e-6) / 8e12, 4)}
+
+
 def time_forward(layer, x, steps, warmup, per_kernel=True):
     """Mean ms per forward over `steps` back-to-back forwards (no events inside
     the forwards), then, if per_kernel, mean ms per kernel from a second pass
@@ -222,14 +277,14 @@ def cpu_baseline(cfg, X, W, min_s=10.0, max_s=30.0):
 
 PROFILE_COMMANDS = {
     "ktrace": "rocprofv3 --kernel-trace --stats -f csv -d {d}/ktrace -o main -- "
-              "python3 bench.py --steps 20 --warmup 5 --no-cpu-baseline --no-gla --no-per-call",
+              "python3 bench.py --steps 20 --warmup 5 --no-cpu-baseline --no-gla --no-per-call --no-decode",
     "fetch": "rocprofv3 --pmc FETCH_SIZE -f csv -d {d}/pmc_fetch -o main -- "
-             "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-gla --no-per-call",
+             "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-gla --no-per-call --no-decode",
     "write": "rocprofv3 --pmc WRITE_SIZE -f csv -d {d}/pmc_write -o main -- "
-             "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-gla --no-per-call",
+             "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-gla --no-per-call --no-decode",
     "util": "rocprofv3 --pmc MfmaUtil VALUBusy LdsUtil LDSBankConflict MfmaFlopsBF16 MfmaFlopsF32 "
             "-f csv -d {d}/pmc_util -o main -- "
-            "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-gla --no-per-call",
+            "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-gla --no-per-call --no-decode",
     "cal_fetch": "rocprofv3 --pmc FETCH_SIZE -f csv -d {d}/cal_fetch -o copy -- "
                  "python3 bench.py --copy-calibration",
     "cal_write": "rocprofv3 --pmc WRITE_SIZE -f csv -d {d}/cal_write -o copy -- "
@@ -377,6 +432,7 @@ def main():
     ap.add_argument("--workload", default="main")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-gla", action="store_true", help="skip the single-scale GLA comparison")
+    ap.add_argument("--no-decode", action="store_true", help="skip the streaming decode timing")
     ap.add_argument("--no-per-call", action="store_true",
                     help="skip the per-call (warm and cold-MALL) distributions")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -455,6 +511,13 @@ def main():
             f"ratio {ratio_vs_gla:.3f}")
         del glayer, xg
 
+    dec = None
+    if not args.no_decode:
+        dec = measure_decode()
+        log(f"[bench] decode {dec['workload']} B={dec['batch']}: {dec['us_per_step']} us/step, "
+            f"{dec['achieved_gb_s']} GB/s ({dec['algorithmic_mb_per_step']} MB/step), host "
+            f"{dec['host_us_per_call']} us/call")
+
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] timing the fp64 CPU oracle on the host ...")
@@ -488,6 +551,7 @@ def main():
         "per_call_cold_mall_us": cold,
         "ratio_vs_gla": None if ratio_vs_gla is None else round(ratio_vs_gla, 4),
         "gla_tokens_per_s": None if gla is None else round(gla, 1),
+        "decode": dec,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
