@@ -185,13 +185,15 @@ def fusion_weights(X: np.ndarray, W_f: np.ndarray, b_f: np.ndarray) -> np.ndarra
 # --------------------------------------------------------------------------
 
 
-def branch_forward(X: np.ndarray, bw, s: int, cfg):
+def branch_forward(X: np.ndarray, bw, s: int, cfg, M: Optional[np.ndarray] = None):
     """One branch: pool -> project -> recurrence -> output projection.
 
+    M: optional [B, L] validity mask of Eq. (8); the branch then pools each
+    complete block as the mask-weighted mean with the max(1, sum M) floor.
     Returns (Y [B, n_s, d], final state S [B, h, d_k, d_v], n_s).
     """
     B, L, d = X.shape
-    xp = pool_complete_blocks(X, s)
+    xp = pool_complete_blocks(X, s) if M is None else pool_eq8(X, s, M)[:, : L // s]
     n = xp.shape[1]
     q, k, v, la = branch_projections(xp, bw, cfg)
     o, S = gla_recurrence(q, k, v, la)
@@ -199,21 +201,30 @@ def branch_forward(X: np.ndarray, bw, s: int, cfg):
     return Y, S, n
 
 
-def layer_forward(X: np.ndarray, W, cfg, return_state: bool = False):
+def layer_forward(X: np.ndarray, W, cfg, return_state: bool = False, M: Optional[np.ndarray] = None):
     """MS-GLA layer forward from a fresh state (Sec. 3, Eqs. (8)-(11)).
 
     X: [B, L, d] float64 (the values the device sees, upcast).  Returns O
     [B, L, d]; with ``return_state`` also the streaming cache after the call
     (see ``decode_step``).
+    M: optional [B, L] token mask of Eq. (8) (nonzero = token).  It enters the
+    pooling only, as the equation is written: every branch pools its complete
+    blocks as mask-weighted means (for s = 1 that is M_t x_t), while the
+    fusion weights still come from the unpooled x_t.  The streaming cache is
+    not defined for a masked call (its pending block keeps no token count).
     """
     X = np.asarray(X, dtype=np.float64)
     B, L, d = X.shape
+    if M is not None:
+        if return_state:
+            raise NotImplementedError("the streaming cache of a masked call is not defined")
+        M = (np.asarray(M) != 0).astype(np.float64).reshape(B, L)
     m = len(cfg.scales)
     w = np.ones((B, L, 1)) if m == 1 else fusion_weights(X, W.W_f, W.b_f)
     O = np.zeros((B, L, d))
     state = {"pos": L, "branches": []}
     for i, (s, bw) in enumerate(zip(cfg.scales, W.branches)):
-        Y, S, n = branch_forward(X, bw, s, cfg)
+        Y, S, n = branch_forward(X, bw, s, cfg, M)
         O += w[:, :, i: i + 1] * causal_hold(Y, s, L)
         if return_state:
             tail = X[:, n * s: L, :]

@@ -16,6 +16,9 @@ in the oracle:
   whole layer   a hand-derived scalar example, causality, decode == forward,
                 edge cases ({2,4} at t=0, L < s), state budget and update
                 ratio (golden), the half-life remark of Sec. 3.3
+  masked layer  Eq. (8) with M against unmasked forwards of edited inputs
+                (all-ones mask, s = 1 zeroed rows, whole and half blocks),
+                causality in the mask, an all-zero mask
 """
 import math
 
@@ -364,3 +367,100 @@ def test_half_life_remark():
         half = next(t for t in range(first, L) if r[t] <= 0.5 * r[first])
         predicted = s * math.log(0.5) / math.log(a)
         assert abs((half - first) - predicted) <= s, (s, half, predicted)
+
+
+# --------------------------------------------------------------------------- masked layer
+
+
+def _mask(rng, B, L, p=0.3):
+    return (rng.random((B, L)) >= p).astype(np.uint8)
+
+
+def test_mask_of_ones_is_the_unmasked_layer():
+    cfg = _tiny()
+    X, W = make_inputs(cfg, 2, 40, seed=6)
+    O = orc.layer_forward(X, W, cfg)
+    Om = orc.layer_forward(X, W, cfg, M=np.ones((2, 40), np.uint8))
+    assert np.allclose(Om, O, rtol=1e-12, atol=1e-14)
+
+
+def test_mask_at_scale_one_zeroes_input_rows():
+    """Eq. (8) at s = 1 pools M_t x_t / max(1, M_t) = M_t x_t; with one branch the
+    fusion weight is 1, so the masked layer is the unmasked layer of X * M."""
+    cfg = MsglaConfig((1,), (2,), 8, 4, 6, 2, 16, 16.0, 1.0, F32)
+    X, W = make_inputs(cfg, 2, 23, seed=7)
+    M = _mask(np.random.default_rng(7), 2, 23)
+    ref = orc.layer_forward(X * M[:, :, None], W, cfg)
+    assert np.allclose(orc.layer_forward(X, W, cfg, M=M), ref, rtol=1e-12, atol=1e-14)
+
+
+def test_mask_denominator_counts_tokens_not_scale():
+    """A single s = 2 branch: a block with one valid token pools that token
+    itself (not half of it), so it equals the unmasked layer whose padded token
+    is overwritten by the valid one; an all-padding block pools to zero."""
+    cfg = MsglaConfig((2,), (1,), 8, 4, 6, 2, 16, 16.0, 1.0, F32)
+    L = 20
+    X, W = make_inputs(cfg, 1, L, seed=8)
+    M = np.ones((1, L), np.uint8)
+    X2 = X.copy()
+    M[0, 5] = 0          # block 2: only position 4 valid
+    X2[0, 5] = X[0, 4]
+    M[0, 8] = 0          # block 4: only position 9 valid
+    X2[0, 8] = X[0, 9]
+    M[0, 12:14] = 0      # block 6: no valid token -> zero input
+    X2[0, 12:14] = 0.0
+    assert np.allclose(orc.layer_forward(X, W, cfg, M=M), orc.layer_forward(X2, W, cfg),
+                       rtol=1e-12, atol=1e-14)
+
+
+def test_mask_is_causal():
+    cfg = _tiny()
+    L = 48
+    X, W = make_inputs(cfg, 1, L, seed=9)
+    rng = np.random.default_rng(9)
+    M = _mask(rng, 1, L)
+    O = orc.layer_forward(X, W, cfg, M=M)
+    for t0 in (0, 7, 30):
+        M2 = M.copy()
+        M2[:, t0 + 1:] = 1 - M2[:, t0 + 1:]
+        O2 = orc.layer_forward(X, W, cfg, M=M2)
+        assert np.array_equal(O[:, : t0 + 1], O2[:, : t0 + 1])
+        assert not np.allclose(O[:, t0 + 1:], O2[:, t0 + 1:])
+
+
+def test_all_padding_gives_zero_output():
+    """Every pooled input is zero, so q = k = v = 0 and every branch output is 0."""
+    cfg = _tiny()
+    X, W = make_inputs(cfg, 2, 33, seed=10)
+    assert np.array_equal(orc.layer_forward(X, W, cfg, M=np.zeros((2, 33), np.uint8)),
+                          np.zeros((2, 33, cfg.d_model)))
+
+
+def test_masked_cache_is_not_defined():
+    cfg = _tiny()
+    X, W = make_inputs(cfg, 1, 8, seed=11)
+    with pytest.raises(NotImplementedError):
+        orc.layer_forward(X, W, cfg, return_state=True, M=np.ones((1, 8)))
+
+
+def test_masked_fusion_weights_come_from_unpooled_x():
+    """Two branches {1, 2}: each branch equals its unmasked forward on an input
+    edited to pool the same way (s = 1: X * M; s = 2: a padded token replaced
+    by its block's valid token, all-padding blocks zeroed), and the fusion
+    weights are those of the original, unmasked X."""
+    cfg = MsglaConfig((1, 2), (1, 1), 8, 4, 6, 2, 16, 16.0, 1.0, F32)
+    L = 18
+    X, W = make_inputs(cfg, 1, L, seed=12)
+    M = np.ones((1, L), np.uint8)
+    M[0, [3, 6, 7, 10, 15]] = 0
+    X1 = X * M[:, :, None]
+    X2 = X.copy()
+    X2[0, 3] = X[0, 2]
+    X2[0, 6:8] = 0.0
+    X2[0, 10] = X[0, 11]
+    X2[0, 15] = X[0, 14]
+    w = orc.fusion_weights(X, W.W_f, W.b_f)
+    Y1, _, _ = orc.branch_forward(X1, W.branches[0], 1, cfg)
+    Y2, _, _ = orc.branch_forward(X2, W.branches[1], 2, cfg)
+    ref = w[:, :, 0:1] * orc.causal_hold(Y1, 1, L) + w[:, :, 1:2] * orc.causal_hold(Y2, 2, L)
+    assert np.allclose(orc.layer_forward(X, W, cfg, M=M), ref, rtol=1e-12, atol=1e-14)
