@@ -179,6 +179,32 @@ def measure_decode(workload="sweep_1248", steps=256, warmup=32):
             "peak_gb_s": 8000.0, "frac": round(alg / (us * 1e-6) / 8e12, 4)}
 
 
+def measure_masked(layer, x, steps, warmup, unmasked_ms):
+    """The same workload with a padded-batch token mask (Eq. (8)): each
+    sequence keeps a prefix of random length (at least half) with 5% holes.
+    Mean ms per forward over `steps` back-to-back masked forwards; every
+    position is still computed, `tokens_per_s` counts the unmasked ones."""
+    import torch
+    from scale_gla_layer_amd.synth import make_mask
+    B, L, _ = x.shape
+    M = make_mask(B, L, seed=2, hole_prob=0.05)
+    m = torch.from_numpy(M).to(x.device)
+    out = layer.new_output(B, L)
+    for _ in range(warmup):
+        layer.forward(x, out=out, mask=m)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        layer.forward(x, out=out, mask=m)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) / steps * 1e3
+    return {"mask": "padded batch: random prefix lengths >= L/2, 5% holes (seed 2)",
+            "token_fraction": round(float(M.mean()), 4), "us_per_step": round(ms * 1e3, 2),
+            "positions_per_s": round(B * L / (ms * 1e-3), 1),
+            "tokens_per_s": round(float(M.sum()) / (ms * 1e-3), 1),
+            "vs_unmasked": round(unmasked_ms / ms, 4)}
+
+
 def time_forward(layer, x, steps, warmup, per_kernel=True):
     """Mean ms per forward over `steps` back-to-back forwards (no events inside
     the forwards), then, if per_kernel, mean ms per kernel from a second pass
@@ -277,14 +303,14 @@ def cpu_baseline(cfg, X, W, min_s=10.0, max_s=30.0):
 
 PROFILE_COMMANDS = {
     "ktrace": "rocprofv3 --kernel-trace --stats -f csv -d {d}/ktrace -o main -- "
-              "python3 bench.py --steps 20 --warmup 5 --no-cpu-baseline --no-gla --no-per-call --no-decode",
+              "python3 bench.py --steps 20 --warmup 5 --no-cpu-baseline --no-gla --no-per-call --no-decode --no-mask",
     "fetch": "rocprofv3 --pmc FETCH_SIZE -f csv -d {d}/pmc_fetch -o main -- "
-             "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-gla --no-per-call --no-decode",
+             "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-gla --no-per-call --no-decode --no-mask",
     "write": "rocprofv3 --pmc WRITE_SIZE -f csv -d {d}/pmc_write -o main -- "
-             "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-gla --no-per-call --no-decode",
+             "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-gla --no-per-call --no-decode --no-mask",
     "util": "rocprofv3 --pmc MfmaUtil VALUBusy LdsUtil LDSBankConflict MfmaFlopsBF16 MfmaFlopsF32 "
             "-f csv -d {d}/pmc_util -o main -- "
-            "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-gla --no-per-call --no-decode",
+            "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-gla --no-per-call --no-decode --no-mask",
     "cal_fetch": "rocprofv3 --pmc FETCH_SIZE -f csv -d {d}/cal_fetch -o copy -- "
                  "python3 bench.py --copy-calibration",
     "cal_write": "rocprofv3 --pmc WRITE_SIZE -f csv -d {d}/cal_write -o copy -- "
@@ -433,6 +459,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-gla", action="store_true", help="skip the single-scale GLA comparison")
     ap.add_argument("--no-decode", action="store_true", help="skip the streaming decode timing")
+    ap.add_argument("--no-mask", action="store_true", help="skip the masked-forward timing")
     ap.add_argument("--no-per-call", action="store_true",
                     help="skip the per-call (warm and cold-MALL) distributions")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -497,6 +524,12 @@ def main():
                 "traffic": traffic_from_profile(d["kernel"], wl.name),
                 "algorithmic_per_launch": d["algorithmic"]}
 
+    masked = None
+    if not args.no_mask:
+        masked = measure_masked(layer, x, args.steps, args.warmup, ms)
+        log(f"[bench] masked forward {masked['us_per_step']} us/step ({masked['vs_unmasked']:.3f} of the "
+            f"unmasked rate), {masked['token_fraction']:.3f} of the positions are tokens")
+
     ratio_vs_gla = None
     gla = None
     if not args.no_gla and args.workload != "gla_baseline":
@@ -552,6 +585,7 @@ def main():
         "ratio_vs_gla": None if ratio_vs_gla is None else round(ratio_vs_gla, 4),
         "gla_tokens_per_s": None if gla is None else round(gla, 1),
         "decode": dec,
+        "masked": masked,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -153,8 +153,14 @@ msgla_status msgla_state_init(const msgla_config* cfg, int64_t B, void* state, s
 /*
  * Layer forward over a batch of B sequences of L tokens from an empty state.
  *   x [B][L][d] (dtype) -> out [B][L][d] (dtype).
- *   mask: must be NULL (masked pooling, Eq. (8) with M, is not implemented:
- *         MSGLA_ERR_UNSUPPORTED).
+ *   mask: NULL (every position is a token), or a device array [B][L] of
+ *         bytes, nonzero for a token and 0 for padding.  It enters the pooling
+ *         only (Eq. (8)): every branch pools each complete block as
+ *         sum M x / max(1, sum M), so at scale 1 a padded position is a zero
+ *         input (the recurrence still decays its state there) and a block
+ *         without tokens pools to zero; the fusion weights still come from the
+ *         unpooled x_t.  A masked call has no streaming state: mask together
+ *         with state_in or state_out gives MSGLA_ERR_UNSUPPORTED.
  *   state_in: NULL (start from an empty state), or a state of the same
  *         config and B (written by msgla_forward's state_out,
  *         msgla_state_init or msgla_decode_step) to continue from: its GLA

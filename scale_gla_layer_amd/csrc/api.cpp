@@ -335,7 +335,8 @@ msgla_status msgla_forward_timed(const msgla_config* cfg, const void* packed, co
   if (!aligned16(packed) || !aligned16(x) || !aligned16(out) || !aligned16(workspace) ||
       (state_out && !aligned16(state_out)) || (state_in && !aligned16(state_in)))
     return MSGLA_ERR_INVALID_ARG;
-  if (mask) return MSGLA_ERR_UNSUPPORTED;
+  // a masked call defines no streaming state (its pending block keeps no token count)
+  if (mask && (state_in || state_out)) return MSGLA_ERR_UNSUPPORTED;
   const PackGeom g = pack_geom(cfg);
   const WsGeom W = ws_geom(g, B, L);
   if (workspace_bytes < W.total) return MSGLA_ERR_WORKSPACE;
@@ -365,6 +366,7 @@ msgla_status msgla_forward_timed(const msgla_config* cfg, const void* packed, co
   // ---------------- K1 ----------------
   K1Params p1{};
   p1.B = (int)B;
+  p1.mask = mask;
   p1.d = g.d;
   p1.dk = g.dk;
   p1.dv = g.dv;
@@ -442,6 +444,7 @@ msgla_status msgla_forward_timed(const msgla_config* cfg, const void* packed, co
   p2.C = g.C;
   p2.inv_gamma = 1.0f / cfg->gate_normalizer;
   p2.q_scale = cfg->q_scale;
+  p2.mask = mask;
   p2.nbranch = g.m;
   int units = 0;
   for (int i = 0; i < g.m; ++i) {
@@ -547,6 +550,7 @@ msgla_status msgla_forward_timed(const msgla_config* cfg, const void* packed, co
       PoolParams& q = pp[npass++];
       q = PoolParams{};
       q.x = x;
+      q.mask = mask;
       q.B = (int)B;
       q.L = (int)L;
       q.d = g.d;

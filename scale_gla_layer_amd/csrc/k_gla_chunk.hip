@@ -156,26 +156,44 @@ __global__ __launch_bounds__(256) void k2a_gla_chunk(const K2Params P) {
   {
     // x W_g1 is given per unpooled position: the block's mean is this row's value
     const float* gr = Bb.g + ((size_t)b * P.L + (size_t)(row0 + pl) * Bb.s) * RP + lg;
+    if (P.mask) {
+      // Eq. (8) with a token mask: the block's mean over its tokens,
+      // sum M x W_g1 / max(1, sum M) (for s = 1: M_t x_t W_g1)
+      const uint8_t* mr = P.mask + (size_t)b * P.L + (size_t)(row0 + pl) * Bb.s;
+      float den = 0.f;
 #pragma unroll
-    for (int k4 = 0; k4 < RP / 4; ++k4) gb[k4] = gr[4 * k4];
-    if (Bb.s > 1) {
-      // three rows per round trip (dead slots reload the last row and are dropped)
-      for (int u0 = 1; u0 < Bb.s; u0 += 3) {
-        float t[3][RP / 4];
+      for (int k4 = 0; k4 < RP / 4; ++k4) gb[k4] = 0.f;
+      for (int u = 0; u < Bb.s; ++u) {
+        const float w = mr[u] ? 1.f : 0.f;
+        den += w;
 #pragma unroll
-        for (int j = 0; j < 3; ++j) {
-          const int u = min(u0 + j, Bb.s - 1);
-#pragma unroll
-          for (int k4 = 0; k4 < RP / 4; ++k4) t[j][k4] = gr[(size_t)u * RP + 4 * k4];
-        }
-#pragma unroll
-        for (int j = 0; j < 3; ++j)
-#pragma unroll
-          for (int k4 = 0; k4 < RP / 4; ++k4) gb[k4] += u0 + j < Bb.s ? t[j][k4] : 0.f;
+        for (int k4 = 0; k4 < RP / 4; ++k4) gb[k4] += w * gr[(size_t)u * RP + 4 * k4];
       }
-      const float inv_s = 1.0f / (float)Bb.s;
+      const float sc = 1.0f / fmaxf(1.f, den);
 #pragma unroll
-      for (int k4 = 0; k4 < RP / 4; ++k4) gb[k4] *= inv_s;
+      for (int k4 = 0; k4 < RP / 4; ++k4) gb[k4] *= sc;
+    } else {
+#pragma unroll
+      for (int k4 = 0; k4 < RP / 4; ++k4) gb[k4] = gr[4 * k4];
+      if (Bb.s > 1) {
+        // three rows per round trip (dead slots reload the last row and are dropped)
+        for (int u0 = 1; u0 < Bb.s; u0 += 3) {
+          float t[3][RP / 4];
+#pragma unroll
+          for (int j = 0; j < 3; ++j) {
+            const int u = min(u0 + j, Bb.s - 1);
+#pragma unroll
+            for (int k4 = 0; k4 < RP / 4; ++k4) t[j][k4] = gr[(size_t)u * RP + 4 * k4];
+          }
+#pragma unroll
+          for (int j = 0; j < 3; ++j)
+#pragma unroll
+            for (int k4 = 0; k4 < RP / 4; ++k4) gb[k4] += u0 + j < Bb.s ? t[j][k4] : 0.f;
+        }
+        const float inv_s = 1.0f / (float)Bb.s;
+#pragma unroll
+        for (int k4 = 0; k4 < RP / 4; ++k4) gb[k4] *= inv_s;
+      }
     }
 #pragma unroll
     for (int k4 = 0; k4 < RP / 4; ++k4) gb[k4] = live ? gb[k4] : 0.f;

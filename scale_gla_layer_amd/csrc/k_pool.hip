@@ -6,7 +6,8 @@
 // and emits the block means of every such scale (a partial tail block is not
 // pooled: it never reaches the recurrence).  Scales that do not divide s_max
 // take a second pass of their own.  HBM-bound: reads B L d elements per pass,
-// writes sum_s B floor(L/s) d.
+// writes sum_s B floor(L/s) d.  With a token mask M the mean of a block is
+// sum M x / max(1, sum M) (Eq. (8)): a block without tokens pools to zero.
 #include "device_common.hpp"
 #include "layout.hpp"
 
@@ -28,19 +29,25 @@ __global__ __launch_bounds__(256) void k_pool(const PoolParams P) {
   const T* x = reinterpret_cast<const T*>(P.x) + ((size_t)b * P.L + (size_t)q * P.smax) * P.d +
                piece * PER;
   const int rows = min(P.smax, P.L - q * P.smax);
-  float acc[MSGLA_MAX_BRANCHES][PER];
+  const uint8_t* mk = P.mask ? P.mask + (size_t)b * P.L + (size_t)q * P.smax : nullptr;
+  float acc[MSGLA_MAX_BRANCHES][PER], den[MSGLA_MAX_BRANCHES];
   int cnt[MSGLA_MAX_BRANCHES], jout[MSGLA_MAX_BRANCHES];
 #pragma unroll
   for (int i = 0; i < MSGLA_MAX_BRANCHES; ++i) {
     cnt[i] = 0;
+    den[i] = 0.f;
     jout[i] = i < P.nout ? q * (P.smax / P.out[i].s) : 0;  // s divides smax
 #pragma unroll
     for (int e = 0; e < PER; ++e) acc[i][e] = 0.f;
   }
   for (int u0 = 0; u0 < rows; u0 += U) {
     u32x4 raw[U];
+    float wt[U];
 #pragma unroll
-    for (int k = 0; k < U; ++k) raw[k] = (u0 + k < rows) ? ld16(x + (size_t)(u0 + k) * P.d) : zero16();
+    for (int k = 0; k < U; ++k) {
+      raw[k] = (u0 + k < rows) ? ld16(x + (size_t)(u0 + k) * P.d) : zero16();
+      wt[k] = (mk && u0 + k < rows) ? (mk[u0 + k] ? 1.f : 0.f) : 1.f;
+    }
 #pragma unroll
     for (int k = 0; k < U; ++k) {
       if (u0 + k >= rows) break;
@@ -51,17 +58,20 @@ __global__ __launch_bounds__(256) void k_pool(const PoolParams P) {
         if (i < P.nout) {
           const PoolOut& o = P.out[i];
 #pragma unroll
-          for (int e = 0; e < PER; ++e) acc[i][e] += v[e];
+          for (int e = 0; e < PER; ++e) acc[i][e] += wt[k] * v[e];
+          den[i] += wt[k];
           if (++cnt[i] == o.s) {  // a block of this scale is complete
             if (jout[i] < o.n) {
+              const float sc = mk ? 1.0f / fmaxf(1.f, den[i]) : o.inv_s;
               float m[PER];
 #pragma unroll
-              for (int e = 0; e < PER; ++e) m[e] = acc[i][e] * o.inv_s;
+              for (int e = 0; e < PER; ++e) m[e] = acc[i][e] * sc;
               st16(reinterpret_cast<T*>(o.xp) + ((size_t)b * o.n + jout[i]) * P.d + piece * PER,
                    pack16<T>(m));
             }
             ++jout[i];
             cnt[i] = 0;
+            den[i] = 0.f;
 #pragma unroll
             for (int e = 0; e < PER; ++e) acc[i][e] = 0.f;
           }
@@ -91,6 +101,12 @@ __global__ __launch_bounds__(256) void k_pool_pow2(const PoolParams P) {
   u32x4 raw[S];
 #pragma unroll
   for (int u = 0; u < S; ++u) raw[u] = ld16(x + (size_t)min(u, last) * P.d);
+  // token weights and counts of Eq. (8) with a mask (a tail block's missing
+  // rows re-read the last row; the blocks they would join are not emitted)
+  const uint8_t* mk = P.mask ? P.mask + (size_t)b * P.L + (size_t)q * S : nullptr;
+  float c[S];
+#pragma unroll
+  for (int u = 0; u < S; ++u) c[u] = mk ? (mk[min(u, last)] ? 1.f : 0.f) : 1.f;
   // every load is issued before the first one is used (the scheduler would
   // otherwise start unpacking between them and wait on the early ones)
 #pragma unroll
@@ -98,12 +114,20 @@ __global__ __launch_bounds__(256) void k_pool_pow2(const PoolParams P) {
   float v[S][PER];
 #pragma unroll
   for (int u = 0; u < S; ++u) unpack16<T>(raw[u], v[u]);
+  if (mk) {
+#pragma unroll
+    for (int u = 0; u < S; ++u)
+#pragma unroll
+      for (int e = 0; e < PER; ++e) v[u][e] *= c[u];
+  }
 #pragma unroll
   for (int l = 1; l <= LS; ++l) {
 #pragma unroll
-    for (int j = 0; j < (S >> l); ++j)
+    for (int j = 0; j < (S >> l); ++j) {
 #pragma unroll
       for (int e = 0; e < PER; ++e) v[j][e] = v[2 * j][e] + v[2 * j + 1][e];
+      c[j] = c[2 * j] + c[2 * j + 1];
+    }
     const int i = P.lvl[l];
     if (i >= 0) {
       const PoolOut& o = P.out[i];
@@ -112,9 +136,10 @@ __global__ __launch_bounds__(256) void k_pool_pow2(const PoolParams P) {
       for (int j = 0; j < (S >> l); ++j) {
         const int jo = q * (S >> l) + j;
         if (jo < o.n) {
+          const float sc = mk ? 1.0f / fmaxf(1.f, c[j]) : o.inv_s;
           float m[PER];
 #pragma unroll
-          for (int e = 0; e < PER; ++e) m[e] = v[j][e] * o.inv_s;
+          for (int e = 0; e < PER; ++e) m[e] = v[j][e] * sc;
           st16(dst + ((size_t)b * o.n + jo) * P.d, pack16<T>(m));
         }
       }

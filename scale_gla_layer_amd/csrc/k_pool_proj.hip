@@ -28,7 +28,8 @@ namespace msgla {
 using K1Cfg = GemmCfg<2, 4, 4, 2, 128, 2>;  // 128 x 128 tiles, 8 waves (32 x 64 each), double-buffered 128-byte K segments
 constexpr int K1_BM = K1Cfg::BM, K1_BN = K1Cfg::BN;
 
-template <typename T>
+// MASKED: a token mask is given (rows of masked positions of the scale-1 group are zeroed)
+template <typename T, bool MASKED>
 struct K1Prob {
   const K1Params& P;
   const K1Group& G;
@@ -41,6 +42,14 @@ struct K1Prob {
       : P(p), G(g), m0(m0_), n0(n0_), small(small_) {}
 
   __device__ int nk() const { return P.d * (int)sizeof(T) / K1Cfg::KSEG; }
+  // 0 for row m of the scale-1 group at a masked position (its pooled input
+  // M_t x_t of Eq. (8) is zero, so are q, k and v), else 1
+  __device__ float keep(int m) const {
+    if constexpr (!MASKED)
+      return 1.f;
+    else
+      return (!small && G.s == 1) ? (P.mask[m] ? 1.f : 0.f) : 1.f;
+  }
   __device__ void setup(int wave, int lane) {
     const size_t row_bytes = (size_t)P.d * sizeof(T);
 #pragma unroll
@@ -114,8 +123,9 @@ struct K1Prob {
           ++b;
         }
         const size_t roff = ((size_t)b * G.h * G.np + j) * P.dk;
+        const float kp = keep(ma + r);
 #pragma unroll
-        for (int bb = 0; bb < K1Cfg::WN; ++bb) dstc[bb][roff] = acc[a][bb][i];
+        for (int bb = 0; bb < K1Cfg::WN; ++bb) dstc[bb][roff] = kp * acc[a][bb][i];
       }
     }
   }
@@ -143,10 +153,12 @@ struct K1Prob {
       const int b = m / G.n, j = m - b * G.n;
       const int chunk = j / P.C, tau = j - chunk * P.C;
       const size_t roff = (((size_t)b * G.h * G.nch + chunk) * P.dv) * P.C + tau;
+      const float kp[4] = {keep(m), keep(m + 1), keep(m + 2), keep(m + 3)};
 #pragma unroll
       for (int bb = 0; bb < K1Cfg::WN; ++bb) {
         if (!cok[bb]) continue;
-        const float f[4] = {acc[a][bb][0], acc[a][bb][1], acc[a][bb][2], acc[a][bb][3]};
+        const float f[4] = {kp[0] * acc[a][bb][0], kp[1] * acc[a][bb][1], kp[2] * acc[a][bb][2],
+                            kp[3] * acc[a][bb][3]};
         T* dst = vT + roff + cbase[bb];
         if constexpr (sizeof(T) == 2)
           st8(dst, pack8<T>(f));
@@ -210,9 +222,10 @@ struct K1Prob {
       const int m = m0 + r, col = n0 + cg * 8;
       if (m >= G.M || col >= G.col_v) continue;  // v: transposed pass below
       const int b = m / G.n, j = m - b * G.n;
+      const float kp = keep(m);
       float v[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = C[r * ldc + cg * 8 + e];
+      for (int e = 0; e < 8; ++e) v[e] = kp * C[r * ldc + cg * 8 + e];
       const bool isq = col < G.col_k;
       const int c = isq ? col : col - G.col_k;
       const int hh = c / P.dk, ch = c - hh * P.dk;
@@ -235,7 +248,7 @@ struct K1Prob {
         if (mA + 7 < G.M && j0 + 7 < G.n && (j0 & 7) == 0) {
           float v[8];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) v[e] = C[(rg * 8 + e) * ldc + cl];
+          for (int e = 0; e < 8; ++e) v[e] = keep(mA + e) * C[(rg * 8 + e) * ldc + cl];
           const int chunk = j0 / P.C, tau = j0 - chunk * P.C;
           store8(vT + ((((size_t)b0 * G.h + hh) * G.nch + chunk) * P.dv + vch) * P.C + tau, v);
         } else {
@@ -245,7 +258,7 @@ struct K1Prob {
             const int b = m / G.n, j = m - b * G.n;
             const int chunk = j / P.C, tau = j - chunk * P.C;
             vT[((((size_t)b * G.h + hh) * G.nch + chunk) * P.dv + vch) * P.C + tau] =
-                from_f32<T>(C[(rg * 8 + e) * ldc + cl]);
+                from_f32<T>(keep(m) * C[(rg * 8 + e) * ldc + cl]);
           }
         }
       }
@@ -253,7 +266,7 @@ struct K1Prob {
   }
 };
 
-template <typename T>
+template <typename T, bool MASKED>
 __global__ __launch_bounds__(K1Cfg::THREADS) void k1_pool_proj(const K1Params P) {
   __shared__ __attribute__((aligned(16))) char lds[K1Cfg::LDS_STAGED];
   const int tile = remap_xcd(blockIdx.x, P.per_xcd);
@@ -263,16 +276,16 @@ __global__ __launch_bounds__(K1Cfg::THREADS) void k1_pool_proj(const K1Params P)
   const K1Group& G = P.g[gi];
   const int local = tile - G.tile_begin;
   const int tm = local / G.tiles_n, tn = local - tm * G.tiles_n;
-  K1Prob<T> prob(P, G, tm * K1_BM, tn * K1_BN, gi == P.sm.group);
+  K1Prob<T, MASKED> prob(P, G, tm * K1_BM, tn * K1_BN, gi == P.sm.group);
   gemm_dma_tile<T, K1Cfg>(prob, G.N - tn * K1_BN, lds);
 }
 
 hipError_t launch_k1(const K1Params& P, bool bf16_path, hipStream_t stream) {
   const dim3 grid(P.per_xcd * N_XCD), block(K1Cfg::THREADS);
   if (bf16_path)
-    hipLaunchKernelGGL(k1_pool_proj<bf16>, grid, block, 0, stream, P);
+    hipLaunchKernelGGL((P.mask ? k1_pool_proj<bf16, true> : k1_pool_proj<bf16, false>), grid, block, 0, stream, P);
   else
-    hipLaunchKernelGGL(k1_pool_proj<float>, grid, block, 0, stream, P);
+    hipLaunchKernelGGL((P.mask ? k1_pool_proj<float, true> : k1_pool_proj<float, false>), grid, block, 0, stream, P);
   return hipGetLastError();
 }
 

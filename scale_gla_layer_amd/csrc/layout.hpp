@@ -66,6 +66,7 @@ struct PoolOut {
 
 struct PoolParams {
   const void* x;    // [B][L][d]
+  const uint8_t* mask;  // [B][L] token mask of Eq. (8) (nonzero = token), or null
   int B, L, d, smax, nout;
   PoolOut out[MSGLA_MAX_BRANCHES];
   int lvl[8];       // power-of-two smax: out index of scale 2^l, or -1 (set by the launcher)
@@ -111,6 +112,7 @@ struct K1Small {
 
 struct K1Params {
   int B, d, dk, dv, C;
+  const uint8_t* mask;  // [B][L] token mask, or null: rows of masked positions of the scale-1 group are zero
   int ngroups, total_tiles, per_xcd;
   K1Group g[MSGLA_MAX_BRANCHES + 1];
   K1Small sm;
@@ -141,6 +143,7 @@ struct K2Params {
   int B, L, dk, dv, r, rp, C;
   float inv_gamma;
   float q_scale;
+  const uint8_t* mask;  // [B][L] token mask: the gate factor is averaged over a block's tokens, or null
   int nbranch;
   int total_units;  // K2a grid
   int total_seqs;   // K2b: number of (branch, b, head) sequences

@@ -87,13 +87,13 @@ class DeviceLayer:
     def new_state(self, B: int):
         return empty_bytes(binding.msgla_state_bytes(self.cfg, B), self.device)
 
-    def forward(self, x, out=None, state_out=None, events=None, state_in=None):
+    def forward(self, x, out=None, state_out=None, events=None, state_in=None, mask=None):
         B, L, _ = x.shape
         ws = self.ensure_workspace(B, L)
         if out is None:
             out = self.new_output(B, L)
         binding.msgla_forward(self.cfg, self.packed, x, B, L, out, ws, state_out=state_out,
-                              state_in=state_in, stream=self.stream, events=events)
+                              state_in=state_in, mask=mask, stream=self.stream, events=events)
         return out
 
     def state_init(self, state, B: int):

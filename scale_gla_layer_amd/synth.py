@@ -114,6 +114,21 @@ def make_tokens(cfg: MsglaConfig, batch: int, n: int, seed: int) -> np.ndarray:
     return round_to(rng.normal(0.0, 1.0, (batch, n, cfg.d_model)), cfg.dtype)
 
 
+def make_mask(batch: int, seq_len: int, seed: int, min_keep: float = 0.5,
+              hole_prob: float = 0.05, hole_start: int = 0) -> np.ndarray:
+    """Token mask [B, L] uint8 of a padded batch: sequence b keeps its first
+    len_b tokens, len_b uniform in [ceil(min_keep L), L], and each kept token
+    from position hole_start on is also dropped with probability hole_prob;
+    1 = token, 0 = padding."""
+    rng = np.random.default_rng(seed)
+    lo = int(np.ceil(min_keep * seq_len))
+    lens = rng.integers(lo, seq_len + 1, size=batch)
+    keep = np.arange(seq_len)[None, :] < lens[:, None]
+    holes = rng.random((batch, seq_len)) < hole_prob
+    holes[:, :hole_start] = False
+    return (keep & ~holes).astype(np.uint8)
+
+
 def storage_array(a: np.ndarray, dtype: str) -> np.ndarray:
     """Host buffer in the storage type: uint16 bf16 bits or float32."""
     if dtype == BF16:

@@ -17,21 +17,26 @@ def say(msg: str):
     sys.stdout.flush()
 
 
-def run_device(cfg: MsglaConfig, X: np.ndarray, W, state_out=False):
+def mask_to_device(M: np.ndarray):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(M, dtype=np.uint8)).to("cuda")
+
+
+def run_device(cfg: MsglaConfig, X: np.ndarray, W, state_out=False, M=None):
     import torch
     layer = DeviceLayer(cfg, W)
     x = to_device(X, cfg.dtype)
     st = layer.new_state(X.shape[0]) if state_out else None
-    out = layer.forward(x, state_out=st)
+    out = layer.forward(x, state_out=st, mask=None if M is None else mask_to_device(M))
     torch.cuda.synchronize()
     return layer, x, out, st
 
 
-def check_against_oracle(cfg, X, W, O_dev: np.ndarray, batches=None, tol=None):
+def check_against_oracle(cfg, X, W, O_dev: np.ndarray, batches=None, tol=None, M=None):
     """Row-normalised max error vs the oracle on the sampled sequences."""
     tol = TOL[cfg.dtype] if tol is None else tol
     idx = list(range(X.shape[0])) if batches is None else list(batches)
-    ref = orc.layer_forward(X[idx], W, cfg)
+    ref = orc.layer_forward(X[idx], W, cfg, M=None if M is None else M[idx])
     err, zeros_exact = orc.row_relative_error(O_dev[idx], ref)
     assert np.all(np.isfinite(O_dev[idx])), "non-finite output"
     assert zeros_exact, "rows the oracle gives as exactly zero are not zero on the device"

@@ -139,8 +139,9 @@ def test_forward_argument_errors_need_no_gpu():
     # bad sizes
     assert f(ctypes.byref(cc), fake, fake, None, 0, 64, fake, None, None, fake, ws, None) == 1
     assert f(ctypes.byref(cc), fake, fake, None, 2, 0, fake, None, None, fake, ws, None) == 1
-    # masked pooling is not implemented
-    assert f(ctypes.byref(cc), fake, fake, fake, 2, 64, fake, None, None, fake, ws, None) == 2
+    # a masked call has no streaming state
+    assert f(ctypes.byref(cc), fake, fake, fake, 2, 64, fake, None, fake, fake, ws, None) == 2
+    assert f(ctypes.byref(cc), fake, fake, fake, 2, 64, fake, fake, None, fake, ws, None) == 2
     # misaligned state_in (a valid one is read on the device: GPU tests)
     assert f(ctypes.byref(cc), fake, fake, None, 2, 64, fake, fake + 8, None, fake, ws, None) == 1
     # workspace too small
