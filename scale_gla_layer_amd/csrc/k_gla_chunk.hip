@@ -17,8 +17,9 @@
 //   A     = [sum_c q_tc k_ic e^{b_tc - b_ic}]_{t >= i}   (zero above the diagonal)
 // b is kept in base-2 units (log2 alpha), so every decay factor is one exp2.
 // q and k arrive in fp32 (a single q_t . k_i can cancel strongly, and A scales
-// whole output rows); A is formed with fp32 MFMA and rounded once to the
-// storage type.
+// whole output rows); A is formed from the fp32 operands (fp32 MFMA, or for
+// bf16 storage three bf16 MFMA products of their hi/lo split) and rounded once
+// to the storage type.
 // Every exponent used is <= 0 except one bounded by 15 positions of decay:
 // the 16 x 16 block A[T][J] (query tile T, key tile J <= T) is built as
 // (q_t e^{b_t - b_16T}) . (k_i e^{b_16J - b_i} D_TJ) with D_TJ = e^{b_16T - b_16J};
@@ -325,27 +326,63 @@ __global__ __launch_bounds__(256) void k2a_gla_chunk(const K2Params P) {
   }
   lds_barrier();  // key side in LDS; the qt, kT stores drain meanwhile
 
-  // ---- A[w][J] for J <= w (zero blocks above the diagonal), fp32 MFMA ----
+  // ---- A[w][J] for J <= w (zero blocks above the diagonal) ----
+  // fp32 storage: fp32 MFMA.  bf16 storage: each fp32 operand is split into
+  // bf16 hi + lo and the product taken as hi.hi + hi.lo + lo.hi with bf16
+  // MFMA over 32 channels at a time (two channel tiles per packet, the same
+  // channel order on both sides); the dropped lo.lo term is below 2^-16 of
+  // each product.
   {
     T* Ag = reinterpret_cast<T*>(Bb.A) + (((size_t)bh * Bb.nch + chunk) * C + p) * C + 4 * lg;
+    constexpr int NP = G::BF ? NT / 2 : 1;  // channel-tile pairs
+    u32x4 qh[NP], ql[NP];
+    if constexpr (G::BF) {
+#pragma unroll
+      for (int rp = 0; rp < NP; ++rp) {
+        const float f[8] = {qv[2 * rp][0], qv[2 * rp][1], qv[2 * rp][2], qv[2 * rp][3],
+                            qv[2 * rp + 1][0], qv[2 * rp + 1][1], qv[2 * rp + 1][2], qv[2 * rp + 1][3]};
+        split_bf16(f, qh[rp], ql[rp]);
+      }
+    }
 #pragma unroll
     for (int J = 0; J < NW; ++J) {
       float out[4] = {0.f, 0.f, 0.f, 0.f};
       if (J <= w) {
         const char* krow = ks + (16 * J + lr) * G::KROW + 16 * lg;
         f32x4 acc = zero4();
+        if constexpr (G::BF) {
 #pragma unroll
-        for (int rt = 0; rt < NT; ++rt) {
-          u32x4 kf = ld16(krow + 64 * rt);
-          if (J < w) {  // key side re-referenced to this wave's first position
-            float k4[4], d4[4];
-            unpack16<float>(kf, k4);
-            unpack16<float>(ld16(Dw + J * DK + 16 * rt + 4 * lg), d4);
+          for (int rp = 0; rp < NP; ++rp) {
+            float k8[8];
+            unpack16<float>(ld16(krow + 64 * (2 * rp)), k8);
+            unpack16<float>(ld16(krow + 64 * (2 * rp + 1)), k8 + 4);
+            if (J < w) {  // key side re-referenced to this wave's first position
+              float d8[8];
+              unpack16<float>(ld16(Dw + J * DK + 16 * (2 * rp) + 4 * lg), d8);
+              unpack16<float>(ld16(Dw + J * DK + 16 * (2 * rp + 1) + 4 * lg), d8 + 4);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) k4[i] *= d4[i];
-            kf = pack16<float>(k4);
+              for (int i = 0; i < 8; ++i) k8[i] *= d8[i];
+            }
+            u32x4 kh, kl;
+            split_bf16(k8, kh, kl);
+            acc = mma_slab<bf16>(kh, qh[rp], acc);
+            acc = mma_slab<bf16>(kh, ql[rp], acc);
+            acc = mma_slab<bf16>(kl, qh[rp], acc);
           }
-          acc = mma_slab<float>(kf, pack16<float>(qv[rt]), acc);
+        } else {
+#pragma unroll
+          for (int rt = 0; rt < NT; ++rt) {
+            u32x4 kf = ld16(krow + 64 * rt);
+            if (J < w) {  // key side re-referenced to this wave's first position
+              float k4[4], d4[4];
+              unpack16<float>(kf, k4);
+              unpack16<float>(ld16(Dw + J * DK + 16 * rt + 4 * lg), d4);
+#pragma unroll
+              for (int i = 0; i < 4; ++i) k4[i] *= d4[i];
+              kf = pack16<float>(k4);
+            }
+            acc = mma_slab<float>(kf, pack16<float>(qv[rt]), acc);
+          }
         }
         // acc[e] = A[16 w + lr][16 J + 4 lg + e]; causal mask on the diagonal block
 #pragma unroll
