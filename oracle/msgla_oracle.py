@@ -180,6 +180,29 @@ def fusion_weights(X: np.ndarray, W_f: np.ndarray, b_f: np.ndarray) -> np.ndarra
     return softmax_lastdim(X @ W_f + b_f)
 
 
+def routing_stability(w: np.ndarray, frac: float = 0.1) -> np.ndarray:
+    """Sec. 5.4 / Table 3 procedure: mean fusion weight of each branch, in
+    percent, over the first, the middle and the last `frac` of the positions.
+
+    w: [B, L, m] fusion weights.  The first region is positions
+    [0, ceil(frac L)), the last [L - ceil(frac L), L), and the middle the same
+    count starting at floor((L - ceil(frac L)) / 2); each mean runs over the
+    region's positions of every sequence.  Returns [3, m].
+    """
+    w = np.asarray(w, dtype=np.float64)
+    B, L, m = w.shape
+    n = max(1, math.ceil(frac * L))
+    mid = (L - n) // 2
+    out = np.zeros((3, m))
+    for r, start in enumerate((0, mid, L - n)):
+        acc = np.zeros(m)
+        for b in range(B):
+            for t in range(start, start + n):
+                acc += w[b, t]
+        out[r] = 100.0 * acc / (B * n)
+    return out
+
+
 # --------------------------------------------------------------------------
 # The whole layer
 # --------------------------------------------------------------------------

@@ -13,6 +13,8 @@ in the oracle:
                 reshape-mean, pool/project commutation
   hold          the notes' s=4 table (golden), repeat-then-shift construction
   fusion        simplex, uniform at W_f = 0, two-branch closed form
+  routing       region means of weights linear in the position (closed form),
+                regions of a 10-position sequence by hand, percentages sum to 100
   whole layer   a hand-derived scalar example, causality, decode == forward,
                 edge cases ({2,4} at t=0, L < s), state budget and update
                 ratio (golden), the half-life remark of Sec. 3.3
@@ -464,3 +466,40 @@ def test_masked_fusion_weights_come_from_unpooled_x():
     Y2, _, _ = orc.branch_forward(X2, W.branches[1], 2, cfg)
     ref = w[:, :, 0:1] * orc.causal_hold(Y1, 1, L) + w[:, :, 1:2] * orc.causal_hold(Y2, 2, L)
     assert np.allclose(orc.layer_forward(X, W, cfg, M=M), ref, rtol=1e-12, atol=1e-14)
+
+
+# --------------------------------------------------------------------------- routing stability
+
+
+def test_routing_regions_by_hand():
+    """L = 10, 10%: one position per region, at t = 0, 4 ((10 - 1) // 2) and 9."""
+    w = np.zeros((1, 10, 2))
+    w[0, :, 0] = np.arange(10) / 10.0
+    w[0, :, 1] = 1.0 - w[0, :, 0]
+    st = orc.routing_stability(w)
+    assert np.allclose(st[:, 0], [0.0, 40.0, 90.0])
+    assert np.allclose(st.sum(axis=1), 100.0)
+
+
+def test_routing_linear_weights_closed_form():
+    """w_t = (a + c t, 1 - a - c t): a region [s, s + n) has mean a + c (s + (n - 1) / 2)."""
+    B, L, a, c = 3, 2000, 0.2, 1e-4
+    t = np.arange(L)
+    w = np.empty((B, L, 2))
+    w[:, :, 0] = a + c * t
+    w[:, :, 1] = 1.0 - w[:, :, 0]
+    n = 200
+    starts = (0, (L - n) // 2, L - n)
+    expect = [100.0 * (a + c * (s0 + (n - 1) / 2.0)) for s0 in starts]
+    st = orc.routing_stability(w)
+    assert np.allclose(st[:, 0], expect, rtol=1e-12)
+    assert np.allclose(st[:, 1], 100.0 - np.array(expect), rtol=1e-12)
+
+
+def test_routing_of_the_layer_weights_sums_to_100():
+    cfg = _tiny()
+    X, W = make_inputs(cfg, 2, 50, seed=13)
+    st = orc.routing_stability(orc.fusion_weights(X, W.W_f, W.b_f))
+    assert st.shape == (3, 3)
+    assert np.allclose(st.sum(axis=1), 100.0, rtol=1e-12)
+    assert np.all(st > 0)
