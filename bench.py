@@ -205,6 +205,38 @@ def measure_masked(layer, x, steps, warmup, unmasked_ms):
             "vs_unmasked": round(unmasked_ms / ms, 4)}
 
 
+def measure_routing(cfg, W, L=32768, steps=50, warmup=10):
+    """Routing stability (Sec. 5.4, Table 3): the fusion weights of one
+    L-token sequence from msgla_fusion_weights, timed over `steps` calls, and
+    their mean per branch, in percent, over the first, middle and last tenth
+    of the positions (n = ceil(L/10); middle window from floor((L - n)/2)).
+    The weights are synthetic, so the percentages are not the printed ones."""
+    import math
+    import torch
+    from scale_gla_layer_amd.runner import DeviceLayer, to_device
+    from scale_gla_layer_amd.synth import make_tokens
+    layer = DeviceLayer(cfg, W)
+    x = to_device(make_tokens(cfg, 1, L, seed=4), cfg.dtype)
+    w = layer.fusion_weights(x)
+    for _ in range(warmup):
+        layer.fusion_weights(x, w_out=w)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        layer.fusion_weights(x, w_out=w)
+    torch.cuda.synchronize()
+    us = (time.perf_counter() - t0) / steps * 1e6
+    m = len(cfg.scales)
+    wh = w[0, :, :m].double().cpu().numpy()
+    n = math.ceil(L / 10)
+    regions = {name: [round(float(v), 3) for v in 100.0 * wh[s0:s0 + n].mean(axis=0)]
+               for name, s0 in (("first", 0), ("middle", (L - n) // 2), ("last", L - n))}
+    nbytes = L * cfg.d_model * (2 if cfg.dtype == "bf16" else 4) + L * 8 * 4
+    return {"seq_len": L, "us_per_call": round(us, 2), "positions_per_s": round(L / (us * 1e-6), 1),
+            "hbm_gb_s": round(nbytes / (us * 1e-6) / 1e9, 1), "peak_gb_s": 8000.0,
+            "percent_by_region": regions}
+
+
 def time_forward(layer, x, steps, warmup, per_kernel=True):
     """Mean ms per forward over `steps` back-to-back forwards (no events inside
     the forwards), then, if per_kernel, mean ms per kernel from a second pass
@@ -303,14 +335,14 @@ def cpu_baseline(cfg, X, W, min_s=10.0, max_s=30.0):
 
 PROFILE_COMMANDS = {
     "ktrace": "rocprofv3 --kernel-trace --stats -f csv -d {d}/ktrace -o main -- "
-              "python3 bench.py --steps 20 --warmup 5 --no-cpu-baseline --no-gla --no-per-call --no-decode --no-mask",
+              "python3 bench.py --steps 20 --warmup 5 --no-cpu-baseline --no-gla --no-per-call --no-decode --no-mask --no-routing",
     "fetch": "rocprofv3 --pmc FETCH_SIZE -f csv -d {d}/pmc_fetch -o main -- "
-             "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-gla --no-per-call --no-decode --no-mask",
+             "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-gla --no-per-call --no-decode --no-mask --no-routing",
     "write": "rocprofv3 --pmc WRITE_SIZE -f csv -d {d}/pmc_write -o main -- "
-             "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-gla --no-per-call --no-decode --no-mask",
+             "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-gla --no-per-call --no-decode --no-mask --no-routing",
     "util": "rocprofv3 --pmc MfmaUtil VALUBusy LdsUtil LDSBankConflict MfmaFlopsBF16 MfmaFlopsF32 "
             "-f csv -d {d}/pmc_util -o main -- "
-            "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-gla --no-per-call --no-decode --no-mask",
+            "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-gla --no-per-call --no-decode --no-mask --no-routing",
     "cal_fetch": "rocprofv3 --pmc FETCH_SIZE -f csv -d {d}/cal_fetch -o copy -- "
                  "python3 bench.py --copy-calibration",
     "cal_write": "rocprofv3 --pmc WRITE_SIZE -f csv -d {d}/cal_write -o copy -- "
@@ -460,6 +492,7 @@ def main():
     ap.add_argument("--no-gla", action="store_true", help="skip the single-scale GLA comparison")
     ap.add_argument("--no-decode", action="store_true", help="skip the streaming decode timing")
     ap.add_argument("--no-mask", action="store_true", help="skip the masked-forward timing")
+    ap.add_argument("--no-routing", action="store_true", help="skip the routing-stability timing")
     ap.add_argument("--no-per-call", action="store_true",
                     help="skip the per-call (warm and cold-MALL) distributions")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -530,6 +563,13 @@ def main():
         log(f"[bench] masked forward {masked['us_per_step']} us/step ({masked['vs_unmasked']:.3f} of the "
             f"unmasked rate), {masked['token_fraction']:.3f} of the positions are tokens")
 
+    routing = None
+    if not args.no_routing and len(cfg.scales) > 1:
+        routing = measure_routing(cfg, W)
+        log(f"[bench] routing: fusion weights of a {routing['seq_len']}-token sequence in "
+            f"{routing['us_per_call']} us ({routing['hbm_gb_s']} GB/s); percent by region "
+            f"{routing['percent_by_region']}")
+
     ratio_vs_gla = None
     gla = None
     if not args.no_gla and args.workload != "gla_baseline":
@@ -586,6 +626,7 @@ def main():
         "gla_tokens_per_s": None if gla is None else round(gla, 1),
         "decode": dec,
         "masked": masked,
+        "routing": routing,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

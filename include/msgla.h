@@ -204,6 +204,19 @@ msgla_status msgla_forward_timed(const msgla_config* cfg, const void* packed, co
                                  size_t workspace_bytes, void* stream,
                                  const msgla_stage_events* events);
 
+/*
+ * Fusion weights alone (Eq. (10)): w_t = softmax(x_t W_f + b_f) for every
+ * position, the quantity whose means over the first, middle and last tenth of
+ * long sequences the notes use to judge routing stability (Sec. 5.4, Table 3).
+ *   x [B][L][d] (dtype) -> w_out [B][L][8] fp32 (device, 16-byte aligned),
+ *   row t holding w_t in its first m = n_branches entries and zeros after.
+ * Same arithmetic as the weights msgla_forward applies.  Needs no workspace.
+ * n_branches must be at least 2 (MSGLA_ERR_INVALID_ARG otherwise: one branch
+ * has weight 1).
+ */
+msgla_status msgla_fusion_weights(const msgla_config* cfg, const void* packed, const void* x,
+                                  int64_t B, int64_t L, float* w_out, void* stream);
+
 /* Device workspace needed by msgla_decode_step for batch B (bytes). */
 size_t msgla_decode_workspace_bytes(const msgla_config* cfg, int64_t B);
 

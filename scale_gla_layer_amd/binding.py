@@ -26,6 +26,7 @@ SYMBOLS = (
     "msgla_status_str", "msgla_validate_config", "msgla_packed_weights_bytes",
     "msgla_pack_weights", "msgla_workspace_bytes", "msgla_state_bytes", "msgla_state_init",
     "msgla_forward", "msgla_forward_timed", "msgla_decode_workspace_bytes", "msgla_decode_step",
+    "msgla_fusion_weights",
 )
 
 
@@ -91,6 +92,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                                ctypes.POINTER(CStageEvents)]),
         "msgla_decode_workspace_bytes": (sz, [cfgp, i64]),
         "msgla_decode_step": (ctypes.c_int, [cfgp, vp, vp, i64, vp, vp, vp, sz, vp]),
+        "msgla_fusion_weights": (ctypes.c_int, [cfgp, vp, vp, i64, i64, vp, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -207,3 +209,9 @@ def msgla_decode_step(cfg: MsglaConfig, packed, x_t, B: int, state, out_t, works
                                           workspace.numel() * workspace.element_size(),
                                           _stream(stream))
     _check("msgla_decode_step", st)
+
+
+def msgla_fusion_weights(cfg: MsglaConfig, packed, x, B: int, L: int, w_out, stream=None):
+    st = load_library().msgla_fusion_weights(ctypes.byref(c_config(cfg)), _ptr(packed), _ptr(x), B, L,
+                                             _ptr(w_out), _stream(stream))
+    _check("msgla_fusion_weights", st)

@@ -400,6 +400,7 @@ msgla_status msgla_forward_timed(const msgla_config* cfg, const void* packed, co
     K1Small& S = p1.sm;
     S.m = g.m;
     S.rp = g.rp;
+    S.gm = g.m;
     int Ns = 0;
     for (int i = 0; i < g.m; ++i) {
       const BranchGeom& b = g.br[i];
@@ -625,6 +626,48 @@ msgla_status msgla_forward(const msgla_config* cfg, const void* packed, const vo
                            size_t workspace_bytes, void* stream) {
   return msgla_forward_timed(cfg, packed, x, mask, B, L, out, state_in, state_out, workspace,
                              workspace_bytes, stream, nullptr);
+}
+
+msgla_status msgla_fusion_weights(const msgla_config* cfg, const void* packed, const void* x,
+                                  int64_t B, int64_t L, float* w_out, void* stream) {
+  if (msgla_status st = check_config(cfg); st != MSGLA_OK) return st;
+  if (!batch_ok(B, L)) return MSGLA_ERR_INVALID_ARG;
+  if (!packed || !x || !w_out || !aligned16(packed) || !aligned16(x) || !aligned16(w_out))
+    return MSGLA_ERR_INVALID_ARG;
+  const PackGeom g = pack_geom(cfg);
+  if (g.m < 2) return MSGLA_ERR_INVALID_ARG;  // one branch has no fusion weights
+  // the projection kernel with its small group alone, holding only the fusion logits
+  K1Params p1{};
+  p1.B = (int)B;
+  p1.d = g.d;
+  p1.dk = g.dk;
+  p1.dv = g.dv;
+  p1.C = g.C;
+  K1Small& S = p1.sm;
+  S.m = g.m;
+  S.rp = g.rp;
+  S.gm = 0;
+  const size_t zoff = g.carrier >= 0
+                          ? g.br[g.carrier].off_Wp + (size_t)g.br[g.carrier].col_z * g.d * g.es
+                          : g.off_Wz;
+  S.seg[S.nseg++] = XSeg{at<char>(packed, zoff), 0, 16};
+  S.zcol = 0;
+  S.bf = at<float>(packed, g.off_bf);
+  S.w = w_out;
+  S.group = 0;
+  K1Group& G = p1.g[0];
+  G.A = x;
+  G.s = 1;
+  G.n = (int)L;
+  G.M = (int)(B * L);
+  G.N = 16;
+  G.tiles_n = 1;
+  G.tile_begin = 0;
+  p1.ngroups = 1;
+  p1.total_tiles = cdiv(G.M, GEMM_TILE);
+  p1.per_xcd = cdiv(p1.total_tiles, N_XCD);
+  HIP_TRY(launch_k1(p1, g.bf16, static_cast<hipStream_t>(stream)));
+  return MSGLA_OK;
 }
 
 msgla_status msgla_decode_step(const msgla_config* cfg, const void* packed, const void* x_t,

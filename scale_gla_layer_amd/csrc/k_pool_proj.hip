@@ -171,7 +171,7 @@ struct K1Prob {
   // gate first factors (fp32 rows of rp) and fusion weights, per unpooled position m
   __device__ void epilogue_small(const float* C, int ldc) {
     const K1Small& S = P.sm;
-    const int gcols = S.m * S.rp;
+    const int gcols = S.gm * S.rp;
     for (int it = threadIdx.x; it < K1_BM * (K1_BN / 8); it += K1Cfg::THREADS) {
       const int r = it / (K1_BN / 8), cg = it % (K1_BN / 8);
       const int m = m0 + r, col = n0 + cg * 8;

@@ -102,6 +102,7 @@ struct K1Group {
 struct K1Small {
   int group;        // index of its group in K1Params::g, -1 if none
   int m, rp;
+  int gm;           // branches whose gate first factors lead the columns (m, or 0 for the weights alone)
   int nseg;
   XSeg seg[MSGLA_MAX_BRANCHES + 1];
   float* g[MSGLA_MAX_BRANCHES];  // per branch [B L][rp] fp32

@@ -99,6 +99,15 @@ class DeviceLayer:
     def state_init(self, state, B: int):
         binding.msgla_state_init(self.cfg, B, state, self.stream)
 
+    def fusion_weights(self, x, w_out=None):
+        """Fusion weights [B, L, 8] fp32 (first n_branches entries) from the library."""
+        torch = _torch()
+        B, L, _ = x.shape
+        if w_out is None:
+            w_out = torch.empty((B, L, 8), dtype=torch.float32, device=self.device)
+        binding.msgla_fusion_weights(self.cfg, self.packed, x, B, L, w_out, self.stream)
+        return w_out
+
     def decode_step(self, x_t, state, out_t=None):
         torch = _torch()
         B = x_t.shape[0]

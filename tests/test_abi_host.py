@@ -151,6 +151,12 @@ def test_forward_argument_errors_need_no_gpu():
     d = lib.msgla_decode_step
     assert d(ctypes.byref(cc), fake, None, 2, fake, fake, fake, dws, None) == 1
     assert d(ctypes.byref(cc), fake, fake, 2, fake, fake, fake, dws - 1, None) == 3
+    # fusion weights: NULL output, one branch
+    fw = lib.msgla_fusion_weights
+    assert fw(ctypes.byref(cc), fake, fake, 2, 64, None, None) == 1
+    one = _raw_cfg()
+    one.n_branches = 1
+    assert fw(ctypes.byref(one), fake, fake, 2, 64, fake, None) == 1
     # packing
     w = binding.CWeights()
     assert lib.msgla_pack_weights(ctypes.byref(cc), ctypes.byref(w), fake,
