@@ -22,7 +22,9 @@ Readings where the notes leave a step open (all listed in the design doc):
     the branch's pooled input;
   * each branch has an output projection W_o [h*d_v, d], no bias; the
     per-branch normalisation the notes name without a form is omitted
-    (identity), as is any output gate; q is not scaled (q_scale = 1);
+    (identity) unless the configuration asks for it (norm), where it is a
+    per-head RMS normalisation over d_v with gains and eps = 1e-6 before W_o;
+    there is no output gate; q is not scaled (q_scale = 1);
   * only complete pooling blocks enter the recurrence; a partial tail block is
     never read by the hold and is kept in the streaming cache instead;
   * positions before a branch's first complete block take zero from that
@@ -208,6 +210,26 @@ def routing_stability(w: np.ndarray, frac: float = 0.1) -> np.ndarray:
 # --------------------------------------------------------------------------
 
 
+# --------------------------------------------------------------------------
+# Sec. 3.2: the per-branch normalisation the notes name (form: a reading)
+# --------------------------------------------------------------------------
+
+NORM_EPS = 1e-6
+
+
+def rms_norm_heads(o: np.ndarray, g: np.ndarray) -> np.ndarray:
+    """Per-head RMS normalisation of a branch's GLA output before W_o.
+
+    o: [..., h, d_v]; g: [h * d_v] gains.  Each head's row is divided by the
+    root of its mean square plus NORM_EPS and multiplied by its gains:
+    o_c / sqrt(mean_c' o_c'^2 + eps) * g_c.
+    """
+    o = np.asarray(o, dtype=np.float64)
+    h, dv = o.shape[-2], o.shape[-1]
+    ms = np.mean(o * o, axis=-1, keepdims=True)
+    return o / np.sqrt(ms + NORM_EPS) * np.asarray(g, dtype=np.float64).reshape(h, dv)
+
+
 def branch_forward(X: np.ndarray, bw, s: int, cfg, M: Optional[np.ndarray] = None):
     """One branch: pool -> project -> recurrence -> output projection.
 
@@ -220,6 +242,8 @@ def branch_forward(X: np.ndarray, bw, s: int, cfg, M: Optional[np.ndarray] = Non
     n = xp.shape[1]
     q, k, v, la = branch_projections(xp, bw, cfg)
     o, S = gla_recurrence(q, k, v, la)
+    if getattr(cfg, "norm", False):
+        o = rms_norm_heads(o, bw.g_norm)
     Y = o.reshape(B, n, o.shape[2] * o.shape[3]) @ bw.W_o
     return Y, S, n
 
@@ -297,6 +321,8 @@ def decode_step(state: Dict, x_t: np.ndarray, W, cfg):
             xp = psum / s
             q, k, v, la = branch_projections(xp[:, None, :], bw, cfg)
             y, S = gla_recurrence(q, k, v, la, S0=S)
+            if getattr(cfg, "norm", False):
+                y = rms_norm_heads(y, bw.g_norm)
             held = y.reshape(B, -1) @ bw.W_o
             psum = np.zeros((B, d))
             count = 0

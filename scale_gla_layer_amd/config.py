@@ -33,6 +33,7 @@ class MsglaConfig:
     gate_normalizer: float = 16.0
     q_scale: float = 1.0
     dtype: str = BF16
+    norm: bool = False  # per-head RMS normalisation of each branch's output before W_o
 
     def __post_init__(self):
         if len(self.scales) != len(self.heads) or not self.scales:

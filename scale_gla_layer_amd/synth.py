@@ -67,6 +67,7 @@ class BranchWeights:
     W_g2: np.ndarray  # [r, h*d_k]
     b_g: np.ndarray   # [h*d_k]  (float32 values)
     W_o: np.ndarray   # [h*d_v, d]
+    g_norm: Optional[np.ndarray] = None  # [h*d_v] (float32 values), configs with norm only
 
 
 @dataclasses.dataclass
@@ -96,6 +97,9 @@ def make_weights(cfg: MsglaConfig, rng: np.random.Generator,
     m = cfg.n_branches
     W_f = rt(rng.normal(0.0, STD, (d, m)))
     b_f = np.zeros(m)
+    if cfg.norm:  # drawn last, so configurations without it keep their streams
+        for br, h in zip(brs, cfg.heads):
+            br.g_norm = round_f32(1.0 + 0.1 * rng.normal(0.0, 1.0, h * dv))
     return LayerWeights(brs, W_f, b_f)
 
 

@@ -13,6 +13,8 @@ in the oracle:
                 reshape-mean, pool/project commutation
   hold          the notes' s=4 table (golden), repeat-then-shift construction
   fusion        simplex, uniform at W_f = 0, two-branch closed form
+  normalisation one-channel heads (sign times gain), invariance of the layer
+                to a positive scale of W_v, decode == forward with it
   routing       region means of weights linear in the position (closed form),
                 regions of a 10-position sequence by hand, percentages sum to 100
   whole layer   a hand-derived scalar example, causality, decode == forward,
@@ -22,6 +24,7 @@ in the oracle:
                 (all-ones mask, s = 1 zeroed rows, whole and half blocks),
                 causality in the mask, an all-zero mask
 """
+import dataclasses
 import math
 
 import numpy as np
@@ -503,3 +506,51 @@ def test_routing_of_the_layer_weights_sums_to_100():
     assert st.shape == (3, 3)
     assert np.allclose(st.sum(axis=1), 100.0, rtol=1e-12)
     assert np.all(st > 0)
+
+
+# --------------------------------------------------------------------------- per-branch normalisation
+
+
+def _norm_cfg(**kw):
+    base = dict(scales=(1, 2), heads=(2, 1), d_model=8, d_k=4, d_v=6, gate_rank=2, chunk=16,
+                dtype=F32, norm=True)
+    base.update(kw)
+    return MsglaConfig(**base)
+
+
+def test_rms_norm_of_one_channel_heads_is_sign_times_gain():
+    """d_v = 1: o / sqrt(o^2 + eps) * g -> sign(o) g for |o| >> sqrt(eps)."""
+    o = np.array([[[3.0], [-0.5]], [[-2e3], [7e-2]]])  # [2, h=2, 1]
+    g = np.array([1.5, -0.25])
+    out = orc.rms_norm_heads(o, g)
+    assert np.allclose(out, np.sign(o) * g.reshape(2, 1), rtol=1e-3)
+
+
+def test_normalised_layer_ignores_the_scale_of_w_v():
+    """y is linear in v, so each head's normalised output, and the layer, do
+    not change when W_v is multiplied by a positive constant (eps aside);
+    without the normalisation the output scales with it."""
+    cfg = _norm_cfg()
+    X, W = make_inputs(cfg, 2, 30, seed=14)
+    for bw in W.branches:  # outputs well above sqrt(eps), so eps plays no part
+        bw.W_q, bw.W_k, bw.W_v = 30.0 * bw.W_q, 30.0 * bw.W_k, 30.0 * bw.W_v
+    O = orc.layer_forward(X, W, cfg)
+    for bw in W.branches:
+        bw.W_v = bw.W_v * 7.0
+    assert np.abs(orc.layer_forward(X, W, cfg) - O).max() <= 1e-5 * np.abs(O).max()
+    plain = dataclasses.replace(cfg, norm=False)
+    O1 = orc.layer_forward(X, W, plain)
+    for bw in W.branches:
+        bw.W_v = bw.W_v / 7.0
+    assert np.allclose(O1, 7.0 * orc.layer_forward(X, W, plain), rtol=1e-10)
+
+
+def test_normalised_decode_equals_forward():
+    cfg = _norm_cfg()
+    L = 21
+    X, W = make_inputs(cfg, 2, L, seed=15)
+    O = orc.layer_forward(X, W, cfg)
+    O0, st = orc.layer_forward(X[:, :8], W, cfg, return_state=True)
+    for t in range(8, L):
+        o, st = orc.decode_step(st, X[:, t], W, cfg)
+        assert np.allclose(o, O[:, t], rtol=1e-11, atol=1e-13), t
