@@ -205,6 +205,33 @@ def measure_masked(layer, x, steps, warmup, unmasked_ms):
             "vs_unmasked": round(unmasked_ms / ms, 4)}
 
 
+def measure_norm(cfg, B, L, steps, warmup, plain_ms):
+    """The same workload with the optional per-head RMS normalisation of each
+    branch's output: mean ms per forward, and the normalisation pass's time
+    taken as the difference to the plain forward, against the bytes it moves
+    (each branch's y read and written once, plus the gains)."""
+    import dataclasses
+    from scale_gla_layer_amd.runner import DeviceLayer, to_device
+    ncfg = dataclasses.replace(cfg, norm=True)
+    X, W = make_inputs_for(ncfg, B, L)
+    layer = DeviceLayer(ncfg, W)
+    x = to_device(X, ncfg.dtype)
+    ms, _ = time_forward(layer, x, steps, warmup, per_kernel=False)
+    es = 2 if cfg.dtype == "bf16" else 4
+    y_bytes = sum(B * h * (L // s) * cfg.d_v * es for s, h in zip(cfg.scales, cfg.heads))
+    nbytes = 2 * y_bytes + sum(h * cfg.d_v * 4 for h in cfg.heads)
+    extra_us = (ms - plain_ms) * 1e3
+    return {"us_per_step": round(ms * 1e3, 2), "vs_plain": round(plain_ms / ms, 4),
+            "norm_pass_us_est": round(extra_us, 2), "algorithmic_mb": round(nbytes / 1e6, 2),
+            "est_gb_s": round(nbytes / (extra_us * 1e-6) / 1e9, 1) if extra_us > 0 else None,
+            "peak_gb_s": 8000.0}
+
+
+def make_inputs_for(cfg, B, L):
+    from scale_gla_layer_amd.synth import make_inputs
+    return make_inputs(cfg, B, L, seed=0)
+
+
 def measure_routing(cfg, W, L=32768, steps=50, warmup=10):
     """Routing stability (Sec. 5.4, Table 3): the fusion weights of one
     L-token sequence from msgla_fusion_weights, timed over `steps` calls, and
@@ -335,14 +362,14 @@ def cpu_baseline(cfg, X, W, min_s=10.0, max_s=30.0):
 
 PROFILE_COMMANDS = {
     "ktrace": "rocprofv3 --kernel-trace --stats -f csv -d {d}/ktrace -o main -- "
-              "python3 bench.py --steps 20 --warmup 5 --no-cpu-baseline --no-gla --no-per-call --no-decode --no-mask --no-routing",
+              "python3 bench.py --steps 20 --warmup 5 --no-cpu-baseline --no-gla --no-per-call --no-decode --no-mask --no-routing --no-norm",
     "fetch": "rocprofv3 --pmc FETCH_SIZE -f csv -d {d}/pmc_fetch -o main -- "
-             "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-gla --no-per-call --no-decode --no-mask --no-routing",
+             "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-gla --no-per-call --no-decode --no-mask --no-routing --no-norm",
     "write": "rocprofv3 --pmc WRITE_SIZE -f csv -d {d}/pmc_write -o main -- "
-             "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-gla --no-per-call --no-decode --no-mask --no-routing",
+             "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-gla --no-per-call --no-decode --no-mask --no-routing --no-norm",
     "util": "rocprofv3 --pmc MfmaUtil VALUBusy LdsUtil LDSBankConflict MfmaFlopsBF16 MfmaFlopsF32 "
             "-f csv -d {d}/pmc_util -o main -- "
-            "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-gla --no-per-call --no-decode --no-mask --no-routing",
+            "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-gla --no-per-call --no-decode --no-mask --no-routing --no-norm",
     "cal_fetch": "rocprofv3 --pmc FETCH_SIZE -f csv -d {d}/cal_fetch -o copy -- "
                  "python3 bench.py --copy-calibration",
     "cal_write": "rocprofv3 --pmc WRITE_SIZE -f csv -d {d}/cal_write -o copy -- "
@@ -493,6 +520,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true", help="skip the streaming decode timing")
     ap.add_argument("--no-mask", action="store_true", help="skip the masked-forward timing")
     ap.add_argument("--no-routing", action="store_true", help="skip the routing-stability timing")
+    ap.add_argument("--no-norm", action="store_true", help="skip the normalised-forward timing")
     ap.add_argument("--no-per-call", action="store_true",
                     help="skip the per-call (warm and cold-MALL) distributions")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -563,6 +591,12 @@ def main():
         log(f"[bench] masked forward {masked['us_per_step']} us/step ({masked['vs_unmasked']:.3f} of the "
             f"unmasked rate), {masked['token_fraction']:.3f} of the positions are tokens")
 
+    normed = None
+    if not args.no_norm:
+        normed = measure_norm(cfg, B, L, args.steps, args.warmup, ms)
+        log(f"[bench] normalised forward {normed['us_per_step']} us/step; normalisation pass about "
+            f"{normed['norm_pass_us_est']} us for {normed['algorithmic_mb']} MB")
+
     routing = None
     if not args.no_routing and len(cfg.scales) > 1:
         routing = measure_routing(cfg, W)
@@ -627,6 +661,7 @@ def main():
         "decode": dec,
         "masked": masked,
         "routing": routing,
+        "norm": normed,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

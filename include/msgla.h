@@ -59,6 +59,11 @@ typedef enum { MSGLA_F32 = 0, MSGLA_BF16 = 1 } msgla_dtype;
  * chunk: length of the GPU chunk schedule; the result does not depend on it
  * beyond rounding (Sec. 3.4 separates it from the pooling block).
  * q_scale multiplies q (1.0 reproduces the notes' recurrence).
+ * norm: the notes name a per-branch normalisation without giving its form.
+ * 0 leaves it out (identity); 1 applies, before the branch's W_o (in the
+ * forward and in the streaming step), a per-head RMS normalisation over d_v
+ * with gains: y_c / sqrt(mean_c' y_c'^2 + 1e-6) * norm_g[head d_v + c].
+ * Other values are invalid.
  * Requirements (MSGLA_ERR_INVALID_ARG otherwise): 1 <= n_branches <= 8; scales
  * positive and distinct; 1 <= heads <= 64; d_model a multiple of 64 up to
  * 65536; 1 <= gate_rank <= 64; gate_normalizer > 0; and, by storage type,
@@ -82,6 +87,7 @@ typedef struct {
   float gate_normalizer;
   float q_scale;
   int32_t dtype; /* msgla_dtype */
+  int32_t norm;  /* 0: none; 1: per-head RMS normalisation of each branch's output (below) */
 } msgla_config;
 
 /*
@@ -100,6 +106,7 @@ typedef struct {
   const void* W_g2;
   const float* b_g;
   const void* W_o;
+  const float* norm_g; /* [h d_v] fp32 gains of the normalisation (config norm = 1), else unused */
 } msgla_branch_weights;
 
 /* All weights.  W_f [d][m] (config dtype) and b_f [m] (fp32) give the fusion

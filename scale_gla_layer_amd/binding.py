@@ -49,11 +49,13 @@ class CConfig(ctypes.Structure):
         ("gate_normalizer", ctypes.c_float),
         ("q_scale", ctypes.c_float),
         ("dtype", ctypes.c_int32),
+        ("norm", ctypes.c_int32),
     ]
 
 
 class CBranchWeights(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_void_p) for n in ("W_q", "W_k", "W_v", "W_g1", "W_g2", "b_g", "W_o")]
+    _fields_ = [(n, ctypes.c_void_p) for n in ("W_q", "W_k", "W_v", "W_g1", "W_g2", "b_g", "W_o",
+                                               "norm_g")]
 
 
 class CWeights(ctypes.Structure):
@@ -125,6 +127,7 @@ def _build_config(cfg: MsglaConfig) -> CConfig:
     c.gate_rank, c.chunk = cfg.gate_rank, cfg.chunk
     c.gate_normalizer, c.q_scale = cfg.gate_normalizer, cfg.q_scale
     c.dtype = 1 if cfg.dtype == BF16 else 0
+    c.norm = 1 if cfg.norm else 0
     return c
 
 
@@ -165,11 +168,12 @@ def msgla_decode_workspace_bytes(cfg: MsglaConfig, B: int) -> int:
 
 
 def msgla_pack_weights(cfg: MsglaConfig, branches: Sequence[dict], W_f, b_f, packed, stream=None):
-    """branches: per branch a dict of device tensors W_q, W_k, W_v, W_g1, W_g2, b_g, W_o."""
+    """branches: per branch a dict of device tensors W_q, W_k, W_v, W_g1, W_g2, b_g, W_o
+    and, for configurations with the normalisation, norm_g."""
     w = CWeights()
     for i, br in enumerate(branches):
-        for name in ("W_q", "W_k", "W_v", "W_g1", "W_g2", "b_g", "W_o"):
-            setattr(w.br[i], name, _ptr(br[name]))
+        for name in ("W_q", "W_k", "W_v", "W_g1", "W_g2", "b_g", "W_o", "norm_g"):
+            setattr(w.br[i], name, _ptr(br.get(name)))
     w.W_f, w.b_f = _ptr(W_f), _ptr(b_f)
     st = load_library().msgla_pack_weights(ctypes.byref(c_config(cfg)), ctypes.byref(w),
                                            _ptr(packed), packed.numel() * packed.element_size(),

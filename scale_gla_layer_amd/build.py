@@ -30,6 +30,7 @@ SOURCES = [
     "k_state.hip",
     "k_decode.hip",
     "k_pack.hip",
+    "k_norm.hip",
 ]
 
 FLAGS = [

@@ -21,6 +21,7 @@ hipError_t launch_k3f(const K3Params& P, bool bf16_path, hipStream_t stream);
 hipError_t launch_state_export(const StateParams& P, bool bf16_path, hipStream_t st);
 hipError_t launch_state_header(void* state, int B, int m, int64_t pos, hipStream_t st);
 hipError_t launch_decode(const DecParams& P, int Nmax, int hmax, bool bf16_path, hipStream_t st);
+hipError_t launch_norm(const NormParams& P, bool bf16_path, hipStream_t st);
 hipError_t pack_transpose(bool bf16_path, const void* src, int R, int Cn, void* dst,
                           size_t dst_ld, hipStream_t st);
 hipError_t pack_to_f32(bool src_bf16, const void* src, size_t n, float* dst, hipStream_t st);
@@ -44,10 +45,11 @@ struct BranchGeom {
   int col_k, col_v, col_g, col_z, N;  // projection columns
   int ko, kp;                         // stacked W_o^T K range
   size_t off_Wp, off_W2, off_bg;      // packed offsets
+  size_t off_gn;                      // normalisation gains [h dv] fp32 (config norm)
 };
 
 struct PackGeom {
-  bool bf16;
+  bool bf16, norm;
   int es, m, d, dk, dv, r, rp, C, Ktot, carrier;
   size_t off_Wz;  // 0 if none (fusion carried by a branch or m == 1)
   bool has_Wz;
@@ -75,6 +77,7 @@ msgla_status check_config(const msgla_config* c) {
          : (c->chunk != 16 && c->chunk != 32 && c->chunk != 64))
     return MSGLA_ERR_INVALID_ARG;
   if (!(c->gate_normalizer > 0.f) || !(c->q_scale == c->q_scale)) return MSGLA_ERR_INVALID_ARG;
+  if (c->norm != 0 && c->norm != 1) return MSGLA_ERR_INVALID_ARG;
   // the state kernel keeps three (or two) chunks of A, qt, kT and V in LDS:
   // shapes whose stages do not fit the CU's 160 KB are not implemented
   const int lds = k2b_lds_bytes(bf, c->chunk, c->d_k);
@@ -85,6 +88,7 @@ msgla_status check_config(const msgla_config* c) {
 PackGeom pack_geom(const msgla_config* c) {
   PackGeom g{};
   g.bf16 = c->dtype == MSGLA_BF16;
+  g.norm = c->norm == 1;
   g.es = g.bf16 ? 2 : 4;
   g.m = c->n_branches;
   g.d = c->d_model;
@@ -118,6 +122,8 @@ PackGeom pack_geom(const msgla_config* c) {
     cur += align256((size_t)g.rp * b.h * g.dk * 4);
     b.off_bg = cur;
     cur += align256((size_t)b.h * g.dk * 4);
+    b.off_gn = cur;
+    if (g.norm) cur += align256((size_t)b.h * g.dv * 4);
     b.ko = ko;
     b.kp = cdiv(b.h * g.dv, e128) * e128;
     ko += b.kp;
@@ -282,6 +288,7 @@ msgla_status msgla_pack_weights(const msgla_config* cfg, const msgla_weights* w,
     const msgla_branch_weights& b = w->br[i];
     if (!b.W_q || !b.W_k || !b.W_v || !b.W_g1 || !b.W_g2 || !b.b_g || !b.W_o)
       return MSGLA_ERR_INVALID_ARG;
+    if (g.norm && !b.norm_g) return MSGLA_ERR_INVALID_ARG;
   }
   if (g.m > 1 && (!w->W_f || !w->b_f)) return MSGLA_ERR_INVALID_ARG;
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -300,6 +307,9 @@ msgla_status msgla_pack_weights(const msgla_config* cfg, const msgla_weights* w,
     HIP_TRY(pack_to_f32(g.bf16, s.W_g2, (size_t)g.r * b.h * g.dk, at<float>(packed, b.off_W2), st));
     HIP_TRY(hipMemcpyAsync(at<char>(packed, b.off_bg), s.b_g, (size_t)b.h * g.dk * 4,
                            hipMemcpyDeviceToDevice, st));
+    if (g.norm)
+      HIP_TRY(hipMemcpyAsync(at<char>(packed, b.off_gn), s.norm_g, (size_t)b.h * g.dv * 4,
+                             hipMemcpyDeviceToDevice, st));
     // W_o [h dv][d] -> WoT[n][ko + k]
     HIP_TRY(pack_transpose(g.bf16, s.W_o, b.h * g.dv, g.d, at<char>(packed, g.off_WoT + (size_t)b.ko * g.es),
                            g.Ktot, st));
@@ -580,6 +590,25 @@ msgla_status msgla_forward_timed(const msgla_config* cfg, const void* packed, co
   HIP_TRY(ev(2, false));
   HIP_TRY(ev(3, true));
   if (p2.total_seqs > 0) HIP_TRY(launch_k2b(p2, g.bf16, st));
+  if (g.norm) {
+    // the branches' y rows, normalised in place before the output projections
+    NormParams pn{};
+    pn.dv = g.dv;
+    int rows = 0;
+    for (int i = 0; i < g.m; ++i) {
+      if (W.br[i].n == 0) continue;
+      NormBranch& nb = pn.br[pn.nbranch++];
+      nb.y = at<char>(workspace, W.br[i].y);
+      nb.g = at<float>(packed, g.br[i].off_gn);
+      nb.h = g.br[i].h;
+      nb.n = W.br[i].n;
+      nb.np = W.br[i].np;
+      nb.row_begin = rows;
+      rows += (int)B * nb.h * nb.n;
+    }
+    pn.total_rows = rows;
+    HIP_TRY(launch_norm(pn, g.bf16, st));
+  }
   HIP_TRY(ev(3, false));
   HIP_TRY(ev(4, true));
   HIP_TRY(launch_k3c(p3, g.bf16, st));
@@ -707,6 +736,7 @@ msgla_status msgla_decode_step(const msgla_config* cfg, const void* packed, cons
   else
     p.Wz = nullptr;
   p.nbranch = g.m;
+  p.norm = g.norm ? 1 : 0;
   int Nmax = 0, hmax = 0;
   for (int i = 0; i < g.m; ++i) {
     const BranchGeom& b = g.br[i];
@@ -727,6 +757,7 @@ msgla_status msgla_decode_step(const msgla_config* cfg, const void* packed, cons
     k.held = at<float>(state, S.held[i]);
     k.proj = at<float>(workspace, D.proj[i]);
     k.y = at<float>(workspace, D.y[i]);
+    k.gn = g.norm ? at<float>(packed, b.off_gn) : nullptr;
     Nmax = std::max(Nmax, b.N);
     hmax = std::max(hmax, b.h);
   }

@@ -196,6 +196,34 @@ __global__ __launch_bounds__(DEC_THREADS) void k_dec_state(const DecParams P) {
     Br.y[(size_t)b * Br.h * P.dv + hh * P.dv + v] = part[lane] + part[64 + lane] + part[128 + lane] + part[192 + lane];
 }
 
+// grid (B * hmax, m), one wave: the per-head RMS normalisation of a completing
+// branch's new y row (gains and eps as in the forward), before the output kernel
+__global__ __launch_bounds__(64) void k_dec_norm(const DecParams P) {
+  const DecBranch& Br = P.br[blockIdx.y];
+  if (!Br.gn || !completes(dec_pos(P.state), Br.s)) return;
+  const int bh = blockIdx.x;
+  if (bh >= P.B * Br.h) return;
+  const int b = bh / Br.h, hh = bh - b * Br.h;
+  const int lane = threadIdx.x;
+  float* y = Br.y + (size_t)b * Br.h * P.dv + hh * P.dv;
+  float v[8];
+  float ss = 0.f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int c = lane + 64 * k;
+    v[k] = c < P.dv ? y[c] : 0.f;
+    ss += v[k] * v[k];
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
+  const float rs = 1.0f / sqrtf(ss / (float)P.dv + NORM_EPS);
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int c = lane + 64 * k;
+    if (c < P.dv) y[c] = v[k] * rs * Br.gn[hh * P.dv + c];
+  }
+}
+
 // grid (d / 16, ceil(B / 16)): output columns 16 x .. 16 x + 15 for sequences
 // 16 y .. 16 y + 15.  Wave w takes branches w, w + 4, ...: a completing branch
 // replaces its held output by y W_o (MFMA over K = h d_v), the others keep
@@ -291,6 +319,7 @@ hipError_t launch_decode(const DecParams& P, int Nmax, int hmax, bool bf16_path,
   else
     hipLaunchKernelGGL(k_dec_proj<float>, g1, blk, 0, st, P);
   hipLaunchKernelGGL(k_dec_state, g2, blk, lds2, st, P);
+  if (P.norm) hipLaunchKernelGGL(k_dec_norm, dim3(P.B * hmax, P.nbranch), dim3(64), 0, st, P);
   if (bf16_path)
     hipLaunchKernelGGL(k_dec_out<bf16>, g3, blk, 0, st, P);
   else

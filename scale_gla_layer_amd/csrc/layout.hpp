@@ -215,6 +215,7 @@ struct DecBranch {
   float* held;      // [B][d]
   float* proj;      // workspace [B][N]
   float* y;         // workspace [B][h dv]
+  const float* gn;  // normalisation gains [h dv], or null (no normalisation)
 };
 
 struct DecParams {
@@ -229,7 +230,23 @@ struct DecParams {
   const float* bf;
   const void* WoT;
   int nbranch;
+  int norm;         // the branches' outputs are normalised before W_o
   DecBranch br[MSGLA_MAX_BRANCHES];
+};
+
+// ---------------- optional per-head RMS normalisation of the branch outputs ---
+constexpr float NORM_EPS = 1e-6f;
+
+struct NormBranch {
+  void* y;          // [B][h][np][dv] storage type, normalised in place
+  const float* g;   // gains [h dv] fp32
+  int h, n, np;     // heads, rows per (b, head), padded row stride
+  int row_begin;    // first flattened row (b, head, j) of this branch
+};
+
+struct NormParams {
+  int dv, nbranch, total_rows;
+  NormBranch br[MSGLA_MAX_BRANCHES];
 };
 
 }  // namespace msgla

@@ -56,7 +56,8 @@ class DeviceLayer:
                 "W_q": to_device(bw.W_q, dt, device), "W_k": to_device(bw.W_k, dt, device),
                 "W_v": to_device(bw.W_v, dt, device), "W_g1": to_device(bw.W_g1, dt, device),
                 "W_g2": to_device(bw.W_g2, dt, device), "b_g": to_device_f32(bw.b_g, device),
-                "W_o": to_device(bw.W_o, dt, device)})
+                "W_o": to_device(bw.W_o, dt, device),
+                "norm_g": to_device_f32(bw.g_norm, device) if cfg.norm else None})
         m = len(cfg.scales)
         self._W_f = to_device(W.W_f, dt, device) if m > 1 else None
         self._b_f = to_device_f32(W.b_f, device) if m > 1 else None

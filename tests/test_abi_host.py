@@ -151,6 +151,20 @@ def test_forward_argument_errors_need_no_gpu():
     d = lib.msgla_decode_step
     assert d(ctypes.byref(cc), fake, None, 2, fake, fake, fake, dws, None) == 1
     assert d(ctypes.byref(cc), fake, fake, 2, fake, fake, fake, dws - 1, None) == 3
+    # normalisation flag out of range; normalisation without gains
+    bad = _raw_cfg()
+    bad.norm = 2
+    assert lib.msgla_validate_config(ctypes.byref(bad)) == 1
+    nc = _raw_cfg()
+    nc.norm = 1
+    wn = binding.CWeights()
+    for i in range(nc.n_branches):
+        for name in ("W_q", "W_k", "W_v", "W_g1", "W_g2", "b_g", "W_o"):
+            setattr(wn.br[i], name, fake)
+    wn.W_f = wn.b_f = fake
+    assert lib.msgla_pack_weights(ctypes.byref(nc), ctypes.byref(wn), fake,
+                                  lib.msgla_packed_weights_bytes(ctypes.byref(nc)), None) == 1
+    assert lib.msgla_packed_weights_bytes(ctypes.byref(nc)) > lib.msgla_packed_weights_bytes(ctypes.byref(cc))
     # fusion weights: NULL output, one branch
     fw = lib.msgla_fusion_weights
     assert fw(ctypes.byref(cc), fake, fake, 2, 64, None, None) == 1
