@@ -11,24 +11,26 @@
 
 namespace msgla {
 
-// Each wave takes NR consecutive rows and issues all their loads before the
-// first reduction, so several rows per wave are in flight.
+// A row takes LPR lanes (32 when it has at most 32 pieces of 16 bytes, so a
+// wave holds two rows side by side, else 64), and each wave takes NORM_NR such
+// row groups, issuing all their loads before the first reduction.
 constexpr int NORM_NR = 4;
 
-template <typename T>
+template <typename T, int LPR>
 __global__ __launch_bounds__(256) void k_norm_rows(const NormParams P) {
-  constexpr int PER = per16<T>();
-  const int row0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * NORM_NR;
-  const int lane = threadIdx.x & 63;
+  constexpr int PER = per16<T>(), RPS = 64 / LPR, PPL = LPR == 64 ? 2 : 1;  // rows per slot, pieces per lane
+  const int lane = threadIdx.x & 63, sub = lane / LPR, l = lane % LPR;
+  const int row0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * NORM_NR * RPS;
   if (row0 >= P.total_rows) return;  // the same for the whole wave
-  const int pieces = P.dv / PER;     // 16-byte pieces of a row, at most 128
+  const int pieces = P.dv / PER;     // 16-byte pieces of a row: at most LPR * PPL
   T* yr[NORM_NR];
   const float* gr[NORM_NR];
   bool ok[NORM_NR];
 #pragma unroll
   for (int u = 0; u < NORM_NR; ++u) {
-    const int row = min(row0 + u, P.total_rows - 1);  // rows past the end redo the last one, unstored
-    ok[u] = row0 + u < P.total_rows;
+    const int want = row0 + u * RPS + sub;
+    const int row = min(want, P.total_rows - 1);  // rows past the end redo the last one, unstored
+    ok[u] = want < P.total_rows;
     int bi = 0;
     while (bi + 1 < P.nbranch && row >= P.br[bi + 1].row_begin) ++bi;
     const NormBranch& Br = P.br[bi];
@@ -37,32 +39,29 @@ __global__ __launch_bounds__(256) void k_norm_rows(const NormParams P) {
     yr[u] = reinterpret_cast<T*>(Br.y) + ((size_t)bh * Br.np + j) * P.dv;
     gr[u] = Br.g + (bh % Br.h) * P.dv;
   }
-  u32x4 raw[NORM_NR][2];
+  u32x4 raw[NORM_NR][PPL];
 #pragma unroll
   for (int u = 0; u < NORM_NR; ++u)
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const int pc = min(lane + 64 * k, pieces - 1);
-      raw[u][k] = ld16(yr[u] + pc * PER);
-    }
+    for (int k = 0; k < PPL; ++k) raw[u][k] = ld16(yr[u] + min(l + LPR * k, pieces - 1) * PER);
 #pragma unroll
   for (int u = 0; u < NORM_NR; ++u) {
-    float v[2][PER];
+    float v[PPL][PER];
     float ss = 0.f;
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
+    for (int k = 0; k < PPL; ++k) {
       unpack16<T>(raw[u][k], v[k]);
-      if (lane + 64 * k < pieces) {
+      if (l + LPR * k < pieces) {
 #pragma unroll
         for (int e = 0; e < PER; ++e) ss += v[k][e] * v[k][e];
       }
     }
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
+    for (int off = LPR / 2; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
     const float rs = 1.0f / sqrtf(ss / (float)P.dv + NORM_EPS);
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const int pc = lane + 64 * k;
+    for (int k = 0; k < PPL; ++k) {
+      const int pc = l + LPR * k;
       if (ok[u] && pc < pieces) {
         float f[PER];
 #pragma unroll
@@ -78,13 +77,23 @@ __global__ __launch_bounds__(256) void k_norm_rows(const NormParams P) {
   }
 }
 
+template <typename T>
+static void launch_norm_t(const NormParams& P, hipStream_t st) {
+  const bool half = P.dv / per16<T>() <= 32;
+  const int rows_per_block = 4 * NORM_NR * (half ? 2 : 1);
+  const dim3 grid((P.total_rows + rows_per_block - 1) / rows_per_block), block(256);
+  if (half)
+    hipLaunchKernelGGL((k_norm_rows<T, 32>), grid, block, 0, st, P);
+  else
+    hipLaunchKernelGGL((k_norm_rows<T, 64>), grid, block, 0, st, P);
+}
+
 hipError_t launch_norm(const NormParams& P, bool bf16_path, hipStream_t st) {
   if (P.total_rows == 0) return hipSuccess;
-  const dim3 grid((P.total_rows + 4 * NORM_NR - 1) / (4 * NORM_NR)), block(256);
   if (bf16_path)
-    hipLaunchKernelGGL(k_norm_rows<bf16>, grid, block, 0, st, P);
+    launch_norm_t<bf16>(P, st);
   else
-    hipLaunchKernelGGL(k_norm_rows<float>, grid, block, 0, st, P);
+    launch_norm_t<float>(P, st);
   return hipGetLastError();
 }
 
