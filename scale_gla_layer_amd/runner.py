@@ -109,18 +109,47 @@ class DeviceLayer:
         binding.msgla_fusion_weights(self.cfg, self.packed, x, B, L, w_out, self.stream)
         return w_out
 
-    def decode_step(self, x_t, state, out_t=None):
-        torch = _torch()
-        B = x_t.shape[0]
+    def ensure_dec_workspace(self, B: int):
         n = binding.msgla_decode_workspace_bytes(self.cfg, B)
         if self.dec_workspace is None or self.dec_workspace.numel() < n:
             self.dec_workspace = empty_bytes(n, self.device)
+        return self.dec_workspace
+
+    def decode_step(self, x_t, state, out_t=None):
+        torch = _torch()
+        B = x_t.shape[0]
+        self.ensure_dec_workspace(B)
         if out_t is None:
             dt = torch.bfloat16 if self.cfg.dtype == BF16 else torch.float32
             out_t = torch.empty((B, self.cfg.d_model), dtype=dt, device=self.device)
         binding.msgla_decode_step(self.cfg, self.packed, x_t, B, state, out_t, self.dec_workspace,
                                   self.stream)
         return out_t
+
+
+class DecodeGraph:
+    """One streaming step (msgla_decode_step) captured once as a HIP graph.
+
+    The step takes its position from the state on the device and allocates
+    nothing, so one graph serves every later step of the same state: step()
+    copies the token into the captured input buffer and replays the graph.
+    Capturing enqueues nothing; the state advances only on replay."""
+
+    def __init__(self, layer: "DeviceLayer", state, B: int):
+        torch = _torch()
+        dt = torch.bfloat16 if layer.cfg.dtype == BF16 else torch.float32
+        self.x = torch.zeros((B, layer.cfg.d_model), dtype=dt, device=layer.device)
+        self.out = torch.empty_like(self.x)
+        ws = layer.ensure_dec_workspace(B)
+        torch.cuda.synchronize()
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph):
+            binding.msgla_decode_step(layer.cfg, layer.packed, self.x, B, state, self.out, ws)
+
+    def step(self, x_t):
+        self.x.copy_(x_t)
+        self.graph.replay()
+        return self.out
 
 
 def read_state(cfg: MsglaConfig, state, B: int) -> dict:

@@ -63,3 +63,29 @@ def test_decode_after_full_prefill(name):
     """Config of the wide sweep: B=16, prefill 4096 tokens, then 256 decode steps."""
     wl = WORKLOADS[name]
     _decode_case(wl.cfg, wl.batch, wl.seq_len, 256, seed=0, batches=(0, 11))
+
+
+def test_decode_graph_replays_match_eager_steps():
+    """The step captured once as a HIP graph and replayed for 24 steps, with
+    eager work and synchronisation between replays, gives bit-identical
+    outputs and state to eager steps from the same prefilled state."""
+    import torch
+    from scale_gla_layer_amd.runner import DecodeGraph
+    cfg = WORKLOADS["sweep_1248"].cfg
+    B, L0, n = 2, 45, 24
+    say(f"decode graph sweep_1248 B={B} L0={L0} steps={n}")
+    X, W = make_inputs(cfg, B, L0 + n, seed=11)
+    layer = DeviceLayer(cfg, W)
+    st_e = layer.new_state(B)
+    layer.forward(to_device(X[:, :L0], cfg.dtype), state_out=st_e)
+    st_g = st_e.clone()
+    xs = [to_device(np.ascontiguousarray(X[:, t]), cfg.dtype) for t in range(L0, L0 + n)]
+    eager = [layer.decode_step(x, st_e).clone() for x in xs]
+    g = DecodeGraph(layer, st_g, B)
+    scratch = torch.zeros(1 << 20, device="cuda")
+    for t, x in enumerate(xs):
+        out = g.step(x)
+        scratch.add_(1.0)  # the program's own eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager[t]), t
+    assert torch.equal(st_g, st_e)
