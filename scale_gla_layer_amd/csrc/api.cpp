@@ -150,6 +150,9 @@ struct WsBranch {
 struct WsGeom {
   WsBranch br[MSGLA_MAX_BRANCHES];
   size_t w, total;
+  int nseg;        // segments of the chunk-state walk (1: one walk per sequence)
+  int seg_base;    // workgroups of one segment
+  size_t Sseg;     // segment states, when nseg > 1
 };
 
 WsGeom ws_geom(const PackGeom& g, int64_t B, int64_t L) {
@@ -179,6 +182,21 @@ WsGeom ws_geom(const PackGeom& g, int64_t B, int64_t L) {
     b.y = take(rows * g.dv * g.es);
   }
   w.w = take((size_t)B * L * FUSION_STRIDE * 4);
+  // The chunk-state walk runs one workgroup per (sequence, 32-wide d_v slice).
+  // With few of them (small batches of long sequences) the sequential walk over
+  // the chunks leaves most CUs idle, so each walk is cut into segments (at least
+  // 8 chunks each) walked in parallel in two passes around a scan over segments.
+  {
+    int seqs = 0, nch_max = 0;
+    for (int i = 0; i < g.m; ++i) {
+      seqs += (int)B * g.br[i].h;
+      nch_max = std::max(nch_max, w.br[i].nch);
+    }
+    w.seg_base = cdiv(seqs, N_XCD) * N_XCD * (g.dv / k2b_dvt());
+    w.nseg = 1;
+    if (w.seg_base < 128) w.nseg = std::max(1, std::min({256 / std::max(w.seg_base, 1), nch_max / 8, 64}));
+    w.Sseg = w.nseg > 1 ? take((size_t)seqs * w.nseg * g.dk * g.dv * 4) : 0;
+  }
   w.total = cur;
   return w;
 }
@@ -496,6 +514,9 @@ msgla_status msgla_forward_timed(const msgla_config* cfg, const void* packed, co
   }
   p2.total_seqs = seqs;
   p2.n_dvt = g.dv / k2b_dvt();
+  p2.nseg = W.nseg;
+  p2.seg_base = W.seg_base;
+  p2.Sseg = W.nseg > 1 ? at<float>(workspace, W.Sseg) : nullptr;
 
   // ---------------- K3 ----------------
   // coarse outputs Y = y W_o reuse the block-mean buffers of their branch

@@ -58,6 +58,7 @@ struct K2bGeom {
   static constexpr int LDS = NST * STAGE + EXTRA;
   // copy instructions per chunk (all issued by the copy wave)
   static constexpr int NCOPY = nA + 2 * nQ + nV + (bL <= 1024 ? 1 : 0);
+  static constexpr int NCOPY_S = nQ + nV + (bL <= 1024 ? 1 : 0);  // state-only walk: kT, V, lam
   static_assert(bA % 1024 == 0 && bQ % 1024 == 0 && bV % 1024 == 0 && bL <= 1024, "block sizes");
   static_assert(NSC >= 1 && NSC <= 4 && NSK >= 1 && NSK <= 16, "slab counts");
 };
@@ -73,11 +74,14 @@ __device__ __forceinline__ int k2b_lane_off(int lg, int k, int lane) {
   return 128 * (lane >> 3) + 16 * ((lane & 7) ^ ((vrow >> hs) & 7));
 }
 
-template <typename T, int C, int DK>
+// SONLY: the state-only pass of the segmented walk (no A, qt or y; the
+// segment's local final state from zero goes to Sseg).
+template <typename T, int C, int DK, bool SONLY>
 __global__ __launch_bounds__(K2B_THREADS) void k2b_gla_state(const K2Params P) {
   using G = K2bGeom<T, C, DK>;
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  const int g = blockIdx.x;
+  const int seg = blockIdx.x / P.seg_base;
+  const int g = blockIdx.x - seg * P.seg_base;
   const int slot = g / N_XCD, xcd = g % N_XCD;
   const int qseq = (slot / P.n_dvt) * N_XCD + xcd;
   const int tile = slot % P.n_dvt;
@@ -87,6 +91,15 @@ __global__ __launch_bounds__(K2B_THREADS) void k2b_gla_state(const K2Params P) {
     if (qseq >= P.br[P.order[o]].seq_begin) bi = P.order[o];
   const K2Branch& Bb = P.br[bi];
   const int bh = qseq - Bb.seq_begin;  // b * h + head
+  // this workgroup's chunks [cb, cb + cnt) and its start / end states
+  const int seg_len = (Bb.nch + P.nseg - 1) / max(P.nseg, 1);
+  const int cb = seg * seg_len;
+  const int cnt = max(0, min(Bb.nch, cb + seg_len) - cb);
+  const bool last_seg = P.nseg == 1 || seg == max(0, (Bb.nch - 1) / max(seg_len, 1));
+  if (P.nseg > 1 && cnt == 0 && (SONLY || !last_seg)) return;  // the whole workgroup
+  float* Sseg_slot = P.Sseg ? P.Sseg + (size_t)(qseq * P.nseg + seg) * DK * P.dv : nullptr;
+  const float* S_start = SONLY ? nullptr : (P.nseg > 1 ? Sseg_slot : (Bb.S_in ? Bb.S_in + (size_t)bh * DK * P.dv : nullptr));
+  float* S_end = SONLY ? Sseg_slot : (last_seg && Bb.S_out ? Bb.S_out + (size_t)bh * DK * P.dv : nullptr);
 
   constexpr int es = G::es;
   constexpr int PER = per16<T>();
@@ -115,8 +128,9 @@ __global__ __launch_bounds__(K2B_THREADS) void k2b_gla_state(const K2Params P) {
   // compute waves never queue behind copy instructions, and the copy wave's
   // vmcnt holds nothing but copies, so its waits are exact.
   const int oL = 16 * lane;  // lam: one partial instruction of one virtual row (key 0)
-  auto issue = [&](int c) {
-    char* st = smem + (c % NST) * G::STAGE;
+  auto issue = [&](int i) {
+    const int c = cb + i;
+    char* st = smem + (i % NST) * G::STAGE;
     const char* a = Ag + (size_t)c * G::bA;
     const char* q = Qg + (size_t)c * G::bQ;
     const char* kk = Kg + (size_t)c * G::bQ;
@@ -128,21 +142,24 @@ __global__ __launch_bounds__(K2B_THREADS) void k2b_gla_state(const K2Params P) {
 #pragma unroll
     for (int k = 0; k < G::nQ; ++k) {
       dma16(kk + 1024 * k + k2b_lane_off(G::lgC, k, lane), st + G::oK + 1024 * k);
-      dma16(q + 1024 * k + k2b_lane_off(G::lgQ, k, lane), st + G::oQ + 1024 * k);
+      if constexpr (!SONLY) dma16(q + 1024 * k + k2b_lane_off(G::lgQ, k, lane), st + G::oQ + 1024 * k);
     }
+    if constexpr (!SONLY) {
 #pragma unroll
-    for (int k = 0; k < G::nA; ++k) dma16(a + 1024 * k + k2b_lane_off(G::lgC, k, lane), st + G::oA + 1024 * k);
+      for (int k = 0; k < G::nA; ++k) dma16(a + 1024 * k + k2b_lane_off(G::lgC, k, lane), st + G::oA + 1024 * k);
+    }
   };
+  constexpr int NCP = SONLY ? G::NCOPY_S : G::NCOPY;
   if (wave == 8) {
-    for (int c = 0; c < NST - 1 && c < Bb.nch; ++c) issue(c);
-    for (int c = 0; c < Bb.nch; ++c) {
-      // stage c has landed once only the copies of later stages remain
-      if (NST > 2 && c + 1 < Bb.nch)
-        wait_vmcnt<(G::NCOPY < 63 ? G::NCOPY : 63)>();
+    for (int i = 0; i < NST - 1 && i < cnt; ++i) issue(i);
+    for (int i = 0; i < cnt; ++i) {
+      // stage i has landed once only the copies of later stages remain
+      if (NST > 2 && i + 1 < cnt)
+        wait_vmcnt<(NCP < 63 ? NCP : 63)>();
       else
         wait_vmcnt<0>();
       lds_barrier();
-      if (c + NST - 1 < Bb.nch) issue(c + NST - 1);
+      if (i + NST - 1 < cnt) issue(i + NST - 1);
     }
     return;
   }
@@ -166,12 +183,12 @@ __global__ __launch_bounds__(K2B_THREADS) void k2b_gla_state(const K2Params P) {
 #pragma unroll
   for (int a = 0; a < G::SRT; ++a) S[a][0] = S[a][1] = zero4();
 
-  if (!Bb.S_in) {
+  if (!S_start) {
     for (int i = tid; i < K2B_DVT * G::LDS_S; i += 512) ST[i] = from_f32<T>(0.f);
   } else if (!out_wave) {
     // continuing from a state: each state wave loads its rows of S and
     // publishes them for chunk 0 as it would a carried state
-    const float* Si = Bb.S_in + (size_t)bh * DK * dv;
+    const float* Si = S_start;
 #pragma unroll
     for (int a = 0; a < G::SRT; ++a) {
       const int rt = w4 + 4 * a;
@@ -192,10 +209,11 @@ __global__ __launch_bounds__(K2B_THREADS) void k2b_gla_state(const K2Params P) {
     }
   }
 
-  for (int c = 0; c < Bb.nch; ++c) {
-    lds_barrier();  // stage c has landed (the copy wave waited for it)
+  for (int i = 0; i < cnt; ++i) {
+    const int c = cb + i;
+    lds_barrier();  // stage i has landed (the copy wave waited for it)
 
-    const char* st = smem + (c % NST) * G::STAGE;
+    const char* st = smem + (i % NST) * G::STAGE;
     const int valid = min(C, Bb.n - c * C);
 
     // V fragments (B-operand of both products); positions >= valid zeroed
@@ -220,12 +238,14 @@ __global__ __launch_bounds__(K2B_THREADS) void k2b_gla_state(const K2Params P) {
         }
     }
 
-    if (out_wave) {
+    if (SONLY && out_wave) {
+      // state-only pass: the output waves only keep the barriers
+    } else if (out_wave) {
       // ---- y rows 16w .. 16w+15 as y^T = V^T A^T + S_c^T qt^T: with V (and the
       // published S^T) as the A-operand, lane l holds 4 consecutive v of
       // position 16w + l % 16, which go straight to global memory ----
       if (w4 < C / 16) {
-        const T* Sb = ST + (c & 1) * K2B_DVT * G::LDS_S;
+        const T* Sb = ST + (i & 1) * K2B_DVT * G::LDS_S;
         u32x4 af[G::NSC], qf[G::NSK], sf[G::NSK][2];
 #pragma unroll
         for (int sl = 0; sl < G::NSC; ++sl) af[sl] = ld16(st + offA[sl]);
@@ -266,7 +286,7 @@ __global__ __launch_bounds__(K2B_THREADS) void k2b_gla_state(const K2Params P) {
       }
     } else {
       // ---- state rows: S_{c+1} = Diag(lam) S_c + kT V, published for chunk c+1 ----
-      T* Sn = ST + ((c + 1) & 1) * K2B_DVT * G::LDS_S;
+      T* Sn = ST + ((i + 1) & 1) * K2B_DVT * G::LDS_S;
 #pragma unroll
       for (int a = 0; a < G::SRT; ++a) {
         const int rt = w4 + 4 * a;
@@ -301,8 +321,8 @@ __global__ __launch_bounds__(K2B_THREADS) void k2b_gla_state(const K2Params P) {
     }
   }
 
-  if (!out_wave && Bb.S_out) {
-    float* So = Bb.S_out + (size_t)bh * DK * dv;
+  if (!out_wave && S_end) {
+    float* So = S_end;
 #pragma unroll
     for (int a = 0; a < G::SRT; ++a) {
       const int rt = w4 + 4 * a;
@@ -318,32 +338,71 @@ __global__ __launch_bounds__(K2B_THREADS) void k2b_gla_state(const K2Params P) {
 }
 
 template <typename T, int C, int DK>
-static void launch_k2b_cd(const K2Params& P, dim3 grid, hipStream_t stream) {
+static void launch_k2b_cd(const K2Params& P, dim3 grid, hipStream_t stream, bool sonly) {
   using G = K2bGeom<T, C, DK>;
-  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k2b_gla_state<T, C, DK>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, G::LDS);
-  hipLaunchKernelGGL((k2b_gla_state<T, C, DK>), grid, dim3(K2B_THREADS), G::LDS, stream, P);
+  if (sonly) {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k2b_gla_state<T, C, DK, true>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, G::LDS);
+    hipLaunchKernelGGL((k2b_gla_state<T, C, DK, true>), grid, dim3(K2B_THREADS), G::LDS, stream, P);
+  } else {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k2b_gla_state<T, C, DK, false>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, G::LDS);
+    hipLaunchKernelGGL((k2b_gla_state<T, C, DK, false>), grid, dim3(K2B_THREADS), G::LDS, stream, P);
+  }
 }
 
 template <typename T, int C>
-static bool launch_k2b_c(const K2Params& P, dim3 grid, hipStream_t stream) {
+static bool launch_k2b_c(const K2Params& P, dim3 grid, hipStream_t stream, bool sonly) {
   switch (P.dk) {
-    case 16: if constexpr (sizeof(T) == 4) { launch_k2b_cd<T, C, 16>(P, grid, stream); return true; } return false;
-    case 32: launch_k2b_cd<T, C, 32>(P, grid, stream); return true;
-    case 64: launch_k2b_cd<T, C, 64>(P, grid, stream); return true;
-    case 128: launch_k2b_cd<T, C, 128>(P, grid, stream); return true;
-    case 256: launch_k2b_cd<T, C, 256>(P, grid, stream); return true;
+    case 16: if constexpr (sizeof(T) == 4) { launch_k2b_cd<T, C, 16>(P, grid, stream, sonly); return true; } return false;
+    case 32: launch_k2b_cd<T, C, 32>(P, grid, stream, sonly); return true;
+    case 64: launch_k2b_cd<T, C, 64>(P, grid, stream, sonly); return true;
+    case 128: launch_k2b_cd<T, C, 128>(P, grid, stream, sonly); return true;
+    case 256: launch_k2b_cd<T, C, 256>(P, grid, stream, sonly); return true;
     default: return false;
   }
 }
 
 template <typename T>
-static bool launch_k2b_t(const K2Params& P, dim3 grid, hipStream_t stream) {
+static bool launch_k2b_t(const K2Params& P, dim3 grid, hipStream_t stream, bool sonly) {
   switch (P.C) {
-    case 16: if constexpr (sizeof(T) == 4) return launch_k2b_c<T, 16>(P, grid, stream); return false;
-    case 32: return launch_k2b_c<T, 32>(P, grid, stream);
-    case 64: return launch_k2b_c<T, 64>(P, grid, stream);
+    case 16: if constexpr (sizeof(T) == 4) return launch_k2b_c<T, 16>(P, grid, stream, sonly); return false;
+    case 32: return launch_k2b_c<T, 32>(P, grid, stream, sonly);
+    case 64: return launch_k2b_c<T, 64>(P, grid, stream, sonly);
     default: return false;
+  }
+}
+
+// Segmented walk, between the two passes: per (sequence, key channel c) and
+// every d_v column, the start state of segment p is
+//   S_start(0) = S_in (or 0),  S_start(p + 1) = Diag(Lam_p) S_start(p) + S_local(p),
+// Lam_p = the product of the segment's per-chunk decays lam (row c).  Sseg
+// holds S_local on entry and S_start on exit.
+__global__ __launch_bounds__(256) void k2b_seg_scan(const K2Params P) {
+  __shared__ float lam_seg[64];
+  const int qseq = blockIdx.x / P.dk, c = blockIdx.x - qseq * P.dk;
+  int bi = P.order[0];
+  for (int o = 1; o < P.nbranch; ++o)
+    if (qseq >= P.br[P.order[o]].seq_begin) bi = P.order[o];
+  const K2Branch& Bb = P.br[bi];
+  const int bh = qseq - Bb.seq_begin;
+  const int seg_len = (Bb.nch + P.nseg - 1) / P.nseg;
+  if (threadIdx.x < P.nseg) {
+    const int p = threadIdx.x;
+    const int c1 = min(Bb.nch, (p + 1) * seg_len);
+    float prod = 1.f;
+    for (int ch = p * seg_len; ch < c1; ++ch) prod *= Bb.lam[((size_t)bh * Bb.nch + ch) * P.dk + c];
+    lam_seg[p] = prod;
+  }
+  __syncthreads();
+  for (int v = threadIdx.x; v < P.dv; v += 256) {
+    float cur = Bb.S_in ? Bb.S_in[((size_t)bh * P.dk + c) * P.dv + v] : 0.f;
+    for (int p = 0; p < P.nseg; ++p) {
+      float* slot = P.Sseg + ((size_t)(qseq * P.nseg + p) * P.dk + c) * P.dv + v;
+      const float loc = *slot;
+      *slot = cur;
+      cur = lam_seg[p] * cur + loc;
+    }
   }
 }
 
@@ -375,9 +434,15 @@ int k2b_lds_bytes(bool bf16_path, int C, int dk) {
 }
 
 hipError_t launch_k2b(const K2Params& P, bool bf16_path, hipStream_t stream) {
-  const dim3 grid(((P.total_seqs + N_XCD - 1) / N_XCD) * N_XCD * P.n_dvt);
-  const bool ok = bf16_path ? launch_k2b_t<bf16>(P, grid, stream) : launch_k2b_t<float>(P, grid, stream);
-  if (!ok) return hipErrorInvalidValue;
+  const dim3 grid(P.seg_base * P.nseg);
+  auto walk = [&](bool sonly) {
+    return bf16_path ? launch_k2b_t<bf16>(P, grid, stream, sonly) : launch_k2b_t<float>(P, grid, stream, sonly);
+  };
+  if (P.nseg > 1) {
+    if (!walk(true)) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k2b_seg_scan, dim3(P.total_seqs * P.dk), dim3(256), 0, stream, P);
+  }
+  if (!walk(false)) return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

@@ -151,6 +151,13 @@ struct K2Params {
   int n_dvt;        // K2b: d_v tiles per sequence
   int per_xcd;      // K2b block remap
   int order[MSGLA_MAX_BRANCHES];  // K2b: branches by decreasing chunk count
+  // K2b segmented walk (few sequences, long chains): each sequence's chunks are
+  // cut into nseg segments walked in parallel, first for their local states
+  // (state-only pass from zero), then, after a scan over the segments, again
+  // from their true start states.  nseg = 1: one walk per sequence.
+  int nseg;
+  int seg_base;     // workgroups of one segment (the plain walk's grid)
+  float* Sseg;      // [total_seqs][nseg][dk][dv] fp32: local, then start states
   K2Branch br[MSGLA_MAX_BRANCHES];
 };
 
