@@ -379,7 +379,9 @@ static bool launch_k2b_t(const K2Params& P, dim3 grid, hipStream_t stream, bool 
 // Lam_p = the product of the segment's per-chunk decays lam (row c).  Sseg
 // holds S_local on entry and S_start on exit.
 __global__ __launch_bounds__(256) void k2b_seg_scan(const K2Params P) {
+  constexpr int NCH_LDS = 8192;
   __shared__ float lam_seg[64];
+  __shared__ float lam_all[NCH_LDS];
   const int qseq = blockIdx.x / P.dk, c = blockIdx.x - qseq * P.dk;
   int bi = P.order[0];
   for (int o = 1; o < P.nbranch; ++o)
@@ -387,11 +389,18 @@ __global__ __launch_bounds__(256) void k2b_seg_scan(const K2Params P) {
   const K2Branch& Bb = P.br[bi];
   const int bh = qseq - Bb.seq_begin;
   const int seg_len = (Bb.nch + P.nseg - 1) / P.nseg;
+  const float* lam = Bb.lam + (size_t)bh * Bb.nch * P.dk + c;  // chunk ch at lam[ch * dk]
+  const bool staged = Bb.nch <= NCH_LDS;
+  if (staged) {
+    // every chunk's decay of channel c, loaded by all threads at once
+    for (int ch = threadIdx.x; ch < Bb.nch; ch += 256) lam_all[ch] = lam[(size_t)ch * P.dk];
+    __syncthreads();
+  }
   if (threadIdx.x < P.nseg) {
     const int p = threadIdx.x;
     const int c1 = min(Bb.nch, (p + 1) * seg_len);
     float prod = 1.f;
-    for (int ch = p * seg_len; ch < c1; ++ch) prod *= Bb.lam[((size_t)bh * Bb.nch + ch) * P.dk + c];
+    for (int ch = p * seg_len; ch < c1; ++ch) prod *= staged ? lam_all[ch] : lam[(size_t)ch * P.dk];
     lam_seg[p] = prod;
   }
   __syncthreads();
