@@ -149,7 +149,7 @@ def test_repeat_runs_are_bitwise_identical():
 
 def test_exported_state_matches_oracle():
     cfg = _with(TINY)
-    for L in (37, 64, 3):
+    for L in (37, 64, 3, 600):  # 600: the chunk-state walk runs in segments
         X, W = make_inputs(cfg, 2, L, seed=13)
         say(f"state export tiny L={L}")
         layer, x, out, st = run_device(cfg, X, W, state_out=True)

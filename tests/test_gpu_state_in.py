@@ -44,6 +44,8 @@ def _split_run(cfg, B, L1, L2, seed, same_buffer, gate_bias=None):
     ("tiny_f32", 1, 4, 1, False),     # one token after one block of every scale
     ("main", 2, 128, 100, True),
     ("main", 1, 256, 2, False),       # scale 4 sees no block in the second part
+    ("tiny_f32", 1, 512, 600, False), # both parts walk the chunk states in segments
+    ("tiny_f32", 2, 400, 300, True),
 ])
 def test_continue_matches_one_pass(cfg_name, B, L1, L2, same):
     cfg = WORKLOADS[cfg_name].cfg
