@@ -164,16 +164,15 @@ def hold_index(t: int, s: int) -> int:
     return (t + 1) // s - 1
 
 
-def causal_hold(Y: np.ndarray, s: int, L: int, held_before: Optional[np.ndarray] = None):
-    """[B, n_s, d] coarse outputs -> [B, L, d] per original position."""
+def causal_hold(Y: np.ndarray, s: int, L: int):
+    """[B, n_s, d] coarse outputs -> [B, L, d] per original position; positions
+    before the first complete block take zero."""
     B, n, d = Y.shape
     out = np.zeros((B, L, d))
     for t in range(L):
         j = hold_index(t, s)
         if j >= 0:
             out[:, t] = Y[:, j]
-        elif held_before is not None:
-            out[:, t] = held_before
     return out
 
 

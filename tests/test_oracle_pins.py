@@ -13,8 +13,12 @@ in the oracle:
                 reshape-mean, pool/project commutation
   hold          the notes' s=4 table (golden), repeat-then-shift construction
   fusion        simplex, uniform at W_f = 0, two-branch closed form
-  normalisation one-channel heads (sign times gain), invariance of the layer
-                to a positive scale of W_v, decode == forward with it
+  normalisation one-channel heads (sign times gain), two- and three-channel
+                heads worked by hand (mean, not sum, of squares; eps),
+                invariance of the layer to a positive scale of W_v,
+                decode == forward with it
+  metric        the row-relative error worked by hand (per-row infinity
+                norms, max over rows, exact-zero rows)
   routing       region means of weights linear in the position (closed form),
                 regions of a 10-position sequence by hand, percentages sum to 100
   whole layer   a hand-derived scalar example, causality, decode == forward,
@@ -554,3 +558,65 @@ def test_normalised_decode_equals_forward():
     for t in range(8, L):
         o, st = orc.decode_step(st, X[:, t], W, cfg)
         assert np.allclose(o, O[:, t], rtol=1e-11, atol=1e-13), t
+
+
+def test_rms_norm_two_and_three_channel_heads_by_hand():
+    """The RMS is the root of the MEAN square over d_v (plus eps = 1e-6), worked
+    by hand: [3, 4] has mean square 12.5 (a sum would give 25), [1, 2, 2] has
+    3 (a sum would give 9); a head of zeros stays zero; for [1e-3, 0] the
+    mean square 5e-7 is comparable to eps, so the result pins eps too."""
+    o = np.array([[[3.0, 4.0, 0.0], [1.0, 2.0, 2.0]],
+                  [[0.0, 0.0, 0.0], [1e-3, 0.0, 0.0]]])  # [2, h=2, d_v=3]
+    g = np.array([1.0, 1.0, 1.0, 2.0, -1.0, 0.5])
+    out = orc.rms_norm_heads(o, g)
+    r0 = math.sqrt(25.0 / 3.0 + 1e-6)       # [3, 4, 0]: mean square 25/3
+    r1 = math.sqrt(3.0 + 1e-6)              # [1, 2, 2]: mean square 3
+    r3 = math.sqrt(1e-6 / 3.0 + 1e-6)       # [1e-3, 0, 0]: mean square 1e-6/3
+    want = np.array([[[3.0 / r0, 4.0 / r0, 0.0], [2.0 / r1, -2.0 / r1, 1.0 / r1]],
+                     [[0.0, 0.0, 0.0], [2e-3 / r3, 0.0, 0.0]]])
+    assert np.allclose(out, want, rtol=1e-13, atol=0)
+    # two channels: [3, 4] -> [3, 4] / sqrt(12.5 + eps)
+    o2 = np.array([[3.0, 4.0]])
+    r = math.sqrt(12.5 + 1e-6)
+    assert np.allclose(orc.rms_norm_heads(o2, np.ones(2)), [[3.0 / r, 4.0 / r]], rtol=1e-13)
+
+
+# --------------------------------------------------------------------------- the parity metric
+
+
+def test_row_relative_error_by_hand():
+    """max over rows of ||dev_t - ref_t||_inf / ||ref_t||_inf, worked by hand.
+
+    Rows of very different size make the per-row and the global normalisation
+    disagree (global: 1/100 = 0.01; per row: 0.05), and the max over rows
+    differs from their mean; the infinity norm differs from the 2-norm on the
+    row [3, 4] (0.5 / 4 against 0.5 / 5)."""
+    ref = np.array([[100.0, 0.0], [1.0, -1.0], [3.0, 4.0], [2.0, 0.0]])
+    dev = np.array([[100.0, 1.0], [1.0, -1.05], [3.0, 4.1], [2.02, 0.0]])
+    err, zeros = orc.row_relative_error(dev, ref)
+    assert zeros
+    assert abs(err - 0.05) <= 1e-12
+    # the largest error sits in the smallest row: a global denominator would hide it
+    dev2 = dev.copy()
+    dev2[1] = [1.0, -1.0]
+    dev2[2] = [3.0, 4.5]
+    err2, _ = orc.row_relative_error(dev2, ref)
+    assert abs(err2 - 0.125) <= 1e-12
+    # leading dimensions are flattened to rows: [B, L, d] gives the same answer
+    err3, _ = orc.row_relative_error(dev.reshape(2, 2, 2), ref.reshape(2, 2, 2))
+    assert abs(err3 - 0.05) <= 1e-12
+
+
+def test_row_relative_error_zero_rows_must_be_exact():
+    """Rows the reference gives as exactly zero are excluded from the ratio and
+    must be exactly zero on the other side; a tiny value there is reported."""
+    ref = np.array([[0.0, 0.0], [1.0, 2.0]])
+    ok = np.array([[0.0, -0.0], [1.0, 2.0]])
+    err, zeros = orc.row_relative_error(ok, ref)
+    assert zeros and err == 0.0
+    bad = np.array([[0.0, 1e-30], [1.0, 2.0]])
+    err, zeros = orc.row_relative_error(bad, ref)
+    assert not zeros and err == 0.0
+    # all reference rows zero: no ratio, the zero check alone decides
+    err, zeros = orc.row_relative_error(np.zeros((3, 2)), np.zeros((3, 2)))
+    assert zeros and err == 0.0
