@@ -20,12 +20,19 @@
 // whole output rows); A is formed from the fp32 operands (fp32 MFMA, or for
 // bf16 storage three bf16 MFMA products of their hi/lo split) and rounded once
 // to the storage type.
-// Every exponent used is <= 0 except one bounded by 15 positions of decay:
-// the 16 x 16 block A[T][J] (query tile T, key tile J <= T) is built as
-// (q_t e^{b_t - b_16T}) . (k_i e^{b_16J - b_i} D_TJ) with D_TJ = e^{b_16T - b_16J};
-// the query factor and D_TJ are <= 1 and the key factor grows over less than
-// 16 positions.  Rows beyond the sequence end are treated as q = k = 0 and
-// log alpha = 0, which leaves the state untouched.
+// Every stored factor has an exponent <= 0.  With e_J = 16 J + 15 the last
+// position of 16-position tile J, the key side is referenced at the end of
+// its own tile, kb_i = k_i e^{b_{e_J} - b_i} (<= |k_i|), so kT = kb e^{b_last -
+// b_{e_J}} and every off-diagonal block A[T][J], J < T, is
+// (q_t e^{b_t - b_16T}) . (kb_i D_TJ) with D_TJ = e^{b_16T - b_{e_J}} <= 1.
+// The diagonal block A[T][T] has one growing factor, C_T = e^{b_16T - b_{e_T}}
+// (the tile's own total decay, inverted): kb_i C_T.  It is used only while
+// C_T <= 2^32 and kb C_T is finite for every channel of the tile (so |k| up
+// to 2^96); otherwise that block is formed pair by pair, A[t][i] =
+// sum_c q_tc k_ic prod_{u=i+1..t} alpha_uc, from the per-step decays alpha <= 1
+// (exact for any gate, and some 8x slower, so it is reserved for tiles that
+// decay by more than 2^-32).  Rows beyond the sequence end are treated as
+// q = k = 0 and log alpha = 0, which leaves the state untouched.
 //
 // Work layout: wave w owns the 16 positions 16w .. 16w+15 of the chunk and all
 // key channels.  Its gate pre-activations z^T = W_g2^T (xp W_g1)^T come from
@@ -33,13 +40,13 @@
 // 16 w + l % 16 for every channel tile rt.  The cumulative sum over positions
 // is a DPP prefix scan inside each 16-lane row; the waves then exchange their
 // totals (and first values) through LDS.  The key side of A (fp32, referenced
-// at its own tile) goes to LDS; the query side stays in registers, referenced
-// at the wave's first position, so it is formed once; wave w scales the key
-// side of tile J by D_wJ (a per-channel table it fills in LDS) and forms the
-// blocks A[w][J], J <= w, with fp32 MFMA as (key side)(query side)^T so that
-// each lane holds 4 consecutive keys of one query row.  All shapes are
-// compile-time (chunk C, key width DK, padded gate rank RP), so every loop
-// unrolls.
+// at the end of its tile) goes to LDS; the query side stays in registers,
+// referenced at the wave's first position, so it is formed once; wave w
+// scales the key side of tile J by D_wJ (J < w, a per-channel table it fills
+// in LDS) or C_w (J = w) and forms the blocks A[w][J] with MFMA as
+// (key side)(query side)^T so that each lane holds 4 consecutive keys of one
+// query row.  All shapes are compile-time (chunk C, key width DK, padded gate
+// rank RP), so every loop unrolls.
 #include "async_copy.hpp"
 #include "device_common.hpp"
 #include "layout.hpp"
@@ -76,6 +83,9 @@ __device__ __forceinline__ float log2sigmoid(float z) {
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// log2 of the largest growing factor the diagonal block may use (C_w <= 2^32)
+constexpr float K2A_DIAG_LOG2_BOUND = 32.f;
+
 template <typename T, int C, int DK>
 struct K2aGeom {
   static constexpr int NW = C / 16;            // waves, one per 16-position tile
@@ -84,10 +94,10 @@ struct K2aGeom {
   static constexpr bool BF = sizeof(T) == 2;
   // key-side rows in LDS (fp32), padded by 16 bytes against bank conflicts between rows
   static constexpr int KROW = DK * 4 + 16;
-  static constexpr int XCH = 4 * NW * DK * 4;  // wave totals, first values, two factor tables
+  static constexpr int XCH = 5 * NW * DK * 4;  // wave totals, first values, three factor tables
   static constexpr int KS = C * KROW;
   static constexpr int DT = NW * (NW - 1) * DK * 4;  // per wave: D_wJ for J < w
-  static constexpr int LDS = XCH + KS + DT;  // 47 KB at C 64, d_k 128: three workgroups per CU
+  static constexpr int LDS = XCH + KS + DT;  // 49 KB at C 64, d_k 128: three workgroups per CU
   static_assert(C == 16 || C == 32 || C == 64, "chunk");
   static_assert(BF ? (DK >= 32 && DK % 32 == 0) : (DK >= 16 && DK % 16 == 0), "key width");
 };
@@ -116,7 +126,7 @@ __global__ __launch_bounds__(256) void k2a_gla_chunk(const K2Params P) {
 
   float* tot = reinterpret_cast<float*>(smem);  // [NW][DK] wave totals of log2 alpha
   float* first = tot + NW * DK;                 // [NW][DK] value at each wave's first row
-  float* Ew = first + NW * DK + w * 2 * DK;     // [NW][2][DK] e^{b_16w}, e^{b_last - b_16w}
+  float* Ew = first + NW * DK + w * 3 * DK;     // [NW][3][DK] e^{b_16w}, e^{b_last - b_e}, C_w
   char* ks = smem + G::XCH;                     // key side [C][KROW] fp32
   float* Dw = reinterpret_cast<float*>(smem + G::XCH + G::KS) + w * (NW - 1) * DK;  // [J][DK]
 
@@ -153,8 +163,8 @@ __global__ __launch_bounds__(256) void k2a_gla_chunk(const K2Params P) {
   // valid row and discard it), so the copies and the gate factor have landed
   // once only the 2 NT q / k loads remain.
   const int pl = live ? p : 0;
-  float gb[RP / 4];
-  {
+  // the gate's first factor of this lane's position (4 of its RP values per lane)
+  auto load_gate_factor = [&](float (&gb)[RP / 4]) {
     // x W_g1 is given per unpooled position: the block's mean is this row's value
     const float* gr = Bb.g + ((size_t)b * P.L + (size_t)(row0 + pl) * Bb.s) * RP + lg;
     if (P.mask) {
@@ -198,7 +208,23 @@ __global__ __launch_bounds__(256) void k2a_gla_chunk(const K2Params P) {
     }
 #pragma unroll
     for (int k4 = 0; k4 < RP / 4; ++k4) gb[k4] = live ? gb[k4] : 0.f;
-  }
+  };
+  // log2 alpha of channel tile rt at this lane's position (z from fp32 MFMA) and
+  // its inclusive scan over the wave's 16 positions
+  auto gate_scan = [&](const float (&gb)[RP / 4], const float* w2, int w2stride, const float* bgp,
+                       int rt, float (&xo)[4]) {
+    f32x4 acc = __builtin_bit_cast(f32x4, ld16(bgp + 16 * rt + 4 * lg));  // gate bias
+#pragma unroll
+    for (int k4 = 0; k4 < RP / 4; ++k4)
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(w2[(4 * k4 + lg) * w2stride + 16 * rt], gb[k4], acc, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float la = live ? log2sigmoid(acc[i]) * P.inv_gamma : 0.f;
+      xo[i] = row_scan16(la);
+    }
+  };
+  float gb[RP / 4];
+  load_gate_factor(gb);
   asm volatile("" ::: "memory");  // keep the q / k loads behind the copies and the gate factor
   u32x4 qraw[NT], kraw[NT];
   {
@@ -222,18 +248,9 @@ __global__ __launch_bounds__(256) void k2a_gla_chunk(const K2Params P) {
     const float* w2 = STAGE_W ? w2s + lr : Bb.W2 + hh * DK + lr;
     const int w2stride = STAGE_W ? DK : hdk;
     const float* bgp = STAGE_W ? bgs : Bb.bg + hh * DK;
-    const float scale = P.inv_gamma;
 #pragma unroll
     for (int rt = 0; rt < NT; ++rt) {
-      f32x4 acc = __builtin_bit_cast(f32x4, ld16(bgp + 16 * rt + 4 * lg));  // gate bias
-#pragma unroll
-      for (int k4 = 0; k4 < RP / 4; ++k4)
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(w2[(4 * k4 + lg) * w2stride + 16 * rt], gb[k4], acc, 0, 0, 0);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float la = live ? log2sigmoid(acc[i]) * scale : 0.f;
-        x[rt][i] = row_scan16(la);  // inclusive scan over this wave's 16 positions
-      }
+      gate_scan(gb, w2, w2stride, bgp, rt, x[rt]);
       if (lr == 15) st16(tot + w * DK + 16 * rt + 4 * lg, pack16<float>(x[rt]));
       if (lr == 0) st16(first + w * DK + 16 * rt + 4 * lg, pack16<float>(x[rt]));
     }
@@ -241,9 +258,13 @@ __global__ __launch_bounds__(256) void k2a_gla_chunk(const K2Params P) {
   lds_barrier();  // the exchange is through LDS only; q and k may still be loading
 
   // ---- per channel (lane owns channels lane, lane + 64, ...): b at this wave's
-  // first position b_16w = (totals of the earlier waves) + (first value), the
-  // factors e^{b_16w} and e^{b_last - b_16w} (LDS), D_wJ = e^{b_16w - b_16J}
-  // for J < w (LDS) and, from wave 0, lam = e^{b_last} (global) ----
+  // first position b_16w = (totals of the earlier waves) + (first value) and at
+  // its last b_e = (totals up to this wave); the factors e^{b_16w},
+  // e^{b_last - b_e} and C_w = e^{b_16w - b_e} (LDS), D_wJ = e^{b_16w - b_{e_J}}
+  // for J < w (LDS) and, from wave 0, lam = e^{b_last} (global).  A tile whose
+  // decay e^{b_e - b_16w} is below 2^-32 in some channel forms its diagonal
+  // block pair by pair ----
+  bool exact_diag = false;
   {
     float* lamg = Bb.lam + ((size_t)bh * Bb.nch + chunk) * DK;
 #pragma unroll
@@ -258,14 +279,18 @@ __global__ __launch_bounds__(256) void k2a_gla_chunk(const K2Params P) {
           if (v < w) carry += tv;
         }
         const float bw = carry + first[w * DK + ch];
+        const float be = carry + tot[w * DK + ch];
+        const float growth = first[w * DK + ch] - tot[w * DK + ch];  // log2 C_w >= 0
+        exact_diag |= !(growth <= K2A_DIAG_LOG2_BOUND);
         Ew[ch] = exp2_fast(bw);
-        Ew[DK + ch] = exp2_fast(blast - bw);
+        Ew[DK + ch] = exp2_fast(blast - be);
+        Ew[2 * DK + ch] = exp2_fast(fminf(growth, K2A_DIAG_LOG2_BOUND));
         if (w == 0) lamg[ch] = exp2_fast(blast);
         float cj = 0.f;
 #pragma unroll
         for (int J = 0; J < NW - 1; ++J) {
-          if (J < w) Dw[J * DK + ch] = exp2_fast(bw - (cj + first[J * DK + ch]));
-          cj += tot[J * DK + ch];
+          cj += tot[J * DK + ch];  // b at the end of tile J
+          if (J < w) Dw[J * DK + ch] = exp2_fast(bw - cj);
         }
       }
     }
@@ -274,10 +299,11 @@ __global__ __launch_bounds__(256) void k2a_gla_chunk(const K2Params P) {
     asm volatile("" ::: "memory");
   }
 
-  // ---- per element, with d = b_t - b_16w (this lane's scan minus the wave's first
-  // value): query side of A q e^d (registers, in place of q), key side k e^{-d}
-  // (LDS), qt = q e^{b_t} = (q e^d) e^{b_16w} and kT = k e^{b_last - b_t} =
-  // (k e^{-d}) e^{b_last - b_16w} (global) ----
+  // ---- per element, with d = b_t - b_16w <= 0 and d_e = b_e - b_t <= 0 (this
+  // lane's scan against the wave's first and last values): query side of A
+  // q e^d (registers, in place of q), key side kb = k e^{d_e} (LDS),
+  // qt = q e^{b_t} = (q e^d) e^{b_16w} and kT = k e^{b_last - b_t} =
+  // kb e^{b_last - b_e} (global); kb C_w is checked for overflow ----
   float qv[NT][4], kv[NT][4];
 #pragma unroll
   for (int rt = 0; rt < NT; ++rt) {
@@ -291,24 +317,26 @@ __global__ __launch_bounds__(256) void k2a_gla_chunk(const K2Params P) {
     char* krow = ks + p * G::KROW + 16 * lg;
 #pragma unroll
     for (int rt = 0; rt < NT; ++rt) {
-      float f4[4], e1[4], e2[4], qo[4], kside[4], kt[4];
+      float f4[4], t4[4], e1[4], e2[4], cw[4], qo[4], kb[4], kt[4];
       unpack16<float>(ld16(first + w * DK + 16 * rt + 4 * lg), f4);
+      unpack16<float>(ld16(tot + w * DK + 16 * rt + 4 * lg), t4);
       unpack16<float>(ld16(Ew + 16 * rt + 4 * lg), e1);
       unpack16<float>(ld16(Ew + DK + 16 * rt + 4 * lg), e2);
+      unpack16<float>(ld16(Ew + 2 * DK + 16 * rt + 4 * lg), cw);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float d = x[rt][i] - f4[i];
-        const float qs = qv[rt][i] * P.q_scale * exp2_fast(d);  // <= |q|
+        const float qs = qv[rt][i] * P.q_scale * exp2_fast(x[rt][i] - f4[i]);  // <= |q|
         qv[rt][i] = qs;
         qo[i] = qs * e1[i];
-        kside[i] = kv[rt][i] * exp2_fast(-d);  // growth < 16 positions
-        kt[i] = kside[i] * e2[i];
+        kb[i] = kv[rt][i] * exp2_fast(t4[i] - x[rt][i]);  // <= |k|
+        kt[i] = kb[i] * e2[i];
+        exact_diag |= __builtin_isinf(kb[i] * cw[i]);
       }
       if constexpr (G::BF)
         st8(qtg + 16 * rt, pack8<T>(qo));
       else
         st16(qtg + 16 * rt, pack16<T>(qo));
-      st16(krow + 64 * rt, pack16<float>(kside));
+      st16(krow + 64 * rt, pack16<float>(kb));
       // kT[c][t]: neighbouring lanes (positions p, p ^ 1) swap one value so that
       // the even lane stores channel c at (p, p + 1) and the odd lane channel
       // c + 1 at (p - 1, p), two consecutive elements per store
@@ -324,6 +352,8 @@ __global__ __launch_bounds__(256) void k2a_gla_chunk(const K2Params P) {
       }
     }
   }
+
+  const bool exact = __builtin_amdgcn_ballot_w64(exact_diag) != 0;
   lds_barrier();  // key side in LDS; the qt, kT stores drain meanwhile
 
   // ---- A[w][J] for J <= w (zero blocks above the diagonal) ----
@@ -346,23 +376,24 @@ __global__ __launch_bounds__(256) void k2a_gla_chunk(const K2Params P) {
     }
 #pragma unroll
     for (int J = 0; J < NW; ++J) {
+      if (J == w && exact) continue;  // formed pair by pair below
       float out[4] = {0.f, 0.f, 0.f, 0.f};
       if (J <= w) {
         const char* krow = ks + (16 * J + lr) * G::KROW + 16 * lg;
+        // the key side (referenced at the end of tile J) moved onto this wave's
+        // first position: D_wJ <= 1 for J < w, the bounded C_w for J = w
+        const float* fac = J < w ? Dw + J * DK : Ew + 2 * DK;
         f32x4 acc = zero4();
         if constexpr (G::BF) {
 #pragma unroll
           for (int rp = 0; rp < NP; ++rp) {
-            float k8[8];
+            float k8[8], d8[8];
             unpack16<float>(ld16(krow + 64 * (2 * rp)), k8);
             unpack16<float>(ld16(krow + 64 * (2 * rp + 1)), k8 + 4);
-            if (J < w) {  // key side re-referenced to this wave's first position
-              float d8[8];
-              unpack16<float>(ld16(Dw + J * DK + 16 * (2 * rp) + 4 * lg), d8);
-              unpack16<float>(ld16(Dw + J * DK + 16 * (2 * rp + 1) + 4 * lg), d8 + 4);
+            unpack16<float>(ld16(fac + 16 * (2 * rp) + 4 * lg), d8);
+            unpack16<float>(ld16(fac + 16 * (2 * rp + 1) + 4 * lg), d8 + 4);
 #pragma unroll
-              for (int i = 0; i < 8; ++i) k8[i] *= d8[i];
-            }
+            for (int i = 0; i < 8; ++i) k8[i] *= d8[i];
             u32x4 kh, kl;
             split_bf16(k8, kh, kl);
             acc = mma_slab<bf16>(kh, qh[rp], acc);
@@ -372,16 +403,12 @@ __global__ __launch_bounds__(256) void k2a_gla_chunk(const K2Params P) {
         } else {
 #pragma unroll
           for (int rt = 0; rt < NT; ++rt) {
-            u32x4 kf = ld16(krow + 64 * rt);
-            if (J < w) {  // key side re-referenced to this wave's first position
-              float k4[4], d4[4];
-              unpack16<float>(kf, k4);
-              unpack16<float>(ld16(Dw + J * DK + 16 * rt + 4 * lg), d4);
+            float k4[4], d4[4];
+            unpack16<float>(ld16(krow + 64 * rt), k4);
+            unpack16<float>(ld16(fac + 16 * rt + 4 * lg), d4);
 #pragma unroll
-              for (int i = 0; i < 4; ++i) k4[i] *= d4[i];
-              kf = pack16<float>(k4);
-            }
-            acc = mma_slab<float>(kf, pack16<float>(qv[rt]), acc);
+            for (int i = 0; i < 4; ++i) k4[i] *= d4[i];
+            acc = mma_slab<float>(pack16<float>(k4), pack16<float>(qv[rt]), acc);
           }
         }
         // acc[e] = A[16 w + lr][16 J + 4 lg + e]; causal mask on the diagonal block
@@ -392,6 +419,63 @@ __global__ __launch_bounds__(256) void k2a_gla_chunk(const K2Params P) {
         st8(Ag + 16 * J, pack8<T>(out));
       else
         st16(Ag + 16 * J, pack16<T>(out));
+    }
+
+    // ---- exact diagonal block (wave-uniform): A[t][t - dl] = sum_c q_tc k_(t-dl)c
+    // prod_{u = t-dl+1..t} alpha_uc for dl = 0..15, every factor <= 1.  Each lane
+    // sums over its own channels (row shifts bring the earlier positions' key
+    // and per-step decay, alpha_t = 2^{x_t - x_(t-1)}, of the same channels),
+    // then the four lanes holding a position's channels add their sums.  The
+    // gate and its scan are formed again, one channel tile at a time (W_g2 from
+    // global memory: its LDS copy is gone), so nothing stays live across the
+    // blocks above and the channel loop need not unroll ----
+    if (exact) {
+      float gx[RP / 4];
+      load_gate_factor(gx);
+      float part[16];
+#pragma unroll
+      for (int dl = 0; dl < 16; ++dl) part[dl] = 0.f;
+      const float* qg = Bb.q + (seq_row + pl) * DK + 4 * lg;
+      const float* kg = Bb.k + (seq_row + pl) * DK + 4 * lg;
+#pragma unroll 1
+      for (int rt = 0; rt < NT; ++rt) {
+        float x4[4], q4[4], k4[4];
+        gate_scan(gx, Bb.W2 + hh * DK + lr, hdk, Bb.bg + hh * DK, rt, x4);
+        unpack16<float>(live ? ld16(qg + 16 * rt) : zero16(), q4);
+        unpack16<float>(live ? ld16(kg + 16 * rt) : zero16(), k4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float qc = q4[i] * P.q_scale;
+          float kc = k4[i];
+          float ac = exp2_fast(x4[i] - dpp_f<0x111>(x4[i]));  // row_shr 1 (0 before the tile)
+          float pr = 1.f;
+          part[0] += qc * kc;
+#pragma unroll
+          for (int dl = 1; dl < 16; ++dl) {
+            kc = dpp_f<0x111>(kc);  // key of position t - dl (0 before the tile)
+            pr *= ac;               // prod of alpha over t-dl+1 .. t
+            ac = dpp_f<0x111>(ac);
+            part[dl] += (qc * pr) * kc;
+          }
+        }
+      }
+#pragma unroll
+      for (int dl = 0; dl < 16; ++dl) {
+        part[dl] += __shfl_xor(part[dl], 16);
+        part[dl] += __shfl_xor(part[dl], 32);
+      }
+      float out[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int dl = lr - 4 * lg - e;  // key 16w + 4 lg + e of query 16w + lr
+        out[e] = 0.f;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) out[e] = dl == j ? part[j] : out[e];
+      }
+      if constexpr (G::BF)
+        st8(Ag + 16 * w, pack8<T>(out));
+      else
+        st16(Ag + 16 * w, pack16<T>(out));
     }
   }
 }
