@@ -279,6 +279,35 @@ def measure_routing(cfg, W, L=32768, steps=50, warmup=10):
             "percent_by_region": regions}
 
 
+def settle_clocks(layer, x, batch=20, tol=0.01, max_s=3.0):
+    """Runs forwards in batches of `batch` until the mean time of a batch is
+    within `tol` of the previous one (the shader clock settles under load;
+    the first forwards after a pause run a few percent slow), at most max_s
+    seconds.  Independent of --warmup.  Returns what it took."""
+    import torch
+    B, L, _ = x.shape
+    out = layer.new_output(B, L)
+    t_start = time.perf_counter()
+    prev, n, means = None, 0, []
+    while True:
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(batch):
+            layer.forward(x, out=out)
+        torch.cuda.synchronize()
+        mean = (time.perf_counter() - t0) / batch
+        n += batch
+        means.append(mean)
+        if prev is not None and abs(mean - prev) <= tol * prev:
+            break
+        if time.perf_counter() - t_start >= max_s:
+            break
+        prev = mean
+    return {"forwards": n, "seconds": round(time.perf_counter() - t_start, 3),
+            "last_batch_us": round(means[-1] * 1e6, 2),
+            "first_batch_us": round(means[0] * 1e6, 2)}
+
+
 def time_forward(layer, x, steps, warmup, per_kernel=True):
     """Mean ms per forward over `steps` back-to-back forwards (no events inside
     the forwards), then, if per_kernel, mean ms per kernel from a second pass
@@ -351,28 +380,57 @@ def traffic_from_profile(kernel: str, workload: str):
     return rec.get("hbm_bytes_per_dispatch")
 
 
-def cpu_baseline(cfg, X, W, min_s=10.0, max_s=30.0):
-    """The oracle as it stands, one sequence at a time, cycling over the batch
-    until at least min_s seconds of work (stopping early past max_s)."""
+def cpu_worker(workload: str, first: int, stride: int, min_s: float):
+    """One single-threaded worker of the CPU baseline: the oracle on sequences
+    first, first + stride, ... of the workload's seeded batch (cycling) until
+    min_s seconds of oracle work; prints {"tokens", "seconds"}."""
     from oracle import msgla_oracle as orc
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = 1
+    from scale_gla_layer_amd.config import WORKLOADS
+    from scale_gla_layer_amd.synth import make_inputs
+    wl = WORKLOADS[workload]
+    X, W = make_inputs(wl.cfg, wl.batch, wl.seq_len, seed=0, gate_bias=wl.gate_bias)
     B, L, _ = X.shape
-    done, t0 = 0, time.perf_counter()
-    while True:
-        orc.layer_forward(X[done % B: done % B + 1], W, cfg)
-        done += 1
-        el = time.perf_counter() - t0
-        if el >= min_s or el >= max_s:
-            break
-    dt = time.perf_counter() - t0
-    return {"value": done * L / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{done} sequence forwards of {L} tokens, cycling over the {B} sequences of "
-                      f"the same workload ({dt:.1f} s; fp64 NumPy, token-by-token recurrence; "
-                      f"BLAS threads {threads}, the recurrence loop itself is single-threaded)"}
+    done, k, t0 = 0, first, time.perf_counter()
+    while time.perf_counter() - t0 < min_s:
+        b = k % B
+        orc.layer_forward(X[b: b + 1], W, wl.cfg)
+        done += L
+        k += stride
+    print(json.dumps({"tokens": done, "seconds": time.perf_counter() - t0}), flush=True)
+
+
+def cpu_baseline(workload: str, min_s: float = 10.0):
+    """The oracle as it stands, on the host's cores: one single-threaded
+    process per core (BLAS limited to one thread), each cycling over the
+    workload's sequences until min_s seconds of work; tokens/s = all tokens
+    over the longest worker's oracle time (input generation excluded)."""
+    import subprocess
+    from scale_gla_layer_amd.config import WORKLOADS
+    L = WORKLOADS[workload].seq_len
+    cores = max(1, min(16, len(os.sched_getaffinity(0))))
+    env = dict(os.environ, OMP_NUM_THREADS="1", OPENBLAS_NUM_THREADS="1", MKL_NUM_THREADS="1",
+               BLIS_NUM_THREADS="1")
+    procs = [subprocess.Popen([sys.executable, os.path.abspath(__file__), "--cpu-worker",
+                               workload, str(i), str(cores), str(min_s)],
+                              stdout=subprocess.PIPE, env=env, text=True) for i in range(cores)]
+    res = []
+    for p in procs:
+        outp, _ = p.communicate(timeout=600)
+        if p.returncode != 0:
+            raise RuntimeError(f"CPU baseline worker failed ({p.returncode})")
+        res.append(json.loads(outp.strip().splitlines()[-1]))
+    tokens = sum(r["tokens"] for r in res)
+    secs = max(r["seconds"] for r in res)
+    model = ""
+    try:
+        with open("/proc/cpuinfo", encoding="utf-8") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:
+        pass
+    return {"value": tokens / secs, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{tokens // L} sequence forwards of {L} tokens of the {workload} "
+                      f"workload over {cores} single-threaded processes ({secs:.1f} s each; fp64 "
+                      f"NumPy, token-by-token recurrence; {model})"}
 
 
 PROFILE_COMMANDS = {
@@ -542,7 +600,17 @@ def main():
                     help="only run the plain-copy reference kernel for counter scaling")
     ap.add_argument("--summarize-profiles", metavar="DIR",
                     help="write profiles/ summaries from rocprofv3 output under DIR (no GPU)")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="skip the other workloads' forward lines (GLA, long, sweeps)")
+    ap.add_argument("--only-decode", action="store_true",
+                    help="time only the streaming decode step and print its JSON")
+    ap.add_argument("--cpu-worker", nargs=4, metavar=("WORKLOAD", "FIRST", "STRIDE", "SECONDS"),
+                    help=argparse.SUPPRESS)
     args = ap.parse_args()
+    if args.cpu_worker:
+        w, first, stride, secs = args.cpu_worker
+        cpu_worker(w, int(first), int(stride), float(secs))
+        return
     if args.summarize_profiles:
         summarize_profiles(args.summarize_profiles, args.workload)
         return
@@ -552,6 +620,11 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.only_decode:
+        dec = measure_decode()
+        log(f"[bench] decode {dec['workload']} B={dec['batch']}: {dec['us_per_step']} us/step")
+        print(json.dumps(dec), flush=True)
         return
 
     import torch  # noqa: F401
@@ -566,6 +639,9 @@ def main():
     X, W = make_inputs(cfg, B, L, seed=0, gate_bias=wl.gate_bias)
     layer = DeviceLayer(cfg, W)
     x = to_device(X, cfg.dtype)
+    settle = settle_clocks(layer, x)
+    log(f"[bench] clocks settled after {settle['forwards']} forwards ({settle['seconds']} s): "
+        f"{settle['first_batch_us']} -> {settle['last_batch_us']} us")
     ms, stage_ms = time_forward(layer, x, args.steps, args.warmup)
     tok_s = B * L / (ms * 1e-3)
     log(f"[bench] {ms * 1e3:.1f} us/step, {tok_s / 1e6:.1f} M tokens/s; kernels (us, event pass): " +
@@ -619,19 +695,43 @@ def main():
             f"{routing['us_per_call']} us ({routing['hbm_gb_s']} GB/s); percent by region "
             f"{routing['percent_by_region']}")
 
+    def workload_line(name, steps):
+        """Another workload's forward, timed like the headline: tokens/s and the
+        layer roofline fraction."""
+        owl = WORKLOADS[name]
+        Xo, Wo = make_inputs(owl.cfg, owl.batch, owl.seq_len, seed=0, gate_bias=owl.gate_bias)
+        olayer = DeviceLayer(owl.cfg, Wo)
+        xo = to_device(Xo, owl.cfg.dtype)
+        settle_clocks(olayer, xo, max_s=1.0)
+        oms, _ = time_forward(olayer, xo, steps, max(5, steps // 4), per_kernel=False)
+        oalg = algorithmic(owl.cfg, owl.batch, owl.seq_len)
+        opeak = PEAK["bf16_mfma_tflops"] if owl.cfg.dtype == "bf16" else PEAK["fp32_mfma_tflops"]
+        oroof = max(oalg["flops"] / (opeak * 1e12), oalg["bytes"] / (PEAK["hbm_gbs"] * 1e9))
+        del olayer, xo
+        return {"batch": owl.batch, "seq_len": owl.seq_len, "scales": list(owl.cfg.scales),
+                "heads": list(owl.cfg.heads), "us_per_step": round(oms * 1e3, 2),
+                "tokens_per_s": round(owl.batch * owl.seq_len / (oms * 1e-3), 1),
+                "algorithmic_gflop": round(oalg["flops"] / 1e9, 2),
+                "t_roof_us": round(oroof * 1e6, 2), "layer_roofline_frac": round(oroof / (oms * 1e-3), 4)}
+
     ratio_vs_gla = None
     gla = None
+    others = {}
     if not args.no_gla and args.workload != "gla_baseline":
-        gwl = WORKLOADS["gla_baseline"]
-        Xg, Wg = make_inputs(gwl.cfg, gwl.batch, gwl.seq_len, seed=0)
-        glayer = DeviceLayer(gwl.cfg, Wg)
-        xg = to_device(Xg, gwl.cfg.dtype)
-        gms, _ = time_forward(glayer, xg, args.steps, args.warmup, per_kernel=False)
-        gla = gwl.batch * gwl.seq_len / (gms * 1e-3)
+        others["gla_baseline"] = workload_line("gla_baseline", args.steps)
+        gla = others["gla_baseline"]["tokens_per_s"]
         ratio_vs_gla = tok_s / gla
-        log(f"[bench] GLA baseline {gms * 1e3:.1f} us/step, {gla / 1e6:.1f} M tokens/s; "
+        log(f"[bench] GLA baseline {others['gla_baseline']['us_per_step']} us/step, {gla / 1e6:.1f} M "
+            f"tokens/s ({others['gla_baseline']['layer_roofline_frac']} of its roofline); "
             f"ratio {ratio_vs_gla:.3f}")
-        del glayer, xg
+    if not args.no_workloads:
+        for name in ("long", "sweep_1248", "sweep_24"):
+            if name == args.workload:
+                continue
+            others[name] = workload_line(name, min(args.steps, 100))
+            o = others[name]
+            log(f"[bench] {name}: {o['us_per_step']} us/step, {o['tokens_per_s'] / 1e6:.1f} M tokens/s, "
+                f"{o['layer_roofline_frac']} of its layer roofline ({o['t_roof_us']} us)")
 
     dec = None
     if not args.no_decode:
@@ -644,7 +744,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] timing the fp64 CPU oracle on the host ...")
-        cpu = cpu_baseline(cfg, X, W)
+        cpu = cpu_baseline(wl.name)
         log(f"[bench] oracle {cpu['value']:.0f} tokens/s ({cpu['sample']})")
 
     line = {
@@ -670,8 +770,11 @@ def main():
                            "t_roof_us": round(t_roof * 1e6, 2),
                            "frac": round(t_roof / (ms * 1e-3), 4)},
         "kernels": stages,
+        "settle": settle,
         "per_call_us": warm,
         "per_call_cold_mall_us": cold,
+        "cold_mall_tokens_per_s": None if cold is None else round(B * L / (cold["p50"] * 1e-6), 1),
+        "workloads": others,
         "ratio_vs_gla": None if ratio_vs_gla is None else round(ratio_vs_gla, 4),
         "gla_tokens_per_s": None if gla is None else round(gla, 1),
         "decode": dec,

@@ -17,9 +17,15 @@
  *  - All tensor pointers are DEVICE pointers unless stated otherwise, row-major,
  *    16-byte aligned.  The caller owns every buffer (inputs, outputs, packed
  *    weights, workspace, state); the library allocates nothing, keeps no
- *    global state and never synchronises: work is enqueued on `stream` (a
- *    hipStream_t; NULL = the null stream) and completes asynchronously.
- *    Calls with distinct workspaces may run concurrently.
+ *    global state and, except msgla_state_query, never synchronises: work is
+ *    enqueued on `stream` (a hipStream_t; NULL = the null stream) and
+ *    completes asynchronously.  Calls with distinct workspaces may run
+ *    concurrently.
+ *  - Weights reach msgla_forward and msgla_decode_step as ONE packed device
+ *    blob (msgla_pack_weights, once per set of weights), not as the struct of
+ *    per-matrix pointers (msgla_weights) that the packing reads: the blob holds
+ *    them transposed and concatenated in the order the kernels stream them,
+ *    so no call re-lays out a weight.
  *  - Errors in arguments are detected on the host before anything is enqueued
  *    and are returned synchronously; a failed kernel launch returns
  *    MSGLA_ERR_HIP.  NaN and Inf in the data are not checked; they propagate.
@@ -174,9 +180,15 @@ msgla_status msgla_state_init(const msgla_config* cfg, int64_t B, void* state, s
  *         states seed the recurrences and its held outputs fill the
  *         positions before each coarse branch's first block of this call.
  *         Its position must be a multiple of every scale (no block in
- *         progress; MSGLA_ERR_UNSUPPORTED otherwise), and a header that does
- *         not match the config or B gives MSGLA_ERR_INVALID_ARG.  Reading the
- *         header synchronises `stream` once.  state_in may equal state_out.
+ *         progress).  Its header is checked on the device, in stream order
+ *         (the call does not synchronise and can be captured in a graph):
+ *         when it does not describe this config and B, records an error, or
+ *         sits inside a block, nothing past the header is read, every element
+ *         of out is NaN, and state_out (if given) records the error
+ *         (MSGLA_ERR_INVALID_ARG, or MSGLA_ERR_UNSUPPORTED for a position
+ *         inside a block) with position -1; msgla_state_query reads it.  The
+ *         call itself then still returns MSGLA_OK.  state_in may equal
+ *         state_out.
  *   state_out: NULL, or a buffer of msgla_state_bytes(cfg, B) that receives
  *         the streaming state after the L tokens (for msgla_decode_step).
  *   workspace: >= msgla_workspace_bytes(cfg, B, L) bytes of device memory;
@@ -223,6 +235,25 @@ msgla_status msgla_forward_timed(const msgla_config* cfg, const void* packed, co
  */
 msgla_status msgla_fusion_weights(const msgla_config* cfg, const void* packed, const void* x,
                                   int64_t B, int64_t L, float* w_out, void* stream);
+
+/*
+ * What a state's header records (msgla_state_query).  status is MSGLA_OK for
+ * a usable state, else the error of the forward that wrote it (a state_in it
+ * could not continue from; position is then -1).
+ */
+typedef struct {
+  int32_t status;   /* msgla_status */
+  int32_t B;        /* batch the state was written for */
+  int32_t m;        /* branches */
+  int64_t position; /* tokens consumed, or -1 */
+} msgla_state_info;
+
+/*
+ * Reads the header of `state` (device) after the work already enqueued on
+ * `stream`: this call waits for that work (the only call that synchronises).
+ * Returns MSGLA_ERR_INVALID_ARG if `state` does not hold a state header.
+ */
+msgla_status msgla_state_query(const void* state, msgla_state_info* info, void* stream);
 
 /* Device workspace needed by msgla_decode_step for batch B (bytes). */
 size_t msgla_decode_workspace_bytes(const msgla_config* cfg, int64_t B);

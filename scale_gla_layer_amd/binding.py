@@ -26,7 +26,7 @@ SYMBOLS = (
     "msgla_status_str", "msgla_validate_config", "msgla_packed_weights_bytes",
     "msgla_pack_weights", "msgla_workspace_bytes", "msgla_state_bytes", "msgla_state_init",
     "msgla_forward", "msgla_forward_timed", "msgla_decode_workspace_bytes", "msgla_decode_step",
-    "msgla_fusion_weights",
+    "msgla_fusion_weights", "msgla_state_query",
 )
 
 
@@ -63,6 +63,11 @@ class CWeights(ctypes.Structure):
                 ("b_f", ctypes.c_void_p)]
 
 
+class CStateInfo(ctypes.Structure):
+    _fields_ = [("status", ctypes.c_int32), ("B", ctypes.c_int32), ("m", ctypes.c_int32),
+                ("position", ctypes.c_int64)]
+
+
 class CStageEvents(ctypes.Structure):
     _fields_ = [("start", ctypes.c_void_p * N_STAGES), ("stop", ctypes.c_void_p * N_STAGES)]
 
@@ -95,6 +100,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "msgla_decode_workspace_bytes": (sz, [cfgp, i64]),
         "msgla_decode_step": (ctypes.c_int, [cfgp, vp, vp, i64, vp, vp, vp, sz, vp]),
         "msgla_fusion_weights": (ctypes.c_int, [cfgp, vp, vp, i64, i64, vp, vp]),
+        "msgla_state_query": (ctypes.c_int, [vp, ctypes.POINTER(CStateInfo), vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -219,3 +225,13 @@ def msgla_fusion_weights(cfg: MsglaConfig, packed, x, B: int, L: int, w_out, str
     st = load_library().msgla_fusion_weights(ctypes.byref(c_config(cfg)), _ptr(packed), _ptr(x), B, L,
                                              _ptr(w_out), _stream(stream))
     _check("msgla_fusion_weights", st)
+
+
+def msgla_state_query(state, stream=None) -> dict:
+    """The state's header: {"status", "B", "m", "position"} (waits for the stream)."""
+    info = CStateInfo()
+    st = load_library().msgla_state_query(_ptr(state), ctypes.byref(info), _stream(stream))
+    _check("msgla_state_query", st)
+    return {"status": int(info.status), "B": int(info.B), "m": int(info.m),
+            "position": int(info.position)}
+

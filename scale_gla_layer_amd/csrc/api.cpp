@@ -1,6 +1,7 @@
 // Host side of the C ABI declared in include/msgla.h: validation, the packed /
 // workspace / state layouts, and the launch sequence of the forward and the
-// decode step.  No allocation, no synchronisation, no global state.
+// decode step.  No allocation, no global state, and no synchronisation except
+// in msgla_state_query, which exists to read a state's header on the host.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -19,7 +20,9 @@ hipError_t launch_k2b(const K2Params& P, bool bf16_path, hipStream_t stream);
 hipError_t launch_k3c(const K3Params& P, bool bf16_path, hipStream_t stream);
 hipError_t launch_k3f(const K3Params& P, bool bf16_path, hipStream_t stream);
 hipError_t launch_state_export(const StateParams& P, bool bf16_path, hipStream_t st);
-hipError_t launch_state_header(void* state, int B, int m, int64_t pos, hipStream_t st);
+hipError_t launch_state_header(void* state, int B, int m, int64_t pos, const StateCheck* chk,
+                               hipStream_t st);
+hipError_t launch_state_check(const StateCheckParams& P, hipStream_t st);
 hipError_t launch_decode(const DecParams& P, int Nmax, int hmax, bool bf16_path, hipStream_t st);
 hipError_t launch_norm(const NormParams& P, bool bf16_path, hipStream_t st);
 hipError_t pack_transpose(bool bf16_path, const void* src, int R, int Cn, void* dst,
@@ -145,11 +148,11 @@ PackGeom pack_geom(const msgla_config* c) {
 // forward workspace
 struct WsBranch {
   int n, nch, np;
-  size_t xp, q, k, qt, kT, vT, g, A, lam, y;
+  size_t xp, xp_lo, q, k, qt, kT, vT, g, A, lam, y;
 };
 struct WsGeom {
   WsBranch br[MSGLA_MAX_BRANCHES];
-  size_t w, total;
+  size_t w, chk, total;
   int nseg;        // segments of the chunk-state walk (1: one walk per sequence)
   int seg_base;    // workgroups of one segment
   size_t Sseg;     // segment states, when nseg > 1
@@ -171,6 +174,8 @@ WsGeom ws_geom(const PackGeom& g, int64_t B, int64_t L) {
     b.np = b.nch * g.C;
     const size_t rows = (size_t)B * bg.h * b.np;
     b.xp = bg.s > 1 ? take((size_t)B * b.n * g.d * g.es) : 0;  // block means
+    // their bf16 rounding residuals, which a masked call's projection adds back
+    b.xp_lo = bg.s > 1 && g.bf16 ? take((size_t)B * b.n * g.d * g.es) : 0;
     b.q = take(rows * g.dk * 4);
     b.k = take(rows * g.dk * 4);
     b.qt = take(rows * g.dk * g.es);
@@ -182,6 +187,7 @@ WsGeom ws_geom(const PackGeom& g, int64_t B, int64_t L) {
     b.y = take(rows * g.dv * g.es);
   }
   w.w = take((size_t)B * L * FUSION_STRIDE * 4);
+  w.chk = take(sizeof(StateCheck));  // the device-side check of state_in
   // The chunk-state walk runs one workgroup per (sequence, 32-wide d_v slice).
   // With few of them (small batches of long sequences) the sequential walk over
   // the chunks leaves most CUs idle, so each walk is cut into segments (at least
@@ -348,7 +354,21 @@ msgla_status msgla_state_init(const msgla_config* cfg, int64_t B, void* state, s
   if (state_bytes < s.total) return MSGLA_ERR_WORKSPACE;
   hipStream_t st = static_cast<hipStream_t>(stream);
   HIP_TRY(fill_zero(state, s.total, st));
-  HIP_TRY(launch_state_header(state, (int)B, g.m, 0, st));
+  HIP_TRY(launch_state_header(state, (int)B, g.m, 0, nullptr, st));
+  return MSGLA_OK;
+}
+
+msgla_status msgla_state_query(const void* state, msgla_state_info* info, void* stream) {
+  if (!state || !info || !aligned16(state)) return MSGLA_ERR_INVALID_ARG;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  StateHeader h{};
+  HIP_TRY(hipMemcpyAsync(&h, state, sizeof h, hipMemcpyDeviceToHost, st));
+  HIP_TRY(hipStreamSynchronize(st));
+  if (h.magic != STATE_MAGIC || h.version != STATE_VERSION) return MSGLA_ERR_INVALID_ARG;
+  info->status = h.status;
+  info->B = h.B;
+  info->m = h.m;
+  info->position = h.pos;
   return MSGLA_OK;
 }
 
@@ -370,19 +390,20 @@ msgla_status msgla_forward_timed(const msgla_config* cfg, const void* packed, co
   if (workspace_bytes < W.total) return MSGLA_ERR_WORKSPACE;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const StGeom S = st_geom(g, B);
-  // Continuing from a state: its header (read once, in stream order) must
-  // describe this batch and a position at a block boundary of every branch,
-  // so that the blocks of this call start at its first token.
-  int64_t pos_in = 0;
+  // Continuing from a state: its header is checked on the device (this
+  // configuration and batch, a position at a block boundary of every branch,
+  // so that the blocks of this call start at its first token); every kernel
+  // that reads the state reads it only if the check passed.
+  const StateCheck* chk = nullptr;
   if (state_in) {
-    StateHeader h{};
-    HIP_TRY(hipMemcpyAsync(&h, state_in, sizeof h, hipMemcpyDeviceToHost, st));
-    HIP_TRY(hipStreamSynchronize(st));
-    if (h.magic != STATE_MAGIC || h.version != STATE_VERSION || h.B != B || h.m != g.m || h.pos < 0)
-      return MSGLA_ERR_INVALID_ARG;
-    for (int i = 0; i < g.m; ++i)
-      if (h.pos % g.br[i].s != 0) return MSGLA_ERR_UNSUPPORTED;
-    pos_in = h.pos;
+    StateCheckParams pc{};
+    pc.state_in = state_in;
+    pc.out = at<StateCheck>(workspace, W.chk);
+    pc.B = (int)B;
+    pc.m = g.m;
+    for (int i = 0; i < g.m; ++i) pc.scale[i] = g.br[i].s;
+    HIP_TRY(launch_state_check(pc, st));
+    chk = pc.out;
   }
 
   auto ev = [&](int stage, bool start) -> hipError_t {
@@ -407,6 +428,7 @@ msgla_status msgla_forward_timed(const msgla_config* cfg, const void* packed, co
     K1Group& G = p1.g[ng++];
     G.Wp = at<char>(packed, b.off_Wp);
     G.A = b.s == 1 ? x : static_cast<const void*>(at<char>(workspace, wb.xp));
+    G.A_lo = (mask && b.s > 1 && g.bf16) ? static_cast<const void*>(at<char>(workspace, wb.xp_lo)) : nullptr;
     G.s = b.s;
     G.n = wb.n;
     G.M = (int)B * wb.n;
@@ -517,6 +539,7 @@ msgla_status msgla_forward_timed(const msgla_config* cfg, const void* packed, co
   p2.nseg = W.nseg;
   p2.seg_base = W.seg_base;
   p2.Sseg = W.nseg > 1 ? at<float>(workspace, W.Sseg) : nullptr;
+  p2.chk = chk;
 
   // ---------------- K3 ----------------
   // coarse outputs Y = y W_o reuse the block-mean buffers of their branch
@@ -563,6 +586,7 @@ msgla_status msgla_forward_timed(const msgla_config* cfg, const void* packed, co
     }
   }
   p3.held_in = state_in != nullptr;
+  p3.chk = chk;
   p3.c_total = ctiles;
   p3.c_per_xcd = cdiv(ctiles, N_XCD);
   p3.f_total = cdiv((int)(B * L), GEMM_TILE) * p3.tiles_n;
@@ -592,6 +616,7 @@ msgla_status msgla_forward_timed(const msgla_config* cfg, const void* packed, co
         if (done[i] || s <= 1 || W.br[i].n == 0 || smax % s != 0) continue;
         PoolOut& o = q.out[q.nout++];
         o.xp = at<char>(workspace, W.br[i].xp);
+        o.xp_lo = (mask && g.bf16) ? at<char>(workspace, W.br[i].xp_lo) : nullptr;
         o.s = s;
         o.n = W.br[i].n;
         o.inv_s = 1.0f / (float)s;
@@ -647,7 +672,8 @@ msgla_status msgla_forward_timed(const msgla_config* cfg, const void* packed, co
     ps.dv = g.dv;
     ps.m = g.m;
     ps.Ktot = g.Ktot;
-    ps.pos = pos_in + L;
+    ps.pos = L;
+    ps.chk = chk;
     ps.x = x;
     ps.WoT = p3.WoT;
     ps.state = state_out;

@@ -133,6 +133,10 @@ __device__ __forceinline__ int remap_xcd(int bid, int per_xcd) {
   return (bid % N_XCD) * per_xcd + bid / N_XCD;
 }
 
+// True when a forward may read its state_in (no entry state, or its header
+// passed the device-side check).
+__device__ __forceinline__ bool state_in_ok(const StateCheck* chk) { return !chk || chk->status == 0; }
+
 // Numerically safe log(sigmoid(z)) = min(z, 0) - log1p(exp(-|z|)).
 __device__ __forceinline__ float logsigmoid_f(float z) {
   return fminf(z, 0.f) - log1pf(__expf(-fabsf(z)));

@@ -5,9 +5,11 @@
 // o = q S, and the held output is replaced; the branches are fused with
 // softmax weights from the unpooled token, Eqs. (10)-(11)).
 //
-// Three launches per token, all enqueued without host synchronisation; each
-// kernel reads the token count from the state header on the device and a
-// branch whose block is not complete skips its work:
+// Three launches per token, all enqueued without host synchronisation; the
+// first kernel reads the token count from the state header on the device
+// (checking that the header describes this configuration and batch; otherwise
+// the step changes nothing and outputs NaN), and a branch whose block is not
+// complete skips its work:
 //   D1 proj:   [q | k | v | g] = xp Wp^T for completing branches, where the
 //              pooled row xp = (pending sum + x_t) / s is formed as the MFMA
 //              operand is loaded, plus the fusion logits x_t W_f
@@ -23,8 +25,14 @@ namespace msgla {
 
 constexpr int DEC_THREADS = 256;
 
-__device__ __forceinline__ int64_t dec_pos(const void* state) {
-  return reinterpret_cast<const StateHeader*>(state)->pos;
+// The step's position from the state header, or -1 when the header does not
+// describe this configuration and batch or records an error: the step then
+// changes nothing and its output is NaN.
+__device__ __forceinline__ int64_t dec_pos(const DecParams& P) {
+  const StateHeader* h = reinterpret_cast<const StateHeader*>(P.state);
+  const bool ok = h->magic == STATE_MAGIC && h->version == STATE_VERSION && h->B == P.B &&
+                  h->m == P.m && h->status == 0 && h->pos >= 0;
+  return ok ? h->pos : -1;
 }
 __device__ __forceinline__ bool completes(int64_t pos, int s) { return ((pos + 1) % s) == 0; }
 
@@ -105,9 +113,10 @@ __device__ __forceinline__ f32x4 dec_reduce4(f32x4 acc, float* red, int wave, in
 // the four waves take a quarter of K each
 template <typename T>
 __global__ __launch_bounds__(DEC_THREADS) void k_dec_proj(const DecParams P) {
-  const int64_t pos = dec_pos(P.state);
+  const int64_t pos = dec_pos(P);
   if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x == 0)
-    *P.pos_ws = pos;  // this step's position, for the output kernel
+    *P.pos_ws = pos;  // this step's position, for the later kernels
+  if (pos < 0) return;
   const bool logits = blockIdx.y == P.nbranch;
   if (logits && P.m == 1) return;
   const DecBranch& Br = P.br[logits ? 0 : blockIdx.y];
@@ -149,7 +158,8 @@ __global__ __launch_bounds__(DEC_THREADS) void k_dec_proj(const DecParams P) {
 // grid (B * hmax, ceil(dv / 64), m); 256 threads: lane -> v column, wave -> quarter of d_k
 __global__ __launch_bounds__(DEC_THREADS) void k_dec_state(const DecParams P) {
   const DecBranch& Br = P.br[blockIdx.z];
-  if (!completes(dec_pos(P.state), Br.s)) return;
+  const int64_t pos = *P.pos_ws;
+  if (pos < 0 || !completes(pos, Br.s)) return;
   const int bh = blockIdx.x;
   if (bh >= P.B * Br.h) return;
   const int b = bh / Br.h, hh = bh - b * Br.h;
@@ -200,7 +210,8 @@ __global__ __launch_bounds__(DEC_THREADS) void k_dec_state(const DecParams P) {
 // branch's new y row (gains and eps as in the forward), before the output kernel
 __global__ __launch_bounds__(64) void k_dec_norm(const DecParams P) {
   const DecBranch& Br = P.br[blockIdx.y];
-  if (!Br.gn || !completes(dec_pos(P.state), Br.s)) return;
+  const int64_t pos = *P.pos_ws;
+  if (!Br.gn || pos < 0 || !completes(pos, Br.s)) return;
   const int bh = blockIdx.x;
   if (bh >= P.B * Br.h) return;
   const int b = bh / Br.h, hh = bh - b * Br.h;
@@ -238,10 +249,21 @@ __global__ __launch_bounds__(DEC_THREADS) void k_dec_out(const DecParams P) {
   const int lr = lane & 15, lg = lane >> 4;
   const int n0 = blockIdx.x * 16, b0 = blockIdx.y * 16;
   const int64_t pos = *P.pos_ws;
-  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0)
-    reinterpret_cast<StateHeader*>(P.state)->pos = pos + 1;
   constexpr int PER = per16<T>();
   const int n = n0 + lr;  // d is a multiple of 64
+  if (pos < 0) {  // unusable state: NaN output, nothing else changes
+    if (wave == 0) {
+      T* out = reinterpret_cast<T*>(P.out);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int bb = b0 + 4 * lg + e;
+        if (bb < P.B) out[(size_t)bb * P.d + n] = from_f32<T>(__builtin_nanf(""));
+      }
+    }
+    return;
+  }
+  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0)
+    reinterpret_cast<StateHeader*>(P.state)->pos = pos + 1;
   // fusion weights of this lane's four sequences: the softmax's maximum and sum
   float zmax[4], zsum[4];
 #pragma unroll

@@ -98,7 +98,8 @@ __global__ __launch_bounds__(K2B_THREADS) void k2b_gla_state(const K2Params P) {
   const bool last_seg = P.nseg == 1 || seg == max(0, (Bb.nch - 1) / max(seg_len, 1));
   if (P.nseg > 1 && cnt == 0 && (SONLY || !last_seg)) return;  // the whole workgroup
   float* Sseg_slot = P.Sseg ? P.Sseg + (size_t)(qseq * P.nseg + seg) * DK * P.dv : nullptr;
-  const float* S_start = SONLY ? nullptr : (P.nseg > 1 ? Sseg_slot : (Bb.S_in ? Bb.S_in + (size_t)bh * DK * P.dv : nullptr));
+  const float* S_in = Bb.S_in && state_in_ok(P.chk) ? Bb.S_in : nullptr;
+  const float* S_start = SONLY ? nullptr : (P.nseg > 1 ? Sseg_slot : (S_in ? S_in + (size_t)bh * DK * P.dv : nullptr));
   float* S_end = SONLY ? Sseg_slot : (last_seg && Bb.S_out ? Bb.S_out + (size_t)bh * DK * P.dv : nullptr);
 
   constexpr int es = G::es;
@@ -404,8 +405,9 @@ __global__ __launch_bounds__(256) void k2b_seg_scan(const K2Params P) {
     lam_seg[p] = prod;
   }
   __syncthreads();
+  const float* S_in = Bb.S_in && state_in_ok(P.chk) ? Bb.S_in : nullptr;
   for (int v = threadIdx.x; v < P.dv; v += 256) {
-    float cur = Bb.S_in ? Bb.S_in[((size_t)bh * P.dk + c) * P.dv + v] : 0.f;
+    float cur = S_in ? S_in[((size_t)bh * P.dk + c) * P.dv + v] : 0.f;
     for (int p = 0; p < P.nseg; ++p) {
       float* slot = P.Sseg + ((size_t)(qseq * P.nseg + p) * P.dk + c) * P.dv + v;
       const float loc = *slot;

@@ -178,7 +178,11 @@ struct K3Fine : K3Rows<T> {
     bool ok[U], held[U][NC > 0 ? NC : 1];
     u32x4 raw[U][NC > 0 ? NC : 1][NP];
     // every lane issues all loads of a batch (pieces outside the problem and
-    // positions before a branch's first block read a valid row and drop it)
+    // positions before a branch's first block read a valid row and drop it).
+    // Continuing from a state whose header failed its check, the entry outputs
+    // are not read (a valid word of the packed weights stands in for them)
+    // and the whole output is NaN.
+    const bool entry_ok = !HELD || state_in_ok(P.chk);
     auto gather = [&](int it_first) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
@@ -199,7 +203,7 @@ struct K3Fine : K3Rows<T> {
           // valid word of its entry output instead (dropped)
           const T* src = !HELD || Bi.n > 0
                              ? reinterpret_cast<const T*>(Bi.yc) + ((size_t)b * Bi.n + max(j, 0)) * P.d + cc
-                             : reinterpret_cast<const T*>(Bi.held_in) + cc;
+                             : (entry_ok ? reinterpret_cast<const T*>(Bi.held_in) : reinterpret_cast<const T*>(P.WoT)) + cc;
 #pragma unroll
           for (int q = 0; q < NP; ++q) raw[u][c][q] = ld16(src + q * PER);
         }
@@ -239,7 +243,7 @@ struct K3Fine : K3Rows<T> {
           float y[8];
 #pragma unroll
           for (int q = 0; q < NP; ++q) unpack16<T>(held[u][c] ? raw[u][c][q] : zero16(), y + q * PER);
-          if (HELD && !held[u][c]) {
+          if (HELD && entry_ok && !held[u][c]) {
             // before this call's first block: the output held on entry (fp32)
             const float* hp = Bi.held_in + (size_t)((this->m0 + r[u]) / P.L) * P.d + col[u];
             unpack16<float>(ld16(hp), y);
@@ -248,6 +252,9 @@ struct K3Fine : K3Rows<T> {
 #pragma unroll
           for (int e = 0; e < 8; ++e) v[e] += wi * y[e];
         }
+        if (!entry_ok)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = __builtin_nanf("");
         k3_store8(out + (size_t)(this->m0 + r[u]) * P.d + col[u], v);
       }
       it0 += U * K3Cfg::THREADS;

@@ -6,20 +6,49 @@
 // has consumed n = floor(L/s) blocks: its GLA state is written by the state
 // kernel directly; this kernel adds the sum of the L - n s pending tokens and
 // the held output Y_{n-1} = y_{n-1} W_o (zero when n = 0), and sets the token
-// count in the header.
+// count in the header.  A forward continuing from a state first checks that
+// state's header on the device (k_state_check); the readers of the entry state
+// use it only if the check passed.
 #include "device_common.hpp"
 #include "layout.hpp"
 
 namespace msgla {
 
-__global__ void k_state_header(void* state, int B, int m, int64_t pos) {
+// Header of a state written after `pos` more tokens: position = entry position
+// (from the forward's check of its state_in, else 0) + pos; a failed check
+// gives status = that check's code and position -1, which later calls reject.
+__global__ void k_state_header(void* state, int B, int m, int64_t pos, const StateCheck* chk) {
   if (threadIdx.x == 0 && blockIdx.x == 0) {
     StateHeader* h = reinterpret_cast<StateHeader*>(state);
+    const int32_t status = chk ? chk->status : 0;
     h->magic = STATE_MAGIC;
     h->version = STATE_VERSION;
     h->B = B;
     h->m = m;
-    h->pos = pos;
+    h->pos = status != 0 ? -1 : (chk ? chk->pos : 0) + pos;
+    h->status = status;
+    h->pad = 0;
+  }
+}
+
+// Check of a forward's state_in header against its configuration and batch
+// (one thread): the codes are those of msgla_status (1 = invalid argument:
+// not a state of this configuration and batch, or a state that records an
+// error; 2 = unsupported: a position inside a block of some scale).
+__global__ void k_state_check(const StateCheckParams P) {
+  if (threadIdx.x == 0 && blockIdx.x == 0) {
+    const StateHeader* h = reinterpret_cast<const StateHeader*>(P.state_in);
+    int32_t status = 0;
+    if (h->magic != STATE_MAGIC || h->version != STATE_VERSION || h->B != P.B || h->m != P.m ||
+        h->status != 0 || h->pos < 0) {
+      status = 1;
+    } else {
+      for (int i = 0; i < P.m; ++i)
+        if (h->pos % P.scale[i] != 0) status = 2;
+    }
+    P.out->status = status;
+    P.out->pad = 0;
+    P.out->pos = status == 0 ? h->pos : 0;
   }
 }
 
@@ -37,7 +66,7 @@ __global__ void k_state_export(const StateParams P) {
     Br.psum[(size_t)b * P.d + col] = s;
     // held output of the last complete block (or, without one, the output
     // held on entry)
-    float acc = Br.held_in ? Br.held_in[(size_t)b * P.d + col] : 0.f;
+    float acc = Br.held_in && state_in_ok(P.chk) ? Br.held_in[(size_t)b * P.d + col] : 0.f;
     if (Br.n > 0) {
       acc = 0.f;
       const T* y = reinterpret_cast<const T*>(Br.y);
@@ -51,7 +80,7 @@ __global__ void k_state_export(const StateParams P) {
   }
   // a branch that saw no complete block keeps its GLA state: zero, or the
   // entry state, which the state kernel has already copied to the output
-  if (Br.n == 0 && !Br.S_in) {
+  if (Br.n == 0 && !(Br.S_in && state_in_ok(P.chk))) {
     const size_t per_b = (size_t)Br.h * P.dk * P.dv;
     for (size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x; e < per_b;
          e += (size_t)gridDim.x * blockDim.x)
@@ -59,8 +88,14 @@ __global__ void k_state_export(const StateParams P) {
   }
 }
 
-hipError_t launch_state_header(void* state, int B, int m, int64_t pos, hipStream_t st) {
-  hipLaunchKernelGGL(k_state_header, dim3(1), dim3(64), 0, st, state, B, m, pos);
+hipError_t launch_state_header(void* state, int B, int m, int64_t pos, const StateCheck* chk,
+                               hipStream_t st) {
+  hipLaunchKernelGGL(k_state_header, dim3(1), dim3(64), 0, st, state, B, m, pos, chk);
+  return hipGetLastError();
+}
+
+hipError_t launch_state_check(const StateCheckParams& P, hipStream_t st) {
+  hipLaunchKernelGGL(k_state_check, dim3(1), dim3(64), 0, st, P);
   return hipGetLastError();
 }
 
@@ -71,7 +106,7 @@ hipError_t launch_state_export(const StateParams& P, bool bf16_path, hipStream_t
   else
     hipLaunchKernelGGL(k_state_export<float>, grid, dim3(256), 0, st, P);
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
-  return launch_state_header(P.state, P.B, P.m, P.pos, st);
+  return launch_state_header(P.state, P.B, P.m, P.pos, P.chk, st);
 }
 
 }  // namespace msgla

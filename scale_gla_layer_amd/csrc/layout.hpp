@@ -28,11 +28,13 @@
 //   A           [B][h][nch][C][C] T     masked decayed q k^T per chunk
 //   lam         [B][h][nch][d_k]  fp32  exp(b_last) per chunk
 //   y           [B][h][np][d_v]   T     GLA outputs o_t
+//   xp, xp_lo   [B][n][d]         T     block means of a coarse branch (s > 1) and,
+//                                       bf16 only, their residuals (masked calls)
 // plus the fusion weights w [B L][8] fp32.  Rows >= n of a chunk are never
 // written by the projection and are masked by every reader.
 //
-// State (fp32 except the header): 256-byte header {magic, version, B, m, pos},
-// then per branch S [B][h][d_k][d_v], psum [B][d], held [B][d].
+// State (fp32 except the header): 256-byte header {magic, version, B, m, pos,
+// status}, then per branch S [B][h][d_k][d_v], psum [B][d], held [B][d].
 #pragma once
 #include <stdint.h>
 #include <stddef.h>
@@ -55,11 +57,31 @@ struct StateHeader {
   int32_t B;
   int32_t m;
   int64_t pos;
+  int32_t status;   // 0, or the msgla_status of the call that wrote it (then pos = -1)
+  int32_t pad;
+};
+
+// A forward's check of its state_in header, made on the device (forward
+// workspace): status 0 if the header describes this configuration and batch
+// at a position that is a multiple of every scale; pos = that position.
+// Every kernel that reads state_in reads it only when status is 0.
+struct StateCheck {
+  int32_t status;
+  int32_t pad;
+  int64_t pos;
+};
+
+struct StateCheckParams {
+  const void* state_in;
+  StateCheck* out;
+  int B, m;
+  int scale[MSGLA_MAX_BRANCHES];
 };
 
 // ---------------- pooling prepass ------------------------------------------------
 struct PoolOut {
   void* xp;         // [B][n][d] block means of scale s
+  void* xp_lo;      // [B][n][d] bf16 residuals m - bf16(m) of the means, or null
   int s, n;
   float inv_s;
 };
@@ -83,6 +105,8 @@ struct XSeg {
 struct K1Group {
   const void* Wp;   // [N][d]: the transposed q, k and v projections (branch groups)
   const void* A;    // A rows: x (scale 1 and the small group) or the block means [M][d]
+  const void* A_lo; // residuals of the block means [M][d] (masked bf16 calls), or null:
+                    // the q / k column tiles then run K over [A | A_lo] against [W | W]
   int s;            // pooling factor
   int n;            // pooled rows per sequence
   int M;            // B * n
@@ -158,6 +182,7 @@ struct K2Params {
   int nseg;
   int seg_base;     // workgroups of one segment (the plain walk's grid)
   float* Sseg;      // [total_seqs][nseg][dk][dv] fp32: local, then start states
+  const StateCheck* chk;  // check of state_in (S_in is read only if it passed), or null
   K2Branch br[MSGLA_MAX_BRANCHES];
 };
 
@@ -180,6 +205,7 @@ struct K3Params {
   int c_total, c_per_xcd;             // coarse GEMM work list (K3c)
   int f_total, f_per_xcd;             // fine GEMM + fusion work list (K3f)
   int held_in;                        // the call continues from a state
+  const StateCheck* chk;              // its check (held_in read only if it passed), or null
   const void* zero; // >= 128 zero bytes (rows outside the problem)
   const void* WoT;  // [d][Ktot]
   const float* w;   // fusion weights [B L][8]
@@ -204,7 +230,8 @@ struct StateBranch {
 
 struct StateParams {
   int B, L, d, dk, dv, m, Ktot;
-  int64_t pos;
+  int64_t pos;      // tokens of this call (added to the entry position)
+  const StateCheck* chk;  // check of the entry state (S_in / held_in read only if it passed), or null
   const void* x;    // forward input (export only)
   const void* WoT;
   void* state;      // header

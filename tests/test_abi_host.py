@@ -185,3 +185,13 @@ def test_workspace_grows_with_batch_and_length():
     b = binding.msgla_workspace_bytes(cfg, 2, 2048)
     c = binding.msgla_workspace_bytes(cfg, 1, 4096)
     assert 0 < a < b and a < c
+
+
+def test_state_query_argument_errors_need_no_gpu():
+    """msgla_state_query rejects a NULL or misaligned state or a NULL result
+    before touching the device."""
+    lib = binding.load_library()
+    info = binding.CStateInfo()
+    assert lib.msgla_state_query(None, ctypes.byref(info), None) == 1
+    assert lib.msgla_state_query(ctypes.c_void_p(8), ctypes.byref(info), None) == 1
+    assert lib.msgla_state_query(ctypes.c_void_p(256), None, None) == 1

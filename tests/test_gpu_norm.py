@@ -36,7 +36,7 @@ def test_bf16_normalised_main_dims():
 
 def test_bf16_normalised_full_size():
     wl = WORKLOADS["main"]
-    layer_case(_n("main"), wl.batch, wl.seq_len, seed=7, batches=[1, 6])
+    layer_case(_n("main"), wl.batch, wl.seq_len, seed=7)
 
 
 @pytest.mark.parametrize("name,L0", [("tiny_f32", 13), ("sweep_1248", 45)])

@@ -7,8 +7,9 @@ running the second part from the first part's state must give the outputs
 bar as every other parity case.  Covers: coarse branches whose first
 positions in the second part take the output held from the first part, a
 second part shorter than a coarse scale (that branch then contributes only
-its held output, and keeps its state), state_in equal to state_out, and the
-errors for a position inside a block and for a header of another batch."""
+its held output, and keeps its state), state_in equal to state_out, the
+device-side checks (a position inside a block, a header of another batch, a
+state that records an error), and graph capture of a continuing forward."""
 import numpy as np
 import pytest
 
@@ -73,25 +74,121 @@ def test_sequence_shards_at_long_context_gates():
     check_against_oracle(wl.cfg, X, W, O)
 
 
+def _all_nan(t) -> bool:
+    import torch
+    return bool(torch.isnan(t.float()).all())
+
+
 def test_position_inside_a_block_is_unsupported():
+    """Checked on the device: the call returns, nothing past the header is
+    read, the output is NaN and state_out records MSGLA_ERR_UNSUPPORTED."""
+    import torch
     cfg = TINY
     X, W = make_inputs(cfg, 1, 40, seed=12)
     layer = DeviceLayer(cfg, W)
     st = layer.new_state(1)
     layer.forward(to_device(X[:, :6], cfg.dtype), state_out=st)  # 6 is not a multiple of 4
     say("state_in at position 6 (scale 4 has a block in progress)")
-    with pytest.raises(binding.MsglaError) as e:
-        layer.forward(to_device(X[:, 6:], cfg.dtype), state_in=st)
-    assert e.value.status == 2
+    st2 = layer.new_state(1)
+    out = layer.forward(to_device(X[:, 6:], cfg.dtype), state_in=st, state_out=st2)
+    torch.cuda.synchronize()
+    assert _all_nan(out)
+    info = binding.msgla_state_query(st2)
+    assert info["status"] == 2 and info["position"] == -1
+    assert binding.msgla_state_query(st) == {"status": 0, "B": 1, "m": 3, "position": 6}
+    # without state_out the NaN output is the only sign
+    assert _all_nan(layer.forward(to_device(X[:, 6:], cfg.dtype), state_in=st))
 
 
 def test_state_of_another_batch_is_rejected():
+    """A state written for B = 1 given to a B = 2 call: only its header is read."""
+    import torch
     cfg = TINY
     X, W = make_inputs(cfg, 2, 16, seed=13)
     layer = DeviceLayer(cfg, W)
     st = layer.new_state(1)
     layer.state_init(st, 1)
     say("state_in written for B=1, used with B=2")
-    with pytest.raises(binding.MsglaError) as e:
-        layer.forward(to_device(X, cfg.dtype), state_in=st)
-    assert e.value.status == 1
+    st2 = layer.new_state(2)
+    out = layer.forward(to_device(X, cfg.dtype), state_in=st, state_out=st2)
+    torch.cuda.synchronize()
+    assert _all_nan(out)
+    assert binding.msgla_state_query(st2)["status"] == 1
+
+
+def test_error_state_propagates_and_decode_refuses_it():
+    """A state that records an error is refused by the next forward (status 1)
+    and by the decode step (NaN output, the state unchanged)."""
+    import torch
+    cfg = TINY
+    X, W = make_inputs(cfg, 1, 48, seed=15)
+    layer = DeviceLayer(cfg, W)
+    st = layer.new_state(1)
+    layer.forward(to_device(X[:, :6], cfg.dtype), state_out=st)
+    bad = layer.new_state(1)
+    layer.forward(to_device(X[:, 6:10], cfg.dtype), state_in=st, state_out=bad)
+    say("forward and decode from a state that records an error")
+    bad2 = layer.new_state(1)
+    out = layer.forward(to_device(X[:, 10:18], cfg.dtype), state_in=bad, state_out=bad2)
+    torch.cuda.synchronize()
+    assert _all_nan(out) and binding.msgla_state_query(bad2)["status"] == 1
+    before = bad.clone()
+    o = layer.decode_step(to_device(X[:, 10], cfg.dtype), bad)
+    torch.cuda.synchronize()
+    assert _all_nan(o) and torch.equal(bad, before)
+    # the usable state still decodes
+    o = layer.decode_step(to_device(X[:, 6], cfg.dtype), st)
+    torch.cuda.synchronize()
+    assert not torch.isnan(o.float()).any()
+    assert binding.msgla_state_query(st)["position"] == 7
+
+
+def test_continuing_forward_captured_in_a_graph():
+    """msgla_forward with state_in and state_out captured once as a HIP graph
+    and replayed with different entry states (eager work and a synchronisation
+    between replays): every replay equals the eager call bit for bit."""
+    import torch
+    cfg = MAIN
+    B, L1, L2 = 2, 128, 72
+    X, W = make_inputs(cfg, B, L1 + L2, seed=16)
+    X_alt = make_inputs(cfg, B, L1, seed=17)[0]
+    layer = DeviceLayer(cfg, W)
+    entry = {"a": layer.new_state(B), "b": layer.new_state(B)}
+    layer.forward(to_device(X[:, :L1], cfg.dtype), state_out=entry["a"])
+    layer.forward(to_device(X_alt, cfg.dtype), state_out=entry["b"])
+    x2 = to_device(X[:, L1:], cfg.dtype)
+    eager = {}
+    for k, s0 in entry.items():
+        s_out = layer.new_state(B)
+        o = layer.forward(x2, state_in=s0, state_out=s_out)
+        eager[k] = (o.clone(), s_out.clone())
+    torch.cuda.synchronize()
+    say(f"graph capture of a continuing forward main dims B={B} L={L2}")
+    s_in = entry["a"].clone()
+    s_out = layer.new_state(B)
+    out = layer.new_output(B, L2)
+    layer.ensure_workspace(B, L2)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        layer.forward(x2, out=out, state_in=s_in, state_out=s_out)
+    scratch = torch.zeros(1 << 20, device="cuda")
+    def same_state(a, b):
+        # the blob's contents (header fields, S, pending sums, held outputs);
+        # its padding bytes are never written and hold whatever was there
+        ra, rb = read_state(cfg, a, B), read_state(cfg, b, B)
+        if any(ra[f] != rb[f] for f in ("magic", "version", "B", "m", "pos")):
+            return False
+        return all(np.array_equal(x[key], y[key]) for x, y in zip(ra["branches"], rb["branches"])
+                   for key in ("S", "psum", "held"))
+
+    for k in ("a", "b", "a", "b", "b", "a"):
+        s_in.copy_(entry[k])
+        g.replay()
+        scratch.add_(1.0)  # the program's own eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager[k][0]), k
+        assert same_state(s_out, eager[k][1]), k
+    ref = orc.layer_forward(X, W, cfg)[:, L1:]
+    err, zeros = orc.row_relative_error(from_device(out), ref)
+    assert zeros and err <= TOL[cfg.dtype]
