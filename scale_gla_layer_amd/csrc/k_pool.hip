@@ -8,10 +8,30 @@
 // take a second pass of their own.  HBM-bound: reads B L d elements per pass,
 // writes sum_s B floor(L/s) d.  With a token mask M the mean of a block is
 // sum M x / max(1, sum M) (Eq. (8)): a block without tokens pools to zero.
+// Masked bf16 calls also write each mean's residual m - bf16(m) (xp_lo), so
+// the projection can take the mean at fp32 accuracy as hi + lo.
 #include "device_common.hpp"
 #include "layout.hpp"
 
 namespace msgla {
+
+// Stores the means m (PER values) at element offset off of the block-mean
+// buffer and, where a residual buffer is given (bf16 storage), m - bf16(m).
+template <typename T>
+__device__ __forceinline__ void store_mean(const PoolOut& o, size_t off, const float* m) {
+  constexpr int PER = per16<T>();
+  const u32x4 hi = pack16<T>(m);
+  st16(reinterpret_cast<T*>(o.xp) + off, hi);
+  if constexpr (sizeof(T) == 2) {
+    if (o.xp_lo) {
+      float h[PER], r[PER];
+      unpack16<T>(hi, h);
+#pragma unroll
+      for (int e = 0; e < PER; ++e) r[e] = m[e] - h[e];
+      st16(reinterpret_cast<T*>(o.xp_lo) + off, pack16<T>(r));
+    }
+  }
+}
 
 // One thread per (row block, 16-byte column piece), consecutive threads on
 // consecutive pieces of the same rows.  The rows of a block are loaded U at a
@@ -66,8 +86,7 @@ __global__ __launch_bounds__(256) void k_pool(const PoolParams P) {
               float m[PER];
 #pragma unroll
               for (int e = 0; e < PER; ++e) m[e] = acc[i][e] * sc;
-              st16(reinterpret_cast<T*>(o.xp) + ((size_t)b * o.n + jout[i]) * P.d + piece * PER,
-                   pack16<T>(m));
+              store_mean<T>(o, ((size_t)b * o.n + jout[i]) * P.d + piece * PER, m);
             }
             ++jout[i];
             cnt[i] = 0;
@@ -131,7 +150,6 @@ __global__ __launch_bounds__(256) void k_pool_pow2(const PoolParams P) {
     const int i = P.lvl[l];
     if (i >= 0) {
       const PoolOut& o = P.out[i];
-      T* dst = reinterpret_cast<T*>(o.xp) + piece * PER;
 #pragma unroll
       for (int j = 0; j < (S >> l); ++j) {
         const int jo = q * (S >> l) + j;
@@ -140,7 +158,7 @@ __global__ __launch_bounds__(256) void k_pool_pow2(const PoolParams P) {
           float m[PER];
 #pragma unroll
           for (int e = 0; e < PER; ++e) m[e] = v[j][e] * sc;
-          st16(dst + ((size_t)b * o.n + jo) * P.d, pack16<T>(m));
+          store_mean<T>(o, ((size_t)b * o.n + jo) * P.d + piece * PER, m);
         }
       }
     }

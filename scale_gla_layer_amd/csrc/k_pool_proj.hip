@@ -7,8 +7,10 @@
 // For branch i (scale s): C_i = P_s(X) * Wp_i^T, where row (b, j) of P_s(X) is
 // the mean of X rows b*L + j*s .. + s-1 (only complete blocks): X itself for
 // s = 1, otherwise the block means written by the pooling prepass (summed in
-// fp32, rounded once).  Wp_i stacks the transposed q, k and v weights; the
-// epilogue writes q, k head-major fp32 rows and v transposed per chunk.
+// fp32, rounded once; with a token mask and bf16 storage the q and k columns
+// also take the means' rounding residuals through a second pass over K).
+// Wp_i stacks the transposed q, k and v weights; the epilogue writes q, k
+// head-major fp32 rows and v transposed per chunk.
 // One more group, the small projection X [W_g1^(1) | ... | W_g1^(m) | W_f]
 // over the unpooled rows, gives every branch's gate first factor at every
 // position (by linearity mean(x) W_g1 = mean(x W_g1), so the recurrence
@@ -35,13 +37,22 @@ struct K1Prob {
   const K1Group& G;
   int m0, n0;
   bool small;  // the small-projection group
+  // Masked bf16 calls: the q / k column tiles of a pooled group run K twice,
+  // first over the rounded block means, then over their residuals (the same
+  // weight rows), so q and k see each mean at fp32 accuracy
+  bool lo_pass;
+  int nk0;     // K segments of one pass over d
   const char* arow[K1Cfg::A_SLOTS];
+  const char* arow_lo[MASKED ? K1Cfg::A_SLOTS : 1];
   const char* brow[K1Cfg::B_SLOTS];
 
   __device__ K1Prob(const K1Params& p, const K1Group& g, int m0_, int n0_, bool small_)
-      : P(p), G(g), m0(m0_), n0(n0_), small(small_) {}
+      : P(p), G(g), m0(m0_), n0(n0_), small(small_) {
+    nk0 = P.d * (int)sizeof(T) / K1Cfg::KSEG;
+    lo_pass = MASKED && !small && G.A_lo != nullptr && n0 < G.col_v;
+  }
 
-  __device__ int nk() const { return P.d * (int)sizeof(T) / K1Cfg::KSEG; }
+  __device__ int nk() const { return lo_pass ? 2 * nk0 : nk0; }
   // 0 for row m of the scale-1 group at a masked position (its pooled input
   // M_t x_t of Eq. (8) is zero, so are q, k and v), else 1
   __device__ float keep(int m) const {
@@ -56,6 +67,9 @@ struct K1Prob {
     for (int j = 0; j < K1Cfg::A_SLOTS; ++j) {
       const int m = m0 + K1Cfg::a_row(j, wave, lane);
       arow[j] = reinterpret_cast<const char*>(G.A) + (size_t)(m < G.M ? m : 0) * row_bytes;
+      if constexpr (MASKED)
+        arow_lo[j] = lo_pass ? reinterpret_cast<const char*>(G.A_lo) + (size_t)(m < G.M ? m : 0) * row_bytes
+                             : arow[j];
     }
 #pragma unroll
     for (int j = 0; j < K1Cfg::B_SLOTS; ++j) {
@@ -73,8 +87,16 @@ struct K1Prob {
   }
   __device__ void started(char*) {}
   __device__ void prep(int) {}
-  __device__ const char* a_row(int j, int kt) const { return arow[j] + kt * K1Cfg::KSEG; }
-  __device__ const char* b_row(int j, int kt) const { return brow[j] + kt * K1Cfg::KSEG; }
+  __device__ const char* a_row(int j, int kt) const {
+    if constexpr (MASKED)
+      if (kt >= nk0) return arow_lo[j] + (kt - nk0) * K1Cfg::KSEG;
+    return arow[j] + kt * K1Cfg::KSEG;
+  }
+  __device__ const char* b_row(int j, int kt) const {
+    if constexpr (MASKED)
+      if (kt >= nk0) return brow[j] + (kt - nk0) * K1Cfg::KSEG;
+    return brow[j] + kt * K1Cfg::KSEG;
+  }
   __device__ bool seg_end(int) const { return false; }
   __device__ void fold(f32x4 (&)[K1Cfg::WM][K1Cfg::WN], int, int, int) {}
   __device__ void finish(f32x4 (&)[K1Cfg::WM][K1Cfg::WN], int, int, int) {}
