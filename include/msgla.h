@@ -255,6 +255,25 @@ typedef struct {
  */
 msgla_status msgla_state_query(const void* state, msgla_state_info* info, void* stream);
 
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the layer
+ * forward of msgla_forward (same arguments and results, without the
+ * workspace), its workspace being a device array of
+ * MSGLA_NOALLOC_WORKSPACE_BYTES that the library holds on every GPU it runs on
+ * until the process ends.  The call allocates nothing.  A call whose
+ * msgla_workspace_bytes(cfg, B, L) exceeds that size returns
+ * MSGLA_ERR_WORKSPACE and enqueues nothing (192 MiB holds the B = 8,
+ * L = 2048 and B = 1, L = 16384 workloads at d = 1024).  Every call on one
+ * GPU uses that GPU's one array: calls that overlap on one GPU (several
+ * streams or threads) race, and the caller must serialise them.  The first
+ * call on a device looks the array's address up (no allocation).
+ */
+#define MSGLA_NOALLOC_WORKSPACE_BYTES (192u << 20)
+msgla_status msgla_forward_noalloc(const msgla_config* cfg, const void* packed, const void* x,
+                                   const uint8_t* mask, int64_t B, int64_t L, void* out,
+                                   const void* state_in, void* state_out, void* stream);
+
 /* Device workspace needed by msgla_decode_step for batch B (bytes). */
 size_t msgla_decode_workspace_bytes(const msgla_config* cfg, int64_t B);
 

@@ -26,8 +26,9 @@ SYMBOLS = (
     "msgla_status_str", "msgla_validate_config", "msgla_packed_weights_bytes",
     "msgla_pack_weights", "msgla_workspace_bytes", "msgla_state_bytes", "msgla_state_init",
     "msgla_forward", "msgla_forward_timed", "msgla_decode_workspace_bytes", "msgla_decode_step",
-    "msgla_fusion_weights", "msgla_state_query",
+    "msgla_fusion_weights", "msgla_state_query", "msgla_forward_noalloc",
 )
+NOALLOC_WORKSPACE_BYTES = 192 << 20  # MSGLA_NOALLOC_WORKSPACE_BYTES
 
 
 class MsglaError(RuntimeError):
@@ -101,6 +102,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "msgla_decode_step": (ctypes.c_int, [cfgp, vp, vp, i64, vp, vp, vp, sz, vp]),
         "msgla_fusion_weights": (ctypes.c_int, [cfgp, vp, vp, i64, i64, vp, vp]),
         "msgla_state_query": (ctypes.c_int, [vp, ctypes.POINTER(CStateInfo), vp]),
+        "msgla_forward_noalloc": (ctypes.c_int, [cfgp, vp, vp, vp, i64, i64, vp, vp, vp, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -235,3 +237,11 @@ def msgla_state_query(state, stream=None) -> dict:
     return {"status": int(info.status), "B": int(info.B), "m": int(info.m),
             "position": int(info.position)}
 
+
+def msgla_forward_noalloc(cfg: MsglaConfig, packed, x, B: int, L: int, out, state_out=None,
+                          state_in=None, mask=None, stream=None):
+    """The forward with the library's own per-device workspace (no allocation)."""
+    st = load_library().msgla_forward_noalloc(ctypes.byref(c_config(cfg)), _ptr(packed), _ptr(x),
+                                              _ptr(mask), B, L, _ptr(out), _ptr(state_in),
+                                              _ptr(state_out), _stream(stream))
+    _check("msgla_forward_noalloc", st)

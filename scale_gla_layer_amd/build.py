@@ -31,6 +31,7 @@ SOURCES = [
     "k_decode.hip",
     "k_pack.hip",
     "k_norm.hip",
+    "api_noalloc.hip",
 ]
 
 FLAGS = [
