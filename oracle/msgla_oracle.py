@@ -256,14 +256,14 @@ def layer_forward(X: np.ndarray, W, cfg, return_state: bool = False, M: Optional
     M: optional [B, L] token mask of Eq. (8) (nonzero = token).  It enters the
     pooling only, as the equation is written: every branch pools its complete
     blocks as mask-weighted means (for s = 1 that is M_t x_t), while the
-    fusion weights still come from the unpooled x_t.  The streaming cache is
-    not defined for a masked call (its pending block keeps no token count).
+    fusion weights still come from the unpooled x_t.  The cache of a masked
+    call keeps, for the incomplete block, the mask-weighted sum of its hidden
+    states and its token count (the denominator of Eq. (8)) beside its count
+    of positions.
     """
     X = np.asarray(X, dtype=np.float64)
     B, L, d = X.shape
     if M is not None:
-        if return_state:
-            raise NotImplementedError("the streaming cache of a masked call is not defined")
         M = (np.asarray(M) != 0).astype(np.float64).reshape(B, L)
     m = len(cfg.scales)
     w = np.ones((B, L, 1)) if m == 1 else fusion_weights(X, W.W_f, W.b_f)
@@ -274,10 +274,12 @@ def layer_forward(X: np.ndarray, W, cfg, return_state: bool = False, M: Optional
         O += w[:, :, i: i + 1] * causal_hold(Y, s, L)
         if return_state:
             tail = X[:, n * s: L, :]
+            mt = np.ones((B, L - n * s)) if M is None else M[:, n * s: L]
             state["branches"].append({
                 "S": S,
-                "psum": tail.sum(axis=1),
+                "psum": (tail * mt[:, :, None]).sum(axis=1),
                 "count": L - n * s,
+                "tokens": mt.sum(axis=1),
                 "held": Y[:, n - 1] if n > 0 else np.zeros((B, d)),
             })
     return (O, state) if return_state else O
@@ -289,6 +291,7 @@ def init_state(cfg, batch: int) -> Dict:
     for h in cfg.heads:
         brs.append({"S": np.zeros((batch, h, cfg.d_k, cfg.d_v)),
                     "psum": np.zeros((batch, cfg.d_model)), "count": 0,
+                    "tokens": np.zeros(batch),
                     "held": np.zeros((batch, cfg.d_model))})
     return {"pos": 0, "branches": brs}
 
@@ -297,9 +300,11 @@ def decode_step(state: Dict, x_t: np.ndarray, W, cfg):
     """One streaming step (the notes' paragraph on token-by-token inference).
 
     Each branch keeps its GLA state, the not-yet-complete block of hidden
-    states (here its running sum and count) and its latest output.  A new
-    token is accumulated; when s tokens have arrived they are pooled, the
-    branch takes one recurrence step, and the held output is replaced;
+    states (here its running sum, its count of positions and its count of
+    tokens, which differ only after a masked forward) and its latest output.
+    A new token is accumulated; when the block's s positions have arrived it
+    is pooled as sum / max(1, tokens) (Eq. (8): the new tokens are real ones),
+    the branch takes one recurrence step, and the held output is replaced;
     otherwise the held output is reused.  The branches are then fused with
     weights from the unpooled x_t (Eqs. (10)-(11)).
     x_t: [B, d].  Returns (o_t [B, d], new state); the input state is not
@@ -315,9 +320,10 @@ def decode_step(state: Dict, x_t: np.ndarray, W, cfg):
         st = state["branches"][i]
         psum = st["psum"] + x_t
         count = st["count"] + 1
+        tokens = st["tokens"] + 1
         S, held = st["S"], st["held"]
         if count == s:
-            xp = psum / s
+            xp = psum / np.maximum(1.0, tokens)[:, None]
             q, k, v, la = branch_projections(xp[:, None, :], bw, cfg)
             y, S = gla_recurrence(q, k, v, la, S0=S)
             if getattr(cfg, "norm", False):
@@ -325,7 +331,9 @@ def decode_step(state: Dict, x_t: np.ndarray, W, cfg):
             held = y.reshape(B, -1) @ bw.W_o
             psum = np.zeros((B, d))
             count = 0
-        new["branches"].append({"S": S, "psum": psum, "count": count, "held": held})
+            tokens = np.zeros(B)
+        new["branches"].append({"S": S, "psum": psum, "count": count, "tokens": tokens,
+                                "held": held})
         o += w[:, i: i + 1] * held
     return o, new
 

@@ -26,7 +26,9 @@ in the oracle:
                 ratio (golden), the half-life remark of Sec. 3.3
   masked layer  Eq. (8) with M against unmasked forwards of edited inputs
                 (all-ones mask, s = 1 zeroed rows, whole and half blocks),
-                causality in the mask, an all-zero mask
+                causality in the mask, an all-zero mask; the cache of a
+                masked call (token count of the incomplete block) continued
+                by decode steps against one masked forward
 """
 import dataclasses
 import math
@@ -445,12 +447,41 @@ def test_all_padding_gives_zero_output():
                           np.zeros((2, 33, cfg.d_model)))
 
 
-def test_masked_cache_is_not_defined():
+def test_masked_prefill_then_decode_equals_masked_forward():
+    """The cache of a masked call (Eq. (8) on the incomplete block: masked sum
+    and token count) continued by decode steps equals one masked forward whose
+    mask is all ones over the decoded positions; prefixes that end inside a
+    block whose tokens are partly or wholly masked exercise the token count."""
     cfg = _tiny()
-    X, W = make_inputs(cfg, 1, 8, seed=11)
-    with pytest.raises(NotImplementedError):
-        orc.layer_forward(X, W, cfg, return_state=True, M=np.ones((1, 8)))
+    L = 30
+    X, W = make_inputs(cfg, 2, L, seed=19)
+    rng = np.random.default_rng(19)
+    for L0 in (5, 6, 7, 13):
+        M = np.ones((2, L))
+        M[:, :L0] = rng.random((2, L0)) < 0.5
+        M[0, L0 - 2: L0] = 0  # the pending block has masked positions
+        O = orc.layer_forward(X, W, cfg, M=M)
+        _, st = orc.layer_forward(X[:, :L0], W, cfg, M=M[:, :L0], return_state=True)
+        for t in range(L0, L):
+            o, st = orc.decode_step(st, X[:, t], W, cfg)
+            assert np.allclose(o, O[:, t], rtol=1e-11, atol=1e-13), (L0, t)
 
+
+def test_masked_cache_counts_tokens_of_the_incomplete_block():
+    """Scale 4, prefix of 6 positions with mask [1, 0, 1, 1, 0, 1]: one complete
+    block, and the pending block (positions 4, 5) holds x_5 alone and one
+    token; two decode steps then pool (x_5 + x_6 + x_7) / 3."""
+    cfg = _tiny()
+    X, W = make_inputs(cfg, 1, 8, seed=20)
+    M = np.array([[1, 0, 1, 1, 0, 1]], dtype=float)
+    _, st = orc.layer_forward(X[:, :6], W, cfg, M=M, return_state=True)
+    br4 = st["branches"][cfg.scales.index(4)]
+    assert br4["count"] == 2 and br4["tokens"][0] == 1.0
+    assert np.allclose(br4["psum"][0], X[0, 5], rtol=0, atol=0)
+    O = orc.layer_forward(X, W, cfg, M=np.concatenate([M, np.ones((1, 2))], axis=1))
+    for t in (6, 7):
+        o, st = orc.decode_step(st, X[:, t], W, cfg)
+        assert np.allclose(o, O[:, t], rtol=1e-11, atol=1e-13)
 
 def test_masked_fusion_weights_come_from_unpooled_x():
     """Two branches {1, 2}: each branch equals its unmasked forward on an input
