@@ -151,10 +151,11 @@ size_t msgla_workspace_bytes(const msgla_config* cfg, int64_t B, int64_t L);
 /*
  * Streaming state ("cache" of the notes' paragraph on token-by-token
  * inference): per branch the fp32 GLA state S [B][h][d_k][d_v], the fp32 sum
- * of the not-yet-complete pooling block [B][d] and the fp32 held output
- * (the branch's latest coarse output after W_o) [B][d], plus the number of
- * tokens consumed so far.  Opaque, versioned blob; its recurrent part is
- * sum_s h_s d_k d_v fp32 elements per sequence.
+ * of the tokens of the not-yet-complete pooling block [B][d] and their count
+ * [B] (the block's positions, unless a masked forward left padding in it),
+ * and the fp32 held output (the branch's latest coarse output after W_o)
+ * [B][d], plus the number of positions consumed so far.  Opaque, versioned
+ * blob; its recurrent part is sum_s h_s d_k d_v fp32 elements per sequence.
  */
 size_t msgla_state_bytes(const msgla_config* cfg, int64_t B);
 
@@ -172,8 +173,10 @@ msgla_status msgla_state_init(const msgla_config* cfg, int64_t B, void* state, s
  *         sum M x / max(1, sum M), so at scale 1 a padded position is a zero
  *         input (the recurrence still decays its state there) and a block
  *         without tokens pools to zero; the fusion weights still come from the
- *         unpooled x_t.  A masked call has no streaming state: mask together
- *         with state_in or state_out gives MSGLA_ERR_UNSUPPORTED.
+ *         unpooled x_t.  A masked call may continue from state_in and
+ *         export state_out: the incomplete block it leaves keeps the sum and
+ *         the count of its tokens, and the decode steps that complete it pool
+ *         it as sum / max(1, tokens).
  *   state_in: NULL (start from an empty state), or a state of the same
  *         config and B (written by msgla_forward's state_out,
  *         msgla_state_init or msgla_decode_step) to continue from: its GLA
@@ -280,12 +283,15 @@ size_t msgla_decode_workspace_bytes(const msgla_config* cfg, int64_t B);
 /*
  * One streaming step for B sequences (the notes' per-branch cache): every
  * branch adds x_t to its pending block; a branch whose block completes (s
- * tokens) pools it, takes one recurrence step and replaces its held output;
+ * positions) pools it (sum of its tokens over their count, Eq. (8)), takes
+ * one recurrence step and replaces its held output;
  * the others keep theirs; the held outputs are fused with weights from the
  * unpooled x_t.  The result equals msgla_forward's output at the same
  * position (up to rounding).
  *   x_t [B][d] (dtype) -> out_t [B][d] (dtype); state: in/out (device,
  *   produced by msgla_state_init or msgla_forward's state_out with the same B).
+ *   The state's header is checked on the device: a state of another config
+ *   or B, or one that records an error, is left unchanged and out_t is NaN.
  */
 msgla_status msgla_decode_step(const msgla_config* cfg, const void* packed, const void* x_t,
                                int64_t B, void* state, void* out_t, void* workspace,

@@ -208,7 +208,8 @@ WsGeom ws_geom(const PackGeom& g, int64_t B, int64_t L) {
 }
 
 struct StGeom {
-  size_t S[MSGLA_MAX_BRANCHES], psum[MSGLA_MAX_BRANCHES], held[MSGLA_MAX_BRANCHES];
+  size_t S[MSGLA_MAX_BRANCHES], psum[MSGLA_MAX_BRANCHES], held[MSGLA_MAX_BRANCHES],
+      tok[MSGLA_MAX_BRANCHES];
   size_t total;
 };
 
@@ -222,6 +223,8 @@ StGeom st_geom(const PackGeom& g, int64_t B) {
     cur += align256((size_t)B * g.d * 4);
     s.held[i] = cur;
     cur += align256((size_t)B * g.d * 4);
+    s.tok[i] = cur;
+    cur += align256((size_t)B * 4);
   }
   s.total = cur;
   return s;
@@ -383,8 +386,6 @@ msgla_status msgla_forward_timed(const msgla_config* cfg, const void* packed, co
   if (!aligned16(packed) || !aligned16(x) || !aligned16(out) || !aligned16(workspace) ||
       (state_out && !aligned16(state_out)) || (state_in && !aligned16(state_in)))
     return MSGLA_ERR_INVALID_ARG;
-  // a masked call defines no streaming state (its pending block keeps no token count)
-  if (mask && (state_in || state_out)) return MSGLA_ERR_UNSUPPORTED;
   const PackGeom g = pack_geom(cfg);
   const WsGeom W = ws_geom(g, B, L);
   if (workspace_bytes < W.total) return MSGLA_ERR_WORKSPACE;
@@ -675,6 +676,7 @@ msgla_status msgla_forward_timed(const msgla_config* cfg, const void* packed, co
     ps.pos = L;
     ps.chk = chk;
     ps.x = x;
+    ps.mask = mask;
     ps.WoT = p3.WoT;
     ps.state = state_out;
     for (int i = 0; i < g.m; ++i) {
@@ -687,6 +689,7 @@ msgla_status msgla_forward_timed(const msgla_config* cfg, const void* packed, co
       b.S = at<float>(state_out, S.S[i]);
       b.psum = at<float>(state_out, S.psum[i]);
       b.held = at<float>(state_out, S.held[i]);
+      b.tok = at<float>(state_out, S.tok[i]);
       b.y = at<char>(workspace, W.br[i].y);
       b.S_in = state_in ? at<float>(state_in, S.S[i]) : nullptr;
       b.held_in = state_in ? at<float>(state_in, S.held[i]) : nullptr;
@@ -802,6 +805,7 @@ msgla_status msgla_decode_step(const msgla_config* cfg, const void* packed, cons
     k.S = at<float>(state, S.S[i]);
     k.psum = at<float>(state, S.psum[i]);
     k.held = at<float>(state, S.held[i]);
+    k.tok = at<float>(state, S.tok[i]);
     k.proj = at<float>(workspace, D.proj[i]);
     k.y = at<float>(workspace, D.y[i]);
     k.gn = g.norm ? at<float>(packed, b.off_gn) : nullptr;

@@ -11,13 +11,13 @@
 // the step changes nothing and outputs NaN), and a branch whose block is not
 // complete skips its work:
 //   D1 proj:   [q | k | v | g] = xp Wp^T for completing branches, where the
-//              pooled row xp = (pending sum + x_t) / s is formed as the MFMA
-//              operand is loaded, plus the fusion logits x_t W_f
+//              pooled row xp = (pending sum + x_t) / (pending tokens + 1) is
+//              formed as the MFMA operand is loaded, plus the fusion logits x_t W_f
 //              (MFMA, 16 sequences x 16 columns per block)
 //   D2 state:  gate, state update and o = q S per (branch, sequence, head, d_v tile)
 //   D3 out:    held = o W_o for completing branches (MFMA as D1), the fusion
-//              softmax, out = sum_i w_i held_i, the pending sums (reset or
-//              accumulate x_t), header position + 1
+//              softmax, out = sum_i w_i held_i, the pending sums and token
+//              counts (reset or accumulate x_t), header position + 1
 #include "device_common.hpp"
 #include "layout.hpp"
 
@@ -138,10 +138,11 @@ __global__ __launch_bounds__(DEC_THREADS) void k_dec_proj(const DecParams P) {
   if (logits) {
     acc = dec_rows_times_cols<T, false, true>(nullptr, trow, 1.f, b < P.B, wrow, k_hi - k_lo, zero4());
   } else {
-    // the completed block: (pending sum + x_t) / s
+    // the completed block: (pending sum + x_t) / its tokens (s, unless a
+    // masked forward left masked positions in it; Eq. (8))
     const float* frow = Br.psum + (size_t)bc * P.d + k_lo + PER * lg;
-    acc = dec_rows_times_cols<T, true, true>(frow, trow, 1.0f / (float)Br.s, b < P.B, wrow, k_hi - k_lo,
-                                             zero4());
+    const float inv = 1.0f / fmaxf(1.f, Br.tok[bc] + 1.f);
+    acc = dec_rows_times_cols<T, true, true>(frow, trow, inv, b < P.B, wrow, k_hi - k_lo, zero4());
   }
   acc = dec_reduce4(acc, red, wave, lane);
   if (wave != 0) return;
@@ -323,6 +324,10 @@ __global__ __launch_bounds__(DEC_THREADS) void k_dec_out(const DecParams P) {
       for (int i = 0; i < P.nbranch; ++i) {
         float* ps = P.br[i].psum + (size_t)bb * P.d + nn;
         *ps = completes(pos, P.br[i].s) ? 0.f : *ps + xv;
+        if (nn == 0) {
+          float* tk = P.br[i].tok + bb;
+          *tk = completes(pos, P.br[i].s) ? 0.f : *tk + 1.f;
+        }
       }
     }
   }

@@ -4,8 +4,9 @@
 // each branch keeps its GLA state, the not-yet-complete block of hidden
 // states and its most recent output.  After a forward over L tokens branch s
 // has consumed n = floor(L/s) blocks: its GLA state is written by the state
-// kernel directly; this kernel adds the sum of the L - n s pending tokens and
-// the held output Y_{n-1} = y_{n-1} W_o (zero when n = 0), and sets the token
+// kernel directly; this kernel adds the sum and the count of the tokens among
+// the L - n s pending positions (all of them without a token mask) and the
+// held output Y_{n-1} = y_{n-1} W_o (zero when n = 0), and sets the token
 // count in the header.  A forward continuing from a state first checks that
 // state's header on the device (k_state_check); the readers of the entry state
 // use it only if the check passed.
@@ -58,11 +59,19 @@ __global__ void k_state_export(const StateParams P) {
   const int col = blockIdx.x * blockDim.x + threadIdx.x;
   const int b = blockIdx.y, i = blockIdx.z;
   const StateBranch& Br = P.br[i];
+  const uint8_t* mk = P.mask ? P.mask + (size_t)b * P.L : nullptr;
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    // tokens of the incomplete block (Eq. (8): its pooling divides by them)
+    float c = 0.f;
+    for (int t = Br.n * Br.s; t < P.L; ++t) c += mk ? (mk[t] ? 1.f : 0.f) : 1.f;
+    Br.tok[b] = c;
+  }
   if (col < P.d) {
-    // pending tokens of the incomplete block
+    // sum of the tokens of the incomplete block
     const T* x = reinterpret_cast<const T*>(P.x);
     float s = 0.f;
-    for (int t = Br.n * Br.s; t < P.L; ++t) s += to_f32(x[((size_t)b * P.L + t) * P.d + col]);
+    for (int t = Br.n * Br.s; t < P.L; ++t)
+      if (!mk || mk[t]) s += to_f32(x[((size_t)b * P.L + t) * P.d + col]);
     Br.psum[(size_t)b * P.d + col] = s;
     // held output of the last complete block (or, without one, the output
     // held on entry)

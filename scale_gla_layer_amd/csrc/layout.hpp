@@ -34,7 +34,9 @@
 // written by the projection and are masked by every reader.
 //
 // State (fp32 except the header): 256-byte header {magic, version, B, m, pos,
-// status}, then per branch S [B][h][d_k][d_v], psum [B][d], held [B][d].
+// status}, then per branch S [B][h][d_k][d_v], psum [B][d], held [B][d] and
+// tok [B] (tokens in the incomplete block: its positions, unless a masked
+// forward left masked positions in it; psum sums only its tokens).
 #pragma once
 #include <stdint.h>
 #include <stddef.h>
@@ -46,7 +48,7 @@
 namespace msgla {
 
 constexpr uint32_t STATE_MAGIC = 0x4C47534Du;  // "MSGL"
-constexpr uint32_t STATE_VERSION = 1;
+constexpr uint32_t STATE_VERSION = 2;
 constexpr size_t STATE_HEADER = 256;
 constexpr int FUSION_STRIDE = 8;  // floats per row of the fusion-weight buffer
 constexpr int N_XCD = 8;          // XCDs (separate L2 caches) of an MI355X
@@ -222,7 +224,7 @@ struct PackSrc {
 // ---------------- state export / init ------------------------------------------
 struct StateBranch {
   int s, h, n, np, ko;
-  float* S; float* psum; float* held;
+  float* S; float* psum; float* held; float* tok;
   const void* y;    // forward workspace y (export only)
   const float* S_in;     // state the forward started from (kept when n == 0), or null
   const float* held_in;
@@ -233,6 +235,7 @@ struct StateParams {
   int64_t pos;      // tokens of this call (added to the entry position)
   const StateCheck* chk;  // check of the entry state (S_in / held_in read only if it passed), or null
   const void* x;    // forward input (export only)
+  const uint8_t* mask;  // the forward's token mask [B][L], or null
   const void* WoT;
   void* state;      // header
   StateBranch br[MSGLA_MAX_BRANCHES];
@@ -247,6 +250,7 @@ struct DecBranch {
   float* S;         // state [B][h][dk][dv]
   float* psum;      // [B][d]
   float* held;      // [B][d]
+  float* tok;       // [B] tokens in the incomplete block
   float* proj;      // workspace [B][N]
   float* y;         // workspace [B][h dv]
   const float* gn;  // normalisation gains [h dv], or null (no normalisation)

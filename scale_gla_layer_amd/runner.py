@@ -154,7 +154,8 @@ class DecodeGraph:
 
 def read_state(cfg: MsglaConfig, state, B: int) -> dict:
     """Decode a state blob (device tensor) into numpy arrays, mirroring the
-    layout documented in include/msgla.h (header + per-branch S, psum, held)."""
+    layout documented in include/msgla.h (header + per-branch S, psum, held,
+    pending token count)."""
     raw = state.detach().cpu().numpy()
     hdr = raw[:24].view(np.int32)
     pos = int(raw[16:24].view(np.int64)[0])
@@ -170,6 +171,8 @@ def read_state(cfg: MsglaConfig, state, B: int) -> dict:
         cur += align(4 * B * cfg.d_model)
         held = raw[cur: cur + 4 * B * cfg.d_model].view(np.float32).reshape(B, cfg.d_model)
         cur += align(4 * B * cfg.d_model)
+        tok = raw[cur: cur + 4 * B].view(np.float32)
+        cur += align(4 * B)
         out["branches"].append({"S": S.astype(np.float64), "psum": psum.astype(np.float64),
-                                "held": held.astype(np.float64)})
+                                "held": held.astype(np.float64), "tokens": tok.astype(np.float64)})
     return out

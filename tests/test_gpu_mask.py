@@ -107,3 +107,86 @@ def test_bf16_masked_full_size():
     against the oracle."""
     wl = WORKLOADS["main"]
     masked_case(wl.cfg, wl.batch, wl.seq_len, seed=12)
+
+
+# ------------------------------------------------------------------ masked calls and the streaming state
+
+
+def _masked_prefix(B, L0, L, seed):
+    """A mask over L positions: holes in the first L0 (also in the last,
+    incomplete blocks of the prefix), ones after them."""
+    rng = np.random.default_rng(seed)
+    M = np.ones((B, L), np.uint8)
+    M[:, :L0] = rng.random((B, L0)) < 0.6
+    M[0, L0 - 2: L0] = 0
+    return M
+
+
+@pytest.mark.parametrize("cfg_name,B,L0,n", [("tiny_f32", 2, 37, 12), ("tiny_f32", 3, 66, 9),
+                                             ("main", 2, 45, 12)])
+def test_masked_prefill_then_decode(cfg_name, B, L0, n):
+    """A masked forward exporting its state, then decode steps: the outputs
+    equal one masked forward whose mask is all ones over the decoded
+    positions (the incomplete blocks' token counts carry over)."""
+    import torch
+    from oracle import msgla_oracle as orc
+    from scale_gla_layer_amd.runner import read_state, to_device
+    from tests.gpu_cases import TOL
+    cfg = WORKLOADS[cfg_name].cfg
+    say(f"masked prefill {cfg_name} B={B} L0={L0} then {n} decode steps")
+    X, W = make_inputs(cfg, B, L0 + n, seed=40 + L0)
+    M = _masked_prefix(B, L0, L0 + n, seed=41 + L0)
+    layer, _, out, st = run_device(cfg, X[:, :L0], W, state_out=True, M=M[:, :L0])
+    outs = [from_device(layer.decode_step(to_device(X[:, t], cfg.dtype), st)) for t in range(L0, L0 + n)]
+    torch.cuda.synchronize()
+    O = np.concatenate([from_device(out), np.stack(outs, axis=1)], axis=1)
+    ref = orc.layer_forward(X, W, cfg, M=M)
+    err, zeros = orc.row_relative_error(O, ref)
+    say(f"row-relative error {err:.3e}")
+    assert zeros and err <= TOL[cfg.dtype]
+    assert read_state(cfg, st, B)["pos"] == L0 + n
+
+
+def test_masked_state_export_matches_oracle():
+    """fp32: the exported cache of a masked forward (S, masked pending sums,
+    pending token counts, held outputs) against the oracle's."""
+    from oracle import msgla_oracle as orc
+    from scale_gla_layer_amd.runner import read_state
+    cfg = TINY
+    for L in (38, 64, 303):
+        X, W = make_inputs(cfg, 2, L, seed=50 + L)
+        M = _masked_prefix(2, L, L, seed=51 + L)
+        say(f"masked state export tiny L={L}")
+        _, _, _, st = run_device(cfg, X, W, state_out=True, M=M)
+        dev = read_state(cfg, st, 2)
+        _, ref = orc.layer_forward(X, W, cfg, return_state=True, M=M)
+        for bd, br in zip(dev["branches"], ref["branches"]):
+            assert np.array_equal(bd["tokens"], br["tokens"]), (L, bd["tokens"], br["tokens"])
+            for key in ("S", "psum", "held"):
+                a, b = bd[key], br[key]
+                scale = max(1e-30, np.abs(b).max())
+                assert np.abs(a - b).max() <= 1e-4 * scale + 1e-12, (L, key)
+
+
+@pytest.mark.parametrize("cfg_name,B,L1,L2", [("tiny_f32", 2, 32, 50), ("main", 2, 128, 100)])
+def test_masked_forward_continues_from_a_state(cfg_name, B, L1, L2):
+    """Two masked forwards, the second from the first's state (split at a
+    block boundary of every scale), against one masked forward."""
+    import torch
+    from oracle import msgla_oracle as orc
+    from scale_gla_layer_amd.runner import DeviceLayer, to_device
+    from tests.gpu_cases import TOL, mask_to_device
+    cfg = WORKLOADS[cfg_name].cfg
+    say(f"masked continuation {cfg_name} B={B} L1={L1} L2={L2}")
+    X, W = make_inputs(cfg, B, L1 + L2, seed=60)
+    M = make_mask(B, L1 + L2, seed=61, min_keep=1.0, hole_prob=0.2)
+    layer = DeviceLayer(cfg, W)
+    st = layer.new_state(B)
+    o1 = layer.forward(to_device(X[:, :L1], cfg.dtype), state_out=st, mask=mask_to_device(M[:, :L1]))
+    o2 = layer.forward(to_device(X[:, L1:], cfg.dtype), state_in=st, state_out=st,
+                       mask=mask_to_device(M[:, L1:]))
+    torch.cuda.synchronize()
+    O = np.concatenate([from_device(o1), from_device(o2)], axis=1)
+    err, zeros = orc.row_relative_error(O, orc.layer_forward(X, W, cfg, M=M))
+    say(f"row-relative error {err:.3e}")
+    assert zeros and err <= TOL[cfg.dtype]
