@@ -435,18 +435,20 @@ def cpu_baseline(workload: str, min_s: float = 10.0):
 
 PROFILE_COMMANDS = {
     "ktrace": "rocprofv3 --kernel-trace --stats -f csv -d {d}/ktrace -o main -- "
-              "python3 bench.py --steps 20 --warmup 5 --no-cpu-baseline --no-gla --no-per-call --no-decode --no-mask --no-routing --no-norm",
+              "python3 bench.py --steps 20 --warmup 5 --no-cpu-baseline --no-gla --no-per-call --no-decode --no-mask --no-routing --no-norm --no-workloads",
     "fetch": "rocprofv3 --pmc FETCH_SIZE -f csv -d {d}/pmc_fetch -o main -- "
-             "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-gla --no-per-call --no-decode --no-mask --no-routing --no-norm",
+             "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-gla --no-per-call --no-decode --no-mask --no-routing --no-norm --no-workloads",
     "write": "rocprofv3 --pmc WRITE_SIZE -f csv -d {d}/pmc_write -o main -- "
-             "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-gla --no-per-call --no-decode --no-mask --no-routing --no-norm",
+             "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-gla --no-per-call --no-decode --no-mask --no-routing --no-norm --no-workloads",
     "util": "rocprofv3 --pmc MfmaUtil VALUBusy LdsUtil LDSBankConflict MfmaFlopsBF16 MfmaFlopsF32 "
             "-f csv -d {d}/pmc_util -o main -- "
-            "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-gla --no-per-call --no-decode --no-mask --no-routing --no-norm",
+            "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-gla --no-per-call --no-decode --no-mask --no-routing --no-norm --no-workloads",
     "cal_fetch": "rocprofv3 --pmc FETCH_SIZE -f csv -d {d}/cal_fetch -o copy -- "
                  "python3 bench.py --copy-calibration",
     "cal_write": "rocprofv3 --pmc WRITE_SIZE -f csv -d {d}/cal_write -o copy -- "
                  "python3 bench.py --copy-calibration",
+    "dec_ktrace": "rocprofv3 --kernel-trace --stats -f csv -d {d}/dec_ktrace -o decode -- "
+                  "python3 bench.py --only-decode",
 }
 
 
@@ -484,7 +486,8 @@ def summarize_profiles(d: str, workload: str = "main"):
     lines = [f"# Kernel trace, workload {workload} ({wl.description})", "",
              "Command (from the repository root, `<out>` any output directory):", "",
              f"    {cmds['ktrace']}", "",
-             "25 forwards (5 warm-up + 20 timed) under the tracer.", "",
+             "The forwards of one short run under the tracer: clock settling (batches of 20 "
+             "until two agree within 1%), 5 warm-up, 20 timed and 20 with stage events.", "",
              "| kernel | calls | avg us | min us | max us | share |", "|---|---|---|---|---|---|"]
     for r in stats:
         lines.append(f"| {_short(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
@@ -568,6 +571,28 @@ def summarize_profiles(d: str, workload: str = "main"):
                 + (f"{hbm / 1e6:.1f} | {hbm / (us * 1e-6) / 1e9:.0f} |" if hbm is not None else "- | - |"))
         with open(os.path.join(out_dir, f"counters_{workload}.md"), "w", encoding="utf-8") as f:
             f.write("\n".join(urows) + "\n")
+    # the streaming decode step (prefill, then the timed eager steps and the
+    # graph replays of measure_decode)
+    dec_csv = os.path.join(d, "dec_ktrace", "decode_kernel_stats.csv")
+    if os.path.exists(dec_csv):
+        with open(dec_csv, newline="", encoding="utf-8") as f:
+            dstats = list(csv.DictReader(f))
+        dwl = WORKLOADS["sweep_1248"]
+        drows = [f"# Kernel trace, decode step, workload sweep_1248 ({dwl.description})", "",
+                 "Command (from the repository root, `<out>` any output directory):", "",
+                 f"    {cmds['dec_ktrace']}", "",
+                 "Two prefills of 4096 tokens (the forward's kernels), then 288 eager decode "
+                 "steps and 288 graph replays, B = 16; each step is k_dec_proj, k_dec_state "
+                 "and k_dec_out.", "",
+                 "| kernel | calls | avg us | min us | max us | share |", "|---|---|---|---|---|---|"]
+        for r in dstats:
+            name = r["Name"]
+            short = next((k for k in ("k_dec_proj", "k_dec_state", "k_dec_out") if k in name), _short(name))
+            drows.append(f"| {short} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                         f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                         f"{float(r['Percentage']):.1f}% |")
+        with open(os.path.join(out_dir, "kernels_decode_sweep_1248.md"), "w", encoding="utf-8") as f:
+            f.write("\n".join(drows) + "\n")
     log(f"[bench] wrote profiles for {workload} from {d}")
 
 

@@ -43,6 +43,32 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 int cdiv(int a, int b) { return (a + b - 1) / b; }
 
+// K1's tile schedule: every group's row tiles are split evenly over the eight
+// XCDs (each keeps the column tiles of its row tiles together, which share the
+// A rows in its L2), so each XCD gets the same mix of work.  Groups whose tiles
+// run K twice (the q / k tiles of pooled groups in a masked bf16 call) are
+// walked first, so the longest tiles start first on every XCD.
+void k1_schedule(K1Params& p) {
+  int n = 0;
+  for (int pass = 0; pass < 2; ++pass)
+    for (int g = 0; g < p.ngroups; ++g) {
+      const bool heavy = p.g[g].A_lo != nullptr;
+      if (heavy == (pass == 0)) p.order[n++] = g;
+    }
+  int longest = 0;
+  for (int x = 0; x < N_XCD; ++x) {
+    int cnt = 0;
+    for (int g = 0; g < p.ngroups; ++g) {
+      const int mt = cdiv(p.g[g].M, GEMM_TILE);
+      p.mt_begin[g][x] = (int)((int64_t)mt * x / N_XCD);
+      p.mt_begin[g][x + 1] = (int)((int64_t)mt * (x + 1) / N_XCD);
+      cnt += (p.mt_begin[g][x + 1] - p.mt_begin[g][x]) * p.g[g].tiles_n;
+    }
+    longest = std::max(longest, cnt);
+  }
+  p.per_xcd = longest;
+}
+
 struct BranchGeom {
   int s, h;
   int col_k, col_v, col_g, col_z, N;  // projection columns
@@ -435,7 +461,6 @@ msgla_status msgla_forward_timed(const msgla_config* cfg, const void* packed, co
     G.M = (int)B * wb.n;
     G.N = b.col_g;  // q, k and v columns
     G.tiles_n = cdiv(G.N, GEMM_TILE);
-    G.tile_begin = tiles;
     tiles += cdiv(G.M, GEMM_TILE) * G.tiles_n;
     G.h = b.h;
     G.col_k = b.col_k;
@@ -478,12 +503,11 @@ msgla_status msgla_forward_timed(const msgla_config* cfg, const void* packed, co
     G.M = (int)(B * L);
     G.N = Ns;
     G.tiles_n = cdiv(Ns, GEMM_TILE);
-    G.tile_begin = tiles;
     tiles += cdiv(G.M, GEMM_TILE) * G.tiles_n;
   }
   p1.ngroups = ng;
   p1.total_tiles = tiles;
-  p1.per_xcd = cdiv(tiles, N_XCD);
+  k1_schedule(p1);
 
   // ---------------- K2 ----------------
   K2Params p2{};
@@ -741,10 +765,9 @@ msgla_status msgla_fusion_weights(const msgla_config* cfg, const void* packed, c
   G.M = (int)(B * L);
   G.N = 16;
   G.tiles_n = 1;
-  G.tile_begin = 0;
   p1.ngroups = 1;
   p1.total_tiles = cdiv(G.M, GEMM_TILE);
-  p1.per_xcd = cdiv(p1.total_tiles, N_XCD);
+  k1_schedule(p1);
   HIP_TRY(launch_k1(p1, g.bf16, static_cast<hipStream_t>(stream)));
   return MSGLA_OK;
 }

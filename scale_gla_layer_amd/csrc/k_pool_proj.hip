@@ -291,13 +291,23 @@ struct K1Prob {
 template <typename T, bool MASKED>
 __global__ __launch_bounds__(K1Cfg::THREADS) void k1_pool_proj(const K1Params P) {
   __shared__ __attribute__((aligned(16))) char lds[K1Cfg::LDS_STAGED];
-  const int tile = remap_xcd(blockIdx.x, P.per_xcd);
-  if (tile >= P.total_tiles) return;
-  int gi = 0;
-  while (gi + 1 < P.ngroups && tile >= P.g[gi + 1].tile_begin) ++gi;
+  // consecutive workgroups go to the eight XCDs in turn: this one is the j-th
+  // of XCD x, which walks its share of every group's row tiles in group order
+  const int x = blockIdx.x % N_XCD;
+  int j = blockIdx.x / N_XCD, gi = -1, tm = 0, tn = 0;
+  for (int o = 0; o < P.ngroups; ++o) {
+    const int g = P.order[o];
+    const int cnt = (P.mt_begin[g][x + 1] - P.mt_begin[g][x]) * P.g[g].tiles_n;
+    if (j < cnt) {
+      gi = g;
+      tm = P.mt_begin[g][x] + j / P.g[g].tiles_n;
+      tn = j % P.g[g].tiles_n;
+      break;
+    }
+    j -= cnt;
+  }
+  if (gi < 0) return;
   const K1Group& G = P.g[gi];
-  const int local = tile - G.tile_begin;
-  const int tm = local / G.tiles_n, tn = local - tm * G.tiles_n;
   K1Prob<T, MASKED> prob(P, G, tm * K1_BM, tn * K1_BN, gi == P.sm.group);
   gemm_dma_tile<T, K1Cfg>(prob, G.N - tn * K1_BN, lds);
 }

@@ -114,7 +114,6 @@ struct K1Group {
   int M;            // B * n
   int N;            // GEMM columns: h (2 dk + dv), or Ns for the small group
   int tiles_n;      // ceil(N / BN)
-  int tile_begin;   // first flattened tile of this group
   int h;            // heads
   int col_k, col_v; // column ranges: q [0, col_k), k [col_k, col_v), v [col_v, N)
   int np, nch;      // padded rows and chunks per (b, head)
@@ -143,6 +142,11 @@ struct K1Params {
   int ngroups, total_tiles, per_xcd;
   K1Group g[MSGLA_MAX_BRANCHES + 1];
   K1Small sm;
+  // Tile schedule: XCD x takes m-tiles [mt_begin[g][x], mt_begin[g][x + 1]) of
+  // every group g (all their column tiles), the groups in the order `order`;
+  // per_xcd is the longest of the eight lists
+  int order[MSGLA_MAX_BRANCHES + 1];
+  int mt_begin[MSGLA_MAX_BRANCHES + 1][N_XCD + 1];
 };
 
 // ---------------- K2a: chunk-local gate, decay and intra-chunk matrix ----------
