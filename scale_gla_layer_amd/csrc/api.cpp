@@ -35,6 +35,8 @@ int k2b_lds_bytes(bool bf16_path, int C, int dk);
 
 using namespace msgla;
 
+static_assert(sizeof(msgla_status) == sizeof(int32_t), "status codes travel as 32-bit ints");
+
 namespace {
 
 constexpr int GEMM_TILE = 128;
@@ -299,7 +301,10 @@ bool batch_ok(int64_t B, int64_t L) {
 extern "C" {
 
 const char* msgla_status_str(msgla_status s) {
-  switch (s) {
+  // a C caller may pass any int: read the bits, not the enum value
+  int32_t v;
+  std::memcpy(&v, &s, sizeof(v));
+  switch (v) {
     case MSGLA_OK: return "ok";
     case MSGLA_ERR_INVALID_ARG: return "invalid argument";
     case MSGLA_ERR_UNSUPPORTED: return "unsupported";
