@@ -279,6 +279,55 @@ def measure_routing(cfg, W, L=32768, steps=50, warmup=10):
             "percent_by_region": regions}
 
 
+def measure_library_gemms(cfg, B, L, stage_ms, steps=50, warmup=10):
+    """Context for the GEMM kernels: the same products as plain torch.matmul
+    calls (hipBLASLt on this stack), one call per group, timed back to back.
+    K1's shapes: every branch's pooled rows times its q | k | v columns, plus
+    the unpooled rows times the gate first factors and fusion logits; K3's:
+    every branch's y rows (coarse length) times its W_o.  Operands are
+    contiguous 2-D bf16 (or fp32) tensors; only time is measured."""
+    import torch
+    dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    d, dk, dv = cfg.d_model, cfg.d_k, cfg.d_v
+    m = len(cfg.scales)
+    rp = 16 if cfg.gate_rank <= 16 else 64
+    g = torch.Generator(device="cuda").manual_seed(5)
+
+    def mats(shapes):
+        return [(torch.randn(M, K, generator=g, device="cuda", dtype=torch.float32).to(dt),
+                 torch.randn(K, N, generator=g, device="cuda", dtype=torch.float32).to(dt))
+                for M, K, N in shapes]
+
+    k1 = [(B * (L // s), d, h * (2 * dk + dv)) for s, h in zip(cfg.scales, cfg.heads)]
+    k1.append((B * L, d, m * rp + (16 if m > 1 else 0)))
+    k3 = [(B * (L // s), h * dv, d) for s, h in zip(cfg.scales, cfg.heads)]
+    out = {}
+    for name, shapes in (("k1", k1), ("k3", k3)):
+        ops = mats(shapes)
+        for _ in range(warmup):
+            for a, w in ops:
+                torch.matmul(a, w)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            for a, w in ops:
+                torch.matmul(a, w)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / steps
+        fl = sum(2.0 * M * K * N for M, K, N in shapes)
+        out[name] = {"shapes": [list(t) for t in shapes], "library_us": round(us, 2),
+                     "library_tflops": round(fl / (us * 1e-6) / 1e12, 1)}
+        del ops
+    out["k1"]["ours_us"] = round(stage_ms.get("proj", 0.0) * 1e3, 2)
+    out["k3"]["ours_us"] = round((stage_ms.get("out_coarse", 0.0) + stage_ms.get("hold_fuse", 0.0)) * 1e3, 2)
+    out["note"] = ("ours: K1 (one launch, with its q/k/v/gate/fusion epilogues) and K3c + K3f "
+                   "(with the hold and fusion epilogue) from the event pass; library: the bare "
+                   "products, one torch.matmul per group")
+    return out
+
+
 def settle_clocks(layer, x, batch=20, tol=0.01, max_s=3.0):
     """Runs forwards in batches of `batch` until the mean time of a batch is
     within `tol` of the previous one (the shader clock settles under load;
@@ -435,14 +484,14 @@ def cpu_baseline(workload: str, min_s: float = 10.0):
 
 PROFILE_COMMANDS = {
     "ktrace": "rocprofv3 --kernel-trace --stats -f csv -d {d}/ktrace -o main -- "
-              "python3 bench.py --steps 20 --warmup 5 --no-cpu-baseline --no-gla --no-per-call --no-decode --no-mask --no-routing --no-norm --no-workloads",
+              "python3 bench.py --steps 20 --warmup 5 --no-cpu-baseline --no-gla --no-per-call --no-decode --no-mask --no-routing --no-norm --no-workloads --no-library-gemms",
     "fetch": "rocprofv3 --pmc FETCH_SIZE -f csv -d {d}/pmc_fetch -o main -- "
-             "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-gla --no-per-call --no-decode --no-mask --no-routing --no-norm --no-workloads",
+             "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-gla --no-per-call --no-decode --no-mask --no-routing --no-norm --no-workloads --no-library-gemms",
     "write": "rocprofv3 --pmc WRITE_SIZE -f csv -d {d}/pmc_write -o main -- "
-             "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-gla --no-per-call --no-decode --no-mask --no-routing --no-norm --no-workloads",
+             "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-gla --no-per-call --no-decode --no-mask --no-routing --no-norm --no-workloads --no-library-gemms",
     "util": "rocprofv3 --pmc MfmaUtil VALUBusy LdsUtil LDSBankConflict MfmaFlopsBF16 MfmaFlopsF32 "
             "-f csv -d {d}/pmc_util -o main -- "
-            "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-gla --no-per-call --no-decode --no-mask --no-routing --no-norm --no-workloads",
+            "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-gla --no-per-call --no-decode --no-mask --no-routing --no-norm --no-workloads --no-library-gemms",
     "cal_fetch": "rocprofv3 --pmc FETCH_SIZE -f csv -d {d}/cal_fetch -o copy -- "
                  "python3 bench.py --copy-calibration",
     "cal_write": "rocprofv3 --pmc WRITE_SIZE -f csv -d {d}/cal_write -o copy -- "
@@ -625,6 +674,8 @@ def main():
                     help="only run the plain-copy reference kernel for counter scaling")
     ap.add_argument("--summarize-profiles", metavar="DIR",
                     help="write profiles/ summaries from rocprofv3 output under DIR (no GPU)")
+    ap.add_argument("--no-library-gemms", action="store_true",
+                    help="skip timing the GEMM shapes as plain library calls")
     ap.add_argument("--no-workloads", action="store_true",
                     help="skip the other workloads' forward lines (GLA, long, sweeps)")
     ap.add_argument("--only-decode", action="store_true",
@@ -700,6 +751,13 @@ def main():
                 "peak": d["peak"], "unit": d["unit"], "frac": d["frac"],
                 "traffic": traffic_from_profile(d["kernel"], wl.name),
                 "algorithmic_per_launch": d["algorithmic"]}
+
+    libg = None
+    if not args.no_library_gemms and stage_ms:
+        libg = measure_library_gemms(cfg, B, L, stage_ms)
+        log(f"[bench] library GEMMs of the same shapes: K1's {libg['k1']['library_us']} us "
+            f"({libg['k1']['library_tflops']} TFLOP/s) against K1 {libg['k1']['ours_us']} us; "
+            f"K3's {libg['k3']['library_us']} us against K3c + K3f {libg['k3']['ours_us']} us")
 
     masked = None
     if not args.no_mask:
@@ -795,6 +853,7 @@ def main():
                            "t_roof_us": round(t_roof * 1e6, 2),
                            "frac": round(t_roof / (ms * 1e-3), 4)},
         "kernels": stages,
+        "library_gemms": libg,
         "settle": settle,
         "per_call_us": warm,
         "per_call_cold_mall_us": cold,
