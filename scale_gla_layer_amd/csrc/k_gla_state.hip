@@ -18,20 +18,24 @@
 // state wave run side by side.  The walk is latency-bound unless the inputs
 // of later chunks are already in flight: A, qt, kT, the chunk's V slice and
 // lam are copied global -> LDS asynchronously (global_load_lds_dwordx4, no
-// VGPRs) into NST rotating stages, NST-1 chunks ahead of the compute, by a
-// ninth wave that does nothing else (the copies of one chunk keep the CU's
-// vector-memory path busy for about as long as the chunk's products take, and
-// a compute wave that issued them would wait that long), with vmcnt waits on
-// the copy wave and one barrier per chunk.  V positions beyond the sequence end
+// VGPRs) into NST rotating stages, NST-1 chunks ahead of the compute, by two
+// more waves that do nothing else and take the copy instructions in turn (the
+// copies of one chunk keep the CU's vector-memory path busy for about as long
+// as the chunk's products take, and a compute wave that issued them would
+// wait that long), with vmcnt waits on the copy waves and one barrier per
+// chunk.  V positions beyond the sequence end
 // are zeroed in the fragments (the workspace there is never written).
 // After the last chunk the fp32 state is optionally written out.
+#include <type_traits>
+
 #include "async_copy.hpp"
 #include "device_common.hpp"
 #include "layout.hpp"
 
 namespace msgla {
 
-constexpr int K2B_THREADS = 576;  // 4 output waves + 4 state waves + 1 copy wave
+constexpr int K2B_COPY_WAVES = 2;
+constexpr int K2B_THREADS = 64 * (8 + K2B_COPY_WAVES);  // 4 output waves + 4 state waves + the copy waves
 constexpr int K2B_DVT = 32;  // d_v columns per workgroup
 
 constexpr int k2b_kb(int b) { return (b + 1023) & ~1023; }
@@ -56,7 +60,7 @@ struct K2bGeom {
   static constexpr int EXTRA = 2 * K2B_DVT * LDS_S * es;
   static constexpr int NST = 3 * STAGE + EXTRA <= 160 * 1024 ? 3 : 2;
   static constexpr int LDS = NST * STAGE + EXTRA;
-  // copy instructions per chunk (all issued by the copy wave)
+  // copy instructions per chunk (all issued by the copy waves)
   static constexpr int NCOPY = nA + 2 * nQ + nV + (bL <= 1024 ? 1 : 0);
   static constexpr int NCOPY_S = nQ + nV + (bL <= 1024 ? 1 : 0);  // state-only walk: kT, V, lam
   static_assert(bA % 1024 == 0 && bQ % 1024 == 0 && bV % 1024 == 0 && bL <= 1024, "block sizes");
@@ -124,12 +128,18 @@ __global__ __launch_bounds__(K2B_THREADS) void k2b_gla_state(const K2Params P) {
   const char* Lg = reinterpret_cast<const char*>(Bb.lam + chunk0 * DK);
   T* yg = reinterpret_cast<T*>(Bb.y) + (size_t)bh * Bb.np * dv + v0;
 
-  // Wave 8 issues every copy (a chunk's ~45 copy instructions occupy the CU's
-  // vector-memory path for about as long as the chunk's products take): the
-  // compute waves never queue behind copy instructions, and the copy wave's
-  // vmcnt holds nothing but copies, so its waits are exact.
+  // Waves 8 and up issue every copy, taking a chunk's copy instructions in turn
+  // (a chunk's ~45 copy instructions occupy the CU's vector-memory path for
+  // about as long as the chunk's products take, and one wave alone issues them
+  // slower than the path takes them): the compute waves never queue behind
+  // copy instructions, and a copy wave's vmcnt holds nothing but its own
+  // copies, so its waits are exact.
   const int oL = 16 * lane;  // lam: one partial instruction of one virtual row (key 0)
-  auto issue = [&](int i) {
+  auto issue = [&](int i, int cw) {
+    int n = 0;  // copy instructions of the chunk so far (wave-uniform)
+    auto cp = [&](const char* src, char* dst, bool lane_on) {
+      if (n++ % K2B_COPY_WAVES == cw && lane_on) dma16(src, dst);
+    };
     const int c = cb + i;
     char* st = smem + (i % NST) * G::STAGE;
     const char* a = Ag + (size_t)c * G::bA;
@@ -138,30 +148,40 @@ __global__ __launch_bounds__(K2B_THREADS) void k2b_gla_state(const K2Params P) {
     const char* v = Vg + (size_t)c * dv * C * es;
     // the V slice first: the one block that comes from HBM rather than L2
 #pragma unroll
-    for (int k = 0; k < G::nV; ++k) dma16(v + 1024 * k + k2b_lane_off(G::lgC, k, lane), st + G::oV + 1024 * k);
-    if (oL < G::bL) dma16(Lg + (size_t)c * G::bL + oL, st + G::oL);
+    for (int k = 0; k < G::nV; ++k) cp(v + 1024 * k + k2b_lane_off(G::lgC, k, lane), st + G::oV + 1024 * k, true);
+    cp(Lg + (size_t)c * G::bL + oL, st + G::oL, oL < G::bL);
 #pragma unroll
     for (int k = 0; k < G::nQ; ++k) {
-      dma16(kk + 1024 * k + k2b_lane_off(G::lgC, k, lane), st + G::oK + 1024 * k);
-      if constexpr (!SONLY) dma16(q + 1024 * k + k2b_lane_off(G::lgQ, k, lane), st + G::oQ + 1024 * k);
+      cp(kk + 1024 * k + k2b_lane_off(G::lgC, k, lane), st + G::oK + 1024 * k, true);
+      if constexpr (!SONLY) cp(q + 1024 * k + k2b_lane_off(G::lgQ, k, lane), st + G::oQ + 1024 * k, true);
     }
     if constexpr (!SONLY) {
 #pragma unroll
-      for (int k = 0; k < G::nA; ++k) dma16(a + 1024 * k + k2b_lane_off(G::lgC, k, lane), st + G::oA + 1024 * k);
+      for (int k = 0; k < G::nA; ++k) cp(a + 1024 * k + k2b_lane_off(G::lgC, k, lane), st + G::oA + 1024 * k, true);
     }
   };
   constexpr int NCP = SONLY ? G::NCOPY_S : G::NCOPY;
-  if (wave == 8) {
-    for (int i = 0; i < NST - 1 && i < cnt; ++i) issue(i);
-    for (int i = 0; i < cnt; ++i) {
-      // stage i has landed once only the copies of later stages remain
-      if (NST > 2 && i + 1 < cnt)
-        wait_vmcnt<(NCP < 63 ? NCP : 63)>();
-      else
-        wait_vmcnt<0>();
-      lds_barrier();
-      if (i + NST - 1 < cnt) issue(i + NST - 1);
-    }
+  if (wave >= 8) {
+    const int cw = wave - 8;
+    // copy wave cw's instructions per chunk: every K2B_COPY_WAVES-th from the cw-th
+    auto copy_loop = [&](auto per_chunk) {
+      constexpr int W = decltype(per_chunk)::value;
+      for (int i = 0; i < NST - 1 && i < cnt; ++i) issue(i, cw);
+      for (int i = 0; i < cnt; ++i) {
+        // stage i has landed once only the copies of later stages remain
+        if (NST > 2 && i + 1 < cnt)
+          wait_vmcnt<(W < 63 ? W : 63)>();
+        else
+          wait_vmcnt<0>();
+        lds_barrier();
+        if (i + NST - 1 < cnt) issue(i + NST - 1, cw);
+      }
+    };
+    static_assert(K2B_COPY_WAVES == 2, "copy-wave split");
+    if (cw == 0)
+      copy_loop(std::integral_constant<int, (NCP + 1) / 2>());
+    else
+      copy_loop(std::integral_constant<int, NCP / 2>());
     return;
   }
 
