@@ -179,19 +179,20 @@ msgla_status msgla_state_init(const msgla_config* cfg, int64_t B, void* state, s
  *         it as sum / max(1, tokens).
  *   state_in: NULL (start from an empty state), or a state of the same
  *         config and B (written by msgla_forward's state_out,
- *         msgla_state_init or msgla_decode_step) to continue from: its GLA
- *         states seed the recurrences and its held outputs fill the
- *         positions before each coarse branch's first block of this call.
- *         Its position must be a multiple of every scale (no block in
- *         progress).  Its header is checked on the device, in stream order
- *         (the call does not synchronise and can be captured in a graph):
- *         when it does not describe this config and B, records an error, or
- *         sits inside a block, nothing past the header is read, every element
- *         of out is NaN, and state_out (if given) records the error
- *         (MSGLA_ERR_INVALID_ARG, or MSGLA_ERR_UNSUPPORTED for a position
- *         inside a block) with position -1; msgla_state_query reads it.  The
- *         call itself then still returns MSGLA_OK.  state_in may equal
- *         state_out.
+ *         msgla_state_init or msgla_decode_step) to continue from, at any
+ *         position: its GLA states seed the recurrences, each branch's block
+ *         in progress (r = position mod s positions, kept as their sum and
+ *         token count) is completed by the first s - r positions of this
+ *         call, and its held outputs fill the positions before each coarse
+ *         branch's first completed block.  The result equals one forward
+ *         over the concatenated tokens.  Its header is checked on the
+ *         device, in stream order (the call does not synchronise and can be
+ *         captured in a graph): when it does not describe this config and B
+ *         or records an error, nothing past the header is read, every
+ *         element of out is NaN, and state_out (if given) records the error
+ *         (MSGLA_ERR_INVALID_ARG) with position -1; msgla_state_query reads
+ *         it.  The call itself then still returns MSGLA_OK.  state_in may
+ *         equal state_out.
  *   state_out: NULL, or a buffer of msgla_state_bytes(cfg, B) that receives
  *         the streaming state after the L tokens (for msgla_decode_step).
  *   workspace: >= msgla_workspace_bytes(cfg, B, L) bytes of device memory;

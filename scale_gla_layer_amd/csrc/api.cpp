@@ -23,6 +23,7 @@ hipError_t launch_state_export(const StateParams& P, bool bf16_path, hipStream_t
 hipError_t launch_state_header(void* state, int B, int m, int64_t pos, const StateCheck* chk,
                                hipStream_t st);
 hipError_t launch_state_check(const StateCheckParams& P, hipStream_t st);
+hipError_t launch_pending_gate(const PendingGateParams& P, bool bf16_path, hipStream_t st);
 hipError_t launch_decode(const DecParams& P, int Nmax, int hmax, bool bf16_path, hipStream_t st);
 hipError_t launch_norm(const NormParams& P, bool bf16_path, hipStream_t st);
 hipError_t pack_transpose(bool bf16_path, const void* src, int R, int Cn, void* dst,
@@ -180,13 +181,15 @@ struct WsBranch {
 };
 struct WsGeom {
   WsBranch br[MSGLA_MAX_BRANCHES];
-  size_t w, chk, total;
+  size_t w, chk, psumg, total;
   int nseg;        // segments of the chunk-state walk (1: one walk per sequence)
   int seg_base;    // workgroups of one segment
   size_t Sseg;     // segment states, when nseg > 1
 };
 
-WsGeom ws_geom(const PackGeom& g, int64_t B, int64_t L) {
+// cont: the call continues from a state, whose blocks may start before the
+// call, so a branch of scale s can complete ceil(L / s) blocks, not floor.
+WsGeom ws_geom(const PackGeom& g, int64_t B, int64_t L, bool cont) {
   WsGeom w{};
   size_t cur = 0;
   auto take = [&](size_t bytes) {
@@ -197,7 +200,7 @@ WsGeom ws_geom(const PackGeom& g, int64_t B, int64_t L) {
   for (int i = 0; i < g.m; ++i) {
     const BranchGeom& bg = g.br[i];
     WsBranch& b = w.br[i];
-    b.n = (int)(L / bg.s);
+    b.n = (int)(cont ? (L + bg.s - 1) / bg.s : L / bg.s);
     b.nch = cdiv(b.n, g.C);
     b.np = b.nch * g.C;
     const size_t rows = (size_t)B * bg.h * b.np;
@@ -216,6 +219,7 @@ WsGeom ws_geom(const PackGeom& g, int64_t B, int64_t L) {
   }
   w.w = take((size_t)B * L * FUSION_STRIDE * 4);
   w.chk = take(sizeof(StateCheck));  // the device-side check of state_in
+  w.psumg = take((size_t)g.m * B * g.rp * 4);  // pending gate sums of a continuing call
   // The chunk-state walk runs one workgroup per (sequence, 32-wide d_v slice).
   // With few of them (small batches of long sequences) the sequential walk over
   // the chunks leaves most CUs idle, so each walk is cut into segments (at least
@@ -323,7 +327,8 @@ size_t msgla_packed_weights_bytes(const msgla_config* cfg) {
 
 size_t msgla_workspace_bytes(const msgla_config* cfg, int64_t B, int64_t L) {
   if (check_config(cfg) != MSGLA_OK || !batch_ok(B, L)) return 0;
-  return ws_geom(pack_geom(cfg), B, L).total;
+  // the larger of the two layouts (a continuing call may pool one more block)
+  return ws_geom(pack_geom(cfg), B, L, true).total;
 }
 
 size_t msgla_state_bytes(const msgla_config* cfg, int64_t B) {
@@ -418,14 +423,17 @@ msgla_status msgla_forward_timed(const msgla_config* cfg, const void* packed, co
       (state_out && !aligned16(state_out)) || (state_in && !aligned16(state_in)))
     return MSGLA_ERR_INVALID_ARG;
   const PackGeom g = pack_geom(cfg);
-  const WsGeom W = ws_geom(g, B, L);
+  const WsGeom W = ws_geom(g, B, L, state_in != nullptr);
   if (workspace_bytes < W.total) return MSGLA_ERR_WORKSPACE;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const StGeom S = st_geom(g, B);
   // Continuing from a state: its header is checked on the device (this
-  // configuration and batch, a position at a block boundary of every branch,
-  // so that the blocks of this call start at its first token); every kernel
-  // that reads the state reads it only if the check passed.
+  // configuration and batch, no recorded error); the check also gives every
+  // branch's entry offset r = position mod s (block 0 of the call completes
+  // the state's pending block) and the number of blocks the call completes.
+  // Every kernel that reads the state, or depends on the offsets, reads the
+  // check's result; the state itself only if the check passed.  The pending
+  // block's gate first factors are summed here, as psum W_g1.
   const StateCheck* chk = nullptr;
   if (state_in) {
     StateCheckParams pc{};
@@ -433,9 +441,22 @@ msgla_status msgla_forward_timed(const msgla_config* cfg, const void* packed, co
     pc.out = at<StateCheck>(workspace, W.chk);
     pc.B = (int)B;
     pc.m = g.m;
+    pc.L = (int)L;
     for (int i = 0; i < g.m; ++i) pc.scale[i] = g.br[i].s;
     HIP_TRY(launch_state_check(pc, st));
     chk = pc.out;
+    PendingGateParams pg{};
+    pg.B = (int)B;
+    pg.d = g.d;
+    pg.rp = g.rp;
+    pg.m = g.m;
+    pg.chk = chk;
+    for (int i = 0; i < g.m; ++i) {
+      pg.br[i].Wg1 = at<char>(packed, g.br[i].off_Wp + (size_t)g.br[i].col_g * g.d * g.es);
+      pg.br[i].psum = at<float>(state_in, S.psum[i]);
+      pg.br[i].out = at<float>(workspace, W.psumg) + (size_t)i * B * g.rp;
+    }
+    HIP_TRY(launch_pending_gate(pg, g.bf16, st));
   }
 
   auto ev = [&](int stage, bool start) -> hipError_t {
@@ -552,6 +573,8 @@ msgla_status msgla_forward_timed(const msgla_config* cfg, const void* packed, co
     k.y = at<char>(workspace, wb.y);
     k.S_out = state_out ? at<float>(state_out, S.S[i]) : nullptr;
     k.S_in = state_in ? at<float>(state_in, S.S[i]) : nullptr;
+    k.psumg = state_in ? at<float>(workspace, W.psumg) + (size_t)i * B * g.rp : nullptr;
+    k.tok_in = state_in ? at<float>(state_in, S.tok[i]) : nullptr;
   }
   p2.total_units = units;
   // K2b: sequences ordered by decreasing chunk count (longest walks start first)
@@ -637,6 +660,7 @@ msgla_status msgla_forward_timed(const msgla_config* cfg, const void* packed, co
       q = PoolParams{};
       q.x = x;
       q.mask = mask;
+      q.chk = chk;
       q.B = (int)B;
       q.L = (int)L;
       q.d = g.d;
@@ -650,6 +674,9 @@ msgla_status msgla_forward_timed(const msgla_config* cfg, const void* packed, co
         o.s = s;
         o.n = W.br[i].n;
         o.inv_s = 1.0f / (float)s;
+        o.branch = i;
+        o.psum_in = state_in ? at<float>(state_in, S.psum[i]) : nullptr;
+        o.tok_in = state_in ? at<float>(state_in, S.tok[i]) : nullptr;
         done[i] = true;
       }
     }
@@ -722,6 +749,8 @@ msgla_status msgla_forward_timed(const msgla_config* cfg, const void* packed, co
       b.y = at<char>(workspace, W.br[i].y);
       b.S_in = state_in ? at<float>(state_in, S.S[i]) : nullptr;
       b.held_in = state_in ? at<float>(state_in, S.held[i]) : nullptr;
+      b.psum_in = state_in ? at<float>(state_in, S.psum[i]) : nullptr;
+      b.tok_in = state_in ? at<float>(state_in, S.tok[i]) : nullptr;
     }
     HIP_TRY(launch_state_export(ps, g.bf16, st));
   }

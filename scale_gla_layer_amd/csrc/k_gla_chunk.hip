@@ -120,7 +120,9 @@ __global__ __launch_bounds__(256) void k2a_gla_chunk(const K2Params P) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 15, lg = lane >> 4;
   const int row0 = chunk * C;                  // first pooled row of the chunk
-  const int valid = min(C, Bb.n - row0);       // real rows in this chunk
+  // real rows in this chunk: the blocks this call completes (continuing from
+  // a state, floor((L + r) / s) with r positions of block 0 pending on entry)
+  const int valid = min(C, blocks_in_call(P.chk, bi, Bb.n) - row0);
   const int p = 16 * w + lr;                   // this lane's position in the chunk
   const bool live = p < valid;
 
@@ -167,18 +169,30 @@ __global__ __launch_bounds__(256) void k2a_gla_chunk(const K2Params P) {
   auto load_gate_factor = [&](float (&gb)[RP / 4]) {
     // x W_g1 is given per unpooled position: the block's mean is this row's value
     const float* gr = Bb.g + ((size_t)b * P.L + (size_t)(row0 + pl) * Bb.s) * RP + lg;
-    if (P.mask) {
-      // Eq. (8) with a token mask: the block's mean over its tokens,
-      // sum M x W_g1 / max(1, sum M) (for s = 1: M_t x_t W_g1)
-      const uint8_t* mr = P.mask + (size_t)b * P.L + (size_t)(row0 + pl) * Bb.s;
+    if (P.mask || P.chk) {
+      // Eq. (8) in general: the block's mean over its tokens, sum M x W_g1 /
+      // max(1, sum M) (for s = 1: M_t x_t W_g1; without a mask every
+      // position is a token).  Continuing from a state, block j covers call
+      // positions [j s - r, (j + 1) s - r): block 0 starts with the entry
+      // state's pending positions, whose x W_g1 sum and token count it holds.
+      const int t_lo = (row0 + pl) * Bb.s - entry_offset(P.chk, bi);
+      const float* gq = Bb.g + (size_t)b * P.L * RP + lg;
+      const uint8_t* mr = P.mask ? P.mask + (size_t)b * P.L : nullptr;
       float den = 0.f;
 #pragma unroll
       for (int k4 = 0; k4 < RP / 4; ++k4) gb[k4] = 0.f;
+      if (t_lo < 0 && Bb.psumg && state_in_ok(P.chk)) {
+#pragma unroll
+        for (int k4 = 0; k4 < RP / 4; ++k4) gb[k4] = Bb.psumg[(size_t)b * RP + 4 * k4 + lg];
+        den = Bb.tok_in[b];
+      }
       for (int u = 0; u < Bb.s; ++u) {
-        const float w = mr[u] ? 1.f : 0.f;
+        const int t = t_lo + u;
+        if (t < 0 || t >= P.L) continue;
+        const float w = mr ? (mr[t] ? 1.f : 0.f) : 1.f;
         den += w;
 #pragma unroll
-        for (int k4 = 0; k4 < RP / 4; ++k4) gb[k4] += w * gr[(size_t)u * RP + 4 * k4];
+        for (int k4 = 0; k4 < RP / 4; ++k4) gb[k4] += w * gq[(size_t)t * RP + 4 * k4];
       }
       const float sc = 1.0f / fmaxf(1.f, den);
 #pragma unroll

@@ -235,7 +235,7 @@ __global__ __launch_bounds__(K2B_THREADS) void k2b_gla_state(const K2Params P) {
     lds_barrier();  // stage i has landed (the copy wave waited for it)
 
     const char* st = smem + (i % NST) * G::STAGE;
-    const int valid = min(C, Bb.n - c * C);
+    const int valid = min(C, blocks_in_call(P.chk, bi, Bb.n) - c * C);
 
     // V fragments (B-operand of both products); positions >= valid zeroed
     u32x4 vf[G::NSC][2];

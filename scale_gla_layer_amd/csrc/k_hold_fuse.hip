@@ -197,7 +197,9 @@ struct K3Fine : K3Rows<T> {
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
           const K3Branch& Bi = P.br[P.coarse[c]];
-          const int j = (t + 1) / Bi.s - 1;  // held coarse row (none before the first block)
+          // held coarse row (none before the call's first block; continuing
+          // from a state, the blocks start r = entry position mod s early)
+          const int j = (t + 1 + (HELD ? entry_offset(P.chk, P.coarse[c]) : 0)) / Bi.s - 1;
           held[u][c] = j >= 0;
           // a branch without a block in this call has no coarse rows: read a
           // valid word of its entry output instead (dropped)

@@ -165,8 +165,69 @@ __global__ __launch_bounds__(256) void k_pool_pow2(const PoolParams P) {
   }
 }
 
+// A forward continuing from a state: branch s's blocks start r = (entry
+// position mod s) positions before the call (block 0 completes the entry
+// state's pending block, whose masked sum and token count the state holds),
+// so they no longer line up across scales.  One thread per (branch, b, block
+// j, 16-byte column piece) sums the block's positions in the call, [j s - r,
+// (j + 1) s - r) within [0, L), plus for block 0 the pending sum, and divides
+// by the token count: Eq. (8), where positions of the call without a mask
+// count as tokens.  Rows j >= floor((L + r) / s) are not written.
+template <typename T>
+__global__ __launch_bounds__(256) void k_pool_cont(const PoolParams P) {
+  constexpr int PER = per16<T>();
+  const int pieces = P.d / PER;
+  long idx = (long)blockIdx.x * 256 + threadIdx.x;
+  int i = 0;
+  for (; i < P.nout; ++i) {
+    const long cnt = (long)P.B * P.out[i].n * pieces;
+    if (idx < cnt) break;
+    idx -= cnt;
+  }
+  if (i >= P.nout) return;
+  const PoolOut& o = P.out[i];
+  const int piece = (int)(idx % pieces);
+  const long bj = idx / pieces;
+  const int j = (int)(bj % o.n), b = (int)(bj / o.n);
+  const int r = entry_offset(P.chk, o.branch), nv = blocks_in_call(P.chk, o.branch, o.n);
+  if (j >= nv) return;
+  const int t_lo = j * o.s - r, t_hi = min(t_lo + o.s, P.L);
+  float acc[PER], den = 0.f;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) acc[e] = 0.f;
+  if (t_lo < 0 && o.psum_in && state_in_ok(P.chk)) {
+    // the entry state's pending positions (block 0 only)
+    const float* ps = o.psum_in + (size_t)b * P.d + piece * PER;
+#pragma unroll
+    for (int e = 0; e < PER; e += 4) unpack16<float>(ld16(ps + e), acc + e);
+    den = o.tok_in[b];
+  }
+  const T* x = reinterpret_cast<const T*>(P.x) + (size_t)b * P.L * P.d + piece * PER;
+  const uint8_t* mk = P.mask ? P.mask + (size_t)b * P.L : nullptr;
+  for (int t = max(t_lo, 0); t < t_hi; ++t) {
+    const float w = mk ? (mk[t] ? 1.f : 0.f) : 1.f;
+    float v[PER];
+    unpack16<T>(ld16(x + (size_t)t * P.d), v);
+#pragma unroll
+    for (int e = 0; e < PER; ++e) acc[e] += w * v[e];
+    den += w;
+  }
+  const float sc = 1.0f / fmaxf(1.f, den);
+  float m[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) m[e] = acc[e] * sc;
+  store_mean<T>(o, ((size_t)b * o.n + j) * P.d + piece * PER, m);
+}
+
 template <typename T>
 static void launch_pool_t(const PoolParams& P, hipStream_t st) {
+  if (P.chk) {
+    long threads = 0;
+    for (int i = 0; i < P.nout; ++i) threads += (long)P.B * P.out[i].n * (P.d / per16<T>());
+    if (threads == 0) return;
+    hipLaunchKernelGGL(k_pool_cont<T>, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, P);
+    return;
+  }
   const long threads = (long)P.B * ((P.L + P.smax - 1) / P.smax) * (P.d / per16<T>());
   const dim3 grid((unsigned)((threads + 255) / 256)), block(256);
   switch (threads + 255 < (1L << 31) ? P.smax : 0) {

@@ -71,14 +71,29 @@ struct StateCheck {
   int32_t status;
   int32_t pad;
   int64_t pos;
+  // per branch: positions of the block in progress on entry (pos mod s), and
+  // the blocks that complete in this call, floor((L + r) / s); block j of the
+  // call covers call positions [j s - r, (j + 1) s - r)
+  int32_t r[MSGLA_MAX_BRANCHES];
+  int32_t nv[MSGLA_MAX_BRANCHES];
 };
 
 struct StateCheckParams {
   const void* state_in;
   StateCheck* out;
-  int B, m;
+  int B, m, L;
   int scale[MSGLA_MAX_BRANCHES];
 };
+
+// The entry offset r and complete-block count of branch i for a forward's
+// kernels: from the device-side check when the call continues from a state
+// that passed it, else (a fresh call) 0 and n.
+__host__ __device__ inline int entry_offset(const StateCheck* chk, int i) {
+  return chk && chk->status == 0 ? chk->r[i] : 0;
+}
+__host__ __device__ inline int blocks_in_call(const StateCheck* chk, int i, int n) {
+  return chk && chk->status == 0 ? chk->nv[i] : n;
+}
 
 // ---------------- pooling prepass ------------------------------------------------
 struct PoolOut {
@@ -86,11 +101,15 @@ struct PoolOut {
   void* xp_lo;      // [B][n][d] bf16 residuals m - bf16(m) of the means, or null
   int s, n;
   float inv_s;
+  int branch;       // index of the branch (its entry offset in StateCheck)
+  const float* psum_in;  // continuing: the entry state's pending sum [B][d] and
+  const float* tok_in;   // token count [B] of this branch (block 0 of the call)
 };
 
 struct PoolParams {
   const void* x;    // [B][L][d]
   const uint8_t* mask;  // [B][L] token mask of Eq. (8) (nonzero = token), or null
+  const StateCheck* chk;  // continuing from a state: its check (entry offsets), else null
   int B, L, d, smax, nout;
   PoolOut out[MSGLA_MAX_BRANCHES];
   int lvl[8];       // power-of-two smax: out index of scale 2^l, or -1 (set by the launcher)
@@ -168,6 +187,11 @@ struct K2Branch {
   void* y;
   float* S_out;     // state S of this branch [B][h][dk][dv] or null
   const float* S_in;  // state S the walk starts from [B][h][dk][dv], null: zero
+  // continuing: block 0 of the call completes the entry state's pending block,
+  // whose gate first factors sum to psumg [B][rp] (its pending sum times W_g1)
+  // over tok_in [B] tokens
+  const float* psumg;
+  const float* tok_in;
 };
 
 struct K2Params {
@@ -232,6 +256,20 @@ struct StateBranch {
   const void* y;    // forward workspace y (export only)
   const float* S_in;     // state the forward started from (kept when n == 0), or null
   const float* held_in;
+  const float* psum_in;  // the entry state's pending sum and token count, or null
+  const float* tok_in;
+};
+
+// Pending-gate sums of a continuing forward (k_pending_gate).
+struct PendingGateBranch {
+  const void* Wg1;  // [rp][d] the branch's W_g1, transposed (rows of its packed block)
+  const float* psum;  // entry state's pending sum [B][d]
+  float* out;       // [B][rp]
+};
+struct PendingGateParams {
+  int B, d, rp, m;
+  const StateCheck* chk;
+  PendingGateBranch br[MSGLA_MAX_BRANCHES];
 };
 
 struct StateParams {

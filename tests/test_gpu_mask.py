@@ -168,10 +168,14 @@ def test_masked_state_export_matches_oracle():
                 assert np.abs(a - b).max() <= 1e-4 * scale + 1e-12, (L, key)
 
 
-@pytest.mark.parametrize("cfg_name,B,L1,L2", [("tiny_f32", 2, 32, 50), ("main", 2, 128, 100)])
+@pytest.mark.parametrize("cfg_name,B,L1,L2", [("tiny_f32", 2, 32, 50), ("main", 2, 128, 100),
+                                               ("tiny_f32", 2, 31, 50), ("tiny_f32", 2, 6, 1),
+                                               ("main", 2, 130, 99)])
 def test_masked_forward_continues_from_a_state(cfg_name, B, L1, L2):
     """Two masked forwards, the second from the first's state (split at a
-    block boundary of every scale), against one masked forward."""
+    block boundary of every scale, or inside blocks: then the second call's
+    first block of a coarse branch completes the pending one, whose masked
+    sum and token count the state holds), against one masked forward."""
     import torch
     from oracle import msgla_oracle as orc
     from scale_gla_layer_amd.runner import DeviceLayer, to_device

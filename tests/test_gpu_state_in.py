@@ -1,15 +1,17 @@
 """GPU: a forward that continues from a state (state_in) against the fp64
 oracle run over the whole sequence in one pass.
 
-Splitting a sequence at a position that is a multiple of every scale and
-running the second part from the first part's state must give the outputs
-(and the final state) of one forward over the whole sequence, to the same
-bar as every other parity case.  Covers: coarse branches whose first
-positions in the second part take the output held from the first part, a
-second part shorter than a coarse scale (that branch then contributes only
-its held output, and keeps its state), state_in equal to state_out, the
-device-side checks (a position inside a block, a header of another batch, a
-state that records an error), and graph capture of a continuing forward."""
+Splitting a sequence anywhere and running the second part from the first
+part's state must give the outputs (and the final state) of one forward over
+the whole sequence, to the same bar as every other parity case.  Covers:
+splits at a block boundary of every scale and inside blocks (then each
+coarse branch's first block in the second part completes the block the state
+holds in progress), coarse branches whose first positions in the second part
+take the output held from the first part, a second part shorter than a
+coarse scale (that branch then contributes only its held output, and keeps
+its state), decode steps between two forwards, state_in equal to state_out,
+the device-side checks (a header of another batch, a state that records an
+error), and graph capture of a continuing forward."""
 import numpy as np
 import pytest
 
@@ -47,6 +49,14 @@ def _split_run(cfg, B, L1, L2, seed, same_buffer, gate_bias=None):
     ("main", 1, 256, 2, False),       # scale 4 sees no block in the second part
     ("tiny_f32", 1, 512, 600, False), # both parts walk the chunk states in segments
     ("tiny_f32", 2, 400, 300, True),
+    # splits inside blocks: block 0 of the second part completes the pending one
+    ("tiny_f32", 2, 6, 50, False),    # r = 2 for scale 4
+    ("tiny_f32", 2, 33, 47, True),    # r = 1 for scales 2 and 4
+    ("tiny_f32", 1, 7, 1, False),     # the second part completes scale 4's block only
+    ("tiny_f32", 2, 5, 2, False),     # scale 4's block stays pending across the call
+    ("tiny_f32", 1, 513, 599, False), # segmented walks after an offset
+    ("main", 2, 131, 101, True),
+    ("main", 1, 258, 3, False),
 ])
 def test_continue_matches_one_pass(cfg_name, B, L1, L2, same):
     cfg = WORKLOADS[cfg_name].cfg
@@ -79,25 +89,31 @@ def _all_nan(t) -> bool:
     return bool(torch.isnan(t.float()).all())
 
 
-def test_position_inside_a_block_is_unsupported():
-    """Checked on the device: the call returns, nothing past the header is
-    read, the output is NaN and state_out records MSGLA_ERR_UNSUPPORTED."""
+@pytest.mark.parametrize("cfg_name,B,L1,steps,L2", [
+    ("tiny_f32", 2, 30, 3, 40),   # 33: inside scale 2's and 4's blocks
+    ("tiny_f32", 1, 8, 1, 5),
+    ("main", 2, 128, 5, 70),
+])
+def test_forward_after_decode_steps(cfg_name, B, L1, steps, L2):
+    """A prefill, a few decode steps (any number, so the position may fall
+    inside a block), then a forward over the rest from the same state: the
+    outputs of all three against one oracle pass."""
     import torch
-    cfg = TINY
-    X, W = make_inputs(cfg, 1, 40, seed=12)
+    cfg = WORKLOADS[cfg_name].cfg
+    say(f"prefill {L1} + {steps} decode steps + forward {L2}: {cfg_name} B={B}")
+    L = L1 + steps + L2
+    X, W = make_inputs(cfg, B, L, seed=16)
     layer = DeviceLayer(cfg, W)
-    st = layer.new_state(1)
-    layer.forward(to_device(X[:, :6], cfg.dtype), state_out=st)  # 6 is not a multiple of 4
-    say("state_in at position 6 (scale 4 has a block in progress)")
-    st2 = layer.new_state(1)
-    out = layer.forward(to_device(X[:, 6:], cfg.dtype), state_in=st, state_out=st2)
+    st = layer.new_state(B)
+    outs = [from_device(layer.forward(to_device(X[:, :L1], cfg.dtype), state_out=st))]
+    for t in range(L1, L1 + steps):
+        o = layer.decode_step(to_device(np.ascontiguousarray(X[:, t]), cfg.dtype), st)
+        outs.append(from_device(o)[:, None, :])
+    outs.append(from_device(layer.forward(to_device(X[:, L1 + steps:], cfg.dtype), state_in=st,
+                                          state_out=st)))
     torch.cuda.synchronize()
-    assert _all_nan(out)
-    info = binding.msgla_state_query(st2)
-    assert info["status"] == 2 and info["position"] == -1
-    assert binding.msgla_state_query(st) == {"status": 0, "B": 1, "m": 3, "position": 6}
-    # without state_out the NaN output is the only sign
-    assert _all_nan(layer.forward(to_device(X[:, 6:], cfg.dtype), state_in=st))
+    check_against_oracle(cfg, X, W, np.concatenate(outs, axis=1))
+    assert binding.msgla_state_query(st)["position"] == L
 
 
 def test_state_of_another_batch_is_rejected():
@@ -117,27 +133,32 @@ def test_state_of_another_batch_is_rejected():
 
 
 def test_error_state_propagates_and_decode_refuses_it():
-    """A state that records an error is refused by the next forward (status 1)
+    """A state that records an error (here: written by a forward whose entry
+    state had another batch size) is refused by the next forward (status 1)
     and by the decode step (NaN output, the state unchanged)."""
     import torch
     cfg = TINY
-    X, W = make_inputs(cfg, 1, 48, seed=15)
+    X, W = make_inputs(cfg, 2, 48, seed=15)
     layer = DeviceLayer(cfg, W)
-    st = layer.new_state(1)
+    st = layer.new_state(2)
     layer.forward(to_device(X[:, :6], cfg.dtype), state_out=st)
-    bad = layer.new_state(1)
-    layer.forward(to_device(X[:, 6:10], cfg.dtype), state_in=st, state_out=bad)
+    one = layer.new_state(1)
+    layer.state_init(one, 1)
+    bad = layer.new_state(2)
+    layer.forward(to_device(X[:, 6:10], cfg.dtype), state_in=one, state_out=bad)
+    torch.cuda.synchronize()
+    assert binding.msgla_state_query(bad)["status"] == 1
     say("forward and decode from a state that records an error")
-    bad2 = layer.new_state(1)
+    bad2 = layer.new_state(2)
     out = layer.forward(to_device(X[:, 10:18], cfg.dtype), state_in=bad, state_out=bad2)
     torch.cuda.synchronize()
     assert _all_nan(out) and binding.msgla_state_query(bad2)["status"] == 1
     before = bad.clone()
-    o = layer.decode_step(to_device(X[:, 10], cfg.dtype), bad)
+    o = layer.decode_step(to_device(np.ascontiguousarray(X[:, 10]), cfg.dtype), bad)
     torch.cuda.synchronize()
     assert _all_nan(o) and torch.equal(bad, before)
     # the usable state still decodes
-    o = layer.decode_step(to_device(X[:, 6], cfg.dtype), st)
+    o = layer.decode_step(to_device(np.ascontiguousarray(X[:, 6]), cfg.dtype), st)
     torch.cuda.synchronize()
     assert not torch.isnan(o.float()).any()
     assert binding.msgla_state_query(st)["position"] == 7
