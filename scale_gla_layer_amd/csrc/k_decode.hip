@@ -172,7 +172,22 @@ __global__ __launch_bounds__(DEC_THREADS) void k_dec_state(const DecParams P) {
   const float* pr = Br.proj + (size_t)b * Br.N;
   for (int c = threadIdx.x; c < P.dk; c += DEC_THREADS) {
     float z = Br.bg[hh * P.dk + c];
-    for (int r = 0; r < P.r; ++r) z = fmaf(pr[Br.col_g + r], Br.W2[(size_t)r * Br.h * P.dk + hh * P.dk + c], z);
+    // z = b_g + g1 W_g2: the rank loop 16 terms at a time, all their loads in
+    // flight before the first product (same summation order)
+    const float* w2 = Br.W2 + hh * P.dk + c;
+    const size_t w2s = (size_t)Br.h * P.dk;
+    for (int r0 = 0; r0 < P.r; r0 += 16) {
+      float pv[16], wv[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const int rr = min(r0 + u, P.r - 1);
+        pv[u] = pr[Br.col_g + rr];
+        wv[u] = w2[(size_t)rr * w2s];
+      }
+#pragma unroll
+      for (int u = 0; u < 16; ++u)
+        if (r0 + u < P.r) z = fmaf(pv[u], wv[u], z);
+    }
     alpha[c] = __expf(logsigmoid_f(z) * P.inv_gamma);
     kk[c] = pr[Br.col_k + hh * P.dk + c];
     qq[c] = pr[hh * P.dk + c] * P.q_scale;
@@ -185,13 +200,13 @@ __global__ __launch_bounds__(DEC_THREADS) void k_dec_state(const DecParams P) {
     const float vv = pr[Br.col_v + hh * P.dv + v];
     float* S = Br.S + (size_t)bh * P.dk * P.dv + v;
     const int cq = (P.dk + 3) / 4, c1 = min(P.dk, (wave + 1) * cq);
-    // rows of S 16 at a time, all 16 loads in flight before the updates
-    for (int c0 = wave * cq; c0 < c1; c0 += 16) {
-      float sv[16];
+    // rows of S 32 at a time, all 32 loads in flight before the updates
+    for (int c0 = wave * cq; c0 < c1; c0 += 32) {
+      float sv[32];
 #pragma unroll
-      for (int u = 0; u < 16; ++u) sv[u] = c0 + u < c1 ? S[(size_t)(c0 + u) * P.dv] : 0.f;
+      for (int u = 0; u < 32; ++u) sv[u] = S[(size_t)min(c0 + u, c1 - 1) * P.dv];
 #pragma unroll
-      for (int u = 0; u < 16; ++u) {
+      for (int u = 0; u < 32; ++u) {
         const int c = c0 + u;
         if (c < c1) {
           const float sn = fmaf(alpha[c], sv[u], kk[c] * vv);
@@ -265,16 +280,26 @@ __global__ __launch_bounds__(DEC_THREADS) void k_dec_out(const DecParams P) {
   }
   if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0)
     reinterpret_cast<StateHeader*>(P.state)->pos = pos + 1;
-  // fusion weights of this lane's four sequences: the softmax's maximum and sum
-  float zmax[4], zsum[4];
+  // fusion logits of this lane's four sequences (all loaded at once), the
+  // softmax's maximum and sum
+  float zl[4][FUSION_STRIDE], zmax[4], zsum[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    const int bb = min(b0 + 4 * lg + e, P.B - 1);
+    const float* wr = P.w + (size_t)min(b0 + 4 * lg + e, P.B - 1) * FUSION_STRIDE;
+#pragma unroll
+    for (int q = 0; q < FUSION_STRIDE; q += 4) unpack16<float>(ld16(wr + q), zl[e] + q);
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
     zmax[e] = -INFINITY;
     zsum[e] = 0.f;
     if (P.m > 1) {
-      for (int i = 0; i < P.m; ++i) zmax[e] = fmaxf(zmax[e], P.w[(size_t)bb * FUSION_STRIDE + i] + P.bf[i]);
-      for (int i = 0; i < P.m; ++i) zsum[e] += __expf(P.w[(size_t)bb * FUSION_STRIDE + i] + P.bf[i] - zmax[e]);
+#pragma unroll
+      for (int i = 0; i < FUSION_STRIDE; ++i)
+        if (i < P.m) zmax[e] = fmaxf(zmax[e], zl[e][i] + P.bf[i]);
+#pragma unroll
+      for (int i = 0; i < FUSION_STRIDE; ++i)
+        if (i < P.m) zsum[e] += __expf(zl[e][i] + P.bf[i] - zmax[e]);
     }
   }
   f32x4 o = zero4();
@@ -301,9 +326,10 @@ __global__ __launch_bounds__(DEC_THREADS) void k_dec_out(const DecParams P) {
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int bb = min(b0 + 4 * lg + e, P.B - 1);
-      const float wi = P.m > 1 ? __expf(P.w[(size_t)bb * FUSION_STRIDE + i] + P.bf[i] - zmax[e]) / zsum[e]
-                               : 1.f;
+      float zi = 0.f;  // branch i's logit (register select, no dynamic index)
+#pragma unroll
+      for (int q = 0; q < FUSION_STRIDE; ++q) zi = q == i ? zl[e][q] : zi;
+      const float wi = P.m > 1 ? __expf(zi + P.bf[i] - zmax[e]) / zsum[e] : 1.f;
       o[e] += wi * held[e];
     }
   }
