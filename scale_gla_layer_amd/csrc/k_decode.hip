@@ -113,20 +113,22 @@ __device__ __forceinline__ f32x4 dec_reduce4(f32x4 acc, float* red, int wave, in
 // the four waves take a quarter of K each
 template <typename T>
 __global__ __launch_bounds__(DEC_THREADS) void k_dec_proj(const DecParams P) {
+  // the header is read first but used only after the block's loads and
+  // products, which do not depend on it, so its round trip overlaps theirs
+  // (a block whose branch does not complete this step discards its result)
   const int64_t pos = dec_pos(P);
-  if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x == 0)
-    *P.pos_ws = pos;  // this step's position, for the later kernels
-  if (pos < 0) return;
   const bool logits = blockIdx.y == P.nbranch;
-  if (logits && P.m == 1) return;
   const DecBranch& Br = P.br[logits ? 0 : blockIdx.y];
-  if (!logits && !completes(pos, Br.s)) return;
   const int N = logits ? P.m : Br.N;
+  const int n0 = blockIdx.x * 16, b0 = blockIdx.z * 16;
+  const bool block0 = blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0;
+  if ((logits && P.m == 1) || n0 >= N) {
+    if (block0 && threadIdx.x == 0) *P.pos_ws = pos;
+    return;
+  }
   __shared__ __attribute__((aligned(16))) float red[3 * 64 * 4];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int lr = lane & 15, lg = lane >> 4;
-  const int n0 = blockIdx.x * 16, b0 = blockIdx.z * 16;
-  if (n0 >= N) return;
   constexpr int PER = per16<T>(), SLAB = 4 * PER;
   const int n = min(n0 + lr, N - 1), b = b0 + lr;  // B-operand row, A-operand row
   const int bc = b < P.B ? b : 0;
@@ -144,6 +146,8 @@ __global__ __launch_bounds__(DEC_THREADS) void k_dec_proj(const DecParams P) {
     const float inv = 1.0f / fmaxf(1.f, Br.tok[bc] + 1.f);
     acc = dec_rows_times_cols<T, true, true>(frow, trow, inv, b < P.B, wrow, k_hi - k_lo, zero4());
   }
+  if (block0 && threadIdx.x == 0) *P.pos_ws = pos;  // this step's position, for the later kernels
+  if (pos < 0 || (!logits && !completes(pos, Br.s))) return;  // block-uniform
   acc = dec_reduce4(acc, red, wave, lane);
   if (wave != 0) return;
   // acc[e]: sequence b0 + 4 lg + e, column n0 + lr
@@ -159,10 +163,11 @@ __global__ __launch_bounds__(DEC_THREADS) void k_dec_proj(const DecParams P) {
 // grid (B * hmax, ceil(dv / 64), m); 256 threads: lane -> v column, wave -> quarter of d_k
 __global__ __launch_bounds__(DEC_THREADS) void k_dec_state(const DecParams P) {
   const DecBranch& Br = P.br[blockIdx.z];
-  const int64_t pos = *P.pos_ws;
-  if (pos < 0 || !completes(pos, Br.s)) return;
   const int bh = blockIdx.x;
   if (bh >= P.B * Br.h) return;
+  // the position is read first and used after the gate, which does not
+  // depend on it (a branch that does not complete discards the gate)
+  const int64_t pos = *P.pos_ws;
   const int b = bh / Br.h, hh = bh - b * Br.h;
   extern __shared__ float sh[];
   float* alpha = sh;             // [dk]
@@ -193,6 +198,7 @@ __global__ __launch_bounds__(DEC_THREADS) void k_dec_state(const DecParams P) {
     qq[c] = pr[hh * P.dk + c] * P.q_scale;
   }
   __syncthreads();
+  if (pos < 0 || !completes(pos, Br.s)) return;  // block-uniform
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int v = blockIdx.y * 64 + lane;
   float acc = 0.f;
@@ -267,6 +273,14 @@ __global__ __launch_bounds__(DEC_THREADS) void k_dec_out(const DecParams P) {
   const int64_t pos = *P.pos_ws;
   constexpr int PER = per16<T>();
   const int n = n0 + lr;  // d is a multiple of 64
+  // fusion logits of this lane's four sequences, loaded with the position
+  float zl[4][FUSION_STRIDE];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float* wr = P.w + (size_t)min(b0 + 4 * lg + e, P.B - 1) * FUSION_STRIDE;
+#pragma unroll
+    for (int q = 0; q < FUSION_STRIDE; q += 4) unpack16<float>(ld16(wr + q), zl[e] + q);
+  }
   if (pos < 0) {  // unusable state: NaN output, nothing else changes
     if (wave == 0) {
       T* out = reinterpret_cast<T*>(P.out);
@@ -280,15 +294,8 @@ __global__ __launch_bounds__(DEC_THREADS) void k_dec_out(const DecParams P) {
   }
   if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0)
     reinterpret_cast<StateHeader*>(P.state)->pos = pos + 1;
-  // fusion logits of this lane's four sequences (all loaded at once), the
-  // softmax's maximum and sum
-  float zl[4][FUSION_STRIDE], zmax[4], zsum[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const float* wr = P.w + (size_t)min(b0 + 4 * lg + e, P.B - 1) * FUSION_STRIDE;
-#pragma unroll
-    for (int q = 0; q < FUSION_STRIDE; q += 4) unpack16<float>(ld16(wr + q), zl[e] + q);
-  }
+  // the softmax's maximum and sum
+  float zmax[4], zsum[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     zmax[e] = -INFINITY;
