@@ -5,8 +5,6 @@ pooling path, blocks of different scales not nested), a gate rank above 16
 each as a plain forward, a masked forward, and a forward split inside blocks
 and continued from its state (the offsets of every branch differ), with
 ragged lengths."""
-import dataclasses
-
 import numpy as np
 import pytest
 
@@ -80,3 +78,25 @@ def test_eight_branches_split_inside_blocks(dtype, masked):
     err, zeros = orc.row_relative_error(O, orc.layer_forward(X, W, cfg, M=M))
     say(f"row-relative error {err:.3e}")
     assert np.all(np.isfinite(O)) and zeros and err <= TOL[cfg.dtype]
+
+
+@pytest.mark.parametrize("dtype", [F32, BF16])
+def test_eight_branches_prefill_decode_forward(dtype):
+    """A prefill, 13 decode steps (every branch completes blocks at its own
+    steps) and a forward over the rest from the same state."""
+    import torch
+    cfg = WIDE[dtype]
+    B, L1, steps, L2 = 2, 50, 13, 40
+    say(f"wide config prefill {L1} + {steps} decode steps + forward {L2}: {dtype}")
+    L = L1 + steps + L2
+    X, W = make_inputs(cfg, B, L, seed=95)
+    layer = DeviceLayer(cfg, W)
+    st = layer.new_state(B)
+    outs = [from_device(layer.forward(to_device(X[:, :L1], cfg.dtype), state_out=st))]
+    for t in range(L1, L1 + steps):
+        o = layer.decode_step(to_device(np.ascontiguousarray(X[:, t]), cfg.dtype), st)
+        outs.append(from_device(o)[:, None, :])
+    outs.append(from_device(layer.forward(to_device(X[:, L1 + steps:], cfg.dtype), state_in=st,
+                                          state_out=st)))
+    torch.cuda.synchronize()
+    check_against_oracle(cfg, X, W, np.concatenate(outs, axis=1))
