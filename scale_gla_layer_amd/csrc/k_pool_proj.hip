@@ -18,9 +18,10 @@
 // logits plus bias (Eq. (10)).  Keeping those few columns out of the branch
 // groups keeps every branch tile full width.
 // Both operands stream global -> LDS asynchronously (gemm_dma.hpp), so the K
-// loop issues no address or conversion arithmetic.  The work list is every
-// (group, m-tile, n-tile), n fastest, laid out so each XCD walks a contiguous
-// range (tiles that share an A tile share an L2).
+// loop issues no address or conversion arithmetic.  Every XCD walks an equal
+// share of every group's row tiles (the groups in the host's order), each row
+// tile's column tiles one after another, so tiles that share an A tile share
+// an L2 and every XCD gets the same mix of work.
 #include "device_common.hpp"
 #include "gemm_dma.hpp"
 #include "layout.hpp"

@@ -65,8 +65,8 @@ struct StateHeader {
 
 // A forward's check of its state_in header, made on the device (forward
 // workspace): status 0 if the header describes this configuration and batch
-// at a position that is a multiple of every scale; pos = that position.
-// Every kernel that reads state_in reads it only when status is 0.
+// and records no error; pos = its position.  Every kernel that reads
+// state_in reads it only when status is 0.
 struct StateCheck {
   int32_t status;
   int32_t pad;

@@ -42,7 +42,7 @@ def test_calls_write_nothing_outside_their_buffers(name, B, L1, L2):
     es = 2 if cfg.dtype == BF16 else 4
     d = cfg.d_model
     lcm = int(np.lcm.reduce(cfg.scales))
-    L1 = L1 // lcm * lcm  # the continuation starts at a block boundary of every scale
+    L1 = L1 // lcm * lcm + 1  # the continuation starts one position into a block of every scale > 1
     X, W = make_inputs(cfg, B, L1 + L2 + 4, seed=41)
     M = make_mask(B, L1, seed=42, hole_prob=0.1)
     layer = DeviceLayer(cfg, W)
