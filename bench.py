@@ -328,6 +328,24 @@ def measure_library_gemms(cfg, B, L, stage_ms, steps=50, warmup=10):
     return out
 
 
+def device_info():
+    """What the line was measured on: the GPU's name, gfx architecture and
+    CU count, the HIP runtime torch was built against, and the host CPU."""
+    import torch
+    props = torch.cuda.get_device_properties(0)
+    cpu = ""
+    try:
+        with open("/proc/cpuinfo", encoding="utf-8") as f:
+            cpu = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:
+        pass
+    return {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
+            "compute_units": props.multi_processor_count,
+            "memory_gib": round(props.total_memory / 2**30, 1),
+            "hip": torch.version.hip, "torch": torch.__version__, "host_cpu": cpu,
+            "host_cores": len(os.sched_getaffinity(0))}
+
+
 def settle_clocks(layer, x, batch=20, tol=0.01, max_s=3.0):
     """Runs forwards in batches of `batch` until the mean time of a batch is
     within `tol` of the previous one (the shader clock settles under load;
@@ -446,6 +464,24 @@ def cpu_worker(workload: str, first: int, stride: int, min_s: float):
         done += L
         k += stride
     print(json.dumps({"tokens": done, "seconds": time.perf_counter() - t0}), flush=True)
+
+
+def cpu_decode_baseline(workload: str = "sweep_1248", steps: int = 64):
+    """The oracle's streaming step on the host (part of the CPU baseline leg):
+    the decode workload's batch from an empty cache (a step's cost does not
+    depend on the position), `steps` steps in one process."""
+    from oracle import msgla_oracle as orc
+    from scale_gla_layer_amd.config import WORKLOADS
+    from scale_gla_layer_amd.synth import make_inputs
+    wl = WORKLOADS[workload]
+    X, W = make_inputs(wl.cfg, wl.batch, steps, seed=0)
+    st = orc.init_state(wl.cfg, wl.batch)
+    t0 = time.perf_counter()
+    for t in range(steps):
+        _, st = orc.decode_step(st, X[:, t], W, wl.cfg)
+    us = (time.perf_counter() - t0) / steps * 1e6
+    return {"workload": workload, "batch": wl.batch, "steps": steps, "us_per_step": round(us, 1),
+            "tokens_per_s": round(wl.batch / (us * 1e-6), 1)}
 
 
 def cpu_baseline(workload: str, min_s: float = 10.0):
@@ -829,6 +865,10 @@ def main():
         log("[bench] timing the fp64 CPU oracle on the host ...")
         cpu = cpu_baseline(wl.name)
         log(f"[bench] oracle {cpu['value']:.0f} tokens/s ({cpu['sample']})")
+        if dec is not None:
+            cpu["decode"] = cpu_decode_baseline(dec["workload"])
+            log(f"[bench] oracle decode step {cpu['decode']['us_per_step']} us (B={cpu['decode']['batch']}, "
+                f"one process)")
 
     line = {
         "metric": "MS-GLA layer fwd tokens/sec (B=8,L=2048,d=1024,bf16); % roofline; ratio vs GLA",
@@ -854,6 +894,7 @@ def main():
                            "frac": round(t_roof / (ms * 1e-3), 4)},
         "kernels": stages,
         "library_gemms": libg,
+        "device": device_info(),
         "settle": settle,
         "per_call_us": warm,
         "per_call_cold_mall_us": cold,
