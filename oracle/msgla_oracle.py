@@ -30,9 +30,15 @@ Readings where the notes leave a step open (all listed in the design doc):
   * positions before a branch's first complete block take zero from that
     branch, and the fusion weights are not renormalised there.
 
+The layer backward (layer_backward and its parts, for training: the notes'
+Sec. 3.4 training paragraph and Sec. 5.5, Table 4) is the vector-Jacobian
+product of layer_forward written out by the chain rule, token by token, from
+a fresh state and without a mask.
+
 Parity: every function here is pinned by tests under tests/ against values
 the notes print (the s=4 hold table, the first pooled input), closed forms,
-textbook identities and brute-force products; see the test module docstrings.
+textbook identities and brute-force products; the backward against central
+finite differences of the (pinned) forward; see the test module docstrings.
 """
 from __future__ import annotations
 
@@ -354,3 +360,169 @@ def row_relative_error(O_dev: np.ndarray, O_ref: np.ndarray):
     err = float((num[nz] / den[nz]).max()) if nz.any() else 0.0
     zero_rows_exact = bool(np.all(O_dev[~nz] == 0.0))
     return err, zero_rows_exact
+
+
+# --------------------------------------------------------------------------
+# Layer backward (training): the notes train each branch with GLA's chunkwise
+# algorithm (Sec. 3.4, training paragraph) and compare training throughput in
+# Sec. 5.5, Table 4.  What training needs from the layer is the vector-Jacobian
+# product of layer_forward: given dO = dLoss/dO, the gradients of the loss
+# with respect to X and every weight.  The functions below are that product
+# written out by the chain rule, walking the forward's steps in reverse, one
+# token at a time (no chunking), from a fresh state and without a mask.
+# --------------------------------------------------------------------------
+
+
+def sigmoid(z: np.ndarray) -> np.ndarray:
+    """1 / (1 + exp(-z)) = exp(logsigmoid(z)), without overflow."""
+    return np.exp(logsigmoid(z))
+
+
+def gla_recurrence_backward(q, k, v, log_alpha, do):
+    """VJP of gla_recurrence from a zero initial state.
+
+    Forward: S_t = Diag(alpha_t) S_{t-1} + k_t^T v_t, o_t = q_t S_t (S_{-1} = 0).
+    With G_t = dLoss/dS_t (everything the loss receives through S_t):
+      G_t = q_t^T do_t + Diag(alpha_{t+1}) G_{t+1}          (G_n = 0 beyond the end)
+      dq_t = do_t S_t^T,  dk_t = G_t v_t^T (per row c: sum_e G_t[c,e] v_t[e]),
+      dv_t = k_t G_t (per column e: sum_c k_t[c] G_t[c,e]),
+      dalpha_t[c] = sum_e G_t[c,e] S_{t-1}[c,e],  dlog_alpha_t = dalpha_t * alpha_t.
+    Shapes as gla_recurrence; do [B, n, h, d_v].  Returns (dq, dk, dv, dlog_alpha).
+    """
+    B, n, h, dk = q.shape
+    dv_ = v.shape[-1]
+    alpha = np.exp(log_alpha)
+    states = np.zeros((n + 1, B, h, dk, dv_))  # states[t + 1] = S_t, states[0] = S_{-1} = 0
+    S = np.zeros((B, h, dk, dv_))
+    for t in range(n):
+        S = alpha[:, t, :, :, None] * S + k[:, t, :, :, None] * v[:, t, :, None, :]
+        states[t + 1] = S
+    dq = np.zeros_like(q)
+    dk_ = np.zeros_like(k)
+    dvv = np.zeros_like(v)
+    dla = np.zeros_like(log_alpha)
+    G = np.zeros((B, h, dk, dv_))
+    for t in reversed(range(n)):
+        G = G + q[:, t, :, :, None] * do[:, t, :, None, :]
+        dq[:, t] = np.einsum("bhv,bhcv->bhc", do[:, t], states[t + 1])
+        dk_[:, t] = np.einsum("bhcv,bhv->bhc", G, v[:, t])
+        dvv[:, t] = np.einsum("bhcv,bhc->bhv", G, k[:, t])
+        dla[:, t] = np.einsum("bhcv,bhcv->bhc", G, states[t]) * alpha[:, t]
+        G = alpha[:, t, :, :, None] * G
+    return dq, dk_, dvv, dla
+
+
+def rms_norm_heads_backward(o: np.ndarray, g: np.ndarray, dy: np.ndarray):
+    """VJP of rms_norm_heads: y_c = o_c g_c / r, r = sqrt(mean_c' o_c'^2 + eps).
+
+    do_c = g_c dy_c / r - o_c (sum_c' g_c' dy_c' o_c') / (d_v r^3);
+    dg_c = sum over positions of o_c dy_c / r.  o, dy: [..., h, d_v].
+    Returns (do, dg [h d_v]).
+    """
+    o = np.asarray(o, dtype=np.float64)
+    h, dv = o.shape[-2], o.shape[-1]
+    gg = np.asarray(g, dtype=np.float64).reshape(h, dv)
+    r = np.sqrt(np.mean(o * o, axis=-1, keepdims=True) + NORM_EPS)
+    inner = np.sum(gg * dy * o, axis=-1, keepdims=True)
+    do = gg * dy / r - o * inner / (dv * r ** 3)
+    dg = (o * dy / r).reshape(-1, h, dv).sum(axis=0).reshape(h * dv)
+    return do, dg
+
+
+def causal_hold_backward(dH: np.ndarray, s: int, n: int) -> np.ndarray:
+    """VJP of causal_hold: [B, L, d] -> [B, n, d]; coarse output j receives
+    the gradients of the positions that show it (hold_index(t, s) == j)."""
+    B, L, d = dH.shape
+    dY = np.zeros((B, n, d))
+    for t in range(L):
+        j = hold_index(t, s)
+        if j >= 0:
+            dY[:, j] += dH[:, t]
+    return dY
+
+
+def branch_backward(X: np.ndarray, bw, s: int, cfg, dY: np.ndarray):
+    """VJP of branch_forward (no mask, zero initial state).
+
+    dY: [B, n_s, d], the gradient of the branch's coarse outputs.  Returns
+    (dX [B, L, d], grads) with grads holding W_q, W_k, W_v, W_g1, W_g2, b_g,
+    W_o (and g_norm when the configuration normalises), shaped as the weights.
+    """
+    X = np.asarray(X, dtype=np.float64)
+    B, L, d = X.shape
+    xp = pool_complete_blocks(X, s)
+    n = xp.shape[1]
+    h = bw.W_q.shape[1] // cfg.d_k
+    q, k, v, la = branch_projections(xp, bw, cfg)
+    o, _ = gla_recurrence(q, k, v, la)
+    norm = getattr(cfg, "norm", False)
+    on = rms_norm_heads(o, bw.g_norm) if norm else o
+    grads = {}
+    # Y = on W_o
+    grads["W_o"] = on.reshape(B * n, h * cfg.d_v).T @ dY.reshape(B * n, d)
+    don = (dY @ bw.W_o.T).reshape(B, n, h, cfg.d_v)
+    if norm:
+        do, grads["g_norm"] = rms_norm_heads_backward(o, bw.g_norm, don)
+    else:
+        do = don
+    dq, dk, dv, dla = gla_recurrence_backward(q, k, v, la, do)
+    # log_alpha = logsigmoid(z) / gamma, z = (xp W_g1) W_g2 + b_g
+    g1 = xp @ bw.W_g1
+    z = g1 @ bw.W_g2 + bw.b_g
+    dz = dla.reshape(B, n, h * cfg.d_k) / cfg.gate_normalizer * sigmoid(-z)
+    grads["W_g2"] = g1.reshape(B * n, -1).T @ dz.reshape(B * n, -1)
+    grads["b_g"] = dz.reshape(B * n, -1).sum(axis=0)
+    dg1 = dz @ bw.W_g2.T
+    # q = q_scale xp W_q, k = xp W_k, v = xp W_v
+    dq = cfg.q_scale * dq.reshape(B, n, h * cfg.d_k)
+    dk = dk.reshape(B, n, h * cfg.d_k)
+    dv = dv.reshape(B, n, h * cfg.d_v)
+    xf = xp.reshape(B * n, d)
+    grads["W_q"] = xf.T @ dq.reshape(B * n, -1)
+    grads["W_k"] = xf.T @ dk.reshape(B * n, -1)
+    grads["W_v"] = xf.T @ dv.reshape(B * n, -1)
+    grads["W_g1"] = xf.T @ dg1.reshape(B * n, -1)
+    dxp = dq @ bw.W_q.T + dk @ bw.W_k.T + dv @ bw.W_v.T + dg1 @ bw.W_g1.T
+    # xp_j = mean of the s positions of complete block j
+    dX = np.zeros((B, L, d))
+    for j in range(s):
+        if n > 0:
+            dX[:, j: n * s: s, :] += dxp / s
+    return dX, grads
+
+
+def layer_backward(X: np.ndarray, W, cfg, dO: np.ndarray):
+    """VJP of layer_forward (fresh state, no mask): dO [B, L, d] ->
+    (dX [B, L, d], grads) with grads["branches"][i] as branch_backward's and
+    grads["W_f"], grads["b_f"] for the fusion logits (zero when m == 1).
+
+    O_t = sum_i w_{t,i} H^(i)_t with H^(i) the held coarse outputs and
+    w_t = softmax(z_t), z_t = x_t W_f + b_f:
+      dH^(i)_t = w_{t,i} dO_t,  dw_{t,i} = dO_t . H^(i)_t,
+      dz_t = w_t * (dw_t - sum_i w_{t,i} dw_{t,i}).
+    """
+    X = np.asarray(X, dtype=np.float64)
+    dO = np.asarray(dO, dtype=np.float64)
+    B, L, d = X.shape
+    m = len(cfg.scales)
+    w = np.ones((B, L, 1)) if m == 1 else fusion_weights(X, W.W_f, W.b_f)
+    dX = np.zeros((B, L, d))
+    dw = np.zeros((B, L, m))
+    grads = {"branches": []}
+    for i, (s, bw) in enumerate(zip(cfg.scales, W.branches)):
+        Y, _, n = branch_forward(X, bw, s, cfg)
+        H = causal_hold(Y, s, L)
+        dw[:, :, i] = np.sum(dO * H, axis=-1)
+        dY = causal_hold_backward(w[:, :, i: i + 1] * dO, s, n)
+        dXi, gi = branch_backward(X, bw, s, cfg, dY)
+        dX += dXi
+        grads["branches"].append(gi)
+    if m > 1:
+        dz = w * (dw - np.sum(w * dw, axis=-1, keepdims=True))
+        grads["W_f"] = X.reshape(B * L, d).T @ dz.reshape(B * L, m)
+        grads["b_f"] = dz.reshape(B * L, m).sum(axis=0)
+        dX += dz @ W.W_f.T
+    else:
+        grads["W_f"] = np.zeros((d, 1))
+        grads["b_f"] = np.zeros(1)
+    return dX, grads
