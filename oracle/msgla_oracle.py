@@ -470,18 +470,19 @@ def branch_backward(X: np.ndarray, bw, s: int, cfg, dY: np.ndarray):
     g1 = xp @ bw.W_g1
     z = g1 @ bw.W_g2 + bw.b_g
     dz = dla.reshape(B, n, h * cfg.d_k) / cfg.gate_normalizer * sigmoid(-z)
-    grads["W_g2"] = g1.reshape(B * n, -1).T @ dz.reshape(B * n, -1)
-    grads["b_g"] = dz.reshape(B * n, -1).sum(axis=0)
+    r, hdk, hdv = bw.W_g1.shape[1], h * cfg.d_k, h * cfg.d_v
+    grads["W_g2"] = g1.reshape(B * n, r).T @ dz.reshape(B * n, hdk)
+    grads["b_g"] = dz.reshape(B * n, hdk).sum(axis=0)
     dg1 = dz @ bw.W_g2.T
     # q = q_scale xp W_q, k = xp W_k, v = xp W_v
-    dq = cfg.q_scale * dq.reshape(B, n, h * cfg.d_k)
-    dk = dk.reshape(B, n, h * cfg.d_k)
-    dv = dv.reshape(B, n, h * cfg.d_v)
+    dq = cfg.q_scale * dq.reshape(B, n, hdk)
+    dk = dk.reshape(B, n, hdk)
+    dv = dv.reshape(B, n, hdv)
     xf = xp.reshape(B * n, d)
-    grads["W_q"] = xf.T @ dq.reshape(B * n, -1)
-    grads["W_k"] = xf.T @ dk.reshape(B * n, -1)
-    grads["W_v"] = xf.T @ dv.reshape(B * n, -1)
-    grads["W_g1"] = xf.T @ dg1.reshape(B * n, -1)
+    grads["W_q"] = xf.T @ dq.reshape(B * n, hdk)
+    grads["W_k"] = xf.T @ dk.reshape(B * n, hdk)
+    grads["W_v"] = xf.T @ dv.reshape(B * n, hdv)
+    grads["W_g1"] = xf.T @ dg1.reshape(B * n, r)
     dxp = dq @ bw.W_q.T + dk @ bw.W_k.T + dv @ bw.W_v.T + dg1 @ bw.W_g1.T
     # xp_j = mean of the s positions of complete block j
     dX = np.zeros((B, L, d))

@@ -88,6 +88,7 @@ def _grad_of(grads, i, key):
     (True, (1, 2, 3), (1, 2, 1), 11),
     (False, (2, 4), (1, 1), 13),   # no scale-1 branch; t < 1 holds nothing
     (False, (1,), (2,), 7),        # one branch: no fusion weights
+    (False, (1, 8), (1, 1), 7),    # the scale-8 branch has no complete block
 ])
 def test_backward_matches_finite_differences(norm, scales, heads, L):
     cfg = _config(norm, scales, heads)
