@@ -298,6 +298,58 @@ msgla_status msgla_decode_step(const msgla_config* cfg, const void* packed, cons
                                int64_t B, void* state, void* out_t, void* workspace,
                                size_t workspace_bytes, void* stream);
 
+/*
+ * Layer backward, for training.  The notes train every branch with GLA's
+ * chunkwise-parallel algorithm (Sec. 3.4, training paragraph) and compare
+ * training throughput with single-scale GLA (Sec. 5.5, Table 4); what training
+ * needs from the layer is its vector-Jacobian product.  For the forward of x
+ * from a fresh state without a mask (what msgla_forward computes with state_in
+ * and mask NULL), given dout = dLoss/dO, msgla_backward writes dx = dLoss/dx and
+ * the gradient of the loss with respect to every weight.
+ *
+ * Gradients are fp32, laid out as the weights of msgla_weights are, [in][out]
+ * row-major, and are overwritten (not accumulated):
+ *   per branch  W_q, W_k [d][h d_k]  W_v [d][h d_v]  W_g1 [d][r]
+ *               W_g2 [r][h d_k]  b_g [h d_k]  W_o [h d_v][d]
+ *   fusion      W_f [d][m], b_f [m]   (ignored, may be NULL, when m == 1)
+ * x, dout, dx: [B][L][d] in the config's storage type.  The call recomputes
+ * the forward's intermediates itself (it needs no saved activations), keeps
+ * every intermediate gradient of the recurrence in fp32, and rounds the
+ * operands of its large products (the weight and input gradients) to the
+ * storage type, accumulating in fp32.  The plain products run on rocBLAS;
+ * everything specific to the layer (the hold and fusion, the chunkwise
+ * recurrence, the gate, the pooling) runs in the library's kernels.
+ * The per-branch normalisation (config norm = 1) has no backward yet:
+ * MSGLA_ERR_UNSUPPORTED.  Pointers are device memory, 16-byte aligned.
+ * Asynchronous on `stream`; the library's rocBLAS handle for the device is
+ * created on the first call (not under graph capture), and calls from several
+ * host threads are serialised by the library.
+ */
+typedef struct {
+  float* W_q;
+  float* W_k;
+  float* W_v;
+  float* W_g1;
+  float* W_g2;
+  float* b_g;
+  float* W_o;
+} msgla_branch_grads;
+
+typedef struct {
+  msgla_branch_grads br[MSGLA_MAX_BRANCHES];
+  float* W_f;
+  float* b_f;
+} msgla_grads;
+
+/* Device workspace needed by msgla_backward for batch B and length L (bytes);
+ * 0 for an invalid configuration or size. */
+size_t msgla_backward_workspace_bytes(const msgla_config* cfg, int64_t B, int64_t L);
+
+msgla_status msgla_backward(const msgla_config* cfg, const void* packed, const void* x,
+                            const void* dout, int64_t B, int64_t L, void* dx,
+                            const msgla_grads* grads, void* workspace, size_t workspace_bytes,
+                            void* stream);
+
 #ifdef __cplusplus
 }
 #endif

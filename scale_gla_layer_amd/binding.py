@@ -27,6 +27,7 @@ SYMBOLS = (
     "msgla_pack_weights", "msgla_workspace_bytes", "msgla_state_bytes", "msgla_state_init",
     "msgla_forward", "msgla_forward_timed", "msgla_decode_workspace_bytes", "msgla_decode_step",
     "msgla_fusion_weights", "msgla_state_query", "msgla_forward_noalloc",
+    "msgla_backward_workspace_bytes", "msgla_backward",
 )
 NOALLOC_WORKSPACE_BYTES = 192 << 20  # MSGLA_NOALLOC_WORKSPACE_BYTES
 
@@ -61,6 +62,15 @@ class CBranchWeights(ctypes.Structure):
 
 class CWeights(ctypes.Structure):
     _fields_ = [("br", CBranchWeights * MAX_BRANCHES), ("W_f", ctypes.c_void_p),
+                ("b_f", ctypes.c_void_p)]
+
+
+class CBranchGrads(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("W_q", "W_k", "W_v", "W_g1", "W_g2", "b_g", "W_o")]
+
+
+class CGrads(ctypes.Structure):
+    _fields_ = [("br", CBranchGrads * MAX_BRANCHES), ("W_f", ctypes.c_void_p),
                 ("b_f", ctypes.c_void_p)]
 
 
@@ -103,6 +113,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "msgla_fusion_weights": (ctypes.c_int, [cfgp, vp, vp, i64, i64, vp, vp]),
         "msgla_state_query": (ctypes.c_int, [vp, ctypes.POINTER(CStateInfo), vp]),
         "msgla_forward_noalloc": (ctypes.c_int, [cfgp, vp, vp, vp, i64, i64, vp, vp, vp, vp]),
+        "msgla_backward_workspace_bytes": (sz, [cfgp, i64, i64]),
+        "msgla_backward": (ctypes.c_int, [cfgp, vp, vp, vp, i64, i64, vp, ctypes.POINTER(CGrads), vp,
+                                          sz, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -227,6 +240,25 @@ def msgla_fusion_weights(cfg: MsglaConfig, packed, x, B: int, L: int, w_out, str
     st = load_library().msgla_fusion_weights(ctypes.byref(c_config(cfg)), _ptr(packed), _ptr(x), B, L,
                                              _ptr(w_out), _stream(stream))
     _check("msgla_fusion_weights", st)
+
+
+def msgla_backward_workspace_bytes(cfg: MsglaConfig, B: int, L: int) -> int:
+    return load_library().msgla_backward_workspace_bytes(ctypes.byref(c_config(cfg)), B, L)
+
+
+def msgla_backward(cfg: MsglaConfig, packed, x, dout, B: int, L: int, dx, branch_grads: Sequence[dict],
+                   W_f, b_f, workspace, stream=None):
+    """branch_grads: per branch a dict of fp32 device tensors W_q, W_k, W_v, W_g1, W_g2, b_g, W_o
+    (written, in the layout of the weights); W_f, b_f: fp32 device tensors (None when m == 1)."""
+    g = CGrads()
+    for i, br in enumerate(branch_grads):
+        for name in ("W_q", "W_k", "W_v", "W_g1", "W_g2", "b_g", "W_o"):
+            setattr(g.br[i], name, _ptr(br.get(name)))
+    g.W_f, g.b_f = _ptr(W_f), _ptr(b_f)
+    st = load_library().msgla_backward(ctypes.byref(c_config(cfg)), _ptr(packed), _ptr(x), _ptr(dout), B, L,
+                                       _ptr(dx), ctypes.byref(g), _ptr(workspace),
+                                       workspace.numel() * workspace.element_size(), _stream(stream))
+    _check("msgla_backward", st)
 
 
 def msgla_state_query(state, stream=None) -> dict:

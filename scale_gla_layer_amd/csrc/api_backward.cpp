@@ -1,0 +1,325 @@
+// Host side of msgla_backward: the layer's vector-Jacobian product (see
+// k_backward.hip for the chain rule it follows).  The call recomputes the
+// forward's intermediates with the forward's own kernels (keeping the coarse
+// outputs Y beside the block means), then walks the layer in reverse: fusion
+// and hold, the output projections, the chunkwise recurrence, the gate, the
+// input projections and the pooling.  The plain products (a weight or input
+// gradient as one GEMM) go to rocBLAS; every layer-specific step runs in the
+// library's kernels.
+#include <rocblas/rocblas.h>
+
+#include <mutex>
+
+#include "api_internal.hpp"
+
+namespace msgla {
+hipError_t launch_bwd_gate(const BwdParams& P, hipStream_t st);
+hipError_t launch_bwd_chunk(const BwdParams& P, int which, bool bf16_path, hipStream_t st);
+hipError_t launch_bwd_scan(float* buf, const float* lb, int seqs, int nch, int np, int C, int dk, int dv,
+                           bool rev, hipStream_t st);
+hipError_t launch_bwd_dzg(const BwdParams& P, int bi, hipStream_t st);
+hipError_t launch_bwd_dg1(const BwdParams& P, int bi, bool bf16_path, hipStream_t st);
+hipError_t launch_bwd_out(const BwdParams& P, bool bf16_path, hipStream_t st);
+hipError_t launch_bwd_hold(const BwdParams& P, int bi, bool bf16_path, hipStream_t st);
+hipError_t launch_bwd_dx(const BwdParams& P, bool bf16_path, hipStream_t st);
+hipError_t launch_bwd_colsum(const float* src, int rows, int cols, int ld, float* partial, int nrb,
+                             float* out, int out_stride, hipStream_t st);
+hipError_t launch_bwd_wf_partial(const BwdParams& P, float* partial, int nrb, bool bf16_path, hipStream_t st);
+hipError_t launch_bwd_wf_finish(const float* partial, int nrb, int d, int m, float* out, hipStream_t st);
+}  // namespace msgla
+
+using namespace msgla;
+using namespace msgla::host;
+
+namespace {
+
+constexpr int BWD_NRB = 64;  // row blocks of the deterministic reductions
+
+struct BwdBranchGeom {
+  size_t lb, sg, g1c, Sst, dSt, AD, rsum, rtot, dob, dzg, dP, dY, Yc, ycat, dxp;
+  int NP;
+};
+
+struct BwdGeom {
+  WsGeom W;
+  BwdBranchGeom br[MSGLA_MAX_BRANCHES];
+  size_t dz, partial, total;
+};
+
+bool bwd_supported(const msgla_config* cfg) { return cfg->norm == 0 && cfg->d_v % 64 == 0; }
+
+BwdGeom bwd_geom(const PackGeom& g, int64_t B, int64_t L) {
+  BwdGeom G{};
+  G.W = ws_geom(g, B, L, false);
+  size_t cur = G.W.total;
+  auto take = [&](size_t bytes) {
+    const size_t o = cur;
+    cur += align256(bytes);
+    return o;
+  };
+  size_t red = (size_t)g.d * FUSION_STRIDE;
+  for (int i = 0; i < g.m; ++i) {
+    const BranchGeom& bg = g.br[i];
+    const WsBranch& w = G.W.br[i];
+    BwdBranchGeom& o = G.br[i];
+    const size_t rows = (size_t)B * bg.h * w.np;  // per-head positions, chunk padded
+    const size_t prow = (size_t)B * w.n;          // pooled positions
+    const size_t chunks = (size_t)B * bg.h * w.nch;
+    o.lb = take(rows * g.dk * 4);
+    o.sg = take(rows * g.dk * 4);
+    o.g1c = take(prow * g.rp * 4);
+    o.Sst = take(chunks * g.dk * g.dv * 4);
+    o.dSt = take(chunks * g.dk * g.dv * 4);
+    o.AD = take(chunks * 2 * 64 * 64 * 4);
+    o.rsum = take(rows * g.dk * 4);
+    o.rtot = take(chunks * g.dk * 4);
+    o.dob = take(prow * bg.h * g.dv * 4);
+    o.dzg = take(prow * bg.h * g.dk * 4);
+    o.NP = bg.col_g + g.rp;
+    o.dP = take(prow * o.NP * g.es);
+    if (bg.s > 1) {
+      o.dY = take(prow * g.d * g.es);
+      o.Yc = take(prow * g.d * g.es);
+    }
+    o.ycat = take(prow * bg.h * g.dv * g.es);
+    o.dxp = take(prow * g.d * 4);
+    red = std::max(red, (size_t)bg.h * g.dk);
+  }
+  G.dz = take((size_t)B * L * FUSION_STRIDE * 4);
+  G.partial = take((size_t)BWD_NRB * red * 4);
+  G.total = cur;
+  return G;
+}
+
+rocblas_datatype storage_type(bool bf16) { return bf16 ? rocblas_datatype_bf16_r : rocblas_datatype_f32_r; }
+
+// Row-major C[M][N] (ldc, fp32) = op(A) op(B), op(X) = X or X^T as stored
+// row-major: A is [M][K] (tA false, lda >= K) or [K][M] (tA true, lda >= M);
+// B is [K][N] (tB false) or [N][K] (tB true).  rocBLAS is column-major, so it
+// computes C^T = op(B)^T op(A)^T on the same memory.
+bool gemm_rm(rocblas_handle h, bool tA, bool tB, int M, int N, int K, const void* A, rocblas_datatype ta,
+             int lda, const void* Bm, rocblas_datatype tb, int ldb, float* C, int ldc) {
+  if (M == 0 || N == 0) return true;
+  const float alpha = 1.f, beta = 0.f;
+  return rocblas_gemm_ex(h, tB ? rocblas_operation_transpose : rocblas_operation_none,
+                         tA ? rocblas_operation_transpose : rocblas_operation_none, N, M, K, &alpha, Bm, tb, ldb, A,
+                         ta, lda, &beta, C, rocblas_datatype_f32_r, ldc, C, rocblas_datatype_f32_r, ldc,
+                         rocblas_datatype_f32_r, rocblas_gemm_algo_standard, 0, 0) == rocblas_status_success;
+}
+
+// one rocBLAS handle per device, created on first use; calls are serialised
+std::mutex g_blas_mu;
+rocblas_handle g_blas[64] = {};
+
+rocblas_handle blas_handle() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  if (!g_blas[dev] && rocblas_create_handle(&g_blas[dev]) != rocblas_status_success) g_blas[dev] = nullptr;
+  return g_blas[dev];
+}
+
+#define BLAS_TRY(expr)                              \
+  do {                                              \
+    if (!(expr)) return MSGLA_ERR_HIP;              \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+size_t msgla_backward_workspace_bytes(const msgla_config* cfg, int64_t B, int64_t L) {
+  if (check_config(cfg) != MSGLA_OK || !batch_ok(B, L) || !bwd_supported(cfg)) return 0;
+  return bwd_geom(pack_geom(cfg), B, L).total;
+}
+
+msgla_status msgla_backward(const msgla_config* cfg, const void* packed, const void* x, const void* dout,
+                            int64_t B, int64_t L, void* dx, const msgla_grads* grads, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  if (msgla_status st = check_config(cfg); st != MSGLA_OK) return st;
+  if (!bwd_supported(cfg)) return MSGLA_ERR_UNSUPPORTED;
+  if (!batch_ok(B, L)) return MSGLA_ERR_INVALID_ARG;
+  if (!packed || !x || !dout || !dx || !grads || !workspace) return MSGLA_ERR_INVALID_ARG;
+  if (!aligned16(packed) || !aligned16(x) || !aligned16(dout) || !aligned16(dx) || !aligned16(workspace))
+    return MSGLA_ERR_INVALID_ARG;
+  const PackGeom g = pack_geom(cfg);
+  for (int i = 0; i < g.m; ++i) {
+    const msgla_branch_grads& b = grads->br[i];
+    if (!b.W_q || !b.W_k || !b.W_v || !b.W_g1 || !b.W_g2 || !b.b_g || !b.W_o) return MSGLA_ERR_INVALID_ARG;
+  }
+  if (g.m > 1 && (!grads->W_f || !grads->b_f)) return MSGLA_ERR_INVALID_ARG;
+  const BwdGeom G = bwd_geom(g, B, L);
+  if (workspace_bytes < G.total) return MSGLA_ERR_WORKSPACE;
+  const WsGeom& W = G.W;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const rocblas_datatype ST = storage_type(g.bf16);
+
+  // forward intermediates (q, k, v^T, x W_g1, y, fusion weights, block means, Y)
+  FwdHooks hooks{};
+  for (int i = 0; i < g.m; ++i)
+    if (g.br[i].s > 1) hooks.yc[i] = at<char>(workspace, G.br[i].Yc);
+  if (msgla_status s = forward_impl(cfg, packed, x, nullptr, B, L, nullptr, nullptr, nullptr, workspace,
+                                    workspace_bytes, stream, nullptr, &hooks);
+      s != MSGLA_OK)
+    return s;
+
+  std::lock_guard<std::mutex> lock(g_blas_mu);
+  rocblas_handle hb = blas_handle();
+  if (!hb || rocblas_set_stream(hb, st) != rocblas_status_success) return MSGLA_ERR_HIP;
+
+  BwdParams P{};
+  P.B = (int)B;
+  P.L = (int)L;
+  P.d = g.d;
+  P.dk = g.dk;
+  P.dv = g.dv;
+  P.C = g.C;
+  P.r = g.r;
+  P.rp = g.rp;
+  P.m = g.m;
+  P.inv_gamma = 1.0f / cfg->gate_normalizer;
+  P.q_scale = cfg->q_scale;
+  P.nbranch = g.m;
+  P.fine = -1;
+  P.x = x;
+  P.dout = dout;
+  P.dx = dx;
+  P.w = at<float>(workspace, W.w);
+  P.dz = at<float>(workspace, G.dz);
+  P.Wf = g.m > 1 ? (g.carrier >= 0 ? at<char>(packed, g.br[g.carrier].off_Wp +
+                                                          (size_t)g.br[g.carrier].col_z * g.d * g.es)
+                                   : at<char>(packed, g.off_Wz))
+                 : nullptr;
+  int units = 0;
+  for (int i = 0; i < g.m; ++i) {
+    const BranchGeom& bg = g.br[i];
+    const WsBranch& wb = W.br[i];
+    const BwdBranchGeom& o = G.br[i];
+    BwdBranch& Br = P.br[i];
+    Br.s = bg.s;
+    Br.h = bg.h;
+    Br.n = wb.n;
+    Br.nch = wb.nch;
+    Br.np = wb.np;
+    Br.unit_begin = units;
+    units += (int)B * bg.h * wb.nch;
+    Br.col_k = bg.col_k;
+    Br.col_v = bg.col_v;
+    Br.col_g = bg.col_g;
+    Br.NP = o.NP;
+    Br.q = at<float>(workspace, wb.q);
+    Br.k = at<float>(workspace, wb.k);
+    Br.vT = at<char>(workspace, wb.vT);
+    Br.g = at<float>(workspace, wb.g);
+    Br.y = at<char>(workspace, wb.y);
+    Br.yc = bg.s > 1 ? at<char>(workspace, o.Yc) : nullptr;
+    Br.W2 = at<float>(packed, bg.off_W2);
+    Br.bg = at<float>(packed, bg.off_bg);
+    Br.lb = at<float>(workspace, o.lb);
+    Br.sg = at<float>(workspace, o.sg);
+    Br.g1c = at<float>(workspace, o.g1c);
+    Br.Sst = at<float>(workspace, o.Sst);
+    Br.dSt = at<float>(workspace, o.dSt);
+    Br.AD = at<float>(workspace, o.AD);
+    Br.rsum = at<float>(workspace, o.rsum);
+    Br.rtot = at<float>(workspace, o.rtot);
+    Br.dob = at<float>(workspace, o.dob);
+    Br.dzg = at<float>(workspace, o.dzg);
+    Br.dP = at<char>(workspace, o.dP);
+    Br.dY = bg.s > 1 ? at<char>(workspace, o.dY) : nullptr;
+    Br.ycat = at<char>(workspace, o.ycat);
+    Br.dxp = at<float>(workspace, o.dxp);
+    if (bg.s == 1) P.fine = i;
+  }
+  P.total_units = units;
+  float* partial = at<float>(workspace, G.partial);
+  const char* WoT = at<char>(packed, g.off_WoT);
+
+  // ---- fusion, hold and the output projections ----
+  for (int i = 0; i < g.m; ++i) {
+    const BwdBranch& Br = P.br[i];
+    const int hdv = Br.h * g.dv;
+    if (Br.n == 0) continue;
+    if (Br.s == 1)  // G = dO W_o^T (scaled by w_1 in k_bwd_out)
+      BLAS_TRY(gemm_rm(hb, false, false, (int)B * Br.n, hdv, g.d, dout, ST, g.d,
+                       WoT + (size_t)g.br[i].ko * g.es, ST, g.Ktot, Br.dob, hdv));
+    else
+      HIP_TRY(launch_bwd_hold(P, i, g.bf16, st));
+  }
+  HIP_TRY(launch_bwd_out(P, g.bf16, st));
+  for (int i = 0; i < g.m; ++i) {
+    const BwdBranch& Br = P.br[i];
+    const int hdv = Br.h * g.dv, rows = (int)B * Br.n;
+    if (Br.n == 0) {
+      HIP_TRY(fill_zero(grads->br[i].W_o, (size_t)hdv * g.d * 4, st));
+      continue;
+    }
+    const void* dYi = Br.s == 1 ? dout : Br.dY;
+    if (Br.s > 1)
+      BLAS_TRY(gemm_rm(hb, false, false, rows, hdv, g.d, dYi, ST, g.d, WoT + (size_t)g.br[i].ko * g.es, ST,
+                       g.Ktot, Br.dob, hdv));
+    BLAS_TRY(gemm_rm(hb, true, false, hdv, g.d, rows, Br.ycat, ST, hdv, dYi, ST, g.d, grads->br[i].W_o, g.d));
+  }
+
+  // ---- the chunkwise recurrence and the gate ----
+  HIP_TRY(launch_bwd_gate(P, st));
+  HIP_TRY(launch_bwd_chunk(P, 0, g.bf16, st));
+  for (int i = 0; i < g.m; ++i)
+    HIP_TRY(launch_bwd_scan(P.br[i].Sst, P.br[i].lb, (int)B * P.br[i].h, P.br[i].nch, P.br[i].np, g.C, g.dk,
+                            g.dv, false, st));
+  HIP_TRY(launch_bwd_chunk(P, 1, g.bf16, st));
+  for (int i = 0; i < g.m; ++i)
+    HIP_TRY(launch_bwd_scan(P.br[i].dSt, P.br[i].lb, (int)B * P.br[i].h, P.br[i].nch, P.br[i].np, g.C, g.dk,
+                            g.dv, true, st));
+  HIP_TRY(launch_bwd_chunk(P, 2, g.bf16, st));
+  HIP_TRY(launch_bwd_chunk(P, 3, g.bf16, st));
+  HIP_TRY(launch_bwd_chunk(P, 4, g.bf16, st));
+  for (int i = 0; i < g.m; ++i) {
+    const BwdBranch& Br = P.br[i];
+    const int hdk = Br.h * g.dk, rows = (int)B * Br.n;
+    if (Br.n == 0) {
+      HIP_TRY(fill_zero(grads->br[i].W_g2, (size_t)g.r * hdk * 4, st));
+      HIP_TRY(fill_zero(grads->br[i].b_g, (size_t)hdk * 4, st));
+      continue;
+    }
+    HIP_TRY(launch_bwd_dzg(P, i, st));
+    HIP_TRY(launch_bwd_dg1(P, i, g.bf16, st));
+    HIP_TRY(launch_bwd_colsum(Br.dzg, rows, hdk, hdk, partial, BWD_NRB, grads->br[i].b_g, 1, st));
+    BLAS_TRY(gemm_rm(hb, true, false, g.r, hdk, rows, Br.g1c, rocblas_datatype_f32_r, g.rp, Br.dzg,
+                     rocblas_datatype_f32_r, hdk, grads->br[i].W_g2, hdk));
+  }
+
+  // ---- the input projections and the pooling ----
+  for (int i = 0; i < g.m; ++i) {
+    const BwdBranch& Br = P.br[i];
+    const BranchGeom& bg = g.br[i];
+    const msgla_branch_grads& gr = grads->br[i];
+    const int hdk = Br.h * g.dk, hdv = Br.h * g.dv, rows = (int)B * Br.n;
+    if (Br.n == 0) {
+      HIP_TRY(fill_zero(gr.W_q, (size_t)g.d * hdk * 4, st));
+      HIP_TRY(fill_zero(gr.W_k, (size_t)g.d * hdk * 4, st));
+      HIP_TRY(fill_zero(gr.W_v, (size_t)g.d * hdv * 4, st));
+      HIP_TRY(fill_zero(gr.W_g1, (size_t)g.d * g.r * 4, st));
+      continue;
+    }
+    const char* dP = static_cast<const char*>(Br.dP);
+    const void* xp = bg.s == 1 ? x : static_cast<const void*>(at<char>(workspace, W.br[i].xp));
+    BLAS_TRY(gemm_rm(hb, false, false, rows, g.d, bg.col_g + g.r, dP, ST, Br.NP, at<char>(packed, bg.off_Wp), ST,
+                     g.d, const_cast<float*>(Br.dxp), g.d));
+    BLAS_TRY(gemm_rm(hb, true, false, g.d, hdk, rows, xp, ST, g.d, dP, ST, Br.NP, gr.W_q, hdk));
+    BLAS_TRY(gemm_rm(hb, true, false, g.d, hdk, rows, xp, ST, g.d, dP + (size_t)bg.col_k * g.es, ST, Br.NP,
+                     gr.W_k, hdk));
+    BLAS_TRY(gemm_rm(hb, true, false, g.d, hdv, rows, xp, ST, g.d, dP + (size_t)bg.col_v * g.es, ST, Br.NP,
+                     gr.W_v, hdv));
+    BLAS_TRY(gemm_rm(hb, true, false, g.d, g.r, rows, xp, ST, g.d, dP + (size_t)bg.col_g * g.es, ST, Br.NP,
+                     gr.W_g1, g.r));
+  }
+  HIP_TRY(launch_bwd_dx(P, g.bf16, st));
+  if (g.m > 1) {
+    HIP_TRY(launch_bwd_wf_partial(P, partial, BWD_NRB, g.bf16, st));
+    HIP_TRY(launch_bwd_wf_finish(partial, BWD_NRB, g.d, g.m, grads->W_f, st));
+    HIP_TRY(launch_bwd_colsum(P.dz, (int)(B * L), g.m, FUSION_STRIDE, partial, BWD_NRB, grads->b_f, 1, st));
+  }
+  return MSGLA_OK;
+}
+
+}  // extern "C"

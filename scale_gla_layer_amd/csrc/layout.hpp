@@ -24,7 +24,7 @@
 //   qt          [B][h][np][d_k]   T     q ⊙ exp(b) (chunk-local)
 //   kT          [B][h][nch][d_k][C] T   (k ⊙ exp(b_last - b))^T per chunk
 //   vT          [B][h][nch][d_v][C] T   v^T per chunk
-//   g           [B][np][rp]       fp32  first gate factor xp W_g1
+//   g           [B][L][rp]        fp32  first gate factor x W_g1 at every position
 //   A           [B][h][nch][C][C] T     masked decayed q k^T per chunk
 //   lam         [B][h][nch][d_k]  fp32  exp(b_last) per chunk
 //   y           [B][h][np][d_v]   T     GLA outputs o_t
@@ -241,6 +241,68 @@ struct K3Params {
   const float* w;   // fusion weights [B L][8]
   void* out;        // [B][L][d]
   K3Branch br[MSGLA_MAX_BRANCHES];
+};
+
+// ---------------- backward ------------------------------------------------------
+// Backward workspace, per branch (n, nch, np as in the forward; T = storage type;
+// rows >= n of a chunk hold no position and are zero or ignored):
+//   lb, sg      [B][h][np][d_k]        fp32  chunk-local cumulative log alpha, and
+//                                            sigmoid(-z) / gamma (the gate's slope)
+//   g1c         [B n][rp]              fp32  block means of x W_g1
+//   Sst, dSt    [B][h][nch][d_k][d_v]  fp32  state entering each chunk, and the
+//                                            loss gradient reaching each chunk's
+//                                            last state from later chunks
+//   AD          [B][h][nch][2][C][C]   fp32  A (decayed q k^T) and D (do v^T), t >= i
+//   rsum, rtot  [B][h][np][d_k], [B][h][nch][d_k]  fp32  in-chunk suffix sums of
+//                                            q dq - k dk, and their chunk totals
+//   dob         [B n][h d_v]           fp32  dLoss/d(GLA output o)
+//   dzg         [B n][h d_k]           fp32  dLoss/d(gate pre-activation z)
+//   dP          [B n][NP]              T     dLoss/d[q | k | v | x W_g1] columns
+//                                            (q_scale folded into q), NP = col_g + rp
+//   dY, Yc      [B n][d]               T     coarse branches: dLoss/dY and Y = y W_o
+//   ycat        [B n][h d_v]           T     y rows position-major (scale 1: w_1 y)
+//   dxp         [B n][d]               fp32  dLoss/d(pooled input)
+// plus dz [B L][8] fp32 (dLoss/d fusion logits) and reduction partials.
+struct BwdBranch {
+  int s, h, n, nch, np;
+  int unit_begin;             // first (b, head, chunk) unit of the branch
+  int col_k, col_v, col_g, NP;
+  const float* q;             // forward workspace: projections (q unscaled)
+  const float* k;
+  const void* vT;
+  const float* g;             // x W_g1 at every unpooled position [B L][rp]
+  const void* y;              // GLA outputs [B][h][np][d_v]
+  const void* yc;             // coarse outputs [B n][d] (s > 1)
+  const float* W2;            // packed gate factor [rp][h d_k] and bias [h d_k]
+  const float* bg;
+  float* lb;
+  float* sg;
+  float* g1c;
+  float* Sst;
+  float* dSt;
+  float* AD;
+  float* rsum;
+  float* rtot;
+  float* dob;
+  float* dzg;
+  void* dP;
+  void* dY;
+  void* ycat;
+  const float* dxp;
+};
+
+struct BwdParams {
+  int B, L, d, dk, dv, C, r, rp, m;
+  float inv_gamma, q_scale;
+  int nbranch, total_units;
+  int fine;                   // branch with scale 1, or -1
+  const void* x;              // [B][L][d] T
+  const void* dout;           // [B][L][d] T
+  void* dx;                   // [B][L][d] T
+  const float* w;             // fusion weights [B L][8]
+  float* dz;                  // [B L][8]
+  const void* Wf;             // fusion logit rows [m][d] T (packed), null when m == 1
+  BwdBranch br[MSGLA_MAX_BRANCHES];
 };
 
 // ---------------- packing ------------------------------------------------------

@@ -71,6 +71,7 @@ class DeviceLayer:
         self._W_f = self._b_f = None
         self.workspace = None
         self.dec_workspace = None
+        self.bwd_workspace = None
 
     def ensure_workspace(self, B: int, L: int):
         n = binding.msgla_workspace_bytes(self.cfg, B, L)
@@ -96,6 +97,33 @@ class DeviceLayer:
         binding.msgla_forward(self.cfg, self.packed, x, B, L, out, ws, state_out=state_out,
                               state_in=state_in, mask=mask, stream=self.stream, events=events)
         return out
+
+    def new_grads(self):
+        """fp32 gradient tensors shaped as the weights ([in][out]); (branch dicts, W_f, b_f)."""
+        torch = _torch()
+        c = self.cfg
+        d, dk, dv, r = c.d_model, c.d_k, c.d_v, c.gate_rank
+        z = lambda *shape: torch.empty(shape, dtype=torch.float32, device=self.device)
+        brs = [{"W_q": z(d, h * dk), "W_k": z(d, h * dk), "W_v": z(d, h * dv), "W_g1": z(d, r),
+                "W_g2": z(r, h * dk), "b_g": z(h * dk), "W_o": z(h * dv, d)} for h in c.heads]
+        m = len(c.scales)
+        return brs, (z(d, m) if m > 1 else None), (z(m) if m > 1 else None)
+
+    def backward(self, x, dout, dx=None, grads=None):
+        """Layer backward of a fresh-state forward of x: returns (dx, (branch grads, dW_f, db_f))."""
+        B, L, _ = x.shape
+        n = binding.msgla_backward_workspace_bytes(self.cfg, B, L)
+        if n == 0:
+            raise ValueError(f"the backward does not support this configuration or size (B={B} L={L})")
+        if self.bwd_workspace is None or self.bwd_workspace.numel() < n:
+            self.bwd_workspace = empty_bytes(n, self.device)
+        if dx is None:
+            dx = self.new_output(B, L)
+        if grads is None:
+            grads = self.new_grads()
+        binding.msgla_backward(self.cfg, self.packed, x, dout, B, L, dx, grads[0], grads[1], grads[2],
+                               self.bwd_workspace, self.stream)
+        return dx, grads
 
     def state_init(self, state, B: int):
         binding.msgla_state_init(self.cfg, B, state, self.stream)

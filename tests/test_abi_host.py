@@ -194,3 +194,37 @@ def test_state_query_argument_errors_need_no_gpu():
     assert lib.msgla_state_query(None, ctypes.byref(info), None) == 1
     assert lib.msgla_state_query(ctypes.c_void_p(8), ctypes.byref(info), None) == 1
     assert lib.msgla_state_query(ctypes.c_void_p(256), None, None) == 1
+
+
+def test_backward_argument_errors_need_no_gpu():
+    """The backward's argument errors are returned before any HIP or rocBLAS call."""
+    lib = binding.load_library()
+    cc = _raw_cfg()
+    fake = 1 << 20
+    ws = lib.msgla_backward_workspace_bytes(ctypes.byref(cc), 2, 64)
+    assert ws > lib.msgla_workspace_bytes(ctypes.byref(cc), 2, 64)
+    g = binding.CGrads()
+    for i in range(cc.n_branches):
+        for name in ("W_q", "W_k", "W_v", "W_g1", "W_g2", "b_g", "W_o"):
+            setattr(g.br[i], name, fake)
+    g.W_f = g.b_f = fake
+    f = lib.msgla_backward
+    ok = (ctypes.byref(cc), fake, fake, fake, 2, 64, fake, ctypes.byref(g), fake, ws, None)
+    # NULL dout, misaligned dx, bad sizes, workspace too small
+    assert f(ok[0], fake, fake, None, 2, 64, fake, ok[7], fake, ws, None) == 1
+    assert f(ok[0], fake, fake, fake, 2, 64, fake + 4, ok[7], fake, ws, None) == 1
+    assert f(ok[0], fake, fake, fake, 0, 64, fake, ok[7], fake, ws, None) == 1
+    assert f(ok[0], fake, fake, fake, 2, 64, fake, ok[7], fake, ws - 1, None) == 3
+    # a missing gradient pointer; a missing fusion gradient with several branches
+    g2 = binding.CGrads()
+    ctypes.memmove(ctypes.byref(g2), ctypes.byref(g), ctypes.sizeof(g))
+    g2.br[1].W_o = None
+    assert f(ok[0], fake, fake, fake, 2, 64, fake, ctypes.byref(g2), fake, ws, None) == 1
+    g2.br[1].W_o = fake
+    g2.b_f = None
+    assert f(ok[0], fake, fake, fake, 2, 64, fake, ctypes.byref(g2), fake, ws, None) == 1
+    # the normalisation has no backward: unsupported, and no workspace size
+    nc = _raw_cfg()
+    nc.norm = 1
+    assert lib.msgla_backward_workspace_bytes(ctypes.byref(nc), 2, 64) == 0
+    assert f(ctypes.byref(nc), fake, fake, fake, 2, 64, fake, ok[7], fake, ws, None) == 2

@@ -1,0 +1,112 @@
+"""GPU: the layer backward (msgla_backward through the C ABI) against the fp64
+oracle's vector-Jacobian product (oracle.layer_backward, itself pinned by
+finite differences of the pinned forward).
+
+Every gradient is compared in full: dx per row (the row-relative error of the
+forward's checker), each weight gradient as a whole (max |device - oracle| over
+max |oracle|), at the forward's bars (1e-4 fp32, 2e-2 bf16).  The cases cover
+several chunks with a ragged last chunk in every branch, tail positions past a
+coarse branch's last complete block, chunks 16, 32 and 64, q_scale and gamma
+off their defaults, strong gates, a scale set without a scale-1 branch, a
+single branch (no fusion), a branch whose scale exceeds the sequence, and the
+main configuration's dimensions in bf16."""
+import dataclasses
+
+import numpy as np
+import pytest
+
+from oracle import msgla_oracle as orc
+from scale_gla_layer_amd.config import BF16, F32, WORKLOADS, MsglaConfig
+from scale_gla_layer_amd.runner import DeviceLayer, from_device, to_device
+from scale_gla_layer_amd.synth import make_inputs, round_to
+from tests.gpu_cases import TOL, say
+
+pytestmark = pytest.mark.gpu
+
+KEYS = ("W_q", "W_k", "W_v", "W_g1", "W_g2", "b_g", "W_o")
+
+
+def _tensor_err(got, ref):
+    den = float(np.abs(ref).max())
+    if den == 0.0:
+        return float(np.abs(got).max())
+    return float(np.abs(got - ref).max()) / den
+
+
+def backward_case(cfg, B, L, seed=0, gate_bias=None, tol=None):
+    import torch
+    tol = TOL[cfg.dtype] if tol is None else tol
+    say(f"backward scales={cfg.scales} heads={cfg.heads} d={cfg.d_model} dk={cfg.d_k} dv={cfg.d_v} "
+        f"r={cfg.gate_rank} C={cfg.chunk} gamma={cfg.gate_normalizer} q_scale={cfg.q_scale} "
+        f"{cfg.dtype} B={B} L={L} seed={seed} gate_bias={gate_bias}")
+    X, W = make_inputs(cfg, B, L, seed=seed, gate_bias=gate_bias)
+    dO = round_to(np.random.default_rng(seed + 1000).normal(0.0, 1.0, X.shape), cfg.dtype)
+    layer = DeviceLayer(cfg, W)
+    x = to_device(X, cfg.dtype)
+    dout = to_device(dO, cfg.dtype)
+    dx, (gb, gWf, gbf) = layer.backward(x, dout)
+    torch.cuda.synchronize()
+    dX_ref, ref = orc.layer_backward(X, W, cfg, dO)
+    errs = {}
+    dX = from_device(dx)
+    assert np.all(np.isfinite(dX)), "non-finite dx"
+    errs["dx"], _ = orc.row_relative_error(dX, dX_ref)
+    for i, g in enumerate(gb):
+        for key in KEYS:
+            got = from_device(g[key])
+            assert np.all(np.isfinite(got)), f"non-finite br{i}.{key}"
+            errs[f"br{i}.{key}"] = _tensor_err(got, ref["branches"][i][key])
+    if cfg.n_branches > 1:
+        errs["W_f"] = _tensor_err(from_device(gWf), ref["W_f"])
+        errs["b_f"] = _tensor_err(from_device(gbf), ref["b_f"])
+    worst = max(errs, key=errs.get)
+    say("errors " + ", ".join(f"{k} {v:.2e}" for k, v in errs.items()))
+    assert errs[worst] <= tol, f"{worst}: {errs[worst]:.3e} > {tol:.1e}"
+    return errs
+
+
+def _cfg(**kw):
+    base = dict(scales=(1, 2, 4), heads=(2, 1, 1), d_model=64, d_k=32, d_v=64, gate_rank=8, chunk=16,
+                gate_normalizer=16.0, q_scale=1.0, dtype=F32)
+    base.update(kw)
+    return MsglaConfig(**base)
+
+
+def test_fp32_small():
+    backward_case(_cfg(), B=2, L=100)
+
+
+@pytest.mark.parametrize("chunk", [16, 32, 64])
+def test_fp32_chunks(chunk):
+    backward_case(_cfg(chunk=chunk, scales=(1, 3, 5), heads=(1, 2, 1)), B=2, L=150, seed=3)
+
+
+def test_fp32_scaled_queries_and_strong_gates():
+    backward_case(_cfg(q_scale=0.7, gate_normalizer=2.0, d_k=16), B=3, L=77, seed=5, gate_bias=(-4.0, 2.0))
+
+
+def test_fp32_no_scale_one_branch():
+    backward_case(_cfg(scales=(2, 4), heads=(1, 2)), B=2, L=90, seed=7)
+
+
+def test_fp32_single_branch():
+    backward_case(_cfg(scales=(1,), heads=(3,), d_k=64, gate_rank=20), B=2, L=70, seed=9)
+
+
+def test_fp32_scale_longer_than_sequence():
+    """The scale-8 branch has no complete block: zero gradients for its weights."""
+    backward_case(_cfg(scales=(1, 8), heads=(1, 1)), B=2, L=7, seed=11)
+
+
+def test_fp32_key_width_128_rank_64():
+    backward_case(_cfg(d_model=128, d_k=128, d_v=128, gate_rank=40, chunk=32), B=1, L=96, seed=13)
+
+
+def test_bf16_main_dimensions():
+    cfg = WORKLOADS["main"].cfg
+    backward_case(cfg, B=2, L=320, seed=17)
+
+
+def test_bf16_sweep_dimensions_with_gate_bias():
+    cfg = dataclasses.replace(WORKLOADS["sweep_1248"].cfg)
+    backward_case(cfg, B=1, L=264, seed=19, gate_bias=(1.0, 4.0))
