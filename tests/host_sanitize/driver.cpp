@@ -60,6 +60,10 @@ static void sizes(const msgla_config& c) {
       if (v != MSGLA_OK || B < 1 || L < 1) EXPECT(ws == 0);
       // accepted shapes: the workspace at least holds the fp32 q and k rows
       if (ws > 0) EXPECT(ws >= (size_t)B * (size_t)L / 4);
+      // the backward's workspace holds at least its fusion-logit gradients (8 fp32 per position)
+      const size_t bw = msgla_backward_workspace_bytes(&c, B, L);
+      if (ws == 0) EXPECT(bw == 0);
+      if (bw > 0) EXPECT(bw >= (size_t)B * (size_t)L * 32);
     }
   }
 }
@@ -164,6 +168,30 @@ int main() {
   EXPECT(msgla_state_query(f + 8, &info, nullptr) == MSGLA_ERR_INVALID_ARG);
   EXPECT(msgla_state_query(f, nullptr, nullptr) == MSGLA_ERR_INVALID_ARG);
   for (int s = -1; s < 7; ++s) EXPECT(msgla_status_str((msgla_status)s) != nullptr);
+  // backward argument errors
+  {
+    const size_t bws = msgla_backward_workspace_bytes(&c, 2, 64);
+    EXPECT(bws > ws);
+    msgla_grads gr;
+    std::memset(&gr, 0, sizeof(gr));
+    for (int i = 0; i < c.n_branches; ++i) {
+      float* p = reinterpret_cast<float*>(f);
+      gr.br[i] = msgla_branch_grads{p, p, p, p, p, p, p};
+    }
+    gr.W_f = gr.b_f = reinterpret_cast<float*>(f);
+    EXPECT(msgla_backward(&c, f, f, nullptr, 2, 64, f, &gr, f, bws, nullptr) == MSGLA_ERR_INVALID_ARG);
+    EXPECT(msgla_backward(&c, f, f, f, 2, 64, f + 4, &gr, f, bws, nullptr) == MSGLA_ERR_INVALID_ARG);
+    EXPECT(msgla_backward(&c, f, f, f, 2, 64, f, nullptr, f, bws, nullptr) == MSGLA_ERR_INVALID_ARG);
+    EXPECT(msgla_backward(&c, f, f, f, INT64_MAX, 64, f, &gr, f, bws, nullptr) == MSGLA_ERR_INVALID_ARG);
+    EXPECT(msgla_backward(&c, f, f, f, 2, 64, f, &gr, f, bws - 1, nullptr) == MSGLA_ERR_WORKSPACE);
+    EXPECT(msgla_backward(nullptr, f, f, f, 2, 64, f, &gr, f, bws, nullptr) != MSGLA_OK);
+    gr.br[2].W_g2 = nullptr;
+    EXPECT(msgla_backward(&c, f, f, f, 2, 64, f, &gr, f, bws, nullptr) == MSGLA_ERR_INVALID_ARG);
+    msgla_config cn = c;
+    cn.norm = 1;
+    EXPECT(msgla_backward_workspace_bytes(&cn, 2, 64) == 0);
+    EXPECT(msgla_backward(&cn, f, f, f, 2, 64, f, &gr, f, bws, nullptr) == MSGLA_ERR_UNSUPPORTED);
+  }
 
   std::printf("configurations %d, failures %d\n", n, failures);
   return failures == 0 ? 0 : 1;

@@ -62,7 +62,7 @@ def _build() -> str:
     with cf.ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 1)) as ex:
         objs = list(ex.map(_compile, jobs))
     tmp = exe + ".tmp"
-    cmd = [_hipcc(), f"--offload-arch={libbuild.ARCH}", *HOST_SAN, *objs, "-o", tmp]
+    cmd = [_hipcc(), f"--offload-arch={libbuild.ARCH}", *HOST_SAN, *objs, "-o", tmp, *libbuild.LIBS]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError("link failed:\n" + res.stdout + res.stderr)
