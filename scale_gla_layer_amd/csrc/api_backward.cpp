@@ -26,6 +26,7 @@ hipError_t launch_bwd_colsum(const float* src, int rows, int cols, int ld, float
                              float* out, int out_stride, hipStream_t st);
 hipError_t launch_bwd_wf_partial(const BwdParams& P, float* partial, int nrb, bool bf16_path, hipStream_t st);
 hipError_t launch_bwd_wf_finish(const float* partial, int nrb, int d, int m, float* out, hipStream_t st);
+hipError_t launch_bwd_splitk_reduce(const float* part, int S, int M, int N, const SplitDst& D, hipStream_t st);
 }  // namespace msgla
 
 using namespace msgla;
@@ -33,7 +34,12 @@ using namespace msgla::host;
 
 namespace {
 
-constexpr int BWD_NRB = 64;  // row blocks of the deterministic reductions
+constexpr int BWD_NRB_MAX = 64;   // row blocks of the deterministic column sums
+constexpr int BWD_WF_NRB = 64;    // row blocks of x^T dz
+constexpr int BWD_SPLIT_MAX = 16; // K slices of a weight-gradient product
+
+// row blocks of a column sum over `rows` rows (at least 128 rows each)
+int colsum_blocks(int rows) { return std::max(1, std::min(BWD_NRB_MAX, (rows + 127) / 128)); }
 
 struct BwdBranchGeom {
   size_t lb, sg, g1c, Sst, dSt, AD, rsum, rtot, dob, dzg, dP, dY, Yc, ycat, dxp;
@@ -43,7 +49,7 @@ struct BwdBranchGeom {
 struct BwdGeom {
   WsGeom W;
   BwdBranchGeom br[MSGLA_MAX_BRANCHES];
-  size_t dz, partial, total;
+  size_t dz, partial, splitk, splitk_floats, total;
 };
 
 bool bwd_supported(const msgla_config* cfg) { return cfg->norm == 0 && cfg->d_v % 64 == 0; }
@@ -57,7 +63,7 @@ BwdGeom bwd_geom(const PackGeom& g, int64_t B, int64_t L) {
     cur += align256(bytes);
     return o;
   };
-  size_t red = (size_t)g.d * FUSION_STRIDE;
+  size_t red = 0, mn = 0;
   for (int i = 0; i < g.m; ++i) {
     const BranchGeom& bg = g.br[i];
     const WsBranch& w = G.W.br[i];
@@ -84,9 +90,13 @@ BwdGeom bwd_geom(const PackGeom& g, int64_t B, int64_t L) {
     o.ycat = take(prow * bg.h * g.dv * g.es);
     o.dxp = take(prow * g.d * 4);
     red = std::max(red, (size_t)bg.h * g.dk);
+    mn = std::max({mn, (size_t)g.d * (bg.col_g + g.r), (size_t)bg.h * g.dv * g.d, (size_t)g.r * bg.h * g.dk});
   }
   G.dz = take((size_t)B * L * FUSION_STRIDE * 4);
-  G.partial = take((size_t)BWD_NRB * red * 4);
+  G.partial = take(std::max((size_t)BWD_NRB_MAX * std::max<size_t>(red, FUSION_STRIDE),
+                            (size_t)BWD_WF_NRB * g.d * FUSION_STRIDE) * 4);
+  G.splitk_floats = (size_t)BWD_SPLIT_MAX * mn;
+  G.splitk = take(G.splitk_floats * 4);
   G.total = cur;
   return G;
 }
@@ -105,6 +115,45 @@ bool gemm_rm(rocblas_handle h, bool tA, bool tB, int M, int N, int K, const void
                          tA ? rocblas_operation_transpose : rocblas_operation_none, N, M, K, &alpha, Bm, tb, ldb, A,
                          ta, lda, &beta, C, rocblas_datatype_f32_r, ldc, C, rocblas_datatype_f32_r, ldc,
                          rocblas_datatype_f32_r, rocblas_gemm_algo_standard, 0, 0) == rocblas_status_success;
+}
+
+// Weight gradient C[M][N] = A^T B with A row-major [K][M] (lda) and B row-major
+// [K][N] (ldb), K the long reduction over positions, written to the column
+// ranges of `dst`.  With few output tiles the K range is cut into S slices
+// computed as one strided batch into `part` [S][M][N] and summed by a kernel,
+// so that the product fills the chip.
+bool gemm_wgrad(rocblas_handle h, int M, int N, int K, const void* A, rocblas_datatype ta, int lda,
+                const void* Bm, rocblas_datatype tb, int ldb, const SplitDst& dst, float* part,
+                size_t part_floats, int elem_bytes, hipStream_t st) {
+  if (M == 0 || N == 0) return true;
+  const int tiles = ((M + 127) / 128) * ((N + 127) / 128);
+  int S = 1;
+  while (S < BWD_SPLIT_MAX && tiles * S * 2 <= 768 && K % (2 * S) == 0 && K / (2 * S) >= 256 &&
+         (size_t)(2 * S) * M * N <= part_floats)
+    S *= 2;
+  const bool direct = S == 1 && dst.n == 1 && dst.c0[0] == 0 && dst.nc[0] == N;
+  float* C = direct ? dst.p[0] : part;
+  if (!direct && (size_t)S * M * N > part_floats) return false;
+  const float alpha = 1.f, beta = 0.f;
+  const int Ks = K / S;
+  const rocblas_stride sA = (rocblas_stride)Ks * lda, sB = (rocblas_stride)Ks * ldb,
+                       sC = (rocblas_stride)M * N;
+  (void)elem_bytes;
+  if (rocblas_gemm_strided_batched_ex(h, rocblas_operation_none, rocblas_operation_transpose, N, M, Ks, &alpha, Bm,
+                                      tb, ldb, sB, A, ta, lda, sA, &beta, C, rocblas_datatype_f32_r, N, sC, C,
+                                      rocblas_datatype_f32_r, N, sC, S, rocblas_datatype_f32_r,
+                                      rocblas_gemm_algo_standard, 0, 0) != rocblas_status_success)
+    return false;
+  return direct || launch_bwd_splitk_reduce(part, S, M, N, dst, st) == hipSuccess;
+}
+
+SplitDst one_dst(float* p, int n) {
+  SplitDst d{};
+  d.p[0] = p;
+  d.c0[0] = 0;
+  d.nc[0] = n;
+  d.n = 1;
+  return d;
 }
 
 // one rocBLAS handle per device, created on first use; calls are serialised
@@ -232,6 +281,7 @@ msgla_status msgla_backward(const msgla_config* cfg, const void* packed, const v
   }
   P.total_units = units;
   float* partial = at<float>(workspace, G.partial);
+  float* sk = at<float>(workspace, G.splitk);
   const char* WoT = at<char>(packed, g.off_WoT);
 
   // ---- fusion, hold and the output projections ----
@@ -257,7 +307,8 @@ msgla_status msgla_backward(const msgla_config* cfg, const void* packed, const v
     if (Br.s > 1)
       BLAS_TRY(gemm_rm(hb, false, false, rows, hdv, g.d, dYi, ST, g.d, WoT + (size_t)g.br[i].ko * g.es, ST,
                        g.Ktot, Br.dob, hdv));
-    BLAS_TRY(gemm_rm(hb, true, false, hdv, g.d, rows, Br.ycat, ST, hdv, dYi, ST, g.d, grads->br[i].W_o, g.d));
+    BLAS_TRY(gemm_wgrad(hb, hdv, g.d, rows, Br.ycat, ST, hdv, dYi, ST, g.d, one_dst(grads->br[i].W_o, g.d), sk,
+                        G.splitk_floats, g.es, st));
   }
 
   // ---- the chunkwise recurrence and the gate ----
@@ -283,9 +334,9 @@ msgla_status msgla_backward(const msgla_config* cfg, const void* packed, const v
     }
     HIP_TRY(launch_bwd_dzg(P, i, st));
     HIP_TRY(launch_bwd_dg1(P, i, g.bf16, st));
-    HIP_TRY(launch_bwd_colsum(Br.dzg, rows, hdk, hdk, partial, BWD_NRB, grads->br[i].b_g, 1, st));
-    BLAS_TRY(gemm_rm(hb, true, false, g.r, hdk, rows, Br.g1c, rocblas_datatype_f32_r, g.rp, Br.dzg,
-                     rocblas_datatype_f32_r, hdk, grads->br[i].W_g2, hdk));
+    HIP_TRY(launch_bwd_colsum(Br.dzg, rows, hdk, hdk, partial, colsum_blocks(rows), grads->br[i].b_g, 1, st));
+    BLAS_TRY(gemm_wgrad(hb, g.r, hdk, rows, Br.g1c, rocblas_datatype_f32_r, g.rp, Br.dzg, rocblas_datatype_f32_r,
+                        hdk, one_dst(grads->br[i].W_g2, hdk), sk, G.splitk_floats, 4, st));
   }
 
   // ---- the input projections and the pooling ----
@@ -305,19 +356,22 @@ msgla_status msgla_backward(const msgla_config* cfg, const void* packed, const v
     const void* xp = bg.s == 1 ? x : static_cast<const void*>(at<char>(workspace, W.br[i].xp));
     BLAS_TRY(gemm_rm(hb, false, false, rows, g.d, bg.col_g + g.r, dP, ST, Br.NP, at<char>(packed, bg.off_Wp), ST,
                      g.d, const_cast<float*>(Br.dxp), g.d));
-    BLAS_TRY(gemm_rm(hb, true, false, g.d, hdk, rows, xp, ST, g.d, dP, ST, Br.NP, gr.W_q, hdk));
-    BLAS_TRY(gemm_rm(hb, true, false, g.d, hdk, rows, xp, ST, g.d, dP + (size_t)bg.col_k * g.es, ST, Br.NP,
-                     gr.W_k, hdk));
-    BLAS_TRY(gemm_rm(hb, true, false, g.d, hdv, rows, xp, ST, g.d, dP + (size_t)bg.col_v * g.es, ST, Br.NP,
-                     gr.W_v, hdv));
-    BLAS_TRY(gemm_rm(hb, true, false, g.d, g.r, rows, xp, ST, g.d, dP + (size_t)bg.col_g * g.es, ST, Br.NP,
-                     gr.W_g1, g.r));
+    // one product for the q | k | v | x W_g1 columns, scattered into the four gradients
+    SplitDst dw{};
+    dw.n = 4;
+    dw.p[0] = gr.W_q, dw.c0[0] = 0, dw.nc[0] = hdk;
+    dw.p[1] = gr.W_k, dw.c0[1] = bg.col_k, dw.nc[1] = hdk;
+    dw.p[2] = gr.W_v, dw.c0[2] = bg.col_v, dw.nc[2] = hdv;
+    dw.p[3] = gr.W_g1, dw.c0[3] = bg.col_g, dw.nc[3] = g.r;
+    BLAS_TRY(gemm_wgrad(hb, g.d, bg.col_g + g.r, rows, xp, ST, g.d, dP, ST, Br.NP, dw, sk, G.splitk_floats, g.es,
+                        st));
   }
   HIP_TRY(launch_bwd_dx(P, g.bf16, st));
   if (g.m > 1) {
-    HIP_TRY(launch_bwd_wf_partial(P, partial, BWD_NRB, g.bf16, st));
-    HIP_TRY(launch_bwd_wf_finish(partial, BWD_NRB, g.d, g.m, grads->W_f, st));
-    HIP_TRY(launch_bwd_colsum(P.dz, (int)(B * L), g.m, FUSION_STRIDE, partial, BWD_NRB, grads->b_f, 1, st));
+    HIP_TRY(launch_bwd_wf_partial(P, partial, BWD_WF_NRB, g.bf16, st));
+    HIP_TRY(launch_bwd_wf_finish(partial, BWD_WF_NRB, g.d, g.m, grads->W_f, st));
+    HIP_TRY(launch_bwd_colsum(P.dz, (int)(B * L), g.m, FUSION_STRIDE, partial, colsum_blocks((int)(B * L)),
+                              grads->b_f, 1, st));
   }
   return MSGLA_OK;
 }

@@ -80,14 +80,41 @@ __device__ __forceinline__ void store8(T* p, const float* v) {
   }
 }
 
+// Stages a ROWS x COLS fp32 tile into LDS: element (row, col) = f(row, col)
+// goes to lds[row * LS + col] (TR: lds[col * LS + row]).  Threads take
+// consecutive columns (COL_FAST) or consecutive rows, whichever keeps the
+// source reads coalesced.  Every load of a thread is issued before its LDS
+// stores, so a staging pass costs one memory round trip; f must load
+// unconditionally (from a clamped address) and select the value afterwards.
+template <int ROWS, int COLS, int LS, bool COL_FAST, bool TR, class F>
+__device__ __forceinline__ void stage(float* lds, F&& f) {
+  static_assert((ROWS * COLS) % 256 == 0, "whole rounds of 256 threads");
+  constexpr int N = ROWS * COLS / 256;
+  float v[N];
+#pragma unroll
+  for (int k = 0; k < N; ++k) {
+    const int idx = threadIdx.x + 256 * k;
+    const int row = COL_FAST ? idx / COLS : idx % ROWS, col = COL_FAST ? idx % COLS : idx / ROWS;
+    v[k] = f(row, col);
+  }
+#pragma unroll
+  for (int k = 0; k < N; ++k) {
+    const int idx = threadIdx.x + 256 * k;
+    const int row = COL_FAST ? idx / COLS : idx % ROWS, col = COL_FAST ? idx % COLS : idx / ROWS;
+    lds[TR ? col * LS + row : row * LS + col] = v[k];
+  }
+}
+
 }  // namespace
 
 // ---- gate recompute: b (chunk-local cumulative log alpha), sigmoid(-z)/gamma, g1 ----
 // One workgroup of d_k threads per (branch, b, head, chunk); thread = key channel.
-constexpr int BWD_GATE_MAX_C = 64, BWD_GATE_MAX_R = 64;
+// Dynamic LDS: the chunk's block means g1s [C][r] (at least 256 floats: the part
+// totals reuse them), the head's W_g2 slice [r][d_k], and log alpha [C][d_k].
 __global__ __launch_bounds__(256) void k_bwd_gate(const BwdParams P) {
-  __shared__ float g1s[BWD_GATE_MAX_C * BWD_GATE_MAX_R];
-  __shared__ float w2s[BWD_GATE_MAX_R * 256];
+  extern __shared__ float gate_lds[];
+  float* g1s = gate_lds;
+  float* w2s = gate_lds + max(P.C * P.r, 256);
   const UnitPos u = unit_pos(P, blockIdx.x);
   const BwdBranch& Br = P.br[u.bi];
   const int j0 = u.ch * P.C;
@@ -102,25 +129,40 @@ __global__ __launch_bounds__(256) void k_bwd_gate(const BwdParams P) {
       acc /= (float)Br.s;
       if (u.head == 0) Br.g1c[((size_t)u.b * Br.n + j) * P.rp + rr] = acc;
     }
-    g1s[jj * BWD_GATE_MAX_R + rr] = acc;
+    g1s[jj * P.r + rr] = acc;
   }
   for (int idx = threadIdx.x; idx < P.r * P.dk; idx += blockDim.x) {
     const int rr = idx / P.dk, c = idx - rr * P.dk;
     w2s[rr * P.dk + c] = Br.W2[(size_t)rr * hdk + u.head * P.dk + c];
   }
   __syncthreads();
-  const int c = threadIdx.x;
-  if (c >= P.dk) return;
+  // thread = (channel, part): the chunk's positions are cut into 256 / d_k
+  // parts scanned side by side, then each part adds the totals of the parts
+  // before it
+  const int parts = 256 / P.dk;
+  const int c = threadIdx.x % P.dk, part = threadIdx.x / P.dk;
+  const int len = (P.C + parts - 1) / parts, jb = part * len, je = min(P.C, jb + len);
   const float bgc = Br.bg[u.head * P.dk + c];
+  float* las = w2s + P.r * P.dk;  // log alpha [C][d_k]
   float bsum = 0.f;
-  const size_t row0 = ((size_t)u.sq * Br.np + j0) * P.dk + c;
-  for (int jj = 0; jj < P.C; ++jj) {
+  for (int jj = jb; jj < je; ++jj) {
     const bool valid = j0 + jj < Br.n;
     float z = bgc;
-    for (int rr = 0; rr < P.r; ++rr) z += g1s[jj * BWD_GATE_MAX_R + rr] * w2s[rr * P.dk + c];
-    bsum += valid ? logsigmoid_f(z) * P.inv_gamma : 0.f;
-    Br.lb[row0 + (size_t)jj * P.dk] = bsum;
-    Br.sg[row0 + (size_t)jj * P.dk] = valid ? __expf(logsigmoid_f(-z)) * P.inv_gamma : 0.f;
+    for (int rr = 0; rr < P.r; ++rr) z += g1s[jj * P.r + rr] * w2s[rr * P.dk + c];
+    const float la = valid ? logsigmoid_f(z) * P.inv_gamma : 0.f;
+    las[jj * P.dk + c] = la;
+    bsum += la;
+    Br.sg[((size_t)u.sq * Br.np + j0 + jj) * P.dk + c] = valid ? __expf(logsigmoid_f(-z)) * P.inv_gamma : 0.f;
+  }
+  __syncthreads();  // the block means are no longer needed: their space takes the part totals
+  float* tot = g1s;
+  tot[part * P.dk + c] = bsum;
+  __syncthreads();
+  float run = 0.f;
+  for (int q = 0; q < part; ++q) run += tot[q * P.dk + c];
+  for (int jj = jb; jj < je; ++jj) {
+    run += las[jj * P.dk + c];
+    Br.lb[((size_t)u.sq * Br.np + j0 + jj) * P.dk + c] = run;
   }
 }
 
@@ -136,29 +178,28 @@ __global__ __launch_bounds__(256) void k_bwd_outer(const BwdParams P) {
   const int j0 = u.ch * P.C, e0 = blockIdx.y * 64;
   const int nvalid = min(P.C, Br.n - j0);
   const size_t row0 = (size_t)u.sq * Br.np + j0;
-  for (int idx = threadIdx.x; idx < P.C * DK; idx += 256) {
-    const int t = idx / DK, c = idx - t * DK;
-    float val = 0.f;
-    if (t < nvalid) {
-      const size_t o = (row0 + t) * DK + c;
-      if constexpr (REV)
-        val = P.q_scale * Br.q[o] * __expf(Br.lb[o]);
-      else
-        val = Br.k[o] * __expf(Br.lb[(row0 + P.C - 1) * DK + c] - Br.lb[o]);
-    }
-    xs[t * DK + c] = val;
-  }
-  for (int idx = threadIdx.x; idx < P.C * 64; idx += 256) {
-    const int t = idx / 64, e = idx - t * 64;
-    float val = 0.f;
-    if (t < nvalid) {
-      if constexpr (REV)
-        val = Br.dob[((size_t)(u.b * Br.n + j0 + t) * Br.h + u.head) * P.dv + e0 + e];
-      else
-        val = to_f32(reinterpret_cast<const T*>(Br.vT)[(((size_t)u.sq * Br.nch + u.ch) * P.dv + e0 + e) * P.C + t]);
-    }
-    ys[t * 64 + e] = val;
-  }
+  stage<64, DK, DK, true, false>(xs, [&](int t, int c) {
+    const bool ok = t < nvalid;
+    const size_t o = (row0 + (ok ? t : 0)) * DK + c;
+    float val;
+    if constexpr (REV)
+      val = P.q_scale * Br.q[o] * __expf(Br.lb[o]);
+    else
+      val = Br.k[o] * __expf(Br.lb[(row0 + P.C - 1) * DK + c] - Br.lb[o]);
+    return ok ? val : 0.f;
+  });
+  if constexpr (REV)
+    stage<64, 64, 64, true, false>(ys, [&](int t, int e) {
+      const bool ok = t < nvalid;
+      const float val = Br.dob[((size_t)(u.b * Br.n + j0 + (ok ? t : 0)) * Br.h + u.head) * P.dv + e0 + e];
+      return ok ? val : 0.f;
+    });
+  else
+    stage<64, 64, 64, false, false>(ys, [&](int t, int e) {
+      const bool ok = t < nvalid;
+      const float val = to_f32(reinterpret_cast<const T*>(Br.vT)[(((size_t)u.sq * Br.nch + u.ch) * P.dv + e0 + e) * P.C + (ok ? t : 0)]);
+      return ok ? val : 0.f;
+    });
   __syncthreads();
   constexpr int NA = DK >= 32 ? DK / 32 : 1;
   const int cr = threadIdx.x & 31, er = threadIdx.x >> 5;
@@ -204,6 +245,7 @@ __global__ __launch_bounds__(256) void k_bwd_scan(float* buf, const float* lb, i
     const int rem = (int)(idx - sq * dk * dv);
     const int c = rem / dv, e = rem - c * dv;
     float S = 0.f;
+#pragma unroll 4
     for (int it = 0; it < nch; ++it) {
       const int ch = rev ? nch - 1 - it : it;
       const size_t o = ((sq * nch + ch) * dk + c) * dv + e;
@@ -234,14 +276,19 @@ __global__ __launch_bounds__(256) void k_bwd_AD(const BwdParams P) {
   float* bs = sm + 2 * 64 * 33;
   constexpr int CW = DK < 32 ? DK : 32;
   for (int c0 = 0; c0 < DK; c0 += CW) {
-    for (int idx = threadIdx.x; idx < 64 * CW; idx += 256) {
-      const int tt = idx / CW, cc = idx - tt * CW;
-      const bool ok = tt < nvalid;
-      const size_t o = (row0 + (ok ? tt : 0)) * DK + c0 + cc;
-      qs[tt * 33 + cc] = ok ? P.q_scale * Br.q[o] : 0.f;
-      ks[tt * 33 + cc] = ok ? Br.k[o] : 0.f;
-      bs[tt * 33 + cc] = ok ? Br.lb[o] : 0.f;
-    }
+    auto at_ = [&](int tt, int cc) { return (row0 + (tt < nvalid ? tt : 0)) * DK + c0 + cc; };
+    stage<64, CW, 33, true, false>(qs, [&](int tt, int cc) {
+      const float v = P.q_scale * Br.q[at_(tt, cc)];
+      return tt < nvalid ? v : 0.f;
+    });
+    stage<64, CW, 33, true, false>(ks, [&](int tt, int cc) {
+      const float v = Br.k[at_(tt, cc)];
+      return tt < nvalid ? v : 0.f;
+    });
+    stage<64, CW, 33, true, false>(bs, [&](int tt, int cc) {
+      const float v = Br.lb[at_(tt, cc)];
+      return tt < nvalid ? v : 0.f;
+    });
     __syncthreads();
     for (int cc = 0; cc < CW; ++cc) {
       const float qv = qs[t * 33 + cc], bt = bs[t * 33 + cc];
@@ -256,16 +303,17 @@ __global__ __launch_bounds__(256) void k_bwd_AD(const BwdParams P) {
   float* ds = sm;
   float* vs = sm + 64 * 65;
   for (int e0 = 0; e0 < P.dv; e0 += 64) {
-    for (int idx = threadIdx.x; idx < 64 * 64; idx += 256) {
-      const int tt = idx / 64, e = idx - tt * 64;
+    stage<64, 64, 65, true, false>(ds, [&](int tt, int e) {
       const bool ok = tt < nvalid;
-      ds[tt * 65 + e] = ok ? Br.dob[((size_t)(u.b * Br.n + j0 + tt) * Br.h + u.head) * P.dv + e0 + e] : 0.f;
-      // v^T per chunk [d_v][C]: consecutive threads take consecutive positions
-      const int e2 = idx / 64, t2 = idx - e2 * 64;
-      vs[t2 * 65 + e2] = t2 < nvalid
-                             ? to_f32(reinterpret_cast<const T*>(Br.vT)[(((size_t)u.sq * Br.nch + u.ch) * P.dv + e0 + e2) * P.C + t2])
-                             : 0.f;
-    }
+      const float v = Br.dob[((size_t)(u.b * Br.n + j0 + (ok ? tt : 0)) * Br.h + u.head) * P.dv + e0 + e];
+      return ok ? v : 0.f;
+    });
+    // v^T per chunk [d_v][C]: consecutive threads take consecutive positions
+    stage<64, 64, 65, false, false>(vs, [&](int tt, int e) {
+      const bool ok = tt < nvalid;
+      const float v = to_f32(reinterpret_cast<const T*>(Br.vT)[(((size_t)u.sq * Br.nch + u.ch) * P.dv + e0 + e) * P.C + (ok ? tt : 0)]);
+      return ok ? v : 0.f;
+    });
     __syncthreads();
     for (int e = 0; e < 64; ++e) {
       const float dv_ = ds[t * 65 + e];
@@ -299,11 +347,12 @@ __global__ __launch_bounds__(256) void k_bwd_dv(const BwdParams P) {
   const size_t row0 = (size_t)u.sq * Br.np + j0;
   const int i = threadIdx.x & 63, eg = threadIdx.x >> 6;
   const float* A = Br.AD + ((size_t)u.sq * Br.nch + u.ch) * 2 * 64 * 64;
-  for (int idx = threadIdx.x; idx < 64 * 64; idx += 256) {
-    const int tt = idx / 64, e = idx - tt * 64;
-    as[tt * 65 + e] = A[idx];
-    dos[idx] = tt < nvalid ? Br.dob[((size_t)(u.b * Br.n + j0 + tt) * Br.h + u.head) * P.dv + e0 + e] : 0.f;
-  }
+  stage<64, 64, 65, true, false>(as, [&](int tt, int i) { return A[tt * 64 + i]; });
+  stage<64, 64, 64, true, false>(dos, [&](int tt, int e) {
+    const bool ok = tt < nvalid;
+    const float v = Br.dob[((size_t)(u.b * Br.n + j0 + (ok ? tt : 0)) * Br.h + u.head) * P.dv + e0 + e];
+    return ok ? v : 0.f;
+  });
   __syncthreads();
   float acc[16];
 #pragma unroll
@@ -320,16 +369,15 @@ __global__ __launch_bounds__(256) void k_bwd_dv(const BwdParams P) {
   constexpr int CW = DK < 64 ? DK : 64;
   for (int c0 = 0; c0 < DK; c0 += CW) {
     __syncthreads();
-    for (int idx = threadIdx.x; idx < 64 * CW; idx += 256) {
-      const int tt = idx / CW, cc = idx - tt * CW;
+    stage<64, CW, 65, true, false>(khs, [&](int tt, int cc) {
       const bool ok = tt < nvalid;
       const size_t o = (row0 + (ok ? tt : 0)) * DK + c0 + cc;
-      khs[tt * 65 + cc] = ok ? Br.k[o] * __expf(Br.lb[(row0 + P.C - 1) * DK + c0 + cc] - Br.lb[o]) : 0.f;
-    }
-    for (int idx = threadIdx.x; idx < CW * 64; idx += 256) {
-      const int cc = idx / 64, e = idx - cc * 64;
-      dss[idx] = Br.dSt[(((size_t)u.sq * Br.nch + u.ch) * DK + c0 + cc) * P.dv + e0 + e];
-    }
+      const float v = Br.k[o] * __expf(Br.lb[(row0 + P.C - 1) * DK + c0 + cc] - Br.lb[o]);
+      return ok ? v : 0.f;
+    });
+    stage<CW, 64, 64, true, false>(dss, [&](int cc, int e) {
+      return Br.dSt[(((size_t)u.sq * Br.nch + u.ch) * DK + c0 + cc) * P.dv + e0 + e];
+    });
     __syncthreads();
     for (int cc = 0; cc < CW; ++cc) {
       const float kv = khs[i * 65 + cc];
@@ -372,20 +420,18 @@ __global__ __launch_bounds__(256) void k_bwd_dqdk(const BwdParams P) {
     float* sT = sm + 2 * 64 * 65;            // [64 e][32 c]
     float* dsT = sm + 2 * 64 * 65 + 64 * 32;
     for (int e0 = 0; e0 < P.dv; e0 += 64) {
-      for (int idx = threadIdx.x; idx < 64 * 64; idx += 256) {
-        const int tt = idx / 64, e = idx - tt * 64;
-        dos[tt * 65 + e] = tt < nvalid ? Br.dob[((size_t)(u.b * Br.n + j0 + tt) * Br.h + u.head) * P.dv + e0 + e] : 0.f;
-        const int e2 = idx / 64, t2 = idx - e2 * 64;
-        vs[t2 * 65 + e2] = t2 < nvalid
-                               ? to_f32(reinterpret_cast<const T*>(Br.vT)[(((size_t)u.sq * Br.nch + u.ch) * P.dv + e0 + e2) * P.C + t2])
-                               : 0.f;
-      }
-      for (int idx = threadIdx.x; idx < CS * 64; idx += 256) {
-        const int cc = idx / 64, e = idx - cc * 64;
-        const size_t o = (sbase + c0 + cc) * P.dv + e0 + e;
-        sT[e * 32 + cc] = Br.Sst[o];
-        dsT[e * 32 + cc] = Br.dSt[o];
-      }
+      stage<64, 64, 65, true, false>(dos, [&](int tt, int e) {
+        const bool ok = tt < nvalid;
+        const float v = Br.dob[((size_t)(u.b * Br.n + j0 + (ok ? tt : 0)) * Br.h + u.head) * P.dv + e0 + e];
+        return ok ? v : 0.f;
+      });
+      stage<64, 64, 65, false, false>(vs, [&](int tt, int e) {
+        const bool ok = tt < nvalid;
+        const float v = to_f32(reinterpret_cast<const T*>(Br.vT)[(((size_t)u.sq * Br.nch + u.ch) * P.dv + e0 + e) * P.C + (ok ? tt : 0)]);
+        return ok ? v : 0.f;
+      });
+      stage<CS, 64, 32, true, true>(sT, [&](int cc, int e) { return Br.Sst[(sbase + c0 + cc) * P.dv + e0 + e]; });
+      stage<CS, 64, 32, true, true>(dsT, [&](int cc, int e) { return Br.dSt[(sbase + c0 + cc) * P.dv + e0 + e]; });
       __syncthreads();
       if (live) {
         for (int e = 0; e < 64; ++e) {
@@ -412,16 +458,18 @@ __global__ __launch_bounds__(256) void k_bwd_dqdk(const BwdParams P) {
   float* ks = qs + 64 * 33;
   float* bs = ks + 64 * 33;
   const float* D = Br.AD + ((size_t)u.sq * Br.nch + u.ch) * 2 * 64 * 64 + 64 * 64;
-  for (int idx = threadIdx.x; idx < 64 * 64; idx += 256) ds[(idx / 64) * 65 + (idx & 63)] = D[idx];
-  for (int idx = threadIdx.x; idx < 64 * CS; idx += 256) {
-    const int tt = idx / CS, cc = idx - tt * CS;
-    const bool ok = tt < nvalid;
-    const size_t o = (row0 + (ok ? tt : 0)) * DK + c0 + cc;
-    qs[tt * 33 + cc] = ok ? P.q_scale * Br.q[o] : 0.f;
-    ks[tt * 33 + cc] = ok ? Br.k[o] : 0.f;
-    // rows past the call's end keep the last valid b (the gate adds nothing there)
-    bs[tt * 33 + cc] = Br.lb[(row0 + min(tt, P.C - 1)) * DK + c0 + cc];
-  }
+  stage<64, 64, 65, true, false>(ds, [&](int tt, int i) { return D[tt * 64 + i]; });
+  auto at_ = [&](int tt, int cc) { return (row0 + (tt < nvalid ? tt : 0)) * DK + c0 + cc; };
+  stage<64, CS, 33, true, false>(qs, [&](int tt, int cc) {
+    const float v = P.q_scale * Br.q[at_(tt, cc)];
+    return tt < nvalid ? v : 0.f;
+  });
+  stage<64, CS, 33, true, false>(ks, [&](int tt, int cc) {
+    const float v = Br.k[at_(tt, cc)];
+    return tt < nvalid ? v : 0.f;
+  });
+  // rows past the chunk keep its last b (the gate adds nothing past the call's end)
+  stage<64, CS, 33, true, false>(bs, [&](int tt, int cc) { return Br.lb[(row0 + min(tt, P.C - 1)) * DK + c0 + cc]; });
   __syncthreads();
   float blast[8];
 #pragma unroll
@@ -490,11 +538,20 @@ __global__ __launch_bounds__(256) void k_bwd_dzg(const BwdParams P, int bi) {
   const int b = sq / Br.h, head = sq - b * Br.h;
   float suffix = 0.f;
   for (int c2 = ch + 1; c2 < Br.nch; ++c2) suffix += Br.rtot[((size_t)sq * Br.nch + c2) * P.dk + c];
-  for (int tt = 0; tt < P.C; ++tt) {
-    const int j = ch * P.C + tt;
-    if (j >= Br.n) break;
-    const size_t o = ((size_t)sq * Br.np + j) * P.dk + c;
-    Br.dzg[((size_t)(b * Br.n + j) * Br.h + head) * P.dk + c] = (Br.rsum[o] + suffix) * Br.sg[o];
+  const int nvalid = min(P.C, Br.n - ch * P.C);
+  for (int t0 = 0; t0 < nvalid; t0 += 8) {
+    float rv[8], sv[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const size_t o = ((size_t)sq * Br.np + ch * P.C + min(t0 + k, nvalid - 1)) * P.dk + c;
+      rv[k] = Br.rsum[o];
+      sv[k] = Br.sg[o];
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int j = ch * P.C + t0 + k;
+      if (t0 + k < nvalid) Br.dzg[((size_t)(b * Br.n + j) * Br.h + head) * P.dk + c] = (rv[k] + suffix) * sv[k];
+    }
   }
 }
 
@@ -667,15 +724,27 @@ __global__ __launch_bounds__(256) void k_bwd_dx(const BwdParams P) {
 }
 
 // ---- column sums and x^T dz, in two deterministic passes ----
-// partial[rb][col] = sum over row block rb of src[row][col] (src fp32, ld)
+// partial[rb][col] = sum over row block rb of src[row][col] (src fp32, ld);
+// a block is 64 columns x 4 row lanes, its row block cut into the lanes
 __global__ __launch_bounds__(256) void k_bwd_colsum_partial(const float* src, int rows, int cols, int ld,
                                                             int rows_per_block, float* partial) {
-  const int col = blockIdx.x * 256 + threadIdx.x;
-  if (col >= cols) return;
+  __shared__ float red[4][64];
+  const int cc = threadIdx.x & 63, lane4 = threadIdx.x >> 6;
+  const int col = blockIdx.x * 64 + cc;
   const int r0 = blockIdx.y * rows_per_block, r1 = min(rows, r0 + rows_per_block);
+  const int colc = min(col, cols - 1);
   float acc = 0.f;
-  for (int r = r0; r < r1; ++r) acc += src[(size_t)r * ld + col];
-  partial[(size_t)blockIdx.y * cols + col] = acc;
+  for (int r = r0 + lane4; r < r1; r += 32) {
+    float v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = src[(size_t)min(r + 4 * k, r1 - 1) * ld + colc];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc += (r + 4 * k < r1) ? v[k] : 0.f;
+  }
+  red[lane4][cc] = acc;
+  __syncthreads();
+  if (lane4 == 0 && col < cols)
+    partial[(size_t)blockIdx.y * cols + col] = red[0][cc] + red[1][cc] + red[2][cc] + red[3][cc];
 }
 
 // out[col] = sum_rb partial[rb][col]
@@ -684,7 +753,13 @@ __global__ __launch_bounds__(256) void k_bwd_colsum_finish(const float* partial,
   const int col = blockIdx.x * 256 + threadIdx.x;
   if (col >= cols) return;
   float acc = 0.f;
-  for (int rb = 0; rb < nrb; ++rb) acc += partial[(size_t)rb * cols + col];
+  for (int rb0 = 0; rb0 < nrb; rb0 += 8) {
+    float v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = partial[(size_t)min(rb0 + k, nrb - 1) * cols + col];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc += (rb0 + k < nrb) ? v[k] : 0.f;
+  }
   out[(size_t)col * out_stride] = acc;
 }
 
@@ -699,6 +774,7 @@ __global__ __launch_bounds__(256) void k_bwd_wf_partial(const BwdParams P, int r
   float acc[FUSION_STRIDE];
 #pragma unroll
   for (int i = 0; i < FUSION_STRIDE; ++i) acc[i] = 0.f;
+#pragma unroll 4
   for (int r = r0 + tg; r < r1; r += 4) {
     const float xv = to_f32(reinterpret_cast<const T*>(P.x)[(size_t)r * P.d + col]);
     const f32x4 z0 = *reinterpret_cast<const f32x4*>(P.dz + (size_t)r * FUSION_STRIDE);
@@ -759,7 +835,9 @@ hipError_t launch_bwd_chunk(const BwdParams& P, int which, bool bf16_path, hipSt
 
 hipError_t launch_bwd_gate(const BwdParams& P, hipStream_t st) {
   if (P.total_units == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_bwd_gate, dim3(P.total_units), dim3(256), 0, st, P);
+  // block means, W_g2 slice, log alpha; the part totals (256 floats) reuse the first
+  const size_t lds = (size_t)(std::max(P.C * P.r, 256) + P.r * P.dk + P.C * P.dk) * sizeof(float);
+  hipLaunchKernelGGL(k_bwd_gate, dim3(P.total_units), dim3(256), lds, st, P);
   return hipGetLastError();
 }
 
@@ -822,8 +900,8 @@ hipError_t launch_bwd_colsum(const float* src, int rows, int cols, int ld, float
                              float* out, int out_stride, hipStream_t st) {
   if (cols == 0) return hipSuccess;
   const int rpb = (rows + nrb - 1) / nrb;
-  hipLaunchKernelGGL(k_bwd_colsum_partial, dim3((cols + 255) / 256, nrb), dim3(256), 0, st, src, rows, cols,
-                     ld, rpb, partial);
+  hipLaunchKernelGGL(k_bwd_colsum_partial, dim3((cols + 63) / 64, nrb), dim3(256), 0, st, src, rows, cols, ld,
+                     rpb, partial);
   hipLaunchKernelGGL(k_bwd_colsum_finish, dim3((cols + 255) / 256), dim3(256), 0, st, partial, nrb, cols, out,
                      out_stride);
   return hipGetLastError();
@@ -844,12 +922,46 @@ __global__ __launch_bounds__(256) void k_bwd_wf_finish(const float* partial, int
   if (idx >= d * m) return;
   const int c = idx / m, i = idx - c * m;
   float acc = 0.f;
-  for (int rb = 0; rb < nrb; ++rb) acc += partial[((size_t)rb * d + c) * FUSION_STRIDE + i];
+  for (int rb0 = 0; rb0 < nrb; rb0 += 8) {
+    float v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = partial[((size_t)min(rb0 + k, nrb - 1) * d + c) * FUSION_STRIDE + i];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc += (rb0 + k < nrb) ? v[k] : 0.f;
+  }
   out[idx] = acc;
 }
 
 hipError_t launch_bwd_wf_finish(const float* partial, int nrb, int d, int m, float* out, hipStream_t st) {
   hipLaunchKernelGGL(k_bwd_wf_finish, dim3((d * m + 255) / 256), dim3(256), 0, st, partial, nrb, d, m, out);
+  return hipGetLastError();
+}
+
+}  // namespace msgla
+
+namespace msgla {
+
+// Sum of S partial products [S][M][N] (fp32) into up to four destinations,
+// each owning a column range of the product: out_k[row][col - c0_k].
+
+__global__ __launch_bounds__(256) void k_bwd_splitk_reduce(const float* part, int S, int M, int N, SplitDst D) {
+  const size_t total = (size_t)M * N;
+  for (size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+       idx += (size_t)gridDim.x * blockDim.x) {
+    float acc = 0.f;
+    for (int s = 0; s < S; ++s) acc += part[(size_t)s * total + idx];
+    const int row = (int)(idx / N), col = (int)(idx - (size_t)row * N);
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      if (k < D.n && col >= D.c0[k] && col < D.c0[k] + D.nc[k]) D.p[k][(size_t)row * D.nc[k] + col - D.c0[k]] = acc;
+  }
+}
+
+hipError_t launch_bwd_splitk_reduce(const float* part, int S, int M, int N, const SplitDst& D, hipStream_t st) {
+  const size_t total = (size_t)M * N;
+  if (total == 0) return hipSuccess;
+  const unsigned grid = (unsigned)std::min<size_t>((total + 255) / 256, 65536);
+  hipLaunchKernelGGL(k_bwd_splitk_reduce, dim3(grid), dim3(256), 0, st, part, S, M, N, D);
   return hipGetLastError();
 }
 

@@ -305,6 +305,13 @@ struct BwdParams {
   BwdBranch br[MSGLA_MAX_BRANCHES];
 };
 
+// Destinations of a split-K weight-gradient product (k_bwd_splitk_reduce).
+struct SplitDst {
+  float* p[4];
+  int c0[4], nc[4];
+  int n;
+};
+
 // ---------------- packing ------------------------------------------------------
 struct PackSrc {
   const void* W_q; const void* W_k; const void* W_v; const void* W_g1; const void* W_g2;
