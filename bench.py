@@ -328,6 +328,56 @@ def measure_library_gemms(cfg, B, L, stage_ms, steps=50, warmup=10):
     return out
 
 
+def measure_training(workload="main", steps=20, warmup=5):
+    """One training step of the layer: the forward and msgla_backward (which
+    recomputes the forward's intermediates itself) on the same input, each timed
+    with events over `steps` back-to-back calls after clock settling; dO is a
+    seeded N(0, 1) tensor.  The backward's algorithmic flops are taken as twice
+    the forward's (each product of the forward appears twice in the backward:
+    once for the input's gradient, once for the weight's)."""
+    import numpy as np
+    import torch
+    from scale_gla_layer_amd.config import WORKLOADS
+    from scale_gla_layer_amd.runner import DeviceLayer, to_device
+    from scale_gla_layer_amd.synth import make_inputs, round_to
+    wl = WORKLOADS[workload]
+    cfg, B, L = wl.cfg, wl.batch, wl.seq_len
+    X, W = make_inputs(cfg, B, L, seed=0, gate_bias=wl.gate_bias)
+    layer = DeviceLayer(cfg, W)
+    x = to_device(X, cfg.dtype)
+    dO = to_device(round_to(np.random.default_rng(1).normal(0.0, 1.0, X.shape), cfg.dtype), cfg.dtype)
+    settle_clocks(layer, x, max_s=1.0)
+    out = layer.new_output(B, L)
+    dx, grads = layer.backward(x, dO)
+    for _ in range(warmup):
+        layer.forward(x, out=out)
+        layer.backward(x, dO, dx=dx, grads=grads)
+    torch.cuda.synchronize()
+
+    def timed(fn):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps * 1e3
+
+    fwd = timed(lambda: layer.forward(x, out=out))
+    bwd = timed(lambda: layer.backward(x, dO, dx=dx, grads=grads))
+    step = timed(lambda: (layer.forward(x, out=out), layer.backward(x, dO, dx=dx, grads=grads)))
+    alg = algorithmic(cfg, B, L)
+    peak = PEAK["bf16_mfma_tflops"] if cfg.dtype == "bf16" else PEAK["fp32_mfma_tflops"]
+    bwd_flops = 2 * alg["flops"]
+    del layer, x, dO, out, dx, grads
+    return {"workload": workload, "batch": B, "seq_len": L, "forward_us": round(fwd, 1),
+            "backward_us": round(bwd, 1), "step_us": round(step, 1),
+            "tokens_per_s": round(B * L / (step * 1e-6), 1),
+            "backward_algorithmic_gflop": round(bwd_flops / 1e9, 2),
+            "backward_tflops": round(bwd_flops / (bwd * 1e-6) / 1e12, 1),
+            "backward_roofline_frac": round(bwd_flops / (peak * 1e12) / (bwd * 1e-6), 4)}
+
+
 def device_info():
     """What the line was measured on: the GPU's name, gfx architecture and
     CU count, the HIP runtime torch was built against, and the host CPU."""
@@ -520,20 +570,22 @@ def cpu_baseline(workload: str, min_s: float = 10.0):
 
 PROFILE_COMMANDS = {
     "ktrace": "rocprofv3 --kernel-trace --stats -f csv -d {d}/ktrace -o main -- "
-              "python3 bench.py --steps 20 --warmup 5 --no-cpu-baseline --no-gla --no-per-call --no-decode --no-mask --no-routing --no-norm --no-workloads --no-library-gemms",
+              "python3 bench.py --steps 20 --warmup 5 --no-cpu-baseline --no-gla --no-per-call --no-decode --no-mask --no-routing --no-norm --no-workloads --no-library-gemms --no-training",
     "fetch": "rocprofv3 --pmc FETCH_SIZE -f csv -d {d}/pmc_fetch -o main -- "
-             "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-gla --no-per-call --no-decode --no-mask --no-routing --no-norm --no-workloads --no-library-gemms",
+             "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-gla --no-per-call --no-decode --no-mask --no-routing --no-norm --no-workloads --no-library-gemms --no-training",
     "write": "rocprofv3 --pmc WRITE_SIZE -f csv -d {d}/pmc_write -o main -- "
-             "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-gla --no-per-call --no-decode --no-mask --no-routing --no-norm --no-workloads --no-library-gemms",
+             "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-gla --no-per-call --no-decode --no-mask --no-routing --no-norm --no-workloads --no-library-gemms --no-training",
     "util": "rocprofv3 --pmc MfmaUtil VALUBusy LdsUtil LDSBankConflict MfmaFlopsBF16 MfmaFlopsF32 "
             "-f csv -d {d}/pmc_util -o main -- "
-            "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-gla --no-per-call --no-decode --no-mask --no-routing --no-norm --no-workloads --no-library-gemms",
+            "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-gla --no-per-call --no-decode --no-mask --no-routing --no-norm --no-workloads --no-library-gemms --no-training",
     "cal_fetch": "rocprofv3 --pmc FETCH_SIZE -f csv -d {d}/cal_fetch -o copy -- "
                  "python3 bench.py --copy-calibration",
     "cal_write": "rocprofv3 --pmc WRITE_SIZE -f csv -d {d}/cal_write -o copy -- "
                  "python3 bench.py --copy-calibration",
     "dec_ktrace": "rocprofv3 --kernel-trace --stats -f csv -d {d}/dec_ktrace -o decode -- "
                   "python3 bench.py --only-decode",
+    "bwd_ktrace": "rocprofv3 --kernel-trace --stats -f csv -d {d}/bwd_ktrace -o backward -- "
+                  "python3 bench.py --only-training --no-gla",
 }
 
 
@@ -553,6 +605,45 @@ def _counter_means(path: str) -> dict:
     return {k: (sum(v) / len(v), len(v)) for k, v in acc.items()}
 
 
+def summarize_training_profile(d, workload, wl, cmds, out_dir):
+    """profiles/kernels_training_<workload>.md from the bwd_ktrace run, if present."""
+    import csv
+    # the training step: forward and backward (its own recompute included)
+    bwd_csv = os.path.join(d, "bwd_ktrace", "backward_kernel_stats.csv")
+    if os.path.exists(bwd_csv):
+        with open(bwd_csv, newline="", encoding="utf-8") as f:
+            bstats = list(csv.DictReader(f))
+        brows = [f"# Kernel trace, training step (forward + backward), workload {workload} "
+                 f"({wl.description})", "",
+                 "Command (from the repository root, `<out>` any output directory):", "",
+                 f"    {cmds['bwd_ktrace']}", "",
+                 "Clock settling forwards, then 5 warm-up steps and 20 forwards, 20 backwards and "
+                 "20 forward + backward steps. Each backward first recomputes the forward's "
+                 "intermediates with the forward's kernels except the fused output launch (so "
+                 "those appear about twice as often as k3f_fine_fuse). rocBLAS kernels are "
+                 "named by their macro tile; k_bwd_outer (S) and (dS) are the chunks' state and "
+                 "state-gradient increments.", "",
+                 "| kernel | calls | avg us | min us | max us | share |", "|---|---|---|---|---|---|"]
+        import re
+        for r in bstats:
+            name = r["Name"]
+            if name.startswith("Cijk"):
+                mt = re.search(r"MT\d+x\d+x\d+", name)
+                short = "rocBLAS " + (mt.group(0) if mt else "gemm") + (" fp32" if "_SB_" in name else "")
+            else:
+                short = _short(name)
+                m = re.search(r"(k_bwd_[A-Za-z0-9_]*?)(?=I[DfL]|E|\(|$)", name)
+                if m:
+                    short = m.group(1)
+                    if short == "k_bwd_outer":
+                        short += " (dS)" if "Lb1E" in name else " (S)"
+            brows.append(f"| {short} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                         f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                         f"{float(r['Percentage']):.1f}% |")
+        with open(os.path.join(out_dir, f"kernels_training_{workload}.md"), "w", encoding="utf-8") as f:
+            f.write("\n".join(brows) + "\n")
+
+
 def summarize_profiles(d: str, workload: str = "main"):
     """Writes profiles/kernels_<workload>.md (kernel trace) and, per kernel of
     the forward, profiles/<kernel>_<workload>_traffic.json (FETCH_SIZE and
@@ -566,6 +657,9 @@ def summarize_profiles(d: str, workload: str = "main"):
     os.makedirs(out_dir, exist_ok=True)
     cmds = {k: v.format(d="<out>") for k, v in PROFILE_COMMANDS.items()}
 
+    if not os.path.exists(os.path.join(d, "ktrace", "main_kernel_stats.csv")):
+        summarize_training_profile(d, workload, wl, cmds, out_dir)
+        return
     with open(os.path.join(d, "ktrace", "main_kernel_stats.csv"), newline="", encoding="utf-8") as f:
         stats = list(csv.DictReader(f))
     lines = [f"# Kernel trace, workload {workload} ({wl.description})", "",
@@ -678,6 +772,7 @@ def summarize_profiles(d: str, workload: str = "main"):
                          f"{float(r['Percentage']):.1f}% |")
         with open(os.path.join(out_dir, "kernels_decode_sweep_1248.md"), "w", encoding="utf-8") as f:
             f.write("\n".join(drows) + "\n")
+    summarize_training_profile(d, workload, wl, cmds, out_dir)
     log(f"[bench] wrote profiles for {workload} from {d}")
 
 
@@ -716,6 +811,10 @@ def main():
                     help="skip the other workloads' forward lines (GLA, long, sweeps)")
     ap.add_argument("--only-decode", action="store_true",
                     help="time only the streaming decode step and print its JSON")
+    ap.add_argument("--no-training", action="store_true",
+                    help="skip the training-step (forward + backward) timing")
+    ap.add_argument("--only-training", action="store_true",
+                    help="time only the training step (main and GLA baseline) and print its JSON")
     ap.add_argument("--cpu-worker", nargs=4, metavar=("WORKLOAD", "FIRST", "STRIDE", "SECONDS"),
                     help=argparse.SUPPRESS)
     args = ap.parse_args()
@@ -732,6 +831,13 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.only_training:
+        tr = measure_training(args.workload)
+        if not args.no_gla and args.workload != "gla_baseline":
+            tr["gla"] = measure_training("gla_baseline")
+            tr["ratio_vs_gla"] = round(tr["tokens_per_s"] / tr["gla"]["tokens_per_s"], 4)
+        print(json.dumps(tr), flush=True)
         return
     if args.only_decode:
         dec = measure_decode()
@@ -860,6 +966,17 @@ def main():
             f"{dec['achieved_gb_s']} GB/s ({dec['algorithmic_mb_per_step']} MB/step), host "
             f"{dec['host_us_per_call']} us/call")
 
+    training = None
+    if not args.no_training:
+        training = measure_training(wl.name)
+        log(f"[bench] training step {training['step_us']} us ({training['forward_us']} forward + "
+            f"{training['backward_us']} backward), {training['tokens_per_s'] / 1e6:.2f} M tokens/s")
+        if args.workload != "gla_baseline" and not args.no_gla:
+            training["gla"] = measure_training("gla_baseline")
+            training["ratio_vs_gla"] = round(training["tokens_per_s"] / training["gla"]["tokens_per_s"], 4)
+            log(f"[bench] GLA baseline training step {training['gla']['step_us']} us; MS-GLA / GLA "
+                f"training throughput {training['ratio_vs_gla']}")
+
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] timing the fp64 CPU oracle on the host ...")
@@ -903,6 +1020,7 @@ def main():
         "ratio_vs_gla": None if ratio_vs_gla is None else round(ratio_vs_gla, 4),
         "gla_tokens_per_s": None if gla is None else round(gla, 1),
         "decode": dec,
+        "training": training,
         "masked": masked,
         "routing": routing,
         "norm": normed,
