@@ -9,7 +9,8 @@ several chunks with a ragged last chunk in every branch, tail positions past a
 coarse branch's last complete block, chunks 16, 32 and 64, q_scale and gamma
 off their defaults, strong gates, a scale set without a scale-1 branch, a
 single branch (no fusion), a branch whose scale exceeds the sequence, and the
-main configuration's dimensions in bf16."""
+main configuration's dimensions in bf16, and the full main workload (B = 8,
+L = 2048)."""
 import dataclasses
 
 import numpy as np
@@ -110,3 +111,39 @@ def test_bf16_main_dimensions():
 def test_bf16_sweep_dimensions_with_gate_bias():
     cfg = dataclasses.replace(WORKLOADS["sweep_1248"].cfg)
     backward_case(cfg, B=1, L=264, seed=19, gate_bias=(1.0, 4.0))
+
+
+def test_bf16_full_size_main_workload():
+    """The main workload at its full size (B = 8, L = 2048): every gradient against the
+    oracle, which runs sequence by sequence (a weight gradient is the sum of the
+    sequences' gradients; dx of a sequence depends on that sequence only)."""
+    import torch
+    wl = WORKLOADS["main"]
+    cfg, B, L = wl.cfg, wl.batch, wl.seq_len
+    say(f"backward full size main B={B} L={L}")
+    X, W = make_inputs(cfg, B, L, seed=23)
+    dO = round_to(np.random.default_rng(24).normal(0.0, 1.0, X.shape), cfg.dtype)
+    layer = DeviceLayer(cfg, W)
+    dx, (gb, gWf, gbf) = layer.backward(to_device(X, cfg.dtype), to_device(dO, cfg.dtype))
+    torch.cuda.synchronize()
+    dX = from_device(dx)
+    got = {f"br{i}.{k}": from_device(g[k]) for i, g in enumerate(gb) for k in KEYS}
+    got["W_f"], got["b_f"] = from_device(gWf), from_device(gbf)
+    ref = {k: np.zeros_like(v, dtype=np.float64) for k, v in got.items()}
+    dx_err = 0.0
+    for b in range(B):
+        dXb, rb = orc.layer_backward(X[b:b + 1], W, cfg, dO[b:b + 1])
+        dx_err = max(dx_err, orc.row_relative_error(dX[b:b + 1], dXb)[0])
+        for i, g in enumerate(rb["branches"]):
+            for k in KEYS:
+                ref[f"br{i}.{k}"] += g[k]
+        ref["W_f"] += rb["W_f"]
+        ref["b_f"] += rb["b_f"]
+        say(f"sequence {b}: dx row-relative error so far {dx_err:.2e}")
+    errs = {"dx": dx_err}
+    for k in got:
+        assert np.all(np.isfinite(got[k])), k
+        errs[k] = _tensor_err(got[k], ref[k])
+    say("errors " + ", ".join(f"{k} {v:.2e}" for k, v in errs.items()))
+    worst = max(errs, key=errs.get)
+    assert errs[worst] <= TOL[cfg.dtype], f"{worst}: {errs[worst]:.3e}"
