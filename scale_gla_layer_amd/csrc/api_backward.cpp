@@ -42,7 +42,7 @@ constexpr int BWD_SPLIT_MAX = 16; // K slices of a weight-gradient product
 int colsum_blocks(int rows) { return std::max(1, std::min(BWD_NRB_MAX, (rows + 127) / 128)); }
 
 struct BwdBranchGeom {
-  size_t lb, sg, g1c, Sst, dSt, AD, rsum, rtot, dob, dzg, dP, dY, Yc, ycat, dxp;
+  size_t lb, sg, g1c, Sst, dSt, AD, QKi, rsum, rtot, dob, dzg, dP, dY, Yc, ycat, dxp;
   int NP;
 };
 
@@ -77,6 +77,7 @@ BwdGeom bwd_geom(const PackGeom& g, int64_t B, int64_t L) {
     o.Sst = take(chunks * g.dk * g.dv * 4);
     o.dSt = take(chunks * g.dk * g.dv * 4);
     o.AD = take(chunks * 2 * 64 * 64 * 4);
+    o.QKi = take(chunks * 2 * 64 * g.dk * 4);
     o.rsum = take(rows * g.dk * 4);
     o.rtot = take(chunks * g.dk * 4);
     o.dob = take(prow * bg.h * g.dv * 4);
@@ -269,6 +270,7 @@ msgla_status msgla_backward(const msgla_config* cfg, const void* packed, const v
     Br.Sst = at<float>(workspace, o.Sst);
     Br.dSt = at<float>(workspace, o.dSt);
     Br.AD = at<float>(workspace, o.AD);
+    Br.QKi = at<float>(workspace, o.QKi);
     Br.rsum = at<float>(workspace, o.rsum);
     Br.rtot = at<float>(workspace, o.rtot);
     Br.dob = at<float>(workspace, o.dob);
@@ -322,6 +324,7 @@ msgla_status msgla_backward(const msgla_config* cfg, const void* packed, const v
     HIP_TRY(launch_bwd_scan(P.br[i].dSt, P.br[i].lb, (int)B * P.br[i].h, P.br[i].nch, P.br[i].np, g.C, g.dk,
                             g.dv, true, st));
   HIP_TRY(launch_bwd_chunk(P, 2, g.bf16, st));
+  HIP_TRY(launch_bwd_chunk(P, 5, g.bf16, st));
   HIP_TRY(launch_bwd_chunk(P, 3, g.bf16, st));
   HIP_TRY(launch_bwd_chunk(P, 4, g.bf16, st));
   for (int i = 0; i < g.m; ++i) {

@@ -105,6 +105,41 @@ __device__ __forceinline__ void stage(float* lds, F&& f) {
   }
 }
 
+// The two halves of stage(), for tiles whose loads should share one round trip
+// (or be issued a step ahead): load_tile fills v[] in registers, store_tile
+// writes it to LDS with the same element order.
+template <int ROWS, int COLS, bool COL_FAST, class F>
+__device__ __forceinline__ void load_tile(float (&v)[ROWS * COLS / 256], F&& f) {
+  static_assert((ROWS * COLS) % 256 == 0, "whole rounds of 256 threads");
+#pragma unroll
+  for (int k = 0; k < ROWS * COLS / 256; ++k) {
+    const int idx = threadIdx.x + 256 * k;
+    const int row = COL_FAST ? idx / COLS : idx % ROWS, col = COL_FAST ? idx % COLS : idx / ROWS;
+    v[k] = f(row, col);
+  }
+}
+template <int ROWS, int COLS, int LS, bool COL_FAST, bool TR>
+__device__ __forceinline__ void store_tile(float* lds, const float (&v)[ROWS * COLS / 256]) {
+#pragma unroll
+  for (int k = 0; k < ROWS * COLS / 256; ++k) {
+    const int idx = threadIdx.x + 256 * k;
+    const int row = COL_FAST ? idx / COLS : idx % ROWS, col = COL_FAST ? idx % COLS : idx / ROWS;
+    lds[TR ? col * LS + row : row * LS + col] = v[k];
+  }
+}
+
+// One 16 x 16 fp32 tile on the matrix cores: acc += A B^T over 16 * ns k-values,
+// A and B rows of fp32 in LDS (16 rows each from a and b, row strides lda and
+// ldb floats, 16-byte aligned).  Lane l holds rows 4 (l / 16) + i, i = 0..3, of
+// column l % 16 of the tile.
+__device__ __forceinline__ f32x4 tile_f32(const float* a, int lda, const float* b, int ldb, int ns, f32x4 acc) {
+  const int l = threadIdx.x & 63;
+  const float* pa = a + (l & 15) * lda + 4 * (l >> 4);
+  const float* pb = b + (l & 15) * ldb + 4 * (l >> 4);
+  for (int s = 0; s < ns; ++s) acc = mma_slab<float>(ld16(pa + 16 * s), ld16(pb + 16 * s), acc);
+  return acc;
+}
+
 }  // namespace
 
 // ---- gate recompute: b (chunk-local cumulative log alpha), sigmoid(-z)/gamma, g1 ----
@@ -169,67 +204,60 @@ __global__ __launch_bounds__(256) void k_bwd_gate(const BwdParams P) {
 // ---- per-chunk outer products (X * F)^T Y  [d_k][64-column slice of d_v] ----
 // REV = false: X = k, F = e^{b_last - b}, Y = v     (the chunk's state increment)
 // REV = true:  X = q_scale q, F = e^{b}, Y = dLoss/do  (its state-gradient increment)
+// On the matrix cores: A = (X * F)^T [d_k][64 positions], B = Y^T [64 columns][64
+// positions]; wave w takes columns 16 w .. 16 w + 15 and every row tile.
 template <typename T, int DK, bool REV>
 __global__ __launch_bounds__(256) void k_bwd_outer(const BwdParams P) {
-  __shared__ float xs[64 * DK];
-  __shared__ __attribute__((aligned(16))) float ys[64 * 64];
+  constexpr int LD = 68, NT = DK / 16;
+  __shared__ __attribute__((aligned(16))) float xt[DK * LD];
+  __shared__ __attribute__((aligned(16))) float yt[64 * LD];
   const UnitPos u = unit_pos(P, blockIdx.x);
   const BwdBranch& Br = P.br[u.bi];
   const int j0 = u.ch * P.C, e0 = blockIdx.y * 64;
   const int nvalid = min(P.C, Br.n - j0);
   const size_t row0 = (size_t)u.sq * Br.np + j0;
-  stage<64, DK, DK, true, false>(xs, [&](int t, int c) {
-    const bool ok = t < nvalid;
-    const size_t o = (row0 + (ok ? t : 0)) * DK + c;
-    float val;
+  {
+    float rx[64 * DK / 256], ry[16];
+    load_tile<64, DK, true>(rx, [&](int t, int c) {
+      const bool ok = t < nvalid;
+      const size_t o = (row0 + (ok ? t : 0)) * DK + c;
+      float val;
+      if constexpr (REV)
+        val = P.q_scale * Br.q[o] * __expf(Br.lb[o]);
+      else
+        val = Br.k[o] * __expf(Br.lb[(row0 + P.C - 1) * DK + c] - Br.lb[o]);
+      return ok ? val : 0.f;
+    });
     if constexpr (REV)
-      val = P.q_scale * Br.q[o] * __expf(Br.lb[o]);
+      load_tile<64, 64, true>(ry, [&](int t, int e) {
+        const bool ok = t < nvalid;
+        const float val = Br.dob[((size_t)(u.b * Br.n + j0 + (ok ? t : 0)) * Br.h + u.head) * P.dv + e0 + e];
+        return ok ? val : 0.f;
+      });
     else
-      val = Br.k[o] * __expf(Br.lb[(row0 + P.C - 1) * DK + c] - Br.lb[o]);
-    return ok ? val : 0.f;
-  });
-  if constexpr (REV)
-    stage<64, 64, 64, true, false>(ys, [&](int t, int e) {
-      const bool ok = t < nvalid;
-      const float val = Br.dob[((size_t)(u.b * Br.n + j0 + (ok ? t : 0)) * Br.h + u.head) * P.dv + e0 + e];
-      return ok ? val : 0.f;
-    });
-  else
-    stage<64, 64, 64, false, false>(ys, [&](int t, int e) {
-      const bool ok = t < nvalid;
-      const float val = to_f32(reinterpret_cast<const T*>(Br.vT)[(((size_t)u.sq * Br.nch + u.ch) * P.dv + e0 + e) * P.C + (ok ? t : 0)]);
-      return ok ? val : 0.f;
-    });
+      load_tile<64, 64, true>(ry, [&](int e, int t) {
+        const bool ok = t < nvalid;
+        const float val = to_f32(reinterpret_cast<const T*>(Br.vT)[(((size_t)u.sq * Br.nch + u.ch) * P.dv + e0 + e) * P.C + (ok ? t : 0)]);
+        return ok ? val : 0.f;
+      });
+    store_tile<64, DK, LD, true, true>(xt, rx);
+    if constexpr (REV)
+      store_tile<64, 64, LD, true, true>(yt, ry);
+    else
+      store_tile<64, 64, LD, true, false>(yt, ry);
+  }
   __syncthreads();
-  constexpr int NA = DK >= 32 ? DK / 32 : 1;
-  const int cr = threadIdx.x & 31, er = threadIdx.x >> 5;
-  float acc[NA][8];
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  f32x4 acc[NT];
 #pragma unroll
-  for (int a = 0; a < NA; ++a)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[a][e] = 0.f;
-  const int crc = DK >= 32 ? cr : (cr & (DK - 1));
-  for (int t = 0; t < nvalid; ++t) {
-    const f32x4 y0 = *reinterpret_cast<const f32x4*>(ys + t * 64 + er * 8);
-    const f32x4 y1 = *reinterpret_cast<const f32x4*>(ys + t * 64 + er * 8 + 4);
-#pragma unroll
-    for (int a = 0; a < NA; ++a) {
-      const float xv = xs[t * DK + crc + 32 * a];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        acc[a][e] += xv * y0[e];
-        acc[a][e + 4] += xv * y1[e];
-      }
-    }
-  }
-  if (DK < 32 && cr >= DK) return;
+  for (int ct = 0; ct < NT; ++ct) acc[ct] = tile_f32(xt + 16 * ct * LD, LD, yt + 16 * w * LD, LD, 4, zero4());
   float* out = REV ? Br.dSt : Br.Sst;
+  const size_t base = ((size_t)u.sq * Br.nch + u.ch) * DK;
 #pragma unroll
-  for (int a = 0; a < NA; ++a) {
-    float* o = out + (((size_t)u.sq * Br.nch + u.ch) * DK + crc + 32 * a) * P.dv + e0 + er * 8;
-    *reinterpret_cast<f32x4*>(o) = f32x4{acc[a][0], acc[a][1], acc[a][2], acc[a][3]};
-    *reinterpret_cast<f32x4*>(o + 4) = f32x4{acc[a][4], acc[a][5], acc[a][6], acc[a][7]};
-  }
+  for (int ct = 0; ct < NT; ++ct)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      out[(base + 16 * ct + 4 * (l >> 4) + i) * P.dv + e0 + 16 * w + (l & 15)] = acc[ct][i];
 }
 
 // ---- scan over chunks, in place: buf[c] <- carried value entering chunk c ----
@@ -257,39 +285,121 @@ __global__ __launch_bounds__(256) void k_bwd_scan(float* buf, const float* lb, i
   }
 }
 
-// ---- A and D of a chunk (t >= i, zero above the diagonal and outside the call) ----
+// ---- the chunk's dense products on the matrix cores: do S_prev^T, v dS_end^T, D ----
+// Over d_v in 32-column steps (do, v, S and dS staged in LDS): wave w takes rows
+// 16 w .. 16 w + 15 of do S^T and v dS^T (every column tile) and of
+// D = do v^T (D_ti for t >= i, zero elsewhere and outside the call).
+template <typename T, int DK>
+__global__ __launch_bounds__(256) void k_bwd_mm1(const BwdParams P) {
+  constexpr int EC = 32, LD = EC + 4, NT = DK / 16;
+  __shared__ __attribute__((aligned(16))) float dos[64 * LD];
+  __shared__ __attribute__((aligned(16))) float vs[64 * LD];
+  __shared__ __attribute__((aligned(16))) float ss[DK * LD];
+  __shared__ __attribute__((aligned(16))) float dss[DK * LD];
+  const UnitPos u = unit_pos(P, blockIdx.x);
+  const BwdBranch& Br = P.br[u.bi];
+  const int j0 = u.ch * P.C;
+  const int nvalid = min(P.C, Br.n - j0);
+  const size_t sbase = ((size_t)u.sq * Br.nch + u.ch) * DK;
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  f32x4 aq[NT], ak[NT], ad[4];
+#pragma unroll
+  for (int ct = 0; ct < NT; ++ct) aq[ct] = ak[ct] = zero4();
+#pragma unroll
+  for (int j = 0; j < 4; ++j) ad[j] = zero4();
+  // the next step's four tiles are loaded into registers while this step's
+  // products run, and stored to LDS after them
+  float rd[64 * EC / 256], rv[64 * EC / 256], rs_[DK * EC / 256], rds[DK * EC / 256];
+  auto load_step = [&](int e0) {
+    load_tile<64, EC, true>(rd, [&](int t, int e) {
+      const bool ok = t < nvalid;
+      const float v = Br.dob[((size_t)(u.b * Br.n + j0 + (ok ? t : 0)) * Br.h + u.head) * P.dv + e0 + e];
+      return ok ? v : 0.f;
+    });
+    load_tile<64, EC, false>(rv, [&](int t, int e) {
+      const bool ok = t < nvalid;
+      const float v = to_f32(reinterpret_cast<const T*>(Br.vT)[(((size_t)u.sq * Br.nch + u.ch) * P.dv + e0 + e) * P.C + (ok ? t : 0)]);
+      return ok ? v : 0.f;
+    });
+    load_tile<DK, EC, true>(rs_, [&](int c, int e) { return Br.Sst[(sbase + c) * P.dv + e0 + e]; });
+    load_tile<DK, EC, true>(rds, [&](int c, int e) { return Br.dSt[(sbase + c) * P.dv + e0 + e]; });
+  };
+  load_step(0);
+  for (int e0 = 0; e0 < P.dv; e0 += EC) {
+    store_tile<64, EC, LD, true, false>(dos, rd);
+    store_tile<64, EC, LD, false, false>(vs, rv);
+    store_tile<DK, EC, LD, true, false>(ss, rs_);
+    store_tile<DK, EC, LD, true, false>(dss, rds);
+    __syncthreads();
+    if (e0 + EC < P.dv) load_step(e0 + EC);
+#pragma unroll
+    for (int ct = 0; ct < NT; ++ct) {
+      aq[ct] = tile_f32(dos + 16 * w * LD, LD, ss + 16 * ct * LD, LD, EC / 16, aq[ct]);
+      ak[ct] = tile_f32(vs + 16 * w * LD, LD, dss + 16 * ct * LD, LD, EC / 16, ak[ct]);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) ad[j] = tile_f32(dos + 16 * w * LD, LD, vs + 16 * j * LD, LD, EC / 16, ad[j]);
+    __syncthreads();
+  }
+  float* QK = Br.QKi + ((size_t)u.sq * Br.nch + u.ch) * 2 * 64 * DK;
+  float* D = Br.AD + ((size_t)u.sq * Br.nch + u.ch) * 2 * 64 * 64 + 64 * 64;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int t = 16 * w + 4 * (l >> 4) + i;
+#pragma unroll
+    for (int ct = 0; ct < NT; ++ct) {
+      QK[t * DK + 16 * ct + (l & 15)] = aq[ct][i];
+      QK[64 * DK + t * DK + 16 * ct + (l & 15)] = ak[ct][i];
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int c = 16 * j + (l & 15);
+      D[t * 64 + c] = (c <= t && t < nvalid) ? ad[j][i] : 0.f;
+    }
+  }
+}
+
+// ---- A of a chunk, A_ti = sum_c q_tc k_ic e^{b_tc - b_ic} (t >= i, zero elsewhere) ----
 // thread: t = lane, i in 16 * wave .. 16 * wave + 15
 template <typename T, int DK>
 __global__ __launch_bounds__(256) void k_bwd_AD(const BwdParams P) {
-  __shared__ float sm[3 * 64 * 33 > 2 * 64 * 65 ? 3 * 64 * 33 : 2 * 64 * 65];
+  __shared__ float sm[3 * 64 * 33];
   const UnitPos u = unit_pos(P, blockIdx.x);
   const BwdBranch& Br = P.br[u.bi];
   const int j0 = u.ch * P.C;
   const int nvalid = min(P.C, Br.n - j0);
   const size_t row0 = (size_t)u.sq * Br.np + j0;
   const int t = threadIdx.x & 63, ig = threadIdx.x >> 6;
-  float accA[16], accD[16];
+  float accA[16];
 #pragma unroll
-  for (int v = 0; v < 16; ++v) accA[v] = accD[v] = 0.f;
+  for (int v = 0; v < 16; ++v) accA[v] = 0.f;
   float* qs = sm;
   float* ks = sm + 64 * 33;
   float* bs = sm + 2 * 64 * 33;
   constexpr int CW = DK < 32 ? DK : 32;
-  for (int c0 = 0; c0 < DK; c0 += CW) {
+  float rq[64 * CW / 256], rk[64 * CW / 256], rb[64 * CW / 256];
+  auto load_step = [&](int c0) {
     auto at_ = [&](int tt, int cc) { return (row0 + (tt < nvalid ? tt : 0)) * DK + c0 + cc; };
-    stage<64, CW, 33, true, false>(qs, [&](int tt, int cc) {
+    load_tile<64, CW, true>(rq, [&](int tt, int cc) {
       const float v = P.q_scale * Br.q[at_(tt, cc)];
       return tt < nvalid ? v : 0.f;
     });
-    stage<64, CW, 33, true, false>(ks, [&](int tt, int cc) {
+    load_tile<64, CW, true>(rk, [&](int tt, int cc) {
       const float v = Br.k[at_(tt, cc)];
       return tt < nvalid ? v : 0.f;
     });
-    stage<64, CW, 33, true, false>(bs, [&](int tt, int cc) {
+    load_tile<64, CW, true>(rb, [&](int tt, int cc) {
       const float v = Br.lb[at_(tt, cc)];
       return tt < nvalid ? v : 0.f;
     });
+  };
+  load_step(0);
+  for (int c0 = 0; c0 < DK; c0 += CW) {
+    store_tile<64, CW, 33, true, false>(qs, rq);
+    store_tile<64, CW, 33, true, false>(ks, rk);
+    store_tile<64, CW, 33, true, false>(bs, rb);
     __syncthreads();
+    if (c0 + CW < DK) load_step(c0 + CW);
     for (int cc = 0; cc < CW; ++cc) {
       const float qv = qs[t * 33 + cc], bt = bs[t * 33 + cc];
 #pragma unroll
@@ -300,107 +410,88 @@ __global__ __launch_bounds__(256) void k_bwd_AD(const BwdParams P) {
     }
     __syncthreads();
   }
-  float* ds = sm;
-  float* vs = sm + 64 * 65;
-  for (int e0 = 0; e0 < P.dv; e0 += 64) {
-    stage<64, 64, 65, true, false>(ds, [&](int tt, int e) {
-      const bool ok = tt < nvalid;
-      const float v = Br.dob[((size_t)(u.b * Br.n + j0 + (ok ? tt : 0)) * Br.h + u.head) * P.dv + e0 + e];
-      return ok ? v : 0.f;
-    });
-    // v^T per chunk [d_v][C]: consecutive threads take consecutive positions
-    stage<64, 64, 65, false, false>(vs, [&](int tt, int e) {
-      const bool ok = tt < nvalid;
-      const float v = to_f32(reinterpret_cast<const T*>(Br.vT)[(((size_t)u.sq * Br.nch + u.ch) * P.dv + e0 + e) * P.C + (ok ? tt : 0)]);
-      return ok ? v : 0.f;
-    });
-    __syncthreads();
-    for (int e = 0; e < 64; ++e) {
-      const float dv_ = ds[t * 65 + e];
-#pragma unroll
-      for (int v = 0; v < 16; ++v) accD[v] += dv_ * vs[(ig * 16 + v) * 65 + e];
-    }
-    __syncthreads();
-  }
   float* A = Br.AD + ((size_t)u.sq * Br.nch + u.ch) * 2 * 64 * 64;
 #pragma unroll
   for (int v = 0; v < 16; ++v) {
     const int i = ig * 16 + v;
-    const bool keep = i <= t && t < nvalid;
-    A[t * 64 + i] = keep ? accA[v] : 0.f;
-    A[64 * 64 + t * 64 + i] = keep ? accD[v] : 0.f;
+    A[t * 64 + i] = (i <= t && t < nvalid) ? accA[v] : 0.f;
   }
 }
 
 // ---- dv_i = sum_{t>=i} A_ti do_t + k-hat_i dS_end, into the v columns of dP ----
-// thread: i = lane, 16 columns 16 * wave .. of the block's 64-column slice
+// On the matrix cores: rows i, columns e of the block's 64-column slice; wave w
+// takes rows 16 w .. 16 w + 15.  A^T and do^T are staged with positions along
+// k; then k-hat and dS_end^T in 32-channel steps.
 template <typename T, int DK>
 __global__ __launch_bounds__(256) void k_bwd_dv(const BwdParams P) {
-  __shared__ float as[64 * 65];
-  __shared__ __attribute__((aligned(16))) float dos[64 * 64];
-  __shared__ float khs[64 * 65];
-  __shared__ __attribute__((aligned(16))) float dss[64 * 64];
+  constexpr int LD = 68, CW = DK < 32 ? DK : 32, LDC = CW + 4;
+  __shared__ __attribute__((aligned(16))) float at[64 * LD];   // A^T [i][t]
+  __shared__ __attribute__((aligned(16))) float dt[64 * LD];   // do^T [e][t]
+  __shared__ __attribute__((aligned(16))) float kh[64 * LDC];  // k-hat [i][c]
+  __shared__ __attribute__((aligned(16))) float dst[64 * LDC]; // dS_end^T [e][c]
   const UnitPos u = unit_pos(P, blockIdx.x);
   const BwdBranch& Br = P.br[u.bi];
   const int j0 = u.ch * P.C, e0 = blockIdx.y * 64;
   const int nvalid = min(P.C, Br.n - j0);
   const size_t row0 = (size_t)u.sq * Br.np + j0;
-  const int i = threadIdx.x & 63, eg = threadIdx.x >> 6;
+  const size_t sbase = ((size_t)u.sq * Br.nch + u.ch) * DK;
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
   const float* A = Br.AD + ((size_t)u.sq * Br.nch + u.ch) * 2 * 64 * 64;
-  stage<64, 64, 65, true, false>(as, [&](int tt, int i) { return A[tt * 64 + i]; });
-  stage<64, 64, 64, true, false>(dos, [&](int tt, int e) {
-    const bool ok = tt < nvalid;
-    const float v = Br.dob[((size_t)(u.b * Br.n + j0 + (ok ? tt : 0)) * Br.h + u.head) * P.dv + e0 + e];
-    return ok ? v : 0.f;
-  });
-  __syncthreads();
-  float acc[16];
-#pragma unroll
-  for (int v = 0; v < 16; ++v) acc[v] = 0.f;
-  for (int tt = 0; tt < 64; ++tt) {
-    const float a = as[tt * 65 + i];
-#pragma unroll
-    for (int v = 0; v < 16; v += 4) {
-      const f32x4 d4 = *reinterpret_cast<const f32x4*>(dos + tt * 64 + eg * 16 + v);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) acc[v + q] += a * d4[q];
-    }
-  }
-  constexpr int CW = DK < 64 ? DK : 64;
-  for (int c0 = 0; c0 < DK; c0 += CW) {
-    __syncthreads();
-    stage<64, CW, 65, true, false>(khs, [&](int tt, int cc) {
+  float rk[64 * CW / 256], rd[CW * 64 / 256];
+  auto load_step = [&](int c0) {
+    load_tile<64, CW, true>(rk, [&](int tt, int cc) {
       const bool ok = tt < nvalid;
       const size_t o = (row0 + (ok ? tt : 0)) * DK + c0 + cc;
       const float v = Br.k[o] * __expf(Br.lb[(row0 + P.C - 1) * DK + c0 + cc] - Br.lb[o]);
       return ok ? v : 0.f;
     });
-    stage<CW, 64, 64, true, false>(dss, [&](int cc, int e) {
-      return Br.dSt[(((size_t)u.sq * Br.nch + u.ch) * DK + c0 + cc) * P.dv + e0 + e];
+    load_tile<CW, 64, true>(rd, [&](int cc, int e) { return Br.dSt[(sbase + c0 + cc) * P.dv + e0 + e]; });
+  };
+  {
+    float ra[16], rt[16];
+    load_tile<64, 64, true>(ra, [&](int tt, int i) { return A[tt * 64 + i]; });
+    load_tile<64, 64, true>(rt, [&](int tt, int e) {
+      const bool ok = tt < nvalid;
+      const float v = Br.dob[((size_t)(u.b * Br.n + j0 + (ok ? tt : 0)) * Br.h + u.head) * P.dv + e0 + e];
+      return ok ? v : 0.f;
     });
-    __syncthreads();
-    for (int cc = 0; cc < CW; ++cc) {
-      const float kv = khs[i * 65 + cc];
-#pragma unroll
-      for (int v = 0; v < 16; v += 4) {
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(dss + cc * 64 + eg * 16 + v);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) acc[v + q] += kv * d4[q];
-      }
-    }
+    load_step(0);
+    store_tile<64, 64, LD, true, true>(at, ra);
+    store_tile<64, 64, LD, true, true>(dt, rt);
   }
-  if (i >= nvalid) return;
-  T* dst = reinterpret_cast<T*>(Br.dP) + (size_t)(u.b * Br.n + j0 + i) * Br.NP + Br.col_v + u.head * P.dv + e0 + eg * 16;
-  store8<T>(dst, acc);
-  store8<T>(dst + 8, acc + 8);
+  __syncthreads();
+  f32x4 acc[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) acc[j] = tile_f32(at + 16 * w * LD, LD, dt + 16 * j * LD, LD, 4, zero4());
+  for (int c0 = 0; c0 < DK; c0 += CW) {
+    __syncthreads();
+    store_tile<64, CW, LDC, true, false>(kh, rk);
+    store_tile<CW, 64, LDC, true, true>(dst, rd);
+    __syncthreads();
+    if (c0 + CW < DK) load_step(c0 + CW);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[j] = tile_f32(kh + 16 * w * LDC, LDC, dst + 16 * j * LDC, LDC, CW / 16, acc[j]);
+  }
+  T* dP = reinterpret_cast<T*>(Br.dP);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 16 * w + 4 * (l >> 4) + i;
+    if (r >= nvalid) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      dP[(size_t)(u.b * Br.n + j0 + r) * Br.NP + Br.col_v + u.head * P.dv + e0 + 16 * j + (l & 15)] =
+          from_f32<T>(acc[j][i]);
+  }
 }
 
 // ---- dq and dk of a chunk's 32-channel slice; in-chunk suffix sums of q dq - k dk ----
+// The dense parts (do S_prev^T and v dS_end^T) come from k_bwd_mm1; here the
+// intra-chunk terms with e^{-|b_t - b_i|} (b is non-increasing along the chunk).
 // thread: t = lane, channels c0 + 8 * wave .. + 7
 template <typename T, int DK>
 __global__ __launch_bounds__(256) void k_bwd_dqdk(const BwdParams P) {
   constexpr int CS = DK < 32 ? DK : 32;  // channels per block
-  __shared__ __attribute__((aligned(16))) float sm[2 * 64 * 65 + 2 * 64 * 32];
+  __shared__ __attribute__((aligned(16))) float sm[64 * 65 + 3 * 64 * 33];
   __shared__ float rs[64 * 33];
   const UnitPos u = unit_pos(P, blockIdx.x);
   const BwdBranch& Br = P.br[u.bi];
@@ -409,74 +500,45 @@ __global__ __launch_bounds__(256) void k_bwd_dqdk(const BwdParams P) {
   const size_t row0 = (size_t)u.sq * Br.np + j0;
   const int t = threadIdx.x & 63, cg = threadIdx.x >> 6;
   const bool live = cg * 8 < CS;  // DK 16: two waves of channels
-  const size_t sbase = ((size_t)u.sq * Br.nch + u.ch) * DK;
-  float aq[8], ak[8], iq[8], ik[8], bt[8];
-#pragma unroll
-  for (int v = 0; v < 8; ++v) aq[v] = ak[v] = iq[v] = ik[v] = 0.f;
-  // inter-chunk terms: do_t S_prev^T and v_t dS_end^T over d_v in 64-column steps
-  {
-    float* dos = sm;
-    float* vs = sm + 64 * 65;
-    float* sT = sm + 2 * 64 * 65;            // [64 e][32 c]
-    float* dsT = sm + 2 * 64 * 65 + 64 * 32;
-    for (int e0 = 0; e0 < P.dv; e0 += 64) {
-      stage<64, 64, 65, true, false>(dos, [&](int tt, int e) {
-        const bool ok = tt < nvalid;
-        const float v = Br.dob[((size_t)(u.b * Br.n + j0 + (ok ? tt : 0)) * Br.h + u.head) * P.dv + e0 + e];
-        return ok ? v : 0.f;
-      });
-      stage<64, 64, 65, false, false>(vs, [&](int tt, int e) {
-        const bool ok = tt < nvalid;
-        const float v = to_f32(reinterpret_cast<const T*>(Br.vT)[(((size_t)u.sq * Br.nch + u.ch) * P.dv + e0 + e) * P.C + (ok ? tt : 0)]);
-        return ok ? v : 0.f;
-      });
-      stage<CS, 64, 32, true, true>(sT, [&](int cc, int e) { return Br.Sst[(sbase + c0 + cc) * P.dv + e0 + e]; });
-      stage<CS, 64, 32, true, true>(dsT, [&](int cc, int e) { return Br.dSt[(sbase + c0 + cc) * P.dv + e0 + e]; });
-      __syncthreads();
-      if (live) {
-        for (int e = 0; e < 64; ++e) {
-          const float dv_ = dos[t * 65 + e], vv = vs[t * 65 + e];
-          const f32x4 s0 = *reinterpret_cast<const f32x4*>(sT + e * 32 + cg * 8);
-          const f32x4 s1 = *reinterpret_cast<const f32x4*>(sT + e * 32 + cg * 8 + 4);
-          const f32x4 g0 = *reinterpret_cast<const f32x4*>(dsT + e * 32 + cg * 8);
-          const f32x4 g1 = *reinterpret_cast<const f32x4*>(dsT + e * 32 + cg * 8 + 4);
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            aq[q] += dv_ * s0[q];
-            aq[q + 4] += dv_ * s1[q];
-            ak[q] += vv * g0[q];
-            ak[q + 4] += vv * g1[q];
-          }
-        }
-      }
-      __syncthreads();
-    }
-  }
-  // intra-chunk terms with e^{-|b_t - b_i|} (b is non-increasing along the chunk)
   float* ds = sm;                  // D[t][i], stride 65
   float* qs = sm + 64 * 65;        // q_scale q, stride 33
   float* ks = qs + 64 * 33;
   float* bs = ks + 64 * 33;
   const float* D = Br.AD + ((size_t)u.sq * Br.nch + u.ch) * 2 * 64 * 64 + 64 * 64;
-  stage<64, 64, 65, true, false>(ds, [&](int tt, int i) { return D[tt * 64 + i]; });
-  auto at_ = [&](int tt, int cc) { return (row0 + (tt < nvalid ? tt : 0)) * DK + c0 + cc; };
-  stage<64, CS, 33, true, false>(qs, [&](int tt, int cc) {
-    const float v = P.q_scale * Br.q[at_(tt, cc)];
-    return tt < nvalid ? v : 0.f;
-  });
-  stage<64, CS, 33, true, false>(ks, [&](int tt, int cc) {
-    const float v = Br.k[at_(tt, cc)];
-    return tt < nvalid ? v : 0.f;
-  });
-  // rows past the chunk keep its last b (the gate adds nothing past the call's end)
-  stage<64, CS, 33, true, false>(bs, [&](int tt, int cc) { return Br.lb[(row0 + min(tt, P.C - 1)) * DK + c0 + cc]; });
-  __syncthreads();
-  float blast[8];
+  const float* QK = Br.QKi + ((size_t)u.sq * Br.nch + u.ch) * 2 * 64 * DK;
+  {
+    // one round trip for the four tiles
+    auto at_ = [&](int tt, int cc) { return (row0 + (tt < nvalid ? tt : 0)) * DK + c0 + cc; };
+    float r0[16], r1[64 * CS / 256], r2[64 * CS / 256], r3[64 * CS / 256];
+    load_tile<64, 64, true>(r0, [&](int tt, int i) { return D[tt * 64 + i]; });
+    load_tile<64, CS, true>(r1, [&](int tt, int cc) {
+      const float v = P.q_scale * Br.q[at_(tt, cc)];
+      return tt < nvalid ? v : 0.f;
+    });
+    load_tile<64, CS, true>(r2, [&](int tt, int cc) {
+      const float v = Br.k[at_(tt, cc)];
+      return tt < nvalid ? v : 0.f;
+    });
+    // rows past the chunk keep its last b (the gate adds nothing past the call's end)
+    load_tile<64, CS, true>(r3, [&](int tt, int cc) { return Br.lb[(row0 + min(tt, P.C - 1)) * DK + c0 + cc]; });
+    store_tile<64, 64, 65, true, false>(ds, r0);
+    store_tile<64, CS, 33, true, false>(qs, r1);
+    store_tile<64, CS, 33, true, false>(ks, r2);
+    store_tile<64, CS, 33, true, false>(bs, r3);
+  }
+  float aq[8], ak[8], iq[8], ik[8], bt[8], blast[8];
+  const int cl = live ? cg * 8 : 0;
 #pragma unroll
   for (int v = 0; v < 8; ++v) {
-    const int cc = live ? cg * 8 + v : 0;
-    bt[v] = bs[t * 33 + cc];
-    blast[v] = bs[(P.C - 1) * 33 + cc];
+    aq[v] = QK[t * DK + c0 + cl + v];
+    ak[v] = QK[64 * DK + t * DK + c0 + cl + v];
+    iq[v] = ik[v] = 0.f;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int v = 0; v < 8; ++v) {
+    bt[v] = bs[t * 33 + cl + v];
+    blast[v] = bs[(P.C - 1) * 33 + cl + v];
   }
   if (live) {
     for (int i = 0; i < 64; ++i) {
@@ -806,6 +868,7 @@ static void launch_chunk_kernels_t(const BwdParams& P, int which, hipStream_t st
     case 0: hipLaunchKernelGGL((k_bwd_outer<T, DK, false>), dim3(P.total_units, slices), dim3(256), 0, st, P); break;
     case 1: hipLaunchKernelGGL((k_bwd_outer<T, DK, true>), dim3(P.total_units, slices), dim3(256), 0, st, P); break;
     case 2: hipLaunchKernelGGL((k_bwd_AD<T, DK>), dim3(P.total_units), dim3(256), 0, st, P); break;
+    case 5: hipLaunchKernelGGL((k_bwd_mm1<T, DK>), dim3(P.total_units), dim3(256), 0, st, P); break;
     case 3: hipLaunchKernelGGL((k_bwd_dv<T, DK>), dim3(P.total_units, slices), dim3(256), 0, st, P); break;
     default: {
       const int cs = DK < 32 ? 1 : DK / 32;
@@ -827,7 +890,8 @@ static hipError_t launch_chunk_kernels_dk(const BwdParams& P, int which, hipStre
   return hipGetLastError();
 }
 
-// which: 0 state increments, 1 state-gradient increments, 2 A and D, 3 dv, 4 dq and dk
+// which: 0 state increments, 1 state-gradient increments, 2 A, 3 dv, 4 dq and dk,
+// 5 the dense products do S^T, v dS^T and D
 hipError_t launch_bwd_chunk(const BwdParams& P, int which, bool bf16_path, hipStream_t st) {
   if (P.total_units == 0) return hipSuccess;
   return bf16_path ? launch_chunk_kernels_dk<bf16>(P, which, st) : launch_chunk_kernels_dk<float>(P, which, st);

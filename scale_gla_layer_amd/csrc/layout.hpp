@@ -252,7 +252,8 @@ struct K3Params {
 //   Sst, dSt    [B][h][nch][d_k][d_v]  fp32  state entering each chunk, and the
 //                                            loss gradient reaching each chunk's
 //                                            last state from later chunks
-//   AD          [B][h][nch][2][C][C]   fp32  A (decayed q k^T) and D (do v^T), t >= i
+//   AD          [B][h][nch][2][64][64] fp32  A (decayed q k^T) and D (do v^T), t >= i
+//   QKi         [B][h][nch][2][64][d_k] fp32 do S_prev^T and v dS_end^T of each chunk
 //   rsum, rtot  [B][h][np][d_k], [B][h][nch][d_k]  fp32  in-chunk suffix sums of
 //                                            q dq - k dk, and their chunk totals
 //   dob         [B n][h d_v]           fp32  dLoss/d(GLA output o)
@@ -281,6 +282,7 @@ struct BwdBranch {
   float* Sst;
   float* dSt;
   float* AD;
+  float* QKi;                 // [B][h][nch][2][64][d_k] do S^T and v dS^T of each chunk
   float* rsum;
   float* rtot;
   float* dob;
