@@ -261,6 +261,7 @@ msgla_status msgla_backward(const msgla_config* cfg, const void* packed, const v
     Br.vT = at<char>(workspace, wb.vT);
     Br.g = at<float>(workspace, wb.g);
     Br.y = at<char>(workspace, wb.y);
+    Br.A = at<char>(workspace, wb.A);
     Br.yc = bg.s > 1 ? at<char>(workspace, o.Yc) : nullptr;
     Br.W2 = at<float>(packed, bg.off_W2);
     Br.bg = at<float>(packed, bg.off_bg);
@@ -323,7 +324,6 @@ msgla_status msgla_backward(const msgla_config* cfg, const void* packed, const v
   for (int i = 0; i < g.m; ++i)
     HIP_TRY(launch_bwd_scan(P.br[i].dSt, P.br[i].lb, (int)B * P.br[i].h, P.br[i].nch, P.br[i].np, g.C, g.dk,
                             g.dv, true, st));
-  HIP_TRY(launch_bwd_chunk(P, 2, g.bf16, st));
   HIP_TRY(launch_bwd_chunk(P, 5, g.bf16, st));
   HIP_TRY(launch_bwd_chunk(P, 3, g.bf16, st));
   HIP_TRY(launch_bwd_chunk(P, 4, g.bf16, st));

@@ -16,7 +16,8 @@
 //    S_prev of every chunk by a forward scan of the chunks' k-hat^T V,
 //    dS_end (what the loss receives through a chunk's last state from later
 //    chunks) by a reverse scan of q-tilde^T dO            (k_bwd_outer, k_bwd_scan)
-//    A_ti = sum_c q_tc k_ic e^{b_tc - b_ic},  D_ti = do_t . v_i   (t >= i)   (k_bwd_AD)
+//    A_ti = sum_c q_tc k_ic e^{b_tc - b_ic} (the forward's), D_ti = do_t . v_i
+//    (t >= i)                                                            (k_bwd_mm1)
 //    dv_i = sum_{t>=i} A_ti do_t + (k_i * e^{b_last - b_i}) dS_end         (k_bwd_dv)
 //    dq_t = e^{b_t} * (do_t S_prev^T) + sum_{i<=t} D_ti k_i * e^{b_t - b_i}
 //    dk_i = e^{b_last - b_i} * (v_i dS_end^T) + sum_{t>=i} D_ti q_t * e^{b_t - b_i}
@@ -359,69 +360,11 @@ __global__ __launch_bounds__(256) void k_bwd_mm1(const BwdParams P) {
   }
 }
 
-// ---- A of a chunk, A_ti = sum_c q_tc k_ic e^{b_tc - b_ic} (t >= i, zero elsewhere) ----
-// thread: t = lane, i in 16 * wave .. 16 * wave + 15
-template <typename T, int DK>
-__global__ __launch_bounds__(256) void k_bwd_AD(const BwdParams P) {
-  __shared__ float sm[3 * 64 * 33];
-  const UnitPos u = unit_pos(P, blockIdx.x);
-  const BwdBranch& Br = P.br[u.bi];
-  const int j0 = u.ch * P.C;
-  const int nvalid = min(P.C, Br.n - j0);
-  const size_t row0 = (size_t)u.sq * Br.np + j0;
-  const int t = threadIdx.x & 63, ig = threadIdx.x >> 6;
-  float accA[16];
-#pragma unroll
-  for (int v = 0; v < 16; ++v) accA[v] = 0.f;
-  float* qs = sm;
-  float* ks = sm + 64 * 33;
-  float* bs = sm + 2 * 64 * 33;
-  constexpr int CW = DK < 32 ? DK : 32;
-  float rq[64 * CW / 256], rk[64 * CW / 256], rb[64 * CW / 256];
-  auto load_step = [&](int c0) {
-    auto at_ = [&](int tt, int cc) { return (row0 + (tt < nvalid ? tt : 0)) * DK + c0 + cc; };
-    load_tile<64, CW, true>(rq, [&](int tt, int cc) {
-      const float v = P.q_scale * Br.q[at_(tt, cc)];
-      return tt < nvalid ? v : 0.f;
-    });
-    load_tile<64, CW, true>(rk, [&](int tt, int cc) {
-      const float v = Br.k[at_(tt, cc)];
-      return tt < nvalid ? v : 0.f;
-    });
-    load_tile<64, CW, true>(rb, [&](int tt, int cc) {
-      const float v = Br.lb[at_(tt, cc)];
-      return tt < nvalid ? v : 0.f;
-    });
-  };
-  load_step(0);
-  for (int c0 = 0; c0 < DK; c0 += CW) {
-    store_tile<64, CW, 33, true, false>(qs, rq);
-    store_tile<64, CW, 33, true, false>(ks, rk);
-    store_tile<64, CW, 33, true, false>(bs, rb);
-    __syncthreads();
-    if (c0 + CW < DK) load_step(c0 + CW);
-    for (int cc = 0; cc < CW; ++cc) {
-      const float qv = qs[t * 33 + cc], bt = bs[t * 33 + cc];
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int i = ig * 16 + v;
-        accA[v] += qv * ks[i * 33 + cc] * __expf(fminf(bt - bs[i * 33 + cc], 0.f));
-      }
-    }
-    __syncthreads();
-  }
-  float* A = Br.AD + ((size_t)u.sq * Br.nch + u.ch) * 2 * 64 * 64;
-#pragma unroll
-  for (int v = 0; v < 16; ++v) {
-    const int i = ig * 16 + v;
-    A[t * 64 + i] = (i <= t && t < nvalid) ? accA[v] : 0.f;
-  }
-}
-
 // ---- dv_i = sum_{t>=i} A_ti do_t + k-hat_i dS_end, into the v columns of dP ----
 // On the matrix cores: rows i, columns e of the block's 64-column slice; wave w
-// takes rows 16 w .. 16 w + 15.  A^T and do^T are staged with positions along
-// k; then k-hat and dS_end^T in 32-channel steps.
+// takes rows 16 w .. 16 w + 15.  A is the forward's (K2a's, in the storage
+// type); A^T and do^T are staged with positions along k; then k-hat and
+// dS_end^T in 32-channel steps.
 template <typename T, int DK>
 __global__ __launch_bounds__(256) void k_bwd_dv(const BwdParams P) {
   constexpr int LD = 68, CW = DK < 32 ? DK : 32, LDC = CW + 4;
@@ -436,7 +379,7 @@ __global__ __launch_bounds__(256) void k_bwd_dv(const BwdParams P) {
   const size_t row0 = (size_t)u.sq * Br.np + j0;
   const size_t sbase = ((size_t)u.sq * Br.nch + u.ch) * DK;
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
-  const float* A = Br.AD + ((size_t)u.sq * Br.nch + u.ch) * 2 * 64 * 64;
+  const T* A = reinterpret_cast<const T*>(Br.A) + ((size_t)u.sq * Br.nch + u.ch) * P.C * P.C;
   float rk[64 * CW / 256], rd[CW * 64 / 256];
   auto load_step = [&](int c0) {
     load_tile<64, CW, true>(rk, [&](int tt, int cc) {
@@ -449,7 +392,12 @@ __global__ __launch_bounds__(256) void k_bwd_dv(const BwdParams P) {
   };
   {
     float ra[16], rt[16];
-    load_tile<64, 64, true>(ra, [&](int tt, int i) { return A[tt * 64 + i]; });
+    // rows past the call's end hold no position (and no defined A): zero
+    load_tile<64, 64, true>(ra, [&](int tt, int i) {
+      const bool ok = tt < nvalid && i < P.C;
+      const float v = to_f32(A[(ok ? tt : 0) * P.C + (ok ? i : 0)]);
+      return ok ? v : 0.f;
+    });
     load_tile<64, 64, true>(rt, [&](int tt, int e) {
       const bool ok = tt < nvalid;
       const float v = Br.dob[((size_t)(u.b * Br.n + j0 + (ok ? tt : 0)) * Br.h + u.head) * P.dv + e0 + e];
@@ -867,7 +815,6 @@ static void launch_chunk_kernels_t(const BwdParams& P, int which, hipStream_t st
   switch (which) {
     case 0: hipLaunchKernelGGL((k_bwd_outer<T, DK, false>), dim3(P.total_units, slices), dim3(256), 0, st, P); break;
     case 1: hipLaunchKernelGGL((k_bwd_outer<T, DK, true>), dim3(P.total_units, slices), dim3(256), 0, st, P); break;
-    case 2: hipLaunchKernelGGL((k_bwd_AD<T, DK>), dim3(P.total_units), dim3(256), 0, st, P); break;
     case 5: hipLaunchKernelGGL((k_bwd_mm1<T, DK>), dim3(P.total_units), dim3(256), 0, st, P); break;
     case 3: hipLaunchKernelGGL((k_bwd_dv<T, DK>), dim3(P.total_units, slices), dim3(256), 0, st, P); break;
     default: {
@@ -890,7 +837,7 @@ static hipError_t launch_chunk_kernels_dk(const BwdParams& P, int which, hipStre
   return hipGetLastError();
 }
 
-// which: 0 state increments, 1 state-gradient increments, 2 A, 3 dv, 4 dq and dk,
+// which: 0 state increments, 1 state-gradient increments, 3 dv, 4 dq and dk,
 // 5 the dense products do S^T, v dS^T and D
 hipError_t launch_bwd_chunk(const BwdParams& P, int which, bool bf16_path, hipStream_t st) {
   if (P.total_units == 0) return hipSuccess;

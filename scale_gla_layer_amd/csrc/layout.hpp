@@ -252,7 +252,7 @@ struct K3Params {
 //   Sst, dSt    [B][h][nch][d_k][d_v]  fp32  state entering each chunk, and the
 //                                            loss gradient reaching each chunk's
 //                                            last state from later chunks
-//   AD          [B][h][nch][2][64][64] fp32  A (decayed q k^T) and D (do v^T), t >= i
+//   AD          [B][h][nch][2][64][64] fp32  D (do v^T, t >= i) in the second half
 //   QKi         [B][h][nch][2][64][d_k] fp32 do S_prev^T and v dS_end^T of each chunk
 //   rsum, rtot  [B][h][np][d_k], [B][h][nch][d_k]  fp32  in-chunk suffix sums of
 //                                            q dq - k dk, and their chunk totals
@@ -273,6 +273,7 @@ struct BwdBranch {
   const void* vT;
   const float* g;             // x W_g1 at every unpooled position [B L][rp]
   const void* y;              // GLA outputs [B][h][np][d_v]
+  const void* A;              // the forward's decayed q k^T per chunk [B][h][nch][C][C] (T)
   const void* yc;             // coarse outputs [B n][d] (s > 1)
   const float* W2;            // packed gate factor [rp][h d_k] and bias [h d_k]
   const float* bg;
