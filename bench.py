@@ -683,6 +683,20 @@ def summarize_profiles(d: str, workload: str = "main"):
     f_fac, w_fac = COPY_CAL_BYTES / ref_f, COPY_CAL_BYTES / ref_w
     fetch = _counter_means(os.path.join(d, "pmc_fetch", "main_counter_collection.csv"))
     write = _counter_means(os.path.join(d, "pmc_write", "main_counter_collection.csv"))
+    # the kernels' source hashes as the counted runs printed them (their logs,
+    # <d>/fetch.log and <d>/write.log): a record is only as current as the code
+    # it was counted on
+    run_hashes = {}
+    for name in ("fetch", "write"):
+        try:
+            with open(os.path.join(d, f"{name}.log"), encoding="utf-8") as f:
+                for ln in f:
+                    if "[bench] kernel source hashes:" in ln:
+                        h = json.loads(ln.split("kernel source hashes:", 1)[1])
+                        run_hashes = h if name == "fetch" else (run_hashes if run_hashes == h else {})
+        except OSError:
+            run_hashes = {}
+            break
     rows = ["# HBM traffic per dispatch, workload " + workload, "",
             "Commands (from the repository root):", ""] + [f"    {cmds[k]}" for k in
                                                         ("fetch", "write", "cal_fetch", "cal_write")]
@@ -700,7 +714,7 @@ def summarize_profiles(d: str, workload: str = "main"):
         alg_txt = f"{amount / 1e6:.1f} MB" if bound == "hbm" else f"{amount / 1e9:.1f} GFLOP"
         ratio = f"{hbm / amount:.2f}" if bound == "hbm" and amount else "-"
         rows.append(f"| {kernel} | {fk:.0f} | {wk:.0f} | {hbm / 1e6:.1f} | {alg_txt} | {ratio} |")
-        rec = {"kernel": kernel, "workload": workload, "source_hash": kernel_source_hash(kernel),
+        rec = {"kernel": kernel, "workload": workload, "source_hash": run_hashes.get(kernel, "unknown"),
                "fetch_kib_per_dispatch": fk, "write_kib_per_dispatch": wk,
                "fetch_factor": f_fac, "write_factor": w_fac, "hbm_bytes_per_dispatch": round(hbm),
                "dispatches": fetch[kernel][1], "commands": [cmds[k] for k in
