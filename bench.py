@@ -534,6 +534,24 @@ def cpu_decode_baseline(workload: str = "sweep_1248", steps: int = 64):
             "tokens_per_s": round(wl.batch / (us * 1e-6), 1)}
 
 
+def cpu_training_baseline(workload: str = "main"):
+    """The oracle's forward and backward (its vector-Jacobian product) of one
+    sequence of the workload in one process (part of the CPU baseline leg)."""
+    import numpy as np
+    from oracle import msgla_oracle as orc
+    from scale_gla_layer_amd.config import WORKLOADS
+    from scale_gla_layer_amd.synth import make_inputs
+    wl = WORKLOADS[workload]
+    X, W = make_inputs(wl.cfg, 1, wl.seq_len, seed=0)
+    dO = np.random.default_rng(1).normal(0.0, 1.0, X.shape)
+    t0 = time.perf_counter()
+    orc.layer_forward(X, W, wl.cfg)
+    orc.layer_backward(X, W, wl.cfg, dO)
+    s = time.perf_counter() - t0
+    return {"workload": workload, "sample": f"one sequence of {wl.seq_len} tokens, forward + backward, "
+            "one process", "seconds": round(s, 2), "tokens_per_s": round(wl.seq_len / s, 1)}
+
+
 def cpu_baseline(workload: str, min_s: float = 10.0):
     """The oracle as it stands, on the host's cores: one single-threaded
     process per core (BLAS limited to one thread), each cycling over the
@@ -996,6 +1014,10 @@ def main():
         log("[bench] timing the fp64 CPU oracle on the host ...")
         cpu = cpu_baseline(wl.name)
         log(f"[bench] oracle {cpu['value']:.0f} tokens/s ({cpu['sample']})")
+        if training is not None:
+            cpu["training"] = cpu_training_baseline(wl.name)
+            log(f"[bench] oracle forward + backward {cpu['training']['tokens_per_s']} tokens/s "
+                f"({cpu['training']['sample']})")
         if dec is not None:
             cpu["decode"] = cpu_decode_baseline(dec["workload"])
             log(f"[bench] oracle decode step {cpu['decode']['us_per_step']} us (B={cpu['decode']['batch']}, "
