@@ -33,7 +33,7 @@ Readings where the notes leave a step open (all listed in the design doc):
 The layer backward (layer_backward and its parts, for training: the notes'
 Sec. 3.4 training paragraph and Sec. 5.5, Table 4) is the vector-Jacobian
 product of layer_forward written out by the chain rule, token by token, from
-a fresh state and without a mask.
+a fresh state, with or without a token mask.
 
 Parity: every function here is pinned by tests under tests/ against values
 the notes print (the s=4 hold table, the first pooled input), closed forms,
@@ -441,16 +441,17 @@ def causal_hold_backward(dH: np.ndarray, s: int, n: int) -> np.ndarray:
     return dY
 
 
-def branch_backward(X: np.ndarray, bw, s: int, cfg, dY: np.ndarray):
-    """VJP of branch_forward (no mask, zero initial state).
+def branch_backward(X: np.ndarray, bw, s: int, cfg, dY: np.ndarray, M: Optional[np.ndarray] = None):
+    """VJP of branch_forward (zero initial state).
 
-    dY: [B, n_s, d], the gradient of the branch's coarse outputs.  Returns
-    (dX [B, L, d], grads) with grads holding W_q, W_k, W_v, W_g1, W_g2, b_g,
-    W_o (and g_norm when the configuration normalises), shaped as the weights.
+    dY: [B, n_s, d], the gradient of the branch's coarse outputs; M: the
+    optional [B, L] token mask of Eq. (8).  Returns (dX [B, L, d], grads) with
+    grads holding W_q, W_k, W_v, W_g1, W_g2, b_g, W_o (and g_norm when the
+    configuration normalises), shaped as the weights.
     """
     X = np.asarray(X, dtype=np.float64)
     B, L, d = X.shape
-    xp = pool_complete_blocks(X, s)
+    xp = pool_complete_blocks(X, s) if M is None else pool_eq8(X, s, M)[:, : L // s]
     n = xp.shape[1]
     h = bw.W_q.shape[1] // cfg.d_k
     q, k, v, la = branch_projections(xp, bw, cfg)
@@ -484,18 +485,28 @@ def branch_backward(X: np.ndarray, bw, s: int, cfg, dY: np.ndarray):
     grads["W_v"] = xf.T @ dv.reshape(B * n, hdv)
     grads["W_g1"] = xf.T @ dg1.reshape(B * n, r)
     dxp = dq @ bw.W_q.T + dk @ bw.W_k.T + dv @ bw.W_v.T + dg1 @ bw.W_g1.T
-    # xp_j = mean of the s positions of complete block j
     dX = np.zeros((B, L, d))
-    for j in range(s):
-        if n > 0:
-            dX[:, j: n * s: s, :] += dxp / s
+    if M is None:
+        # xp_j = mean of the s positions of complete block j
+        for j in range(s):
+            if n > 0:
+                dX[:, j: n * s: s, :] += dxp / s
+    else:
+        # xp_j = sum_t M_t x_t / max(1, sum_t M_t) over the block's positions t
+        Mf = (np.asarray(M) != 0).astype(np.float64).reshape(B, L)
+        for b in range(B):
+            for j in range(n):
+                cnt = max(1.0, Mf[b, j * s: (j + 1) * s].sum())
+                for t in range(j * s, (j + 1) * s):
+                    dX[b, t] += Mf[b, t] * dxp[b, j] / cnt
     return dX, grads
 
 
-def layer_backward(X: np.ndarray, W, cfg, dO: np.ndarray):
-    """VJP of layer_forward (fresh state, no mask): dO [B, L, d] ->
-    (dX [B, L, d], grads) with grads["branches"][i] as branch_backward's and
-    grads["W_f"], grads["b_f"] for the fusion logits (zero when m == 1).
+def layer_backward(X: np.ndarray, W, cfg, dO: np.ndarray, M: Optional[np.ndarray] = None):
+    """VJP of layer_forward (fresh state; M the optional token mask of Eq. (8),
+    which enters the pooling only): dO [B, L, d] -> (dX [B, L, d], grads) with
+    grads["branches"][i] as branch_backward's and grads["W_f"], grads["b_f"]
+    for the fusion logits (zero when m == 1).
 
     O_t = sum_i w_{t,i} H^(i)_t with H^(i) the held coarse outputs and
     w_t = softmax(z_t), z_t = x_t W_f + b_f:
@@ -511,11 +522,11 @@ def layer_backward(X: np.ndarray, W, cfg, dO: np.ndarray):
     dw = np.zeros((B, L, m))
     grads = {"branches": []}
     for i, (s, bw) in enumerate(zip(cfg.scales, W.branches)):
-        Y, _, n = branch_forward(X, bw, s, cfg)
+        Y, _, n = branch_forward(X, bw, s, cfg, M)
         H = causal_hold(Y, s, L)
         dw[:, :, i] = np.sum(dO * H, axis=-1)
         dY = causal_hold_backward(w[:, :, i: i + 1] * dO, s, n)
-        dXi, gi = branch_backward(X, bw, s, cfg, dY)
+        dXi, gi = branch_backward(X, bw, s, cfg, dY, M)
         dX += dXi
         grads["branches"].append(gi)
     if m > 1:

@@ -104,6 +104,26 @@ def test_backward_matches_finite_differences(norm, scales, heads, L):
         _check(name, _grad_of(grads, i, key), _fd(f, arr))
 
 
+@pytest.mark.parametrize("scales,heads,L", [((1, 2, 3), (1, 2, 1), 11), ((2, 4), (1, 1), 13)])
+def test_masked_backward_matches_finite_differences(scales, heads, L):
+    """Eq. (8) with a token mask: holes anywhere, a fully masked block, a block
+    with one token; the mask enters the pooling only."""
+    cfg = _config(False, scales, heads)
+    rng = np.random.default_rng(31 + L)
+    B = 2
+    X = rng.normal(0, 1, (B, L, cfg.d_model))
+    W = _weights(cfg, rng)
+    dO = rng.normal(0, 1, (B, L, cfg.d_model))
+    M = (rng.random((B, L)) > 0.3).astype(np.uint8)
+    M[0, 4:8] = 0   # a whole padded block at s = 2 and s = 4
+    M[1, 0:3] = 0   # one token left in the first block of s = 4
+    dX, grads = orc.layer_backward(X, W, cfg, dO, M=M)
+    f = lambda: float(np.sum(dO * orc.layer_forward(X, W, cfg, M=M)))
+    _check("dX", dX, _fd(f, X))
+    for name, i, key, arr in _all_params(W, cfg):
+        _check(name, _grad_of(grads, i, key), _fd(f, arr))
+
+
 def test_gla_backward_matches_finite_differences_with_strong_decay():
     """The recurrence alone, gates from alpha ~ 1 to alpha ~ 1e-3, 9 steps."""
     rng = np.random.default_rng(3)
