@@ -303,9 +303,10 @@ msgla_status msgla_decode_step(const msgla_config* cfg, const void* packed, cons
  * chunkwise-parallel algorithm (Sec. 3.4, training paragraph) and compare
  * training throughput with single-scale GLA (Sec. 5.5, Table 4); what training
  * needs from the layer is its vector-Jacobian product.  For the forward of x
- * from a fresh state without a mask (what msgla_forward computes with state_in
- * and mask NULL), given dout = dLoss/dO, msgla_backward writes dx = dLoss/dx and
- * the gradient of the loss with respect to every weight.
+ * from a fresh state (what msgla_forward computes with state_in NULL and the
+ * same mask: NULL, or the [B][L] token mask of Eq. (8), which enters the
+ * pooling only), given dout = dLoss/dO, msgla_backward writes dx = dLoss/dx
+ * and the gradient of the loss with respect to every weight.
  *
  * Gradients are fp32, laid out as the weights of msgla_weights are, [in][out]
  * row-major, and are overwritten (not accumulated):
@@ -346,9 +347,9 @@ typedef struct {
 size_t msgla_backward_workspace_bytes(const msgla_config* cfg, int64_t B, int64_t L);
 
 msgla_status msgla_backward(const msgla_config* cfg, const void* packed, const void* x,
-                            const void* dout, int64_t B, int64_t L, void* dx,
-                            const msgla_grads* grads, void* workspace, size_t workspace_bytes,
-                            void* stream);
+                            const void* dout, const uint8_t* mask, int64_t B, int64_t L,
+                            void* dx, const msgla_grads* grads, void* workspace,
+                            size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

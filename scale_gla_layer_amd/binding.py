@@ -114,8 +114,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "msgla_state_query": (ctypes.c_int, [vp, ctypes.POINTER(CStateInfo), vp]),
         "msgla_forward_noalloc": (ctypes.c_int, [cfgp, vp, vp, vp, i64, i64, vp, vp, vp, vp]),
         "msgla_backward_workspace_bytes": (sz, [cfgp, i64, i64]),
-        "msgla_backward": (ctypes.c_int, [cfgp, vp, vp, vp, i64, i64, vp, ctypes.POINTER(CGrads), vp,
-                                          sz, vp]),
+        "msgla_backward": (ctypes.c_int, [cfgp, vp, vp, vp, vp, i64, i64, vp, ctypes.POINTER(CGrads),
+                                          vp, sz, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -247,16 +247,17 @@ def msgla_backward_workspace_bytes(cfg: MsglaConfig, B: int, L: int) -> int:
 
 
 def msgla_backward(cfg: MsglaConfig, packed, x, dout, B: int, L: int, dx, branch_grads: Sequence[dict],
-                   W_f, b_f, workspace, stream=None):
+                   W_f, b_f, workspace, mask=None, stream=None):
     """branch_grads: per branch a dict of fp32 device tensors W_q, W_k, W_v, W_g1, W_g2, b_g, W_o
-    (written, in the layout of the weights); W_f, b_f: fp32 device tensors (None when m == 1)."""
+    (written, in the layout of the weights); W_f, b_f: fp32 device tensors (None when m == 1);
+    mask: the forward's [B, L] uint8 token mask, or None."""
     g = CGrads()
     for i, br in enumerate(branch_grads):
         for name in ("W_q", "W_k", "W_v", "W_g1", "W_g2", "b_g", "W_o"):
             setattr(g.br[i], name, _ptr(br.get(name)))
     g.W_f, g.b_f = _ptr(W_f), _ptr(b_f)
-    st = load_library().msgla_backward(ctypes.byref(c_config(cfg)), _ptr(packed), _ptr(x), _ptr(dout), B, L,
-                                       _ptr(dx), ctypes.byref(g), _ptr(workspace),
+    st = load_library().msgla_backward(ctypes.byref(c_config(cfg)), _ptr(packed), _ptr(x), _ptr(dout),
+                                       _ptr(mask), B, L, _ptr(dx), ctypes.byref(g), _ptr(workspace),
                                        workspace.numel() * workspace.element_size(), _stream(stream))
     _check("msgla_backward", st)
 

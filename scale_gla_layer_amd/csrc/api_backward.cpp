@@ -22,6 +22,7 @@ hipError_t launch_bwd_dg1(const BwdParams& P, int bi, bool bf16_path, hipStream_
 hipError_t launch_bwd_out(const BwdParams& P, bool bf16_path, hipStream_t st);
 hipError_t launch_bwd_hold(const BwdParams& P, int bi, bool bf16_path, hipStream_t st);
 hipError_t launch_bwd_dx(const BwdParams& P, bool bf16_path, hipStream_t st);
+hipError_t launch_bwd_mask_rows(const BwdParams& P, int bi, bool bf16_path, hipStream_t st);
 hipError_t launch_bwd_colsum(const float* src, int rows, int cols, int ld, float* partial, int nrb,
                              float* out, int out_stride, hipStream_t st);
 hipError_t launch_bwd_wf_partial(const BwdParams& P, float* partial, int nrb, bool bf16_path, hipStream_t st);
@@ -183,8 +184,8 @@ size_t msgla_backward_workspace_bytes(const msgla_config* cfg, int64_t B, int64_
 }
 
 msgla_status msgla_backward(const msgla_config* cfg, const void* packed, const void* x, const void* dout,
-                            int64_t B, int64_t L, void* dx, const msgla_grads* grads, void* workspace,
-                            size_t workspace_bytes, void* stream) {
+                            const uint8_t* mask, int64_t B, int64_t L, void* dx, const msgla_grads* grads,
+                            void* workspace, size_t workspace_bytes, void* stream) {
   if (msgla_status st = check_config(cfg); st != MSGLA_OK) return st;
   if (!bwd_supported(cfg)) return MSGLA_ERR_UNSUPPORTED;
   if (!batch_ok(B, L)) return MSGLA_ERR_INVALID_ARG;
@@ -207,7 +208,7 @@ msgla_status msgla_backward(const msgla_config* cfg, const void* packed, const v
   FwdHooks hooks{};
   for (int i = 0; i < g.m; ++i)
     if (g.br[i].s > 1) hooks.yc[i] = at<char>(workspace, G.br[i].Yc);
-  if (msgla_status s = forward_impl(cfg, packed, x, nullptr, B, L, nullptr, nullptr, nullptr, workspace,
+  if (msgla_status s = forward_impl(cfg, packed, x, mask, B, L, nullptr, nullptr, nullptr, workspace,
                                     workspace_bytes, stream, nullptr, &hooks);
       s != MSGLA_OK)
     return s;
@@ -231,6 +232,7 @@ msgla_status msgla_backward(const msgla_config* cfg, const void* packed, const v
   P.nbranch = g.m;
   P.fine = -1;
   P.x = x;
+  P.mask = mask;
   P.dout = dout;
   P.dx = dx;
   P.w = at<float>(workspace, W.w);
@@ -355,6 +357,7 @@ msgla_status msgla_backward(const msgla_config* cfg, const void* packed, const v
       HIP_TRY(fill_zero(gr.W_g1, (size_t)g.d * g.r * 4, st));
       continue;
     }
+    if (bg.s == 1 && mask) HIP_TRY(launch_bwd_mask_rows(P, i, g.bf16, st));
     const char* dP = static_cast<const char*>(Br.dP);
     const void* xp = bg.s == 1 ? x : static_cast<const void*>(at<char>(workspace, W.br[i].xp));
     BLAS_TRY(gemm_rm(hb, false, false, rows, g.d, bg.col_g + g.r, dP, ST, Br.NP, at<char>(packed, bg.off_Wp), ST,

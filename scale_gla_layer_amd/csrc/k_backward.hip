@@ -160,9 +160,21 @@ __global__ __launch_bounds__(256) void k_bwd_gate(const BwdParams P) {
     const int j = j0 + jj;
     float acc = 0.f;
     if (j < Br.n) {
-      const float* gp = Br.g + ((size_t)u.b * P.L + (size_t)j * Br.s) * P.rp + rr;
-      for (int v = 0; v < Br.s; ++v) acc += gp[(size_t)v * P.rp];
-      acc /= (float)Br.s;
+      // the block mean of x W_g1 (Eq. (8): over the block's tokens when masked)
+      const size_t t0 = (size_t)u.b * P.L + (size_t)j * Br.s;
+      const float* gp = Br.g + t0 * P.rp + rr;
+      if (P.mask) {
+        int cnt = 0;
+        for (int v = 0; v < Br.s; ++v) {
+          const bool tok = P.mask[t0 + v] != 0;
+          acc += tok ? gp[(size_t)v * P.rp] : 0.f;
+          cnt += tok ? 1 : 0;
+        }
+        acc /= (float)max(cnt, 1);
+      } else {
+        for (int v = 0; v < Br.s; ++v) acc += gp[(size_t)v * P.rp];
+        acc /= (float)Br.s;
+      }
       if (u.head == 0) Br.g1c[((size_t)u.b * Br.n + j) * P.rp + rr] = acc;
     }
     g1s[jj * P.r + rr] = acc;
@@ -706,12 +718,21 @@ __global__ __launch_bounds__(256) void k_bwd_dx(const BwdParams P) {
     const size_t pos = idx / pd;
     const int col = (int)(idx - pos * pd) * 8;
     const int b = (int)(pos / P.L), t = (int)(pos - (size_t)b * P.L);
+    const uint8_t* Mrow = P.mask ? P.mask + (size_t)b * P.L : nullptr;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     for (int i = 0; i < P.nbranch; ++i) {
       const BwdBranch& Br = P.br[i];
       if (t >= Br.n * Br.s) continue;
-      const float* src = Br.dxp + ((size_t)b * Br.n + t / Br.s) * P.d + col;
-      const float inv = 1.f / (float)Br.s;
+      const int j = t / Br.s;
+      const float* src = Br.dxp + ((size_t)b * Br.n + j) * P.d + col;
+      // Eq. (8): the block mean is sum M x / max(1, sum M)
+      float inv = 1.f / (float)Br.s;
+      if (Mrow) {
+        if (!Mrow[t]) continue;
+        int cnt = 0;
+        for (int v = j * Br.s; v < (j + 1) * Br.s; ++v) cnt += Mrow[v] != 0;
+        inv = 1.f / (float)max(cnt, 1);
+      }
       const f32x4 a = *reinterpret_cast<const f32x4*>(src);
       const f32x4 c = *reinterpret_cast<const f32x4*>(src + 4);
 #pragma unroll
@@ -730,6 +751,22 @@ __global__ __launch_bounds__(256) void k_bwd_dx(const BwdParams P) {
       }
     }
     store8<T>(reinterpret_cast<T*>(P.dx) + pos * P.d + col, acc);
+  }
+}
+
+// ---- a masked call's scale-1 branch: its pooled input is M_t x_t, so the rows
+// of dP at masked positions carry nothing to x or to the weights: zero them ----
+template <typename T>
+__global__ __launch_bounds__(256) void k_bwd_mask_rows(const BwdParams P, int bi) {
+  const BwdBranch& Br = P.br[bi];
+  const int pieces = Br.NP / 8;
+  const size_t total = (size_t)P.B * P.L * pieces;
+  for (size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+       idx += (size_t)gridDim.x * blockDim.x) {
+    const size_t row = idx / pieces;
+    if (P.mask[row]) continue;
+    const float z[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    store8<T>(reinterpret_cast<T*>(Br.dP) + row * Br.NP + (idx - row * pieces) * 8, z);
   }
 }
 
@@ -895,6 +932,15 @@ hipError_t launch_bwd_hold(const BwdParams& P, int bi, bool bf16_path, hipStream
   const unsigned grid = (unsigned)std::min<size_t>((total + 255) / 256, 65536);
   if (bf16_path) hipLaunchKernelGGL(k_bwd_hold<bf16>, dim3(grid), dim3(256), 0, st, P, bi);
   else hipLaunchKernelGGL(k_bwd_hold<float>, dim3(grid), dim3(256), 0, st, P, bi);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_mask_rows(const BwdParams& P, int bi, bool bf16_path, hipStream_t st) {
+  const size_t total = (size_t)P.B * P.L * (P.br[bi].NP / 8);
+  if (total == 0 || !P.mask) return hipSuccess;
+  const unsigned grid = (unsigned)std::min<size_t>((total + 255) / 256, 65536);
+  if (bf16_path) hipLaunchKernelGGL(k_bwd_mask_rows<bf16>, dim3(grid), dim3(256), 0, st, P, bi);
+  else hipLaunchKernelGGL(k_bwd_mask_rows<float>, dim3(grid), dim3(256), 0, st, P, bi);
   return hipGetLastError();
 }
 

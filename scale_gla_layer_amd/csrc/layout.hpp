@@ -300,6 +300,7 @@ struct BwdParams {
   int nbranch, total_units;
   int fine;                   // branch with scale 1, or -1
   const void* x;              // [B][L][d] T
+  const uint8_t* mask;        // [B][L] token mask of the forward, or null
   const void* dout;           // [B][L][d] T
   void* dx;                   // [B][L][d] T
   const float* w;             // fusion weights [B L][8]

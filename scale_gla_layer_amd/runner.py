@@ -109,8 +109,9 @@ class DeviceLayer:
         m = len(c.scales)
         return brs, (z(d, m) if m > 1 else None), (z(m) if m > 1 else None)
 
-    def backward(self, x, dout, dx=None, grads=None):
-        """Layer backward of a fresh-state forward of x: returns (dx, (branch grads, dW_f, db_f))."""
+    def backward(self, x, dout, dx=None, grads=None, mask=None):
+        """Layer backward of a fresh-state forward of x (with the forward's token mask, if
+        any): returns (dx, (branch grads, dW_f, db_f))."""
         B, L, _ = x.shape
         n = binding.msgla_backward_workspace_bytes(self.cfg, B, L)
         if n == 0:
@@ -122,7 +123,7 @@ class DeviceLayer:
         if grads is None:
             grads = self.new_grads()
         binding.msgla_backward(self.cfg, self.packed, x, dout, B, L, dx, grads[0], grads[1], grads[2],
-                               self.bwd_workspace, self.stream)
+                               self.bwd_workspace, mask=mask, stream=self.stream)
         return dx, grads
 
     def state_init(self, state, B: int):

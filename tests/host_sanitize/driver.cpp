@@ -179,18 +179,18 @@ int main() {
       gr.br[i] = msgla_branch_grads{p, p, p, p, p, p, p};
     }
     gr.W_f = gr.b_f = reinterpret_cast<float*>(f);
-    EXPECT(msgla_backward(&c, f, f, nullptr, 2, 64, f, &gr, f, bws, nullptr) == MSGLA_ERR_INVALID_ARG);
-    EXPECT(msgla_backward(&c, f, f, f, 2, 64, f + 4, &gr, f, bws, nullptr) == MSGLA_ERR_INVALID_ARG);
-    EXPECT(msgla_backward(&c, f, f, f, 2, 64, f, nullptr, f, bws, nullptr) == MSGLA_ERR_INVALID_ARG);
-    EXPECT(msgla_backward(&c, f, f, f, INT64_MAX, 64, f, &gr, f, bws, nullptr) == MSGLA_ERR_INVALID_ARG);
-    EXPECT(msgla_backward(&c, f, f, f, 2, 64, f, &gr, f, bws - 1, nullptr) == MSGLA_ERR_WORKSPACE);
-    EXPECT(msgla_backward(nullptr, f, f, f, 2, 64, f, &gr, f, bws, nullptr) != MSGLA_OK);
+    EXPECT(msgla_backward(&c, f, f, nullptr, nullptr, 2, 64, f, &gr, f, bws, nullptr) == MSGLA_ERR_INVALID_ARG);
+    EXPECT(msgla_backward(&c, f, f, f, nullptr, 2, 64, f + 4, &gr, f, bws, nullptr) == MSGLA_ERR_INVALID_ARG);
+    EXPECT(msgla_backward(&c, f, f, f, nullptr, 2, 64, f, nullptr, f, bws, nullptr) == MSGLA_ERR_INVALID_ARG);
+    EXPECT(msgla_backward(&c, f, f, f, nullptr, INT64_MAX, 64, f, &gr, f, bws, nullptr) == MSGLA_ERR_INVALID_ARG);
+    EXPECT(msgla_backward(&c, f, f, f, nullptr, 2, 64, f, &gr, f, bws - 1, nullptr) == MSGLA_ERR_WORKSPACE);
+    EXPECT(msgla_backward(nullptr, f, f, f, nullptr, 2, 64, f, &gr, f, bws, nullptr) != MSGLA_OK);
     gr.br[2].W_g2 = nullptr;
-    EXPECT(msgla_backward(&c, f, f, f, 2, 64, f, &gr, f, bws, nullptr) == MSGLA_ERR_INVALID_ARG);
+    EXPECT(msgla_backward(&c, f, f, f, nullptr, 2, 64, f, &gr, f, bws, nullptr) == MSGLA_ERR_INVALID_ARG);
     msgla_config cn = c;
     cn.norm = 1;
     EXPECT(msgla_backward_workspace_bytes(&cn, 2, 64) == 0);
-    EXPECT(msgla_backward(&cn, f, f, f, 2, 64, f, &gr, f, bws, nullptr) == MSGLA_ERR_UNSUPPORTED);
+    EXPECT(msgla_backward(&cn, f, f, f, nullptr, 2, 64, f, &gr, f, bws, nullptr) == MSGLA_ERR_UNSUPPORTED);
   }
 
   std::printf("configurations %d, failures %d\n", n, failures);

@@ -209,22 +209,23 @@ def test_backward_argument_errors_need_no_gpu():
             setattr(g.br[i], name, fake)
     g.W_f = g.b_f = fake
     f = lib.msgla_backward
-    ok = (ctypes.byref(cc), fake, fake, fake, 2, 64, fake, ctypes.byref(g), fake, ws, None)
+    cfgp = ctypes.byref(cc)
+    gp = ctypes.byref(g)
     # NULL dout, misaligned dx, bad sizes, workspace too small
-    assert f(ok[0], fake, fake, None, 2, 64, fake, ok[7], fake, ws, None) == 1
-    assert f(ok[0], fake, fake, fake, 2, 64, fake + 4, ok[7], fake, ws, None) == 1
-    assert f(ok[0], fake, fake, fake, 0, 64, fake, ok[7], fake, ws, None) == 1
-    assert f(ok[0], fake, fake, fake, 2, 64, fake, ok[7], fake, ws - 1, None) == 3
+    assert f(cfgp, fake, fake, None, None, 2, 64, fake, gp, fake, ws, None) == 1
+    assert f(cfgp, fake, fake, fake, None, 2, 64, fake + 4, gp, fake, ws, None) == 1
+    assert f(cfgp, fake, fake, fake, None, 0, 64, fake, gp, fake, ws, None) == 1
+    assert f(cfgp, fake, fake, fake, None, 2, 64, fake, gp, fake, ws - 1, None) == 3
     # a missing gradient pointer; a missing fusion gradient with several branches
     g2 = binding.CGrads()
     ctypes.memmove(ctypes.byref(g2), ctypes.byref(g), ctypes.sizeof(g))
     g2.br[1].W_o = None
-    assert f(ok[0], fake, fake, fake, 2, 64, fake, ctypes.byref(g2), fake, ws, None) == 1
+    assert f(cfgp, fake, fake, fake, None, 2, 64, fake, ctypes.byref(g2), fake, ws, None) == 1
     g2.br[1].W_o = fake
     g2.b_f = None
-    assert f(ok[0], fake, fake, fake, 2, 64, fake, ctypes.byref(g2), fake, ws, None) == 1
+    assert f(cfgp, fake, fake, fake, None, 2, 64, fake, ctypes.byref(g2), fake, ws, None) == 1
     # the normalisation has no backward: unsupported, and no workspace size
     nc = _raw_cfg()
     nc.norm = 1
     assert lib.msgla_backward_workspace_bytes(ctypes.byref(nc), 2, 64) == 0
-    assert f(ctypes.byref(nc), fake, fake, fake, 2, 64, fake, ok[7], fake, ws, None) == 2
+    assert f(ctypes.byref(nc), fake, fake, fake, None, 2, 64, fake, gp, fake, ws, None) == 2
