@@ -320,8 +320,10 @@ msgla_status msgla_decode_step(const msgla_config* cfg, const void* packed, cons
  * storage type, accumulating in fp32.  The plain products run on rocBLAS;
  * everything specific to the layer (the hold and fusion, the chunkwise
  * recurrence, the gate, the pooling) runs in the library's kernels.
- * The per-branch normalisation (config norm = 1) has no backward yet:
- * MSGLA_ERR_UNSUPPORTED.  Pointers are device memory, 16-byte aligned.
+ * With the per-branch normalisation (config norm = 1) the gains' gradient is
+ * written too (norm_g required).  d_v must be a multiple of 64
+ * (MSGLA_ERR_UNSUPPORTED otherwise: fp32 configurations with d_v 32 or 96).
+ * Pointers are device memory, 16-byte aligned.
  * Asynchronous on `stream`; the library's rocBLAS handle for the device is
  * created on the first call (not under graph capture), and calls from several
  * host threads are serialised by the library.
@@ -334,6 +336,7 @@ typedef struct {
   float* W_g2;
   float* b_g;
   float* W_o;
+  float* norm_g; /* [h d_v] gradient of the normalisation gains (config norm = 1), else unused */
 } msgla_branch_grads;
 
 typedef struct {
@@ -343,7 +346,8 @@ typedef struct {
 } msgla_grads;
 
 /* Device workspace needed by msgla_backward for batch B and length L (bytes);
- * 0 for an invalid configuration or size. */
+ * 0 for an invalid configuration or size, or one msgla_backward does not
+ * support. */
 size_t msgla_backward_workspace_bytes(const msgla_config* cfg, int64_t B, int64_t L);
 
 msgla_status msgla_backward(const msgla_config* cfg, const void* packed, const void* x,

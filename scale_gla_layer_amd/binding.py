@@ -66,7 +66,8 @@ class CWeights(ctypes.Structure):
 
 
 class CBranchGrads(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_void_p) for n in ("W_q", "W_k", "W_v", "W_g1", "W_g2", "b_g", "W_o")]
+    _fields_ = [(n, ctypes.c_void_p) for n in ("W_q", "W_k", "W_v", "W_g1", "W_g2", "b_g", "W_o",
+                                               "norm_g")]
 
 
 class CGrads(ctypes.Structure):
@@ -249,11 +250,12 @@ def msgla_backward_workspace_bytes(cfg: MsglaConfig, B: int, L: int) -> int:
 def msgla_backward(cfg: MsglaConfig, packed, x, dout, B: int, L: int, dx, branch_grads: Sequence[dict],
                    W_f, b_f, workspace, mask=None, stream=None):
     """branch_grads: per branch a dict of fp32 device tensors W_q, W_k, W_v, W_g1, W_g2, b_g, W_o
-    (written, in the layout of the weights); W_f, b_f: fp32 device tensors (None when m == 1);
+    and, for configurations with the normalisation, norm_g (written, in the layout of the
+    weights); W_f, b_f: fp32 device tensors (None when m == 1);
     mask: the forward's [B, L] uint8 token mask, or None."""
     g = CGrads()
     for i, br in enumerate(branch_grads):
-        for name in ("W_q", "W_k", "W_v", "W_g1", "W_g2", "b_g", "W_o"):
+        for name in ("W_q", "W_k", "W_v", "W_g1", "W_g2", "b_g", "W_o", "norm_g"):
             setattr(g.br[i], name, _ptr(br.get(name)))
     g.W_f, g.b_f = _ptr(W_f), _ptr(b_f)
     st = load_library().msgla_backward(ctypes.byref(c_config(cfg)), _ptr(packed), _ptr(x), _ptr(dout),

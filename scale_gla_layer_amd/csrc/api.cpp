@@ -323,7 +323,7 @@ msgla_status msgla::host::forward_impl(const msgla_config* cfg, const void* pack
   int ctiles = 0;
   for (int i = 0; i < g.m; ++i) {
     K3Branch& k = p3.br[i];
-    k.y = at<char>(workspace, W.br[i].y);
+    k.y = (hooks && hooks->yn[i]) ? static_cast<const void*>(hooks->yn[i]) : at<char>(workspace, W.br[i].y);
     k.s = g.br[i].s;
     k.h = g.br[i].h;
     k.np = W.br[i].np;
@@ -412,6 +412,7 @@ msgla_status msgla::host::forward_impl(const msgla_config* cfg, const void* pack
       if (W.br[i].n == 0) continue;
       NormBranch& nb = pn.br[pn.nbranch++];
       nb.y = at<char>(workspace, W.br[i].y);
+      nb.yo = hooks ? hooks->yn[i] : nullptr;
       nb.g = at<float>(packed, g.br[i].off_gn);
       nb.h = g.br[i].h;
       nb.n = W.br[i].n;

@@ -23,6 +23,7 @@ hipError_t launch_bwd_out(const BwdParams& P, bool bf16_path, hipStream_t st);
 hipError_t launch_bwd_hold(const BwdParams& P, int bi, bool bf16_path, hipStream_t st);
 hipError_t launch_bwd_dx(const BwdParams& P, bool bf16_path, hipStream_t st);
 hipError_t launch_bwd_mask_rows(const BwdParams& P, int bi, bool bf16_path, hipStream_t st);
+hipError_t launch_bwd_norm(const BwdParams& P, int bi, bool bf16_path, hipStream_t st);
 hipError_t launch_bwd_colsum(const float* src, int rows, int cols, int ld, float* partial, int nrb,
                              float* out, int out_stride, hipStream_t st);
 hipError_t launch_bwd_wf_partial(const BwdParams& P, float* partial, int nrb, bool bf16_path, hipStream_t st);
@@ -43,7 +44,7 @@ constexpr int BWD_SPLIT_MAX = 16; // K slices of a weight-gradient product
 int colsum_blocks(int rows) { return std::max(1, std::min(BWD_NRB_MAX, (rows + 127) / 128)); }
 
 struct BwdBranchGeom {
-  size_t lb, sg, g1c, Sst, dSt, AD, QKi, rsum, rtot, dob, dzg, dP, dY, Yc, ycat, dxp;
+  size_t lb, sg, g1c, Sst, dSt, AD, QKi, rsum, rtot, dob, dzg, dP, dY, Yc, ycat, dxp, yn, ngt;
   int NP;
 };
 
@@ -53,7 +54,7 @@ struct BwdGeom {
   size_t dz, partial, splitk, splitk_floats, total;
 };
 
-bool bwd_supported(const msgla_config* cfg) { return cfg->norm == 0 && cfg->d_v % 64 == 0; }
+bool bwd_supported(const msgla_config* cfg) { return cfg->d_v % 64 == 0; }
 
 BwdGeom bwd_geom(const PackGeom& g, int64_t B, int64_t L) {
   BwdGeom G{};
@@ -91,7 +92,12 @@ BwdGeom bwd_geom(const PackGeom& g, int64_t B, int64_t L) {
     }
     o.ycat = take(prow * bg.h * g.dv * g.es);
     o.dxp = take(prow * g.d * 4);
+    if (g.norm) {
+      o.yn = take(rows * g.dv * g.es);         // normalised rows, laid out as y
+      o.ngt = take(prow * bg.h * g.dv * 4);    // per-row terms of the gains' gradient
+    }
     red = std::max(red, (size_t)bg.h * g.dk);
+    if (g.norm) red = std::max(red, (size_t)bg.h * g.dv);
     mn = std::max({mn, (size_t)g.d * (bg.col_g + g.r), (size_t)bg.h * g.dv * g.d, (size_t)g.r * bg.h * g.dk});
   }
   G.dz = take((size_t)B * L * FUSION_STRIDE * 4);
@@ -196,6 +202,7 @@ msgla_status msgla_backward(const msgla_config* cfg, const void* packed, const v
   for (int i = 0; i < g.m; ++i) {
     const msgla_branch_grads& b = grads->br[i];
     if (!b.W_q || !b.W_k || !b.W_v || !b.W_g1 || !b.W_g2 || !b.b_g || !b.W_o) return MSGLA_ERR_INVALID_ARG;
+    if (g.norm && !b.norm_g) return MSGLA_ERR_INVALID_ARG;
   }
   if (g.m > 1 && (!grads->W_f || !grads->b_f)) return MSGLA_ERR_INVALID_ARG;
   const BwdGeom G = bwd_geom(g, B, L);
@@ -206,8 +213,10 @@ msgla_status msgla_backward(const msgla_config* cfg, const void* packed, const v
 
   // forward intermediates (q, k, v^T, x W_g1, y, fusion weights, block means, Y)
   FwdHooks hooks{};
-  for (int i = 0; i < g.m; ++i)
+  for (int i = 0; i < g.m; ++i) {
     if (g.br[i].s > 1) hooks.yc[i] = at<char>(workspace, G.br[i].Yc);
+    if (g.norm) hooks.yn[i] = at<char>(workspace, G.br[i].yn);
+  }
   if (msgla_status s = forward_impl(cfg, packed, x, mask, B, L, nullptr, nullptr, nullptr, workspace,
                                     workspace_bytes, stream, nullptr, &hooks);
       s != MSGLA_OK)
@@ -263,6 +272,9 @@ msgla_status msgla_backward(const msgla_config* cfg, const void* packed, const v
     Br.vT = at<char>(workspace, wb.vT);
     Br.g = at<float>(workspace, wb.g);
     Br.y = at<char>(workspace, wb.y);
+    Br.yv = g.norm ? at<char>(workspace, o.yn) : Br.y;
+    Br.gn = g.norm ? at<float>(packed, bg.off_gn) : nullptr;
+    Br.ngt = g.norm ? at<float>(workspace, o.ngt) : nullptr;
     Br.A = at<char>(workspace, wb.A);
     Br.yc = bg.s > 1 ? at<char>(workspace, o.Yc) : nullptr;
     Br.W2 = at<float>(packed, bg.off_W2);
@@ -315,6 +327,19 @@ msgla_status msgla_backward(const msgla_config* cfg, const void* packed, const v
     BLAS_TRY(gemm_wgrad(hb, hdv, g.d, rows, Br.ycat, ST, hdv, dYi, ST, g.d, one_dst(grads->br[i].W_o, g.d), sk,
                         G.splitk_floats, g.es, st));
   }
+
+  // ---- the normalisation: dLoss/d(normalised rows) -> dLoss/do, and the gains' gradient ----
+  if (g.norm)
+    for (int i = 0; i < g.m; ++i) {
+      const BwdBranch& Br = P.br[i];
+      const int hdv = Br.h * g.dv, rows = (int)B * Br.n;
+      if (Br.n == 0) {
+        HIP_TRY(fill_zero(grads->br[i].norm_g, (size_t)hdv * 4, st));
+        continue;
+      }
+      HIP_TRY(launch_bwd_norm(P, i, g.bf16, st));
+      HIP_TRY(launch_bwd_colsum(Br.ngt, rows, hdv, hdv, partial, colsum_blocks(rows), grads->br[i].norm_g, 1, st));
+    }
 
   // ---- the chunkwise recurrence and the gate ----
   HIP_TRY(launch_bwd_gate(P, st));

@@ -631,7 +631,7 @@ __global__ __launch_bounds__(256) void k_bwd_out(const BwdParams P) {
       for (int p = lane * 8; p < hdv; p += 64 * 8) {
         const int hh = p / P.dv, e = p - hh * P.dv;
         float y8[8], g8[8];
-        load8<T>(reinterpret_cast<const T*>(Br.y) + (((size_t)b * Br.h + hh) * Br.np + t) * P.dv + e, y8);
+        load8<T>(reinterpret_cast<const T*>(Br.yv) + (((size_t)b * Br.h + hh) * Br.np + t) * P.dv + e, y8);
         const f32x4 ga = *reinterpret_cast<const f32x4*>(G + p);
         const f32x4 gb = *reinterpret_cast<const f32x4*>(G + p + 4);
 #pragma unroll
@@ -700,7 +700,7 @@ __global__ __launch_bounds__(256) void k_bwd_hold(const BwdParams P, int bi) {
       const int row = (int)(k / py), p = (int)(k - (size_t)row * py) * 8;
       const int b = row / Br.n, j = row - b * Br.n;
       const int hh = p / P.dv, e = p - hh * P.dv;
-      const T* src = reinterpret_cast<const T*>(Br.y) + (((size_t)b * Br.h + hh) * Br.np + j) * P.dv + e;
+      const T* src = reinterpret_cast<const T*>(Br.yv) + (((size_t)b * Br.h + hh) * Br.np + j) * P.dv + e;
       T* dst = reinterpret_cast<T*>(Br.ycat) + (size_t)row * Br.h * P.dv + p;
       st16(dst, ld16(src));
       if constexpr (sizeof(T) == 4) st16(dst + 4, ld16(src + 4));
@@ -751,6 +751,38 @@ __global__ __launch_bounds__(256) void k_bwd_dx(const BwdParams P) {
       }
     }
     store8<T>(reinterpret_cast<T*>(P.dx) + pos * P.d + col, acc);
+  }
+}
+
+// ---- the normalisation (config norm): dLoss/do from dLoss/d(normalised row) ----
+// y = o g / r per head row, r = sqrt(mean o^2 + eps):
+//   do_c = g_c dy_c / r - o_c (sum_c' g_c' dy_c' o_c') / (d_v r^3),
+// written over dy in place; o_c dy_c / r goes to ngt for the gains' gradient.
+// One wave per (pooled position, head).
+template <typename T>
+__global__ __launch_bounds__(256) void k_bwd_norm(const BwdParams P, int bi) {
+  const BwdBranch& Br = P.br[bi];
+  const int rh = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (rh >= P.B * Br.n * Br.h) return;
+  const int row = rh / Br.h, hh = rh - row * Br.h;
+  const int b = row / Br.n, j = row - b * Br.n;
+  const T* o = reinterpret_cast<const T*>(Br.y) + (((size_t)b * Br.h + hh) * Br.np + j) * P.dv;
+  float* dy = Br.dob + (size_t)rh * P.dv;
+  const float* g = Br.gn + hh * P.dv;
+  float ss = 0.f, inner = 0.f;
+  for (int c = lane; c < P.dv; c += 64) {
+    const float oc = to_f32(o[c]);
+    ss += oc * oc;
+    inner += g[c] * dy[c] * oc;
+  }
+  ss = wave_sum(ss);
+  inner = wave_sum(inner);
+  const float r = sqrtf(ss / (float)P.dv + NORM_EPS);
+  const float ir = 1.f / r, k3 = inner / ((float)P.dv * r * r * r);
+  for (int c = lane; c < P.dv; c += 64) {
+    const float oc = to_f32(o[c]), dyc = dy[c];
+    dy[c] = g[c] * dyc * ir - oc * k3;
+    Br.ngt[(size_t)rh * P.dv + c] = oc * dyc * ir;
   }
 }
 
@@ -941,6 +973,15 @@ hipError_t launch_bwd_mask_rows(const BwdParams& P, int bi, bool bf16_path, hipS
   const unsigned grid = (unsigned)std::min<size_t>((total + 255) / 256, 65536);
   if (bf16_path) hipLaunchKernelGGL(k_bwd_mask_rows<bf16>, dim3(grid), dim3(256), 0, st, P, bi);
   else hipLaunchKernelGGL(k_bwd_mask_rows<float>, dim3(grid), dim3(256), 0, st, P, bi);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_norm(const BwdParams& P, int bi, bool bf16_path, hipStream_t st) {
+  const int n = P.B * P.br[bi].n * P.br[bi].h;
+  if (n == 0) return hipSuccess;
+  const dim3 grid((n + 3) / 4);
+  if (bf16_path) hipLaunchKernelGGL(k_bwd_norm<bf16>, grid, dim3(256), 0, st, P, bi);
+  else hipLaunchKernelGGL(k_bwd_norm<float>, grid, dim3(256), 0, st, P, bi);
   return hipGetLastError();
 }
 

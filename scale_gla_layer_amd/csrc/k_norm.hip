@@ -3,9 +3,10 @@
 // normalisation without giving its form; the form taken is
 //   y_c <- y_c / sqrt(mean_c' y_c'^2 + eps) * g_c   over the d_v channels of a head,
 // with fp32 gains g per branch and eps = 1e-6.  Rows (b, head, j) of a
-// branch's y [B][h][np][d_v] are normalised in place, between the chunk-state kernel
-// that writes y and the output projections that read it.  HBM-bound: reads and
-// writes y once.
+// branch's y [B][h][np][d_v] are normalised in place (or into a second buffer of
+// the same layout, for the backward's recompute), between the chunk-state
+// kernel that writes y and the output projections that read it.  HBM-bound:
+// reads and writes y once.
 #include "device_common.hpp"
 #include "layout.hpp"
 
@@ -24,6 +25,7 @@ __global__ __launch_bounds__(256) void k_norm_rows(const NormParams P) {
   if (row0 >= P.total_rows) return;  // the same for the whole wave
   const int pieces = P.dv / PER;     // 16-byte pieces of a row: at most LPR * PPL
   T* yr[NORM_NR];
+  T* yw[NORM_NR];
   const float* gr[NORM_NR];
   bool ok[NORM_NR];
 #pragma unroll
@@ -37,6 +39,7 @@ __global__ __launch_bounds__(256) void k_norm_rows(const NormParams P) {
     const int local = row - Br.row_begin;
     const int bh = local / Br.n, j = local - bh * Br.n;
     yr[u] = reinterpret_cast<T*>(Br.y) + ((size_t)bh * Br.np + j) * P.dv;
+    yw[u] = reinterpret_cast<T*>(Br.yo ? Br.yo : Br.y) + ((size_t)bh * Br.np + j) * P.dv;
     gr[u] = Br.g + (bh % Br.h) * P.dv;
   }
   u32x4 raw[NORM_NR][PPL];
@@ -71,7 +74,7 @@ __global__ __launch_bounds__(256) void k_norm_rows(const NormParams P) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) f[e + i] = v[k][e + i] * rs * g4[i];
         }
-        st16(yr[u] + pc * PER, pack16<T>(f));
+        st16(yw[u] + pc * PER, pack16<T>(f));
       }
     }
   }

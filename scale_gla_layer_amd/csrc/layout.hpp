@@ -273,6 +273,9 @@ struct BwdBranch {
   const void* vT;
   const float* g;             // x W_g1 at every unpooled position [B L][rp]
   const void* y;              // GLA outputs [B][h][np][d_v]
+  const void* yv;             // the rows the output projection read: y, or y normalised
+  const float* gn;            // normalisation gains [h d_v] (config norm), or null
+  float* ngt;                 // per-row terms of the gains' gradient [B n][h d_v], or null
   const void* A;              // the forward's decayed q k^T per chunk [B][h][nch][C][C] (T)
   const void* yc;             // coarse outputs [B n][d] (s > 1)
   const float* W2;            // packed gate factor [rp][h d_k] and bias [h d_k]
@@ -392,6 +395,7 @@ constexpr float NORM_EPS = 1e-6f;
 
 struct NormBranch {
   void* y;          // [B][h][np][dv] storage type, normalised in place
+  void* yo;         // or, when set, written here (same layout) and y kept
   const float* g;   // gains [h dv] fp32
   int h, n, np;     // heads, rows per (b, head), padded row stride
   int row_begin;    // first flattened row (b, head, j) of this branch

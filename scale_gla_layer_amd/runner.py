@@ -106,6 +106,9 @@ class DeviceLayer:
         z = lambda *shape: torch.empty(shape, dtype=torch.float32, device=self.device)
         brs = [{"W_q": z(d, h * dk), "W_k": z(d, h * dk), "W_v": z(d, h * dv), "W_g1": z(d, r),
                 "W_g2": z(r, h * dk), "b_g": z(h * dk), "W_o": z(h * dv, d)} for h in c.heads]
+        if c.norm:
+            for br, h in zip(brs, c.heads):
+                br["norm_g"] = z(h * dv)
         m = len(c.scales)
         return brs, (z(d, m) if m > 1 else None), (z(m) if m > 1 else None)
 

@@ -187,10 +187,12 @@ int main() {
     EXPECT(msgla_backward(nullptr, f, f, f, nullptr, 2, 64, f, &gr, f, bws, nullptr) != MSGLA_OK);
     gr.br[2].W_g2 = nullptr;
     EXPECT(msgla_backward(&c, f, f, f, nullptr, 2, 64, f, &gr, f, bws, nullptr) == MSGLA_ERR_INVALID_ARG);
+    gr.br[2].W_g2 = reinterpret_cast<float*>(f);
     msgla_config cn = c;
     cn.norm = 1;
-    EXPECT(msgla_backward_workspace_bytes(&cn, 2, 64) == 0);
-    EXPECT(msgla_backward(&cn, f, f, f, nullptr, 2, 64, f, &gr, f, bws, nullptr) == MSGLA_ERR_UNSUPPORTED);
+    const size_t bwn = msgla_backward_workspace_bytes(&cn, 2, 64);
+    EXPECT(bwn > bws);
+    EXPECT(msgla_backward(&cn, f, f, f, nullptr, 2, 64, f, &gr, f, bwn, nullptr) == MSGLA_ERR_INVALID_ARG);
   }
 
   std::printf("configurations %d, failures %d\n", n, failures);

@@ -224,8 +224,14 @@ def test_backward_argument_errors_need_no_gpu():
     g2.br[1].W_o = fake
     g2.b_f = None
     assert f(cfgp, fake, fake, fake, None, 2, 64, fake, ctypes.byref(g2), fake, ws, None) == 1
-    # the normalisation has no backward: unsupported, and no workspace size
+    # with the normalisation the gains' gradient is required
     nc = _raw_cfg()
     nc.norm = 1
-    assert lib.msgla_backward_workspace_bytes(ctypes.byref(nc), 2, 64) == 0
-    assert f(ctypes.byref(nc), fake, fake, fake, None, 2, 64, fake, gp, fake, ws, None) == 2
+    assert lib.msgla_backward_workspace_bytes(ctypes.byref(nc), 2, 64) > ws
+    wsn = lib.msgla_backward_workspace_bytes(ctypes.byref(nc), 2, 64)
+    assert f(ctypes.byref(nc), fake, fake, fake, None, 2, 64, fake, gp, fake, wsn, None) == 1
+    # d_v not a multiple of 64 (an fp32 configuration): unsupported, no workspace size
+    odd = _raw_cfg(dtype="f32", d_v=96)
+    assert lib.msgla_validate_config(ctypes.byref(odd)) == 0
+    assert lib.msgla_backward_workspace_bytes(ctypes.byref(odd), 2, 64) == 0
+    assert f(ctypes.byref(odd), fake, fake, fake, None, 2, 64, fake, gp, fake, ws, None) == 2

@@ -83,10 +83,10 @@ def backward_case(cfg, B, L, seed=0, gate_bias=None, tol=None, M=None):
     assert np.all(np.isfinite(dX)), "non-finite dx"
     errs["dx"] = dx_error(dX, dX_ref, X, W, cfg, dO, M)
     for i, g in enumerate(gb):
-        for key in KEYS:
+        for key in KEYS + (("norm_g",) if cfg.norm else ()):
             got = from_device(g[key])
             assert np.all(np.isfinite(got)), f"non-finite br{i}.{key}"
-            errs[f"br{i}.{key}"] = _tensor_err(got, ref["branches"][i][key])
+            errs[f"br{i}.{key}"] = _tensor_err(got, ref["branches"][i]["g_norm" if key == "norm_g" else key])
     if cfg.n_branches > 1:
         errs["W_f"] = _tensor_err(from_device(gWf), ref["W_f"])
         errs["b_f"] = _tensor_err(from_device(gbf), ref["b_f"])
@@ -155,6 +155,17 @@ def test_fp32_masked(scales, heads):
 def test_bf16_main_dimensions_masked():
     B, L = 2, 320
     backward_case(WORKLOADS["main"].cfg, B=B, L=L, seed=31, M=make_mask(B, L, seed=31, hole_prob=0.1))
+
+
+def test_fp32_normalised():
+    """The per-head RMS normalisation before W_o, with its gains' gradient."""
+    backward_case(_cfg(norm=True, scales=(1, 2, 3), heads=(1, 2, 1)), B=2, L=101, seed=37)
+
+
+def test_bf16_main_dimensions_normalised_and_masked():
+    B, L = 2, 200
+    cfg = dataclasses.replace(WORKLOADS["main"].cfg, norm=True)
+    backward_case(cfg, B=B, L=L, seed=41, M=make_mask(B, L, seed=41, hole_prob=0.1))
 
 
 def test_bf16_full_size_main_workload():
