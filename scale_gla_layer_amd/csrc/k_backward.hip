@@ -155,33 +155,59 @@ __global__ __launch_bounds__(256) void k_bwd_gate(const BwdParams P) {
   const BwdBranch& Br = P.br[u.bi];
   const int j0 = u.ch * P.C;
   const int hdk = Br.h * P.dk;
-  for (int idx = threadIdx.x; idx < P.C * P.r; idx += blockDim.x) {
-    const int jj = idx / P.r, rr = idx - jj * P.r;
-    const int j = j0 + jj;
-    float acc = 0.f;
-    if (j < Br.n) {
-      // the block mean of x W_g1 (Eq. (8): over the block's tokens when masked)
-      const size_t t0 = (size_t)u.b * P.L + (size_t)j * Br.s;
-      const float* gp = Br.g + t0 * P.rp + rr;
-      if (P.mask) {
-        int cnt = 0;
-        for (int v = 0; v < Br.s; ++v) {
-          const bool tok = P.mask[t0 + v] != 0;
-          acc += tok ? gp[(size_t)v * P.rp] : 0.f;
-          cnt += tok ? 1 : 0;
+  // the block means of x W_g1 (Eq. (8): over the block's tokens when masked);
+  // four entries per thread and round, their rows' loads issued together
+  for (int base = 0; base < P.C * P.r; base += 4 * 256) {
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    int cnt[4] = {0, 0, 0, 0};
+    for (int v0 = 0; v0 < Br.s; v0 += 4) {
+      float gv[4][4];
+      bool tok[4][4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int idx = min(base + threadIdx.x + 256 * k, P.C * P.r - 1);
+        const int jj = idx / P.r, rr = idx - jj * P.r;
+        const int j = min(j0 + jj, Br.n - 1);
+        const size_t t0 = (size_t)u.b * P.L + (size_t)j * Br.s;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int v = min(v0 + q, Br.s - 1);
+          gv[k][q] = Br.g[(t0 + v) * P.rp + rr];
+          tok[k][q] = v0 + q < Br.s && (!P.mask || P.mask[t0 + v] != 0);
         }
-        acc /= (float)max(cnt, 1);
-      } else {
-        for (int v = 0; v < Br.s; ++v) acc += gp[(size_t)v * P.rp];
-        acc /= (float)Br.s;
       }
-      if (u.head == 0) Br.g1c[((size_t)u.b * Br.n + j) * P.rp + rr] = acc;
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          acc[k] += tok[k][q] ? gv[k][q] : 0.f;
+          cnt[k] += tok[k][q] ? 1 : 0;
+        }
     }
-    g1s[jj * P.r + rr] = acc;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int idx = base + threadIdx.x + 256 * k;
+      if (idx >= P.C * P.r) continue;
+      const int jj = idx / P.r, rr = idx - jj * P.r;
+      const int j = j0 + jj;
+      const float mean = j < Br.n ? acc[k] / (float)(P.mask ? max(cnt[k], 1) : Br.s) : 0.f;
+      if (j < Br.n && u.head == 0) Br.g1c[((size_t)u.b * Br.n + j) * P.rp + rr] = mean;
+      g1s[jj * P.r + rr] = mean;
+    }
   }
-  for (int idx = threadIdx.x; idx < P.r * P.dk; idx += blockDim.x) {
-    const int rr = idx / P.dk, c = idx - rr * P.dk;
-    w2s[rr * P.dk + c] = Br.W2[(size_t)rr * hdk + u.head * P.dk + c];
+  for (int base = 0; base < P.r * P.dk; base += 8 * 256) {
+    float wv[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int idx = min(base + threadIdx.x + 256 * k, P.r * P.dk - 1);
+      const int rr = idx / P.dk, c = idx - rr * P.dk;
+      wv[k] = Br.W2[(size_t)rr * hdk + u.head * P.dk + c];
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int idx = base + threadIdx.x + 256 * k;
+      if (idx < P.r * P.dk) w2s[idx] = wv[k];
+    }
   }
   __syncthreads();
   // thread = (channel, part): the chunk's positions are cut into 256 / d_k
