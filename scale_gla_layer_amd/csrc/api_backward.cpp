@@ -15,17 +15,14 @@
 namespace msgla {
 hipError_t launch_bwd_gate(const BwdParams& P, hipStream_t st);
 hipError_t launch_bwd_chunk(const BwdParams& P, int which, bool bf16_path, hipStream_t st);
-hipError_t launch_bwd_scan(float* buf, const float* lb, int seqs, int nch, int np, int C, int dk, int dv,
-                           bool rev, hipStream_t st);
-hipError_t launch_bwd_dzg(const BwdParams& P, int bi, hipStream_t st);
-hipError_t launch_bwd_dg1(const BwdParams& P, int bi, bool bf16_path, hipStream_t st);
+hipError_t launch_bwd_scan(const BwdParams& P, bool rev, hipStream_t st);
+hipError_t launch_bwd_gate_grads(const BwdParams& P, bool bf16_path, hipStream_t st);
 hipError_t launch_bwd_out(const BwdParams& P, bool bf16_path, hipStream_t st);
 hipError_t launch_bwd_hold(const BwdParams& P, int bi, bool bf16_path, hipStream_t st);
 hipError_t launch_bwd_dx(const BwdParams& P, bool bf16_path, hipStream_t st);
 hipError_t launch_bwd_mask_rows(const BwdParams& P, int bi, bool bf16_path, hipStream_t st);
 hipError_t launch_bwd_norm(const BwdParams& P, int bi, bool bf16_path, hipStream_t st);
-hipError_t launch_bwd_colsum(const float* src, int rows, int cols, int ld, float* partial, int nrb,
-                             float* out, int out_stride, hipStream_t st);
+hipError_t launch_bwd_mcolsum(const ColsumJobs& J, float* part, hipStream_t st);
 hipError_t launch_bwd_wf_partial(const BwdParams& P, float* partial, int nrb, bool bf16_path, hipStream_t st);
 hipError_t launch_bwd_wf_finish(const float* partial, int nrb, int d, int m, float* out, hipStream_t st);
 hipError_t launch_bwd_splitk_reduce(const float* part, int S, int M, int N, const SplitDst& D, hipStream_t st);
@@ -44,14 +41,14 @@ constexpr int BWD_SPLIT_MAX = 16; // K slices of a weight-gradient product
 int colsum_blocks(int rows) { return std::max(1, std::min(BWD_NRB_MAX, (rows + 127) / 128)); }
 
 struct BwdBranchGeom {
-  size_t lb, sg, g1c, Sst, dSt, AD, QKi, rsum, rtot, dob, dzg, dP, dY, Yc, ycat, dxp, yn, ngt;
+  size_t lb, sg, g1c, Sst, dSt, AD, QKi, rsum, rtot, dob, gpart, dP, dY, Yc, ycat, dxp, yn, ngt;
   int NP;
 };
 
 struct BwdGeom {
   WsGeom W;
   BwdBranchGeom br[MSGLA_MAX_BRANCHES];
-  size_t dz, partial, splitk, splitk_floats, total;
+  size_t dz, partial, mcol, mcol_floats, splitk, splitk_floats, total;
 };
 
 bool bwd_supported(const msgla_config* cfg) { return cfg->d_v % 64 == 0; }
@@ -65,7 +62,7 @@ BwdGeom bwd_geom(const PackGeom& g, int64_t B, int64_t L) {
     cur += align256(bytes);
     return o;
   };
-  size_t red = 0, mn = 0;
+  size_t gate_cols = 0, norm_cols = 0, mn = 0;
   for (int i = 0; i < g.m; ++i) {
     const BranchGeom& bg = g.br[i];
     const WsBranch& w = G.W.br[i];
@@ -78,12 +75,12 @@ BwdGeom bwd_geom(const PackGeom& g, int64_t B, int64_t L) {
     o.g1c = take(prow * g.rp * 4);
     o.Sst = take(chunks * g.dk * g.dv * 4);
     o.dSt = take(chunks * g.dk * g.dv * 4);
-    o.AD = take(chunks * 2 * 64 * 64 * 4);
+    o.AD = take(chunks * 64 * 64 * 4);
     o.QKi = take(chunks * 2 * 64 * g.dk * 4);
     o.rsum = take(rows * g.dk * 4);
     o.rtot = take(chunks * g.dk * 4);
     o.dob = take(prow * bg.h * g.dv * 4);
-    o.dzg = take(prow * bg.h * g.dk * 4);
+    o.gpart = take((size_t)B * w.nch * 2 * (g.r + 1) * bg.h * g.dk * 4);
     o.NP = bg.col_g + g.rp;
     o.dP = take(prow * o.NP * g.es);
     if (bg.s > 1) {
@@ -96,13 +93,15 @@ BwdGeom bwd_geom(const PackGeom& g, int64_t B, int64_t L) {
       o.yn = take(rows * g.dv * g.es);         // normalised rows, laid out as y
       o.ngt = take(prow * bg.h * g.dv * 4);    // per-row terms of the gains' gradient
     }
-    red = std::max(red, (size_t)bg.h * g.dk);
-    if (g.norm) red = std::max(red, (size_t)bg.h * g.dv);
-    mn = std::max({mn, (size_t)g.d * (bg.col_g + g.r), (size_t)bg.h * g.dv * g.d, (size_t)g.r * bg.h * g.dk});
+    gate_cols += (size_t)(g.r + 1) * bg.h * g.dk;
+    norm_cols += (size_t)bg.h * g.dv;
+    mn = std::max({mn, (size_t)g.d * (bg.col_g + g.r), (size_t)bg.h * g.dv * g.d});
   }
   G.dz = take((size_t)B * L * FUSION_STRIDE * 4);
-  G.partial = take(std::max((size_t)BWD_NRB_MAX * std::max<size_t>(red, FUSION_STRIDE),
-                            (size_t)BWD_WF_NRB * g.d * FUSION_STRIDE) * 4);
+  G.partial = take((size_t)BWD_WF_NRB * g.d * FUSION_STRIDE * 4);
+  // column-sum partials: the gate's dW_g2 and db_g with db_f, or the gains' gradients
+  G.mcol_floats = (size_t)BWD_NRB_MAX * std::max(gate_cols + g.m, norm_cols);
+  G.mcol = take(G.mcol_floats * 4);
   G.splitk_floats = (size_t)BWD_SPLIT_MAX * mn;
   G.splitk = take(G.splitk_floats * 4);
   G.total = cur;
@@ -153,6 +152,24 @@ bool gemm_wgrad(rocblas_handle h, int M, int N, int K, const void* A, rocblas_da
                                       rocblas_gemm_algo_standard, 0, 0) != rocblas_status_success)
     return false;
   return direct || launch_bwd_splitk_reduce(part, S, M, N, dst, st) == hipSuccess;
+}
+
+// Appends a column sum of src [rows][cols] (row stride ld) into dst[cols].
+bool add_colsum(ColsumJobs& J, size_t& used, size_t cap, const float* src, int rows, int cols, int ld,
+                float* dst) {
+  if (J.n >= ColsumJobs::MAX) return false;
+  const int j = J.n++;
+  J.src[j] = src;
+  J.dst[j] = dst;
+  J.rows[j] = rows;
+  J.cols[j] = cols;
+  J.ld[j] = ld;
+  J.nrb[j] = colsum_blocks(rows);
+  J.pofs[j] = used;
+  used += (size_t)J.nrb[j] * cols;
+  J.cb[j + 1] = J.cb[j] + (cols + 63) / 64;
+  J.fb[j + 1] = J.fb[j] + (cols + 255) / 256;
+  return used <= cap;
 }
 
 SplitDst one_dst(float* p, int n) {
@@ -250,7 +267,7 @@ msgla_status msgla_backward(const msgla_config* cfg, const void* packed, const v
                                                           (size_t)g.br[g.carrier].col_z * g.d * g.es)
                                    : at<char>(packed, g.off_Wz))
                  : nullptr;
-  int units = 0;
+  int units = 0, gunits = 0;
   for (int i = 0; i < g.m; ++i) {
     const BranchGeom& bg = g.br[i];
     const WsBranch& wb = W.br[i];
@@ -263,6 +280,8 @@ msgla_status msgla_backward(const msgla_config* cfg, const void* packed, const v
     Br.np = wb.np;
     Br.unit_begin = units;
     units += (int)B * bg.h * wb.nch;
+    Br.gg_begin = gunits;
+    gunits += (int)B * wb.nch;
     Br.col_k = bg.col_k;
     Br.col_v = bg.col_v;
     Br.col_g = bg.col_g;
@@ -289,7 +308,7 @@ msgla_status msgla_backward(const msgla_config* cfg, const void* packed, const v
     Br.rsum = at<float>(workspace, o.rsum);
     Br.rtot = at<float>(workspace, o.rtot);
     Br.dob = at<float>(workspace, o.dob);
-    Br.dzg = at<float>(workspace, o.dzg);
+    Br.gpart = at<float>(workspace, o.gpart);
     Br.dP = at<char>(workspace, o.dP);
     Br.dY = bg.s > 1 ? at<char>(workspace, o.dY) : nullptr;
     Br.ycat = at<char>(workspace, o.ycat);
@@ -297,7 +316,9 @@ msgla_status msgla_backward(const msgla_config* cfg, const void* packed, const v
     if (bg.s == 1) P.fine = i;
   }
   P.total_units = units;
+  P.gate_units = gunits;
   float* partial = at<float>(workspace, G.partial);
+  float* mcol = at<float>(workspace, G.mcol);
   float* sk = at<float>(workspace, G.splitk);
   const char* WoT = at<char>(packed, g.off_WoT);
 
@@ -329,7 +350,9 @@ msgla_status msgla_backward(const msgla_config* cfg, const void* packed, const v
   }
 
   // ---- the normalisation: dLoss/d(normalised rows) -> dLoss/do, and the gains' gradient ----
-  if (g.norm)
+  if (g.norm) {
+    ColsumJobs J{};
+    size_t used = 0;
     for (int i = 0; i < g.m; ++i) {
       const BwdBranch& Br = P.br[i];
       const int hdv = Br.h * g.dv, rows = (int)B * Br.n;
@@ -338,35 +361,41 @@ msgla_status msgla_backward(const msgla_config* cfg, const void* packed, const v
         continue;
       }
       HIP_TRY(launch_bwd_norm(P, i, g.bf16, st));
-      HIP_TRY(launch_bwd_colsum(Br.ngt, rows, hdv, hdv, partial, colsum_blocks(rows), grads->br[i].norm_g, 1, st));
+      if (!add_colsum(J, used, G.mcol_floats, Br.ngt, rows, hdv, hdv, grads->br[i].norm_g)) return MSGLA_ERR_HIP;
     }
+    HIP_TRY(launch_bwd_mcolsum(J, mcol, st));
+  }
 
   // ---- the chunkwise recurrence and the gate ----
   HIP_TRY(launch_bwd_gate(P, st));
   HIP_TRY(launch_bwd_chunk(P, 0, g.bf16, st));
-  for (int i = 0; i < g.m; ++i)
-    HIP_TRY(launch_bwd_scan(P.br[i].Sst, P.br[i].lb, (int)B * P.br[i].h, P.br[i].nch, P.br[i].np, g.C, g.dk,
-                            g.dv, false, st));
+  HIP_TRY(launch_bwd_scan(P, false, st));
   HIP_TRY(launch_bwd_chunk(P, 1, g.bf16, st));
-  for (int i = 0; i < g.m; ++i)
-    HIP_TRY(launch_bwd_scan(P.br[i].dSt, P.br[i].lb, (int)B * P.br[i].h, P.br[i].nch, P.br[i].np, g.C, g.dk,
-                            g.dv, true, st));
+  HIP_TRY(launch_bwd_scan(P, true, st));
   HIP_TRY(launch_bwd_chunk(P, 5, g.bf16, st));
   HIP_TRY(launch_bwd_chunk(P, 3, g.bf16, st));
   HIP_TRY(launch_bwd_chunk(P, 4, g.bf16, st));
-  for (int i = 0; i < g.m; ++i) {
-    const BwdBranch& Br = P.br[i];
-    const int hdk = Br.h * g.dk, rows = (int)B * Br.n;
-    if (Br.n == 0) {
-      HIP_TRY(fill_zero(grads->br[i].W_g2, (size_t)g.r * hdk * 4, st));
-      HIP_TRY(fill_zero(grads->br[i].b_g, (size_t)hdk * 4, st));
-      continue;
+  // the gate: dz, dg1 into dP, and dW_g2, db_g (with db_f) as column sums
+  HIP_TRY(launch_bwd_gate_grads(P, g.bf16, st));
+  {
+    ColsumJobs J{};
+    size_t used = 0;
+    for (int i = 0; i < g.m; ++i) {
+      const BwdBranch& Br = P.br[i];
+      const int hdk = Br.h * g.dk;
+      if (Br.n == 0) {
+        HIP_TRY(fill_zero(grads->br[i].W_g2, (size_t)g.r * hdk * 4, st));
+        HIP_TRY(fill_zero(grads->br[i].b_g, (size_t)hdk * 4, st));
+        continue;
+      }
+      const int parts = 2 * (int)B * Br.nch, ld = (g.r + 1) * hdk;
+      if (!add_colsum(J, used, G.mcol_floats, Br.gpart, parts, g.r * hdk, ld, grads->br[i].W_g2) ||
+          !add_colsum(J, used, G.mcol_floats, Br.gpart + (size_t)g.r * hdk, parts, hdk, ld, grads->br[i].b_g))
+        return MSGLA_ERR_HIP;
     }
-    HIP_TRY(launch_bwd_dzg(P, i, st));
-    HIP_TRY(launch_bwd_dg1(P, i, g.bf16, st));
-    HIP_TRY(launch_bwd_colsum(Br.dzg, rows, hdk, hdk, partial, colsum_blocks(rows), grads->br[i].b_g, 1, st));
-    BLAS_TRY(gemm_wgrad(hb, g.r, hdk, rows, Br.g1c, rocblas_datatype_f32_r, g.rp, Br.dzg, rocblas_datatype_f32_r,
-                        hdk, one_dst(grads->br[i].W_g2, hdk), sk, G.splitk_floats, 4, st));
+    if (g.m > 1 && !add_colsum(J, used, G.mcol_floats, P.dz, (int)(B * L), g.m, FUSION_STRIDE, grads->b_f))
+      return MSGLA_ERR_HIP;
+    HIP_TRY(launch_bwd_mcolsum(J, mcol, st));
   }
 
   // ---- the input projections and the pooling ----
@@ -401,8 +430,6 @@ msgla_status msgla_backward(const msgla_config* cfg, const void* packed, const v
   if (g.m > 1) {
     HIP_TRY(launch_bwd_wf_partial(P, partial, BWD_WF_NRB, g.bf16, st));
     HIP_TRY(launch_bwd_wf_finish(partial, BWD_WF_NRB, g.d, g.m, grads->W_f, st));
-    HIP_TRY(launch_bwd_colsum(P.dz, (int)(B * L), g.m, FUSION_STRIDE, partial, colsum_blocks((int)(B * L)),
-                              grads->b_f, 1, st));
   }
   return MSGLA_OK;
 }

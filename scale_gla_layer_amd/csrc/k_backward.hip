@@ -25,7 +25,8 @@
 //    and, from a zero initial state, dlog alpha_u = sum_{t>=u} (q_t dq_t - k_t dk_t)
 //    per channel: in-chunk suffix sums plus the totals of later chunks;
 //  the gate (Sec. 2.1), log alpha = logsigmoid(z) / gamma, z = g1 W_g2 + b_g:
-//    dz = dlog alpha sigmoid(-z) / gamma, dg1 = dz W_g2^T        (k_bwd_dzg, k_bwd_dg1);
+//    dz = dlog alpha sigmoid(-z) / gamma, dg1 = dz W_g2^T, dW_g2 = g1^T dz and
+//    db_g = sum of dz                              (k_bwd_gate_grads, k_bwd_mcolsum_*);
 //  the pooling (Sec. 3.1, Eq. (8)): dx_t += dxp_j / s for t in complete block j,
 //  plus the fusion logits' dz_t W_f^T                                   (k_bwd_dx).
 // The plain products around these (dY W_o^T, the weight gradients and the
@@ -300,23 +301,26 @@ __global__ __launch_bounds__(256) void k_bwd_outer(const BwdParams P) {
 }
 
 // ---- scan over chunks, in place: buf[c] <- carried value entering chunk c ----
-// forward: S_prev(c+1) = Diag(lambda_c) S_prev(c) + dS_c, S_prev(0) = 0
-// reverse: G(c-1)      = Diag(lambda_c) G(c) + dG_c,     G(last) = 0
-// lambda_c = e^{b_last} of chunk c (per key channel).  One thread per element.
-__global__ __launch_bounds__(256) void k_bwd_scan(float* buf, const float* lb, int seqs, int nch,
-                                                  int np, int C, int dk, int dv, int rev) {
-  const size_t total = (size_t)seqs * dk * dv;
+// forward (S):  S_prev(c+1) = Diag(lambda_c) S_prev(c) + dS_c, S_prev(0) = 0
+// reverse (dS): G(c-1)      = Diag(lambda_c) G(c) + dG_c,     G(last) = 0
+// lambda_c = e^{b_last} of chunk c (per key channel).  One thread per element;
+// blockIdx.y = branch, so every branch scans in one launch.
+__global__ __launch_bounds__(256) void k_bwd_scan(const BwdParams P, int rev) {
+  const BwdBranch& Br = P.br[blockIdx.y];
+  float* buf = rev ? Br.dSt : Br.Sst;
+  const int nch = Br.nch;
+  const size_t total = (size_t)P.B * Br.h * P.dk * P.dv;
   for (size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
        idx += (size_t)gridDim.x * blockDim.x) {
-    const size_t sq = idx / ((size_t)dk * dv);
-    const int rem = (int)(idx - sq * dk * dv);
-    const int c = rem / dv, e = rem - c * dv;
+    const size_t sq = idx / ((size_t)P.dk * P.dv);
+    const int rem = (int)(idx - sq * P.dk * P.dv);
+    const int c = rem / P.dv, e = rem - c * P.dv;
     float S = 0.f;
 #pragma unroll 4
     for (int it = 0; it < nch; ++it) {
       const int ch = rev ? nch - 1 - it : it;
-      const size_t o = ((sq * nch + ch) * dk + c) * dv + e;
-      const float lam = __expf(lb[(sq * np + (size_t)ch * C + C - 1) * dk + c]);
+      const size_t o = ((sq * nch + ch) * P.dk + c) * P.dv + e;
+      const float lam = __expf(Br.lb[(sq * Br.np + (size_t)ch * P.C + P.C - 1) * P.dk + c]);
       const float t = buf[o];
       buf[o] = S;
       S = lam * S + t;
@@ -381,7 +385,7 @@ __global__ __launch_bounds__(256) void k_bwd_mm1(const BwdParams P) {
     __syncthreads();
   }
   float* QK = Br.QKi + ((size_t)u.sq * Br.nch + u.ch) * 2 * 64 * DK;
-  float* D = Br.AD + ((size_t)u.sq * Br.nch + u.ch) * 2 * 64 * 64 + 64 * 64;
+  float* D = Br.AD + ((size_t)u.sq * Br.nch + u.ch) * 64 * 64;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int t = 16 * w + 4 * (l >> 4) + i;
@@ -490,7 +494,7 @@ __global__ __launch_bounds__(256) void k_bwd_dqdk(const BwdParams P) {
   float* qs = sm + 64 * 65;        // q_scale q, stride 33
   float* ks = qs + 64 * 33;
   float* bs = ks + 64 * 33;
-  const float* D = Br.AD + ((size_t)u.sq * Br.nch + u.ch) * 2 * 64 * 64 + 64 * 64;
+  const float* D = Br.AD + ((size_t)u.sq * Br.nch + u.ch) * 64 * 64;
   const float* QK = Br.QKi + ((size_t)u.sq * Br.nch + u.ch) * 2 * 64 * DK;
   {
     // one round trip for the four tiles
@@ -573,59 +577,139 @@ __global__ __launch_bounds__(256) void k_bwd_dqdk(const BwdParams P) {
   }
 }
 
-// ---- dz of the gate: (suffix of q dq - k dk) * sigmoid(-z) / gamma, position-major ----
-__global__ __launch_bounds__(256) void k_bwd_dzg(const BwdParams P, int bi) {
-  const BwdBranch& Br = P.br[bi];
-  const size_t total = (size_t)P.B * Br.h * Br.nch * P.dk;
-  const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= total) return;
-  const int c = (int)(idx % P.dk);
-  const size_t sc = idx / P.dk;
-  const int ch = (int)(sc % Br.nch);
-  const int sq = (int)(sc / Br.nch);
-  const int b = sq / Br.h, head = sq - b * Br.h;
-  float suffix = 0.f;
-  for (int c2 = ch + 1; c2 < Br.nch; ++c2) suffix += Br.rtot[((size_t)sq * Br.nch + c2) * P.dk + c];
-  const int nvalid = min(P.C, Br.n - ch * P.C);
-  for (int t0 = 0; t0 < nvalid; t0 += 8) {
-    float rv[8], sv[8];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const size_t o = ((size_t)sq * Br.np + ch * P.C + min(t0 + k, nvalid - 1)) * P.dk + c;
-      rv[k] = Br.rsum[o];
-      sv[k] = Br.sg[o];
-    }
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int j = ch * P.C + t0 + k;
-      if (t0 + k < nvalid) Br.dzg[((size_t)(b * Br.n + j) * Br.h + head) * P.dk + c] = (rv[k] + suffix) * sv[k];
-    }
-  }
-}
-
-// ---- dg1 = dz W_g2^T into the gate columns of dP: one wave per pooled position ----
+// ---- the gate's gradients over one (branch, b, chunk) ----
+// dz_tc = (sum over positions u >= t of q dq - k dk in channel c) * sigmoid(-z_tc) / gamma:
+// the in-chunk suffix (rsum) plus the later chunks' totals (rtot).  From dz:
+//   dg1 = dz W_g2^T into the gate columns of dP (fp32 MFMA over 128-channel
+//   slices of dz staged in LDS),
+//   and per (chunk, half of its rows) the sums of g1 dz (toward dW_g2 = g1^T dz)
+//   and of dz (toward db_g) into gpart, summed over chunks by k_bwd_mcolsum_*.
+// thread = (channel of the slice, half of the chunk's rows); wave w takes the
+// dg1 tiles w, w + 4, ... of the chunk's (C / 16) x (RP / 16) tiles.
 template <typename T, int RP>
-__global__ __launch_bounds__(256) void k_bwd_dg1(const BwdParams P, int bi) {
+__global__ __launch_bounds__(256) void k_bwd_gate_grads(const BwdParams P) {
+  constexpr int SW = 128, LDZ = SW + 4, LDG = RP + 4;
+  __shared__ __attribute__((aligned(16))) float dzs[64 * LDZ];   // dz [t][channel]
+  __shared__ __attribute__((aligned(16))) float w2s[RP * LDZ];   // W_g2 [rank][channel]
+  __shared__ __attribute__((aligned(16))) float g1s[64 * LDG];   // block means [t][rank]
+  int bi = 0;
+  while (bi + 1 < P.nbranch && (int)blockIdx.x >= P.br[bi + 1].gg_begin) ++bi;
   const BwdBranch& Br = P.br[bi];
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (row >= P.B * Br.n) return;
-  const int hdk = Br.h * P.dk;
-  float acc[RP];
+  const int local = blockIdx.x - Br.gg_begin;
+  const int b = local / Br.nch, ch = local - b * Br.nch;
+  const int j0 = ch * P.C, nvalid = min(P.C, Br.n - j0);
+  const int hdk = Br.h * P.dk, r = P.r;
+  const int tid = threadIdx.x, cs = tid & (SW - 1), half = tid >> 7;
+  const int w = tid >> 6, l = tid & 63;
+  const size_t row0 = (size_t)b * Br.n + j0;  // the chunk's first pooled position row
+  {
+    // the block means of the chunk's rows; zero past the call's end and for ranks >= r
+    constexpr int NG = 64 * RP / 256;
+    float gv[NG];
 #pragma unroll
-  for (int r = 0; r < RP; ++r) acc[r] = 0.f;
-  const float* dz = Br.dzg + (size_t)row * hdk;
-  for (int c = lane; c < hdk; c += 64) {
-    const float z = dz[c];
+    for (int k = 0; k < NG; ++k) {
+      const int idx = tid + 256 * k, t = idx / RP, rr = idx - t * RP;
+      const bool ok = t < nvalid && rr < r;
+      gv[k] = Br.g1c[(row0 + (ok ? t : 0)) * P.rp + (ok ? rr : 0)];
+    }
 #pragma unroll
-    for (int r = 0; r < RP; ++r) acc[r] += z * Br.W2[(size_t)r * hdk + c];
+    for (int k = 0; k < NG; ++k) {
+      const int idx = tid + 256 * k, t = idx / RP, rr = idx - t * RP;
+      g1s[t * LDG + rr] = (t < nvalid && rr < r) ? gv[k] : 0.f;
+    }
   }
+  const int MT = P.C / 16, ntile = MT * (RP / 16);
+  f32x4 acc[4];
 #pragma unroll
-  for (int r = 0; r < RP; ++r) acc[r] = wave_sum(acc[r]);
-  T* dst = reinterpret_cast<T*>(Br.dP) + (size_t)row * Br.NP + Br.col_g;
+  for (int k = 0; k < 4; ++k) acc[k] = zero4();
+  const int hr = P.C / 2, t0 = half * hr;
+  __syncthreads();  // g1s
+  for (int hc0 = 0; hc0 < hdk; hc0 += SW) {
+    const int hc = hc0 + cs;
+    const bool act = hc < hdk;
+    const int hcc = act ? hc : hdk - 1;
+    const int head = hcc / P.dk, c = hcc - head * P.dk;
+    const size_t sq = (size_t)b * Br.h + head;
+    {
+      // the slice of W_g2 (its rows >= r are zero in the packed weights)
+      constexpr int NW = RP * SW / 256;
+      float wv[NW];
 #pragma unroll
-  for (int r = 0; r < RP; ++r)
-    if (lane == r) dst[r] = from_f32<T>(acc[r]);
+      for (int k = 0; k < NW; ++k) {
+        const int idx = tid + 256 * k, rr = idx / SW, col = idx - rr * SW;
+        wv[k] = Br.W2[(size_t)rr * hdk + min(hc0 + col, hdk - 1)];
+      }
+#pragma unroll
+      for (int k = 0; k < NW; ++k) {
+        const int idx = tid + 256 * k, rr = idx / SW, col = idx - rr * SW;
+        w2s[rr * LDZ + col] = hc0 + col < hdk ? wv[k] : 0.f;
+      }
+    }
+    // the later chunks' totals of this channel
+    float suf = 0.f;
+    for (int c2 = ch + 1; c2 < Br.nch; c2 += 8) {
+      float v[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[k] = Br.rtot[(sq * Br.nch + min(c2 + k, Br.nch - 1)) * P.dk + c];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) suf += c2 + k < Br.nch ? v[k] : 0.f;
+    }
+    float bs = 0.f, aw[RP];
+#pragma unroll
+    for (int rr = 0; rr < RP; ++rr) aw[rr] = 0.f;
+    for (int tb = 0; tb < hr; tb += 8) {
+      float rv[8], sv[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const size_t o = (sq * Br.np + j0 + min(t0 + tb + k, nvalid - 1)) * P.dk + c;
+        rv[k] = Br.rsum[o];
+        sv[k] = Br.sg[o];
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int t = t0 + tb + k;
+        const float dz = (act && t < nvalid) ? (rv[k] + suf) * sv[k] : 0.f;
+        dzs[t * LDZ + cs] = dz;
+        bs += dz;
+#pragma unroll
+        for (int q = 0; q < RP / 4; ++q) {
+          float g4[4];
+          unpack16<float>(ld16(g1s + t * LDG + 4 * q), g4);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) aw[4 * q + i] += g4[i] * dz;
+        }
+      }
+    }
+    if (act) {
+      float* gp = Br.gpart + (size_t)(2 * local + half) * (r + 1) * hdk + hc;
+#pragma unroll
+      for (int rr = 0; rr < RP; ++rr)
+        if (rr < r) gp[(size_t)rr * hdk] = aw[rr];
+      gp[(size_t)r * hdk] = bs;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int tt = w + 4 * k;
+      if (tt < ntile) {
+        const int mt = tt % MT, rt = tt / MT;
+        acc[k] = tile_f32(dzs + 16 * mt * LDZ, LDZ, w2s + 16 * rt * LDZ, LDZ, SW / 16, acc[k]);
+      }
+    }
+    __syncthreads();  // before the next slice overwrites dzs and w2s
+  }
+  T* dP = reinterpret_cast<T*>(Br.dP);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int tt = w + 4 * k;
+    if (tt >= ntile) continue;
+    const int mt = tt % MT, rt = tt / MT, rr = 16 * rt + (l & 15);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = 16 * mt + 4 * (l >> 4) + i;
+      if (t < nvalid && rr < r) dP[(row0 + t) * Br.NP + Br.col_g + rr] = from_f32<T>(acc[k][i]);
+    }
+  }
 }
 
 // ---- fusion and hold, per position (one wave each) ----
@@ -829,43 +913,51 @@ __global__ __launch_bounds__(256) void k_bwd_mask_rows(const BwdParams P, int bi
 }
 
 // ---- column sums and x^T dz, in two deterministic passes ----
-// partial[rb][col] = sum over row block rb of src[row][col] (src fp32, ld);
-// a block is 64 columns x 4 row lanes, its row block cut into the lanes
-__global__ __launch_bounds__(256) void k_bwd_colsum_partial(const float* src, int rows, int cols, int ld,
-                                                            int rows_per_block, float* partial) {
+// Several column sums in one pair of launches (ColsumJobs): the partial pass
+// writes part[pofs + rb * cols + col] = sum over row block rb of src[row][col]
+// (a block is 64 columns x 4 row lanes); the finishing pass adds the row blocks.
+__global__ __launch_bounds__(256) void k_bwd_mcolsum_partial(const ColsumJobs J, float* part) {
   __shared__ float red[4][64];
+  int j = 0;
+  while (j + 1 < J.n && (int)blockIdx.x >= J.cb[j + 1]) ++j;
+  if ((int)blockIdx.y >= J.nrb[j]) return;  // the whole block
   const int cc = threadIdx.x & 63, lane4 = threadIdx.x >> 6;
-  const int col = blockIdx.x * 64 + cc;
-  const int r0 = blockIdx.y * rows_per_block, r1 = min(rows, r0 + rows_per_block);
+  const int rows = J.rows[j], cols = J.cols[j], ld = J.ld[j];
+  const int col = ((int)blockIdx.x - J.cb[j]) * 64 + cc;
+  const int rpb = (rows + J.nrb[j] - 1) / J.nrb[j];
+  const int r0 = blockIdx.y * rpb, r1 = min(rows, r0 + rpb);
   const int colc = min(col, cols - 1);
+  const float* src = J.src[j];
   float acc = 0.f;
-  for (int r = r0 + lane4; r < r1; r += 32) {
+  for (int rw = r0 + lane4; rw < r1; rw += 32) {
     float v[8];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) v[k] = src[(size_t)min(r + 4 * k, r1 - 1) * ld + colc];
+    for (int k = 0; k < 8; ++k) v[k] = src[(size_t)min(rw + 4 * k, r1 - 1) * ld + colc];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) acc += (r + 4 * k < r1) ? v[k] : 0.f;
+    for (int k = 0; k < 8; ++k) acc += (rw + 4 * k < r1) ? v[k] : 0.f;
   }
   red[lane4][cc] = acc;
   __syncthreads();
   if (lane4 == 0 && col < cols)
-    partial[(size_t)blockIdx.y * cols + col] = red[0][cc] + red[1][cc] + red[2][cc] + red[3][cc];
+    part[J.pofs[j] + (size_t)blockIdx.y * cols + col] = red[0][cc] + red[1][cc] + red[2][cc] + red[3][cc];
 }
 
-// out[col] = sum_rb partial[rb][col]
-__global__ __launch_bounds__(256) void k_bwd_colsum_finish(const float* partial, int nrb, int cols, float* out,
-                                                           int out_stride) {
-  const int col = blockIdx.x * 256 + threadIdx.x;
+__global__ __launch_bounds__(256) void k_bwd_mcolsum_finish(const ColsumJobs J, const float* part) {
+  int j = 0;
+  while (j + 1 < J.n && (int)blockIdx.x >= J.fb[j + 1]) ++j;
+  const int cols = J.cols[j], nrb = J.nrb[j];
+  const int col = ((int)blockIdx.x - J.fb[j]) * 256 + threadIdx.x;
   if (col >= cols) return;
+  const float* p = part + J.pofs[j];
   float acc = 0.f;
   for (int rb0 = 0; rb0 < nrb; rb0 += 8) {
     float v[8];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) v[k] = partial[(size_t)min(rb0 + k, nrb - 1) * cols + col];
+    for (int k = 0; k < 8; ++k) v[k] = p[(size_t)min(rb0 + k, nrb - 1) * cols + col];
 #pragma unroll
     for (int k = 0; k < 8; ++k) acc += (rb0 + k < nrb) ? v[k] : 0.f;
   }
-  out[(size_t)col * out_stride] = acc;
+  J.dst[j][col] = acc;
 }
 
 // partial[rb][col][i] = sum over row block rb of x[row][col] dz[row][i], i < 8
@@ -947,32 +1039,27 @@ hipError_t launch_bwd_gate(const BwdParams& P, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_scan(float* buf, const float* lb, int seqs, int nch, int np, int C, int dk, int dv,
-                           bool rev, hipStream_t st) {
-  const size_t total = (size_t)seqs * dk * dv;
-  if (total == 0) return hipSuccess;
-  const unsigned grid = (unsigned)std::min<size_t>((total + 255) / 256, 65536);
-  hipLaunchKernelGGL(k_bwd_scan, dim3(grid), dim3(256), 0, st, buf, lb, seqs, nch, np, C, dk, dv, rev ? 1 : 0);
+// every branch's scan in one launch (blockIdx.y = branch)
+hipError_t launch_bwd_scan(const BwdParams& P, bool rev, hipStream_t st) {
+  size_t most = 0;
+  for (int i = 0; i < P.nbranch; ++i) most = std::max(most, (size_t)P.B * P.br[i].h * P.dk * P.dv);
+  if (most == 0 || P.nbranch == 0) return hipSuccess;
+  const unsigned grid = (unsigned)std::min<size_t>((most + 255) / 256, 65536);
+  hipLaunchKernelGGL(k_bwd_scan, dim3(grid, P.nbranch), dim3(256), 0, st, P, rev ? 1 : 0);
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_dzg(const BwdParams& P, int bi, hipStream_t st) {
-  const size_t total = (size_t)P.B * P.br[bi].h * P.br[bi].nch * P.dk;
-  if (total == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_bwd_dzg, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, P, bi);
-  return hipGetLastError();
-}
-
-hipError_t launch_bwd_dg1(const BwdParams& P, int bi, bool bf16_path, hipStream_t st) {
-  const int rows = P.B * P.br[bi].n;
-  if (rows == 0) return hipSuccess;
-  const dim3 grid((rows + 3) / 4);
+// dz, dg1 and the dW_g2 / db_g partials of every branch in one launch
+hipError_t launch_bwd_gate_grads(const BwdParams& P, bool bf16_path, hipStream_t st) {
+  if (P.gate_units == 0) return hipSuccess;
+  if (P.C % 16 != 0 || P.C > 64 || P.r > P.rp || (P.rp != 16 && P.rp != 64)) return hipErrorInvalidValue;
+  const dim3 grid(P.gate_units);
   if (P.rp == 16) {
-    if (bf16_path) hipLaunchKernelGGL((k_bwd_dg1<bf16, 16>), grid, dim3(256), 0, st, P, bi);
-    else hipLaunchKernelGGL((k_bwd_dg1<float, 16>), grid, dim3(256), 0, st, P, bi);
+    if (bf16_path) hipLaunchKernelGGL((k_bwd_gate_grads<bf16, 16>), grid, dim3(256), 0, st, P);
+    else hipLaunchKernelGGL((k_bwd_gate_grads<float, 16>), grid, dim3(256), 0, st, P);
   } else {
-    if (bf16_path) hipLaunchKernelGGL((k_bwd_dg1<bf16, 64>), grid, dim3(256), 0, st, P, bi);
-    else hipLaunchKernelGGL((k_bwd_dg1<float, 64>), grid, dim3(256), 0, st, P, bi);
+    if (bf16_path) hipLaunchKernelGGL((k_bwd_gate_grads<bf16, 64>), grid, dim3(256), 0, st, P);
+    else hipLaunchKernelGGL((k_bwd_gate_grads<float, 64>), grid, dim3(256), 0, st, P);
   }
   return hipGetLastError();
 }
@@ -1019,19 +1106,17 @@ hipError_t launch_bwd_dx(const BwdParams& P, bool bf16_path, hipStream_t st) {
   return hipGetLastError();
 }
 
-// out[c * out_stride] = sum over rows of src[row][c]; partial holds nrb * cols floats
-hipError_t launch_bwd_colsum(const float* src, int rows, int cols, int ld, float* partial, int nrb,
-                             float* out, int out_stride, hipStream_t st) {
-  if (cols == 0) return hipSuccess;
-  const int rpb = (rows + nrb - 1) / nrb;
-  hipLaunchKernelGGL(k_bwd_colsum_partial, dim3((cols + 63) / 64, nrb), dim3(256), 0, st, src, rows, cols, ld,
-                     rpb, partial);
-  hipLaunchKernelGGL(k_bwd_colsum_finish, dim3((cols + 255) / 256), dim3(256), 0, st, partial, nrb, cols, out,
-                     out_stride);
+// every job of J (partials at part, J.pofs) in one pair of launches
+hipError_t launch_bwd_mcolsum(const ColsumJobs& J, float* part, hipStream_t st) {
+  if (J.n == 0 || J.cb[J.n] == 0) return hipSuccess;
+  int nrb = 1;
+  for (int j = 0; j < J.n; ++j) nrb = std::max(nrb, J.nrb[j]);
+  hipLaunchKernelGGL(k_bwd_mcolsum_partial, dim3(J.cb[J.n], nrb), dim3(256), 0, st, J, part);
+  hipLaunchKernelGGL(k_bwd_mcolsum_finish, dim3(J.fb[J.n]), dim3(256), 0, st, J, static_cast<const float*>(part));
   return hipGetLastError();
 }
 
-// partial [nrb][d][8]: x^T dz per row block; the host sums them with colsum_finish
+// partial [nrb][d][8]: x^T dz per row block, summed by k_bwd_wf_finish
 hipError_t launch_bwd_wf_partial(const BwdParams& P, float* partial, int nrb, bool bf16_path, hipStream_t st) {
   const int rpb = (P.B * P.L + nrb - 1) / nrb;
   const dim3 grid(P.d / 64, nrb);

@@ -252,12 +252,14 @@ struct K3Params {
 //   Sst, dSt    [B][h][nch][d_k][d_v]  fp32  state entering each chunk, and the
 //                                            loss gradient reaching each chunk's
 //                                            last state from later chunks
-//   AD          [B][h][nch][2][64][64] fp32  D (do v^T, t >= i) in the second half
+//   AD          [B][h][nch][64][64]    fp32  D (do v^T, t >= i) of each chunk
 //   QKi         [B][h][nch][2][64][d_k] fp32 do S_prev^T and v dS_end^T of each chunk
 //   rsum, rtot  [B][h][np][d_k], [B][h][nch][d_k]  fp32  in-chunk suffix sums of
 //                                            q dq - k dk, and their chunk totals
 //   dob         [B n][h d_v]           fp32  dLoss/d(GLA output o)
-//   dzg         [B n][h d_k]           fp32  dLoss/d(gate pre-activation z)
+//   gpart       [B nch][2][r + 1][h d_k]  fp32  per (chunk, half of its rows):
+//                                            sums of g1 dz (rows 0..r-1) and of dz
+//                                            (row r), dz = dLoss/d(gate pre-activation)
 //   dP          [B n][NP]              T     dLoss/d[q | k | v | x W_g1] columns
 //                                            (q_scale folded into q), NP = col_g + rp
 //   dY, Yc      [B n][d]               T     coarse branches: dLoss/dY and Y = y W_o
@@ -267,6 +269,7 @@ struct K3Params {
 struct BwdBranch {
   int s, h, n, nch, np;
   int unit_begin;             // first (b, head, chunk) unit of the branch
+  int gg_begin;               // first (b, chunk) unit of the branch's gate gradients
   int col_k, col_v, col_g, NP;
   const float* q;             // forward workspace: projections (q unscaled)
   const float* k;
@@ -290,7 +293,7 @@ struct BwdBranch {
   float* rsum;
   float* rtot;
   float* dob;
-  float* dzg;
+  float* gpart;
   void* dP;
   void* dY;
   void* ycat;
@@ -300,7 +303,7 @@ struct BwdBranch {
 struct BwdParams {
   int B, L, d, dk, dv, C, r, rp, m;
   float inv_gamma, q_scale;
-  int nbranch, total_units;
+  int nbranch, total_units, gate_units;
   int fine;                   // branch with scale 1, or -1
   const void* x;              // [B][L][d] T
   const uint8_t* mask;        // [B][L] token mask of the forward, or null
@@ -310,6 +313,20 @@ struct BwdParams {
   float* dz;                  // [B L][8]
   const void* Wf;             // fusion logit rows [m][d] T (packed), null when m == 1
   BwdBranch br[MSGLA_MAX_BRANCHES];
+};
+
+// Column sums of several row-major fp32 matrices in one pair of launches
+// (k_bwd_mcolsum_*): job j sums rows x cols of src[j] (row stride ld) into
+// dst[j][cols] through nrb[j] row blocks of partials at part + pofs[j].
+struct ColsumJobs {
+  static constexpr int MAX = 2 * MSGLA_MAX_BRANCHES + 1;
+  int n;
+  const float* src[MAX];
+  float* dst[MAX];
+  int rows[MAX], cols[MAX], ld[MAX], nrb[MAX];
+  int cb[MAX + 1];   // first 64-column block of each job (partial pass)
+  int fb[MAX + 1];   // first 256-column block of each job (finishing pass)
+  size_t pofs[MAX];
 };
 
 // Destinations of a split-K weight-gradient product (k_bwd_splitk_reduce).
