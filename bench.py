@@ -650,7 +650,7 @@ def summarize_training_profile(d, workload, wl, cmds, out_dir):
                 short = "rocBLAS " + (mt.group(0) if mt else "gemm") + (" fp32" if "_SB_" in name else "")
             else:
                 short = _short(name)
-                m = re.search(r"(k_bwd_[A-Za-z0-9_]*?)(?=I[DfL]|E|\(|$)", name)
+                m = re.search(r"(k_bwd_[A-Za-z0-9_]*?)(?=I[DfL]|E|<|\(|$)", name)
                 if m:
                     short = m.group(1)
                     if short == "k_bwd_outer":

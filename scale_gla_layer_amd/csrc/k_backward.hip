@@ -402,6 +402,128 @@ __global__ __launch_bounds__(256) void k_bwd_mm1(const BwdParams P) {
   }
 }
 
+// ---- the same products for bf16 storage, on bf16 matrix cores ----
+// Each fp32 operand (do, S, dS) is carried as hi + lo bf16 (hi = bf16(x),
+// lo = bf16(x - hi)) and a product as hi.hi + hi.lo + lo.hi, fp32 accumulate:
+// the dropped lo.lo term and lo's rounding leave about 2^-16 of each product.
+// v is exact in bf16 (its storage type), so its products take two terms.
+// Over d_v in 32-column steps (one bf16 k-slab): LDS planes of bf16 rows; wave w
+// takes rows 16 w .. 16 w + 15 as in the fp32 kernel.
+__device__ __forceinline__ f32x4 slab_bf(const bf16* a, int lda, const bf16* b, int ldb, f32x4 acc) {
+  const int l = threadIdx.x & 63;
+  return mma_slab<bf16>(ld16(a + (l & 15) * lda + 8 * (l >> 4)), ld16(b + (l & 15) * ldb + 8 * (l >> 4)), acc);
+}
+
+template <int DK>
+__global__ __launch_bounds__(256) void k_bwd_mm1_split(const BwdParams P) {
+  constexpr int EC = 32, LB = EC + 8, NT = DK / 16;
+  constexpr int SG = (DK * EC / 8 + 255) / 256;  // 8-column groups of S (and dS) per thread
+  __shared__ __attribute__((aligned(16))) bf16 doh[64 * LB], dol[64 * LB], vh[64 * LB];
+  __shared__ __attribute__((aligned(16))) bf16 sh[DK * LB], sl[DK * LB], dsh[DK * LB], dsl[DK * LB];
+  const UnitPos u = unit_pos(P, blockIdx.x);
+  const BwdBranch& Br = P.br[u.bi];
+  const int j0 = u.ch * P.C;
+  const int nvalid = min(P.C, Br.n - j0);
+  const size_t sbase = ((size_t)u.sq * Br.nch + u.ch) * DK;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const bf16* vT = reinterpret_cast<const bf16*>(Br.vT) + ((size_t)u.sq * Br.nch + u.ch) * P.dv * P.C;
+  f32x4 aq[NT], ak[NT], ad[4];
+#pragma unroll
+  for (int ct = 0; ct < NT; ++ct) aq[ct] = ak[ct] = zero4();
+#pragma unroll
+  for (int j = 0; j < 4; ++j) ad[j] = zero4();
+  // thread's pieces: do row tid / 4, columns 8 (tid % 4) ..; v column e = tid / 8
+  // (of the step), positions 8 (tid % 8) ..; S and dS rows tid / 4 + 64 g
+  const int dr = tid >> 2, dc = 8 * (tid & 3);
+  const int ve = tid >> 3, vt = 8 * (tid & 7);
+  const bool dok = dr < nvalid, vok = vt < P.C;
+  const float* dsrc = Br.dob + ((size_t)(u.b * Br.n + j0 + (dok ? dr : 0)) * Br.h + u.head) * P.dv + dc;
+  float rd[8], rs_[SG][8], rds[SG][8];
+  u32x4 rv;
+  auto load_step = [&](int e0) {
+    unpack16<float>(ld16(dsrc + e0), rd);
+    unpack16<float>(ld16(dsrc + e0 + 4), rd + 4);
+    rv = ld16(vT + (size_t)(e0 + ve) * P.C + (vok ? vt : 0));
+#pragma unroll
+    for (int g = 0; g < SG; ++g) {
+      const int c = min(dr + 64 * g, DK - 1);
+      const float* ps = Br.Sst + (sbase + c) * P.dv + e0 + dc;
+      const float* pd = Br.dSt + (sbase + c) * P.dv + e0 + dc;
+      unpack16<float>(ld16(ps), rs_[g]);
+      unpack16<float>(ld16(ps + 4), rs_[g] + 4);
+      unpack16<float>(ld16(pd), rds[g]);
+      unpack16<float>(ld16(pd + 4), rds[g] + 4);
+    }
+  };
+  auto store_step = [&]() {
+    u32x4 hi, lo;
+    if (!dok)
+#pragma unroll
+      for (int k = 0; k < 8; ++k) rd[k] = 0.f;
+    split_bf16(rd, hi, lo);
+    st16(doh + dr * LB + dc, hi);
+    st16(dol + dr * LB + dc, lo);
+    {
+      // every row is written: zero past the call's end and past the chunk (C < 64)
+      float v8[8];
+      unpack16<bf16>(rv, v8);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) vh[(vt + k) * LB + ve] = (bf16)(vok && vt + k < nvalid ? v8[k] : 0.f);
+    }
+#pragma unroll
+    for (int g = 0; g < SG; ++g) {
+      const int c = dr + 64 * g;
+      if (c < DK) {
+        split_bf16(rs_[g], hi, lo);
+        st16(sh + c * LB + dc, hi);
+        st16(sl + c * LB + dc, lo);
+        split_bf16(rds[g], hi, lo);
+        st16(dsh + c * LB + dc, hi);
+        st16(dsl + c * LB + dc, lo);
+      }
+    }
+  };
+  load_step(0);
+  for (int e0 = 0; e0 < P.dv; e0 += EC) {
+    store_step();
+    __syncthreads();
+    if (e0 + EC < P.dv) load_step(e0 + EC);
+    const bf16* ra = doh + 16 * w * LB;
+    const bf16* rl = dol + 16 * w * LB;
+    const bf16* rvv = vh + 16 * w * LB;
+#pragma unroll
+    for (int ct = 0; ct < NT; ++ct) {
+      aq[ct] = slab_bf(ra, LB, sh + 16 * ct * LB, LB, aq[ct]);
+      aq[ct] = slab_bf(ra, LB, sl + 16 * ct * LB, LB, aq[ct]);
+      aq[ct] = slab_bf(rl, LB, sh + 16 * ct * LB, LB, aq[ct]);
+      ak[ct] = slab_bf(rvv, LB, dsh + 16 * ct * LB, LB, ak[ct]);
+      ak[ct] = slab_bf(rvv, LB, dsl + 16 * ct * LB, LB, ak[ct]);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      ad[j] = slab_bf(ra, LB, vh + 16 * j * LB, LB, ad[j]);
+      ad[j] = slab_bf(rl, LB, vh + 16 * j * LB, LB, ad[j]);
+    }
+    __syncthreads();
+  }
+  float* QK = Br.QKi + ((size_t)u.sq * Br.nch + u.ch) * 2 * 64 * DK;
+  float* D = Br.AD + ((size_t)u.sq * Br.nch + u.ch) * 64 * 64;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int t = 16 * w + 4 * (l >> 4) + i;
+#pragma unroll
+    for (int ct = 0; ct < NT; ++ct) {
+      QK[t * DK + 16 * ct + (l & 15)] = aq[ct][i];
+      QK[64 * DK + t * DK + 16 * ct + (l & 15)] = ak[ct][i];
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int c = 16 * j + (l & 15);
+      D[t * 64 + c] = (c <= t && t < nvalid) ? ad[j][i] : 0.f;
+    }
+  }
+}
+
 // ---- dv_i = sum_{t>=i} A_ti do_t + k-hat_i dS_end, into the v columns of dP ----
 // On the matrix cores: rows i, columns e of the block's 64-column slice; wave w
 // takes rows 16 w .. 16 w + 15.  A is the forward's (K2a's, in the storage
@@ -1002,7 +1124,12 @@ static void launch_chunk_kernels_t(const BwdParams& P, int which, hipStream_t st
   switch (which) {
     case 0: hipLaunchKernelGGL((k_bwd_outer<T, DK, false>), dim3(P.total_units, slices), dim3(256), 0, st, P); break;
     case 1: hipLaunchKernelGGL((k_bwd_outer<T, DK, true>), dim3(P.total_units, slices), dim3(256), 0, st, P); break;
-    case 5: hipLaunchKernelGGL((k_bwd_mm1<T, DK>), dim3(P.total_units), dim3(256), 0, st, P); break;
+    case 5:
+      if constexpr (sizeof(T) == 2)
+        hipLaunchKernelGGL((k_bwd_mm1_split<DK>), dim3(P.total_units), dim3(256), 0, st, P);
+      else
+        hipLaunchKernelGGL((k_bwd_mm1<T, DK>), dim3(P.total_units), dim3(256), 0, st, P);
+      break;
     case 3: hipLaunchKernelGGL((k_bwd_dv<T, DK>), dim3(P.total_units, slices), dim3(256), 0, st, P); break;
     default: {
       const int cs = DK < 32 ? 1 : DK / 32;
