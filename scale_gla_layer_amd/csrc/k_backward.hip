@@ -300,6 +300,118 @@ __global__ __launch_bounds__(256) void k_bwd_outer(const BwdParams P) {
       out[(base + 16 * ct + 4 * (l >> 4) + i) * P.dv + e0 + 16 * w + (l & 15)] = acc[ct][i];
 }
 
+// ---- the same increments for bf16 storage, on bf16 matrix cores ----
+// X * F is carried as hi + lo bf16; Y = v is exact in bf16, Y = dLoss/do is
+// split like X (products hi.hi + hi.lo + lo.hi; see k_bwd_mm1_split).  X^T and
+// Y^T are staged as bf16 rows over the chunk's 64 positions (two k-slabs);
+// wave w takes columns 16 w .. 16 w + 15 and every row tile.
+__device__ __forceinline__ f32x4 slab_bf(const bf16* a, int lda, const bf16* b, int ldb, f32x4 acc) {
+  const int l = threadIdx.x & 63;
+  return mma_slab<bf16>(ld16(a + (l & 15) * lda + 8 * (l >> 4)), ld16(b + (l & 15) * ldb + 8 * (l >> 4)), acc);
+}
+
+// 8 positions of a column of a position-major fp32 matrix (rows t0 .. t0 + 7 at
+// src + t * ld, zero from nvalid on), split into hi and lo bf16 packets
+__device__ __forceinline__ void col8_split(const float* src, size_t ld, int t0, int nvalid, u32x4& hi, u32x4& lo) {
+  float v[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) v[k] = src[(size_t)min(t0 + k, max(nvalid - 1, 0)) * ld];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) v[k] = t0 + k < nvalid ? v[k] : 0.f;
+  split_bf16(v, hi, lo);
+}
+
+template <int DK, bool REV>
+__global__ __launch_bounds__(256) void k_bwd_outer_split(const BwdParams P) {
+  constexpr int LB = 64 + 8, NT = DK / 16;
+  constexpr int TPC = 256 / DK;              // threads per channel
+  constexpr int GPT = (8 + TPC - 1) / TPC;   // 8-position groups per thread
+  __shared__ __attribute__((aligned(16))) bf16 xh[DK * LB], xl[DK * LB];       // (X * F)^T [c][t]
+  __shared__ __attribute__((aligned(16))) bf16 yh[64 * LB], yl[(REV ? 64 : 1) * LB];  // Y^T [e][t]
+  const UnitPos u = unit_pos(P, blockIdx.x);
+  const BwdBranch& Br = P.br[u.bi];
+  const int j0 = u.ch * P.C, e0 = blockIdx.y * 64;
+  const int nvalid = min(P.C, Br.n - j0);
+  const size_t row0 = (size_t)u.sq * Br.np + j0;
+  const int tid = threadIdx.x;
+  {
+    // X^T: thread = channel c (loads coalesced over channels), groups of 8 positions
+    const int c = tid % DK;
+    const float lastb = Br.lb[(row0 + P.C - 1) * DK + c];
+#pragma unroll
+    for (int gi = 0; gi < GPT; ++gi) {
+      const int g = tid / DK + gi * TPC;
+      if (g >= 8) break;
+      float xv[8], lv[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const size_t o = (row0 + min(8 * g + k, nvalid - 1)) * DK + c;
+        xv[k] = REV ? Br.q[o] : Br.k[o];
+        lv[k] = Br.lb[o];
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const float f = REV ? P.q_scale * xv[k] * __expf(lv[k]) : xv[k] * __expf(lastb - lv[k]);
+        xv[k] = 8 * g + k < nvalid ? f : 0.f;
+      }
+      u32x4 hi, lo;
+      split_bf16(xv, hi, lo);
+      st16(xh + c * LB + 8 * g, hi);
+      st16(xl + c * LB + 8 * g, lo);
+    }
+  }
+  if constexpr (REV) {
+    // dLoss/do^T: thread = column e (coalesced), position groups tid / 64 and + 4
+    const int e = tid & 63;
+    const float* src = Br.dob + ((size_t)(u.b * Br.n + j0) * Br.h + u.head) * P.dv + e0 + e;
+#pragma unroll
+    for (int gi = 0; gi < 2; ++gi) {
+      const int g = (tid >> 6) + 4 * gi;
+      u32x4 hi, lo;
+      col8_split(src, (size_t)Br.h * P.dv, 8 * g, nvalid, hi, lo);
+      st16(yh + e * LB + 8 * g, hi);
+      st16(yl + e * LB + 8 * g, lo);
+    }
+  } else {
+    // v^T rows straight from the chunk's v^T (exact in bf16), zero past the call's end
+    const bf16* vT = reinterpret_cast<const bf16*>(Br.vT) + ((size_t)u.sq * Br.nch + u.ch) * P.dv * P.C;
+    const int e = tid >> 2;
+#pragma unroll
+    for (int gi = 0; gi < 2; ++gi) {
+      const int g = (tid & 3) + 4 * gi;
+      const bool inc = 8 * g < P.C;
+      float v8[8];
+      unpack16<bf16>(ld16(vT + (size_t)(e0 + e) * P.C + (inc ? 8 * g : 0)), v8);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v8[k] = inc && 8 * g + k < nvalid ? v8[k] : 0.f;
+      st16(yh + e * LB + 8 * g, pack16<bf16>(v8));
+    }
+  }
+  __syncthreads();
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  f32x4 acc[NT];
+#pragma unroll
+  for (int ct = 0; ct < NT; ++ct) {
+    acc[ct] = zero4();
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const bf16* a = xh + 16 * ct * LB + 32 * s;
+      const bf16* al = xl + 16 * ct * LB + 32 * s;
+      const bf16* b = yh + 16 * w * LB + 32 * s;
+      acc[ct] = slab_bf(a, LB, b, LB, acc[ct]);
+      acc[ct] = slab_bf(al, LB, b, LB, acc[ct]);
+      if constexpr (REV) acc[ct] = slab_bf(a, LB, yl + 16 * w * LB + 32 * s, LB, acc[ct]);
+    }
+  }
+  float* out = REV ? Br.dSt : Br.Sst;
+  const size_t base = ((size_t)u.sq * Br.nch + u.ch) * DK;
+#pragma unroll
+  for (int ct = 0; ct < NT; ++ct)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      out[(base + 16 * ct + 4 * (l >> 4) + i) * P.dv + e0 + 16 * w + (l & 15)] = acc[ct][i];
+}
+
 // ---- scan over chunks, in place: buf[c] <- carried value entering chunk c ----
 // forward (S):  S_prev(c+1) = Diag(lambda_c) S_prev(c) + dS_c, S_prev(0) = 0
 // reverse (dS): G(c-1)      = Diag(lambda_c) G(c) + dG_c,     G(last) = 0
@@ -409,11 +521,6 @@ __global__ __launch_bounds__(256) void k_bwd_mm1(const BwdParams P) {
 // v is exact in bf16 (its storage type), so its products take two terms.
 // Over d_v in 32-column steps (one bf16 k-slab): LDS planes of bf16 rows; wave w
 // takes rows 16 w .. 16 w + 15 as in the fp32 kernel.
-__device__ __forceinline__ f32x4 slab_bf(const bf16* a, int lda, const bf16* b, int ldb, f32x4 acc) {
-  const int l = threadIdx.x & 63;
-  return mma_slab<bf16>(ld16(a + (l & 15) * lda + 8 * (l >> 4)), ld16(b + (l & 15) * ldb + 8 * (l >> 4)), acc);
-}
-
 template <int DK>
 __global__ __launch_bounds__(256) void k_bwd_mm1_split(const BwdParams P) {
   constexpr int EC = 32, LB = EC + 8, NT = DK / 16;
@@ -593,6 +700,123 @@ __global__ __launch_bounds__(256) void k_bwd_dv(const BwdParams P) {
     for (int j = 0; j < 4; ++j)
       dP[(size_t)(u.b * Br.n + j0 + r) * Br.NP + Br.col_v + u.head * P.dv + e0 + 16 * j + (l & 15)] =
           from_f32<T>(acc[j][i]);
+  }
+}
+
+// ---- dv for bf16 storage, on bf16 matrix cores ----
+// A^T do over the chunk's positions (A exact in bf16, do as hi + lo), then
+// k-hat dS_end^T over the key channels in 64-channel steps (both as hi + lo);
+// see k_bwd_mm1_split.  Wave w takes rows 16 w .. 16 w + 15, every column tile
+// of the block's 64-column slice.  d_k >= 32 (one bf16 k-slab per 32 channels).
+template <int DK>
+__global__ __launch_bounds__(256) void k_bwd_dv_split(const BwdParams P) {
+  constexpr int LB = 64 + 8, CW = DK < 64 ? DK : 64, LC = CW + 8, NS = CW / 32;
+  constexpr int KG = 64 * CW / 8 / 256;  // k-hat 8-channel groups per thread
+  static_assert(DK >= 32 && DK % 32 == 0, "whole bf16 k-slabs of channels");
+  __shared__ __attribute__((aligned(16))) bf16 at[64 * LB];                   // A^T [i][t]
+  __shared__ __attribute__((aligned(16))) bf16 dth[64 * LB], dtl[64 * LB];    // do^T [e][t]
+  __shared__ __attribute__((aligned(16))) bf16 kh[64 * LC], kl[64 * LC];      // k-hat [i][c]
+  __shared__ __attribute__((aligned(16))) bf16 sh[64 * LC], sl[64 * LC];      // dS_end^T [e][c]
+  const UnitPos u = unit_pos(P, blockIdx.x);
+  const BwdBranch& Br = P.br[u.bi];
+  const int j0 = u.ch * P.C, e0 = blockIdx.y * 64;
+  const int nvalid = min(P.C, Br.n - j0);
+  const size_t row0 = (size_t)u.sq * Br.np + j0;
+  const size_t sbase = ((size_t)u.sq * Br.nch + u.ch) * DK;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  {
+    // A^T: thread = (row t, 8-column group), two rows; written transposed
+    const bf16* A = reinterpret_cast<const bf16*>(Br.A) + ((size_t)u.sq * Br.nch + u.ch) * P.C * P.C;
+    const int ig = tid & 7;
+#pragma unroll
+    for (int gi = 0; gi < 2; ++gi) {
+      const int t = (tid >> 3) + 32 * gi;
+      const bool ok = t < nvalid && 8 * ig < P.C;
+      float a8[8];
+      unpack16<bf16>(ld16(A + (size_t)(ok ? t : 0) * P.C + (ok ? 8 * ig : 0)), a8);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) at[(8 * ig + k) * LB + t] = (bf16)(ok ? a8[k] : 0.f);
+    }
+    // do^T: thread = column e (coalesced), position groups tid / 64 and + 4
+    const int e = tid & 63;
+    const float* src = Br.dob + ((size_t)(u.b * Br.n + j0) * Br.h + u.head) * P.dv + e0 + e;
+#pragma unroll
+    for (int gi = 0; gi < 2; ++gi) {
+      const int g = (tid >> 6) + 4 * gi;
+      u32x4 hi, lo;
+      col8_split(src, (size_t)Br.h * P.dv, 8 * g, nvalid, hi, lo);
+      st16(dth + e * LB + 8 * g, hi);
+      st16(dtl + e * LB + 8 * g, lo);
+    }
+  }
+  f32x4 acc[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) acc[j] = zero4();
+  for (int c0 = 0; c0 < DK; c0 += CW) {
+    // k-hat [i][c0 .. c0 + CW): thread = (row i, 8-channel group)
+#pragma unroll
+    for (int gi = 0; gi < KG; ++gi) {
+      const int idx = tid + 256 * gi, i = idx / (CW / 8), cg = 8 * (idx % (CW / 8));
+      const size_t o = (row0 + min(i, nvalid - 1)) * DK + c0 + cg;
+      float k8[8], b8[8], bl8[8];
+      unpack16<float>(ld16(Br.k + o), k8);
+      unpack16<float>(ld16(Br.k + o + 4), k8 + 4);
+      unpack16<float>(ld16(Br.lb + o), b8);
+      unpack16<float>(ld16(Br.lb + o + 4), b8 + 4);
+      const float* pl = Br.lb + (row0 + P.C - 1) * DK + c0 + cg;
+      unpack16<float>(ld16(pl), bl8);
+      unpack16<float>(ld16(pl + 4), bl8 + 4);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) k8[k] = i < nvalid ? k8[k] * __expf(bl8[k] - b8[k]) : 0.f;
+      u32x4 hi, lo;
+      split_bf16(k8, hi, lo);
+      st16(kh + i * LC + cg, hi);
+      st16(kl + i * LC + cg, lo);
+    }
+    // dS_end^T [e][c]: thread = column e (coalesced over e), 8-channel groups
+    {
+      const int e = tid & 63;
+#pragma unroll
+      for (int g = tid >> 6; g < CW / 8; g += 4) {
+        u32x4 hi, lo;
+        col8_split(Br.dSt + (sbase + c0) * P.dv + e0 + e, P.dv, 8 * g, CW, hi, lo);
+        st16(sh + e * LC + 8 * g, hi);
+        st16(sl + e * LC + 8 * g, lo);
+      }
+    }
+    __syncthreads();
+    if (c0 == 0) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          const bf16* a = at + 16 * w * LB + 32 * s;
+          acc[j] = slab_bf(a, LB, dth + 16 * j * LB + 32 * s, LB, acc[j]);
+          acc[j] = slab_bf(a, LB, dtl + 16 * j * LB + 32 * s, LB, acc[j]);
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const bf16* a = kh + 16 * w * LC + 32 * s;
+        const bf16* al = kl + 16 * w * LC + 32 * s;
+        const bf16* b = sh + 16 * j * LC + 32 * s;
+        acc[j] = slab_bf(a, LC, b, LC, acc[j]);
+        acc[j] = slab_bf(a, LC, sl + 16 * j * LC + 32 * s, LC, acc[j]);
+        acc[j] = slab_bf(al, LC, b, LC, acc[j]);
+      }
+    __syncthreads();
+  }
+  bf16* dP = reinterpret_cast<bf16*>(Br.dP);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 16 * w + 4 * (l >> 4) + i;
+    if (r >= nvalid) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      dP[(size_t)(u.b * Br.n + j0 + r) * Br.NP + Br.col_v + u.head * P.dv + e0 + 16 * j + (l & 15)] =
+          (bf16)acc[j][i];
   }
 }
 
@@ -1122,15 +1346,30 @@ template <typename T, int DK>
 static void launch_chunk_kernels_t(const BwdParams& P, int which, hipStream_t st) {
   const int slices = P.dv / 64;
   switch (which) {
-    case 0: hipLaunchKernelGGL((k_bwd_outer<T, DK, false>), dim3(P.total_units, slices), dim3(256), 0, st, P); break;
-    case 1: hipLaunchKernelGGL((k_bwd_outer<T, DK, true>), dim3(P.total_units, slices), dim3(256), 0, st, P); break;
+    case 0:
+      if constexpr (sizeof(T) == 2)
+        hipLaunchKernelGGL((k_bwd_outer_split<DK, false>), dim3(P.total_units, slices), dim3(256), 0, st, P);
+      else
+        hipLaunchKernelGGL((k_bwd_outer<T, DK, false>), dim3(P.total_units, slices), dim3(256), 0, st, P);
+      break;
+    case 1:
+      if constexpr (sizeof(T) == 2)
+        hipLaunchKernelGGL((k_bwd_outer_split<DK, true>), dim3(P.total_units, slices), dim3(256), 0, st, P);
+      else
+        hipLaunchKernelGGL((k_bwd_outer<T, DK, true>), dim3(P.total_units, slices), dim3(256), 0, st, P);
+      break;
     case 5:
       if constexpr (sizeof(T) == 2)
         hipLaunchKernelGGL((k_bwd_mm1_split<DK>), dim3(P.total_units), dim3(256), 0, st, P);
       else
         hipLaunchKernelGGL((k_bwd_mm1<T, DK>), dim3(P.total_units), dim3(256), 0, st, P);
       break;
-    case 3: hipLaunchKernelGGL((k_bwd_dv<T, DK>), dim3(P.total_units, slices), dim3(256), 0, st, P); break;
+    case 3:
+      if constexpr (sizeof(T) == 2 && DK >= 32)
+        hipLaunchKernelGGL((k_bwd_dv_split<DK>), dim3(P.total_units, slices), dim3(256), 0, st, P);
+      else
+        hipLaunchKernelGGL((k_bwd_dv<T, DK>), dim3(P.total_units, slices), dim3(256), 0, st, P);
+      break;
     default: {
       const int cs = DK < 32 ? 1 : DK / 32;
       hipLaunchKernelGGL((k_bwd_dqdk<T, DK>), dim3(P.total_units, cs), dim3(256), 0, st, P);

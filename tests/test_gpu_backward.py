@@ -7,7 +7,8 @@ norm and the magnitude of its fusion-logit term before cancellation, see
 dx_error), each weight gradient as a whole (max |device - oracle| over
 max |oracle|), at the forward's bars (1e-4 fp32, 2e-2 bf16).  The cases cover
 several chunks with a ragged last chunk in every branch, tail positions past a
-coarse branch's last complete block, chunks 16, 32 and 64, q_scale and gamma
+coarse branch's last complete block, chunks 16, 32 and 64 (bf16: 32 and 64, key widths
+32 to 256), q_scale and gamma
 off their defaults, strong gates, a scale set without a scale-1 branch, a
 single branch (no fusion), a branch whose scale exceeds the sequence, and the
 main configuration's dimensions in bf16, and the full main workload (B = 8,
@@ -136,6 +137,14 @@ def test_fp32_key_width_128_rank_64():
 def test_bf16_main_dimensions():
     cfg = WORKLOADS["main"].cfg
     backward_case(cfg, B=2, L=320, seed=17)
+
+
+@pytest.mark.parametrize("dk,dv,chunk,r,d", [(32, 64, 32, 8, 64), (64, 128, 64, 20, 128), (256, 64, 32, 8, 128)])
+def test_bf16_other_key_widths_and_chunks(dk, dv, chunk, r, d):
+    """bf16 storage at the other key widths, a chunk of 32 (tiles with rows past the
+    chunk), a rank above 16 and a ragged last chunk in every branch."""
+    cfg = _cfg(dtype=BF16, d_model=d, d_k=dk, d_v=dv, chunk=chunk, gate_rank=r, scales=(1, 2, 3), heads=(1, 2, 1))
+    backward_case(cfg, B=2, L=150, seed=43 + dk)
 
 
 def test_bf16_sweep_dimensions_with_gate_bias():
