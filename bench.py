@@ -653,8 +653,8 @@ def summarize_training_profile(d, workload, wl, cmds, out_dir):
                 m = re.search(r"(k_bwd_[A-Za-z0-9_]*?)(?=I[DfL]|E|<|\(|$)", name)
                 if m:
                     short = m.group(1)
-                    if short == "k_bwd_outer":
-                        short += " (dS)" if "Lb1E" in name else " (S)"
+                    if short in ("k_bwd_outer", "k_bwd_outer_split"):
+                        short += " (dS)" if ("Lb1E" in name or "true>" in name) else " (S)"
             brows.append(f"| {short} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                          f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
                          f"{float(r['Percentage']):.1f}% |")

@@ -822,24 +822,35 @@ __global__ __launch_bounds__(256) void k_bwd_dv_split(const BwdParams P) {
 
 // ---- dq and dk of a chunk's 32-channel slice; in-chunk suffix sums of q dq - k dk ----
 // The dense parts (do S_prev^T and v dS_end^T) come from k_bwd_mm1; here the
-// intra-chunk terms with e^{-|b_t - b_i|} (b is non-increasing along the chunk).
-// thread: t = lane, channels c0 + 8 * wave .. + 7
+// intra-chunk terms.  The chunk's positions form four blocks of 16, with e_J =
+// 16 J + 15 the last position of block J.  b is non-increasing along the chunk,
+// so for i in block J and t in a later block, e^{b_t - b_i} = e^{b_t - b_eJ}
+// e^{b_eJ - b_i} with both factors <= 1:
+//   dq_t (block w) += sum_{J<w} e^{b_t - b_eJ} * (D[t, block J] K~J),
+//       K~J_ic = k_ic e^{b_eJ,c - b_ic};
+//   dk_i (block w) += sum_{J>=w} e^{b_eJ - b_i} * (D[block J+1, i]^T Q~J),
+//       Q~J_tc = q_tc e^{b_tc - b_eJ,c}, t in block J + 1;
+// those products run on the matrix cores (fp32); the four diagonal blocks take
+// one factor e^{-|b_t - b_i|} per pair.  Thread elements follow the MFMA
+// accumulator layout: wave w, rows 16 w + 4 (lane / 16) + i, channel tiles ct,
+// channel 16 ct + lane % 16.
 template <typename T, int DK>
 __global__ __launch_bounds__(256) void k_bwd_dqdk(const BwdParams P) {
   constexpr int CS = DK < 32 ? DK : 32;  // channels per block
-  __shared__ __attribute__((aligned(16))) float sm[64 * 65 + 3 * 64 * 33];
-  __shared__ float rs[64 * 33];
+  constexpr int NCT = CS / 16, LDD = 68, LQ = CS + 4, LT = 20, LR = CS + 1;
+  __shared__ __attribute__((aligned(16))) float ds[64 * LDD];   // D[t][i]
+  __shared__ __attribute__((aligned(16))) float qs[64 * LQ];    // q_scale q
+  __shared__ __attribute__((aligned(16))) float ks[64 * LQ];
+  __shared__ __attribute__((aligned(16))) float bs[64 * LQ];
+  __shared__ __attribute__((aligned(16))) float kt[3 * CS * LT];  // K~J^T [J][c][i in block J]
+  __shared__ __attribute__((aligned(16))) float qt[3 * CS * LT];  // Q~J^T [J][c][t in block J + 1]
+  __shared__ float rs[64 * LR];
   const UnitPos u = unit_pos(P, blockIdx.x);
   const BwdBranch& Br = P.br[u.bi];
   const int j0 = u.ch * P.C, c0 = blockIdx.y * CS;
   const int nvalid = min(P.C, Br.n - j0);
   const size_t row0 = (size_t)u.sq * Br.np + j0;
-  const int t = threadIdx.x & 63, cg = threadIdx.x >> 6;
-  const bool live = cg * 8 < CS;  // DK 16: two waves of channels
-  float* ds = sm;                  // D[t][i], stride 65
-  float* qs = sm + 64 * 65;        // q_scale q, stride 33
-  float* ks = qs + 64 * 33;
-  float* bs = ks + 64 * 33;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lr = l & 15, lg = l >> 4;
   const float* D = Br.AD + ((size_t)u.sq * Br.nch + u.ch) * 64 * 64;
   const float* QK = Br.QKi + ((size_t)u.sq * Br.nch + u.ch) * 2 * 64 * DK;
   {
@@ -857,66 +868,105 @@ __global__ __launch_bounds__(256) void k_bwd_dqdk(const BwdParams P) {
     });
     // rows past the chunk keep its last b (the gate adds nothing past the call's end)
     load_tile<64, CS, true>(r3, [&](int tt, int cc) { return Br.lb[(row0 + min(tt, P.C - 1)) * DK + c0 + cc]; });
-    store_tile<64, 64, 65, true, false>(ds, r0);
-    store_tile<64, CS, 33, true, false>(qs, r1);
-    store_tile<64, CS, 33, true, false>(ks, r2);
-    store_tile<64, CS, 33, true, false>(bs, r3);
+    store_tile<64, 64, LDD, true, false>(ds, r0);
+    store_tile<64, CS, LQ, true, false>(qs, r1);
+    store_tile<64, CS, LQ, true, false>(ks, r2);
+    store_tile<64, CS, LQ, true, false>(bs, r3);
   }
-  float aq[8], ak[8], iq[8], ik[8], bt[8], blast[8];
-  const int cl = live ? cg * 8 : 0;
+  // the inter-chunk parts of this thread's elements
+  float aq[NCT][4], ak[NCT][4];
 #pragma unroll
-  for (int v = 0; v < 8; ++v) {
-    aq[v] = QK[t * DK + c0 + cl + v];
-    ak[v] = QK[64 * DK + t * DK + c0 + cl + v];
-    iq[v] = ik[v] = 0.f;
+  for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = 16 * w + 4 * lg + i, c = c0 + 16 * ct + lr;
+      aq[ct][i] = QK[t * DK + c];
+      ak[ct][i] = QK[64 * DK + t * DK + c];
+    }
+  __syncthreads();
+  for (int idx = tid; idx < 3 * CS * 16; idx += 256) {
+    const int J = idx / (CS * 16), rem = idx - J * CS * 16, c = rem >> 4, i = rem & 15;
+    const int tk = 16 * J + i, tq = tk + 16;
+    const float be = bs[(16 * J + 15) * LQ + c];
+    kt[(J * CS + c) * LT + i] = ks[tk * LQ + c] * __expf(be - bs[tk * LQ + c]);
+    qt[(J * CS + c) * LT + i] = qs[tq * LQ + c] * __expf(bs[tq * LQ + c] - be);
   }
   __syncthreads();
+  float bt[NCT][4], iq[NCT][4], ik[NCT][4];
 #pragma unroll
-  for (int v = 0; v < 8; ++v) {
-    bt[v] = bs[t * 33 + cl + v];
-    blast[v] = bs[(P.C - 1) * 33 + cl + v];
-  }
-  if (live) {
-    for (int i = 0; i < 64; ++i) {
-      const float dti = ds[t * 65 + i];  // D_ti, zero unless i <= t
-      const float dit = ds[i * 65 + t];  // D_it, zero unless i >= t
+  for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-      for (int v = 0; v < 8; ++v) {
-        const int cc = cg * 8 + v;
-        const float E = __expf(-fabsf(bt[v] - bs[i * 33 + cc]));
-        iq[v] += dti * ks[i * 33 + cc] * E;
-        ik[v] += dit * qs[i * 33 + cc] * E;
+    for (int i = 0; i < 4; ++i) {
+      bt[ct][i] = bs[(16 * w + 4 * lg + i) * LQ + 16 * ct + lr];
+      iq[ct][i] = ik[ct][i] = 0.f;
+    }
+  // off-diagonal blocks (wave-uniform loops)
+  for (int J = 0; J < w; ++J)
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      const f32x4 p = tile_f32(ds + 16 * w * LDD + 16 * J, LDD, kt + (J * CS + 16 * ct) * LT, LT, 1, zero4());
+      const float be = bs[(16 * J + 15) * LQ + 16 * ct + lr];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) iq[ct][i] += p[i] * __expf(bt[ct][i] - be);
+    }
+  for (int J = w; J < 3; ++J)
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      // A[i][t] = D[16 (J + 1) + t][16 w + i], four positions per lane
+      f32x4 a;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) a[j] = ds[(16 * (J + 1) + 4 * lg + j) * LDD + 16 * w + lr];
+      const f32x4 p = mma_slab<float>(__builtin_bit_cast(u32x4, a),
+                                      ld16(qt + (J * CS + 16 * ct + lr) * LT + 4 * lg), zero4());
+      const float be = bs[(16 * J + 15) * LQ + 16 * ct + lr];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ik[ct][i] += p[i] * __expf(be - bt[ct][i]);
+    }
+  // the diagonal block, pair by pair
+  for (int i2 = 16 * w; i2 < 16 * w + 16; ++i2) {
+    float bi[NCT], ki[NCT], qi[NCT];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      bi[ct] = bs[i2 * LQ + 16 * ct + lr];
+      ki[ct] = ks[i2 * LQ + 16 * ct + lr];
+      qi[ct] = qs[i2 * LQ + 16 * ct + lr];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = 16 * w + 4 * lg + i;
+      const float dti = ds[t * LDD + i2];  // D_t,i2: zero unless i2 <= t
+      const float dit = ds[i2 * LDD + t];  // D_i2,t: zero unless i2 >= t
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) {
+        const float E = __expf(-fabsf(bt[ct][i] - bi[ct]));
+        iq[ct][i] += dti * ki[ct] * E;
+        ik[ct][i] += dit * qi[ct] * E;
       }
     }
   }
-  float dq[8], dk[8];
+  T* dPq = reinterpret_cast<T*>(Br.dP) + (size_t)(u.b * Br.n + j0) * Br.NP + u.head * DK + c0;
 #pragma unroll
-  for (int v = 0; v < 8; ++v) {
-    dq[v] = __expf(bt[v]) * aq[v] + iq[v];
-    dk[v] = __expf(blast[v] - bt[v]) * ak[v] + ik[v];
-    if (t >= nvalid) dq[v] = dk[v] = 0.f;
-  }
-  if (live) {
+  for (int ct = 0; ct < NCT; ++ct) {
+    const float blast = bs[(P.C - 1) * LQ + 16 * ct + lr];
 #pragma unroll
-    for (int v = 0; v < 8; ++v) {
-      const int cc = cg * 8 + v;
-      rs[t * 33 + cc] = qs[t * 33 + cc] * dq[v] - ks[t * 33 + cc] * dk[v];
-    }
-    if (t < nvalid) {
-      const size_t prow = (size_t)(u.b * Br.n + j0 + t) * Br.NP + u.head * DK + c0 + cg * 8;
-      float sq8[8];
-#pragma unroll
-      for (int v = 0; v < 8; ++v) sq8[v] = P.q_scale * dq[v];
-      store8<T>(reinterpret_cast<T*>(Br.dP) + prow, sq8);
-      store8<T>(reinterpret_cast<T*>(Br.dP) + prow + Br.col_k, dk);
+    for (int i = 0; i < 4; ++i) {
+      const int t = 16 * w + 4 * lg + i, c = 16 * ct + lr;
+      float dq = __expf(bt[ct][i]) * aq[ct][i] + iq[ct][i];
+      float dk = __expf(blast - bt[ct][i]) * ak[ct][i] + ik[ct][i];
+      if (t >= nvalid) dq = dk = 0.f;
+      rs[t * LR + c] = qs[t * LQ + c] * dq - ks[t * LQ + c] * dk;
+      if (t < nvalid) {
+        dPq[(size_t)t * Br.NP + c] = from_f32<T>(P.q_scale * dq);
+        dPq[(size_t)t * Br.NP + Br.col_k + c] = from_f32<T>(dk);
+      }
     }
   }
   __syncthreads();
-  if (threadIdx.x < CS) {
-    const int cc = threadIdx.x;
+  if (tid < CS) {
+    const int cc = tid;
     float run = 0.f;
     for (int tt = P.C - 1; tt >= 0; --tt) {
-      run += rs[tt * 33 + cc];
+      run += rs[tt * LR + cc];
       Br.rsum[(row0 + tt) * DK + c0 + cc] = run;
     }
     Br.rtot[((size_t)u.sq * Br.nch + u.ch) * DK + c0 + cc] = run;
