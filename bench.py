@@ -655,6 +655,9 @@ def summarize_training_profile(d, workload, wl, cmds, out_dir):
                     short = m.group(1)
                     if short in ("k_bwd_outer", "k_bwd_outer_split"):
                         short += " (dS)" if ("Lb1E" in name or "true>" in name) else " (S)"
+                if "k_bwd_gemm" in name:
+                    # storage-type output: the pooled inputs' gradient; fp32: dLoss/do
+                    short = "k_bwd_gemm " + ("(dxp)" if ("DF16bDF16b" in name or "IffE" in name) else "(do)")
             brows.append(f"| {short} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                          f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
                          f"{float(r['Percentage']):.1f}% |")

@@ -33,6 +33,7 @@ SOURCES = [
     "k_norm.hip",
     "api_noalloc.hip",
     "k_backward.hip",
+    "k_bwd_gemm.hip",
     "api_backward.cpp",
 ]
 

@@ -26,6 +26,8 @@ hipError_t launch_bwd_mcolsum(const ColsumJobs& J, float* part, hipStream_t st);
 hipError_t launch_bwd_wf_partial(const BwdParams& P, float* partial, int nrb, bool bf16_path, hipStream_t st);
 hipError_t launch_bwd_wf_finish(const float* partial, int nrb, int d, int m, float* out, hipStream_t st);
 hipError_t launch_bwd_splitk_reduce(const float* part, int S, int M, int N, const SplitDst& D, hipStream_t st);
+hipError_t launch_bwd_gemm(const BwdGemm& P, bool bf16_path, bool out_storage, hipStream_t st);
+hipError_t launch_bwd_transpose(const BwdTranspose& P, bool bf16_path, hipStream_t st);
 }  // namespace msgla
 
 using namespace msgla;
@@ -41,14 +43,14 @@ constexpr int BWD_SPLIT_MAX = 16; // K slices of a weight-gradient product
 int colsum_blocks(int rows) { return std::max(1, std::min(BWD_NRB_MAX, (rows + 127) / 128)); }
 
 struct BwdBranchGeom {
-  size_t lb, sg, g1c, Sst, dSt, AD, QKi, rsum, rtot, dob, gpart, dP, dY, Yc, ycat, dxp, yn, ngt;
+  size_t lb, sg, g1c, Sst, dSt, AD, QKi, rsum, rtot, dob, gpart, dP, dY, Yc, ycat, dxp, yn, ngt, WpT;
   int NP;
 };
 
 struct BwdGeom {
   WsGeom W;
   BwdBranchGeom br[MSGLA_MAX_BRANCHES];
-  size_t dz, partial, mcol, mcol_floats, splitk, splitk_floats, total;
+  size_t dz, partial, mcol, mcol_floats, splitk, splitk_floats, Wo, total;
 };
 
 bool bwd_supported(const msgla_config* cfg) { return cfg->d_v % 64 == 0; }
@@ -81,14 +83,17 @@ BwdGeom bwd_geom(const PackGeom& g, int64_t B, int64_t L) {
     o.rtot = take(chunks * g.dk * 4);
     o.dob = take(prow * bg.h * g.dv * 4);
     o.gpart = take((size_t)B * w.nch * 2 * (g.r + 1) * bg.h * g.dk * 4);
-    o.NP = bg.col_g + g.rp;
+    // whole 128-byte K segments for the grouped products (the pad columns are zero)
+    const int seg = 128 / g.es;
+    o.NP = (bg.col_g + g.r + seg - 1) / seg * seg;
     o.dP = take(prow * o.NP * g.es);
     if (bg.s > 1) {
       o.dY = take(prow * g.d * g.es);
       o.Yc = take(prow * g.d * g.es);
     }
     o.ycat = take(prow * bg.h * g.dv * g.es);
-    o.dxp = take(prow * g.d * 4);
+    o.dxp = take(prow * g.d * g.es);
+    o.WpT = take((size_t)g.d * o.NP * g.es);  // Wp^T [d][NP]
     if (g.norm) {
       o.yn = take(rows * g.dv * g.es);         // normalised rows, laid out as y
       o.ngt = take(prow * bg.h * g.dv * 4);    // per-row terms of the gains' gradient
@@ -102,6 +107,7 @@ BwdGeom bwd_geom(const PackGeom& g, int64_t B, int64_t L) {
   // column-sum partials: the gate's dW_g2 and db_g with db_f, or the gains' gradients
   G.mcol_floats = (size_t)BWD_NRB_MAX * std::max(gate_cols + g.m, norm_cols);
   G.mcol = take(G.mcol_floats * 4);
+  G.Wo = take((size_t)g.Ktot * g.d * g.es);  // W_o rows [Ktot][d]
   G.splitk_floats = (size_t)BWD_SPLIT_MAX * mn;
   G.splitk = take(G.splitk_floats * 4);
   G.total = cur;
@@ -170,6 +176,50 @@ bool add_colsum(ColsumJobs& J, size_t& used, size_t cap, const float* src, int r
   J.cb[j + 1] = J.cb[j] + (cols + 63) / 64;
   J.fb[j + 1] = J.fb[j] + (cols + 255) / 256;
   return used <= cap;
+}
+
+// Appends the group C [M][N] (ldc) = A [M][K] B [N][K]^T to a grouped product.
+void add_group(BwdGemm& Gm, const void* A, int lda, const void* Bm, int ldb, void* C, int ldc, int M, int N,
+               int K) {
+  if (M == 0 || N == 0 || K == 0) return;
+  BwdGemmGroup& gg = Gm.g[Gm.ngroups++];
+  gg.A = A;
+  gg.B = Bm;
+  gg.C = C;
+  gg.M = M;
+  gg.N = N;
+  gg.K = K;
+  gg.lda = lda;
+  gg.ldb = ldb;
+  gg.ldc = ldc;
+  gg.tiles_n = (N + 127) / 128;
+  gg.total = (M + 127) / 128 * gg.tiles_n;
+  // XCD x receives the x-th eighth of every group
+  int most = 0;
+  for (int x = 0; x < N_XCD; ++x) {
+    int n = 0;
+    for (int i = 0; i < Gm.ngroups; ++i) {
+      const int T = Gm.g[i].total;
+      n += (int)((int64_t)T * (x + 1) / N_XCD) - (int)((int64_t)T * x / N_XCD);
+    }
+    most = std::max(most, n);
+  }
+  Gm.per_xcd = most;
+}
+
+// Appends out [C][Rp] (ldo) = in [R][C]^T (ldi), rows R .. Rp of out zero.
+void add_transpose(BwdTranspose& T, const void* in, int R, int C, int ldi, void* out, int Rp, int ldo) {
+  BwdTransposeJob& j = T.j[T.njobs++];
+  j.in = in;
+  j.out = out;
+  j.R = R;
+  j.C = C;
+  j.Rp = Rp;
+  j.ldi = ldi;
+  j.ldo = ldo;
+  j.tile_begin = T.total_tiles;
+  j.tiles_c = (C + 63) / 64;
+  T.total_tiles += (Rp + 63) / 64 * j.tiles_c;
 }
 
 SplitDst one_dst(float* p, int n) {
@@ -312,7 +362,7 @@ msgla_status msgla_backward(const msgla_config* cfg, const void* packed, const v
     Br.dP = at<char>(workspace, o.dP);
     Br.dY = bg.s > 1 ? at<char>(workspace, o.dY) : nullptr;
     Br.ycat = at<char>(workspace, o.ycat);
-    Br.dxp = at<float>(workspace, o.dxp);
+    Br.dxp = at<char>(workspace, o.dxp);
     if (bg.s == 1) P.fine = i;
   }
   P.total_units = units;
@@ -322,16 +372,32 @@ msgla_status msgla_backward(const msgla_config* cfg, const void* packed, const v
   float* sk = at<float>(workspace, G.splitk);
   const char* WoT = at<char>(packed, g.off_WoT);
 
+  // ---- the weights as the grouped products read them: W_o rows, Wp^T ----
+  {
+    BwdTranspose T{};
+    add_transpose(T, WoT, g.d, g.Ktot, g.Ktot, at<char>(workspace, G.Wo), g.d, g.d);
+    for (int i = 0; i < g.m; ++i)
+      if (P.br[i].n > 0)
+        add_transpose(T, at<char>(packed, g.br[i].off_Wp), g.br[i].col_g + g.r, g.d, g.d,
+                      at<char>(workspace, G.br[i].WpT), P.br[i].NP, P.br[i].NP);
+    HIP_TRY(launch_bwd_transpose(T, g.bf16, st));
+  }
+  const char* Wo = at<char>(workspace, G.Wo);
+
   // ---- fusion, hold and the output projections ----
-  for (int i = 0; i < g.m; ++i) {
-    const BwdBranch& Br = P.br[i];
-    const int hdv = Br.h * g.dv;
-    if (Br.n == 0) continue;
-    if (Br.s == 1)  // G = dO W_o^T (scaled by w_1 in k_bwd_out)
-      BLAS_TRY(gemm_rm(hb, false, false, (int)B * Br.n, hdv, g.d, dout, ST, g.d,
-                       WoT + (size_t)g.br[i].ko * g.es, ST, g.Ktot, Br.dob, hdv));
-    else
-      HIP_TRY(launch_bwd_hold(P, i, g.bf16, st));
+  // dY of the coarse branches, then every branch's dLoss/do = dO W_o^T (scale 1,
+  // scaled by w_1 in k_bwd_out) or dY W_o^T as one grouped product
+  for (int i = 0; i < g.m; ++i)
+    if (P.br[i].n > 0 && P.br[i].s > 1) HIP_TRY(launch_bwd_hold(P, i, g.bf16, st));
+  {
+    BwdGemm Gm{};
+    for (int i = 0; i < g.m; ++i) {
+      const BwdBranch& Br = P.br[i];
+      const int hdv = Br.h * g.dv;
+      add_group(Gm, Br.s == 1 ? dout : Br.dY, g.d, Wo + (size_t)g.br[i].ko * g.d * g.es, g.d, Br.dob, hdv,
+                (int)B * Br.n, hdv, g.d);
+    }
+    HIP_TRY(launch_bwd_gemm(Gm, g.bf16, false, st));
   }
   HIP_TRY(launch_bwd_out(P, g.bf16, st));
   for (int i = 0; i < g.m; ++i) {
@@ -342,9 +408,6 @@ msgla_status msgla_backward(const msgla_config* cfg, const void* packed, const v
       continue;
     }
     const void* dYi = Br.s == 1 ? dout : Br.dY;
-    if (Br.s > 1)
-      BLAS_TRY(gemm_rm(hb, false, false, rows, hdv, g.d, dYi, ST, g.d, WoT + (size_t)g.br[i].ko * g.es, ST,
-                       g.Ktot, Br.dob, hdv));
     BLAS_TRY(gemm_wgrad(hb, hdv, g.d, rows, Br.ycat, ST, hdv, dYi, ST, g.d, one_dst(grads->br[i].W_o, g.d), sk,
                         G.splitk_floats, g.es, st));
   }
@@ -399,6 +462,18 @@ msgla_status msgla_backward(const msgla_config* cfg, const void* packed, const v
   }
 
   // ---- the input projections and the pooling ----
+  // dLoss/d(pooled input) of every branch as one grouped product dP Wp^T, then
+  // the weight gradients of the q | k | v | x W_g1 columns, one product per branch
+  if (mask && P.fine >= 0 && P.br[P.fine].n > 0) HIP_TRY(launch_bwd_mask_rows(P, P.fine, g.bf16, st));
+  {
+    BwdGemm Gm{};
+    for (int i = 0; i < g.m; ++i) {
+      const BwdBranch& Br = P.br[i];
+      add_group(Gm, Br.dP, Br.NP, at<char>(workspace, G.br[i].WpT), Br.NP, const_cast<void*>(Br.dxp), g.d,
+                (int)B * Br.n, g.d, Br.NP);
+    }
+    HIP_TRY(launch_bwd_gemm(Gm, g.bf16, true, st));
+  }
   for (int i = 0; i < g.m; ++i) {
     const BwdBranch& Br = P.br[i];
     const BranchGeom& bg = g.br[i];
@@ -411,11 +486,8 @@ msgla_status msgla_backward(const msgla_config* cfg, const void* packed, const v
       HIP_TRY(fill_zero(gr.W_g1, (size_t)g.d * g.r * 4, st));
       continue;
     }
-    if (bg.s == 1 && mask) HIP_TRY(launch_bwd_mask_rows(P, i, g.bf16, st));
     const char* dP = static_cast<const char*>(Br.dP);
     const void* xp = bg.s == 1 ? x : static_cast<const void*>(at<char>(workspace, W.br[i].xp));
-    BLAS_TRY(gemm_rm(hb, false, false, rows, g.d, bg.col_g + g.r, dP, ST, Br.NP, at<char>(packed, bg.off_Wp), ST,
-                     g.d, const_cast<float*>(Br.dxp), g.d));
     // one product for the q | k | v | x W_g1 columns, scattered into the four gradients
     SplitDst dw{};
     dw.n = 4;

@@ -146,19 +146,22 @@ __device__ __forceinline__ f32x4 tile_f32(const float* a, int lda, const float* 
 
 // ---- gate recompute: b (chunk-local cumulative log alpha), sigmoid(-z)/gamma, g1 ----
 // One workgroup of d_k threads per (branch, b, head, chunk); thread = key channel.
-// Dynamic LDS: the chunk's block means g1s [C][r] (at least 256 floats: the part
-// totals reuse them), the head's W_g2 slice [r][d_k], and log alpha [C][d_k].
+// Dynamic LDS: the chunk's block means g1s [C][RP] (ranks >= r zero; at least 256
+// floats: the part totals reuse them), the head's W_g2 slice [r][d_k], and
+// log alpha [C][d_k].  With E = e^{-|z|}: log alpha = (min(z, 0) - log1p(E)) / gamma
+// and sigmoid(-z) = (z > 0 ? E : 1) / (1 + E).
+template <int RP>
 __global__ __launch_bounds__(256) void k_bwd_gate(const BwdParams P) {
-  extern __shared__ float gate_lds[];
+  extern __shared__ __attribute__((aligned(16))) float gate_lds[];
   float* g1s = gate_lds;
-  float* w2s = gate_lds + max(P.C * P.r, 256);
+  float* w2s = gate_lds + max(P.C * RP, 256);
   const UnitPos u = unit_pos(P, blockIdx.x);
   const BwdBranch& Br = P.br[u.bi];
   const int j0 = u.ch * P.C;
   const int hdk = Br.h * P.dk;
   // the block means of x W_g1 (Eq. (8): over the block's tokens when masked);
   // four entries per thread and round, their rows' loads issued together
-  for (int base = 0; base < P.C * P.r; base += 4 * 256) {
+  for (int base = 0; base < P.C * RP; base += 4 * 256) {
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
     int cnt[4] = {0, 0, 0, 0};
     for (int v0 = 0; v0 < Br.s; v0 += 4) {
@@ -166,8 +169,8 @@ __global__ __launch_bounds__(256) void k_bwd_gate(const BwdParams P) {
       bool tok[4][4];
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const int idx = min(base + threadIdx.x + 256 * k, P.C * P.r - 1);
-        const int jj = idx / P.r, rr = idx - jj * P.r;
+        const int idx = min(base + threadIdx.x + 256 * k, P.C * RP - 1);
+        const int jj = idx / RP, rr = min(idx - jj * RP, P.r - 1);
         const int j = min(j0 + jj, Br.n - 1);
         const size_t t0 = (size_t)u.b * P.L + (size_t)j * Br.s;
 #pragma unroll
@@ -188,12 +191,13 @@ __global__ __launch_bounds__(256) void k_bwd_gate(const BwdParams P) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int idx = base + threadIdx.x + 256 * k;
-      if (idx >= P.C * P.r) continue;
-      const int jj = idx / P.r, rr = idx - jj * P.r;
+      if (idx >= P.C * RP) continue;
+      const int jj = idx / RP, rr = idx - jj * RP;
       const int j = j0 + jj;
-      const float mean = j < Br.n ? acc[k] / (float)(P.mask ? max(cnt[k], 1) : Br.s) : 0.f;
-      if (j < Br.n && u.head == 0) Br.g1c[((size_t)u.b * Br.n + j) * P.rp + rr] = mean;
-      g1s[jj * P.r + rr] = mean;
+      const float mean =
+          (j < Br.n && rr < P.r) ? acc[k] / (float)(P.mask ? max(cnt[k], 1) : Br.s) : 0.f;
+      if (j < Br.n && rr < P.r && u.head == 0) Br.g1c[((size_t)u.b * Br.n + j) * P.rp + rr] = mean;
+      g1s[jj * RP + rr] = mean;
     }
   }
   for (int base = 0; base < P.r * P.dk; base += 8 * 256) {
@@ -218,16 +222,27 @@ __global__ __launch_bounds__(256) void k_bwd_gate(const BwdParams P) {
   const int c = threadIdx.x % P.dk, part = threadIdx.x / P.dk;
   const int len = (P.C + parts - 1) / parts, jb = part * len, je = min(P.C, jb + len);
   const float bgc = Br.bg[u.head * P.dk + c];
+  float w2r[RP];
+#pragma unroll
+  for (int rr = 0; rr < RP; ++rr) w2r[rr] = rr < P.r ? w2s[rr * P.dk + c] : 0.f;
   float* las = w2s + P.r * P.dk;  // log alpha [C][d_k]
   float bsum = 0.f;
+#pragma unroll 4
   for (int jj = jb; jj < je; ++jj) {
     const bool valid = j0 + jj < Br.n;
     float z = bgc;
-    for (int rr = 0; rr < P.r; ++rr) z += g1s[jj * P.r + rr] * w2s[rr * P.dk + c];
-    const float la = valid ? logsigmoid_f(z) * P.inv_gamma : 0.f;
+#pragma unroll
+    for (int q = 0; q < RP / 4; ++q) {
+      float g4[4];
+      unpack16<float>(ld16(g1s + jj * RP + 4 * q), g4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) z += g4[i] * w2r[4 * q + i];
+    }
+    const float E = __expf(-fabsf(z)), L1 = log1pf(E);
+    const float la = valid ? (fminf(z, 0.f) - L1) * P.inv_gamma : 0.f;
     las[jj * P.dk + c] = la;
     bsum += la;
-    Br.sg[((size_t)u.sq * Br.np + j0 + jj) * P.dk + c] = valid ? __expf(logsigmoid_f(-z)) * P.inv_gamma : 0.f;
+    Br.sg[((size_t)u.sq * Br.np + j0 + jj) * P.dk + c] = valid ? (z > 0.f ? E : 1.f) / (1.f + E) * P.inv_gamma : 0.f;
   }
   __syncthreads();  // the block means are no longer needed: their space takes the part totals
   float* tot = g1s;
@@ -1106,6 +1121,13 @@ __global__ __launch_bounds__(256) void k_bwd_gate_grads(const BwdParams P) {
       if (t < nvalid && rr < r) dP[(row0 + t) * Br.NP + Br.col_g + rr] = from_f32<T>(acc[k][i]);
     }
   }
+  // the columns past the rank (padding to whole K segments of the input-gradient
+  // product) are zero
+  const int pad0 = Br.col_g + r, npad = Br.NP - pad0;
+  for (int idx = tid; idx < nvalid * npad; idx += 256) {
+    const int t = idx / npad;
+    dP[(row0 + t) * Br.NP + pad0 + (idx - t * npad)] = from_f32<T>(0.f);
+  }
 }
 
 // ---- fusion and hold, per position (one wave each) ----
@@ -1230,7 +1252,7 @@ __global__ __launch_bounds__(256) void k_bwd_dx(const BwdParams P) {
       const BwdBranch& Br = P.br[i];
       if (t >= Br.n * Br.s) continue;
       const int j = t / Br.s;
-      const float* src = Br.dxp + ((size_t)b * Br.n + j) * P.d + col;
+      const T* src = reinterpret_cast<const T*>(Br.dxp) + ((size_t)b * Br.n + j) * P.d + col;
       // Eq. (8): the block mean is sum M x / max(1, sum M)
       float inv = 1.f / (float)Br.s;
       if (Mrow) {
@@ -1239,13 +1261,10 @@ __global__ __launch_bounds__(256) void k_bwd_dx(const BwdParams P) {
         for (int v = j * Br.s; v < (j + 1) * Br.s; ++v) cnt += Mrow[v] != 0;
         inv = 1.f / (float)max(cnt, 1);
       }
-      const f32x4 a = *reinterpret_cast<const f32x4*>(src);
-      const f32x4 c = *reinterpret_cast<const f32x4*>(src + 4);
+      float a[8];
+      load8<T>(src, a);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        acc[q] += a[q] * inv;
-        acc[q + 4] += c[q] * inv;
-      }
+      for (int q = 0; q < 8; ++q) acc[q] += a[q] * inv;
     }
     if (P.m > 1) {
       for (int i = 0; i < P.m; ++i) {
@@ -1450,8 +1469,10 @@ hipError_t launch_bwd_chunk(const BwdParams& P, int which, bool bf16_path, hipSt
 hipError_t launch_bwd_gate(const BwdParams& P, hipStream_t st) {
   if (P.total_units == 0) return hipSuccess;
   // block means, W_g2 slice, log alpha; the part totals (256 floats) reuse the first
-  const size_t lds = (size_t)(std::max(P.C * P.r, 256) + P.r * P.dk + P.C * P.dk) * sizeof(float);
-  hipLaunchKernelGGL(k_bwd_gate, dim3(P.total_units), dim3(256), lds, st, P);
+  if (P.rp != 16 && P.rp != 64) return hipErrorInvalidValue;
+  const size_t lds = (size_t)(std::max(P.C * P.rp, 256) + P.r * P.dk + P.C * P.dk) * sizeof(float);
+  if (P.rp == 16) hipLaunchKernelGGL(k_bwd_gate<16>, dim3(P.total_units), dim3(256), lds, st, P);
+  else hipLaunchKernelGGL(k_bwd_gate<64>, dim3(P.total_units), dim3(256), lds, st, P);
   return hipGetLastError();
 }
 

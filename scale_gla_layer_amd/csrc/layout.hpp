@@ -261,10 +261,12 @@ struct K3Params {
 //                                            sums of g1 dz (rows 0..r-1) and of dz
 //                                            (row r), dz = dLoss/d(gate pre-activation)
 //   dP          [B n][NP]              T     dLoss/d[q | k | v | x W_g1] columns
-//                                            (q_scale folded into q), NP = col_g + rp
+//                                            (q_scale folded into q); NP = col_g + r
+//                                            rounded up to whole 128-byte segments,
+//                                            the columns past col_g + r zero
 //   dY, Yc      [B n][d]               T     coarse branches: dLoss/dY and Y = y W_o
 //   ycat        [B n][h d_v]           T     y rows position-major (scale 1: w_1 y)
-//   dxp         [B n][d]               fp32  dLoss/d(pooled input)
+//   dxp         [B n][d]               T     dLoss/d(pooled input)
 // plus dz [B L][8] fp32 (dLoss/d fusion logits) and reduction partials.
 struct BwdBranch {
   int s, h, n, nch, np;
@@ -297,7 +299,7 @@ struct BwdBranch {
   void* dP;
   void* dY;
   void* ycat;
-  const float* dxp;
+  const void* dxp;
 };
 
 struct BwdParams {
@@ -327,6 +329,34 @@ struct ColsumJobs {
   int cb[MAX + 1];   // first 64-column block of each job (partial pass)
   int fb[MAX + 1];   // first 256-column block of each job (finishing pass)
   size_t pofs[MAX];
+};
+
+// Grouped products on the matrix cores (k_bwd_gemm): per group g,
+// C_g [M][N] (ldc) = A_g [M][K] B_g [N][K]^T, A and B in the storage type
+// with K contiguous (lda, ldb elements); K a multiple of 128 bytes of elements.
+struct BwdGemmGroup {
+  const void* A;
+  const void* B;
+  void* C;                  // fp32 or the storage type (per launch)
+  int M, N, K, lda, ldb, ldc;
+  int total, tiles_n;       // 128 x 128 tiles of the group, column tiles
+};
+struct BwdGemm {
+  int ngroups, per_xcd;     // per_xcd: the most tiles any XCD receives
+  BwdGemmGroup g[MSGLA_MAX_BRANCHES];
+};
+
+// Transposes with zero padding (k_bwd_transpose): out[c][r] (ldo) = in[r][c]
+// (ldi) for r < R, c < C; out[c][r] = 0 for R <= r < Rp.
+struct BwdTransposeJob {
+  const void* in;
+  void* out;
+  int R, C, Rp, ldi, ldo;
+  int tile_begin, tiles_c;  // first 64 x 64 tile, tiles along C
+};
+struct BwdTranspose {
+  int njobs, total_tiles;
+  BwdTransposeJob j[MSGLA_MAX_BRANCHES + 1];
 };
 
 // Destinations of a split-K weight-gradient product (k_bwd_splitk_reduce).

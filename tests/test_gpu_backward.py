@@ -171,6 +171,14 @@ def test_fp32_normalised():
     backward_case(_cfg(norm=True, scales=(1, 2, 3), heads=(1, 2, 1)), B=2, L=101, seed=37)
 
 
+def test_fp32_normalised_and_masked():
+    """The normalisation with the token mask: a masked scale-1 position has o = 0 and
+    r = sqrt(eps), so its dLoss/do is large; every term it enters must carry q = 0."""
+    B, L = 2, 133
+    M = make_mask(B, L, seed=47, hole_prob=0.15)
+    backward_case(_cfg(norm=True, scales=(1, 2, 3), heads=(1, 2, 1)), B=B, L=L, seed=47, M=M)
+
+
 def test_bf16_main_dimensions_normalised_and_masked():
     B, L = 2, 200
     cfg = dataclasses.replace(WORKLOADS["main"].cfg, norm=True)

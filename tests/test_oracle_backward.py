@@ -185,3 +185,31 @@ def test_planted_mistakes_fail_the_finite_difference_check(mistake, monkeypatch)
         errs.append(float(np.abs(_grad_of(grads, i, key) - want).max()) / max(1.0, float(np.abs(want).max())))
     errs.append(float(np.abs(dX - _fd(f, X)).max()))
     assert max(errs) > 1e-3, f"planted mistake {mistake} not detected: {max(errs):.2e}"
+
+
+def test_normalised_query_and_key_gradients_are_sensitive_to_the_stored_output(monkeypatch):
+    """The bar of the bf16 normalised backward: rounding only the GLA output o to
+    bf16 (its storage type in the bf16 layer) inside the normalisation moves the
+    exact gradients of the scale-1 branch's W_q and W_k by about 1e-2 of their
+    largest entry, while W_v moves by far less.  The normalisation's backward
+    removes the component of dLoss/do along o, and dq = do S^T nearly cancels
+    when do is orthogonal to o = q S; so these two gradients carry o's storage
+    rounding amplified, which bounds what a bf16 layer can reach against the
+    fp64 function (main dimensions, B = 2, L = 200)."""
+    from scale_gla_layer_amd.config import WORKLOADS
+    from scale_gla_layer_amd.synth import make_inputs, round_to
+    cfg = dataclasses.replace(WORKLOADS["main"].cfg, norm=True)
+    X, W = make_inputs(cfg, 2, 200, seed=41)
+    dO = round_to(np.random.default_rng(1041).normal(0.0, 1.0, X.shape), cfg.dtype)
+    _, exact = orc.layer_backward(X, W, cfg, dO)
+    fwd, bwd = orc.rms_norm_heads, orc.rms_norm_heads_backward
+    monkeypatch.setattr(orc, "rms_norm_heads", lambda o, g: fwd(round_to(o, "bf16"), g))
+    monkeypatch.setattr(orc, "rms_norm_heads_backward", lambda o, g, dy: bwd(round_to(o, "bf16"), g, dy))
+    _, rounded = orc.layer_backward(X, W, cfg, dO)
+
+    def moved(key):
+        a, b = rounded["branches"][0][key], exact["branches"][0][key]
+        return float(np.abs(a - b).max() / np.abs(b).max())
+
+    assert 5e-3 < moved("W_q") < 2e-2 and 5e-3 < moved("W_k") < 2e-2
+    assert moved("W_v") < 1e-3
