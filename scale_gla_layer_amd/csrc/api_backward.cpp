@@ -16,6 +16,7 @@ namespace msgla {
 hipError_t launch_bwd_gate(const BwdParams& P, hipStream_t st);
 hipError_t launch_bwd_chunk(const BwdParams& P, int which, bool bf16_path, hipStream_t st);
 hipError_t launch_bwd_scan(const BwdParams& P, bool rev, hipStream_t st);
+hipError_t launch_bwd_walk(const BwdParams& P, bool rev, hipStream_t st);
 hipError_t launch_bwd_gate_grads(const BwdParams& P, bool bf16_path, hipStream_t st);
 hipError_t launch_bwd_out(const BwdParams& P, bool bf16_path, hipStream_t st);
 hipError_t launch_bwd_hold(const BwdParams& P, int bi, bool bf16_path, hipStream_t st);
@@ -317,7 +318,7 @@ msgla_status msgla_backward(const msgla_config* cfg, const void* packed, const v
                                                           (size_t)g.br[g.carrier].col_z * g.d * g.es)
                                    : at<char>(packed, g.off_Wz))
                  : nullptr;
-  int units = 0, gunits = 0;
+  int units = 0, gunits = 0, wunits = 0;
   for (int i = 0; i < g.m; ++i) {
     const BranchGeom& bg = g.br[i];
     const WsBranch& wb = W.br[i];
@@ -332,6 +333,8 @@ msgla_status msgla_backward(const msgla_config* cfg, const void* packed, const v
     units += (int)B * bg.h * wb.nch;
     Br.gg_begin = gunits;
     gunits += (int)B * wb.nch;
+    Br.walk_begin = wunits;
+    if (wb.nch > 0) wunits += (int)B * bg.h * (g.dv / 64) * (g.dk / 32);
     Br.col_k = bg.col_k;
     Br.col_v = bg.col_v;
     Br.col_g = bg.col_g;
@@ -367,6 +370,7 @@ msgla_status msgla_backward(const msgla_config* cfg, const void* packed, const v
   }
   P.total_units = units;
   P.gate_units = gunits;
+  P.walk_units = wunits;
   float* partial = at<float>(workspace, G.partial);
   float* mcol = at<float>(workspace, G.mcol);
   float* sk = at<float>(workspace, G.splitk);
@@ -431,10 +435,17 @@ msgla_status msgla_backward(const msgla_config* cfg, const void* packed, const v
 
   // ---- the chunkwise recurrence and the gate ----
   HIP_TRY(launch_bwd_gate(P, st));
-  HIP_TRY(launch_bwd_chunk(P, 0, g.bf16, st));
-  HIP_TRY(launch_bwd_scan(P, false, st));
-  HIP_TRY(launch_bwd_chunk(P, 1, g.bf16, st));
-  HIP_TRY(launch_bwd_scan(P, true, st));
+  if (g.bf16) {
+    // the states entering each chunk and the state gradients reaching each chunk's end
+    HIP_TRY(launch_bwd_walk(P, false, st));
+    HIP_TRY(launch_bwd_walk(P, true, st));
+  } else {
+    // the same as per-chunk increments and scans over the chunks
+    HIP_TRY(launch_bwd_chunk(P, 0, g.bf16, st));
+    HIP_TRY(launch_bwd_scan(P, false, st));
+    HIP_TRY(launch_bwd_chunk(P, 1, g.bf16, st));
+    HIP_TRY(launch_bwd_scan(P, true, st));
+  }
   HIP_TRY(launch_bwd_chunk(P, 5, g.bf16, st));
   HIP_TRY(launch_bwd_chunk(P, 3, g.bf16, st));
   HIP_TRY(launch_bwd_chunk(P, 4, g.bf16, st));

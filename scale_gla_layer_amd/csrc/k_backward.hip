@@ -31,6 +31,7 @@
 //  plus the fusion logits' dz_t W_f^T                                   (k_bwd_dx).
 // The plain products around these (dY W_o^T, the weight gradients and the
 // pooled inputs' gradient) are left to the host's GEMM calls.
+#include "async_copy.hpp"
 #include "device_common.hpp"
 #include "layout.hpp"
 
@@ -54,6 +55,18 @@ __device__ __forceinline__ UnitPos unit_pos(const BwdParams& P, int unit) {
   u.b = u.sq / Br.h;
   u.head = u.sq - u.b * Br.h;
   return u;
+}
+
+// The work item (unit, slice) of this block when the launch has 8 * per blocks
+// for nwork = units * inner items, unit-major: each XCD (block id mod 8) takes
+// one contiguous range of items, so the slices of one unit, which read its
+// operands, share that XCD's L2.  False for blocks past the end.
+__device__ __forceinline__ bool xcd_item(int nwork, int inner, int& unit, int& slice) {
+  const int wk = remap_xcd(blockIdx.x, (nwork + N_XCD - 1) / N_XCD);
+  if (wk >= nwork) return false;
+  unit = wk / inner;
+  slice = wk - unit * inner;
+  return true;
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
@@ -266,9 +279,11 @@ __global__ __launch_bounds__(256) void k_bwd_outer(const BwdParams P) {
   constexpr int LD = 68, NT = DK / 16;
   __shared__ __attribute__((aligned(16))) float xt[DK * LD];
   __shared__ __attribute__((aligned(16))) float yt[64 * LD];
-  const UnitPos u = unit_pos(P, blockIdx.x);
+  int unit, slice;
+  if (!xcd_item(P.total_units * (P.dv / 64), P.dv / 64, unit, slice)) return;
+  const UnitPos u = unit_pos(P, unit);
   const BwdBranch& Br = P.br[u.bi];
-  const int j0 = u.ch * P.C, e0 = blockIdx.y * 64;
+  const int j0 = u.ch * P.C, e0 = slice * 64;
   const int nvalid = min(P.C, Br.n - j0);
   const size_t row0 = (size_t)u.sq * Br.np + j0;
   {
@@ -343,9 +358,11 @@ __global__ __launch_bounds__(256) void k_bwd_outer_split(const BwdParams P) {
   constexpr int GPT = (8 + TPC - 1) / TPC;   // 8-position groups per thread
   __shared__ __attribute__((aligned(16))) bf16 xh[DK * LB], xl[DK * LB];       // (X * F)^T [c][t]
   __shared__ __attribute__((aligned(16))) bf16 yh[64 * LB], yl[(REV ? 64 : 1) * LB];  // Y^T [e][t]
-  const UnitPos u = unit_pos(P, blockIdx.x);
+  int unit, slice;
+  if (!xcd_item(P.total_units * (P.dv / 64), P.dv / 64, unit, slice)) return;
+  const UnitPos u = unit_pos(P, unit);
   const BwdBranch& Br = P.br[u.bi];
-  const int j0 = u.ch * P.C, e0 = blockIdx.y * 64;
+  const int j0 = u.ch * P.C, e0 = slice * 64;
   const int nvalid = min(P.C, Br.n - j0);
   const size_t row0 = (size_t)u.sq * Br.np + j0;
   const int tid = threadIdx.x;
@@ -425,6 +442,173 @@ __global__ __launch_bounds__(256) void k_bwd_outer_split(const BwdParams P) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       out[(base + 16 * ct + 4 * (l >> 4) + i) * P.dv + e0 + 16 * w + (l & 15)] = acc[ct][i];
+}
+
+// ---- chunk states by a walk over the chunks (bf16 storage) ----
+// REV = false: Sst[c] = S entering chunk c:  S(0) = 0,    S(c+1) = Diag(lambda_c) S(c) + k-hat_c^T V_c;
+// REV = true:  dSt[c] = G reaching c's end:  G(last) = 0, G(c-1) = Diag(lambda_c) G(c) + q-tilde_c^T dO_c;
+// lambda_c = e^{b_last} of chunk c per key channel (the same values the increments
+// and scans of the fp32 layer produce).  One workgroup per (branch, b, head,
+// 64-column slice of d_v, 32-channel part of d_k) walks its sequence's chunks
+// and keeps its 32 x 64 slice of the state in the accumulators of its four
+// waves (wave w: columns 16 w .. 16 w + 15, both 16-channel tiles).  Per chunk
+// it writes the slice, scales its rows by lambda and adds the chunk's increment
+// on bf16 matrix cores (hi + lo operands, see k_bwd_mm1_split); the operands of
+// the next two chunks are loaded while the current one is multiplied (the
+// barriers wait for LDS only).  Block ids go round-robin over the XCDs, which
+// spreads the long walks of the scale-1 branch over all of them.
+template <int DK, bool REV, int CP>
+__global__ __launch_bounds__(256) void k_bwd_walk(const BwdParams P) {
+  constexpr int LB = 64 + 8, NCP = DK / CP, NCT = CP / 16, XG = CP * 64 / 8 / 256;
+  __shared__ __attribute__((aligned(16))) bf16 xh[CP * LB], xl[CP * LB];              // (X * F)^T [c][t]
+  __shared__ __attribute__((aligned(16))) bf16 yh[64 * LB], yl[(REV ? 64 : 1) * LB];  // Y^T [e][t]
+  const int wunit = blockIdx.x;
+  if (wunit >= P.walk_units) return;
+  int bi = 0;
+  while (bi + 1 < P.nbranch && wunit >= P.br[bi + 1].walk_begin) ++bi;
+  const BwdBranch& Br = P.br[bi];
+  const int ns = P.dv / 64;
+  int local = wunit - Br.walk_begin;
+  const int cp = local % NCP;
+  local /= NCP;
+  const int es = local % ns, sq = local / ns;
+  const int c0 = CP * cp, e0 = 64 * es;
+  const int b = sq / Br.h, head = sq - b * Br.h;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const int nch = Br.nch;
+  // staging pieces.  X: channel xc, positions 8 xg .. 8 xg + 7.  Y: v^T row
+  // e = tid / 4 with positions 8 (tid % 4) and + 32 (forward), or dLoss/do
+  // column e = tid % 64 with positions 8 (tid / 64) and + 32 (reverse)
+  const int xc = tid % CP, xg0 = tid / CP;
+  struct Regs {
+    float xv[XG][8], lv[XG][8], lastb, lam[NCT][4];
+    float dv8[2][8];
+    u32x4 vv[2];
+  };
+  auto load = [&](Regs& R, int ch) {
+    const int j0 = ch * P.C, nvalid = min(P.C, Br.n - j0);
+    const size_t row0 = (size_t)sq * Br.np + j0;
+#pragma unroll
+    for (int gi = 0; gi < XG; ++gi) {
+      const int xg = xg0 + (256 / CP) * gi;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const size_t o = (row0 + min(8 * xg + k, nvalid - 1)) * DK + c0 + xc;
+        R.xv[gi][k] = REV ? Br.q[o] : Br.k[o];
+        R.lv[gi][k] = Br.lb[o];
+      }
+    }
+    R.lastb = Br.lb[(row0 + P.C - 1) * DK + c0 + xc];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) R.lam[ct][i] = Br.lb[(row0 + P.C - 1) * DK + c0 + 16 * ct + 4 * (l >> 4) + i];
+    if constexpr (REV) {
+      const float* src = Br.dob + ((size_t)(b * Br.n + j0) * Br.h + head) * P.dv + e0 + (tid & 63);
+      const size_t ld = (size_t)Br.h * P.dv;
+#pragma unroll
+      for (int gi = 0; gi < 2; ++gi) {
+        const int g = (tid >> 6) + 4 * gi;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) R.dv8[gi][k] = src[(size_t)min(8 * g + k, nvalid - 1) * ld];
+      }
+    } else {
+      const bf16* vT = reinterpret_cast<const bf16*>(Br.vT) + (((size_t)sq * nch + ch) * P.dv + e0 + (tid >> 2)) * P.C;
+#pragma unroll
+      for (int gi = 0; gi < 2; ++gi) {
+        const int g = (tid & 3) + 4 * gi;
+        R.vv[gi] = ld16(vT + (8 * g < P.C ? 8 * g : 0));
+      }
+    }
+  };
+  auto stage = [&](Regs& R, int ch) {
+    const int nvalid = min(P.C, Br.n - ch * P.C);
+    u32x4 hi, lo;
+#pragma unroll
+    for (int gi = 0; gi < XG; ++gi) {
+      const int xg = xg0 + (256 / CP) * gi;
+      float f[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const float v = REV ? P.q_scale * R.xv[gi][k] * __expf(R.lv[gi][k]) : R.xv[gi][k] * __expf(R.lastb - R.lv[gi][k]);
+        f[k] = 8 * xg + k < nvalid ? v : 0.f;
+      }
+      split_bf16(f, hi, lo);
+      st16(xh + xc * LB + 8 * xg, hi);
+      st16(xl + xc * LB + 8 * xg, lo);
+    }
+    if constexpr (REV) {
+#pragma unroll
+      for (int gi = 0; gi < 2; ++gi) {
+        const int g = (tid >> 6) + 4 * gi;
+        float d8[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) d8[k] = 8 * g + k < nvalid ? R.dv8[gi][k] : 0.f;
+        split_bf16(d8, hi, lo);
+        st16(yh + (tid & 63) * LB + 8 * g, hi);
+        st16(yl + (tid & 63) * LB + 8 * g, lo);
+      }
+    } else {
+#pragma unroll
+      for (int gi = 0; gi < 2; ++gi) {
+        const int g = (tid & 3) + 4 * gi;
+        u32x4 v = R.vv[gi];
+        if (8 * g + 8 > nvalid) {  // a position past the call's end (or the chunk) in this piece
+          float v8[8];
+          unpack16<bf16>(v, v8);
+#pragma unroll
+          for (int k = 0; k < 8; ++k) v8[k] = 8 * g + k < nvalid ? v8[k] : 0.f;
+          v = pack16<bf16>(v8);
+        }
+        st16(yh + (tid >> 2) * LB + 8 * g, v);
+      }
+    }
+  };
+  float* out = REV ? Br.dSt : Br.Sst;
+  f32x4 acc[NCT];
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) acc[ct] = zero4();
+  auto chunk = [&](int it) { return REV ? nch - 1 - it : it; };
+  // one walk step: the operands of step it (in R) go to LDS and R takes those
+  // of step it + 2
+  auto step = [&](Regs& R, int it) {
+    const int ch = chunk(it);
+    float lc[NCT][4];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) lc[ct][i] = __expf(R.lam[ct][i]);
+    lds_barrier();  // the previous chunk's products are done with the LDS tiles
+    stage(R, ch);
+    lds_barrier();
+    if (it + 2 < nch) load(R, chunk(it + 2));
+    const size_t base = ((size_t)sq * nch + ch) * DK + c0;
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        out[(base + 16 * ct + 4 * (l >> 4) + i) * P.dv + e0 + 16 * w + (l & 15)] = acc[ct][i];
+        acc[ct][i] *= lc[ct][i];
+      }
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const bf16* bh = yh + 16 * w * LB + 32 * s;
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) {
+        const bf16* ah = xh + 16 * ct * LB + 32 * s;
+        acc[ct] = slab_bf(ah, LB, bh, LB, acc[ct]);
+        acc[ct] = slab_bf(xl + 16 * ct * LB + 32 * s, LB, bh, LB, acc[ct]);
+        if constexpr (REV) acc[ct] = slab_bf(ah, LB, yl + 16 * w * LB + 32 * s, LB, acc[ct]);
+      }
+    }
+  };
+  Regs ra, rb;
+  if (nch > 0) load(ra, chunk(0));
+  if (nch > 1) load(rb, chunk(1));
+  for (int it = 0; it < nch; it += 2) {
+    step(ra, it);
+    if (it + 1 < nch) step(rb, it + 1);
+  }
 }
 
 // ---- scan over chunks, in place: buf[c] <- carried value entering chunk c ----
@@ -608,7 +792,7 @@ __global__ __launch_bounds__(256) void k_bwd_mm1_split(const BwdParams P) {
   load_step(0);
   for (int e0 = 0; e0 < P.dv; e0 += EC) {
     store_step();
-    __syncthreads();
+    lds_barrier();  // LDS only: the next step's loads below stay in flight past the barriers
     if (e0 + EC < P.dv) load_step(e0 + EC);
     const bf16* ra = doh + 16 * w * LB;
     const bf16* rl = dol + 16 * w * LB;
@@ -626,7 +810,7 @@ __global__ __launch_bounds__(256) void k_bwd_mm1_split(const BwdParams P) {
       ad[j] = slab_bf(ra, LB, vh + 16 * j * LB, LB, ad[j]);
       ad[j] = slab_bf(rl, LB, vh + 16 * j * LB, LB, ad[j]);
     }
-    __syncthreads();
+    lds_barrier();
   }
   float* QK = Br.QKi + ((size_t)u.sq * Br.nch + u.ch) * 2 * 64 * DK;
   float* D = Br.AD + ((size_t)u.sq * Br.nch + u.ch) * 64 * 64;
@@ -658,9 +842,11 @@ __global__ __launch_bounds__(256) void k_bwd_dv(const BwdParams P) {
   __shared__ __attribute__((aligned(16))) float dt[64 * LD];   // do^T [e][t]
   __shared__ __attribute__((aligned(16))) float kh[64 * LDC];  // k-hat [i][c]
   __shared__ __attribute__((aligned(16))) float dst[64 * LDC]; // dS_end^T [e][c]
-  const UnitPos u = unit_pos(P, blockIdx.x);
+  int unit, slice;
+  if (!xcd_item(P.total_units * (P.dv / 64), P.dv / 64, unit, slice)) return;
+  const UnitPos u = unit_pos(P, unit);
   const BwdBranch& Br = P.br[u.bi];
-  const int j0 = u.ch * P.C, e0 = blockIdx.y * 64;
+  const int j0 = u.ch * P.C, e0 = slice * 64;
   const int nvalid = min(P.C, Br.n - j0);
   const size_t row0 = (size_t)u.sq * Br.np + j0;
   const size_t sbase = ((size_t)u.sq * Br.nch + u.ch) * DK;
@@ -732,9 +918,11 @@ __global__ __launch_bounds__(256) void k_bwd_dv_split(const BwdParams P) {
   __shared__ __attribute__((aligned(16))) bf16 dth[64 * LB], dtl[64 * LB];    // do^T [e][t]
   __shared__ __attribute__((aligned(16))) bf16 kh[64 * LC], kl[64 * LC];      // k-hat [i][c]
   __shared__ __attribute__((aligned(16))) bf16 sh[64 * LC], sl[64 * LC];      // dS_end^T [e][c]
-  const UnitPos u = unit_pos(P, blockIdx.x);
+  int unit, slice;
+  if (!xcd_item(P.total_units * (P.dv / 64), P.dv / 64, unit, slice)) return;
+  const UnitPos u = unit_pos(P, unit);
   const BwdBranch& Br = P.br[u.bi];
-  const int j0 = u.ch * P.C, e0 = blockIdx.y * 64;
+  const int j0 = u.ch * P.C, e0 = slice * 64;
   const int nvalid = min(P.C, Br.n - j0);
   const size_t row0 = (size_t)u.sq * Br.np + j0;
   const size_t sbase = ((size_t)u.sq * Br.nch + u.ch) * DK;
@@ -860,9 +1048,11 @@ __global__ __launch_bounds__(256) void k_bwd_dqdk(const BwdParams P) {
   __shared__ __attribute__((aligned(16))) float kt[3 * CS * LT];  // K~J^T [J][c][i in block J]
   __shared__ __attribute__((aligned(16))) float qt[3 * CS * LT];  // Q~J^T [J][c][t in block J + 1]
   __shared__ float rs[64 * LR];
-  const UnitPos u = unit_pos(P, blockIdx.x);
+  int unit, slice;
+  if (!xcd_item(P.total_units * (DK / CS), DK / CS, unit, slice)) return;
+  const UnitPos u = unit_pos(P, unit);
   const BwdBranch& Br = P.br[u.bi];
-  const int j0 = u.ch * P.C, c0 = blockIdx.y * CS;
+  const int j0 = u.ch * P.C, c0 = slice * CS;
   const int nvalid = min(P.C, Br.n - j0);
   const size_t row0 = (size_t)u.sq * Br.np + j0;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lr = l & 15, lg = l >> 4;
@@ -1414,18 +1604,20 @@ __global__ __launch_bounds__(256) void k_bwd_wf_partial(const BwdParams P, int r
 template <typename T, int DK>
 static void launch_chunk_kernels_t(const BwdParams& P, int which, hipStream_t st) {
   const int slices = P.dv / 64;
+  // a flat grid over (unit, slice) items, 8 * ceil(items / 8) blocks (see xcd_item)
+  auto xg = [&](int inner) { return dim3((unsigned)(((int64_t)P.total_units * inner + N_XCD - 1) / N_XCD * N_XCD)); };
   switch (which) {
     case 0:
       if constexpr (sizeof(T) == 2)
-        hipLaunchKernelGGL((k_bwd_outer_split<DK, false>), dim3(P.total_units, slices), dim3(256), 0, st, P);
+        hipLaunchKernelGGL((k_bwd_outer_split<DK, false>), xg(slices), dim3(256), 0, st, P);
       else
-        hipLaunchKernelGGL((k_bwd_outer<T, DK, false>), dim3(P.total_units, slices), dim3(256), 0, st, P);
+        hipLaunchKernelGGL((k_bwd_outer<T, DK, false>), xg(slices), dim3(256), 0, st, P);
       break;
     case 1:
       if constexpr (sizeof(T) == 2)
-        hipLaunchKernelGGL((k_bwd_outer_split<DK, true>), dim3(P.total_units, slices), dim3(256), 0, st, P);
+        hipLaunchKernelGGL((k_bwd_outer_split<DK, true>), xg(slices), dim3(256), 0, st, P);
       else
-        hipLaunchKernelGGL((k_bwd_outer<T, DK, true>), dim3(P.total_units, slices), dim3(256), 0, st, P);
+        hipLaunchKernelGGL((k_bwd_outer<T, DK, true>), xg(slices), dim3(256), 0, st, P);
       break;
     case 5:
       if constexpr (sizeof(T) == 2)
@@ -1435,13 +1627,13 @@ static void launch_chunk_kernels_t(const BwdParams& P, int which, hipStream_t st
       break;
     case 3:
       if constexpr (sizeof(T) == 2 && DK >= 32)
-        hipLaunchKernelGGL((k_bwd_dv_split<DK>), dim3(P.total_units, slices), dim3(256), 0, st, P);
+        hipLaunchKernelGGL((k_bwd_dv_split<DK>), xg(slices), dim3(256), 0, st, P);
       else
-        hipLaunchKernelGGL((k_bwd_dv<T, DK>), dim3(P.total_units, slices), dim3(256), 0, st, P);
+        hipLaunchKernelGGL((k_bwd_dv<T, DK>), xg(slices), dim3(256), 0, st, P);
       break;
     default: {
       const int cs = DK < 32 ? 1 : DK / 32;
-      hipLaunchKernelGGL((k_bwd_dqdk<T, DK>), dim3(P.total_units, cs), dim3(256), 0, st, P);
+      hipLaunchKernelGGL((k_bwd_dqdk<T, DK>), xg(cs), dim3(256), 0, st, P);
     }
   }
 }
@@ -1475,6 +1667,30 @@ hipError_t launch_bwd_gate(const BwdParams& P, hipStream_t st) {
   else hipLaunchKernelGGL(k_bwd_gate<64>, dim3(P.total_units), dim3(256), lds, st, P);
   return hipGetLastError();
 }
+
+// the state walks of every branch in one launch (bf16 storage), 32 channels per
+// walk (64-channel walks, with half the restaging of the shared V or dO tile,
+// took 1.5x as long: one workgroup per CU leaves each walk's latency exposed)
+#define WALK_CP(DKV) 32
+hipError_t launch_bwd_walk(const BwdParams& P, bool rev, hipStream_t st) {
+  if (P.walk_units == 0) return hipSuccess;
+  const dim3 grid(P.walk_units), block(256);
+  switch (P.dk) {
+#define MSGLA_WALK(DKV)                                                                         \
+  case DKV:                                                                                     \
+    if (rev) hipLaunchKernelGGL((k_bwd_walk<DKV, true, WALK_CP(DKV)>), grid, block, 0, st, P);  \
+    else hipLaunchKernelGGL((k_bwd_walk<DKV, false, WALK_CP(DKV)>), grid, block, 0, st, P);     \
+    break;
+    MSGLA_WALK(32)
+    MSGLA_WALK(64)
+    MSGLA_WALK(128)
+    MSGLA_WALK(256)
+#undef MSGLA_WALK
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+#undef WALK_CP
 
 // every branch's scan in one launch (blockIdx.y = branch)
 hipError_t launch_bwd_scan(const BwdParams& P, bool rev, hipStream_t st) {

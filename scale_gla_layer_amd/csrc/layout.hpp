@@ -272,6 +272,7 @@ struct BwdBranch {
   int s, h, n, nch, np;
   int unit_begin;             // first (b, head, chunk) unit of the branch
   int gg_begin;               // first (b, chunk) unit of the branch's gate gradients
+  int walk_begin;             // first (b, head, d_v slice, d_k part) unit of its state walks
   int col_k, col_v, col_g, NP;
   const float* q;             // forward workspace: projections (q unscaled)
   const float* k;
@@ -305,7 +306,7 @@ struct BwdBranch {
 struct BwdParams {
   int B, L, d, dk, dv, C, r, rp, m;
   float inv_gamma, q_scale;
-  int nbranch, total_units, gate_units;
+  int nbranch, total_units, gate_units, walk_units;
   int fine;                   // branch with scale 1, or -1
   const void* x;              // [B][L][d] T
   const uint8_t* mask;        // [B][L] token mask of the forward, or null
