@@ -135,14 +135,18 @@ bool gemm_rm(rocblas_handle h, bool tA, bool tB, int M, int N, int K, const void
 // [K][N] (ldb), K the long reduction over positions, written to the column
 // ranges of `dst`.  With few output tiles the K range is cut into S slices
 // computed as one strided batch into `part` [S][M][N] and summed by a kernel,
-// so that the product fills the chip.
+// so that the product fills the chip.  S doubles while the batch stays within
+// 192 output tiles of 128 x 128: measured on the main workload's backward
+// against caps of 0 (no split) to 1536, more slices cost more in partial
+// traffic and summing than they gain in occupancy (caps 768 and 1536: +15 and
+// +40 us; 96 and below: +60 us and more).
 bool gemm_wgrad(rocblas_handle h, int M, int N, int K, const void* A, rocblas_datatype ta, int lda,
                 const void* Bm, rocblas_datatype tb, int ldb, const SplitDst& dst, float* part,
                 size_t part_floats, int elem_bytes, hipStream_t st) {
   if (M == 0 || N == 0) return true;
   const int tiles = ((M + 127) / 128) * ((N + 127) / 128);
   int S = 1;
-  while (S < BWD_SPLIT_MAX && tiles * S * 2 <= 768 && K % (2 * S) == 0 && K / (2 * S) >= 256 &&
+  while (S < BWD_SPLIT_MAX && tiles * S * 2 <= 192 && K % (2 * S) == 0 && K / (2 * S) >= 256 &&
          (size_t)(2 * S) * M * N <= part_floats)
     S *= 2;
   const bool direct = S == 1 && dst.n == 1 && dst.c0[0] == 0 && dst.nc[0] == N;
