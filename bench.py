@@ -329,12 +329,13 @@ def measure_library_gemms(cfg, B, L, stage_ms, steps=50, warmup=10):
 
 
 def measure_training(workload="main", steps=20, warmup=5):
-    """One training step of the layer: the forward and msgla_backward (which
-    recomputes the forward's intermediates itself) on the same input, each timed
-    with events over `steps` back-to-back calls after clock settling; dO is a
-    seeded N(0, 1) tensor.  The backward's algorithmic flops are taken as twice
-    the forward's (each product of the forward appears twice in the backward:
-    once for the input's gradient, once for the weight's)."""
+    """One training step of the layer on one input, each part timed with events over
+    `steps` back-to-back calls after clock settling (dO a seeded N(0, 1) tensor):
+    the step is msgla_forward_train + msgla_backward_saved (the backward reads the
+    intermediates the training forward kept); msgla_forward + msgla_backward (which
+    recomputes them) is reported beside it.  The backward's algorithmic flops are
+    taken as twice the forward's (each product of the forward appears twice in the
+    backward: once for the input's gradient, once for the weight's)."""
     import numpy as np
     import torch
     from scale_gla_layer_amd.config import WORKLOADS
@@ -349,9 +350,13 @@ def measure_training(workload="main", steps=20, warmup=5):
     settle_clocks(layer, x, max_s=1.0)
     out = layer.new_output(B, L)
     dx, grads = layer.backward(x, dO)
+    fwd_t = lambda: layer.forward_train(x, out=out)
+    bwd_s = lambda: layer.backward(x, dO, dx=dx, grads=grads, saved=True)
     for _ in range(warmup):
         layer.forward(x, out=out)
         layer.backward(x, dO, dx=dx, grads=grads)
+        fwd_t()
+        bwd_s()
     torch.cuda.synchronize()
 
     def timed(fn):
@@ -364,15 +369,21 @@ def measure_training(workload="main", steps=20, warmup=5):
         return e0.elapsed_time(e1) / steps * 1e3
 
     fwd = timed(lambda: layer.forward(x, out=out))
-    bwd = timed(lambda: layer.backward(x, dO, dx=dx, grads=grads))
-    step = timed(lambda: (layer.forward(x, out=out), layer.backward(x, dO, dx=dx, grads=grads)))
+    fwdt = timed(fwd_t)
+    bwd = timed(bwd_s)
+    bwd_r = timed(lambda: layer.backward(x, dO, dx=dx, grads=grads))
+    step = timed(lambda: (fwd_t(), bwd_s()))
+    step_r = timed(lambda: (layer.forward(x, out=out), layer.backward(x, dO, dx=dx, grads=grads)))
     alg = algorithmic(cfg, B, L)
     peak = PEAK["bf16_mfma_tflops"] if cfg.dtype == "bf16" else PEAK["fp32_mfma_tflops"]
     bwd_flops = 2 * alg["flops"]
     del layer, x, dO, out, dx, grads
     return {"workload": workload, "batch": B, "seq_len": L, "forward_us": round(fwd, 1),
-            "backward_us": round(bwd, 1), "step_us": round(step, 1),
+            "forward_train_us": round(fwdt, 1), "backward_us": round(bwd, 1),
+            "backward_recompute_us": round(bwd_r, 1), "step_us": round(step, 1),
+            "step_recompute_us": round(step_r, 1),
             "tokens_per_s": round(B * L / (step * 1e-6), 1),
+            "tokens_per_s_recompute": round(B * L / (step_r * 1e-6), 1),
             "backward_algorithmic_gflop": round(bwd_flops / 1e9, 2),
             "backward_tflops": round(bwd_flops / (bwd * 1e-6) / 1e12, 1),
             "backward_roofline_frac": round(bwd_flops / (peak * 1e12) / (bwd * 1e-6), 4)}
@@ -626,7 +637,8 @@ def _counter_means(path: str) -> dict:
 def summarize_training_profile(d, workload, wl, cmds, out_dir):
     """profiles/kernels_training_<workload>.md from the bwd_ktrace run, if present."""
     import csv
-    # the training step: forward and backward (its own recompute included)
+    # the training step: the training forward, the backward from its saved intermediates,
+    # and the recomputing backward
     bwd_csv = os.path.join(d, "bwd_ktrace", "backward_kernel_stats.csv")
     if os.path.exists(bwd_csv):
         with open(bwd_csv, newline="", encoding="utf-8") as f:
@@ -635,12 +647,14 @@ def summarize_training_profile(d, workload, wl, cmds, out_dir):
                  f"({wl.description})", "",
                  "Command (from the repository root, `<out>` any output directory):", "",
                  f"    {cmds['bwd_ktrace']}", "",
-                 "Clock settling forwards, then 5 warm-up steps and 20 forwards, 20 backwards and "
-                 "20 forward + backward steps. Each backward first recomputes the forward's "
-                 "intermediates with the forward's kernels except the fused output launch (so "
-                 "those appear about twice as often as k3f_fine_fuse). rocBLAS kernels are "
-                 "named by their macro tile; k_bwd_outer (S) and (dS) are the chunks' state and "
-                 "state-gradient increments.", "",
+                 "Clock settling forwards, then 5 warm-up rounds and 20 calls each of the forward, "
+                 "the training forward (msgla_forward_train), the backward from its saved "
+                 "intermediates (msgla_backward_saved), the recomputing backward (msgla_backward), "
+                 "and the two steps (training forward + saved backward; forward + recomputing "
+                 "backward). The recomputing backward runs the forward's kernels except the fused "
+                 "output launch, so those appear more often than k3f_fine_fuse. rocBLAS kernels are "
+                 "named by their macro tile; k_bwd_walk runs once per direction (states, state "
+                 "gradients) per backward.", "",
                  "| kernel | calls | avg us | min us | max us | share |", "|---|---|---|---|---|---|"]
         import re
         for r in bstats:
@@ -655,6 +669,8 @@ def summarize_training_profile(d, workload, wl, cmds, out_dir):
                     short = m.group(1)
                     if short in ("k_bwd_outer", "k_bwd_outer_split"):
                         short += " (dS)" if ("Lb1E" in name or "true>" in name) else " (S)"
+                    if short == "k_bwd_walk":
+                        short += " (dS)" if ("Lb1E" in name or ", true," in name) else " (S)"
                 if "k_bwd_gemm" in name:
                     # storage-type output: the pooled inputs' gradient; fp32: dLoss/do
                     short = "k_bwd_gemm " + ("(dxp)" if ("DF16bDF16b" in name or "IffE" in name) else "(do)")
@@ -1004,8 +1020,11 @@ def main():
     training = None
     if not args.no_training:
         training = measure_training(wl.name)
-        log(f"[bench] training step {training['step_us']} us ({training['forward_us']} forward + "
-            f"{training['backward_us']} backward), {training['tokens_per_s'] / 1e6:.2f} M tokens/s")
+        log(f"[bench] training step {training['step_us']} us ({training['forward_train_us']} training "
+            f"forward + {training['backward_us']} backward from the saved intermediates), "
+            f"{training['tokens_per_s'] / 1e6:.2f} M tokens/s; with the recomputing backward "
+            f"{training['step_recompute_us']} us ({training['forward_us']} + "
+            f"{training['backward_recompute_us']})")
         if args.workload != "gla_baseline" and not args.no_gla:
             training["gla"] = measure_training("gla_baseline")
             training["ratio_vs_gla"] = round(training["tokens_per_s"] / training["gla"]["tokens_per_s"], 4)

@@ -355,6 +355,33 @@ msgla_status msgla_backward(const msgla_config* cfg, const void* packed, const v
                             void* dx, const msgla_grads* grads, void* workspace,
                             size_t workspace_bytes, void* stream);
 
+/*
+ * A training step without the backward's recompute (Sec. 3.4, training
+ * paragraph; Sec. 5.5, Table 4): the forward's intermediates are kept from the
+ * step's own forward instead of being computed twice.
+ *
+ * msgla_forward_train computes what msgla_forward computes from a fresh state
+ * (out [B][L][d], the same values: the same launches), in a workspace of at
+ * least msgla_backward_workspace_bytes(cfg, B, L) bytes, where it leaves every
+ * intermediate the backward reads.  msgla_backward_saved then takes the same
+ * arguments as msgla_backward and returns the same gradients (bit for bit),
+ * reading those intermediates instead of recomputing them.  The caller keeps
+ * the contract of such a saved workspace: the same cfg, packed weights, x,
+ * mask, B and L in both calls, and the workspace unchanged in between; a
+ * mismatch is not detected and gives wrong gradients.  msgla_backward_saved
+ * leaves the saved intermediates unchanged, so several backward calls (other
+ * dout) may follow one training forward.  Errors as msgla_backward; both are
+ * asynchronous on `stream`.
+ */
+msgla_status msgla_forward_train(const msgla_config* cfg, const void* packed, const void* x,
+                                 const uint8_t* mask, int64_t B, int64_t L, void* out,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
+msgla_status msgla_backward_saved(const msgla_config* cfg, const void* packed, const void* x,
+                                  const void* dout, const uint8_t* mask, int64_t B, int64_t L,
+                                  void* dx, const msgla_grads* grads, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

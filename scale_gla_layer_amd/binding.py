@@ -27,7 +27,7 @@ SYMBOLS = (
     "msgla_pack_weights", "msgla_workspace_bytes", "msgla_state_bytes", "msgla_state_init",
     "msgla_forward", "msgla_forward_timed", "msgla_decode_workspace_bytes", "msgla_decode_step",
     "msgla_fusion_weights", "msgla_state_query", "msgla_forward_noalloc",
-    "msgla_backward_workspace_bytes", "msgla_backward",
+    "msgla_backward_workspace_bytes", "msgla_backward", "msgla_forward_train", "msgla_backward_saved",
 )
 NOALLOC_WORKSPACE_BYTES = 192 << 20  # MSGLA_NOALLOC_WORKSPACE_BYTES
 
@@ -117,6 +117,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "msgla_backward_workspace_bytes": (sz, [cfgp, i64, i64]),
         "msgla_backward": (ctypes.c_int, [cfgp, vp, vp, vp, vp, i64, i64, vp, ctypes.POINTER(CGrads),
                                           vp, sz, vp]),
+        "msgla_backward_saved": (ctypes.c_int, [cfgp, vp, vp, vp, vp, i64, i64, vp, ctypes.POINTER(CGrads),
+                                                vp, sz, vp]),
+        "msgla_forward_train": (ctypes.c_int, [cfgp, vp, vp, vp, i64, i64, vp, vp, sz, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -248,20 +251,31 @@ def msgla_backward_workspace_bytes(cfg: MsglaConfig, B: int, L: int) -> int:
 
 
 def msgla_backward(cfg: MsglaConfig, packed, x, dout, B: int, L: int, dx, branch_grads: Sequence[dict],
-                   W_f, b_f, workspace, mask=None, stream=None):
+                   W_f, b_f, workspace, mask=None, stream=None, saved=False):
     """branch_grads: per branch a dict of fp32 device tensors W_q, W_k, W_v, W_g1, W_g2, b_g, W_o
     and, for configurations with the normalisation, norm_g (written, in the layout of the
     weights); W_f, b_f: fp32 device tensors (None when m == 1);
-    mask: the forward's [B, L] uint8 token mask, or None."""
+    mask: the forward's [B, L] uint8 token mask, or None;
+    saved: msgla_backward_saved (the workspace holds msgla_forward_train's intermediates)."""
     g = CGrads()
     for i, br in enumerate(branch_grads):
         for name in ("W_q", "W_k", "W_v", "W_g1", "W_g2", "b_g", "W_o", "norm_g"):
             setattr(g.br[i], name, _ptr(br.get(name)))
     g.W_f, g.b_f = _ptr(W_f), _ptr(b_f)
-    st = load_library().msgla_backward(ctypes.byref(c_config(cfg)), _ptr(packed), _ptr(x), _ptr(dout),
+    name = "msgla_backward_saved" if saved else "msgla_backward"
+    st = getattr(load_library(), name)(ctypes.byref(c_config(cfg)), _ptr(packed), _ptr(x), _ptr(dout),
                                        _ptr(mask), B, L, _ptr(dx), ctypes.byref(g), _ptr(workspace),
                                        workspace.numel() * workspace.element_size(), _stream(stream))
-    _check("msgla_backward", st)
+    _check(name, st)
+
+
+def msgla_forward_train(cfg: MsglaConfig, packed, x, B: int, L: int, out, workspace, mask=None, stream=None):
+    """The training forward: out as msgla_forward, the backward's intermediates kept in
+    workspace (at least msgla_backward_workspace_bytes)."""
+    st = load_library().msgla_forward_train(ctypes.byref(c_config(cfg)), _ptr(packed), _ptr(x), _ptr(mask), B, L,
+                                            _ptr(out), _ptr(workspace),
+                                            workspace.numel() * workspace.element_size(), _stream(stream))
+    _check("msgla_forward_train", st)
 
 
 def msgla_state_query(state, stream=None) -> dict:

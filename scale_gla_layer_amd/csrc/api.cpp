@@ -428,7 +428,7 @@ msgla_status msgla::host::forward_impl(const msgla_config* cfg, const void* pack
   HIP_TRY(launch_k3c(p3, g.bf16, st));
   HIP_TRY(ev(4, false));
   HIP_TRY(ev(5, true));
-  if (!hooks) HIP_TRY(launch_k3f(p3, g.bf16, st));
+  if (!hooks || out) HIP_TRY(launch_k3f(p3, g.bf16, st));
   HIP_TRY(ev(5, false));
 
   if (state_out) {

@@ -243,7 +243,17 @@ rocblas_handle g_blas[64] = {};
 rocblas_handle blas_handle() {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
-  if (!g_blas[dev] && rocblas_create_handle(&g_blas[dev]) != rocblas_status_success) g_blas[dev] = nullptr;
+  if (!g_blas[dev]) {
+    rocblas_handle h = nullptr;
+    if (rocblas_create_handle(&h) != rocblas_status_success) return nullptr;
+    // no atomic accumulation inside the library's kernels: the gradients are the
+    // same bits from call to call
+    if (rocblas_set_atomics_mode(h, rocblas_atomics_not_allowed) != rocblas_status_success) {
+      rocblas_destroy_handle(h);
+      return nullptr;
+    }
+    g_blas[dev] = h;
+  }
   return g_blas[dev];
 }
 
@@ -261,9 +271,25 @@ size_t msgla_backward_workspace_bytes(const msgla_config* cfg, int64_t B, int64_
   return bwd_geom(pack_geom(cfg), B, L).total;
 }
 
-msgla_status msgla_backward(const msgla_config* cfg, const void* packed, const void* x, const void* dout,
-                            const uint8_t* mask, int64_t B, int64_t L, void* dx, const msgla_grads* grads,
-                            void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The hooks that keep the forward's intermediates where the backward reads them.
+FwdHooks bwd_hooks(const PackGeom& g, const BwdGeom& G, void* workspace) {
+  FwdHooks hooks{};
+  for (int i = 0; i < g.m; ++i) {
+    if (g.br[i].s > 1) hooks.yc[i] = at<char>(workspace, G.br[i].Yc);
+    if (g.norm) hooks.yn[i] = at<char>(workspace, G.br[i].yn);
+  }
+  return hooks;
+}
+
+// recompute: run the forward's launches first (msgla_backward); otherwise the
+// workspace holds them from msgla_forward_train (msgla_backward_saved)
+msgla_status backward_impl(const msgla_config* cfg, const void* packed, const void* x, const void* dout,
+                           const uint8_t* mask, int64_t B, int64_t L, void* dx, const msgla_grads* grads,
+                           void* workspace, size_t workspace_bytes, void* stream, bool recompute) {
   if (msgla_status st = check_config(cfg); st != MSGLA_OK) return st;
   if (!bwd_supported(cfg)) return MSGLA_ERR_UNSUPPORTED;
   if (!batch_ok(B, L)) return MSGLA_ERR_INVALID_ARG;
@@ -283,16 +309,14 @@ msgla_status msgla_backward(const msgla_config* cfg, const void* packed, const v
   hipStream_t st = static_cast<hipStream_t>(stream);
   const rocblas_datatype ST = storage_type(g.bf16);
 
-  // forward intermediates (q, k, v^T, x W_g1, y, fusion weights, block means, Y)
-  FwdHooks hooks{};
-  for (int i = 0; i < g.m; ++i) {
-    if (g.br[i].s > 1) hooks.yc[i] = at<char>(workspace, G.br[i].Yc);
-    if (g.norm) hooks.yn[i] = at<char>(workspace, G.br[i].yn);
+  // forward intermediates (q, k, v^T, x W_g1, y, A, fusion weights, block means, Y)
+  if (recompute) {
+    const FwdHooks hooks = bwd_hooks(g, G, workspace);
+    if (msgla_status s = forward_impl(cfg, packed, x, mask, B, L, nullptr, nullptr, nullptr, workspace,
+                                      workspace_bytes, stream, nullptr, &hooks);
+        s != MSGLA_OK)
+      return s;
   }
-  if (msgla_status s = forward_impl(cfg, packed, x, mask, B, L, nullptr, nullptr, nullptr, workspace,
-                                    workspace_bytes, stream, nullptr, &hooks);
-      s != MSGLA_OK)
-    return s;
 
   std::lock_guard<std::mutex> lock(g_blas_mu);
   rocblas_handle hb = blas_handle();
@@ -519,6 +543,37 @@ msgla_status msgla_backward(const msgla_config* cfg, const void* packed, const v
     HIP_TRY(launch_bwd_wf_finish(partial, BWD_WF_NRB, g.d, g.m, grads->W_f, st));
   }
   return MSGLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+msgla_status msgla_backward(const msgla_config* cfg, const void* packed, const void* x, const void* dout,
+                            const uint8_t* mask, int64_t B, int64_t L, void* dx, const msgla_grads* grads,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  return backward_impl(cfg, packed, x, dout, mask, B, L, dx, grads, workspace, workspace_bytes, stream, true);
+}
+
+msgla_status msgla_backward_saved(const msgla_config* cfg, const void* packed, const void* x, const void* dout,
+                                  const uint8_t* mask, int64_t B, int64_t L, void* dx, const msgla_grads* grads,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  return backward_impl(cfg, packed, x, dout, mask, B, L, dx, grads, workspace, workspace_bytes, stream, false);
+}
+
+msgla_status msgla_forward_train(const msgla_config* cfg, const void* packed, const void* x, const uint8_t* mask,
+                                 int64_t B, int64_t L, void* out, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+  if (msgla_status st = check_config(cfg); st != MSGLA_OK) return st;
+  if (!bwd_supported(cfg)) return MSGLA_ERR_UNSUPPORTED;
+  if (!batch_ok(B, L)) return MSGLA_ERR_INVALID_ARG;
+  if (!out || !workspace) return MSGLA_ERR_INVALID_ARG;
+  const PackGeom g = pack_geom(cfg);
+  const BwdGeom G = bwd_geom(g, B, L);
+  if (workspace_bytes < G.total) return MSGLA_ERR_WORKSPACE;
+  const FwdHooks hooks = bwd_hooks(g, G, workspace);
+  return forward_impl(cfg, packed, x, mask, B, L, out, nullptr, nullptr, workspace, workspace_bytes, stream,
+                      nullptr, &hooks);
 }
 
 }  // extern "C"

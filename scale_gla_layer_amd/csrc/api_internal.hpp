@@ -300,10 +300,11 @@ inline bool batch_ok(int64_t B, int64_t L) {
 }
 
 
-// Internal hooks of the forward launch sequence for the backward's recompute:
-// coarse outputs Y = y W_o go to yc[i] (instead of the dead block-mean buffer,
-// which the backward still needs), normalised rows to yn[i] (keeping the GLA
-// outputs), and the fused output launch is skipped.
+// Internal hooks of the forward launch sequence for the backward (its recompute,
+// and the training forward): coarse outputs Y = y W_o go to yc[i] (instead of
+// the dead block-mean buffer, which the backward still needs), normalised rows
+// to yn[i] (keeping the GLA outputs); the fused output launch runs only when
+// an output is given.
 struct FwdHooks {
   void* yc[MSGLA_MAX_BRANCHES];
   void* yn[MSGLA_MAX_BRANCHES];  // configs with the normalisation: normalised rows go here

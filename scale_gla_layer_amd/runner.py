@@ -112,21 +112,36 @@ class DeviceLayer:
         m = len(c.scales)
         return brs, (z(d, m) if m > 1 else None), (z(m) if m > 1 else None)
 
-    def backward(self, x, dout, dx=None, grads=None, mask=None):
-        """Layer backward of a fresh-state forward of x (with the forward's token mask, if
-        any): returns (dx, (branch grads, dW_f, db_f))."""
-        B, L, _ = x.shape
+    def ensure_bwd_workspace(self, B: int, L: int):
         n = binding.msgla_backward_workspace_bytes(self.cfg, B, L)
         if n == 0:
             raise ValueError(f"the backward does not support this configuration or size (B={B} L={L})")
         if self.bwd_workspace is None or self.bwd_workspace.numel() < n:
             self.bwd_workspace = empty_bytes(n, self.device)
+        return self.bwd_workspace
+
+    def forward_train(self, x, out=None, mask=None):
+        """The training forward: the forward's output, with the backward's intermediates kept
+        in the backward workspace for backward(..., saved=True)."""
+        B, L, _ = x.shape
+        ws = self.ensure_bwd_workspace(B, L)
+        if out is None:
+            out = self.new_output(B, L)
+        binding.msgla_forward_train(self.cfg, self.packed, x, B, L, out, ws, mask=mask, stream=self.stream)
+        return out
+
+    def backward(self, x, dout, dx=None, grads=None, mask=None, saved=False):
+        """Layer backward of a fresh-state forward of x (with the forward's token mask, if
+        any): returns (dx, (branch grads, dW_f, db_f)).  saved: read the intermediates of
+        the preceding forward_train of the same x (and mask) instead of recomputing them."""
+        B, L, _ = x.shape
+        ws = self.ensure_bwd_workspace(B, L)
         if dx is None:
             dx = self.new_output(B, L)
         if grads is None:
             grads = self.new_grads()
         binding.msgla_backward(self.cfg, self.packed, x, dout, B, L, dx, grads[0], grads[1], grads[2],
-                               self.bwd_workspace, mask=mask, stream=self.stream)
+                               ws, mask=mask, stream=self.stream, saved=saved)
         return dx, grads
 
     def state_init(self, state, B: int):

@@ -193,6 +193,13 @@ int main() {
     const size_t bwn = msgla_backward_workspace_bytes(&cn, 2, 64);
     EXPECT(bwn > bws);
     EXPECT(msgla_backward(&cn, f, f, f, nullptr, 2, 64, f, &gr, f, bwn, nullptr) == MSGLA_ERR_INVALID_ARG);
+    // the training pair: the forward needs the backward's workspace, the saved backward
+    // validates as the backward does
+    EXPECT(msgla_forward_train(&c, f, f, nullptr, 2, 64, nullptr, f, bws, nullptr) == MSGLA_ERR_INVALID_ARG);
+    EXPECT(msgla_forward_train(&c, f, f, nullptr, 2, 64, f, f, ws, nullptr) == MSGLA_ERR_WORKSPACE);
+    EXPECT(msgla_forward_train(&c, f, f + 4, nullptr, 2, 64, f, f, bws, nullptr) == MSGLA_ERR_INVALID_ARG);
+    EXPECT(msgla_backward_saved(&c, f, f, nullptr, nullptr, 2, 64, f, &gr, f, bws, nullptr) == MSGLA_ERR_INVALID_ARG);
+    EXPECT(msgla_backward_saved(&c, f, f, f, nullptr, 2, 64, f, &gr, f, bws - 1, nullptr) == MSGLA_ERR_WORKSPACE);
   }
 
   std::printf("configurations %d, failures %d\n", n, failures);

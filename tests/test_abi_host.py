@@ -235,3 +235,34 @@ def test_backward_argument_errors_need_no_gpu():
     assert lib.msgla_validate_config(ctypes.byref(odd)) == 0
     assert lib.msgla_backward_workspace_bytes(ctypes.byref(odd), 2, 64) == 0
     assert f(ctypes.byref(odd), fake, fake, fake, None, 2, 64, fake, gp, fake, ws, None) == 2
+
+
+def test_training_pair_argument_errors_need_no_gpu():
+    """msgla_forward_train and msgla_backward_saved return their argument errors before
+    any HIP or rocBLAS call: the training forward needs the backward's workspace size."""
+    lib = binding.load_library()
+    cc = _raw_cfg()
+    cfgp = ctypes.byref(cc)
+    fake = 1 << 20
+    ws = lib.msgla_backward_workspace_bytes(cfgp, 2, 64)
+    fwd_ws = lib.msgla_workspace_bytes(cfgp, 2, 64)
+    ft = lib.msgla_forward_train
+    # NULL output, bad sizes, misaligned input, the forward's (smaller) workspace size
+    assert ft(cfgp, fake, fake, None, 2, 64, None, fake, ws, None) == 1
+    assert ft(cfgp, fake, fake, None, 0, 64, fake, fake, ws, None) == 1
+    assert ft(cfgp, fake, fake + 4, None, 2, 64, fake, fake, ws, None) == 1
+    assert ft(cfgp, fake, fake, None, 2, 64, fake, fake, fwd_ws, None) == 3
+    assert ft(cfgp, fake, fake, None, 2, 64, fake, fake, ws - 1, None) == 3
+    odd = _raw_cfg(dtype="f32", d_v=96)
+    assert ft(ctypes.byref(odd), fake, fake, None, 2, 64, fake, fake, ws, None) == 2
+    g = binding.CGrads()
+    for i in range(cc.n_branches):
+        for name in ("W_q", "W_k", "W_v", "W_g1", "W_g2", "b_g", "W_o"):
+            setattr(g.br[i], name, fake)
+    g.W_f = g.b_f = fake
+    bs = lib.msgla_backward_saved
+    gp = ctypes.byref(g)
+    assert bs(cfgp, fake, fake, None, None, 2, 64, fake, gp, fake, ws, None) == 1
+    assert bs(cfgp, fake, fake, fake, None, 2, 64, fake, gp, fake, ws - 1, None) == 3
+    assert bs(cfgp, fake, fake, fake, None, 2, 64, fake, None, fake, ws, None) == 1
+    assert bs(ctypes.byref(odd), fake, fake, fake, None, 2, 64, fake, gp, fake, ws, None) == 2

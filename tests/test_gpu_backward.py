@@ -219,3 +219,45 @@ def test_bf16_full_size_main_workload():
     say("errors " + ", ".join(f"{k} {v:.2e}" for k, v in errs.items()))
     worst = max(errs, key=errs.get)
     assert errs[worst] <= TOL[cfg.dtype], f"{worst}: {errs[worst]:.3e}"
+
+
+@pytest.mark.parametrize("case", ["bf16_masked", "bf16_normalised", "fp32"])
+def test_saved_backward_matches_recompute(case):
+    """msgla_forward_train writes msgla_forward's output bit for bit, and msgla_backward_saved
+    after it returns msgla_backward's gradients bit for bit; a second saved backward with
+    another dO (the saved intermediates unchanged by the first) matches that dO's
+    recomputing backward."""
+    import torch
+    if case == "fp32":
+        cfg, B, L, M = _cfg(), 2, 100, None
+    else:
+        cfg = dataclasses.replace(WORKLOADS["main"].cfg, norm=case == "bf16_normalised")
+        B, L = 2, 200
+        M = make_mask(B, L, seed=53, hole_prob=0.1) if case == "bf16_masked" else None
+    say(f"saved backward {case} B={B} L={L}")
+    X, W = make_inputs(cfg, B, L, seed=53)
+    rng = np.random.default_rng(54)
+    dO1, dO2 = (round_to(rng.normal(0.0, 1.0, X.shape), cfg.dtype) for _ in range(2))
+    layer = DeviceLayer(cfg, W)
+    x = to_device(X, cfg.dtype)
+    m = None if M is None else mask_to_device(M)
+    d1, d2 = to_device(dO1, cfg.dtype), to_device(dO2, cfg.dtype)
+
+    def grads_of(res):
+        dx, (gb, gWf, gbf) = res
+        ts = [dx] + [g[k] for g in gb for k in sorted(g)] + [t for t in (gWf, gbf) if t is not None]
+        return [t.clone() for t in ts]
+
+    def same(a, b, what):
+        for i, (u, v) in enumerate(zip(a, b)):
+            assert torch.equal(u, v), f"{what}: tensor {i} differs"
+
+    out_ref = layer.forward(x, mask=m).clone()
+    ref1 = grads_of(layer.backward(x, d1, mask=m))
+    ref2 = grads_of(layer.backward(x, d2, mask=m))
+    out = layer.forward_train(x, mask=m)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out_ref), "training forward output differs from the forward's"
+    same(grads_of(layer.backward(x, d1, mask=m, saved=True)), ref1, "saved backward, first dO")
+    same(grads_of(layer.backward(x, d2, mask=m, saved=True)), ref2, "saved backward, second dO")
+    torch.cuda.synchronize()
