@@ -26,7 +26,7 @@ hipError_t launch_bwd_norm(const BwdParams& P, int bi, bool bf16_path, hipStream
 hipError_t launch_bwd_mcolsum(const ColsumJobs& J, float* part, hipStream_t st);
 hipError_t launch_bwd_wf_partial(const BwdParams& P, float* partial, int nrb, bool bf16_path, hipStream_t st);
 hipError_t launch_bwd_wf_finish(const float* partial, int nrb, int d, int m, float* out, hipStream_t st);
-hipError_t launch_bwd_splitk_reduce(const float* part, int S, int M, int N, const SplitDst& D, hipStream_t st);
+hipError_t launch_bwd_splitk_reduce(const SplitJobs& J, hipStream_t st);
 hipError_t launch_bwd_gemm(const BwdGemm& P, bool bf16_path, bool out_storage, hipStream_t st);
 hipError_t launch_bwd_transpose(const BwdTranspose& P, bool bf16_path, hipStream_t st);
 }  // namespace msgla
@@ -56,6 +56,20 @@ struct BwdGeom {
 
 bool bwd_supported(const msgla_config* cfg) { return cfg->d_v % 64 == 0; }
 
+// K slices of a weight-gradient product C [M][N] over K positions (see gemm_wgrad)
+int wgrad_slices(int M, int N, int K) {
+  const int tiles = ((M + 127) / 128) * ((N + 127) / 128);
+  int S = 1;
+  while (S < BWD_SPLIT_MAX && tiles * S * 2 <= 192 && K % (2 * S) == 0 && K / (2 * S) >= 256) S *= 2;
+  return S;
+}
+
+// fp32 partials a weight-gradient product leaves for the reduction (0: written directly)
+size_t wgrad_part_floats(int M, int N, int K, bool one_full_dst) {
+  const int S = wgrad_slices(M, N, K);
+  return (S == 1 && one_full_dst) ? 0 : (size_t)S * M * N;
+}
+
 BwdGeom bwd_geom(const PackGeom& g, int64_t B, int64_t L) {
   BwdGeom G{};
   G.W = ws_geom(g, B, L, false);
@@ -65,7 +79,7 @@ BwdGeom bwd_geom(const PackGeom& g, int64_t B, int64_t L) {
     cur += align256(bytes);
     return o;
   };
-  size_t gate_cols = 0, norm_cols = 0, mn = 0;
+  size_t gate_cols = 0, norm_cols = 0, part = 0;
   for (int i = 0; i < g.m; ++i) {
     const BranchGeom& bg = g.br[i];
     const WsBranch& w = G.W.br[i];
@@ -101,7 +115,12 @@ BwdGeom bwd_geom(const PackGeom& g, int64_t B, int64_t L) {
     }
     gate_cols += (size_t)(g.r + 1) * bg.h * g.dk;
     norm_cols += (size_t)bg.h * g.dv;
-    mn = std::max({mn, (size_t)g.d * (bg.col_g + g.r), (size_t)bg.h * g.dv * g.d});
+    // the partials of its two weight-gradient products, each in a region of its own
+    const int K = (int)prow;
+    if (K > 0) {
+      part += wgrad_part_floats(bg.h * g.dv, g.d, K, true);          // W_o
+      part += wgrad_part_floats(g.d, bg.col_g + g.r, K, false);     // q | k | v | W_g1
+    }
   }
   G.dz = take((size_t)B * L * FUSION_STRIDE * 4);
   G.partial = take((size_t)BWD_WF_NRB * g.d * FUSION_STRIDE * 4);
@@ -109,8 +128,8 @@ BwdGeom bwd_geom(const PackGeom& g, int64_t B, int64_t L) {
   G.mcol_floats = (size_t)BWD_NRB_MAX * std::max(gate_cols + g.m, norm_cols);
   G.mcol = take(G.mcol_floats * 4);
   G.Wo = take((size_t)g.Ktot * g.d * g.es);  // W_o rows [Ktot][d]
-  G.splitk_floats = (size_t)BWD_SPLIT_MAX * mn;
-  G.splitk = take(G.splitk_floats * 4);
+  G.splitk_floats = part;
+  G.splitk = take(std::max<size_t>(part, 1) * 4);
   G.total = cur;
   return G;
 }
@@ -134,35 +153,41 @@ bool gemm_rm(rocblas_handle h, bool tA, bool tB, int M, int N, int K, const void
 // Weight gradient C[M][N] = A^T B with A row-major [K][M] (lda) and B row-major
 // [K][N] (ldb), K the long reduction over positions, written to the column
 // ranges of `dst`.  With few output tiles the K range is cut into S slices
-// computed as one strided batch into `part` [S][M][N] and summed by a kernel,
-// so that the product fills the chip.  S doubles while the batch stays within
+// computed as one strided batch into its own region `part` [S][M][N] (the
+// cursor advances past it), to be summed by one reduction launch for every
+// product (`jobs`), so that the product fills the chip.  S doubles while the batch stays within
 // 192 output tiles of 128 x 128: measured on the main workload's backward
 // against caps of 0 (no split) to 1536, more slices cost more in partial
 // traffic and summing than they gain in occupancy (caps 768 and 1536: +15 and
 // +40 us; 96 and below: +60 us and more).
 bool gemm_wgrad(rocblas_handle h, int M, int N, int K, const void* A, rocblas_datatype ta, int lda,
-                const void* Bm, rocblas_datatype tb, int ldb, const SplitDst& dst, float* part,
-                size_t part_floats, int elem_bytes, hipStream_t st) {
+                const void* Bm, rocblas_datatype tb, int ldb, const SplitDst& dst, float*& part, const float* part_end,
+                SplitJobs& jobs) {
   if (M == 0 || N == 0) return true;
-  const int tiles = ((M + 127) / 128) * ((N + 127) / 128);
-  int S = 1;
-  while (S < BWD_SPLIT_MAX && tiles * S * 2 <= 192 && K % (2 * S) == 0 && K / (2 * S) >= 256 &&
-         (size_t)(2 * S) * M * N <= part_floats)
-    S *= 2;
+  const int S = wgrad_slices(M, N, K);
   const bool direct = S == 1 && dst.n == 1 && dst.c0[0] == 0 && dst.nc[0] == N;
   float* C = direct ? dst.p[0] : part;
-  if (!direct && (size_t)S * M * N > part_floats) return false;
+  if (!direct && (part + (size_t)S * M * N > part_end || jobs.n >= SplitJobs::MAX)) return false;
   const float alpha = 1.f, beta = 0.f;
   const int Ks = K / S;
   const rocblas_stride sA = (rocblas_stride)Ks * lda, sB = (rocblas_stride)Ks * ldb,
                        sC = (rocblas_stride)M * N;
-  (void)elem_bytes;
   if (rocblas_gemm_strided_batched_ex(h, rocblas_operation_none, rocblas_operation_transpose, N, M, Ks, &alpha, Bm,
                                       tb, ldb, sB, A, ta, lda, sA, &beta, C, rocblas_datatype_f32_r, N, sC, C,
                                       rocblas_datatype_f32_r, N, sC, S, rocblas_datatype_f32_r,
                                       rocblas_gemm_algo_standard, 0, 0) != rocblas_status_success)
     return false;
-  return direct || launch_bwd_splitk_reduce(part, S, M, N, dst, st) == hipSuccess;
+  if (!direct) {
+    // summed with the other products' partials by one launch at the end
+    const int j = jobs.n++;
+    jobs.part[j] = part;
+    jobs.S[j] = S;
+    jobs.M[j] = M;
+    jobs.N[j] = N;
+    jobs.dst[j] = dst;
+    part += (size_t)S * M * N;
+  }
+  return true;
 }
 
 // Appends a column sum of src [rows][cols] (row stride ld) into dst[cols].
@@ -402,6 +427,8 @@ msgla_status backward_impl(const msgla_config* cfg, const void* packed, const vo
   float* partial = at<float>(workspace, G.partial);
   float* mcol = at<float>(workspace, G.mcol);
   float* sk = at<float>(workspace, G.splitk);
+  const float* sk_end = sk + G.splitk_floats;
+  SplitJobs sjobs{};
   const char* WoT = at<char>(packed, g.off_WoT);
 
   // ---- the weights as the grouped products read them: W_o rows, Wp^T ----
@@ -441,7 +468,7 @@ msgla_status backward_impl(const msgla_config* cfg, const void* packed, const vo
     }
     const void* dYi = Br.s == 1 ? dout : Br.dY;
     BLAS_TRY(gemm_wgrad(hb, hdv, g.d, rows, Br.ycat, ST, hdv, dYi, ST, g.d, one_dst(grads->br[i].W_o, g.d), sk,
-                        G.splitk_floats, g.es, st));
+                        sk_end, sjobs));
   }
 
   // ---- the normalisation: dLoss/d(normalised rows) -> dLoss/do, and the gains' gradient ----
@@ -534,9 +561,9 @@ msgla_status backward_impl(const msgla_config* cfg, const void* packed, const vo
     dw.p[1] = gr.W_k, dw.c0[1] = bg.col_k, dw.nc[1] = hdk;
     dw.p[2] = gr.W_v, dw.c0[2] = bg.col_v, dw.nc[2] = hdv;
     dw.p[3] = gr.W_g1, dw.c0[3] = bg.col_g, dw.nc[3] = g.r;
-    BLAS_TRY(gemm_wgrad(hb, g.d, bg.col_g + g.r, rows, xp, ST, g.d, dP, ST, Br.NP, dw, sk, G.splitk_floats, g.es,
-                        st));
+    BLAS_TRY(gemm_wgrad(hb, g.d, bg.col_g + g.r, rows, xp, ST, g.d, dP, ST, Br.NP, dw, sk, sk_end, sjobs));
   }
+  HIP_TRY(launch_bwd_splitk_reduce(sjobs, st));
   HIP_TRY(launch_bwd_dx(P, g.bf16, st));
   if (g.m > 1) {
     HIP_TRY(launch_bwd_wf_partial(P, partial, BWD_WF_NRB, g.bf16, st));

@@ -1568,34 +1568,57 @@ __global__ __launch_bounds__(256) void k_bwd_mcolsum_finish(const ColsumJobs J, 
 // partial[rb][col][i] = sum over row block rb of x[row][col] dz[row][i], i < 8
 template <typename T>
 __global__ __launch_bounds__(256) void k_bwd_wf_partial(const BwdParams P, int rows_per_block, float* partial) {
+  // 64 columns per block: lane = (8-column group, row lane); 32 row lanes, 8 per wave
   __shared__ float red[4][64][FUSION_STRIDE];
-  const int cc = threadIdx.x & 63, tg = threadIdx.x >> 6;
-  const int col = blockIdx.x * 64 + cc;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int cg = lane & 7, rl = (lane >> 3) + 8 * wv;
+  const int col0 = blockIdx.x * 64 + 8 * cg;
   const int rows = P.B * P.L;
   const int r0 = blockIdx.y * rows_per_block, r1 = min(rows, r0 + rows_per_block);
-  float acc[FUSION_STRIDE];
+  float acc[8][FUSION_STRIDE];
 #pragma unroll
-  for (int i = 0; i < FUSION_STRIDE; ++i) acc[i] = 0.f;
-#pragma unroll 4
-  for (int r = r0 + tg; r < r1; r += 4) {
-    const float xv = to_f32(reinterpret_cast<const T*>(P.x)[(size_t)r * P.d + col]);
+  for (int c = 0; c < 8; ++c)
+#pragma unroll
+    for (int i = 0; i < FUSION_STRIDE; ++i) acc[c][i] = 0.f;
+#pragma unroll 2
+  for (int r = r0 + rl; r < r1; r += 32) {
+    float xv[8];
+    load8<T>(reinterpret_cast<const T*>(P.x) + (size_t)r * P.d + col0, xv);
     const f32x4 z0 = *reinterpret_cast<const f32x4*>(P.dz + (size_t)r * FUSION_STRIDE);
     const f32x4 z1 = *reinterpret_cast<const f32x4*>(P.dz + (size_t)r * FUSION_STRIDE + 4);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      acc[q] += xv * z0[q];
-      acc[q + 4] += xv * z1[q];
-    }
+    for (int c = 0; c < 8; ++c)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        acc[c][q] += xv[c] * z0[q];
+        acc[c][q + 4] += xv[c] * z1[q];
+      }
   }
+  // the wave's 8 row lanes (lane bits 3..5), then its 4 waves through LDS
 #pragma unroll
-  for (int i = 0; i < FUSION_STRIDE; ++i) red[tg][cc][i] = acc[i];
+  for (int c = 0; c < 8; ++c)
+#pragma unroll
+    for (int i = 0; i < FUSION_STRIDE; ++i)
+      if (i < P.m) {
+        float v = acc[c][i];
+        v += __shfl_xor(v, 8, WAVE);
+        v += __shfl_xor(v, 16, WAVE);
+        v += __shfl_xor(v, 32, WAVE);
+        acc[c][i] = v;
+      }
+  if (lane < 8)
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+#pragma unroll
+      for (int i = 0; i < FUSION_STRIDE; ++i) red[wv][8 * cg + c][i] = acc[c][i];
   __syncthreads();
-  if (tg == 0) {
+  if (tid < 64) {
+    const int col = blockIdx.x * 64 + tid;
 #pragma unroll
-    for (int i = 0; i < FUSION_STRIDE; ++i) {
-      const float v = red[0][cc][i] + red[1][cc][i] + red[2][cc][i] + red[3][cc][i];
-      partial[((size_t)blockIdx.y * P.d + col) * FUSION_STRIDE + i] = v;
-    }
+    for (int i = 0; i < FUSION_STRIDE; ++i)
+      if (i < P.m)
+        partial[((size_t)blockIdx.y * P.d + col) * FUSION_STRIDE + i] =
+            red[0][tid][i] + red[1][tid][i] + red[2][tid][i] + red[3][tid][i];
   }
 }
 
@@ -1804,10 +1827,17 @@ hipError_t launch_bwd_wf_finish(const float* partial, int nrb, int d, int m, flo
 namespace msgla {
 
 // Sum of S partial products [S][M][N] (fp32) into up to four destinations,
-// each owning a column range of the product: out_k[row][col - c0_k].
+// each owning a column range of the product: out_k[row][col - c0_k]; every
+// split-K product of a backward in one launch.
 
-__global__ __launch_bounds__(256) void k_bwd_splitk_reduce(const float* part, int S, int M, int N, SplitDst D) {
-  const size_t total = (size_t)M * N;
+__global__ __launch_bounds__(256) void k_bwd_splitk_reduce(const SplitJobs J) {
+  // blockIdx.y = job; a grid-stride walk over its M x N sums
+  const int j = blockIdx.y;
+  if (j >= J.n) return;
+  const int S = J.S[j], N = J.N[j];
+  const size_t total = (size_t)J.M[j] * N;
+  const float* part = J.part[j];
+  const SplitDst& D = J.dst[j];
   for (size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
        idx += (size_t)gridDim.x * blockDim.x) {
     float acc = 0.f;
@@ -1819,11 +1849,12 @@ __global__ __launch_bounds__(256) void k_bwd_splitk_reduce(const float* part, in
   }
 }
 
-hipError_t launch_bwd_splitk_reduce(const float* part, int S, int M, int N, const SplitDst& D, hipStream_t st) {
-  const size_t total = (size_t)M * N;
-  if (total == 0) return hipSuccess;
-  const unsigned grid = (unsigned)std::min<size_t>((total + 255) / 256, 65536);
-  hipLaunchKernelGGL(k_bwd_splitk_reduce, dim3(grid), dim3(256), 0, st, part, S, M, N, D);
+hipError_t launch_bwd_splitk_reduce(const SplitJobs& J, hipStream_t st) {
+  if (J.n == 0) return hipSuccess;
+  size_t most = 0;
+  for (int j = 0; j < J.n; ++j) most = std::max(most, (size_t)J.M[j] * J.N[j]);
+  const unsigned grid = (unsigned)std::min<size_t>((most + 255) / 256, 1024);
+  hipLaunchKernelGGL(k_bwd_splitk_reduce, dim3(grid, J.n), dim3(256), 0, st, J);
   return hipGetLastError();
 }
 

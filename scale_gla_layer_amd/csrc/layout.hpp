@@ -367,6 +367,16 @@ struct SplitDst {
   int n;
 };
 
+// Every split-K product of a backward, summed by one launch: job j adds the S[j]
+// slices part[j] [S][M][N] into its destinations.
+struct SplitJobs {
+  static constexpr int MAX = 2 * MSGLA_MAX_BRANCHES;
+  int n;
+  const float* part[MAX];
+  int S[MAX], M[MAX], N[MAX];
+  SplitDst dst[MAX];
+};
+
 // ---------------- packing ------------------------------------------------------
 struct PackSrc {
   const void* W_q; const void* W_k; const void* W_v; const void* W_g1; const void* W_g2;
