@@ -162,7 +162,7 @@ __device__ __forceinline__ f32x4 tile_f32(const float* a, int lda, const float* 
 // Dynamic LDS: the chunk's block means g1s [C][RP] (ranks >= r zero; at least 256
 // floats: the part totals reuse them), the head's W_g2 slice [r][d_k], and
 // log alpha [C][d_k].  With E = e^{-|z|}: log alpha = (min(z, 0) - log1p(E)) / gamma
-// and sigmoid(-z) = (z > 0 ? E : 1) / (1 + E).
+// and sigmoid(-z) = (z > 0 ? E : 1) / (1 + E), both from one reciprocal of 1 + E.
 template <int RP>
 __global__ __launch_bounds__(256) void k_bwd_gate(const BwdParams P) {
   extern __shared__ __attribute__((aligned(16))) float gate_lds[];
@@ -251,11 +251,14 @@ __global__ __launch_bounds__(256) void k_bwd_gate(const BwdParams P) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) z += g4[i] * w2r[4 * q + i];
     }
-    const float E = __expf(-fabsf(z)), L1 = log1pf(E);
+    // log1p(E) as log(v) for v = 1 + E rounded, plus the first-order correction
+    // (E - (v - 1)) / v for that rounding
+    const float E = __expf(-fabsf(z)), v = 1.f + E, rv = __frcp_rn(v);
+    const float L1 = __logf(v) + (E - (v - 1.f)) * rv;
     const float la = valid ? (fminf(z, 0.f) - L1) * P.inv_gamma : 0.f;
     las[jj * P.dk + c] = la;
     bsum += la;
-    Br.sg[((size_t)u.sq * Br.np + j0 + jj) * P.dk + c] = valid ? (z > 0.f ? E : 1.f) / (1.f + E) * P.inv_gamma : 0.f;
+    Br.sg[((size_t)u.sq * Br.np + j0 + jj) * P.dk + c] = valid ? (z > 0.f ? E : 1.f) * rv * P.inv_gamma : 0.f;
   }
   __syncthreads();  // the block means are no longer needed: their space takes the part totals
   float* tot = g1s;
