@@ -29,6 +29,7 @@ hipError_t launch_bwd_wf_finish(const float* partial, int nrb, int d, int m, flo
 hipError_t launch_bwd_splitk_reduce(const SplitJobs& J, hipStream_t st);
 hipError_t launch_bwd_gemm(const BwdGemm& P, bool bf16_path, bool out_storage, hipStream_t st);
 hipError_t launch_bwd_transpose(const BwdTranspose& P, bool bf16_path, hipStream_t st);
+hipError_t launch_bwd_wgrad(const Wgrad& P, hipStream_t st);
 }  // namespace msgla
 
 using namespace msgla;
@@ -56,8 +57,22 @@ struct BwdGeom {
 
 bool bwd_supported(const msgla_config* cfg) { return cfg->d_v % 64 == 0; }
 
-// K slices of a weight-gradient product C [M][N] over K positions (see gemm_wgrad)
-int wgrad_slices(int M, int N, int K) {
+// K slices of a weight-gradient product C [M][N] over K positions (see gemm_wgrad).
+// bf16 storage (the library's kernel): slices of about 2048 positions (whole
+// 64-position steps), so that the slices of the layer's six products give the
+// chip a few workgroups per CU.  fp32 storage (rocBLAS): slices double while
+// the batch stays within 192 output tiles of 128 x 128 (measured on the main
+// workload's bf16 backward when rocBLAS ran it: caps 768 and 1536 cost 15 and
+// 40 us more, 96 and below 60 us and more).
+int wgrad_ks(int K) {
+  const int S = std::max(1, std::min(BWD_SPLIT_MAX, K / 2048));
+  return ((K + S - 1) / S + 63) & ~63;
+}
+int wgrad_slices(bool bf16, int M, int N, int K) {
+  if (bf16) {
+    const int Ks = wgrad_ks(K);
+    return (K + Ks - 1) / Ks;
+  }
   const int tiles = ((M + 127) / 128) * ((N + 127) / 128);
   int S = 1;
   while (S < BWD_SPLIT_MAX && tiles * S * 2 <= 192 && K % (2 * S) == 0 && K / (2 * S) >= 256) S *= 2;
@@ -65,8 +80,8 @@ int wgrad_slices(int M, int N, int K) {
 }
 
 // fp32 partials a weight-gradient product leaves for the reduction (0: written directly)
-size_t wgrad_part_floats(int M, int N, int K, bool one_full_dst) {
-  const int S = wgrad_slices(M, N, K);
+size_t wgrad_part_floats(bool bf16, int M, int N, int K, bool one_full_dst) {
+  const int S = wgrad_slices(bf16, M, N, K);
   return (S == 1 && one_full_dst) ? 0 : (size_t)S * M * N;
 }
 
@@ -118,8 +133,8 @@ BwdGeom bwd_geom(const PackGeom& g, int64_t B, int64_t L) {
     // the partials of its two weight-gradient products, each in a region of its own
     const int K = (int)prow;
     if (K > 0) {
-      part += wgrad_part_floats(bg.h * g.dv, g.d, K, true);          // W_o
-      part += wgrad_part_floats(g.d, bg.col_g + g.r, K, false);     // q | k | v | W_g1
+      part += wgrad_part_floats(g.bf16, bg.h * g.dv, g.d, K, true);       // W_o
+      part += wgrad_part_floats(g.bf16, g.d, bg.col_g + g.r, K, false);  // q | k | v | W_g1
     }
   }
   G.dz = take((size_t)B * L * FUSION_STRIDE * 4);
@@ -162,29 +177,50 @@ bool gemm_rm(rocblas_handle h, bool tA, bool tB, int M, int N, int K, const void
 // +40 us; 96 and below: +60 us and more).
 bool gemm_wgrad(rocblas_handle h, int M, int N, int K, const void* A, rocblas_datatype ta, int lda,
                 const void* Bm, rocblas_datatype tb, int ldb, const SplitDst& dst, float*& part, const float* part_end,
-                SplitJobs& jobs) {
+                SplitJobs& jobs, Wgrad* wg) {
   if (M == 0 || N == 0) return true;
-  const int S = wgrad_slices(M, N, K);
+  const bool bf16 = wg != nullptr;
+  const int S = wgrad_slices(bf16, M, N, K);
   const bool direct = S == 1 && dst.n == 1 && dst.c0[0] == 0 && dst.nc[0] == N;
   float* C = direct ? dst.p[0] : part;
   if (!direct && (part + (size_t)S * M * N > part_end || jobs.n >= SplitJobs::MAX)) return false;
-  const float alpha = 1.f, beta = 0.f;
-  const int Ks = K / S;
-  const rocblas_stride sA = (rocblas_stride)Ks * lda, sB = (rocblas_stride)Ks * ldb,
-                       sC = (rocblas_stride)M * N;
-  if (rocblas_gemm_strided_batched_ex(h, rocblas_operation_none, rocblas_operation_transpose, N, M, Ks, &alpha, Bm,
-                                      tb, ldb, sB, A, ta, lda, sA, &beta, C, rocblas_datatype_f32_r, N, sC, C,
-                                      rocblas_datatype_f32_r, N, sC, S, rocblas_datatype_f32_r,
-                                      rocblas_gemm_algo_standard, 0, 0) != rocblas_status_success)
-    return false;
+  if (bf16) {
+    // the library's kernel, launched once for every product (launch_bwd_wgrad)
+    if (wg->njobs >= 2 * MSGLA_MAX_BRANCHES) return false;
+    WgradJob& j = wg->j[wg->njobs++];
+    j.A = A;
+    j.B = Bm;
+    j.C = C;
+    j.M = M;
+    j.N = N;
+    j.K = K;
+    j.lda = lda;
+    j.ldb = ldb;
+    j.S = S;
+    j.Ks = wgrad_ks(K);
+    j.tiles_n = (N + 127) / 128;
+    j.tiles = (M + 127) / 128 * j.tiles_n;
+    j.item_begin = wg->items;
+    wg->items += j.tiles * S;
+  } else {
+    const float alpha = 1.f, beta = 0.f;
+    const int Ks = K / S;
+    const rocblas_stride sA = (rocblas_stride)Ks * lda, sB = (rocblas_stride)Ks * ldb,
+                         sC = (rocblas_stride)M * N;
+    if (rocblas_gemm_strided_batched_ex(h, rocblas_operation_none, rocblas_operation_transpose, N, M, Ks, &alpha,
+                                        Bm, tb, ldb, sB, A, ta, lda, sA, &beta, C, rocblas_datatype_f32_r, N, sC, C,
+                                        rocblas_datatype_f32_r, N, sC, S, rocblas_datatype_f32_r,
+                                        rocblas_gemm_algo_standard, 0, 0) != rocblas_status_success)
+      return false;
+  }
   if (!direct) {
     // summed with the other products' partials by one launch at the end
-    const int j = jobs.n++;
-    jobs.part[j] = part;
-    jobs.S[j] = S;
-    jobs.M[j] = M;
-    jobs.N[j] = N;
-    jobs.dst[j] = dst;
+    const int jn = jobs.n++;
+    jobs.part[jn] = part;
+    jobs.S[jn] = S;
+    jobs.M[jn] = M;
+    jobs.N[jn] = N;
+    jobs.dst[jn] = dst;
     part += (size_t)S * M * N;
   }
   return true;
@@ -429,6 +465,8 @@ msgla_status backward_impl(const msgla_config* cfg, const void* packed, const vo
   float* sk = at<float>(workspace, G.splitk);
   const float* sk_end = sk + G.splitk_floats;
   SplitJobs sjobs{};
+  Wgrad wgrad{};  // bf16 storage: the weight-gradient products, one launch
+  Wgrad* wgp = g.bf16 ? &wgrad : nullptr;
   const char* WoT = at<char>(packed, g.off_WoT);
 
   // ---- the weights as the grouped products read them: W_o rows, Wp^T ----
@@ -468,7 +506,7 @@ msgla_status backward_impl(const msgla_config* cfg, const void* packed, const vo
     }
     const void* dYi = Br.s == 1 ? dout : Br.dY;
     BLAS_TRY(gemm_wgrad(hb, hdv, g.d, rows, Br.ycat, ST, hdv, dYi, ST, g.d, one_dst(grads->br[i].W_o, g.d), sk,
-                        sk_end, sjobs));
+                        sk_end, sjobs, wgp));
   }
 
   // ---- the normalisation: dLoss/d(normalised rows) -> dLoss/do, and the gains' gradient ----
@@ -561,8 +599,9 @@ msgla_status backward_impl(const msgla_config* cfg, const void* packed, const vo
     dw.p[1] = gr.W_k, dw.c0[1] = bg.col_k, dw.nc[1] = hdk;
     dw.p[2] = gr.W_v, dw.c0[2] = bg.col_v, dw.nc[2] = hdv;
     dw.p[3] = gr.W_g1, dw.c0[3] = bg.col_g, dw.nc[3] = g.r;
-    BLAS_TRY(gemm_wgrad(hb, g.d, bg.col_g + g.r, rows, xp, ST, g.d, dP, ST, Br.NP, dw, sk, sk_end, sjobs));
+    BLAS_TRY(gemm_wgrad(hb, g.d, bg.col_g + g.r, rows, xp, ST, g.d, dP, ST, Br.NP, dw, sk, sk_end, sjobs, wgp));
   }
+  if (wgp) HIP_TRY(launch_bwd_wgrad(wgrad, st));
   HIP_TRY(launch_bwd_splitk_reduce(sjobs, st));
   HIP_TRY(launch_bwd_dx(P, g.bf16, st));
   if (g.m > 1) {

@@ -149,4 +149,129 @@ hipError_t launch_bwd_transpose(const BwdTranspose& P, bool bf16_path, hipStream
   return hipGetLastError();
 }
 
+
+
+// ---- weight gradients: C = A^T B over the position axis, bf16 storage ----
+// MS-GLA notes, Sec. 3.4 (training paragraph): the gradient of every weight
+// matrix of the layer is a sum over positions of outer products of its input
+// rows and its output's gradient rows, C [M][N] = sum_k A[k][m] B[k][n], with
+// both operands position-major.  The matrix cores read operands with K
+// contiguous, so each 64-position step of a 128 x 128 tile is copied into LDS
+// transposed: a thread loads four positions' 16-byte pieces (eight m, or eight
+// n) and writes each m as one 8-byte run of four positions.  The 16-byte
+// K chunks of an LDS row are XOR-swizzled by (row / 8) % 8, which spreads the
+// transposing writes and the fragment reads over the banks.  Four waves of
+// 64 x 64 (4 x 4 bf16 MFMA tiles) per workgroup; the next step's pieces are
+// loaded into registers while the current step is multiplied.  The K range is
+// cut into slices (work items = (job, slice, tile)) whose fp32 partials are
+// summed by k_bwd_splitk_reduce.
+namespace {
+
+constexpr int WG_T = 128, WG_K = 64;
+
+// byte offset of element k of LDS row r (rows of WG_K bf16, 16-byte chunks swizzled)
+__device__ __forceinline__ int wg_off(int r, int k) {
+  return r * (WG_K * 2) + ((((k >> 3) ^ ((r >> 3) & 7))) << 4) + ((k & 7) << 1);
+}
+
+__global__ __launch_bounds__(256) void k_bwd_wgrad(const Wgrad P) {
+  __shared__ __attribute__((aligned(16))) char at[WG_T * WG_K * 2];  // A^T [m][k]
+  __shared__ __attribute__((aligned(16))) char bt[WG_T * WG_K * 2];  // B^T [n][k]
+  const int item = remap_xcd(blockIdx.x, (P.items + N_XCD - 1) / N_XCD);
+  if (item >= P.items) return;
+  int ji = 0;
+  while (ji + 1 < P.njobs && item >= P.j[ji + 1].item_begin) ++ji;
+  const WgradJob& J = P.j[ji];
+  const int local = item - J.item_begin;
+  // slices outermost: consecutive items are tiles of one slice, which share the
+  // slice's rows of A (along a tile row) and of B
+  const int sl = local / J.tiles, tile = local - sl * J.tiles;
+  const int tm = tile / J.tiles_n, tn = tile - tm * J.tiles_n;
+  const int m0 = tm * WG_T, n0 = tn * WG_T;
+  const int k0 = sl * J.Ks, k1 = min(J.K, k0 + J.Ks);
+  const bf16* A = reinterpret_cast<const bf16*>(J.A);
+  const bf16* B = reinterpret_cast<const bf16*>(J.B);
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lr = l & 15, lg = l >> 4;
+  const int wm = w & 1, wn = w >> 1;
+  // the thread's pieces: columns 8 g .. 8 g + 7 of the tile, positions 4 q .. 4 q + 3
+  const int g = tid & 15, q = tid >> 4;
+  const bool am = m0 + 8 * g < J.M, bn = n0 + 8 * g < J.N;
+  const bf16* pa = A + (am ? m0 + 8 * g : 0);
+  const bf16* pb = B + (bn ? n0 + 8 * g : 0);
+  u32x4 ra[4], rb[4];
+  auto load = [&](int kb) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int k = kb + 4 * q + r;
+      const bool ok = k < k1;
+      const size_t kk = ok ? k : k0;
+      ra[r] = ld16(pa + kk * J.lda);
+      rb[r] = ld16(pb + kk * J.ldb);
+      if (!ok || !am) ra[r] = zero16();
+      if (!ok || !bn) rb[r] = zero16();
+    }
+  };
+  // element e of the four pieces, as one 8-byte run of four positions
+  auto quad = [&](const u32x4 (&v)[4], int e) {
+    const int wd = e >> 1, hi = e & 1;
+    uint32_t h[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) h[r] = hi ? (v[r][wd] >> 16) : (v[r][wd] & 0xffffu);
+    return u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+  };
+  auto stage = [&]() {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      st8(at + wg_off(8 * g + e, 4 * q), quad(ra, e));
+      st8(bt + wg_off(8 * g + e, 4 * q), quad(rb, e));
+    }
+  };
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int jt = 0; jt < 4; ++jt) acc[i][jt] = zero4();
+  if (k0 < k1) load(k0);
+  for (int kb = k0; kb < k1; kb += WG_K) {
+    lds_barrier();  // the previous step's fragments are read
+    stage();
+    lds_barrier();
+    if (kb + WG_K < k1) load(kb + WG_K);
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      u32x4 fa[4], fb[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) fa[i] = ld16(at + wg_off(64 * wm + 16 * i + lr, 32 * s + 8 * lg));
+#pragma unroll
+      for (int jt = 0; jt < 4; ++jt) fb[jt] = ld16(bt + wg_off(64 * wn + 16 * jt + lr, 32 * s + 8 * lg));
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int jt = 0; jt < 4; ++jt) acc[i][jt] = mma_slab<bf16>(fa[i], fb[jt], acc[i][jt]);
+    }
+  }
+  float* C = J.C + (size_t)sl * J.M * J.N;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int m = m0 + 64 * wm + 16 * i + 4 * lg + e;
+      if (m >= J.M) continue;
+#pragma unroll
+      for (int jt = 0; jt < 4; ++jt) {
+        const int n = n0 + 64 * wn + 16 * jt + lr;
+        if (n < J.N) C[(size_t)m * J.N + n] = acc[i][jt][e];
+      }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_bwd_wgrad(const Wgrad& P, hipStream_t st) {
+  if (P.items == 0) return hipSuccess;
+  const int per = (P.items + N_XCD - 1) / N_XCD;
+  hipLaunchKernelGGL(k_bwd_wgrad, dim3(per * N_XCD), dim3(256), 0, st, P);
+  return hipGetLastError();
+}
+
 }  // namespace msgla

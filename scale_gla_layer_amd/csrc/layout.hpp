@@ -367,6 +367,23 @@ struct SplitDst {
   int n;
 };
 
+// Weight-gradient products on the matrix cores (k_bwd_wgrad), bf16 storage:
+// per job C_s [M][N] fp32 = sum over positions k in slice s of A[k][m] B[k][n],
+// A [K][lda] and B [K][ldb] position-major (m and n contiguous), for the
+// slices s < S of Ks positions each; C_s at C + s M N.
+struct WgradJob {
+  const void* A;
+  const void* B;
+  float* C;
+  int M, N, K, lda, ldb, S, Ks;
+  int tiles_n, tiles;  // 128 x 128 output tiles: along N, in all
+  int item_begin;      // first work item (tile, slice) of the job
+};
+struct Wgrad {
+  int njobs, items;
+  WgradJob j[2 * MSGLA_MAX_BRANCHES];
+};
+
 // Every split-K product of a backward, summed by one launch: job j adds the S[j]
 // slices part[j] [S][M][N] into its destinations.
 struct SplitJobs {
