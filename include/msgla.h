@@ -317,16 +317,18 @@ msgla_status msgla_decode_step(const msgla_config* cfg, const void* packed, cons
  * the forward's intermediates itself (it needs no saved activations), keeps
  * every intermediate gradient of the recurrence in fp32, and rounds the
  * operands of its large products (the weight and input gradients) to the
- * storage type, accumulating in fp32.  The plain products run on rocBLAS;
- * everything specific to the layer (the hold and fusion, the chunkwise
- * recurrence, the gate, the pooling) runs in the library's kernels.
+ * storage type, accumulating in fp32.  Everything runs in the library's
+ * kernels (the hold and fusion, the chunkwise recurrence, the gate, the
+ * pooling, and the plain products as grouped GEMMs), except the weight
+ * gradients of fp32 configurations, which run on rocBLAS.
  * With the per-branch normalisation (config norm = 1) the gains' gradient is
  * written too (norm_g required).  d_v must be a multiple of 64
  * (MSGLA_ERR_UNSUPPORTED otherwise: fp32 configurations with d_v 32 or 96).
  * Pointers are device memory, 16-byte aligned.
- * Asynchronous on `stream`; the library's rocBLAS handle for the device is
- * created on the first call (not under graph capture), and calls from several
- * host threads are serialised by the library.
+ * Asynchronous on `stream`.  For fp32 configurations the library's rocBLAS
+ * handle for the device is created on the first call (not under graph
+ * capture), and such calls from several host threads are serialised by the
+ * library.
  */
 typedef struct {
   float* W_q;

@@ -3,9 +3,10 @@
 // forward's intermediates with the forward's own kernels (keeping the coarse
 // outputs Y beside the block means), then walks the layer in reverse: fusion
 // and hold, the output projections, the chunkwise recurrence, the gate, the
-// input projections and the pooling.  The plain products (a weight or input
-// gradient as one GEMM) go to rocBLAS; every layer-specific step runs in the
-// library's kernels.
+// input projections and the pooling.  Every step runs in the library's
+// kernels, the plain products too (grouped GEMMs for the activation gradients,
+// the weight-gradient kernel); only the fp32 layer's weight gradients go to
+// rocBLAS.
 #include <rocblas/rocblas.h>
 
 #include <mutex>
@@ -150,20 +151,6 @@ BwdGeom bwd_geom(const PackGeom& g, int64_t B, int64_t L) {
 }
 
 rocblas_datatype storage_type(bool bf16) { return bf16 ? rocblas_datatype_bf16_r : rocblas_datatype_f32_r; }
-
-// Row-major C[M][N] (ldc, fp32) = op(A) op(B), op(X) = X or X^T as stored
-// row-major: A is [M][K] (tA false, lda >= K) or [K][M] (tA true, lda >= M);
-// B is [K][N] (tB false) or [N][K] (tB true).  rocBLAS is column-major, so it
-// computes C^T = op(B)^T op(A)^T on the same memory.
-bool gemm_rm(rocblas_handle h, bool tA, bool tB, int M, int N, int K, const void* A, rocblas_datatype ta,
-             int lda, const void* Bm, rocblas_datatype tb, int ldb, float* C, int ldc) {
-  if (M == 0 || N == 0) return true;
-  const float alpha = 1.f, beta = 0.f;
-  return rocblas_gemm_ex(h, tB ? rocblas_operation_transpose : rocblas_operation_none,
-                         tA ? rocblas_operation_transpose : rocblas_operation_none, N, M, K, &alpha, Bm, tb, ldb, A,
-                         ta, lda, &beta, C, rocblas_datatype_f32_r, ldc, C, rocblas_datatype_f32_r, ldc,
-                         rocblas_datatype_f32_r, rocblas_gemm_algo_standard, 0, 0) == rocblas_status_success;
-}
 
 // Weight gradient C[M][N] = A^T B with A row-major [K][M] (lda) and B row-major
 // [K][N] (ldb), K the long reduction over positions, written to the column
@@ -379,9 +366,14 @@ msgla_status backward_impl(const msgla_config* cfg, const void* packed, const vo
       return s;
   }
 
-  std::lock_guard<std::mutex> lock(g_blas_mu);
-  rocblas_handle hb = blas_handle();
-  if (!hb || rocblas_set_stream(hb, st) != rocblas_status_success) return MSGLA_ERR_HIP;
+  // rocBLAS (the fp32 layer's weight gradients only): the device's handle, one caller at a time
+  std::unique_lock<std::mutex> lock(g_blas_mu, std::defer_lock);
+  rocblas_handle hb = nullptr;
+  if (!g.bf16) {
+    lock.lock();
+    hb = blas_handle();
+    if (!hb || rocblas_set_stream(hb, st) != rocblas_status_success) return MSGLA_ERR_HIP;
+  }
 
   BwdParams P{};
   P.B = (int)B;

@@ -29,8 +29,8 @@
 //    db_g = sum of dz                              (k_bwd_gate_grads, k_bwd_mcolsum_*);
 //  the pooling (Sec. 3.1, Eq. (8)): dx_t += dxp_j / s for t in complete block j,
 //  plus the fusion logits' dz_t W_f^T                                   (k_bwd_dx).
-// The plain products around these (dY W_o^T, the weight gradients and the
-// pooled inputs' gradient) are left to the host's GEMM calls.
+// The plain products around these (dO W_o^T and dY W_o^T, the pooled inputs'
+// gradient, the weight gradients) run in k_bwd_gemm.hip.
 #include "async_copy.hpp"
 #include "device_common.hpp"
 #include "layout.hpp"
