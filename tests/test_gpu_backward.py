@@ -10,7 +10,9 @@ several chunks with a ragged last chunk in every branch, tail positions past a
 coarse branch's last complete block, chunks 16, 32 and 64 (bf16: 32 and 64, key widths
 32 to 256), q_scale and gamma
 off their defaults, strong gates, a scale set without a scale-1 branch, a
-single branch (no fusion), a branch whose scale exceeds the sequence, and the
+single branch (no fusion), a branch whose scale exceeds the sequence, sequences
+shorter than a chunk (down to one position, where no coarse branch or, at scales
+{2, 4}, no branch at all has a complete block), and the
 main configuration's dimensions in bf16, and the full main workload (B = 8,
 L = 2048)."""
 import dataclasses
@@ -128,6 +130,25 @@ def test_fp32_single_branch():
 def test_fp32_scale_longer_than_sequence():
     """The scale-8 branch has no complete block: zero gradients for its weights."""
     backward_case(_cfg(scales=(1, 8), heads=(1, 1)), B=2, L=7, seed=11)
+
+
+@pytest.mark.parametrize("L", [1, 3, 5])
+def test_bf16_main_dimensions_short_sequences(L):
+    """Fewer positions than a chunk: at L = 1 the coarse branches have no complete
+    block, at 3 the scale-2 branch has one, at 5 the scale-4 branch has one."""
+    backward_case(WORKLOADS["main"].cfg, B=3, L=L, seed=61 + L)
+
+
+def test_bf16_no_complete_block_in_any_branch():
+    """Every branch's scale exceeds the sequence: the output is zero, so dx and every
+    gradient are exactly zero (dx_error requires exact zeros where the oracle's are)."""
+    cfg = _cfg(dtype=BF16, scales=(2, 4), heads=(1, 2), d_model=128, d_v=64, chunk=32)
+    errs = backward_case(cfg, B=2, L=1, seed=67)
+    assert all(v == 0.0 for v in errs.values()), errs
+
+
+def test_fp32_single_position():
+    backward_case(_cfg(), B=2, L=1, seed=71)
 
 
 def test_fp32_key_width_128_rank_64():
