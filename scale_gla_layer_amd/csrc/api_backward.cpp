@@ -59,14 +59,16 @@ struct BwdGeom {
 bool bwd_supported(const msgla_config* cfg) { return cfg->d_v % 64 == 0; }
 
 // K slices of a weight-gradient product C [M][N] over K positions (see gemm_wgrad).
-// bf16 storage (the library's kernel): slices of about 2048 positions (whole
-// 64-position steps), so that the slices of the layer's six products give the
-// chip a few workgroups per CU.  fp32 storage (rocBLAS): slices double while
-// the batch stays within 192 output tiles of 128 x 128 (measured on the main
-// workload's bf16 backward when rocBLAS ran it: caps 768 and 1536 cost 15 and
-// 40 us more, 96 and below 60 us and more).
+// bf16 storage (the library's kernel): slices of about 4096 positions (whole
+// 64-position multiples), which give the main workload's six products 680 work
+// items, about three workgroups per CU in one round (measured against 2048,
+// 3072 and 8192 positions: the kernel plus the reduction took 163, 154 and 254
+// us against 151 us).  fp32 storage (rocBLAS): slices double while the batch
+// stays within 192 output tiles of 128 x 128 (measured on the main workload's
+// bf16 backward when rocBLAS ran it: caps 768 and 1536 cost 15 and 40 us more,
+// 96 and below 60 us and more).
 int wgrad_ks(int K) {
-  const int S = std::max(1, std::min(BWD_SPLIT_MAX, K / 2048));
+  const int S = std::max(1, std::min(BWD_SPLIT_MAX, K / 4096));
   return ((K + S - 1) / S + 63) & ~63;
 }
 int wgrad_slices(bool bf16, int M, int N, int K) {

@@ -155,28 +155,66 @@ hipError_t launch_bwd_transpose(const BwdTranspose& P, bool bf16_path, hipStream
 // MS-GLA notes, Sec. 3.4 (training paragraph): the gradient of every weight
 // matrix of the layer is a sum over positions of outer products of its input
 // rows and its output's gradient rows, C [M][N] = sum_k A[k][m] B[k][n], with
-// both operands position-major.  The matrix cores read operands with K
-// contiguous, so each 64-position step of a 128 x 128 tile is copied into LDS
-// transposed: a thread loads four positions' 16-byte pieces (eight m, or eight
-// n) and writes each m as one 8-byte run of four positions.  The 16-byte
-// K chunks of an LDS row are XOR-swizzled by (row / 8) % 8, which spreads the
-// transposing writes and the fragment reads over the banks.  Four waves of
-// 64 x 64 (4 x 4 bf16 MFMA tiles) per workgroup; the next step's pieces are
-// loaded into registers while the current step is multiplied.  The K range is
-// cut into slices (work items = (job, slice, tile)) whose fp32 partials are
-// summed by k_bwd_splitk_reduce.
+// both operands position-major.  A workgroup forms a 128 x 128 tile with four
+// waves of 64 x 64 (4 x 4 bf16 MFMA tiles).  Each step of WG_KS positions
+// copies both operands global -> LDS asynchronously, one 256-byte row per
+// position (the tile's 128 columns), into one of WG_NST rotating stages,
+// WG_NST - 1 steps ahead of the products, with one LDS-only barrier per step.
+// The matrix cores want each lane's operand K-contiguous; the LDS transpose
+// read (ds_read_b64_tr_b16) supplies that from the position-major rows: in
+// each 16-lane group, lane i receives element i % 4 of the 8-byte reads of
+// lanes 4 e + i / 4 (e = 0 .. 3).  So a lane that reads the four columns
+// 4 q .. 4 q + 3 of position row 4 h + e of its group's eight (lane = 16 g +
+// 4 e + q) hands every lane of the group one column's four consecutive
+// positions, and two such reads (h = 0, 1) make the eight positions of a
+// 16 x 16 x 32 operand.  The 16-byte pieces of row r sit XOR-swizzled by
+// (r % 4) + 4 ((r / 8) % 4), which gives the 16 rows of one read 16 distinct
+// keys: the read's 32 pieces cover each bank pair twice (the minimum).  The
+// K range is cut into slices (work items = (job, slice, tile)) whose fp32
+// partials are summed by k_bwd_splitk_reduce.
 namespace {
 
-constexpr int WG_T = 128, WG_K = 64;
+constexpr int WG_T = 128;                      // output tile edge
+// 32 positions per step in two stages (32 KB of LDS, three workgroups per CU at
+// 131 registers): measured against 64-position steps in two stages (2 per CU)
+// and 32-position steps in three or four stages, and against a cap of 128
+// registers for a fourth workgroup, all slower
+constexpr int WG_KS = 32;                      // positions per step
+constexpr int WG_NST = 2;                      // LDS stages
+constexpr int WG_ROW = WG_T * 2;               // bytes of one position row of an operand tile
+constexpr int WG_OPB = WG_KS * WG_ROW;         // bytes of one operand per stage
+constexpr int WG_STAGE = 2 * WG_OPB;
+constexpr int WG_CP = WG_OPB / 1024 / 4;       // copy instructions per wave, operand and step
+static_assert(WG_KS % 32 == 0 && WG_CP >= 1 && (WG_NST - 2) * 2 * WG_CP < 64, "weight-gradient pipeline");
 
-// byte offset of element k of LDS row r (rows of WG_K bf16, 16-byte chunks swizzled)
-__device__ __forceinline__ int wg_off(int r, int k) {
-  return r * (WG_K * 2) + ((((k >> 3) ^ ((r >> 3) & 7))) << 4) + ((k & 7) << 1);
+__device__ __forceinline__ int wg_key(int r) { return (r & 3) | (((r >> 3) & 3) << 2); }
+
+typedef short wg_v4s __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) wg_v4s lds_v4s;
+
+// 8 bf16 operand values: positions 8 g .. 8 g + 7 of the lane's column, from
+// the two transpose reads at byte offsets off and off + 4 rows
+__device__ __forceinline__ u32x4 wg_frag(const char* p) {
+  const wg_v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(p));
+  const wg_v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(p + 4 * WG_ROW));
+  const u32x2 a = __builtin_bit_cast(u32x2, lo), b = __builtin_bit_cast(u32x2, hi);
+  return u32x4{a[0], a[1], b[0], b[1]};
+}
+
+// zero the operand values of positions >= valid (slab-local position of value
+// j: 8 g + j)
+__device__ __forceinline__ u32x4 wg_mask(u32x4 v, int g, int valid) {
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const int k = 8 * g + 2 * w;
+    const uint32_t lo = k < valid ? 0xffffu : 0u, hi = k + 1 < valid ? 0xffff0000u : 0u;
+    v[w] &= lo | hi;
+  }
+  return v;
 }
 
 __global__ __launch_bounds__(256) void k_bwd_wgrad(const Wgrad P) {
-  __shared__ __attribute__((aligned(16))) char at[WG_T * WG_K * 2];  // A^T [m][k]
-  __shared__ __attribute__((aligned(16))) char bt[WG_T * WG_K * 2];  // B^T [n][k]
+  __shared__ __attribute__((aligned(16))) char lds[WG_NST * WG_STAGE];
   const int item = remap_xcd(blockIdx.x, (P.items + N_XCD - 1) / N_XCD);
   if (item >= P.items) return;
   int ji = 0;
@@ -189,61 +227,82 @@ __global__ __launch_bounds__(256) void k_bwd_wgrad(const Wgrad P) {
   const int tm = tile / J.tiles_n, tn = tile - tm * J.tiles_n;
   const int m0 = tm * WG_T, n0 = tn * WG_T;
   const int k0 = sl * J.Ks, k1 = min(J.K, k0 + J.Ks);
-  const bf16* A = reinterpret_cast<const bf16*>(J.A);
-  const bf16* B = reinterpret_cast<const bf16*>(J.B);
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lr = l & 15, lg = l >> 4;
+  const char* A = reinterpret_cast<const char*>(J.A);
+  const char* B = reinterpret_cast<const char*>(J.B);
+  const int tid = threadIdx.x, l = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = w & 1, wn = w >> 1;
-  // the thread's pieces: columns 8 g .. 8 g + 7 of the tile, positions 4 q .. 4 q + 3
-  const int g = tid & 15, q = tid >> 4;
-  const bool am = m0 + 8 * g < J.M, bn = n0 + 8 * g < J.N;
-  const bf16* pa = A + (am ? m0 + 8 * g : 0);
-  const bf16* pb = B + (bn ? n0 + 8 * g : 0);
-  u32x4 ra[4], rb[4];
-  auto load = [&](int kb) {
+
+  // copy slots: instruction j of this wave fills rows 4 (WG_CP w + j) .. + 3 of
+  // a stage's operand block; the lane's 16 bytes land in row 4 (WG_CP w + j) +
+  // l / 16, physical piece l % 16, and carry the logical piece (columns)
+  // (l % 16) ^ key(row).  Pieces past the problem's columns read column 0
+  // (their results are not stored).
+  const int crow = 4 * WG_CP * w + (l >> 4);
+  int acol[WG_CP], bcol[WG_CP];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int k = kb + 4 * q + r;
-      const bool ok = k < k1;
-      const size_t kk = ok ? k : k0;
-      ra[r] = ld16(pa + kk * J.lda);
-      rb[r] = ld16(pb + kk * J.ldb);
-      if (!ok || !am) ra[r] = zero16();
-      if (!ok || !bn) rb[r] = zero16();
+  for (int j = 0; j < WG_CP; ++j) {
+    const int lp = (l & 15) ^ wg_key(crow + 4 * j);
+    const int ma = m0 + 8 * lp, nb = n0 + 8 * lp;
+    acol[j] = (ma < J.M ? ma : 0) * 2;
+    bcol[j] = (nb < J.N ? nb : 0) * 2;
+  }
+  const size_t lda = (size_t)J.lda * 2, ldb = (size_t)J.ldb * 2;
+  const int nsteps = (k1 - k0 + WG_KS - 1) / WG_KS;
+  // positions past the slice's end read its first row (their values are zeroed
+  // after the transpose reads)
+  auto issue = [&](int t) {
+    char* st = lds + (t % WG_NST) * WG_STAGE;
+#pragma unroll
+    for (int j = 0; j < WG_CP; ++j) {
+      const int k = k0 + t * WG_KS + crow + 4 * j;
+      const size_t kk = k < k1 ? k : k0;
+      dma16(A + kk * lda + acol[j], st + 1024 * (WG_CP * w + j));
+      dma16(B + kk * ldb + bcol[j], st + WG_OPB + 1024 * (WG_CP * w + j));
     }
   };
-  // element e of the four pieces, as one 8-byte run of four positions
-  auto quad = [&](const u32x4 (&v)[4], int e) {
-    const int wd = e >> 1, hi = e & 1;
-    uint32_t h[4];
+
+  // transpose-read offsets: lane 16 g + 4 e + q reads columns 4 q .. 4 q + 3 of
+  // 16-column tile i, position row 8 g + e (+ 4 for the second read) of a slab
+  const int g = l >> 4, e = (l >> 2) & 3, q = l & 3;
+  const int key = e | (g << 2);
+  int offA[4], offB[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) h[r] = hi ? (v[r][wd] >> 16) : (v[r][wd] & 0xffffu);
-    return u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
-  };
-  auto stage = [&]() {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      st8(at + wg_off(8 * g + e, 4 * q), quad(ra, e));
-      st8(bt + wg_off(8 * g + e, 4 * q), quad(rb, e));
-    }
-  };
+  for (int i = 0; i < 4; ++i) {
+    const int base = (8 * g + e) * WG_ROW + 8 * (q & 1);
+    offA[i] = base + 16 * (((8 * wm + 2 * i) + (q >> 1)) ^ key);
+    offB[i] = WG_OPB + base + 16 * (((8 * wn + 2 * i) + (q >> 1)) ^ key);
+  }
+
   f32x4 acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int jt = 0; jt < 4; ++jt) acc[i][jt] = zero4();
-  if (k0 < k1) load(k0);
-  for (int kb = k0; kb < k1; kb += WG_K) {
-    lds_barrier();  // the previous step's fragments are read
-    stage();
+
+  for (int t = 0; t < WG_NST - 1 && t < nsteps; ++t) issue(t);
+  for (int t = 0; t < nsteps; ++t) {
+    // step t has landed once only the copies of later steps remain
+    wait_stages<2 * WG_CP, WG_NST - 2>(min(WG_NST - 2, nsteps - 1 - t));
     lds_barrier();
-    if (kb + WG_K < k1) load(kb + WG_K);
+    if (t + WG_NST - 1 < nsteps) issue(t + WG_NST - 1);
+    const char* st = lds + (t % WG_NST) * WG_STAGE;
+    const int valid = k1 - k0 - t * WG_KS;  // positions of this step inside the slice
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
+    for (int s = 0; s < WG_KS / 32; ++s) {
       u32x4 fa[4], fb[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) fa[i] = ld16(at + wg_off(64 * wm + 16 * i + lr, 32 * s + 8 * lg));
+      for (int i = 0; i < 4; ++i) {
+        fa[i] = wg_frag(st + offA[i] + 32 * s * WG_ROW);
+        fb[i] = wg_frag(st + offB[i] + 32 * s * WG_ROW);
+      }
+      if (valid < WG_KS) {
 #pragma unroll
-      for (int jt = 0; jt < 4; ++jt) fb[jt] = ld16(bt + wg_off(64 * wn + 16 * jt + lr, 32 * s + 8 * lg));
+        for (int i = 0; i < 4; ++i) {
+          fa[i] = wg_mask(fa[i], g, valid - 32 * s);
+          fb[i] = wg_mask(fb[i], g, valid - 32 * s);
+        }
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -251,16 +310,17 @@ __global__ __launch_bounds__(256) void k_bwd_wgrad(const Wgrad P) {
     }
   }
   float* C = J.C + (size_t)sl * J.M * J.N;
+  const int lr = l & 15, lg = l >> 4;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int m = m0 + 64 * wm + 16 * i + 4 * lg + e;
+    for (int r = 0; r < 4; ++r) {
+      const int m = m0 + 64 * wm + 16 * i + 4 * lg + r;
       if (m >= J.M) continue;
 #pragma unroll
       for (int jt = 0; jt < 4; ++jt) {
         const int n = n0 + 64 * wn + 16 * jt + lr;
-        if (n < J.N) C[(size_t)m * J.N + n] = acc[i][jt][e];
+        if (n < J.N) C[(size_t)m * J.N + n] = acc[i][jt][r];
       }
     }
 }
