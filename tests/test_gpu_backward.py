@@ -206,6 +206,14 @@ def test_bf16_main_dimensions_normalised_and_masked():
     backward_case(cfg, B=B, L=L, seed=41, M=make_mask(B, L, seed=41, hole_prob=0.1))
 
 
+def test_bf16_weight_gradient_slices_with_a_ragged_step():
+    """B = 3, L = 2731 at the main dimensions: the scale-1 branch's weight gradients
+    reduce over 8193 positions, cut into two slices of which the second ends 1 position
+    into a 32-position step (the step's other positions zeroed in the operands); the
+    coarse branches reduce over 4095 and 2046 positions in one slice each."""
+    backward_case(WORKLOADS["main"].cfg, B=3, L=2731, seed=47)
+
+
 def test_bf16_full_size_main_workload():
     """The main workload at its full size (B = 8, L = 2048): every gradient against the
     oracle, which runs sequence by sequence (a weight gradient is the sum of the
